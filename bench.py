@@ -1,0 +1,242 @@
+"""Benchmark: one layer decode step of low-rank KV-cache attention on one MI355X.
+
+A step is one pass of the whole hot path for one layer and one new token per sequence:
+lowrank_kv_append (project the new K/V rows with the caller's pseudo-inverse, store them in
+the cache format, advance the lengths) followed by lowrank_attn_decode (fold, split-token latent
+decode, combine + up-projection). Inputs are seeded synthetic data already resident in HBM.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+Default workload: batch 16, 32768 cached tokens per sequence, rank 256 for K and V, bf16 latents
+(the long-context point of the TraceKV latency setting: batch 16, 4K-32K context).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_TBS = 8.0   # MI355X HBM3E peak, TB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime the process already uses (torch's)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime first)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, e: int) -> None:
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def latent_bytes_per_token(latent: str, rank: int) -> int:
+    if latent == "bf16":
+        return 2 * rank
+    if latent == "f32":
+        return 4 * rank
+    g = (rank + 31) // 32
+    return (rank + 1) // 2 + 4 * g          # packed nibbles + fp16 scale and zero per group
+
+
+def step_bytes(cfg, rk, rv, lat_len, win_len, n_new):
+    """Algorithmic HBM bytes of one layer step (append + decode), see the benchmark notes."""
+    D, Hq, d, B = cfg.kv_width, cfg.n_q_heads, cfg.head_dim, cfg.batch
+    base_e = 4 if cfg.latent == "f32" else 2
+    lat = int(np.sum(lat_len)) * (latent_bytes_per_token(cfg.latent, rk) + latent_bytes_per_token(cfg.latent, rv))
+    win = int(np.sum(win_len)) * 2 * D * 2
+    bases = (rk + rv) * D * base_e
+    q_out = B * Hq * d * (base_e + 4)
+    append = (B * n_new * 2 * D * 2 + (rk + rv) * D * base_e
+              + B * n_new * (latent_bytes_per_token(cfg.latent, rk) + latent_bytes_per_token(cfg.latent, rv)))
+    return dict(latents=lat, window=win, bases=bases, q_out=q_out, append=append,
+                total=lat + win + bases + q_out + append)
+
+
+def cpu_baseline(cfg, li, budget_s: float = 20.0):
+    """Times the fp64 oracle (latent-domain path) on the host cores over whole sequences of the
+    same workload, as many as fit the time budget (at least one)."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as OA
+    from oracle import quant as OQ
+
+    def oracle_latents(which, b):
+        z = li.zk if which == "k" else li.zv
+        r = li.rank_k if which == "k" else li.rank_v
+        rows = z[b, :int(li.lat_len[b]), :r].float().numpy()
+        if cfg.latent == "i4g32":
+            rows = OQ.dequant_rows(*OQ.quantize_rows(rows), r)
+        return rows.astype(np.float64)
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    q = li.q.float().numpy()
+    bk = li.bk.float().numpy()
+    bv = li.bv.float().numpy()
+    done, t_total, nbytes = 0, 0.0, 0
+    for b in range(cfg.batch):
+        zk = oracle_latents("k", b)
+        zv = oracle_latents("v", b)
+
+        class One:
+            def __init__(self, rows):
+                self.rows = rows
+
+            def __getitem__(self, i):
+                return self.rows
+
+        t0 = time.perf_counter()
+        OA.decode_latent(q, One(zk), One(zv), bk, bv, li.lat_len, li.rank_k, li.rank_v, cfg.n_kv_heads,
+                         cfg.sm_scale, batches=[b])
+        t_total += time.perf_counter() - t0
+        done += 1
+        nbytes += int(li.lat_len[b]) * (latent_bytes_per_token(cfg.latent, li.rank_k)
+                                        + latent_bytes_per_token(cfg.latent, li.rank_v))
+        if t_total >= budget_s:
+            break
+    return dict(value=nbytes / t_total / 1e12, unit="TB/s", cores=int(threads), kind="oracle",
+                sample=f"{done} of {cfg.batch} sequences x {int(li.lat_len[0])} tokens, fp64 latent-domain "
+                       f"oracle, {t_total:.2f} s; latent bytes per second in the benchmark's units",
+                us_per_layer_step=t_total / done * cfg.batch * 1e6)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--nsplit", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py: only --gpus 1 is supported (single-GPU build)")
+        sys.exit(2)
+
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+    import synth
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = "cuda"
+    cfg = synth.CONFIGS[args.config]
+    if cfg.n_layers != 1 or cfg.window:
+        raise SystemExit("bench.py times single-layer configurations without a window (0-3)")
+    K, W = args.steps, args.warmup
+    T = cfg.seq_len
+    n_new = 1
+    # Lengths start W+K short of T so that the last timed step attends over exactly T tokens.
+    start_len = np.full(cfg.batch, T - (W + K) * n_new, np.int32)
+    log(f"generating inputs for {cfg.name} ...")
+    t0 = time.time()
+    li = synth.make_layer(cfg, t_cap=T, lat_len=np.full(cfg.batch, T, np.int32))
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+    from synth.device import device_layer
+    model, cache = device_layer(li, dev, with_proj=True)
+    lat0 = torch.from_numpy(start_len).to(dev)
+    cache.tensors["lat_len"].copy_(lat0)
+    q = li.q.to(dev)
+    gen = np.random.default_rng(12345)
+    k_new = torch.from_numpy(gen.standard_normal((cfg.batch, n_new, cfg.kv_width), dtype=np.float32)).to(
+        torch.bfloat16).to(dev)
+    v_new = torch.from_numpy(gen.standard_normal((cfg.batch, n_new, cfg.kv_width), dtype=np.float32)).to(
+        torch.bfloat16).to(dev)
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+    ws = lr.workspace(model, 0, cfg.batch, T, args.nsplit)
+    ev = HipEvents()
+    evs = [(ev.create(), ev.create()) for _ in range(K)]
+    torch.cuda.synchronize()
+
+    lens = []
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for i in range(W + K):
+        if i == W:
+            torch.cuda.synchronize()
+            start.record()
+        lr.lowrank_kv_append(model, 0, cache, k_new, v_new)
+        timed = i >= W
+        lr.lowrank_attn_decode(model, 0, cache, q, out, T, ws, nsplit=args.nsplit,
+                               events=evs[i - W] if timed else None)
+        if timed:
+            lens.append(start_len + (i + 1) * n_new)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / K
+    kern_ms = [ev.elapsed_ms(a, b) for a, b in evs]
+    kern_avg_ms = float(np.mean(kern_ms))
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    assert torch.isfinite(out).all(), "non-finite output"
+
+    by = [step_bytes(cfg, li.rank_k, li.rank_v, L, np.zeros_like(L), n_new) for L in lens]
+    step_total = float(np.mean([x["total"] for x in by]))
+    lat_avg = float(np.mean([x["latents"] + x["window"] for x in by]))
+    value = step_total / (ms_per_step * 1e-3) / 1e12
+    achieved = lat_avg / (kern_avg_ms * 1e-3) / 1e9
+    log(f"ms/step {ms_per_step:.4f}  decode kernel {kern_avg_ms * 1e3:.2f} us  step {value:.3f} TB/s  "
+        f"kernel {achieved / 1e3:.3f} TB/s")
+
+    rec = {
+        "metric": "µs per layer decode step & achieved HBM TB/s (B=16, T=4K–32K)",
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_layer_step": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.latent,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": T, "rank_k": li.rank_k,
+                   "rank_v": li.rank_v, "latent": cfg.latent, "q_heads": cfg.n_q_heads,
+                   "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "new_tokens_per_step": n_new,
+                   "parallelism": "single GPU"},
+        "step_bytes": int(step_total),
+        "roofline": {"bound": "hbm", "kernel": "lr_decode", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s",
+                     "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4), "traffic": None,
+                     "kernel_us": round(kern_avg_ms * 1e3, 2), "bytes_per_launch": int(lat_avg)},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(cfg, li)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

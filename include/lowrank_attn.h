@@ -1,0 +1,197 @@
+/*
+ * lowrank_attn.h -- C ABI of the MI355X (gfx950) low-rank KV-cache decode-attention library.
+ *
+ * The method: the KV cache stores low-dimensional latents of the key and value states,
+ * optionally quantised, and decode attention is computed from those latents (TraceKV,
+ * "TraceKV: Policy-Preserving Low-Rank KV Cache Compression for Reasoning Vision-Language
+ * Models", abstract; ai4snews page on TraceKV, Synopsis: 70% rank ratio with 4-bit
+ * quantisation). An exact window of the most recent tokens can sit beside the latent history,
+ * older tokens being folded into the latents (iS-KV, "iS-KV: Online Low-Rank KV Cache
+ * Compression via Block-Incremental SVD", English abstract). Ranks may differ per layer
+ * (TraceKV abstract and ai4snews Interpretation: global rank allocation).
+ *
+ * One layer l of a model with Hq query heads, Hkv KV heads and head dimension d (D = Hkv*d):
+ *   K = Zk Bk,  V = Zv Bv           Zk [T, rank_k[l]], Bk [rank_k[l], D]  (same for V)
+ *   head j uses KV head g = j / (Hq/Hkv), columns g*d .. g*d+d-1 of K and V
+ *   out_j = softmax_t(sm_scale * q_j . K[t, g]) V[t, g]  over latent and window tokens
+ * The library never reconstructs K or V: it folds q_j into the latent space
+ * (qt_j = q_j Bk[:, g]^T), scores the latent keys, runs an online softmax split over token
+ * ranges, accumulates the probability-weighted latent values and up-projects once through Bv.
+ *
+ * Conventions (all entry points)
+ *   - Every pointer not marked "host" is HIP device memory owned by the caller. The library
+ *     allocates nothing, keeps no pointer after a call returns and holds no state.
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     nothing synchronises with the host. Buffers must stay alive until the stream reaches
+ *     the work.
+ *   - Every precondition the host can check is checked before any launch. On failure the
+ *     call returns LR_EINVAL or LR_EUNSUPPORTED, launches nothing and records a message for
+ *     lowrank_last_error(). A launch failure returns LR_EHIP. No exception crosses the ABI
+ *     and nothing is printed. Outputs are undefined after an error.
+ *   - Device-side lengths (lat_len, win_len) cannot be checked without a sync; kernels clamp
+ *     them to [0, t_cap] and [0, window] (and decode to max_lat_len), so no access is ever out
+ *     of bounds, but the result for an out-of-range length is unspecified.
+ *   - Calls on the same stream are ordered; calls that share an output or workspace buffer on
+ *     different streams race.
+ */
+#ifndef LOWRANK_ATTN_H
+#define LOWRANK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWRANK_ABI_VERSION 1
+
+typedef enum {
+  LR_OK = 0,
+  LR_EINVAL = -1,        /* a null pointer, a size out of range, an inconsistent layout */
+  LR_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. head_dim != 128, > 32 q heads) */
+  LR_EWORKSPACE = -3,    /* workspace smaller than lowrank_attn_decode_workspace_size() */
+  LR_EHIP = -4           /* a HIP launch or runtime call failed */
+} lr_status;
+
+typedef enum {
+  LR_F32 = 0,    /* float32 */
+  LR_BF16 = 1,   /* bfloat16 */
+  LR_I4G32 = 2   /* int4 codes in groups of 32 along the rank, float16 scale and zero per group */
+} lr_dtype;
+
+/* Static description of a model; host memory. */
+typedef struct {
+  int32_t n_layers;        /* >= 1 */
+  int32_t n_q_heads;       /* Hq, 1..32 */
+  int32_t n_kv_heads;      /* Hkv, divides Hq */
+  int32_t head_dim;        /* d; must be 128 */
+  const int32_t* rank_k;   /* host [n_layers]: the per-layer key rank table, each in 1..512 */
+  const int32_t* rank_v;   /* host [n_layers]: the per-layer value rank table, each in 1..512 */
+  float sm_scale;          /* softmax scale, normally 1/sqrt(d) */
+  int32_t window;          /* W: exact recent tokens kept dense per sequence; 0 = none */
+  int32_t latent_dtype;    /* lr_dtype of the stored latents: LR_F32, LR_BF16 or LR_I4G32 */
+} lr_model_desc;
+
+/*
+ * One layer's cache. B sequences, each with t_cap latent rows allocated.
+ *
+ * Latent storage, per sequence b and row t (row = absolute token position t < lat_len[b]):
+ *   LR_F32 / LR_BF16: zk [B][t_cap][ld_k], zv [B][t_cap][ld_v] elements of that dtype.
+ *                     Elements rank..ld-1 of a row are never read into a result.
+ *   LR_I4G32:         zk [B][t_cap][ceil(rank_k/32)*16] bytes of packed codes: group g of a
+ *                     row is 16 bytes, code i of the group in byte i/2, even i in the low
+ *                     nibble; unused nibbles of a partial last group are 0.
+ *                     zk_qp [B][t_cap][ceil(rank_k/32)] uint32: float16 scale in the low half,
+ *                     float16 zero in the high half. Element value = code * scale + zero,
+ *                     evaluated as one float32 fused multiply-add. ld_k, ld_v are ignored.
+ *   Quantisation of a row z (float32), per group of 32 indices (the last may be partial; its
+ *   min/max run over its real elements): zero = f16(min), scale = f16(f32(max-min)/15),
+ *   code = clamp(rint((z - zero)/scale), 0, 15) in float32, all codes 0 if scale == 0.
+ * Bases (row-major): bk [rank_k][D], bv [rank_v][D]; float32 if latent_dtype == LR_F32, else
+ *   bfloat16. Down-projections pk [D][rank_k], pv [D][rank_v] (the caller's pseudo-inverse of
+ *   the bases, same dtype as the bases): used by append only, may be NULL for decode.
+ * Exact window (window W > 0): kwin, vwin [B][W][D] bfloat16 rings; the token at absolute
+ *   position p sits in slot p mod W. Sequence b holds win_len[b] window tokens at positions
+ *   lat_len[b] .. lat_len[b]+win_len[b]-1. NULL when W == 0.
+ * Lengths: lat_len, win_len [B] int32 device arrays; decode reads them, append advances them.
+ *   win_len may be NULL when W == 0.
+ */
+typedef struct {
+  void* zk;
+  void* zv;
+  void* zk_qp;
+  void* zv_qp;
+  const void* bk;
+  const void* bv;
+  const void* pk;
+  const void* pv;
+  void* kwin;
+  void* vwin;
+  int32_t* lat_len;
+  int32_t* win_len;
+  int32_t ld_k;            /* latent row stride in elements (F32/BF16): >= rank_k, multiple of 8 */
+  int32_t ld_v;            /* >= rank_v, multiple of 8 */
+  int64_t t_cap;           /* latent rows allocated per sequence, >= 1 */
+} lr_layer_cache;
+
+/* Optional decode tuning and timing hooks. */
+typedef struct {
+  int32_t nsplit;          /* token ranges per sequence; 0 = automatic */
+  int32_t reserved0;       /* must be 0 */
+  void* event_begin;       /* NULL, or a hipEvent_t recorded on `stream` just before the latent
+                              decode kernel (the one that streams the cache) */
+  void* event_end;         /* NULL, or a hipEvent_t recorded on `stream` just after it */
+  int32_t reserved[4];     /* must be 0 */
+} lr_decode_opts;
+
+/*
+ * Bytes of device workspace lowrank_attn_decode needs for this layer, batch and length bound
+ * (256-byte aligned base required). Returns 0 if the arguments are invalid.
+ */
+size_t lowrank_attn_decode_workspace_size(const lr_model_desc* model, int32_t layer, int32_t batch,
+                                          int32_t max_lat_len, const lr_decode_opts* opts);
+
+/*
+ * Decode attention for one new query token per sequence, layer `layer`.
+ *   q   [B][Hq][d]: float32 if latent_dtype == LR_F32, else bfloat16.
+ *   out [B][Hq][d]: out_dtype LR_F32 or LR_BF16. Sequences with no token give 0.
+ *   max_lat_len: host upper bound on lat_len[b] (sizes the grid); 0 <= max_lat_len <= t_cap.
+ *   workspace: >= lowrank_attn_decode_workspace_size(...) bytes, 256-byte aligned; its
+ *   contents on entry do not matter.
+ * Writes only `out` and `workspace`. opts may be NULL.
+ */
+int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                        int32_t batch, int32_t max_lat_len, const void* q, void* out,
+                        int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                        const lr_decode_opts* opts, void* stream);
+
+/*
+ * Append n_new tokens per sequence (iS-KV abstract: keep the recent window exact, fold older
+ * tokens into the latent history; TraceKV abstract: latents optionally quantised).
+ *   k_new, v_new [B][n_new][D] bfloat16 dense rows, in arrival order.
+ * W == 0: token i of sequence b becomes latent row lat_len[b] + i, z = x P (float32
+ *   accumulation), stored in the cache dtype (bf16: round to nearest even; int4: quantised
+ *   as described above).
+ * W > 0: tokens enter the window ring; whenever the window is full the oldest window token
+ *   (absolute position lat_len[b]) is projected and stored as latent row lat_len[b], and
+ *   lat_len[b] grows by one. Requires n_new <= W.
+ * Requires lat_len[b] + (number of new latent rows) <= t_cap (clamped otherwise: rows past
+ * t_cap are dropped and lengths stop at t_cap).
+ * z_debug: NULL, or [B][n_new][rank_k + rank_v] float32 receiving, for each latent row this
+ *   call writes (the i-th such row of sequence b at index i), its z before storage rounding.
+ * Writes latent rows, window slots and the two length arrays, nothing else.
+ */
+int lowrank_kv_append(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                      int32_t batch, int32_t n_new, const void* k_new, const void* v_new,
+                      float* z_debug, void* stream);
+
+/*
+ * Bulk store of given latent rows (e.g. a prompt compressed elsewhere): rows
+ * [row0, row0 + n_rows) of every sequence receive zk_rows [B][n_rows][rank_k] and zv_rows
+ * [B][n_rows][rank_v] (float32), converted to the cache dtype exactly as append stores z.
+ * Lengths are not touched. Requires 0 <= row0 and row0 + n_rows <= t_cap.
+ */
+int lowrank_kv_store(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                     int32_t batch, int64_t row0, int64_t n_rows, const float* zk_rows,
+                     const float* zv_rows, void* stream);
+
+/*
+ * Dequantise (or widen) stored latent rows [0, n_rows) of every sequence to float32:
+ * zk_out [B][n_rows][rank_k], zv_out [B][n_rows][rank_v], with the element value decode uses
+ * before it rounds to its bfloat16 matrix-core operand. Requires n_rows <= t_cap.
+ */
+int lowrank_kv_dequant(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                       int32_t batch, int64_t n_rows, float* zk_out, float* zv_out, void* stream);
+
+/* Message for the last non-OK status returned on this host thread ("" if none). */
+const char* lowrank_last_error(void);
+
+/* LOWRANK_ABI_VERSION of the library. */
+int lowrank_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWRANK_ATTN_H */

@@ -1,0 +1,306 @@
+// C ABI: argument validation, launch planning and the exported entry points.
+// Every host-checkable precondition is checked before any launch; no exception crosses the ABI.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <exception>
+#include <string>
+
+#include "internal.h"
+#include "lowrank_attn.h"
+
+namespace lr {
+
+static thread_local std::string g_last_error;
+
+static int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_model(const lr_model_desc* m, int layer, int* rk, int* rv, const char** msg) {
+  if (!m) return *msg = "model descriptor is NULL", LR_EINVAL;
+  if (m->n_layers < 1) return *msg = "n_layers must be >= 1", LR_EINVAL;
+  if (layer < 0 || layer >= m->n_layers) return *msg = "layer out of range", LR_EINVAL;
+  if (!m->rank_k || !m->rank_v) return *msg = "rank tables must not be NULL", LR_EINVAL;
+  if (m->n_q_heads < 1 || m->n_kv_heads < 1) return *msg = "head counts must be >= 1", LR_EINVAL;
+  if (m->n_q_heads % m->n_kv_heads != 0) return *msg = "n_q_heads must be a multiple of n_kv_heads", LR_EINVAL;
+  if (m->n_q_heads > kHeadsPad) return *msg = "more than 32 query heads is not supported", LR_EUNSUPPORTED;
+  if (m->head_dim != 128) return *msg = "head_dim must be 128", LR_EUNSUPPORTED;
+  if (m->latent_dtype != LR_F32 && m->latent_dtype != LR_BF16 && m->latent_dtype != LR_I4G32)
+    return *msg = "unknown latent dtype", LR_EINVAL;
+  if (!(isfinite(m->sm_scale))) return *msg = "sm_scale must be finite", LR_EINVAL;
+  if (m->window < 0 || m->window > 65536) return *msg = "window must be in 0..65536", LR_EINVAL;
+  *rk = m->rank_k[layer];
+  *rv = m->rank_v[layer];
+  if (*rk < 1 || *rk > 512 || *rv < 1 || *rv > 512) return *msg = "ranks must be in 1..512", LR_EINVAL;
+  return LR_OK;
+}
+
+static int row_bytes(int latent, int r, int ld) {
+  if (latent == LR_I4G32) return (r + 31) / 32 * 16;
+  return ld * (latent == LR_F32 ? 4 : 2);
+}
+
+// Workspace layout (independent of the cache strides).
+static void layout_workspace(DecodePlan* p) {
+  size_t off = 0;
+  p->off_qt = off;
+  off = align256(off + (size_t)p->B * kHeadsPad * p->rk_pad * 2);
+  p->off_ml = off;
+  off = align256(off + (size_t)p->B * p->nsplit * p->Hq * 2 * 4);
+  p->off_acc = off;
+  off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * 4);
+  p->off_win = off;
+  if (p->window > 0) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);
+  p->ws_bytes = off > 0 ? off : 256;
+}
+
+int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const lr_decode_opts* o,
+                DecodePlan* p, const char** msg) {
+  int rk = 0, rv = 0;
+  int st = check_model(m, layer, &rk, &rv, msg);
+  if (st != LR_OK) return st;
+  if (batch < 0) return *msg = "batch must be >= 0", LR_EINVAL;
+  if (max_len < 0) return *msg = "max_lat_len must be >= 0", LR_EINVAL;
+  if (o) {
+    bool bad = o->reserved0 != 0;
+    for (int i = 0; i < 4; ++i) bad = bad || o->reserved[i] != 0;
+    if (bad) return *msg = "lr_decode_opts reserved fields must be zero", LR_EINVAL;
+    if (o->nsplit < 0) return *msg = "nsplit must be >= 0", LR_EINVAL;
+  }
+  if (m->latent_dtype == LR_I4G32) return *msg = "int4 latents are not supported by decode yet", LR_EUNSUPPORTED;
+  memset(p, 0, sizeof(*p));
+  p->B = batch;
+  p->Hq = m->n_q_heads;
+  p->Hkv = m->n_kv_heads;
+  p->d = m->head_dim;
+  p->D = m->n_kv_heads * m->head_dim;
+  p->rk = rk;
+  p->rv = rv;
+  p->rk_pad = round_up(rk, 32);
+  p->rv_pad16 = round_up(rv, 16);
+  p->nks = p->rk_pad / 32;
+  p->nrb = p->rv_pad16 / 16;
+  p->latent = m->latent_dtype;
+  p->sm_scale = m->sm_scale;
+  p->window = m->window;
+  p->max_len = max_len;
+
+  // token ranges: about one workgroup per compute unit over the batch unless overridden
+  const int max_split = max_len > 0 ? (max_len + kTileTokens - 1) / kTileTokens : 1;
+  int target = (o && o->nsplit > 0) ? o->nsplit : (device_cu_count() + (batch > 0 ? batch : 1) - 1) / (batch > 0 ? batch : 1);
+  if (target < 1) target = 1;
+  if (target > max_split) target = max_split;
+  if (max_len == 0) {
+    p->split_tokens = kTileTokens;
+    p->nsplit = 1;
+  } else {
+    p->split_tokens = round_up((max_len + target - 1) / target, kTileTokens);
+    p->nsplit = (max_len + p->split_tokens - 1) / p->split_tokens;
+  }
+
+  layout_workspace(p);
+  return LR_OK;
+}
+
+// LDS ring for the cache's row strides.
+static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
+  p->row_bytes_k = row_bytes(p->latent, p->rk, ld_k);
+  p->row_bytes_v = row_bytes(p->latent, p->rv, ld_v);
+  p->stage_bytes = kTileTokens * (p->row_bytes_k + p->row_bytes_v);
+  p->zv_off = kTileTokens * p->row_bytes_k;
+  const int avail = kLdsBytes - kExchangeBytes - kLdsPad;
+  int nst = avail / p->stage_bytes;
+  if (nst > 4) nst = 4;
+  if (nst < 2) return *msg = "latent rows too wide for the LDS ring (reduce ld or rank)", LR_EUNSUPPORTED;
+  p->nst = nst;
+  int lds = nst * p->stage_bytes + kLdsPad + kExchangeBytes;
+  if (p->window > 0) {
+    const int wlds = p->Hq * p->d * 4 + 2 * 32 * p->D * 2 + p->Hq * 32 * 4 + p->Hq * 3 * 4;
+    if (wlds > lds) lds = wlds;
+  }
+  if (lds > kLdsBytes) return *msg = "window staging exceeds LDS", LR_EUNSUPPORTED;
+  p->lds_bytes = lds;
+  return LR_OK;
+}
+
+static int check_cache_common(const lr_model_desc* m, const lr_layer_cache* c, int rk, int rv,
+                              const char** msg) {
+  if (!c) return *msg = "cache is NULL", LR_EINVAL;
+  if (!c->zk || !c->zv) return *msg = "latent buffers zk/zv must not be NULL", LR_EINVAL;
+  if (!c->lat_len) return *msg = "lat_len must not be NULL", LR_EINVAL;
+  if (c->t_cap < 1 || c->t_cap > (int64_t)1 << 30) return *msg = "t_cap must be in 1..2^30", LR_EINVAL;
+  if (!aligned(c->zk, 16) || !aligned(c->zv, 16)) return *msg = "latent buffers must be 16-byte aligned", LR_EINVAL;
+  if (m->latent_dtype == LR_I4G32) {
+    if (!c->zk_qp || !c->zv_qp) return *msg = "int4 caches need zk_qp/zv_qp", LR_EINVAL;
+    if (!aligned(c->zk_qp, 4) || !aligned(c->zv_qp, 4)) return *msg = "scale/zero buffers must be 4-byte aligned", LR_EINVAL;
+  } else {
+    if (c->ld_k < rk || c->ld_v < rv) return *msg = "ld must be >= rank", LR_EINVAL;
+    if (c->ld_k % 8 != 0 || c->ld_v % 8 != 0) return *msg = "ld must be a multiple of 8", LR_EINVAL;
+    if (c->ld_k > 4096 || c->ld_v > 4096) return *msg = "ld must be <= 4096", LR_EINVAL;
+  }
+  if (m->window > 0) {
+    if (!c->kwin || !c->vwin || !c->win_len) return *msg = "window buffers and win_len are required when window > 0", LR_EINVAL;
+    if (!aligned(c->kwin, 16) || !aligned(c->vwin, 16)) return *msg = "window rings must be 16-byte aligned", LR_EINVAL;
+  }
+  return LR_OK;
+}
+
+}  // namespace lr
+
+using namespace lr;
+
+#define LR_GUARD_BEGIN try {
+#define LR_GUARD_END                                              \
+  }                                                               \
+  catch (const std::exception& ex) {                              \
+    return fail(LR_EINVAL, ex.what());                            \
+  }                                                               \
+  catch (...) {                                                   \
+    return fail(LR_EINVAL, "unexpected internal error");          \
+  }
+
+extern "C" {
+
+size_t lowrank_attn_decode_workspace_size(const lr_model_desc* model, int32_t layer, int32_t batch,
+                                          int32_t max_lat_len, const lr_decode_opts* opts) {
+  try {
+    DecodePlan p;
+    const char* msg = "";
+    if (plan_decode(model, layer, batch, max_lat_len, opts, &p, &msg) != LR_OK) return 0;
+    return p.ws_bytes;
+  } catch (...) {
+    return 0;
+  }
+}
+
+int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                        int32_t batch, int32_t max_lat_len, const void* q, void* out, int32_t out_dtype,
+                        void* workspace, size_t workspace_bytes, const lr_decode_opts* opts, void* stream) {
+  LR_GUARD_BEGIN
+  DecodePlan p;
+  const char* msg = "";
+  int st = plan_decode(model, layer, batch, max_lat_len, opts, &p, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  st = check_cache_common(model, cache, p.rk, p.rv, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if ((int64_t)max_lat_len > cache->t_cap) return fail(LR_EINVAL, "max_lat_len must be <= t_cap");
+  if (!q || !out) return fail(LR_EINVAL, "q and out must not be NULL");
+  if (!cache->bk || !cache->bv) return fail(LR_EINVAL, "bases bk/bv must not be NULL");
+  if (!aligned(cache->bk, 16) || !aligned(cache->bv, 16) || !aligned(q, 16))
+    return fail(LR_EINVAL, "q and the bases must be 16-byte aligned");
+  if (out_dtype != LR_F32 && out_dtype != LR_BF16) return fail(LR_EINVAL, "out_dtype must be LR_F32 or LR_BF16");
+  st = plan_lds(&p, cache->ld_k, cache->ld_v, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (!workspace) return fail(LR_EINVAL, "workspace must not be NULL");
+  if (!aligned(workspace, 256)) return fail(LR_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.ws_bytes) return fail(LR_EWORKSPACE, "workspace too small");
+  if (batch == 0) return LR_OK;
+  p.t_cap = cache->t_cap;
+  hipError_t e = launch_decode(p, cache, q, out, out_dtype, workspace, (hipStream_t)stream,
+                               opts ? (hipEvent_t)opts->event_begin : nullptr,
+                               opts ? (hipEvent_t)opts->event_end : nullptr);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+static int plan_append(const lr_model_desc* model, int layer, const lr_layer_cache* cache, int batch,
+                       AppendPlan* p, const char** msg) {
+  int rk = 0, rv = 0;
+  int st = check_model(model, layer, &rk, &rv, msg);
+  if (st != LR_OK) return st;
+  st = check_cache_common(model, cache, rk, rv, msg);
+  if (st != LR_OK) return st;
+  if (batch < 0) return *msg = "batch must be >= 0", LR_EINVAL;
+  p->B = batch;
+  p->D = model->n_kv_heads * model->head_dim;
+  p->rk = rk;
+  p->rv = rv;
+  p->latent = model->latent_dtype;
+  p->window = model->window;
+  p->t_cap = cache->t_cap;
+  p->ld_k = cache->ld_k;
+  p->ld_v = cache->ld_v;
+  p->n_new = 0;
+  return LR_OK;
+}
+
+int lowrank_kv_append(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache, int32_t batch,
+                      int32_t n_new, const void* k_new, const void* v_new, float* z_debug, void* stream) {
+  LR_GUARD_BEGIN
+  AppendPlan p;
+  const char* msg = "";
+  int st = plan_append(model, layer, cache, batch, &p, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (n_new < 0) return fail(LR_EINVAL, "n_new must be >= 0");
+  if (model->window > 0 && n_new > model->window) return fail(LR_EINVAL, "n_new must be <= window");
+  if (n_new > 0 && (!k_new || !v_new)) return fail(LR_EINVAL, "k_new/v_new must not be NULL");
+  if (!cache->pk || !cache->pv) return fail(LR_EINVAL, "append needs the down-projections pk/pv");
+  if ((k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)))
+    return fail(LR_EINVAL, "k_new/v_new must be 16-byte aligned");
+  if (batch == 0 || n_new == 0) return LR_OK;
+  p.n_new = n_new;
+  hipError_t e = launch_append(p, cache, k_new, v_new, z_debug, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+int lowrank_kv_store(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache, int32_t batch,
+                     int64_t row0, int64_t n_rows, const float* zk_rows, const float* zv_rows, void* stream) {
+  LR_GUARD_BEGIN
+  AppendPlan p;
+  const char* msg = "";
+  int st = plan_append(model, layer, cache, batch, &p, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (row0 < 0 || n_rows < 0 || row0 + n_rows > cache->t_cap) return fail(LR_EINVAL, "rows out of range");
+  if (n_rows > 0 && batch > 0 && (!zk_rows || !zv_rows)) return fail(LR_EINVAL, "zk_rows/zv_rows must not be NULL");
+  if (batch == 0 || n_rows == 0) return LR_OK;
+  if (n_rows > (int64_t)4 * 65535 * 16384) return fail(LR_EINVAL, "too many rows for one call");
+  hipError_t e = launch_store(p, cache, row0, n_rows, zk_rows, zv_rows, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+int lowrank_kv_dequant(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache, int32_t batch,
+                       int64_t n_rows, float* zk_out, float* zv_out, void* stream) {
+  LR_GUARD_BEGIN
+  AppendPlan p;
+  const char* msg = "";
+  int st = plan_append(model, layer, cache, batch, &p, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (n_rows < 0 || n_rows > cache->t_cap) return fail(LR_EINVAL, "n_rows must be in 0..t_cap");
+  if (n_rows > 0 && batch > 0 && (!zk_out || !zv_out)) return fail(LR_EINVAL, "outputs must not be NULL");
+  if (batch == 0 || n_rows == 0) return LR_OK;
+  hipError_t e = launch_dequant(p, cache, n_rows, zk_out, zv_out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+const char* lowrank_last_error(void) { return g_last_error.c_str(); }
+
+int lowrank_abi_version(void) { return LOWRANK_ABI_VERSION; }
+
+}  // extern "C"

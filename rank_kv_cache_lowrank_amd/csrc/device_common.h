@@ -1,0 +1,85 @@
+// Device helpers shared by the decode and append kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lr {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kGroup = 32;        // int4 quantisation group along the rank
+constexpr int kGroupBytes = 16;   // packed bytes per group
+
+#define LR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// ---- s_waitcnt helpers (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14)
+#define LR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+#define LR_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14))
+
+// Wait until at most n vector-memory instructions of this wave are outstanding (n in 0..63).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define LR_C4(b) case b: LR_WAIT_VM(b); break; case b + 1: LR_WAIT_VM(b + 1); break; \
+                 case b + 2: LR_WAIT_VM(b + 2); break; case b + 3: LR_WAIT_VM(b + 3); break;
+  switch (n) {
+    LR_C4(0) LR_C4(4) LR_C4(8) LR_C4(12) LR_C4(16) LR_C4(20) LR_C4(24) LR_C4(28)
+    LR_C4(32) LR_C4(36) LR_C4(40) LR_C4(44) LR_C4(48) LR_C4(52) LR_C4(56) LR_C4(60)
+    default: LR_WAIT_VM(0); break;
+  }
+#undef LR_C4
+}
+
+// Workgroup barrier that orders LDS traffic only: this wave's LDS writes complete, then all
+// waves meet. (No global-memory fence: outstanding direct-to-LDS loads are waited for with
+// wait_vmcnt by the code that owns them.)
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  LR_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes lds_base + 16*l.
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, LR_LDS(lds_wave_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }  // RNE
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_lg(float v) {   // across the 4 lane groups (xor 16, 32)
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_lg(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---- int4 groups of 32: element value = fma(code, scale, zero) in float32 (one rounding).
+__device__ __forceinline__ float dequant_one(unsigned code, float scale, float zero) {
+  return __builtin_fmaf((float)code, scale, zero);
+}
+
+__device__ __forceinline__ float half_lo(unsigned w) {
+  _Float16 h = __builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+  return (float)h;
+}
+__device__ __forceinline__ float half_hi(unsigned w) {
+  _Float16 h = __builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+  return (float)h;
+}
+
+}  // namespace lr

@@ -1,0 +1,77 @@
+"""Shared test plumbing: device copies of synthetic inputs, oracle arguments, error metric."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+import rank_kv_cache_lowrank_amd as lr
+from synth.device import device_layer  # noqa: F401
+from oracle import attention as OA
+from oracle import quant as OQ
+
+TOL = {"f32": 5e-3, "bf16": 5e-3, "i4g32": 1e-2}
+
+
+def rel_err(gpu, ref) -> float:
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    if den == 0.0:
+        return float(np.max(np.abs(gpu))) if gpu.size else 0.0
+    return float(np.max(np.abs(gpu - ref)) / den)
+
+
+def oracle_latents(li: synth.LayerInputs, which: str, batches) -> list:
+    """Stored latent values as the oracle sees them, per requested sequence (float64)."""
+    z = li.zk if which == "k" else li.zv
+    r = li.rank_k if which == "k" else li.rank_v
+    out = []
+    for b in batches:
+        L = int(li.lat_len[b])
+        rows = z[b, :L, :r].float().numpy()
+        if li.cfg.latent == "i4g32":
+            codes, s, zz = OQ.quantize_rows(rows)
+            rows = OQ.dequant_rows(codes, s, zz, r)
+        out.append(rows.astype(np.float64))
+    return out
+
+
+def oracle_decode(li: synth.LayerInputs, batches=None, fn=OA.decode_latent) -> np.ndarray:
+    cfg = li.cfg
+    batches = list(range(cfg.batch)) if batches is None else list(batches)
+    zk = oracle_latents(li, "k", batches)
+    zv = oracle_latents(li, "v", batches)
+    idx = {b: i for i, b in enumerate(batches)}
+    # the oracle indexes sequences by b: give it views keyed through a small adapter
+    q = li.q.float().numpy()
+    kw = li.kwin.float().numpy() if li.kwin is not None else None
+    vw = li.vwin.float().numpy() if li.vwin is not None else None
+
+    class ByB:
+        def __init__(self, rows):
+            self.rows = rows
+
+        def __getitem__(self, b):
+            return self.rows[idx[b]]
+
+    return fn(q, ByB(zk), ByB(zv), li.bk.float().numpy(), li.bv.float().numpy(), li.lat_len,
+              li.rank_k, li.rank_v, cfg.n_kv_heads, cfg.sm_scale, kwin=kw, vwin=vw,
+              win_len=li.win_len, window=cfg.window, batches=batches)
+
+
+def run_decode(model, cache, q, max_lat_len, nsplit=0, out_dtype=torch.float32, guard=True):
+    """Runs lowrank_attn_decode; checks guard bands around the output; returns out (CPU)."""
+    B, Hq, d = q.shape
+    n = B * Hq * d
+    pad = 1024
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=out_dtype, device=q.device)
+    out = buf[pad:pad + n].view(B, Hq, d)
+    ws = lr.workspace(model, 0, B, max_lat_len, nsplit)
+    lr.lowrank_attn_decode(model, 0, cache, q, out, max_lat_len, ws, nsplit=nsplit)
+    torch.cuda.synchronize()
+    if guard:
+        head = buf[:pad].float()
+        tail = buf[pad + n:].float()
+        assert torch.isnan(head).all() and torch.isnan(tail).all(), "decode wrote outside out"
+    return out.float().cpu()

@@ -1,0 +1,139 @@
+"""GPU parity of lowrank_attn_decode against the fp64 oracle (max|gpu-ref|/max|ref| gates:
+5e-3 for fp32/bf16 latents, 1e-2 for int4)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import TOL, device_layer, oracle_decode, rel_err, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def check(li, batches=None, nsplit=0, max_lat_len=None, out_dtype=torch.float32, tol=None):
+    model, cache = device_layer(li)
+    q = li.q.cuda()
+    mx = int(li.lat_len.max()) if max_lat_len is None else max_lat_len
+    out = run_decode(model, cache, q, mx, nsplit=nsplit, out_dtype=out_dtype)
+    b_list = list(range(li.cfg.batch)) if batches is None else list(batches)
+    ref = oracle_decode(li, b_list)
+    err = rel_err(out[b_list].numpy(), ref)
+    t = TOL[li.cfg.latent] if tol is None else tol
+    print(f"cfg={li.cfg.name} B={li.cfg.batch} r=({li.rank_k},{li.rank_v}) nsplit={nsplit} err={err:.3e}",
+          flush=True)
+    assert err <= t, err
+    return out, ref
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 32.0])
+def test_config0_tiny_f32(q_scale):
+    check(synth.make_layer(synth.CONFIGS[0], q_scale=q_scale))
+
+
+def test_config0_needle():
+    check(synth.selection_needle(synth.CONFIGS[0]))
+
+
+def test_config1_full_size_sampled():
+    """B=16, T=4096, r=358 bf16 in the launch configuration the benchmark uses."""
+    li = synth.make_layer(synth.CONFIGS[1])
+    check(li, batches=[0, 7, 15])
+
+
+def test_config2_full_size_sampled():
+    """B=16, T=32768, r=256 bf16: long context, many token ranges."""
+    li = synth.make_layer(synth.CONFIGS[2])
+    check(li, batches=[0, 15])
+
+
+@pytest.mark.parametrize("q_scale", [32.0, 128.0])
+def test_config1_sharp_reduced(q_scale):
+    cfg = synth.CONFIGS[1].replace(batch=4, seq_len=1000)
+    check(synth.make_layer(cfg, q_scale=q_scale))
+
+
+def test_config2_needle_reduced():
+    cfg = synth.CONFIGS[2].replace(batch=3, seq_len=2000)
+    check(synth.selection_needle(cfg))
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 7, 16, 64])
+def test_split_invariance(nsplit):
+    cfg = synth.CONFIGS[1].replace(batch=3, seq_len=2100)
+    li = synth.make_layer(cfg, q_scale=32.0)
+    out, _ = check(li, nsplit=nsplit)
+    ref_out, _ = check(li, nsplit=3)
+    assert rel_err(out.numpy(), ref_out.numpy()) < 2e-3
+
+
+def test_ragged_lengths_and_empty_sequences():
+    cfg = synth.CONFIGS[1].replace(batch=8, seq_len=300)
+    lens = np.array([0, 1, 31, 32, 33, 200, 299, 300], np.int32)
+    li = synth.make_layer(cfg, q_scale=32.0, lat_len=lens, t_cap=300)
+    out, _ = check(li, batches=list(range(1, 8)))
+    assert torch.all(out[0] == 0)
+
+
+def test_lengths_below_max_and_ragged_tail():
+    cfg = synth.CONFIGS[2].replace(batch=5, seq_len=3000)
+    lens = np.array([3000, 2999, 1500, 77, 2048], np.int32)
+    li = synth.make_layer(cfg, q_scale=32.0, lat_len=lens, t_cap=3000)
+    check(li)
+
+
+@pytest.mark.parametrize("rank", [1, 16, 33, 100, 128, 255, 256, 300, 358, 384, 448, 500, 512])
+def test_rank_sweep(rank):
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=97, rank_k=rank, rank_v=rank)
+    check(synth.make_layer(cfg, q_scale=32.0))
+
+
+def test_unequal_ranks():
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=150, rank_k=136, rank_v=504)
+    check(synth.make_layer(cfg, q_scale=32.0))
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=150, rank_k=512, rank_v=128)
+    check(synth.make_layer(cfg, q_scale=32.0))
+
+
+def test_nan_in_pad_columns_is_ignored():
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=200)
+    li = synth.make_layer(cfg, q_scale=32.0, pad_fill=float("nan"), t_cap=256)
+    # rows past lat_len are NaN too (pad_fill covers them)
+    assert torch.isnan(li.zk.float()).any()
+    check(li)
+
+
+def test_nan_query_head_stays_confined():
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=200)
+    li = synth.make_layer(cfg, q_scale=32.0)
+    li.q[1, 5, 3] = float("nan")
+    model, cache = device_layer(li)
+    out = run_decode(model, cache, li.q.cuda(), 200)
+    assert torch.isnan(out[1, 5]).all()
+    mask = torch.ones(2, 28, dtype=torch.bool)
+    mask[1, 5] = False
+    assert not torch.isnan(out[mask]).any()
+
+
+def test_bf16_output():
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=500)
+    check(synth.make_layer(cfg, q_scale=32.0), out_dtype=torch.bfloat16, tol=8e-3)
+
+
+def test_deterministic():
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=700)
+    li = synth.make_layer(cfg, q_scale=32.0)
+    model, cache = device_layer(li)
+    q = li.q.cuda()
+    a = run_decode(model, cache, q, 700)
+    b = run_decode(model, cache, q, 700)
+    assert torch.equal(a, b)
+
+
+def test_max_len_zero_gives_zero():
+    cfg = synth.CONFIGS[1].replace(batch=2, seq_len=64)
+    li = synth.make_layer(cfg, lat_len=np.zeros(2, np.int32), t_cap=64)
+    model, cache = device_layer(li)
+    out = run_decode(model, cache, li.q.cuda(), 0)
+    assert torch.all(out == 0)
