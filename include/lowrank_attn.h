@@ -119,9 +119,10 @@ typedef struct {
 typedef struct {
   int32_t nsplit;          /* token ranges per sequence; 0 = automatic */
   int32_t reserved0;       /* must be 0 */
-  void* event_begin;       /* NULL, or a hipEvent_t recorded on `stream` just before the latent
-                              decode kernel (the one that streams the cache) */
-  void* event_end;         /* NULL, or a hipEvent_t recorded on `stream` just after it */
+  void* event_begin;       /* NULL, or a hipEvent_t stamped when the latent decode kernel (the
+                              one that streams the cache) starts; it is attached to that
+                              kernel's dispatch, so the pair times exactly its execution */
+  void* event_end;         /* NULL, or a hipEvent_t stamped when that kernel ends */
   int32_t reserved[4];     /* must be 0 */
 } lr_decode_opts;
 

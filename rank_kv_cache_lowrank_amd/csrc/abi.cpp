@@ -122,23 +122,32 @@ int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const
   return LR_OK;
 }
 
-// LDS ring for the cache's row strides.
+// LDS ring for the cache's row strides (the geometry itself is fixed by the kernel's bounds).
 static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   p->row_bytes_k = row_bytes(p->latent, p->rk, ld_k);
   p->row_bytes_v = row_bytes(p->latent, p->rv, ld_v);
-  p->stage_bytes = kTileTokens * (p->row_bytes_k + p->row_bytes_v);
-  p->zv_off = kTileTokens * p->row_bytes_k;
-  const int avail = kLdsBytes - kExchangeBytes - kLdsPad;
-  int nst = avail / p->stage_bytes;
-  if (nst > 4) nst = 4;
-  if (nst < 2) return *msg = "latent rows too wide for the LDS ring (reduce ld or rank)", LR_EUNSUPPORTED;
-  p->nst = nst;
-  int lds = nst * p->stage_bytes + kLdsPad + kExchangeBytes;
+  const int es = p->latent == LR_F32 ? 4 : 2;
+  const int KS = decode_ks(p->nks), RB = decode_rb(p->nrb);
+  if (p->latent == LR_F32 && (KS > 8 || RB > 8))
+    return *msg = "float32 latents support ranks up to 256", LR_EUNSUPPORTED;
+  const int sk = lds_stride_k(KS, es), sv = lds_stride_v(RB, es);
+  // copy the 16-byte granules that hold the rank's elements; the rest of the LDS row is zero
+  p->copy_k = (p->rk * es + 15) / 16 * 16;
+  p->copy_v = (p->rv * es + 15) / 16 * 16;
+  if (p->copy_k > sk - 16 || p->copy_v > sv - 32) return *msg = "rank exceeds the kernel bounds", LR_EINVAL;
+  p->stage_bytes = lds_stage(KS, RB, es);
+  p->zv_off = kTileTokens * sk;
+  p->nst = lds_nst(KS, RB, es);
+  const int G = decode_groups(KS, RB);
+  if (p->nst < 2 * G) return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
+  int lds = p->nst * p->stage_bytes + kLdsPad;
+  const int merge = G > 1 ? (2048 + 4 * RB * 1024) * (G - 1) : 0;
+  if (merge > lds) lds = merge;
   if (p->window > 0) {
     const int wlds = p->Hq * p->d * 4 + 2 * 32 * p->D * 2 + p->Hq * 32 * 4 + p->Hq * 3 * 4;
     if (wlds > lds) lds = wlds;
   }
-  if (lds > kLdsBytes) return *msg = "window staging exceeds LDS", LR_EUNSUPPORTED;
+  if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;
   p->lds_bytes = lds;
   return LR_OK;
 }

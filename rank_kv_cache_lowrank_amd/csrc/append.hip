@@ -93,15 +93,18 @@ struct AppendArgs {
 
 // Projection + storage of every latent row this call creates.
 // grid (column chunks of 64 over max(rk, rv), 2 = {K, V}, B); 256 threads = 4 waves.
-// Wave w handles rows w, w+4, ... of the rows to write; lane = column in the chunk.
+// For each row: wave w accumulates z over input dims [w*D/4, (w+1)*D/4) for the chunk's 64
+// columns (lane = column; the loads of P are independent and coalesced), the 4 partial sums
+// are added in a fixed order through LDS and wave 0 stores the row.
 template <typename PT>
 __global__ __launch_bounds__(256) void lr_append_project(AppendArgs a) {
-  extern __shared__ float xs[];    // [4 waves][D] source row staged as float
+  extern __shared__ float xs[];    // [D] source row as float, then [4][64] partial sums
   const int kv = blockIdx.y, b = blockIdx.z;
   const int r = kv == 0 ? a.rk : a.rv;
   const int col0 = blockIdx.x * 64;
   if (col0 >= r) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   int L = a.lat_len[b];
   L = L < 0 ? 0 : (L > a.t_cap ? (int)a.t_cap : L);
   int wl = 0, n_rows;
@@ -121,25 +124,35 @@ __global__ __launch_bounds__(256) void lr_append_project(AppendArgs a) {
   const int ld = kv == 0 ? a.ld_k : a.ld_v;
   const int rb = row_bytes_of(a.latent, r, ld);
   const int G = (r + kGroup - 1) / kGroup;
-  float* x = xs + wave * a.D;
   const int col = col0 + lane;
+  const int dq = a.D / 4;
+  float* x = xs;
+  float* zpart = xs + a.D;
 
-  for (int e0 = 0; e0 < n_rows; e0 += 4) {
-    const int e = e0 + wave;
-    const bool live = e < n_rows;
-    const __bf16* src = nullptr;
-    if (live) {
-      if (a.window > 0) src = win + ((size_t)b * a.window + (L + e) % a.window) * a.D;
-      else src = xnew + ((size_t)b * a.n_new + e) * a.D;
-      for (int c = lane; c < a.D; c += 64) x[c] = (float)src[c];
-    }
+  for (int e = 0; e < n_rows; ++e) {
+    const __bf16* src = (a.window > 0) ? win + ((size_t)b * a.window + (L + e) % a.window) * a.D
+                                       : xnew + ((size_t)b * a.n_new + e) * a.D;
     __syncthreads();
-    if (live) {
-      float z = 0.f;
-      if (col < r) {
-        const PT* pc = P + col;
-        for (int c = 0; c < a.D; ++c) z += x[c] * to_f32(pc[(size_t)c * r]);
+    for (int c = tid; c < a.D; c += 256) x[c] = (float)src[c];
+    __syncthreads();
+    float z = 0.f;
+    if (col < r) {
+      const PT* pc = P + (size_t)(wave * dq) * r + col;
+      const float* xw = x + wave * dq;
+      int c = 0;
+      for (; c + 16 <= dq; c += 16) {
+        float pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) pv[u] = to_f32(pc[(size_t)(c + u) * r]);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) z += xw[c + u] * pv[u];
       }
+      for (; c < dq; ++c) z += xw[c] * to_f32(pc[(size_t)c * r]);
+    }
+    zpart[wave * 64 + lane] = z;
+    __syncthreads();
+    if (wave == 0) {
+      z = ((zpart[lane] + zpart[64 + lane]) + zpart[128 + lane]) + zpart[192 + lane];
       const long long row = (long long)L + e;
       if (a.z_debug && col < r)
         a.z_debug[((size_t)b * a.n_new + e) * (a.rk + a.rv) + (kv == 0 ? 0 : a.rk) + col] = z;
@@ -147,7 +160,6 @@ __global__ __launch_bounds__(256) void lr_append_project(AppendArgs a) {
         store_chunk(a.latent, z, lane, col0, r, zbase + ((size_t)b * a.t_cap + row) * rb,
                     qbase ? qbase + ((size_t)b * a.t_cap + row) * G : nullptr);
     }
-    __syncthreads();
   }
 }
 
@@ -288,7 +300,7 @@ hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const voi
   a.B = p.B;
   const int rmax = p.rk > p.rv ? p.rk : p.rv;
   dim3 grid((rmax + 63) / 64, 2, p.B);
-  const size_t lds = (size_t)4 * p.D * sizeof(float);
+  const size_t lds = (size_t)(p.D + 256) * sizeof(float);
   if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append_project<float>, grid, dim3(256), lds, st, a);
   else hipLaunchKernelGGL(lr_append_project<__bf16>, grid, dim3(256), lds, st, a);
   hipError_t e = hipGetLastError();

@@ -18,6 +18,8 @@
 //               Extra workgroups (first in the grid) attend over the exact window, if any.
 //   lr_combine  one workgroup per (sequence, head): merges the ranges and the window partial
 //               and up-projects through Bv[:, g(j)].
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -49,6 +51,7 @@ struct DecodeArgs {
   float wscale;
   int n_win_blocks;
   int stage_bytes, zv_off, qpk_off, qpv_off, nst;
+  int copy_k, copy_v;       // bytes of each stored row the LDS ring holds
 };
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
@@ -67,6 +70,7 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 // ---------------------------------------------------------------------------------------------
 template <int LT>
 __device__ __forceinline__ bf16x8 k_operand(const unsigned char* row, int k0) {
+  // row already points at this lane's 8-element slice of K step 0; k0 = 32 * K step
   if constexpr (LT == LT_F32) {
     const f32x4 x0 = *(const f32x4*)(row + k0 * 4);
     const f32x4 x1 = *(const f32x4*)(row + k0 * 4 + 16);
@@ -79,28 +83,37 @@ __device__ __forceinline__ bf16x8 k_operand(const unsigned char* row, int k0) {
   }
 }
 
-__device__ __forceinline__ int slot_token(int lg, int e) {
-  return e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4);
-}
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
-template <int LT>
-__device__ __forceinline__ bf16x8 v_operand(const unsigned char* sv, int row_bytes, int rv, int lg) {
+// Value operand of the 16x16x16 bf16 product: lane (lg, li) holds latent index rv of tokens
+// 4*lg .. 4*lg+3 (K index = token), the rows the score tile's C layout gives this lane.
+template <int LT, int SV>
+__device__ __forceinline__ bf16x4 v_operand4(const unsigned char* base, int col_bytes) {
+  // base = stage value region + 4*lg rows + 2*li (bf16) / 4*li (f32); col_bytes = 32*rb (bf16)
   if constexpr (LT == LT_F32) {
-    bf16x8 r;
+    bf16x4 r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      r[e] = (__bf16)(*(const float*)(sv + slot_token(lg, e) * row_bytes + rv * 4));
+    for (int e = 0; e < 4; ++e) r[e] = (__bf16)(*(const float*)(base + e * SV + col_bytes));
     return r;
   } else {
-    unsigned short h[8];
+    unsigned short h[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      h[e] = *(const unsigned short*)(sv + slot_token(lg, e) * row_bytes + rv * 2);
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (unsigned)h[2 * i] | ((unsigned)h[2 * i + 1] << 16);
-    return __builtin_bit_cast(bf16x8, w);
+    for (int e = 0; e < 4; ++e) h[e] = *(const unsigned short*)(base + e * SV + col_bytes);
+    u32x2 w;
+    w[0] = (unsigned)h[0] | ((unsigned)h[1] << 16);
+    w[1] = (unsigned)h[2] | ((unsigned)h[3] << 16);
+    return __builtin_bit_cast(bf16x4, w);
   }
+}
+
+// Value operand through the gfx950 transpose read: within each 16-lane group g, lane j's element
+// e comes from the address given by lane 16g + 4e + j/4, at element offset j%4. Lane
+// 16g + 4e + q therefore points at row 4g+e, column 4q of the 16-column block, and every lane j
+// receives column j of rows 4g .. 4g+3: the A operand of the 16x16x16 product with K = token.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+__device__ __forceinline__ bf16x4 v_operand_tr(const unsigned char* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) s16x4*)(p)));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -108,7 +121,7 @@ __device__ __forceinline__ bf16x8 v_operand(const unsigned char* sv, int row_byt
 // sequence (iS-KV abstract: the recent window is kept exact). Writes (Aw[d], m, l) per head,
 // in base-2 softmax units like the latent partials.
 // ---------------------------------------------------------------------------------------------
-template <int LT>
+template <int LT, int NTHR>
 __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -125,15 +138,15 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
   float* sc = (float*)(vc + 32 * D);                     // [Hq][32]
   float* st = sc + Hq * 32;                              // [Hq][3]: m, l, alpha
 
-  for (int i = tid; i < Hq * d; i += kDecodeThreads) {
+  for (int i = tid; i < Hq * d; i += NTHR) {
     float qv;
     if constexpr (LT == LT_F32) qv = ((const float*)a.q)[(size_t)b * Hq * d + i];
     else qv = (float)((const __bf16*)a.q)[(size_t)b * Hq * d + i];
     qs[i] = qv * a.wscale;
   }
-  for (int j = tid; j < Hq; j += kDecodeThreads) { st[j * 3] = -INFINITY; st[j * 3 + 1] = 0.f; }
+  for (int j = tid; j < Hq; j += NTHR) { st[j * 3] = -INFINITY; st[j * 3 + 1] = 0.f; }
 
-  constexpr int kMaxAcc = 16;                            // Hq*d <= 32*128 = 16 * 256
+  constexpr int kMaxAcc = (kHeadsPad * 128 + NTHR - 1) / NTHR;  // Hq*d <= 32*128
   float acc[kMaxAcc];
 #pragma unroll
   for (int u = 0; u < kMaxAcc; ++u) acc[u] = 0.f;
@@ -144,7 +157,7 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
     __syncthreads();
     // stage n window rows (16 bytes per thread per step)
     const int vec_per_row = D / 8;
-    for (int i = tid; i < n * vec_per_row; i += kDecodeThreads) {
+    for (int i = tid; i < n * vec_per_row; i += NTHR) {
       const int u = i / vec_per_row, c = i - u * vec_per_row;
       const int slot = (L + c0 + u) % W;
       const size_t src = ((size_t)b * W + slot) * D + c * 8;
@@ -152,7 +165,7 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
       *(u32x4*)(vc + u * D + c * 8) = *(const u32x4*)(a.vwin + src);
     }
     __syncthreads();
-    for (int i = tid; i < Hq * 32; i += kDecodeThreads) {
+    for (int i = tid; i < Hq * 32; i += NTHR) {
       const int j = i >> 5, u = i & 31;
       float s = -INFINITY;
       if (u < n) {
@@ -166,7 +179,7 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
       sc[i] = s;
     }
     __syncthreads();
-    for (int j = tid; j < Hq; j += kDecodeThreads) {
+    for (int j = tid; j < Hq; j += NTHR) {
       float mx = -INFINITY;
       for (int u = 0; u < n; ++u) mx = fmaxf(mx, sc[j * 32 + u]);
       const float mold = st[j * 3];
@@ -185,7 +198,7 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kMaxAcc; ++u) {
-      const int o = tid + u * kDecodeThreads;
+      const int o = tid + u * NTHR;
       if (o < nout) {
         const int j = o / d, c = o - j * d;
         const int g = j / grp;
@@ -199,216 +212,318 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
   float* wp = a.win_part + (size_t)b * Hq * (d + 2);
 #pragma unroll
   for (int u = 0; u < kMaxAcc; ++u) {
-    const int o = tid + u * kDecodeThreads;
+    const int o = tid + u * NTHR;
     if (o < nout) {
       const int j = o / d, c = o - j * d;
       wp[j * (d + 2) + c] = acc[u];
     }
   }
-  for (int j = tid; j < Hq; j += kDecodeThreads) {
+  for (int j = tid; j < Hq; j += NTHR) {
     wp[j * (d + 2) + d] = st[j * 3];
     wp[j * (d + 2) + d + 1] = st[j * 3 + 1];
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Latent workgroup: one (sequence b, token range s).
-// KS: compile-time bound on K steps of 32 (rank_k); RB: bound on value blocks per wave.
+// Latent workgroup: one (sequence b, token range s), 8 waves in two ping-pong groups.
+//
+// The token range is cut into 16-token tiles that stream through an LDS ring (stage = the 16 Zk
+// rows then the 16 Zv rows, each row padded so that the 16 rows a score operand reads fall in
+// distinct banks). Group 0 (waves 0-3) computes the even tiles, group 1 the odd ones; inside a
+// group wave (hb, half) owns query-head block hb (heads 16*hb .. 16*hb+15) and value blocks
+// half, half+2, ... (16 latent indices each). Per tile a wave computes
+//   S^T[16 tokens, 16 heads] = Zk qt^T            (16x16x32 bf16, K = rank)
+//   online softmax of its 4 scores per lane       (base 2; only cross-lane max)
+//   A^T[16 rv, 16 heads] += Zv^T P^T               (16x16x16 bf16, K = the 16 tokens)
+// so no data crosses waves inside a tile and the workgroup meets at one barrier per tile pair.
+// At the end the two groups' (m, l, A) are merged through LDS and written once.
+// KS: compile-time bound on K steps of 32; RB: bound on value blocks per wave.
 // ---------------------------------------------------------------------------------------------
-template <int KS, int RB, int LT>
+constexpr int kProducers = 4;           // waves that only move data (direct-to-LDS loads)
+constexpr int kMaxChunkPerProducer = 5; // 1 KB DMA chunks per producer per matrix and tile
+constexpr float kRescaleSlack = 8.f;    // base-2 headroom before the running reference max moves
+
+// Threads of the decode workgroup for G consumer groups.
+constexpr int decode_threads(int G) { return 64 * (4 * G + kProducers); }
+
+template <int KS, int RB, int LT, int G>
 __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char* smem, int wg) {
+  constexpr int NTHR = decode_threads(G);
+  constexpr int ES = LT == LT_F32 ? 4 : 2;             // bytes per stored latent element
+  constexpr int SK = lds_stride_k(KS, ES);             // LDS row strides (bytes)
+  constexpr int SV = lds_stride_v(RB, ES);
+  constexpr int ZV = kTileTokens * SK;                 // value rows' offset inside a stage
+  constexpr int STAGE = lds_stage(KS, RB, ES);
+  constexpr int NST = lds_nst(KS, RB, ES);
+  constexpr int GPR = NST / G;                         // tile groups the ring holds
+  static_assert(NST % G == 0 && GPR >= 2, "LDS ring must hold two tile groups");
+  static_assert((kTileTokens * SK + 1023) / 1024 <= kProducers * kMaxChunkPerProducer &&
+                (kTileTokens * SV + 1023) / 1024 <= kProducers * kMaxChunkPerProducer, "DMA chunks");
+
   const int b = wg / a.nsplit;
   const int s = wg - b * a.nsplit;
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const bool producer = wave >= 4 * G;
 
   int L = a.lat_len[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int t_begin = s * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, L);
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTileTokens - 1) / kTileTokens : 0;
+  const int niter = (ntiles + G - 1) / G;
 
   unsigned char* ring = smem;
-  float* sx = (float*)(smem + a.nst * a.stage_bytes + kLdsPad);
+  // Zero the ring once: LDS columns past the copied part of a row (K steps and value blocks
+  // beyond the rank, row padding) then read as exact zeros for the whole workgroup.
+  for (int i = tid; i < NST * STAGE / 16; i += NTHR) *(u32x4*)(ring + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  barrier_lds();
 
-  const unsigned char* gk = a.zk + ((size_t)b * a.t_cap + t_begin) * a.row_bytes_k;
-  const unsigned char* gv = a.zv + ((size_t)b * a.t_cap + t_begin) * a.row_bytes_v;
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Per-wave count of direct-to-LDS instructions for a tile of `rows` rows.
-  auto wave_chunks = [&](int bytes) {
-    const int nch = (bytes + 1023) >> 10;
-    return nch > wave ? (nch - wave + 3) >> 2 : 0;
-  };
-  const int rows_last = ntiles > 0 ? t_end - (t_begin + (ntiles - 1) * kTileTokens) : 0;
-  const int cpw_full = wave_chunks(kTileTokens * a.row_bytes_k) + wave_chunks(kTileTokens * a.row_bytes_v);
-  const int cpw_last = wave_chunks(rows_last * a.row_bytes_k) + wave_chunks(rows_last * a.row_bytes_v);
-
-  auto issue = [&](int t) {
-    unsigned char* stg = ring + (t % a.nst) * a.stage_bytes;
-    const int t0 = t * kTileTokens;
-    const int rows = min(kTileTokens, t_end - t_begin - t0);
-    const int bk = rows * a.row_bytes_k;
-    const unsigned char* srck = gk + (size_t)t0 * a.row_bytes_k;
-    for (int c = wave; c * 1024 < bk; c += 4) {
-      const int off = c * 1024 + lane * 16;
-      if (off < bk) dma16(srck + off, stg + c * 1024);
+  if (producer) {
+    // ---------------- producer waves: keep the ring full ----------------
+    const int pw = wave - 4 * G;
+    const unsigned char* gk = a.zk + ((size_t)b * a.t_cap + t_begin) * a.row_bytes_k;
+    const unsigned char* gv = a.zv + ((size_t)b * a.t_cap + t_begin) * a.row_bytes_v;
+    // Source offset, inside a tile's stored rows, of the 16 bytes this lane lands at LDS
+    // position c*1024 + 16*lane of a stage region (c = pw + kProducers*u); -1 = not copied.
+    int offk[kMaxChunkPerProducer], offv[kMaxChunkPerProducer];
+#pragma unroll
+    for (int u = 0; u < kMaxChunkPerProducer; ++u) {
+      const int o = (pw + kProducers * u) * 1024 + lane * 16;
+      int row = o / SK, col = o - row * SK;
+      offk[u] = (col < a.copy_k) ? row * a.row_bytes_k + col : -1;
+      row = o / SV;
+      col = o - row * SV;
+      offv[u] = (col < a.copy_v) ? row * a.row_bytes_v + col : -1;
     }
-    const int bv = rows * a.row_bytes_v;
-    const unsigned char* srcv = gv + (size_t)t0 * a.row_bytes_v;
-    unsigned char* stv = stg + a.zv_off;
-    for (int c = wave; c * 1024 < bv; c += 4) {
-      const int off = c * 1024 + lane * 16;
-      if (off < bv) dma16(srcv + off, stv + c * 1024);
+    // chunks holding at least one needed byte of a tile with `rows` rows
+    auto nchunks = [](int rows, int stride, int cp) { return ((rows - 1) * stride + cp + 1023) >> 10; };
+    auto pcnt = [&](int nch) { return nch > pw ? (nch - pw + kProducers - 1) / kProducers : 0; };
+    auto tile_cnt = [&](int rows) {
+      return pcnt(nchunks(rows, SK, a.copy_k)) + pcnt(nchunks(rows, SV, a.copy_v));
+    };
+    const int rows_last = ntiles > 0 ? t_end - (t_begin + (ntiles - 1) * kTileTokens) : 0;
+    const int cnt_full = tile_cnt(kTileTokens);
+    const int cnt_last = ntiles > 0 ? tile_cnt(rows_last) : 0;
+    // loads issued for tiles (lo, hi] (hi <= ntiles - 1)
+    auto count = [&](int lo, int hi) {
+      if (hi <= lo) return 0;
+      return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
+    };
+    auto issue = [&](int t) {
+      unsigned char* stg = ring + (t % NST) * STAGE;
+      const int t0 = t * kTileTokens;
+      const int rows = min(kTileTokens, t_end - t_begin - t0);
+      const unsigned char* srck = gk + (size_t)t0 * a.row_bytes_k;
+      const unsigned char* srcv = gv + (size_t)t0 * a.row_bytes_v;
+      const int nck = nchunks(rows, SK, a.copy_k);
+      const int ncv = nchunks(rows, SV, a.copy_v);
+      const int limk = rows * a.row_bytes_k, limv = rows * a.row_bytes_v;
+#pragma unroll
+      for (int u = 0; u < kMaxChunkPerProducer; ++u) {
+        const int c = pw + kProducers * u;
+        if (c < nck && offk[u] >= 0 && offk[u] < limk) dma16(srck + offk[u], stg + c * 1024);
+      }
+#pragma unroll
+      for (int u = 0; u < kMaxChunkPerProducer; ++u) {
+        const int c = pw + kProducers * u;
+        if (c < ncv && offv[u] >= 0 && offv[u] < limv) dma16(srcv + offv[u], stg + ZV + c * 1024);
+      }
+    };
+    const int pro = min(NST - G, ntiles);
+    for (int t = 0; t < pro; ++t) issue(t);
+    wait_vmcnt(count(G - 1, pro - 1));                 // tile group 0 landed
+    for (int it = 0; it < niter; ++it) {
+      barrier_lds();                                   // group `it` visible; group it-1's stages free
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (G * it + NST - G + j < ntiles) issue(G * it + NST - G + j);
+      const int hi = min(G * it + NST - 1, ntiles - 1);
+      wait_vmcnt(count(G * it + 2 * G - 1, hi));       // group it+1 landed
     }
-  };
-
-  // Prologue: the first nst-1 tiles, then the folded query of this wave's head block.
-  const int pro = min(a.nst - 1, ntiles);
-  for (int t = 0; t < pro; ++t) issue(t);
-
-  const int tb1 = wave & 1, hb1 = wave >> 1;   // this wave's score block (token half, head half)
-  bf16x8 qop[KS];
-  {
-    const __bf16* qrow = a.qt + ((size_t)b * kHeadsPad + hb1 * 16 + li) * a.rk_pad + lg * 8;
+  } else {
+    // ---------------- consumer waves: scores, online softmax, values ----------------
+    const int grp = wave >> 2;
+    const int hb = wave & 1;
+    const int half = (wave >> 1) & 1;
+    bf16x8 qop[KS];
+    {
+      const __bf16* qrow = a.qt + ((size_t)b * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[ks] = (ks < a.nks) ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
-  }
-  LR_WAIT_VM(0);
-
-  float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  f32x4 acc[2][RB];
+      for (int ks = 0; ks < KS; ++ks)
+        qop[ks] = (ks < a.nks) ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
+    }
+    LR_WAIT_VM(0);
+    // AND-mask for the last K step: latent indices >= rk read as 0 (the copied granule may
+    // hold pad columns, and they may hold anything, including NaN patterns).
+    u32x4 tailmask;
+    {
+      const int k0 = (a.nks - 1) * 32 + lg * 8;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int j = 0; j < RB; ++j) acc[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i)
+        tailmask[i] = (k0 + 2 * i < a.rk ? 0x0000FFFFu : 0u) | (k0 + 2 * i + 1 < a.rk ? 0xFFFF0000u : 0u);
+    }
+    const bool ktail = (a.rk & 7) != 0;
+    // value block j of this wave covers latent indices 16*(half+2j) .. +15 (blocks past the
+    // rank read the zero-filled tail of the rows and are never stored)
+    const int krow_off = li * SK + lg * 8 * ES;
+    const int vrow_off = (LT == LT_F32) ? ZV + 4 * lg * SV + li * ES + half * 16 * ES
+                                        : ZV + (4 * lg + (li >> 2)) * SV + (li & 3) * 8 + half * 32;
 
-  for (int i = 0; i < ntiles; ++i) {
-    const int hi = min(i + a.nst - 2, ntiles - 1);
-    int younger = 0;
-    if (hi > i) younger = (hi - i) * cpw_full + (hi == ntiles - 1 ? cpw_last - cpw_full : 0);
-    wait_vmcnt(younger);
-    barrier_lds();
-    if (i + a.nst - 1 < ntiles) issue(i + a.nst - 1);
+    for (int it = 0; it < niter; ++it) {
+      barrier_lds();
+      const int t = G * it + grp;
+      if (t < ntiles) {
+        const unsigned char* stg = ring + (t % NST) * STAGE;
+        const int nvalid = min(kTileTokens, t_end - t_begin - t * kTileTokens);
 
-    const unsigned char* stg = ring + (i % a.nst) * a.stage_bytes;
-    const int nvalid = min(kTileTokens, t_end - (t_begin + i * kTileTokens));
-
-    // ---- scores: this wave's 16 tokens x 16 heads block over the whole rank
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* krow = stg + (tb1 * 16 + li) * a.row_bytes_k;
+        // ---- scores of this wave's head block: S^T[token 4*lg+i][head li]
+        const unsigned char* krow = stg + krow_off;
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks < a.nks) {
-        const int k0 = ks * 32 + lg * 8;
-        bf16x8 av = k_operand<LT>(krow, k0);
-        if (k0 + 8 > a.rk) {
+        for (int ks0 = 0; ks0 < KS; ks0 += 4) {      // 4 K steps of reads in flight, then 4 products
+          bf16x8 av[4];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (k0 + e >= a.rk) av[e] = (__bf16)0.f;
+          for (int u = 0; u < 4; ++u)
+            if (ks0 + u < KS) av[u] = k_operand<LT>(krow, (ks0 + u) * 32);
+          if (ktail) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (ks0 + u < KS && ks0 + u == a.nks - 1)
+                av[u] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, av[u]) & tailmask);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (ks0 + u < KS) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], qop[ks0 + u], sacc, 0, 0, 0);
         }
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qop[ks], sacc, 0, 0, 0);
-      }
-    }
-    *(f32x4*)(sx + ((tb1 * 2 + hb1) * 64 + lane) * 4) = sacc;
-    barrier_lds();
 
-    // ---- online softmax (base 2; the fold carries log2 e) for both head blocks
-    bf16x8 pb[2];
+        // ---- value operands, all LDS reads issued before the softmax
+        const unsigned char* vbase = stg + vrow_off;
+        bf16x4 vop[RB];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const f32x4 s0 = *(const f32x4*)(sx + ((0 * 2 + hb) * 64 + lane) * 4);
-      const f32x4 s1 = *(const f32x4*)(sx + ((1 * 2 + hb) * 64 + lane) * 4);
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { v[e] = s0[e]; v[4 + e] = s1[e]; }
-      // A NaN score becomes +inf so that it survives the max and poisons exactly this head's
-      // sums (fmaxf would drop it and the head would read as empty).
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (v[e] != v[e]) ? INFINITY : v[e];
-      if (nvalid < kTileTokens) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (slot_token(lg, e) >= nvalid) v[e] = -INFINITY;
-      }
-      float mx = v[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, v[e]);
-      mx = wave_max_lg(mx);
-      const float mnew = fmaxf(m[hb], mx);
-      const bool live = mnew != -INFINITY;
-      const float alpha = live ? fast_exp2(m[hb] - mnew) : 1.f;
-      m[hb] = mnew;
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 p = (__bf16)(live ? fast_exp2(v[e] - mnew) : 0.f);
-        pb[hb][e] = p;
-        ps += (float)p;
-      }
-      lsum[hb] = lsum[hb] * alpha + ps;
-#pragma unroll
-      for (int j = 0; j < RB; ++j) acc[hb][j] *= alpha;
-    }
+        for (int j = 0; j < RB; ++j) {
+          if constexpr (LT == LT_F32) vop[j] = v_operand4<LT, SV>(vbase, j * 32 * ES);
+          else vop[j] = v_operand_tr(vbase + j * 64);
+        }
 
-    // ---- values: this wave's 16-wide latent blocks, both head blocks
-    const unsigned char* sv = stg + a.zv_off;
+        // ---- online softmax over the tile's 16 tokens (4 per lane, 4 lane groups)
+        float v[4];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int rb = wave + 4 * j;
-      if (rb < a.nrb) {
-        bf16x8 av = v_operand<LT>(sv, a.row_bytes_v, rb * 16 + li, lg);
+        for (int i = 0; i < 4; ++i) {
+          v[i] = sacc[i];
+          v[i] = (v[i] != v[i]) ? INFINITY : v[i];   // NaN survives the max, poisons only this head
+        }
         if (nvalid < kTileTokens) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (slot_token(lg, e) >= nvalid) av[e] = (__bf16)0.f;
+          for (int i = 0; i < 4; ++i)
+            if (4 * lg + i >= nvalid) v[i] = -INFINITY;
+          u32x2 tm;
+          tm[0] = (4 * lg < nvalid ? 0x0000FFFFu : 0u) | (4 * lg + 1 < nvalid ? 0xFFFF0000u : 0u);
+          tm[1] = (4 * lg + 2 < nvalid ? 0x0000FFFFu : 0u) | (4 * lg + 3 < nvalid ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int j = 0; j < RB; ++j) vop[j] = __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, vop[j]) & tm);
         }
-        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[0], acc[0][j], 0, 0, 0);
-        acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[1], acc[1][j], 0, 0, 0);
+        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        mx = wave_max_lg(mx);
+        // m is a reference max: scores are exponentiated against it and it only moves when a
+        // tile's max exceeds it by more than kRescaleSlack, so most tiles skip the rescale.
+        const bool move = mx > m + kRescaleSlack;     // false when the tile is empty (mx = -inf)
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float mnew = move ? mx : m;
+          const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+          m = mnew;
+          lsum *= alpha;
+#pragma unroll
+          for (int j = 0; j < RB; ++j) acc[j] *= alpha;
+        }
+        const bool live = m != -INFINITY;
+        bf16x4 pb;
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 p = (__bf16)(live ? fast_exp2(v[i] - m) : 0.f);
+          pb[i] = p;
+          ps += (float)p;
+        }
+        lsum += ps;
+
+        // ---- values: A^T[rv][head li] over this wave's value blocks
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[j], pb, acc[j], 0, 0, 0);
       }
     }
+    lsum = wave_sum_lg(lsum);
   }
 
-  // ---- partials of this range
+  // ---- merge the consumer groups, write this range's partial
+  barrier_lds();                                   // the ring is no longer read
+  float* mbuf = (float*)smem;                      // [G-1][4 roles][64]
+  float* lbuf = mbuf + 4 * 64 * (G > 1 ? G - 1 : 1);
+  f32x4* abuf = (f32x4*)(smem + 2048 * (G > 1 ? G - 1 : 1));   // [G-1][4 roles][RB][64]
+  const int role = wave & 3;
+  const int grp = wave >> 2;
+  if (!producer && grp > 0) {
+    const int slot = (grp - 1) * 4 + role;
+    mbuf[slot * 64 + lane] = m;
+    lbuf[slot * 64 + lane] = lsum;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) lsum[hb] = wave_sum_lg(lsum[hb]);
-  const size_t pidx = (size_t)b * a.nsplit + s;
-  if (wave == 0 && lg == 0) {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int head = hb * 16 + li;
-      if (head < a.Hq) {
-        a.part_ml[(pidx * a.Hq + head) * 2] = m[hb];
-        a.part_ml[(pidx * a.Hq + head) * 2 + 1] = lsum[hb];
-      }
-    }
+    for (int j = 0; j < RB; ++j) abuf[(slot * RB + j) * 64 + lane] = acc[j];
   }
+  barrier_lds();
+  if (!producer && grp == 0) {
+    const int hb = wave & 1;
+    const int half = (wave >> 1) & 1;
+    float ms = m;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+    for (int g2 = 1; g2 < G; ++g2) ms = fmaxf(ms, mbuf[((g2 - 1) * 4 + role) * 64 + lane]);
+    const float wa = (m == -INFINITY) ? 0.f : fast_exp2(m - ms);
+    float lt = lsum * wa;
+#pragma unroll
+    for (int j = 0; j < RB; ++j) acc[j] *= wa;
+#pragma unroll
+    for (int g2 = 1; g2 < G; ++g2) {
+      const int slot = (g2 - 1) * 4 + role;
+      const float mo = mbuf[slot * 64 + lane];
+      const float wb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - ms);
+      lt += lbuf[slot * 64 + lane] * wb;
+#pragma unroll
+      for (int j = 0; j < RB; ++j) acc[j] += abuf[(slot * RB + j) * 64 + lane] * wb;
+    }
+    const size_t pidx = (size_t)b * a.nsplit + s;
     const int head = hb * 16 + li;
+    if (half == 0 && lg == 0 && head < a.Hq) {
+      a.part_ml[(pidx * a.Hq + head) * 2] = ms;
+      a.part_ml[(pidx * a.Hq + head) * 2 + 1] = lt;
+    }
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
-      const int rb = wave + 4 * j;
+      const int rb = half + 2 * j;
       if (rb < a.nrb && head < a.Hq)
-        *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + rb * 16 + 4 * lg) = acc[hb][j];
+        *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + rb * 16 + 4 * lg) = acc[j];
     }
   }
 }
 
-template <int KS, int RB, int LT>
-__global__ __launch_bounds__(kDecodeThreads) void lr_decode(DecodeArgs a) {
+template <int KS, int RB, int LT, int G>
+__global__ __launch_bounds__(decode_threads(G)) void lr_decode(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   if ((int)blockIdx.x < a.n_win_blocks) {
-    window_block<LT>(a, smem);
+    window_block<LT, decode_threads(G)>(a, smem);
     return;
   }
-  latent_block<KS, RB, LT>(a, smem, (int)blockIdx.x - a.n_win_blocks);
+  latent_block<KS, RB, LT, G>(a, smem, (int)blockIdx.x - a.n_win_blocks);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Fold: qt[b][j][k] = scale * sum_c q[b][j][c] * Bk[k][g(j)*d + c], bf16, zero-padded.
-// grid (rk_pad/64, B), 256 threads: thread (slot, k) handles KV heads slot, slot+4, ...
+// grid (rk_pad/64, Hkv, B), 256 threads: thread (hs, k) computes heads hs, hs+4, ... of KV head
+// g for latent index k; its 256-byte slice of Bk row k is loaded with independent 16-byte loads.
 // ---------------------------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* out);
@@ -426,46 +541,40 @@ __device__ __forceinline__ void load8<float>(const float* p, float* out) {
   for (int e = 0; e < 4; ++e) { out[e] = v0[e]; out[4 + e] = v1[e]; }
 }
 
+constexpr int kFoldD = 128;     // head_dim handled by the fold (validated on the host)
+
 template <typename T>
 __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T* __restrict__ bk,
-                                               __bf16* __restrict__ qt, int Hq, int Hkv, int d, int D,
+                                               __bf16* __restrict__ qt, int Hq, int Hkv, int D,
                                                int rk, int rk_pad, float scale) {
-  extern __shared__ float qs[];
-  const int b = blockIdx.y;
-  for (int i = threadIdx.x; i < Hq * d; i += 256) qs[i] = to_f32(q[(size_t)b * Hq * d + i]) * scale;
-  __syncthreads();
-  const int k = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int slot = threadIdx.x >> 6;
-  if (k >= rk_pad) return;
+  __shared__ float qs[kHeadsPad * kFoldD];
+  const int g = blockIdx.y, b = blockIdx.z;
   const int grp = Hq / Hkv;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < grp * kFoldD; i += 256)
+    qs[i] = to_f32(q[((size_t)b * Hq + g * grp) * kFoldD + i]) * scale;
+  __syncthreads();
+  const int k = blockIdx.x * 64 + (tid & 63);
+  const int hs = tid >> 6;
+  if (k >= rk_pad) return;
   __bf16* out = qt + (size_t)b * kHeadsPad * rk_pad + k;
-  for (int g = slot; g < Hkv; g += 4) {
-    for (int h0 = 0; h0 < grp; h0 += 8) {
-      float acc[8];
+  float bvals[kFoldD];
+  if (k < rk) {
+    const T* brow = bk + (size_t)k * D + g * kFoldD;
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh) acc[hh] = 0.f;
-      if (k < rk) {
-        const T* brow = bk + (size_t)k * D + g * d;
-        for (int c = 0; c < d; c += 8) {
-          float bv[8];
-          load8<T>(brow + c, bv);
-#pragma unroll
-          for (int hh = 0; hh < 8; ++hh) {
-            if (h0 + hh < grp) {
-              const float* qj = qs + (g * grp + h0 + hh) * d + c;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[hh] += qj[e] * bv[e];
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 8; ++hh)
-        if (h0 + hh < grp) out[(size_t)(g * grp + h0 + hh) * rk_pad] = (__bf16)acc[hh];
-    }
+    for (int c = 0; c < kFoldD; c += 8) load8<T>(brow + c, bvals + c);
   }
-  if (slot == 0)
-    for (int j = Hq; j < kHeadsPad; ++j) out[(size_t)j * rk_pad] = (__bf16)0.f;
+  for (int h = hs; h < grp; h += 4) {
+    float acc = 0.f;
+    if (k < rk) {
+      const float* qh = qs + h * kFoldD;
+#pragma unroll
+      for (int c = 0; c < kFoldD; ++c) acc += qh[c] * bvals[c];
+    }
+    out[(size_t)(g * grp + h) * rk_pad] = (__bf16)acc;
+  }
+  if (g == 0)
+    for (int j = Hq + hs; j < kHeadsPad; j += 4) out[(size_t)j * rk_pad] = (__bf16)0.f;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -495,15 +604,24 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return r;
 }
 
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float* out) { load8<T>(p, out); }
+
+// Layout: phase 1 (weights): threads over ranges. Phase 2 (merge): thread (sg, r4) sums ranges
+// s = sg, sg+4, ... over 4 consecutive latent indices with 16-byte loads. Phase 3 (up-project):
+// thread (rg, cg) accumulates 8 output columns over latent rows rg, rg+16, ... with 16-byte
+// loads of Bv; the 16 row groups are reduced through LDS.
 template <typename BT, typename OT>
 __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   extern __shared__ float cs[];
   const int tid = threadIdx.x;
   const int b = blockIdx.x / a.Hq, j = blockIdx.x - b * a.Hq;
   const int g = j / (a.Hq / a.Hkv);
-  float* ws = cs;                       // [nsplit]
-  float* ahat = ws + a.nsplit;          // [rv]
-  float* red = ahat + a.rv_pad16;       // [256]
+  const int pw = a.rv_pad16 > 512 ? a.rv_pad16 : 512;
+  float* part = cs;                       // [4][pw] merge partials, reused as [16][128]
+  float* ahat = part + 4 * pw;            // [rv_pad16]
+  float* ws = ahat + a.rv_pad16;          // [nsplit]
+  float* red = ws + a.nsplit;             // [8]
   const size_t base = (size_t)b * a.nsplit;
 
   float mloc = -INFINITY;
@@ -525,59 +643,124 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   const float lstar = block_reduce(lloc, red, false) + ww * lw;
   __syncthreads();
 
-  for (int r = tid; r < a.rv; r += 256) {
-    float acc = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float w = ws[s];
-      if (w != 0.f) acc += w * a.part_acc[((base + s) * a.Hq + j) * a.rv_pad16 + r];
+  // merge the ranges: Ahat[r] = sum_s w_s A_s[r]
+  {
+    const int sg = tid >> 6, r4 = (tid & 63) * 4;
+    for (int r0 = 0; r0 < a.rv_pad16; r0 += 256) {
+      const int r = r0 + r4;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (r < a.rv_pad16) {
+        int s = sg;
+        for (; s + 12 < a.nsplit; s += 16) {
+          f32x4 v[4];
+          float w[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            w[u] = ws[s + 4 * u];
+            v[u] = *(const f32x4*)(a.part_acc + ((base + s + 4 * u) * a.Hq + j) * a.rv_pad16 + r);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (w[u] != 0.f) acc += w[u] * v[u];
+        }
+        for (; s < a.nsplit; s += 4) {
+          const float w = ws[s];
+          if (w != 0.f) acc += w * *(const f32x4*)(a.part_acc + ((base + s) * a.Hq + j) * a.rv_pad16 + r);
+        }
+        *(f32x4*)(part + sg * pw + r) = acc;
+      }
     }
-    ahat[r] = acc;
   }
   __syncthreads();
-
-  const int c = tid & 127, half = tid >> 7;
-  const BT* bv = (const BT*)a.bv + g * a.d + c;
-  float o = 0.f;
-  for (int r = half; r < a.rv; r += 2) o += ahat[r] * to_f32(bv[(size_t)r * a.D]);
-  red[tid] = o;
+  for (int r = tid; r < a.rv_pad16; r += 256)
+    ahat[r] = r < a.rv ? part[r] + part[pw + r] + part[2 * pw + r] + part[3 * pw + r]
+                       : 0.f;
   __syncthreads();
-  if (half == 0) {
-    o = red[tid] + red[tid + 128];
-    if (ww != 0.f) o += ww * wp[c];
+
+  // up-project: o[c] = sum_r ahat[r] Bv[r][g*d + c]
+  {
+    const int cg = tid & 15, rg = tid >> 4;
+    const BT* bv = (const BT*)a.bv + g * a.d + cg * 8;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    int r = rg;
+    for (; r + 48 < a.rv; r += 64) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8f<BT>(bv + (size_t)(r + 16 * u) * a.D, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float h = ahat[r + 16 * u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += h * v[u][e];
+      }
+    }
+    for (; r < a.rv; r += 16) {
+      float v[8];
+      load8f<BT>(bv + (size_t)r * a.D, v);
+      const float h = ahat[r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += h * v[e];
+    }
+    float* ored = part;     // [16][128]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ored[rg * 128 + cg * 8 + e] = o[e];
+  }
+  __syncthreads();
+  if (tid < 128) {
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o += part[i * 128 + tid];
+    if (ww != 0.f) o += ww * wp[tid];
     o = (lstar == 0.f) ? 0.f : o / lstar;   // 0 only for a sequence with no tokens; NaN stays NaN
-    ((OT*)a.out)[((size_t)b * a.Hq + j) * a.d + c] = from_f32<OT>(o);
+    ((OT*)a.out)[((size_t)b * a.Hq + j) * a.d + tid] = from_f32<OT>(o);
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Host launch
 // ---------------------------------------------------------------------------------------------
-template <int KS, int RB, int LT>
-static hipError_t launch_decode_kernel(const DecodeArgs& args, int grid, int lds, hipStream_t st) {
+// ev_begin/ev_end (optional) are attached to the kernel's own dispatch, so they bracket exactly
+// its execution (no separate marker packets in the stream).
+template <int KS, int RB, int LT, int G>
+static hipError_t launch_decode_kernel(const DecodeArgs& args, int grid, int lds, hipStream_t st,
+                                       hipEvent_t ev_begin, hipEvent_t ev_end) {
   static bool attr_set[64] = {false};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    e = hipFuncSetAttribute((const void*)lr_decode<KS, RB, LT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void*)lr_decode<KS, RB, LT, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
-  hipLaunchKernelGGL((lr_decode<KS, RB, LT>), dim3(grid), dim3(kDecodeThreads), lds, st, args);
+  if (ev_begin || ev_end)
+    hipExtLaunchKernelGGL((lr_decode<KS, RB, LT, G>), dim3(grid), dim3(decode_threads(G)), lds, st, ev_begin, ev_end,
+                          0, args);
+  else
+    hipLaunchKernelGGL((lr_decode<KS, RB, LT, G>), dim3(grid), dim3(decode_threads(G)), lds, st, args);
   return hipGetLastError();
 }
 
 template <int LT>
-static hipError_t dispatch_decode(const DecodePlan& p, const DecodeArgs& args, int grid, hipStream_t st) {
-  const int ks = p.nks <= 8 ? 8 : (p.nks <= 12 ? 12 : 16);
-  const int rbw = (p.nrb + 3) / 4;
-  const int rb = rbw <= 4 ? 4 : (rbw <= 6 ? 6 : 8);
-#define LR_CASE(K, R) \
-  if (ks == K && rb == R) return launch_decode_kernel<K, R, LT>(args, grid, p.lds_bytes, st);
-  LR_CASE(8, 4) LR_CASE(8, 6) LR_CASE(8, 8)
-  LR_CASE(12, 4) LR_CASE(12, 6) LR_CASE(12, 8)
-  LR_CASE(16, 4) LR_CASE(16, 6) LR_CASE(16, 8)
+static hipError_t dispatch_decode(const DecodePlan& p, const DecodeArgs& args, int grid, hipStream_t st,
+                                  hipEvent_t ev_begin, hipEvent_t ev_end) {
+  const int ks = decode_ks(p.nks);
+  const int rb = decode_rb(p.nrb);
+  const int g = decode_groups(ks, rb);
+#define LR_CASE(K, R)                                                                    \
+  if (ks == K && rb == R) {                                                             \
+    if constexpr (decode_groups(K, R) == 2)                                               \
+      return launch_decode_kernel<K, R, LT, 2>(args, grid, p.lds_bytes, st, ev_begin, ev_end);              \
+    else                                                                                  \
+      return launch_decode_kernel<K, R, LT, 1>(args, grid, p.lds_bytes, st, ev_begin, ev_end);              \
+  }
+  (void)g;
+  LR_CASE(8, 8) LR_CASE(8, 12) LR_CASE(8, 16)
+  LR_CASE(12, 8) LR_CASE(12, 12) LR_CASE(12, 16)
+  LR_CASE(16, 8) LR_CASE(16, 12) LR_CASE(16, 16)
 #undef LR_CASE
   return hipErrorInvalidValue;
 }
@@ -590,14 +773,13 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
 
   // 1. fold
   {
-    dim3 grid((p.rk_pad + 63) / 64, p.B);
-    const size_t lds = (size_t)p.Hq * p.d * sizeof(float);
+    dim3 grid((p.rk_pad + 63) / 64, p.Hkv, p.B);
     if (p.latent == LR_F32)
-      hipLaunchKernelGGL(lr_fold<float>, grid, dim3(256), lds, st, (const float*)q, (const float*)c->bk, qt,
-                         p.Hq, p.Hkv, p.d, p.D, p.rk, p.rk_pad, scale);
+      hipLaunchKernelGGL(lr_fold<float>, grid, dim3(256), 0, st, (const float*)q, (const float*)c->bk, qt,
+                         p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
     else
-      hipLaunchKernelGGL(lr_fold<__bf16>, grid, dim3(256), lds, st, (const __bf16*)q, (const __bf16*)c->bk, qt,
-                         p.Hq, p.Hkv, p.d, p.D, p.rk, p.rk_pad, scale);
+      hipLaunchKernelGGL(lr_fold<__bf16>, grid, dim3(256), 0, st, (const __bf16*)q, (const __bf16*)c->bk, qt,
+                         p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -643,13 +825,13 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.qpk_off = p.qpk_off;
   a.qpv_off = p.qpv_off;
   a.nst = p.nst;
+  a.copy_k = p.copy_k;
+  a.copy_v = p.copy_v;
   const int grid = a.n_win_blocks + p.B * p.nsplit;
   hipError_t e;
-  if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-  if (p.latent == LR_F32) e = dispatch_decode<LT_F32>(p, a, grid, st);
-  else e = dispatch_decode<LT_BF16>(p, a, grid, st);
+  if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
+  else e = dispatch_decode<LT_BF16>(p, a, grid, st, ev_begin, ev_end);
   if (e != hipSuccess) return e;
-  if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
 
   // 3. combine + up-projection
   CombineArgs ca;
@@ -666,7 +848,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   ca.rv_pad16 = p.rv_pad16;
   ca.nsplit = p.nsplit;
   ca.window = p.window;
-  const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 256) * sizeof(float);
+  const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);
   const bool f32b = p.latent == LR_F32;
   const bool f32o = out_dtype == LR_F32;

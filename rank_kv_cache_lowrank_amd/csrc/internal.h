@@ -9,12 +9,36 @@
 
 namespace lr {
 
-constexpr int kTileTokens = 32;     // tokens per decode tile
-constexpr int kHeadsPad = 32;       // query heads padded for the 16x16x32 matrix-core tiles
-constexpr int kDecodeThreads = 256; // 4 waves
+constexpr int kTileTokens = 16;     // tokens per decode tile
+constexpr int kHeadsPad = 32;       // query heads padded for the 16x16 matrix-core tiles
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kExchangeBytes = 4 * 64 * 16;   // score exchange between the 4 waves
-constexpr int kLdsPad = 128;                  // slack after the ring for operand over-reads
+constexpr int kLdsPad = 128;        // slack after the ring for operand over-reads
+
+// Compile-time bounds the decode kernel is instantiated for: KS K steps of 32 latent indices
+// for the keys, RB value blocks of 16 per wave (two waves share the value blocks, so
+// 32*RB value indices).
+inline int decode_ks(int nks) { return nks <= 8 ? 8 : (nks <= 12 ? 12 : 16); }
+inline int decode_rb(int nrb) {
+  const int w = (nrb + 1) / 2;
+  return w <= 8 ? 8 : (w <= 12 ? 12 : 16);
+}
+// LDS ring geometry for given bounds and element size (bytes): each stage holds 16 key rows of
+// KS*32 elements then 16 value rows of RB*32 elements. Row padding keeps the operand reads free
+// of bank conflicts: key rows are read 16 B per lane down 16 rows (stride = 4 dwords mod 64),
+// value rows by the transpose read, 8 B per lane over 4 rows x 4 chunks (stride = 8 dwords
+// mod 16, so the 4 rows land on disjoint 8-bank groups).
+constexpr int lds_stride_k(int KS, int es) { return KS * 32 * es + 16; }
+constexpr int lds_stride_v(int RB, int es) { return RB * 32 * es + 32; }
+constexpr int lds_stage(int KS, int RB, int es) {
+  return kTileTokens * (lds_stride_k(KS, es) + lds_stride_v(RB, es));
+}
+// Consumer groups (4 waves each) of the decode workgroup: two when their registers allow three
+// waves per SIMD (10 waves with the 2 producer waves), else one.
+constexpr int decode_groups(int KS, int RB) { return (KS <= 8 && RB <= 12) ? 2 : 1; }
+constexpr int lds_nst(int KS, int RB, int es) {   // stages in the ring: even, at most 8
+  return ((kLdsBytes - kLdsPad) / lds_stage(KS, RB, es) > 8 ? 8
+                                                             : (kLdsBytes - kLdsPad) / lds_stage(KS, RB, es)) & ~1;
+}
 
 struct DecodePlan {
   int B, Hq, Hkv, d, D;
@@ -30,6 +54,7 @@ struct DecodePlan {
   int row_bytes_k, row_bytes_v;     // bytes of one stored latent row (codes for int4)
   int qp_bytes_k, qp_bytes_v;       // int4: bytes of one row's scale/zero words, else 0
   int stage_bytes, zv_off, qpk_off, qpv_off, nst;  // LDS ring layout
+  int copy_k, copy_v;               // bytes of each stored row the ring holds
   int lds_bytes;                    // dynamic LDS of the decode kernel
   size_t off_qt, off_ml, off_acc, off_win, ws_bytes;
 };

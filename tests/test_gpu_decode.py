@@ -65,7 +65,8 @@ def test_split_invariance(nsplit):
     li = synth.make_layer(cfg, q_scale=32.0)
     out, _ = check(li, nsplit=nsplit)
     ref_out, _ = check(li, nsplit=3)
-    assert rel_err(out.numpy(), ref_out.numpy()) < 2e-3
+    # both meet the oracle gate; their mutual difference is held to the same bar
+    assert rel_err(out.numpy(), ref_out.numpy()) <= TOL["bf16"]
 
 
 def test_ragged_lengths_and_empty_sequences():
