@@ -1,0 +1,176 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared entry point, and
+rejects invalid arguments before any launch (no GPU needed: these return before touching it)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import rank_kv_cache_lowrank_amd as lr
+from rank_kv_cache_lowrank_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lowrank_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lowrank_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lr.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version():
+    assert lr.lowrank_abi_version() == 1
+
+
+# The validation tests hand the library addresses that map nothing; every case is rejected before
+# a launch, but they are kept off machines with a visible GPU all the same.
+host_only = pytest.mark.skipif(torch.cuda.is_available(), reason="passes unmapped device addresses")
+
+
+def desc(**kw):
+    base = dict(n_layers=1, n_q_heads=28, n_kv_heads=4, head_dim=128, rank_k=[358], rank_v=[358],
+                sm_scale=128 ** -0.5, window=0, latent_dtype="bf16")
+    base.update(kw)
+    return lr.Model(**base)
+
+
+def ws_size(model, layer=0, batch=16, max_len=4096, nsplit=0):
+    return lr.lowrank_attn_decode_workspace_size(model, layer, batch, max_len, nsplit)
+
+
+def test_workspace_size_valid_and_invalid():
+    assert ws_size(desc()) > 0
+    assert ws_size(desc(), layer=1) == 0                       # layer out of range
+    assert ws_size(desc(n_q_heads=30)) == 0                     # 30 % 4 != 0
+    assert ws_size(desc(head_dim=64)) == 0                      # unsupported head_dim
+    assert ws_size(desc(rank_k=[0])) == 0
+    assert ws_size(desc(rank_v=[513])) == 0
+    assert ws_size(desc(), batch=-1) == 0
+    assert ws_size(desc(), max_len=-5) == 0
+    # more token ranges -> more partials
+    assert ws_size(desc(), nsplit=64) > ws_size(desc(), nsplit=2)
+
+
+def call_decode(model, cache_struct, **kw):
+    lib = lr.load()
+    args = dict(layer=0, batch=2, max_len=16, q=1 << 20, out=1 << 21, out_dtype=L.LR_F32, ws=1 << 22,
+                ws_bytes=1 << 30, opts=None, stream=None)
+    args.update(kw)
+    return lib.lowrank_attn_decode(ctypes.byref(model.desc), args["layer"],
+                                   ctypes.byref(cache_struct) if cache_struct is not None else None,
+                                   args["batch"], args["max_len"], args["q"], args["out"], args["out_dtype"],
+                                   args["ws"], args["ws_bytes"], args["opts"], args["stream"])
+
+
+def fake_cache(**kw):
+    c = L.lr_layer_cache()
+    c.zk, c.zv = 1 << 24, 1 << 25
+    c.bk, c.bv = 1 << 26, 1 << 27
+    c.lat_len = 1 << 28
+    c.ld_k = c.ld_v = 360
+    c.t_cap = 64
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@host_only
+@pytest.mark.parametrize("case,code", [
+    (dict(cache=None), L.LR_EINVAL),
+    (dict(cache_kw=dict(zk=None)), L.LR_EINVAL),
+    (dict(cache_kw=dict(ld_k=356)), L.LR_EINVAL),             # ld < rank
+    (dict(cache_kw=dict(ld_k=362)), L.LR_EINVAL),             # ld not a multiple of 8
+    (dict(cache_kw=dict(zk=(1 << 24) + 4)), L.LR_EINVAL),     # misaligned latents
+    (dict(max_len=65), L.LR_EINVAL),                          # max_lat_len > t_cap
+    (dict(q=None), L.LR_EINVAL),
+    (dict(out_dtype=7), L.LR_EINVAL),
+    (dict(ws=None), L.LR_EINVAL),
+    (dict(ws=(1 << 22) + 64), L.LR_EINVAL),                   # workspace not 256-aligned
+    (dict(ws_bytes=16), L.LR_EWORKSPACE),
+    (dict(layer=3), L.LR_EINVAL),
+])
+def test_decode_rejects_invalid_arguments(case, code):
+    model = desc()
+    cache = None if case.get("cache", 1) is None else fake_cache(**case.get("cache_kw", {}))
+    kw = {k: v for k, v in case.items() if k not in ("cache", "cache_kw")}
+    assert call_decode(model, cache, **kw) == code
+    assert lr.lowrank_last_error() != ""
+
+
+@host_only
+def test_window_requires_ring_buffers():
+    model = desc(window=128)
+    assert call_decode(model, fake_cache()) == L.LR_EINVAL
+    assert "window" in lr.lowrank_last_error()
+
+
+@host_only
+def test_unsupported_combinations():
+    assert call_decode(desc(n_q_heads=40, n_kv_heads=4), fake_cache()) == L.LR_EUNSUPPORTED
+    assert call_decode(desc(latent_dtype="f32", rank_k=[300], rank_v=[300]),
+                       fake_cache(ld_k=304, ld_v=304)) == L.LR_EUNSUPPORTED
+
+
+@host_only
+def test_opts_reserved_fields_must_be_zero():
+    o = L.lr_decode_opts()
+    o.reserved[2] = 5
+    assert call_decode(desc(), fake_cache(), opts=ctypes.byref(o)) == L.LR_EINVAL
+    o = L.lr_decode_opts()
+    o.nsplit = -1
+    assert call_decode(desc(), fake_cache(), opts=ctypes.byref(o)) == L.LR_EINVAL
+
+
+@host_only
+def test_append_store_dequant_validation():
+    lib = lr.load()
+    model = desc(window=8)
+    c = fake_cache(pk=1 << 29, pv=1 << 30)
+    # window set but no ring
+    assert lib.lowrank_kv_append(ctypes.byref(model.desc), 0, ctypes.byref(c), 2, 1, 1 << 20, 1 << 21,
+                                 None, None) == L.LR_EINVAL
+    model = desc()
+    # n_new negative
+    assert lib.lowrank_kv_append(ctypes.byref(model.desc), 0, ctypes.byref(c), 2, -1, 1 << 20, 1 << 21,
+                                 None, None) == L.LR_EINVAL
+    # missing projections
+    c2 = fake_cache()
+    assert lib.lowrank_kv_append(ctypes.byref(model.desc), 0, ctypes.byref(c2), 2, 1, 1 << 20, 1 << 21,
+                                 None, None) == L.LR_EINVAL
+    # store out of range
+    assert lib.lowrank_kv_store(ctypes.byref(model.desc), 0, ctypes.byref(c), 2, 60, 10, 1 << 20, 1 << 21,
+                                None) == L.LR_EINVAL
+    # dequant beyond t_cap
+    assert lib.lowrank_kv_dequant(ctypes.byref(model.desc), 0, ctypes.byref(c), 2, 65, 1 << 20, 1 << 21,
+                                  None) == L.LR_EINVAL
+    # int4 cache without scale/zero buffers
+    m4 = desc(latent_dtype="i4g32")
+    assert lib.lowrank_kv_store(ctypes.byref(m4.desc), 0, ctypes.byref(c), 2, 0, 1, 1 << 20, 1 << 21,
+                                None) == L.LR_EINVAL
+
+
+@host_only
+def test_zero_batch_is_a_no_op():
+    # valid arguments with batch 0 return OK without launching anything
+    assert call_decode(desc(), fake_cache(), batch=0) == L.LR_OK
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = L._lib
+    try:
+        L._lib = None
+        with pytest.raises(RuntimeError):
+            L.load(str(tmp_path / "missing.so"))
+    finally:
+        L._lib = saved
