@@ -227,11 +227,14 @@ class LayerInputs:
 
 
 def make_layer(cfg: Config, layer: int = 0, q_scale: float = 1.0, t_cap: Optional[int] = None,
-               pad_fill: float = 0.0, lat_len: Optional[np.ndarray] = None) -> LayerInputs:
+               pad_fill: float = 0.0, lat_len: Optional[np.ndarray] = None,
+               win_len: Optional[np.ndarray] = None) -> LayerInputs:
     rk, rv = layer_ranks(cfg, layer)
     ll, wl = split_lengths(cfg)
     if lat_len is not None:
         ll = np.asarray(lat_len, dtype=np.int32)
+    if win_len is not None:
+        wl = np.asarray(win_len, dtype=np.int32)
     if t_cap is None:
         t_cap = max(int(ll.max()) if len(ll) else 0, 1)
     ld_k, ld_v = latent_ld(rk), latent_ld(rv)

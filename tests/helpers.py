@@ -60,15 +60,15 @@ def oracle_decode(li: synth.LayerInputs, batches=None, fn=OA.decode_latent) -> n
               win_len=li.win_len, window=cfg.window, batches=batches)
 
 
-def run_decode(model, cache, q, max_lat_len, nsplit=0, out_dtype=torch.float32, guard=True):
+def run_decode(model, cache, q, max_lat_len, nsplit=0, out_dtype=torch.float32, guard=True, layer=0):
     """Runs lowrank_attn_decode; checks guard bands around the output; returns out (CPU)."""
     B, Hq, d = q.shape
     n = B * Hq * d
     pad = 1024
     buf = torch.full((n + 2 * pad,), float("nan"), dtype=out_dtype, device=q.device)
     out = buf[pad:pad + n].view(B, Hq, d)
-    ws = lr.workspace(model, 0, B, max_lat_len, nsplit)
-    lr.lowrank_attn_decode(model, 0, cache, q, out, max_lat_len, ws, nsplit=nsplit)
+    ws = lr.workspace(model, layer, B, max_lat_len, nsplit)
+    lr.lowrank_attn_decode(model, layer, cache, q, out, max_lat_len, ws, nsplit=nsplit)
     torch.cuda.synchronize()
     if guard:
         head = buf[:pad].float()

@@ -1,0 +1,83 @@
+"""GPU parity of the exact recent window and of per-layer rank dispatch (28-layer model with a
+global rank-allocation table), against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import rank_kv_cache_lowrank_amd as lr
+import synth
+from helpers import TOL, device_layer, oracle_decode, rel_err, run_decode
+
+pytestmark = pytest.mark.gpu
+CFG4 = synth.CONFIGS[4]
+
+
+def check(li, batches=None, model=None, layer=0, nsplit=0):
+    m1, cache = device_layer(li)
+    model = m1 if model is None else model
+    mx = int(li.lat_len.max())
+    out = run_decode(model, cache, li.q.cuda(), mx, nsplit=nsplit, layer=layer)
+    b_list = list(range(li.cfg.batch)) if batches is None else list(batches)
+    ref = oracle_decode(li, b_list)
+    err = rel_err(out[b_list].numpy(), ref)
+    print(f"layer={li.layer} r=({li.rank_k},{li.rank_v}) L={li.lat_len[b_list]} W={li.win_len[b_list]} "
+          f"err={err:.3e}", flush=True)
+    assert err <= TOL["bf16"], err
+    return out
+
+
+def model28(cfg):
+    ranks = [synth.layer_ranks(cfg, l) for l in range(cfg.n_layers)]
+    return lr.Model(cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, [r[0] for r in ranks],
+                    [r[1] for r in ranks], cfg.sm_scale, cfg.window, cfg.latent)
+
+
+@pytest.mark.parametrize("layer", [0, 13, 27])
+def test_config4_full_size_layers_sampled(layer):
+    """B=16, lengths U{2048..8192} (last 128 tokens exact), the layer's drawn ranks."""
+    li = synth.make_layer(CFG4, layer)
+    assert np.all(li.win_len == 128)
+    check(li, batches=[0, 6, 15], model=model28(CFG4), layer=layer)
+
+
+def test_all_28_layers_through_one_rank_table():
+    """Every layer of the 28-layer descriptor at a reduced length: the host derives each layer's
+    ranks, padding and kernel bounds from the table."""
+    cfg = CFG4.replace(batch=2)
+    model = model28(cfg)
+    for layer in range(cfg.n_layers):
+        li = synth.make_layer(cfg, layer, q_scale=16.0, lat_len=np.array([300, 77], np.int32),
+                              win_len=np.array([128, 40], np.int32))
+        check(li, model=model, layer=layer)
+
+
+def test_window_only_sequences():
+    cfg = CFG4.replace(batch=5)
+    li = synth.make_layer(cfg, 3, q_scale=16.0, lat_len=np.zeros(5, np.int32),
+                          win_len=np.array([1, 7, 64, 127, 128], np.int32), t_cap=16)
+    check(li)
+
+
+def test_partial_windows_wrapping_ring():
+    """Live window slots start at position L mod W and wrap around the ring."""
+    cfg = CFG4.replace(batch=6)
+    li = synth.make_layer(cfg, 5, q_scale=16.0, lat_len=np.array([130, 1, 255, 64, 500, 0], np.int32),
+                          win_len=np.array([50, 128, 3, 128, 0, 0], np.int32))
+    out = check(li, batches=[0, 1, 2, 3, 4])
+    assert torch.all(out[5] == 0)
+
+
+def test_sharp_scores_mixed_window_and_history():
+    """Large query scale: the softmax mass moves between window and latent history per head."""
+    cfg = CFG4.replace(batch=3)
+    li = synth.make_layer(cfg, 9, q_scale=96.0, lat_len=np.array([1000, 2000, 17], np.int32),
+                          win_len=np.array([128, 100, 128], np.int32))
+    check(li)
+
+
+@pytest.mark.parametrize("nsplit", [1, 5, 32])
+def test_window_with_split_counts(nsplit):
+    cfg = CFG4.replace(batch=2)
+    li = synth.make_layer(cfg, 20, q_scale=16.0, lat_len=np.array([1500, 999], np.int32),
+                          win_len=np.array([128, 128], np.int32))
+    check(li, nsplit=nsplit)
