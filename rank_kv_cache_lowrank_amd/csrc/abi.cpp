@@ -71,6 +71,8 @@ static void layout_workspace(DecodePlan* p) {
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * 4);
   p->off_win = off;
   if (p->window > 0) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);
+  p->off_qexp = off;
+  if (p->latent == LR_I4G32) off = align256(off + (size_t)p->B * kHeadsPad * 4);
   p->ws_bytes = off > 0 ? off : 256;
 }
 
@@ -87,7 +89,6 @@ int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const
     if (bad) return *msg = "lr_decode_opts reserved fields must be zero", LR_EINVAL;
     if (o->nsplit < 0) return *msg = "nsplit must be >= 0", LR_EINVAL;
   }
-  if (m->latent_dtype == LR_I4G32) return *msg = "int4 latents are not supported by decode yet", LR_EUNSUPPORTED;
   memset(p, 0, sizeof(*p));
   p->B = batch;
   p->Hq = m->n_q_heads;
@@ -109,6 +110,7 @@ int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const
   const int max_split = max_len > 0 ? (max_len + kTileTokens - 1) / kTileTokens : 1;
   int target = (o && o->nsplit > 0) ? o->nsplit : (device_cu_count() + (batch > 0 ? batch : 1) - 1) / (batch > 0 ? batch : 1);
   if (target < 1) target = 1;
+  if (target > kMaxSplit) target = kMaxSplit;
   if (target > max_split) target = max_split;
   if (max_len == 0) {
     p->split_tokens = kTileTokens;
@@ -128,6 +130,27 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   p->row_bytes_v = row_bytes(p->latent, p->rv, ld_v);
   const int es = p->latent == LR_F32 ? 4 : 2;
   const int KS = decode_ks(p->nks), RB = decode_rb(p->nrb);
+  int window_lds = 0;
+  if (p->window > 0)
+    window_lds = p->Hq * p->d * 4 + 2 * 32 * p->D * 2 + p->Hq * 32 * 4 + p->Hq * 3 * 4;
+  if (p->latent == LR_I4G32) {
+    const int gk = (p->rk + 31) / 32, gv = (p->rv + 31) / 32;
+    p->qp_bytes_k = gk * 4;
+    p->qp_bytes_v = gv * 4;
+    p->stage_bytes = lds_stage(KS, RB, 2);
+    p->zv_off = kTileTokens * lds_stride_k(KS, 2);
+    p->nst = kI4DeqStages;
+    p->raw_stage = i4_raw_stage(gk, gv);
+    int nr = (kLdsBytes - kLdsPad - kI4DeqStages * p->stage_bytes) / p->raw_stage;
+    if (nr > kI4MaxRawStages) nr = kI4MaxRawStages;
+    if (nr < 3) return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
+    p->nr = nr;
+    int lds = kI4DeqStages * p->stage_bytes + nr * p->raw_stage + kLdsPad;
+    if (window_lds > lds) lds = window_lds;
+    if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;
+    p->lds_bytes = lds;
+    return LR_OK;
+  }
   if (p->latent == LR_F32 && (KS > 8 || RB > 8))
     return *msg = "float32 latents support ranks up to 256", LR_EUNSUPPORTED;
   const int sk = lds_stride_k(KS, es), sv = lds_stride_v(RB, es);
@@ -143,10 +166,7 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   int lds = p->nst * p->stage_bytes + kLdsPad;
   const int merge = G > 1 ? (2048 + 4 * RB * 1024) * (G - 1) : 0;
   if (merge > lds) lds = merge;
-  if (p->window > 0) {
-    const int wlds = p->Hq * p->d * 4 + 2 * 32 * p->D * 2 + p->Hq * 32 * 4 + p->Hq * 3 * 4;
-    if (wlds > lds) lds = wlds;
-  }
+  if (window_lds > lds) lds = window_lds;
   if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;
   p->lds_bytes = lds;
   return LR_OK;
@@ -218,6 +238,8 @@ int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_laye
   if (!aligned(cache->bk, 16) || !aligned(cache->bv, 16) || !aligned(q, 16))
     return fail(LR_EINVAL, "q and the bases must be 16-byte aligned");
   if (out_dtype != LR_F32 && out_dtype != LR_BF16) return fail(LR_EINVAL, "out_dtype must be LR_F32 or LR_BF16");
+  if (p.latent == LR_I4G32 && (!aligned(cache->zk_qp, 16) || !aligned(cache->zv_qp, 16)))
+    return fail(LR_EINVAL, "int4 decode needs 16-byte aligned scale/zero buffers");
   st = plan_lds(&p, cache->ld_k, cache->ld_v, &msg);
   if (st != LR_OK) return fail(st, msg);
   if (!workspace) return fail(LR_EINVAL, "workspace must not be NULL");

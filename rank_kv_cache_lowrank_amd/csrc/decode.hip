@@ -18,6 +18,10 @@
 //               Extra workgroups (first in the grid) attend over the exact window, if any.
 //   lr_combine  one workgroup per (sequence, head): merges the ranges and the window partial
 //               and up-projects through Bv[:, g(j)].
+// int4 latents (groups of 32 with an fp16 scale and zero): the loads bring the codes and the
+// scale/zero words into a raw LDS ring, the producer waves dequantise each tile into an fp16
+// tile of the same geometry, and the matrix-core products run in fp16 (fp32 accumulate) against
+// an fp16 folded query that carries a per-head power-of-two scale.
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
@@ -52,6 +56,8 @@ struct DecodeArgs {
   int n_win_blocks;
   int stage_bytes, zv_off, qpk_off, qpv_off, nst;
   int copy_k, copy_v;       // bytes of each stored row the LDS ring holds
+  const float* qexp;        // int4: per (sequence, head) power of two the folded query was scaled by
+  int nr, raw_stage;        // int4: raw stages in the ring and their size in bytes
 };
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
@@ -105,6 +111,49 @@ __device__ __forceinline__ bf16x4 v_operand4(const unsigned char* base, int col_
     return __builtin_bit_cast(bf16x4, w);
   }
 }
+
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+
+// Matrix-core products on 16-bit operands held as raw bits: bf16 for float32/bf16 latents,
+// fp16 for the dequantised int4 tiles.
+template <int LT>
+__device__ __forceinline__ f32x4 mfma_k(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (LT == LT_I4)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+template <int LT>
+__device__ __forceinline__ f32x4 mfma_v(bf16x4 a, bf16x4 b, f32x4 c) {
+  if constexpr (LT == LT_I4)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c,
+                                                 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Eight int4 codes (w: index i in bits 4i..4i+3) -> eight fp16 values zhat = fma(code, scale,
+// zero), one rounding. Output dword i holds indices i and i + 4 (block order 0,4,1,5,2,6,3,7):
+// (w >> 4i) & 0x000F000F places those two codes in the two halves, and or-ing in 0x6400 makes
+// each half the fp16 number 1024 + code exactly, so one packed subtraction recovers the code.
+// kMask / kMagic arrive in registers (0x000F000F, 0x64006400) so that the and-or is one
+// three-operand instruction.
+__device__ __forceinline__ u32x4 dequant8_f16(unsigned w, f16x2 s2, f16x2 z2, unsigned kMask, unsigned kMagic) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned m = ((w >> (4 * i)) & kMask) | kMagic;
+    const f16x2 c = __builtin_bit_cast(f16x2, m) - (f16x2){(_Float16)1024.f, (_Float16)1024.f};
+    o[i] = __builtin_bit_cast(unsigned, __builtin_elementwise_fma(c, s2, z2));
+  }
+  return o;
+}
+
+// Position of latent index k inside a dequantised row (the 8-block order above).
+__device__ __forceinline__ int i4_pos(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
 // Value operand through the gfx950 transpose read: within each 16-lane group g, lane j's element
 // e comes from the address given by lane 16g + 4e + j/4, at element offset j%4. Lane
@@ -240,25 +289,149 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
 // KS: compile-time bound on K steps of 32; RB: bound on value blocks per wave.
 // ---------------------------------------------------------------------------------------------
 constexpr int kProducers = 4;           // waves that only move data (direct-to-LDS loads)
+// int4: dequantisation items (half groups) per producer lane and tile at rank 512
+constexpr int kI4MaxItems = (kTileTokens * 2 * 32 + kProducers * 64 - 1) / (kProducers * 64);
 constexpr int kMaxChunkPerProducer = 5; // 1 KB DMA chunks per producer per matrix and tile
 constexpr float kRescaleSlack = 8.f;    // base-2 headroom before the running reference max moves
 
 // Threads of the decode workgroup for G consumer groups.
 constexpr int decode_threads(int G) { return 64 * (4 * G + kProducers); }
 
+// ---------------------------------------------------------------------------------------------
+// int4 producer waves. A tile's stored bytes (16 rows of codes and of scale/zero words, for Zk
+// then Zv) are four contiguous runs in HBM, copied by 1 KB direct-to-LDS chunks into raw stage
+// t % nr. One tile later the producers dequantise it into fp16 stage t % 2, which the consumers
+// read with the bf16 geometry. Per iteration (one workgroup barrier):
+//   issue raw tile it + nr (its stage held tile it, dequantised before this barrier),
+//   dequantise tile it + 1 (landed before this barrier) into the stage tile it - 1 used,
+//   wait for tile it + 2.
+// ---------------------------------------------------------------------------------------------
+template <int KS, int RB>
+__device__ __forceinline__ void producer_i4(const DecodeArgs& a, unsigned char* smem, int b, int t_begin,
+                                            int t_end, int ntiles, int pw) {
+  constexpr int SK = lds_stride_k(KS, 2);
+  constexpr int SV = lds_stride_v(RB, 2);
+  constexpr int ZV = kTileTokens * SK;
+  constexpr int STAGE = lds_stage(KS, RB, 2);
+  const int lane = threadIdx.x & 63;
+  unsigned char* raw = smem + kI4DeqStages * STAGE;
+  const int cbk = a.row_bytes_k, qbk = a.qp_bytes_k, cbv = a.row_bytes_v, qbv = a.qp_bytes_v;
+  const int o_qk = kTileTokens * cbk;
+  const int o_cv = o_qk + kTileTokens * qbk;
+  const int o_qv = o_cv + kTileTokens * cbv;
+  const int rs = a.raw_stage, NR = a.nr;
+  const size_t row0 = (size_t)b * a.t_cap + t_begin;
+  const unsigned char* gck = a.zk + row0 * cbk;
+  const unsigned char* gqk = a.zkq + row0 * qbk;
+  const unsigned char* gcv = a.zv + row0 * cbv;
+  const unsigned char* gqv = a.zvq + row0 * qbv;
+
+  auto nch = [](int bytes) { return (bytes + 1023) >> 10; };
+  auto tile_chunks = [&](int rows) { return nch(rows * cbk) + nch(rows * qbk) + nch(rows * cbv) + nch(rows * qbv); };
+  auto pcnt = [&](int n) { return n > pw ? (n - pw + kProducers - 1) / kProducers : 0; };
+  const int rows_last = ntiles > 0 ? t_end - (t_begin + (ntiles - 1) * kTileTokens) : 0;
+  const int cnt_full = pcnt(tile_chunks(kTileTokens));
+  const int cnt_last = ntiles > 0 ? pcnt(tile_chunks(rows_last)) : 0;
+  auto count = [&](int lo, int hi) {     // this wave's loads for tiles (lo, hi]
+    if (hi <= lo) return 0;
+    return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
+  };
+  auto issue = [&](int t) {
+    unsigned char* st = raw + (t % NR) * rs;
+    const int t0 = t * kTileTokens;
+    const int rows = min(kTileTokens, t_end - t_begin - t0);
+    int gc0 = 0;                         // first chunk of the run in the tile's chunk list
+    auto run = [&](const unsigned char* src, unsigned char* dst, int bytes) {
+      const int n = nch(bytes);
+      for (int c = ((pw - gc0) % kProducers + kProducers) % kProducers; c < n; c += kProducers) {
+        const int off = c * 1024 + lane * 16;
+        if (off < bytes) dma16(src + off, dst + c * 1024);
+      }
+      gc0 += n;
+    };
+    run(gck + (size_t)t0 * cbk, st, rows * cbk);
+    run(gqk + (size_t)t0 * qbk, st + o_qk, rows * qbk);
+    run(gcv + (size_t)t0 * cbv, st + o_cv, rows * cbv);
+    run(gqv + (size_t)t0 * qbv, st + o_qv, rows * qbv);
+  };
+
+  // Dequantisation: one item = half a group (16 codes) of one row; a tile has 16 * (hk + hv)
+  // items, item i = lane + 256 u of the producers. The stage offsets of each lane's items are
+  // the same for every tile, so they are computed once.
+  const int hk = 2 * (cbk >> 4), hv = 2 * (cbv >> 4);              // items per row
+  const int pl = pw * 64 + lane;
+  int i_src[kI4MaxItems], i_qp[kI4MaxItems], i_dst[kI4MaxItems], i_row[kI4MaxItems];
+#pragma unroll
+  for (int u = 0; u < kI4MaxItems; ++u) {
+    const int i = pl + u * kProducers * 64;
+    i_row[u] = kTileTokens;                          // no item
+    i_src[u] = i_qp[u] = i_dst[u] = 0;
+    if (i < kTileTokens * (hk + hv)) {
+      const bool isk = i < kTileTokens * hk;
+      const int j = isk ? i : i - kTileTokens * hk;
+      const int h = isk ? hk : hv;
+      const int row = j / h, part = j - row * h;     // part = 2 * group + half
+      i_row[u] = row;
+      i_src[u] = (isk ? row * cbk : o_cv + row * cbv) + part * 8;
+      i_qp[u] = (isk ? o_qk + row * qbk : o_qv + row * qbv) + (part >> 1) * 4;
+      i_dst[u] = (isk ? row * SK : ZV + row * SV) + part * 32;
+    }
+  }
+  unsigned kMask = 0x000F000Fu, kMagic = 0x64006400u;
+  asm volatile("" : "+v"(kMask), "+v"(kMagic));
+  auto dequant = [&](int t) {
+    const unsigned char* st = raw + (t % NR) * rs;
+    unsigned char* dq = smem + (t % kI4DeqStages) * STAGE;
+    const int rows = min(kTileTokens, t_end - t_begin - t * kTileTokens);
+    u32x2 w[kI4MaxItems];
+    unsigned qp[kI4MaxItems];
+#pragma unroll
+    for (int u = 0; u < kI4MaxItems; ++u) {          // all reads first, one wait
+      if (i_row[u] < rows) {
+        w[u] = *(const u32x2*)(st + i_src[u]);
+        qp[u] = *(const unsigned*)(st + i_qp[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kI4MaxItems; ++u) {
+      if (i_row[u] < rows) {
+        const f16x2 s2 = __builtin_bit_cast(f16x2, (qp[u] & 0xFFFFu) * 0x10001u);
+        const f16x2 z2 = __builtin_bit_cast(f16x2, (qp[u] >> 16) * 0x10001u);
+        *(u32x4*)(dq + i_dst[u]) = dequant8_f16(w[u][0], s2, z2, kMask, kMagic);
+        *(u32x4*)(dq + i_dst[u] + 16) = dequant8_f16(w[u][1], s2, z2, kMask, kMagic);
+      }
+    }
+  };
+
+  const int pro = min(NR, ntiles);
+  for (int t = 0; t < pro; ++t) issue(t);
+  wait_vmcnt(count(0, pro - 1));
+  barrier_lds();                                     // raw tile 0 visible to every producer
+  if (ntiles > 0) dequant(0);
+  wait_vmcnt(count(1, pro - 1));
+  for (int it = 0; it < ntiles; ++it) {
+    barrier_lds();                                   // fp16 tile it visible; raw tile it + 1 landed
+    if (it + NR < ntiles) issue(it + NR);
+    if (it + 1 < ntiles) dequant(it + 1);
+    wait_vmcnt(count(it + 2, min(it + NR, ntiles - 1)));
+  }
+}
+
 template <int KS, int RB, int LT, int G>
 __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char* smem, int wg) {
   constexpr int NTHR = decode_threads(G);
-  constexpr int ES = LT == LT_F32 ? 4 : 2;             // bytes per stored latent element
+  constexpr bool I4 = LT == LT_I4;
+  constexpr int ES = LT == LT_F32 ? 4 : 2;             // bytes per latent element in the LDS tile
   constexpr int SK = lds_stride_k(KS, ES);             // LDS row strides (bytes)
   constexpr int SV = lds_stride_v(RB, ES);
   constexpr int ZV = kTileTokens * SK;                 // value rows' offset inside a stage
   constexpr int STAGE = lds_stage(KS, RB, ES);
-  constexpr int NST = lds_nst(KS, RB, ES);
+  constexpr int NST = I4 ? kI4DeqStages : lds_nst(KS, RB, ES);
   constexpr int GPR = NST / G;                         // tile groups the ring holds
   static_assert(NST % G == 0 && GPR >= 2, "LDS ring must hold two tile groups");
-  static_assert((kTileTokens * SK + 1023) / 1024 <= kProducers * kMaxChunkPerProducer &&
-                (kTileTokens * SV + 1023) / 1024 <= kProducers * kMaxChunkPerProducer, "DMA chunks");
+  static_assert(!I4 || G == 1, "int4 tiles are consumed by one group");
+  static_assert(I4 || ((kTileTokens * SK + 1023) / 1024 <= kProducers * kMaxChunkPerProducer &&
+                       (kTileTokens * SV + 1023) / 1024 <= kProducers * kMaxChunkPerProducer), "DMA chunks");
 
   const int b = wg / a.nsplit;
   const int s = wg - b * a.nsplit;
@@ -284,7 +457,9 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
 #pragma unroll
   for (int j = 0; j < RB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (producer) {
+  if (I4 && producer) {
+    producer_i4<KS, RB>(a, smem, b, t_begin, t_end, ntiles, wave - 4 * G);
+  } else if (producer) {
     // ---------------- producer waves: keep the ring full ----------------
     const int pw = wave - 4 * G;
     const unsigned char* gk = a.zk + ((size_t)b * a.t_cap + t_begin) * a.row_bytes_k;
@@ -358,17 +533,25 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       for (int ks = 0; ks < KS; ++ks)
         qop[ks] = (ks < a.nks) ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
     }
+    float qx = 1.f;                                  // int4: the folded query's per-head scale
+    if constexpr (I4) qx = a.qexp[(size_t)b * kHeadsPad + hb * 16 + li];
     LR_WAIT_VM(0);
+    if constexpr (I4) barrier_lds();                 // pairs with the producers' first barrier
     // AND-mask for the last K step: latent indices >= rk read as 0 (the copied granule may
-    // hold pad columns, and they may hold anything, including NaN patterns).
+    // hold pad columns, and they may hold anything, including NaN patterns; a dequantised int4
+    // tile holds zero + 0 * scale there, which is infinite for an infinite zero).
     u32x4 tailmask;
     {
       const int k0 = (a.nks - 1) * 32 + lg * 8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        tailmask[i] = (k0 + 2 * i < a.rk ? 0x0000FFFFu : 0u) | (k0 + 2 * i + 1 < a.rk ? 0xFFFF0000u : 0u);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (I4)   // dword i holds indices i and i + 4 of the 8-block
+          tailmask[i] = (k0 + i < a.rk ? 0x0000FFFFu : 0u) | (k0 + i + 4 < a.rk ? 0xFFFF0000u : 0u);
+        else
+          tailmask[i] = (k0 + 2 * i < a.rk ? 0x0000FFFFu : 0u) | (k0 + 2 * i + 1 < a.rk ? 0xFFFF0000u : 0u);
+      }
     }
-    const bool ktail = (a.rk & 7) != 0;
+    const bool ktail = I4 ? (a.rk & 31) != 0 : (a.rk & 7) != 0;
     // value block j of this wave covers latent indices 16*(half+2j) .. +15 (blocks past the
     // rank read the zero-filled tail of the rows and are never stored)
     const int krow_off = li * SK + lg * 8 * ES;
@@ -384,7 +567,10 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
 
         // ---- scores of this wave's head block: S^T[token 4*lg+i][head li]
         const unsigned char* krow = stg + krow_off;
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        // two independent accumulation chains (even / odd K steps) halve the dependent latency
+        // (one chain where the registers of two consumer groups with wide value blocks are tight)
+        constexpr int NCH = (G == 2 && RB > 8) ? 1 : 2;
+        f32x4 sacc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int ks0 = 0; ks0 < KS; ks0 += 4) {      // 4 K steps of reads in flight, then 4 products
           bf16x8 av[4];
@@ -399,8 +585,9 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            if (ks0 + u < KS) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], qop[ks0 + u], sacc, 0, 0, 0);
+            if (ks0 + u < KS) sacc2[u % NCH] = mfma_k<LT>(av[u], qop[ks0 + u], sacc2[u % NCH]);
         }
+        const f32x4 sacc = NCH == 2 ? sacc2[0] + sacc2[1] : sacc2[0];
 
         // ---- value operands, all LDS reads issued before the softmax
         const unsigned char* vbase = stg + vrow_off;
@@ -415,7 +602,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[i] = sacc[i];
+          v[i] = I4 ? sacc[i] * qx : sacc[i];
           v[i] = (v[i] != v[i]) ? INFINITY : v[i];   // NaN survives the max, poisons only this head
         }
         if (nvalid < kTileTokens) {
@@ -446,16 +633,23 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const __bf16 p = (__bf16)(live ? fast_exp2(v[i] - m) : 0.f);
-          pb[i] = p;
-          ps += (float)p;
+          const float pf = live ? fast_exp2(v[i] - m) : 0.f;
+          if constexpr (I4) {
+            const _Float16 p = (_Float16)pf;
+            pb[i] = __builtin_bit_cast(__bf16, p);
+            ps += (float)p;
+          } else {
+            const __bf16 p = (__bf16)pf;
+            pb[i] = p;
+            ps += (float)p;
+          }
         }
         lsum += ps;
 
         // ---- values: A^T[rv][head li] over this wave's value blocks
 #pragma unroll
         for (int j = 0; j < RB; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[j], pb, acc[j], 0, 0, 0);
+          acc[j] = mfma_v<LT>(vop[j], pb, acc[j]);
       }
     }
     lsum = wave_sum_lg(lsum);
@@ -578,6 +772,103 @@ __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T*
 }
 
 // ---------------------------------------------------------------------------------------------
+// Fold on the matrix cores for bf16 q and Bk: one workgroup per (KV head g, sequence b). Wave w
+// computes the 16-column blocks w, w+4, ... of C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d]
+// (16x16x32 bf16, A = up to 16 query heads of the group, B = Bk^T; C row h = 4*lg + i, column
+// k = lane % 16). F16 (int4 latents): each head's row is scaled by the power of two 2^-e that
+// puts its largest magnitude in [2^14, 2^15), written as fp16 at the dequantised tiles' block
+// order, and 2^e is stored for the decode kernel to undo on the scores.
+// ---------------------------------------------------------------------------------------------
+constexpr int kFoldMaxBlk = 512 / 16 / 4;   // column blocks per wave at rank 512
+
+template <bool F16>
+__global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q, const __bf16* __restrict__ bk,
+                                                    unsigned short* __restrict__ qt, float* __restrict__ qexp,
+                                                    int Hq, int Hkv, int D, int rk, int rk_pad, float scale) {
+  __shared__ float red[4][16];
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int grp = Hq / Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int nblk = rk_pad >> 4;
+  for (int h0 = 0; h0 < grp; h0 += 16) {
+    bf16x8 aop[4];
+    {
+      const int hl = h0 + li;
+      const __bf16* qrow = q + ((size_t)b * Hq + g * grp + hl) * kFoldD + lg * 8;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) aop[ks] = hl < grp ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
+    }
+    f32x4 c[kFoldMaxBlk];
+    float mx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kFoldMaxBlk; ++u) {
+      c[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int blk = wave + 4 * u;
+      if (blk < nblk) {
+        const int k = blk * 16 + li;
+        bf16x8 bop[4];
+        const __bf16* brow = bk + (size_t)k * D + g * kFoldD + lg * 8;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) bop[ks] = k < rk ? *(const bf16x8*)(brow + ks * 32) : zero_bf16x8();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ks], bop[ks], c[u], 0, 0, 0);
+        c[u] *= scale;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], fabsf(c[u][i]));
+      }
+    }
+    float fac[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (F16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        for (int o = 1; o < 16; o <<= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o));
+      if (li == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][4 * lg + i] = mx[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * lg + i;
+        const float m = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+        int e = 0;
+        if (m > 0.f && m <= 3.4e38f) {
+          e = ilogbf(m) - 14;
+          e = e < -100 ? -100 : (e > 100 ? 100 : e);
+        }
+        fac[i] = ldexpf(1.f, -e);
+        if (wave == 0 && li == 0 && h0 + h < grp) qexp[(size_t)b * kHeadsPad + g * grp + h0 + h] = ldexpf(1.f, e);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldMaxBlk; ++u) {
+      const int blk = wave + 4 * u;
+      if (blk < nblk) {
+        const int k = blk * 16 + li;
+        const int pos = F16 ? i4_pos(k) : k;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = h0 + 4 * lg + i;
+          if (h < grp) {
+            const float v = c[u][i] * fac[i];
+            const unsigned short bits = F16 ? __builtin_bit_cast(unsigned short, (_Float16)v)
+                                            : __builtin_bit_cast(unsigned short, (__bf16)v);
+            qt[((size_t)b * kHeadsPad + g * grp + h) * rk_pad + pos] = bits;
+          }
+        }
+      }
+    }
+  }
+  if (g == 0) {   // query heads past Hq: zero rows, unit scale
+    for (int i = tid; i < (kHeadsPad - Hq) * rk_pad; i += 256)
+      qt[((size_t)b * kHeadsPad + Hq) * rk_pad + i] = 0;
+    if (F16)
+      for (int h = Hq + tid; h < kHeadsPad; h += 256) qexp[(size_t)b * kHeadsPad + h] = 1.f;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Combine: one workgroup per (b, j). m* = max over ranges (and window), weights 2^(m_s - m*),
 // l* = sum w_s l_s, Ahat = sum w_s A_s, out = (Ahat Bv[:, g] + w_win Aw) / l*.
 // ---------------------------------------------------------------------------------------------
@@ -588,6 +879,7 @@ struct CombineArgs {
   const void* bv;
   void* out;
   int Hq, Hkv, d, D, rv, rv_pad16, nsplit, window;
+  int i4_order;             // partials are in the dequantised int4 tiles' block order
 };
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
@@ -672,9 +964,10 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
     }
   }
   __syncthreads();
-  for (int r = tid; r < a.rv_pad16; r += 256)
-    ahat[r] = r < a.rv ? part[r] + part[pw + r] + part[2 * pw + r] + part[3 * pw + r]
-                       : 0.f;
+  for (int r = tid; r < a.rv_pad16; r += 256) {
+    const int p = a.i4_order ? i4_pos(r) : r;
+    ahat[r] = r < a.rv ? part[p] + part[pw + p] + part[2 * pw + p] + part[3 * pw + p] : 0.f;
+  }
   __syncthreads();
 
   // up-project: o[c] = sum_r ahat[r] Bv[r][g*d + c]
@@ -752,7 +1045,7 @@ static hipError_t dispatch_decode(const DecodePlan& p, const DecodeArgs& args, i
   const int g = decode_groups(ks, rb);
 #define LR_CASE(K, R)                                                                    \
   if (ks == K && rb == R) {                                                             \
-    if constexpr (decode_groups(K, R) == 2)                                               \
+    if constexpr (LT != LT_I4 && decode_groups(K, R) == 2)                                \
       return launch_decode_kernel<K, R, LT, 2>(args, grid, p.lds_bytes, st, ev_begin, ev_end);              \
     else                                                                                  \
       return launch_decode_kernel<K, R, LT, 1>(args, grid, p.lds_bytes, st, ev_begin, ev_end);              \
@@ -777,6 +1070,10 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
     if (p.latent == LR_F32)
       hipLaunchKernelGGL(lr_fold<float>, grid, dim3(256), 0, st, (const float*)q, (const float*)c->bk, qt,
                          p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
+    else if (p.latent == LR_I4G32)
+      hipLaunchKernelGGL(lr_fold_mfma<true>, dim3(p.Hkv, p.B), dim3(256), 0, st, (const __bf16*)q,
+                         (const __bf16*)c->bk, (unsigned short*)qt, (float*)(w + p.off_qexp), p.Hq, p.Hkv, p.D,
+                         p.rk, p.rk_pad, scale);
     else
       hipLaunchKernelGGL(lr_fold<__bf16>, grid, dim3(256), 0, st, (const __bf16*)q, (const __bf16*)c->bk, qt,
                          p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
@@ -827,9 +1124,13 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.nst = p.nst;
   a.copy_k = p.copy_k;
   a.copy_v = p.copy_v;
+  a.qexp = (const float*)(w + p.off_qexp);
+  a.nr = p.nr;
+  a.raw_stage = p.raw_stage;
   const int grid = a.n_win_blocks + p.B * p.nsplit;
   hipError_t e;
   if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
+  else if (p.latent == LR_I4G32) e = dispatch_decode<LT_I4>(p, a, grid, st, ev_begin, ev_end);
   else e = dispatch_decode<LT_BF16>(p, a, grid, st, ev_begin, ev_end);
   if (e != hipSuccess) return e;
 
@@ -848,6 +1149,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   ca.rv_pad16 = p.rv_pad16;
   ca.nsplit = p.nsplit;
   ca.window = p.window;
+  ca.i4_order = p.latent == LR_I4G32;
   const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);
   const bool f32b = p.latent == LR_F32;

@@ -13,6 +13,7 @@ constexpr int kTileTokens = 16;     // tokens per decode tile
 constexpr int kHeadsPad = 32;       // query heads padded for the 16x16 matrix-core tiles
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kLdsPad = 128;        // slack after the ring for operand over-reads
+constexpr int kMaxSplit = 4096;     // token ranges per sequence (bounds the combine's LDS)
 
 // Compile-time bounds the decode kernel is instantiated for: KS K steps of 32 latent indices
 // for the keys, RB value blocks of 16 per wave (two waves share the value blocks, so
@@ -32,9 +33,14 @@ constexpr int lds_stride_v(int RB, int es) { return RB * 32 * es + 32; }
 constexpr int lds_stage(int KS, int RB, int es) {
   return kTileTokens * (lds_stride_k(KS, es) + lds_stride_v(RB, es));
 }
-// Consumer groups (4 waves each) of the decode workgroup: two when their registers allow three
-// waves per SIMD (10 waves with the 2 producer waves), else one.
+// Consumer groups (4 waves each) of the decode workgroup, beside the 4 producer waves: two when
+// their registers allow three waves per SIMD (12 waves), else one.
 constexpr int decode_groups(int KS, int RB) { return (KS <= 8 && RB <= 12) ? 2 : 1; }
+// int4 latents: raw stages (16 rows of codes and scale/zero words, as stored) for the
+// direct-to-LDS loads, dequantised into two fp16 stages of the geometry above.
+constexpr int kI4DeqStages = 2;
+constexpr int kI4MaxRawStages = 16;
+constexpr int i4_raw_stage(int gk, int gv) { return kTileTokens * 20 * (gk + gv); }
 constexpr int lds_nst(int KS, int RB, int es) {   // stages in the ring: even, at most 8
   return ((kLdsBytes - kLdsPad) / lds_stage(KS, RB, es) > 8 ? 8
                                                              : (kLdsBytes - kLdsPad) / lds_stage(KS, RB, es)) & ~1;
@@ -55,8 +61,9 @@ struct DecodePlan {
   int qp_bytes_k, qp_bytes_v;       // int4: bytes of one row's scale/zero words, else 0
   int stage_bytes, zv_off, qpk_off, qpv_off, nst;  // LDS ring layout
   int copy_k, copy_v;               // bytes of each stored row the ring holds
+  int nr, raw_stage;                // int4: raw (codes + scale/zero) stages and their bytes
   int lds_bytes;                    // dynamic LDS of the decode kernel
-  size_t off_qt, off_ml, off_acc, off_win, ws_bytes;
+  size_t off_qt, off_ml, off_acc, off_win, off_qexp, ws_bytes;
 };
 
 // Fills *p; returns LR_OK or an error code with a message in *msg.

@@ -138,3 +138,66 @@ def test_max_len_zero_gives_zero():
     model, cache = device_layer(li)
     out = run_decode(model, cache, li.q.cuda(), 0)
     assert torch.all(out == 0)
+
+
+# ---- int4 latents (groups of 32, fp16 scale and zero): dequantised in-kernel -----------------
+
+def test_config3_full_size_sampled():
+    """B=16, T=16384, r=358 int4 (12 groups, the last with 6 live indices)."""
+    li = synth.make_layer(synth.CONFIGS[3])
+    check(li, batches=[0, 9, 15])
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 32.0, 128.0])
+def test_int4_reduced(q_scale):
+    cfg = synth.CONFIGS[3].replace(batch=3, seq_len=1200)
+    check(synth.make_layer(cfg, q_scale=q_scale))
+
+
+@pytest.mark.parametrize("rank", [1, 7, 31, 32, 33, 40, 64, 100, 200, 256, 300, 384, 448, 500, 512])
+def test_int4_rank_sweep(rank):
+    cfg = synth.CONFIGS[3].replace(batch=2, seq_len=97, rank_k=rank, rank_v=rank)
+    check(synth.make_layer(cfg, q_scale=32.0))
+
+
+def test_int4_unequal_ranks():
+    cfg = synth.CONFIGS[3].replace(batch=2, seq_len=333, rank_k=72, rank_v=488)
+    check(synth.make_layer(cfg, q_scale=32.0))
+    cfg = synth.CONFIGS[3].replace(batch=2, seq_len=333, rank_k=504, rank_v=40)
+    check(synth.make_layer(cfg, q_scale=32.0))
+
+
+def test_int4_needle():
+    cfg = synth.CONFIGS[3].replace(batch=2, seq_len=3000)
+    check(synth.selection_needle(cfg))
+
+
+@pytest.mark.parametrize("nsplit", [1, 7, 64])
+def test_int4_split_invariance(nsplit):
+    cfg = synth.CONFIGS[3].replace(batch=2, seq_len=2500)
+    li = synth.make_layer(cfg, q_scale=32.0)
+    out, _ = check(li, nsplit=nsplit)
+    ref_out, _ = check(li, nsplit=3)
+    assert rel_err(out.numpy(), ref_out.numpy()) <= TOL["i4g32"]
+
+
+def test_int4_ragged_lengths_and_empty():
+    cfg = synth.CONFIGS[3].replace(batch=6, seq_len=400)
+    lens = np.array([0, 1, 15, 16, 17, 400], np.int32)
+    li = synth.make_layer(cfg, q_scale=32.0, lat_len=lens, t_cap=400)
+    out, _ = check(li, batches=list(range(1, 6)))
+    assert torch.all(out[0] == 0)
+
+
+def test_int4_folded_query_beyond_fp16_range():
+    """A selection needle whose folded query entries (~8e4) exceed the fp16 range: the per-head
+    power-of-two scale keeps them representable and the one-hot softmax picks the needle."""
+    cfg = synth.CONFIGS[3].replace(batch=2, seq_len=700)
+    check(synth.selection_needle(cfg, delta=40.0 * 4096))
+
+
+def test_int4_with_exact_window():
+    cfg = synth.CONFIGS[4].replace(batch=3, latent="i4g32")
+    li = synth.make_layer(cfg, 11, q_scale=16.0, lat_len=np.array([900, 33, 0], np.int32),
+                          win_len=np.array([128, 60, 5], np.int32))
+    check(li)
