@@ -127,6 +127,32 @@ def cpu_baseline(cfg, li, budget_s: float = 20.0):
                 us_per_layer_step=t_total / done * cfg.batch * 1e6)
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the decode kernel's sources: counter figures are valid only for this code."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_kv_cache_lowrank_amd", "csrc")
+    for name in ("decode.hip", "device_common.h", "internal.h", "abi.cpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of lr_decode from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE runs, scaled by a copy kernel of known size), or None when there is none for
+    this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "lr_decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get("workloads", {}).get(workload)
+    if entry is None or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(entry["hbm_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +161,10 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--nsplit", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="cache copies rotated over the steps (0: enough that the copies exceed 2 x 256 MB)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 256 MiB device copy (the counter calibration reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -161,9 +191,16 @@ def main():
     li = synth.make_layer(cfg, t_cap=T, lat_len=np.full(cfg.batch, T, np.int32))
     log(f"inputs ready in {time.time() - t0:.1f} s")
     from synth.device import device_layer
-    model, cache = device_layer(li, dev, with_proj=True)
-    lat0 = torch.from_numpy(start_len).to(dev)
-    cache.tensors["lat_len"].copy_(lat0)
+    # The MI355X Infinity Cache holds 256 MB: workloads smaller than that rotate over copies of
+    # the cache so that every step streams its latents from HBM.
+    lat_bytes = step_bytes(cfg, li.rank_k, li.rank_v, li.lat_len, np.zeros_like(li.lat_len), 0)["latents"]
+    n_copies = args.copies if args.copies > 0 else max(1, min(8, -(-(2 * 256 * 2**20) // lat_bytes)))
+    caches = []
+    for _ in range(n_copies):
+        model, cache = device_layer(li, dev, with_proj=True)
+        cache.tensors["lat_len"].copy_(torch.from_numpy(start_len).to(dev))
+        caches.append(cache)
+    log(f"{n_copies} cache cop{'y' if n_copies == 1 else 'ies'} of {lat_bytes / 1e6:.1f} MB")
     q = li.q.to(dev)
     gen = np.random.default_rng(12345)
     k_new = torch.from_numpy(gen.standard_normal((cfg.batch, n_new, cfg.kv_width), dtype=np.float32)).to(
@@ -176,6 +213,11 @@ def main():
     evs = [(ev.create(), ev.create()) for _ in range(K)]
     torch.cuda.synchronize()
 
+    # every copy takes the same number of appends: lengths advance once per pass over the copies
+    steps_per_copy = -(-(W + K) // n_copies)
+    for cache in caches:
+        cache.tensors["lat_len"].copy_(torch.from_numpy(np.full(cfg.batch, T - steps_per_copy * n_new,
+                                                                 np.int32)).to(dev))
     lens = []
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -183,12 +225,13 @@ def main():
         if i == W:
             torch.cuda.synchronize()
             start.record()
+        cache = caches[i % n_copies]
         lr.lowrank_kv_append(model, 0, cache, k_new, v_new)
         timed = i >= W
         lr.lowrank_attn_decode(model, 0, cache, q, out, T, ws, nsplit=args.nsplit,
                                events=evs[i - W] if timed else None)
         if timed:
-            lens.append(start_len + (i + 1) * n_new)
+            lens.append(np.full(cfg.batch, T - steps_per_copy * n_new + (i // n_copies + 1) * n_new, np.int32))
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -199,6 +242,14 @@ def main():
         ev.destroy(a)
         ev.destroy(b)
     assert torch.isfinite(out).all(), "non-finite output"
+
+    if args.copy_probe:
+        # one elementwise kernel that reads 256 MiB and writes 256 MiB (a plain copy of known size)
+        src = torch.zeros(64 * 2**20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
 
     by = [step_bytes(cfg, li.rank_k, li.rank_v, L, np.zeros_like(L), n_new) for L in lens]
     step_total = float(np.mean([x["total"] for x in by]))
@@ -229,8 +280,10 @@ def main():
         "step_bytes": int(step_total),
         "roofline": {"bound": "hbm", "kernel": "lr_decode", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s",
-                     "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4), "traffic": None,
+                     "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4),
+                     "traffic": measured_traffic(cfg.name),
                      "kernel_us": round(kern_avg_ms * 1e3, 2), "bytes_per_launch": int(lat_avg)},
+        "cache_copies": n_copies,
     }
     if not args.no_cpu:
         log("timing the CPU oracle ...")

@@ -85,6 +85,10 @@ typedef struct {
  *                     zk_qp [B][t_cap][ceil(rank_k/32)] uint32: float16 scale in the low half,
  *                     float16 zero in the high half. Element value = code * scale + zero,
  *                     evaluated as one float32 fused multiply-add. ld_k, ld_v are ignored.
+ *                     Decode needs zk, zv, zk_qp and zv_qp 16-byte aligned; it evaluates the
+ *                     element as one float16 fused multiply-add (the float16 matrix-core
+ *                     operand), so groups whose values lie below float16's normal range
+ *                     (|value| < 2^-14) lose relative precision there.
  *   Quantisation of a row z (float32), per group of 32 indices (the last may be partial; its
  *   min/max run over its real elements): zero = f16(min), scale = f16(f32(max-min)/15),
  *   code = clamp(rint((z - zero)/scale), 0, 15) in float32, all codes 0 if scale == 0.
@@ -179,8 +183,10 @@ int lowrank_kv_store(const lr_model_desc* model, int32_t layer, const lr_layer_c
 
 /*
  * Dequantise (or widen) stored latent rows [0, n_rows) of every sequence to float32:
- * zk_out [B][n_rows][rank_k], zv_out [B][n_rows][rank_v], with the element value decode uses
- * before it rounds to its bfloat16 matrix-core operand. Requires n_rows <= t_cap.
+ * zk_out [B][n_rows][rank_k], zv_out [B][n_rows][rank_v]: the stored value itself (float32,
+ * bfloat16 widened exactly, int4 as the float32 fused multiply-add above). Decode rounds this
+ * value once to its 16-bit matrix-core operand (bfloat16 for float32/bf16 caches, float16 for
+ * int4). Requires n_rows <= t_cap.
  */
 int lowrank_kv_dequant(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
                        int32_t batch, int64_t n_rows, float* zk_out, float* zv_out, void* stream);
