@@ -63,16 +63,14 @@ static int row_bytes(int latent, int r, int ld) {
 // Workspace layout (independent of the cache strides).
 static void layout_workspace(DecodePlan* p) {
   size_t off = 0;
-  p->off_qt = off;
-  off = align256(off + (size_t)p->B * kHeadsPad * p->rk_pad * 2);
+  p->off_qt = off;   // folded query: bf16, or float32 for int4 latents
+  off = align256(off + (size_t)p->B * kHeadsPad * p->rk_pad * (p->latent == LR_I4G32 ? 4 : 2));
   p->off_ml = off;
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * 2 * 4);
   p->off_acc = off;
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * 4);
   p->off_win = off;
   if (p->window > 0) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);
-  p->off_qexp = off;
-  if (p->latent == LR_I4G32) off = align256(off + (size_t)p->B * kHeadsPad * 4);
   p->ws_bytes = off > 0 ? off : 256;
 }
 
@@ -161,10 +159,16 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   p->stage_bytes = lds_stage(KS, RB, es);
   p->zv_off = kTileTokens * sk;
   p->nst = lds_nst(KS, RB, es);
-  const int G = decode_groups(KS, RB);
-  if (p->nst < 2 * G) return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
+  const int G = decode_groups(p->latent, KS, RB);
+  const int tpi = decode_tpi(p->latent, KS, RB);
+  const bool split = decode_split(p->latent, KS, RB);
+  if (p->nst < 2 * tpi || p->nst % tpi != 0)
+    return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
   int lds = p->nst * p->stage_bytes + kLdsPad;
-  const int merge = G > 1 ? (2048 + 4 * RB * 1024) * (G - 1) : 0;
+  // end-of-range merge of the consumer waves' partials: (m, l, value blocks) per extra wave
+  const int extra = split ? 4 * G - 2 : 4 * (G - 1);
+  const int nvb = split ? 2 * RB : RB;
+  const int merge = extra * (512 + nvb * 1024);
   if (merge > lds) lds = merge;
   if (window_lds > lds) lds = window_lds;
   if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;

@@ -92,13 +92,15 @@ struct AppendArgs {
 };
 
 // Projection + storage of every latent row this call creates.
-// grid (column chunks of 64 over max(rk, rv), 2 = {K, V}, B); 256 threads = 4 waves.
-// For each row: wave w accumulates z over input dims [w*D/4, (w+1)*D/4) for the chunk's 64
-// columns (lane = column; the loads of P are independent and coalesced), the 4 partial sums
-// are added in a fixed order through LDS and wave 0 stores the row.
+// grid (column chunks of 64 over max(rk, rv), 2 = {K, V}, B); 512 threads = 8 waves.
+// For each row: wave w accumulates z over input dims [w*D/8, (w+1)*D/8) for the chunk's 64
+// columns (lane = column; the loads of P are independent and coalesced, 32 in flight per
+// lane), the 8 partial sums are added in a fixed order through LDS and wave 0 stores the row.
+constexpr int kAppendWaves = 8;
+
 template <typename PT>
-__global__ __launch_bounds__(256) void lr_append_project(AppendArgs a) {
-  extern __shared__ float xs[];    // [D] source row as float, then [4][64] partial sums
+__global__ __launch_bounds__(kAppendWaves * 64) void lr_append_project(AppendArgs a) {
+  extern __shared__ float xs[];    // [D] source row as float, then [8][64] partial sums
   const int kv = blockIdx.y, b = blockIdx.z;
   const int r = kv == 0 ? a.rk : a.rv;
   const int col0 = blockIdx.x * 64;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void lr_append_project(AppendArgs a) {
   const int rb = row_bytes_of(a.latent, r, ld);
   const int G = (r + kGroup - 1) / kGroup;
   const int col = col0 + lane;
-  const int dq = a.D / 4;
+  const int dq = a.D / kAppendWaves;
   float* x = xs;
   float* zpart = xs + a.D;
 
@@ -133,26 +135,28 @@ __global__ __launch_bounds__(256) void lr_append_project(AppendArgs a) {
     const __bf16* src = (a.window > 0) ? win + ((size_t)b * a.window + (L + e) % a.window) * a.D
                                        : xnew + ((size_t)b * a.n_new + e) * a.D;
     __syncthreads();
-    for (int c = tid; c < a.D; c += 256) x[c] = (float)src[c];
+    for (int c = tid; c < a.D; c += kAppendWaves * 64) x[c] = (float)src[c];
     __syncthreads();
     float z = 0.f;
     if (col < r) {
       const PT* pc = P + (size_t)(wave * dq) * r + col;
       const float* xw = x + wave * dq;
       int c = 0;
-      for (; c + 16 <= dq; c += 16) {
-        float pv[16];
+      for (; c + 32 <= dq; c += 32) {
+        float pv[32];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) pv[u] = to_f32(pc[(size_t)(c + u) * r]);
+        for (int u = 0; u < 32; ++u) pv[u] = to_f32(pc[(size_t)(c + u) * r]);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) z += xw[c + u] * pv[u];
+        for (int u = 0; u < 32; ++u) z += xw[c + u] * pv[u];
       }
       for (; c < dq; ++c) z += xw[c] * to_f32(pc[(size_t)c * r]);
     }
     zpart[wave * 64 + lane] = z;
     __syncthreads();
     if (wave == 0) {
-      z = ((zpart[lane] + zpart[64 + lane]) + zpart[128 + lane]) + zpart[192 + lane];
+      z = 0.f;
+#pragma unroll
+      for (int w = 0; w < kAppendWaves; ++w) z += zpart[w * 64 + lane];
       const long long row = (long long)L + e;
       if (a.z_debug && col < r)
         a.z_debug[((size_t)b * a.n_new + e) * (a.rk + a.rv) + (kv == 0 ? 0 : a.rk) + col] = z;
@@ -300,9 +304,9 @@ hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const voi
   a.B = p.B;
   const int rmax = p.rk > p.rv ? p.rk : p.rv;
   dim3 grid((rmax + 63) / 64, 2, p.B);
-  const size_t lds = (size_t)(p.D + 256) * sizeof(float);
-  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append_project<float>, grid, dim3(256), lds, st, a);
-  else hipLaunchKernelGGL(lr_append_project<__bf16>, grid, dim3(256), lds, st, a);
+  const size_t lds = (size_t)(p.D + kAppendWaves * 64) * sizeof(float);
+  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append_project<float>, grid, dim3(kAppendWaves * 64), lds, st, a);
+  else hipLaunchKernelGGL(lr_append_project<__bf16>, grid, dim3(kAppendWaves * 64), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lr_append_finish, dim3(p.B), dim3(256), 0, st, a);

@@ -56,7 +56,6 @@ struct DecodeArgs {
   int n_win_blocks;
   int stage_bytes, zv_off, qpk_off, qpv_off, nst;
   int copy_k, copy_v;       // bytes of each stored row the LDS ring holds
-  const float* qexp;        // int4: per (sequence, head) power of two the folded query was scaled by
   int nr, raw_stage;        // int4: raw stages in the ring and their size in bytes
 };
 
@@ -274,19 +273,22 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Latent workgroup: one (sequence b, token range s), 8 waves in two ping-pong groups.
+// Latent workgroup: one (sequence b, token range s): 4 producer waves and G groups of 4 consumer
+// waves.
 //
 // The token range is cut into 16-token tiles that stream through an LDS ring (stage = the 16 Zk
 // rows then the 16 Zv rows, each row padded so that the 16 rows a score operand reads fall in
-// distinct banks). Group 0 (waves 0-3) computes the even tiles, group 1 the odd ones; inside a
-// group wave (hb, half) owns query-head block hb (heads 16*hb .. 16*hb+15) and value blocks
-// half, half+2, ... (16 latent indices each). Per tile a wave computes
-//   S^T[16 tokens, 16 heads] = Zk qt^T            (16x16x32 bf16, K = rank)
+// distinct banks). Each iteration consumes TPI tiles between two workgroup barriers. Consumer
+// wave roles (hb = query-head block, heads 16*hb .. 16*hb+15):
+//   SP (split): wave (hb, slot) takes tile TPI*it + slot, all value blocks (TPI = 2G);
+//   else:       waves (hb, half) of group g share tile G*it + g; value blocks half, half+2, ...
+// Per tile a wave computes
+//   S^T[16 tokens, 16 heads] = Zk qt^T            (16x16x32, K = rank)
 //   online softmax of its 4 scores per lane       (base 2; only cross-lane max)
-//   A^T[16 rv, 16 heads] += Zv^T P^T               (16x16x16 bf16, K = the 16 tokens)
-// so no data crosses waves inside a tile and the workgroup meets at one barrier per tile pair.
-// At the end the two groups' (m, l, A) are merged through LDS and written once.
-// KS: compile-time bound on K steps of 32; RB: bound on value blocks per wave.
+//   A^T[16 rv, 16 heads] += Zv^T P^T               (16x16x16, K = the 16 tokens)
+// so no data crosses waves inside a tile. At the end the waves holding the same role's partial
+// (m, l, A) for different tiles are merged through LDS and written once.
+// KS: compile-time bound on K steps of 32; RB: bound on value blocks of a half.
 // ---------------------------------------------------------------------------------------------
 constexpr int kProducers = 4;           // waves that only move data (direct-to-LDS loads)
 // int4: dequantisation items (half groups) per producer lane and tile at rank 512
@@ -417,7 +419,7 @@ __device__ __forceinline__ void producer_i4(const DecodeArgs& a, unsigned char* 
   }
 }
 
-template <int KS, int RB, int LT, int G>
+template <int KS, int RB, int LT, int G, bool SP>
 __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char* smem, int wg) {
   constexpr int NTHR = decode_threads(G);
   constexpr bool I4 = LT == LT_I4;
@@ -427,9 +429,10 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   constexpr int ZV = kTileTokens * SK;                 // value rows' offset inside a stage
   constexpr int STAGE = lds_stage(KS, RB, ES);
   constexpr int NST = I4 ? kI4DeqStages : lds_nst(KS, RB, ES);
-  constexpr int GPR = NST / G;                         // tile groups the ring holds
-  static_assert(NST % G == 0 && GPR >= 2, "LDS ring must hold two tile groups");
-  static_assert(!I4 || G == 1, "int4 tiles are consumed by one group");
+  constexpr int TPI = SP ? 2 * G : G;                  // tiles per iteration
+  constexpr int NVB = SP ? 2 * RB : RB;                // value blocks per consumer wave
+  static_assert(NST % TPI == 0 && NST / TPI >= 2, "LDS ring must hold two iterations of tiles");
+  static_assert(!I4 || (G == 1 && !SP), "int4 tiles are consumed by one group of halves");
   static_assert(I4 || ((kTileTokens * SK + 1023) / 1024 <= kProducers * kMaxChunkPerProducer &&
                        (kTileTokens * SV + 1023) / 1024 <= kProducers * kMaxChunkPerProducer), "DMA chunks");
 
@@ -444,7 +447,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   const int t_begin = s * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, L);
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTileTokens - 1) / kTileTokens : 0;
-  const int niter = (ntiles + G - 1) / G;
+  const int niter = (ntiles + TPI - 1) / TPI;
 
   unsigned char* ring = smem;
   // Zero the ring once: LDS columns past the copied part of a row (K steps and value blocks
@@ -453,9 +456,9 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   barrier_lds();
 
   float m = -INFINITY, lsum = 0.f;
-  f32x4 acc[RB];
+  f32x4 acc[NVB];
 #pragma unroll
-  for (int j = 0; j < RB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NVB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (I4 && producer) {
     producer_i4<KS, RB>(a, smem, b, t_begin, t_end, ntiles, wave - 4 * G);
@@ -510,31 +513,66 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         if (c < ncv && offv[u] >= 0 && offv[u] < limv) dma16(srcv + offv[u], stg + ZV + c * 1024);
       }
     };
-    const int pro = min(NST - G, ntiles);
+    const int pro = min(NST - TPI, ntiles);
     for (int t = 0; t < pro; ++t) issue(t);
-    wait_vmcnt(count(G - 1, pro - 1));                 // tile group 0 landed
+    wait_vmcnt(count(TPI - 1, pro - 1));               // iteration 0's tiles landed
     for (int it = 0; it < niter; ++it) {
-      barrier_lds();                                   // group `it` visible; group it-1's stages free
+      barrier_lds();                                   // iteration it visible; it-1's stages free
 #pragma unroll
-      for (int j = 0; j < G; ++j)
-        if (G * it + NST - G + j < ntiles) issue(G * it + NST - G + j);
-      const int hi = min(G * it + NST - 1, ntiles - 1);
-      wait_vmcnt(count(G * it + 2 * G - 1, hi));       // group it+1 landed
+      for (int j = 0; j < TPI; ++j)
+        if (TPI * it + NST - TPI + j < ntiles) issue(TPI * it + NST - TPI + j);
+      const int hi = min(TPI * it + NST - 1, ntiles - 1);
+      wait_vmcnt(count(TPI * it + 2 * TPI - 1, hi));   // iteration it+1's tiles landed
     }
   } else {
     // ---------------- consumer waves: scores, online softmax, values ----------------
-    const int grp = wave >> 2;
+    const int slot = SP ? (wave >> 1) : (wave >> 2);   // tile of the iteration this wave takes
     const int hb = wave & 1;
-    const int half = (wave >> 1) & 1;
+    const int half = SP ? 0 : (wave >> 1) & 1;
     bf16x8 qop[KS];
-    {
+    float qx = 1.f;          // int4: the power of two the fp16 folded query was divided by
+    if constexpr (I4) {
+      // The folded query arrives in float32. Its largest magnitude per head is brought into
+      // [2^14, 2^15) by a power of two so that the fp16 operand cannot overflow; the scores are
+      // multiplied back by that power. The 4 lane groups holding a head share its scale.
+      const float* qrow = (const float*)a.qt + ((size_t)b * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
+      float qf[KS][8];
+      float mxq = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks < a.nks) {
+          const f32x4 x0 = *(const f32x4*)(qrow + ks * 32);
+          const f32x4 x1 = *(const f32x4*)(qrow + ks * 32 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { qf[ks][e] = x0[e]; qf[ks][4 + e] = x1[e]; }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[ks][e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mxq = fmaxf(mxq, fabsf(qf[ks][e]));
+      }
+      mxq = wave_max_lg(mxq);
+      int ex = 0;
+      if (mxq > 0.f && mxq <= 3.4e38f) {
+        ex = ilogbf(mxq) - 14;
+        ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+      }
+      const float fac = ldexpf(1.f, -ex);
+      qx = ldexpf(1.f, ex);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)(qf[ks][e] * fac);
+        qop[ks] = __builtin_bit_cast(bf16x8, h);
+      }
+    } else {
       const __bf16* qrow = a.qt + ((size_t)b * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         qop[ks] = (ks < a.nks) ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
     }
-    float qx = 1.f;                                  // int4: the folded query's per-head scale
-    if constexpr (I4) qx = a.qexp[(size_t)b * kHeadsPad + hb * 16 + li];
     LR_WAIT_VM(0);
     if constexpr (I4) barrier_lds();                 // pairs with the producers' first barrier
     // AND-mask for the last K step: latent indices >= rk read as 0 (the copied granule may
@@ -552,15 +590,15 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       }
     }
     const bool ktail = I4 ? (a.rk & 31) != 0 : (a.rk & 7) != 0;
-    // value block j of this wave covers latent indices 16*(half+2j) .. +15 (blocks past the
-    // rank read the zero-filled tail of the rows and are never stored)
+    // value block j of this wave covers latent indices 16*rb .. 16*rb+15 with rb = j (split) or
+    // half + 2j (blocks past the rank read the zero-filled tail of the rows, never stored)
     const int krow_off = li * SK + lg * 8 * ES;
     const int vrow_off = (LT == LT_F32) ? ZV + 4 * lg * SV + li * ES + half * 16 * ES
                                         : ZV + (4 * lg + (li >> 2)) * SV + (li & 3) * 8 + half * 32;
 
     for (int it = 0; it < niter; ++it) {
       barrier_lds();
-      const int t = G * it + grp;
+      const int t = TPI * it + slot;
       if (t < ntiles) {
         const unsigned char* stg = ring + (t % NST) * STAGE;
         const int nvalid = min(kTileTokens, t_end - t_begin - t * kTileTokens);
@@ -569,7 +607,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         const unsigned char* krow = stg + krow_off;
         // two independent accumulation chains (even / odd K steps) halve the dependent latency
         // (one chain where the registers of two consumer groups with wide value blocks are tight)
-        constexpr int NCH = (G == 2 && RB > 8) ? 1 : 2;
+        constexpr int NCH = (G == 2 && NVB > 8) ? 1 : 2;
         f32x4 sacc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int ks0 = 0; ks0 < KS; ks0 += 4) {      // 4 K steps of reads in flight, then 4 products
@@ -589,14 +627,17 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         }
         const f32x4 sacc = NCH == 2 ? sacc2[0] + sacc2[1] : sacc2[0];
 
-        // ---- value operands, all LDS reads issued before the softmax
+        // ---- value operands: read in chunks of VC blocks; the first chunk's reads are issued
+        // before the softmax so that its LDS latency hides under it
+        constexpr int VC = NVB < 8 ? NVB : 8;
         const unsigned char* vbase = stg + vrow_off;
-        bf16x4 vop[RB];
+        auto vread = [&](int j) -> bf16x4 {
+          if constexpr (LT == LT_F32) return v_operand4<LT, SV>(vbase, j * (SP ? 16 : 32) * ES);
+          else return v_operand_tr(vbase + j * (SP ? 32 : 64));
+        };
+        bf16x4 vop[VC];
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          if constexpr (LT == LT_F32) vop[j] = v_operand4<LT, SV>(vbase, j * 32 * ES);
-          else vop[j] = v_operand_tr(vbase + j * 64);
-        }
+        for (int u = 0; u < VC; ++u) vop[u] = vread(u);
 
         // ---- online softmax over the tile's 16 tokens (4 per lane, 4 lane groups)
         float v[4];
@@ -605,15 +646,15 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
           v[i] = I4 ? sacc[i] * qx : sacc[i];
           v[i] = (v[i] != v[i]) ? INFINITY : v[i];   // NaN survives the max, poisons only this head
         }
-        if (nvalid < kTileTokens) {
+        // rows past the range's end: score -inf, value operand 0 (the stage may hold stale rows)
+        u32x2 tm = {0xFFFFFFFFu, 0xFFFFFFFFu};
+        const bool partial = nvalid < kTileTokens;
+        if (partial) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (4 * lg + i >= nvalid) v[i] = -INFINITY;
-          u32x2 tm;
           tm[0] = (4 * lg < nvalid ? 0x0000FFFFu : 0u) | (4 * lg + 1 < nvalid ? 0xFFFF0000u : 0u);
           tm[1] = (4 * lg + 2 < nvalid ? 0x0000FFFFu : 0u) | (4 * lg + 3 < nvalid ? 0xFFFF0000u : 0u);
-#pragma unroll
-          for (int j = 0; j < RB; ++j) vop[j] = __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, vop[j]) & tm);
         }
         float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         mx = wave_max_lg(mx);
@@ -626,7 +667,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
           m = mnew;
           lsum *= alpha;
 #pragma unroll
-          for (int j = 0; j < RB; ++j) acc[j] *= alpha;
+          for (int j = 0; j < NVB; ++j) acc[j] *= alpha;
         }
         const bool live = m != -INFINITY;
         bf16x4 pb;
@@ -648,46 +689,65 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
 
         // ---- values: A^T[rv][head li] over this wave's value blocks
 #pragma unroll
-        for (int j = 0; j < RB; ++j)
-          acc[j] = mfma_v<LT>(vop[j], pb, acc[j]);
+        for (int j0 = 0; j0 < NVB; j0 += VC) {
+          if (j0 > 0) {
+#pragma unroll
+            for (int u = 0; u < VC; ++u)
+              if (j0 + u < NVB) vop[u] = vread(j0 + u);
+          }
+          if (partial) {
+#pragma unroll
+            for (int u = 0; u < VC; ++u)
+              vop[u] = __builtin_bit_cast(bf16x4, __builtin_bit_cast(u32x2, vop[u]) & tm);
+          }
+#pragma unroll
+          for (int u = 0; u < VC; ++u)
+            if (j0 + u < NVB) acc[j0 + u] = mfma_v<LT>(vop[u], pb, acc[j0 + u]);
+        }
       }
     }
     lsum = wave_sum_lg(lsum);
   }
 
-  // ---- merge the consumer groups, write this range's partial
+  // ---- merge the consumer waves' partials per role, write this range's partial
+  // Roles: hb (split) or (hb, half). The main wave of a role (slot 0) absorbs the NX extra
+  // waves of its role through LDS: m [NX][64], l [NX][64], A [NX][NVB][64] f32x4.
+  constexpr int NROLE = SP ? 2 : 4;
+  constexpr int NX = 4 * G - NROLE;
   barrier_lds();                                   // the ring is no longer read
-  float* mbuf = (float*)smem;                      // [G-1][4 roles][64]
-  float* lbuf = mbuf + 4 * 64 * (G > 1 ? G - 1 : 1);
-  f32x4* abuf = (f32x4*)(smem + 2048 * (G > 1 ? G - 1 : 1));   // [G-1][4 roles][RB][64]
-  const int role = wave & 3;
-  const int grp = wave >> 2;
-  if (!producer && grp > 0) {
-    const int slot = (grp - 1) * 4 + role;
-    mbuf[slot * 64 + lane] = m;
-    lbuf[slot * 64 + lane] = lsum;
+  float* mbuf = (float*)smem;
+  float* lbuf = mbuf + 64 * (NX > 0 ? NX : 1);
+  f32x4* abuf = (f32x4*)(smem + 512 * (NX > 0 ? NX : 1));
+  const int role = wave % NROLE;
+  const int wslot = wave / NROLE;                  // 0 = the role's main wave
+  if constexpr (NX > 0) {
+    if (!producer && wslot > 0) {
+      const int x = (wslot - 1) * NROLE + role;
+      mbuf[x * 64 + lane] = m;
+      lbuf[x * 64 + lane] = lsum;
 #pragma unroll
-    for (int j = 0; j < RB; ++j) abuf[(slot * RB + j) * 64 + lane] = acc[j];
+      for (int j = 0; j < NVB; ++j) abuf[(x * NVB + j) * 64 + lane] = acc[j];
+    }
   }
   barrier_lds();
-  if (!producer && grp == 0) {
+  if (!producer && wslot == 0) {
     const int hb = wave & 1;
-    const int half = (wave >> 1) & 1;
+    const int half = SP ? 0 : (wave >> 1) & 1;
     float ms = m;
 #pragma unroll
-    for (int g2 = 1; g2 < G; ++g2) ms = fmaxf(ms, mbuf[((g2 - 1) * 4 + role) * 64 + lane]);
+    for (int w2 = 1; w2 <= NX / NROLE; ++w2) ms = fmaxf(ms, mbuf[((w2 - 1) * NROLE + role) * 64 + lane]);
     const float wa = (m == -INFINITY) ? 0.f : fast_exp2(m - ms);
     float lt = lsum * wa;
 #pragma unroll
-    for (int j = 0; j < RB; ++j) acc[j] *= wa;
+    for (int j = 0; j < NVB; ++j) acc[j] *= wa;
 #pragma unroll
-    for (int g2 = 1; g2 < G; ++g2) {
-      const int slot = (g2 - 1) * 4 + role;
-      const float mo = mbuf[slot * 64 + lane];
+    for (int w2 = 1; w2 <= NX / NROLE; ++w2) {
+      const int x = (w2 - 1) * NROLE + role;
+      const float mo = mbuf[x * 64 + lane];
       const float wb = (mo == -INFINITY) ? 0.f : fast_exp2(mo - ms);
-      lt += lbuf[slot * 64 + lane] * wb;
+      lt += lbuf[x * 64 + lane] * wb;
 #pragma unroll
-      for (int j = 0; j < RB; ++j) acc[j] += abuf[(slot * RB + j) * 64 + lane] * wb;
+      for (int j = 0; j < NVB; ++j) acc[j] += abuf[(x * NVB + j) * 64 + lane] * wb;
     }
     const size_t pidx = (size_t)b * a.nsplit + s;
     const int head = hb * 16 + li;
@@ -696,22 +756,22 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       a.part_ml[(pidx * a.Hq + head) * 2 + 1] = lt;
     }
 #pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int rb = half + 2 * j;
+    for (int j = 0; j < NVB; ++j) {
+      const int rb = SP ? j : half + 2 * j;
       if (rb < a.nrb && head < a.Hq)
         *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + rb * 16 + 4 * lg) = acc[j];
     }
   }
 }
 
-template <int KS, int RB, int LT, int G>
+template <int KS, int RB, int LT, int G, bool SP>
 __global__ __launch_bounds__(decode_threads(G)) void lr_decode(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   if ((int)blockIdx.x < a.n_win_blocks) {
     window_block<LT, decode_threads(G)>(a, smem);
     return;
   }
-  latent_block<KS, RB, LT, G>(a, smem, (int)blockIdx.x - a.n_win_blocks);
+  latent_block<KS, RB, LT, G, SP>(a, smem, (int)blockIdx.x - a.n_win_blocks);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -772,99 +832,55 @@ __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T*
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fold on the matrix cores for bf16 q and Bk: one workgroup per (KV head g, sequence b). Wave w
-// computes the 16-column blocks w, w+4, ... of C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d]
-// (16x16x32 bf16, A = up to 16 query heads of the group, B = Bk^T; C row h = 4*lg + i, column
-// k = lane % 16). F16 (int4 latents): each head's row is scaled by the power of two 2^-e that
-// puts its largest magnitude in [2^14, 2^15), written as fp16 at the dequantised tiles' block
-// order, and 2^e is stored for the decode kernel to undo on the scores.
+// Fold on the matrix cores for bf16 q and Bk: one wave per (16-column block of latent indices k,
+// KV head g, sequence b). C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d] over d = 128 in four
+// 16x16x32 bf16 steps (A = 16 query heads of the group, zero past grp; B = Bk^T; C row
+// h = 4*lg + i, column k = lane % 16), scaled by sm_scale * log2 e.
+// F32OUT (int4 latents): float32 output at the dequantised tiles' block order; the decode
+// kernel picks each head's power-of-two scale and rounds to fp16. Else bf16 output.
 // ---------------------------------------------------------------------------------------------
-constexpr int kFoldMaxBlk = 512 / 16 / 4;   // column blocks per wave at rank 512
-
-template <bool F16>
+template <bool F32OUT>
 __global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q, const __bf16* __restrict__ bk,
-                                                    unsigned short* __restrict__ qt, float* __restrict__ qexp,
-                                                    int Hq, int Hkv, int D, int rk, int rk_pad, float scale) {
-  __shared__ float red[4][16];
-  const int g = blockIdx.x, b = blockIdx.y;
+                                                    void* __restrict__ qt, int Hq, int Hkv, int D, int rk,
+                                                    int rk_pad, float scale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 4, li = lane & 15;
+  const int blk = blockIdx.x * 4 + wave;
+  const int g = blockIdx.y, b = blockIdx.z;
   const int grp = Hq / Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, li = lane & 15;
-  const int nblk = rk_pad >> 4;
+  if (blk >= (rk_pad >> 4)) return;
+  const int k = blk * 16 + li;
+  bf16x8 bop[4];
+  {
+    const __bf16* brow = bk + (size_t)k * D + g * kFoldD + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bop[ks] = k < rk ? *(const bf16x8*)(brow + ks * 32) : zero_bf16x8();
+  }
+  const int pos = F32OUT ? i4_pos(k) : k;
   for (int h0 = 0; h0 < grp; h0 += 16) {
+    const int hl = h0 + li;
+    const __bf16* qrow = q + ((size_t)b * Hq + g * grp + hl) * kFoldD + lg * 8;
     bf16x8 aop[4];
-    {
-      const int hl = h0 + li;
-      const __bf16* qrow = q + ((size_t)b * Hq + g * grp + hl) * kFoldD + lg * 8;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) aop[ks] = hl < grp ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
-    }
-    f32x4 c[kFoldMaxBlk];
-    float mx[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < 4; ++ks) aop[ks] = hl < grp ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < kFoldMaxBlk; ++u) {
-      c[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int blk = wave + 4 * u;
-      if (blk < nblk) {
-        const int k = blk * 16 + li;
-        bf16x8 bop[4];
-        const __bf16* brow = bk + (size_t)k * D + g * kFoldD + lg * 8;
+    for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ks], bop[ks], c, 0, 0, 0);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) bop[ks] = k < rk ? *(const bf16x8*)(brow + ks * 32) : zero_bf16x8();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ks], bop[ks], c[u], 0, 0, 0);
-        c[u] *= scale;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], fabsf(c[u][i]));
-      }
-    }
-    float fac[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (F16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        for (int o = 1; o < 16; o <<= 1) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o));
-      if (li == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][4 * lg + i] = mx[i];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * lg + i;
-        const float m = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
-        int e = 0;
-        if (m > 0.f && m <= 3.4e38f) {
-          e = ilogbf(m) - 14;
-          e = e < -100 ? -100 : (e > 100 ? 100 : e);
-        }
-        fac[i] = ldexpf(1.f, -e);
-        if (wave == 0 && li == 0 && h0 + h < grp) qexp[(size_t)b * kHeadsPad + g * grp + h0 + h] = ldexpf(1.f, e);
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int u = 0; u < kFoldMaxBlk; ++u) {
-      const int blk = wave + 4 * u;
-      if (blk < nblk) {
-        const int k = blk * 16 + li;
-        const int pos = F16 ? i4_pos(k) : k;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = h0 + 4 * lg + i;
-          if (h < grp) {
-            const float v = c[u][i] * fac[i];
-            const unsigned short bits = F16 ? __builtin_bit_cast(unsigned short, (_Float16)v)
-                                            : __builtin_bit_cast(unsigned short, (__bf16)v);
-            qt[((size_t)b * kHeadsPad + g * grp + h) * rk_pad + pos] = bits;
-          }
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int h = h0 + 4 * lg + i;
+      if (h < grp) {
+        const size_t o = ((size_t)b * kHeadsPad + g * grp + h) * rk_pad + pos;
+        if constexpr (F32OUT) ((float*)qt)[o] = c[i] * scale;
+        else ((__bf16*)qt)[o] = (__bf16)(c[i] * scale);
       }
     }
   }
-  if (g == 0) {   // query heads past Hq: zero rows, unit scale
-    for (int i = tid; i < (kHeadsPad - Hq) * rk_pad; i += 256)
-      qt[((size_t)b * kHeadsPad + Hq) * rk_pad + i] = 0;
-    if (F16)
-      for (int h = Hq + tid; h < kHeadsPad; h += 256) qexp[(size_t)b * kHeadsPad + h] = 1.f;
+  if (g == 0) {   // query heads past Hq: zero rows
+    for (int h = Hq + lg; h < kHeadsPad; h += 4) {
+      const size_t o = ((size_t)b * kHeadsPad + h) * rk_pad + k;
+      if constexpr (F32OUT) ((float*)qt)[o] = 0.f;
+      else ((__bf16*)qt)[o] = (__bf16)0.f;
+    }
   }
 }
 
@@ -1014,9 +1030,9 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
 // ---------------------------------------------------------------------------------------------
 // Host launch
 // ---------------------------------------------------------------------------------------------
-// ev_begin/ev_end (optional) are attached to the kernel's own dispatch, so they bracket exactly
-// its execution (no separate marker packets in the stream).
-template <int KS, int RB, int LT, int G>
+// ev_begin/ev_end (optional) are attached to the kernel's own dispatch (hipExtLaunchKernel),
+// so no separate marker packets enter the stream.
+template <int KS, int RB, int LT, int G, bool SP>
 static hipError_t launch_decode_kernel(const DecodeArgs& args, int grid, int lds, hipStream_t st,
                                        hipEvent_t ev_begin, hipEvent_t ev_end) {
   static bool attr_set[64] = {false};
@@ -1024,33 +1040,31 @@ static hipError_t launch_decode_kernel(const DecodeArgs& args, int grid, int lds
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    e = hipFuncSetAttribute((const void*)lr_decode<KS, RB, LT, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kLdsBytes);
+    e = hipFuncSetAttribute((const void*)lr_decode<KS, RB, LT, G, SP>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
   if (ev_begin || ev_end)
-    hipExtLaunchKernelGGL((lr_decode<KS, RB, LT, G>), dim3(grid), dim3(decode_threads(G)), lds, st, ev_begin, ev_end,
-                          0, args);
+    hipExtLaunchKernelGGL((lr_decode<KS, RB, LT, G, SP>), dim3(grid), dim3(decode_threads(G)), lds, st, ev_begin,
+                          ev_end, 0, args);
   else
-    hipLaunchKernelGGL((lr_decode<KS, RB, LT, G>), dim3(grid), dim3(decode_threads(G)), lds, st, args);
+    hipLaunchKernelGGL((lr_decode<KS, RB, LT, G, SP>), dim3(grid), dim3(decode_threads(G)), lds, st, args);
   return hipGetLastError();
 }
 
+// One instantiation per (KS, RB) bound of the latent dtype; the consumer layout and group count
+// follow from the bounds (decode_split / decode_groups).
 template <int LT>
 static hipError_t dispatch_decode(const DecodePlan& p, const DecodeArgs& args, int grid, hipStream_t st,
                                   hipEvent_t ev_begin, hipEvent_t ev_end) {
+  constexpr int LAT = LT == LT_I4 ? LR_I4G32 : (LT == LT_F32 ? LR_F32 : LR_BF16);
   const int ks = decode_ks(p.nks);
   const int rb = decode_rb(p.nrb);
-  const int g = decode_groups(ks, rb);
-#define LR_CASE(K, R)                                                                    \
-  if (ks == K && rb == R) {                                                             \
-    if constexpr (LT != LT_I4 && decode_groups(K, R) == 2)                                \
-      return launch_decode_kernel<K, R, LT, 2>(args, grid, p.lds_bytes, st, ev_begin, ev_end);              \
-    else                                                                                  \
-      return launch_decode_kernel<K, R, LT, 1>(args, grid, p.lds_bytes, st, ev_begin, ev_end);              \
-  }
-  (void)g;
+#define LR_CASE(K, R)                                                                                     \
+  if (ks == K && rb == R)                                                                                \
+    return launch_decode_kernel<K, R, LT, decode_groups(LAT, K, R), decode_split(LAT, K, R)>(           \
+        args, grid, p.lds_bytes, st, ev_begin, ev_end);
   LR_CASE(8, 8) LR_CASE(8, 12) LR_CASE(8, 16)
   LR_CASE(12, 8) LR_CASE(12, 12) LR_CASE(12, 16)
   LR_CASE(16, 8) LR_CASE(16, 12) LR_CASE(16, 16)
@@ -1071,12 +1085,13 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
       hipLaunchKernelGGL(lr_fold<float>, grid, dim3(256), 0, st, (const float*)q, (const float*)c->bk, qt,
                          p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
     else if (p.latent == LR_I4G32)
-      hipLaunchKernelGGL(lr_fold_mfma<true>, dim3(p.Hkv, p.B), dim3(256), 0, st, (const __bf16*)q,
-                         (const __bf16*)c->bk, (unsigned short*)qt, (float*)(w + p.off_qexp), p.Hq, p.Hkv, p.D,
-                         p.rk, p.rk_pad, scale);
+      hipLaunchKernelGGL(lr_fold_mfma<true>, dim3((p.rk_pad / 16 + 3) / 4, p.Hkv, p.B), dim3(256), 0, st,
+                         (const __bf16*)q, (const __bf16*)c->bk, (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad,
+                         scale);
     else
-      hipLaunchKernelGGL(lr_fold<__bf16>, grid, dim3(256), 0, st, (const __bf16*)q, (const __bf16*)c->bk, qt,
-                         p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
+      hipLaunchKernelGGL(lr_fold_mfma<false>, dim3((p.rk_pad / 16 + 3) / 4, p.Hkv, p.B), dim3(256), 0, st,
+                         (const __bf16*)q, (const __bf16*)c->bk, (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad,
+                         scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1124,12 +1139,11 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.nst = p.nst;
   a.copy_k = p.copy_k;
   a.copy_v = p.copy_v;
-  a.qexp = (const float*)(w + p.off_qexp);
   a.nr = p.nr;
   a.raw_stage = p.raw_stage;
   const int grid = a.n_win_blocks + p.B * p.nsplit;
   hipError_t e;
-  if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
+  if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2, false>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
   else if (p.latent == LR_I4G32) e = dispatch_decode<LT_I4>(p, a, grid, st, ev_begin, ev_end);
   else e = dispatch_decode<LT_BF16>(p, a, grid, st, ev_begin, ev_end);
   if (e != hipSuccess) return e;

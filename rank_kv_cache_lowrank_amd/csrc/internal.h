@@ -33,9 +33,25 @@ constexpr int lds_stride_v(int RB, int es) { return RB * 32 * es + 32; }
 constexpr int lds_stage(int KS, int RB, int es) {
   return kTileTokens * (lds_stride_k(KS, es) + lds_stride_v(RB, es));
 }
-// Consumer groups (4 waves each) of the decode workgroup, beside the 4 producer waves: two when
-// their registers allow three waves per SIMD (12 waves), else one.
-constexpr int decode_groups(int KS, int RB) { return (KS <= 8 && RB <= 12) ? 2 : 1; }
+// Consumer layout of the decode workgroup (beside the 4 producer waves), chosen where the
+// registers fit:
+//   split: each consumer wave owns one 16-head block for every other tile of its group and
+//          accumulates all value blocks (bf16 latents, value rank <= 384);
+//   half:  the two waves of a head block share each tile and split the value blocks.
+// (split needs up to 256 registers per consumer wave: one group; the narrowest rows keep two
+// groups of halves instead, which fit three waves per SIMD.)
+constexpr bool decode_split(int latent, int KS, int RB) {
+  return latent == LR_BF16 && !(KS <= 8 && RB <= 8) && ((KS <= 12 && RB <= 12) || (KS == 16 && RB == 8));
+}
+constexpr int decode_groups(int latent, int KS, int RB) {
+  return latent == LR_I4G32 ? 1
+       : latent == LR_F32   ? 2
+       : (KS <= 8 && RB <= 8) ? 2 : 1;
+}
+// Tiles each iteration of the decode loop consumes (one workgroup barrier per iteration).
+constexpr int decode_tpi(int latent, int KS, int RB) {
+  return decode_groups(latent, KS, RB) * (decode_split(latent, KS, RB) ? 2 : 1);
+}
 // int4 latents: raw stages (16 rows of codes and scale/zero words, as stored) for the
 // direct-to-LDS loads, dequantised into two fp16 stages of the geometry above.
 constexpr int kI4DeqStages = 2;
@@ -63,7 +79,7 @@ struct DecodePlan {
   int copy_k, copy_v;               // bytes of each stored row the ring holds
   int nr, raw_stage;                // int4: raw (codes + scale/zero) stages and their bytes
   int lds_bytes;                    // dynamic LDS of the decode kernel
-  size_t off_qt, off_ml, off_acc, off_win, off_qexp, ws_bytes;
+  size_t off_qt, off_ml, off_acc, off_win, ws_bytes;
 };
 
 // Fills *p; returns LR_OK or an error code with a message in *msg.
