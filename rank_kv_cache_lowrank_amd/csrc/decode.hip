@@ -291,45 +291,54 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
 // KS: compile-time bound on K steps of 32; RB: bound on value blocks of a half.
 // ---------------------------------------------------------------------------------------------
 constexpr int kProducers = 4;           // waves that only move data (direct-to-LDS loads)
-// int4: dequantisation items (half groups) per producer lane and tile at rank 512
-constexpr int kI4MaxItems = (kTileTokens * 2 * 32 + kProducers * 64 - 1) / (kProducers * 64);
 constexpr int kMaxChunkPerProducer = 5; // 1 KB DMA chunks per producer per matrix and tile
 constexpr float kRescaleSlack = 8.f;    // base-2 headroom before the running reference max moves
 
-// Threads of the decode workgroup for G consumer groups.
-constexpr int decode_threads(int G) { return 64 * (4 * G + kProducers); }
+// Threads of the decode workgroup for G consumer groups (int4: plus its dequantisation waves).
+constexpr int decode_threads(int G, int LT) { return 64 * (4 * G + kProducers + (LT == LT_I4 ? 4 : 0)); }
 
 // ---------------------------------------------------------------------------------------------
-// int4 producer waves. A tile's stored bytes (16 rows of codes and of scale/zero words, for Zk
-// then Zv) are four contiguous runs in HBM, copied by 1 KB direct-to-LDS chunks into raw stage
-// t % nr. One tile later the producers dequantise it into fp16 stage t % 2, which the consumers
-// read with the bf16 geometry. Per iteration (one workgroup barrier):
-//   issue raw tile it + nr (its stage held tile it, dequantised before this barrier),
-//   dequantise tile it + 1 (landed before this barrier) into the stage tile it - 1 used,
-//   wait for tile it + 2.
+// int4 latents: three roles of 4 waves each, one workgroup barrier per 16-token tile.
+//   DMA waves      copy a tile's stored bytes (16 rows of codes and of scale/zero words, for Zk
+//                  then Zv: four contiguous runs in HBM) by 1 KB direct-to-LDS chunks into raw
+//                  stage t % nr; per iteration they issue tile it + nr (its stage held tile it,
+//                  dequantised before this barrier) and wait for tile it + 2.
+//   dequant waves  turn raw tile it + 1 (landed before this barrier) into fp16 stage
+//                  (it + 1) % 2 with the bf16 tile geometry (consumers finished tile it - 1
+//                  there before this barrier). One item = one dword of codes (8 latent
+//                  indices) -> 16 bytes of fp16, so consecutive lanes write consecutive bytes.
+//   consumers      as for bf16, on fp16 stage it % 2.
 // ---------------------------------------------------------------------------------------------
+constexpr int kI4DequantWaves = 4;
+// dequantisation items (8 codes each) per dequant lane and tile at rank 512
+constexpr int kI4MaxItems = (kTileTokens * 2 * 64 + kI4DequantWaves * 64 - 1) / (kI4DequantWaves * 64);
+
+struct I4Raw {      // byte offsets of the four runs inside a raw stage, and the stage size
+  int cbk, qbk, cbv, qbv, o_qk, o_cv, o_qv, rs;
+  __device__ I4Raw(const DecodeArgs& a)
+      : cbk(a.row_bytes_k), qbk(a.qp_bytes_k), cbv(a.row_bytes_v), qbv(a.qp_bytes_v),
+        o_qk(kTileTokens * a.row_bytes_k), o_cv(o_qk + kTileTokens * a.qp_bytes_k),
+        o_qv(o_cv + kTileTokens * a.row_bytes_v), rs(a.raw_stage) {}
+};
+
 template <int KS, int RB>
-__device__ __forceinline__ void producer_i4(const DecodeArgs& a, unsigned char* smem, int b, int t_begin,
-                                            int t_end, int ntiles, int pw) {
-  constexpr int SK = lds_stride_k(KS, 2);
-  constexpr int SV = lds_stride_v(RB, 2);
-  constexpr int ZV = kTileTokens * SK;
+__device__ __forceinline__ void i4_dma(const DecodeArgs& a, unsigned char* smem, int b, int t_begin, int t_end,
+                                       int ntiles, int pw) {
   constexpr int STAGE = lds_stage(KS, RB, 2);
   const int lane = threadIdx.x & 63;
   unsigned char* raw = smem + kI4DeqStages * STAGE;
-  const int cbk = a.row_bytes_k, qbk = a.qp_bytes_k, cbv = a.row_bytes_v, qbv = a.qp_bytes_v;
-  const int o_qk = kTileTokens * cbk;
-  const int o_cv = o_qk + kTileTokens * qbk;
-  const int o_qv = o_cv + kTileTokens * cbv;
-  const int rs = a.raw_stage, NR = a.nr;
+  const I4Raw R(a);
+  const int NR = a.nr;
   const size_t row0 = (size_t)b * a.t_cap + t_begin;
-  const unsigned char* gck = a.zk + row0 * cbk;
-  const unsigned char* gqk = a.zkq + row0 * qbk;
-  const unsigned char* gcv = a.zv + row0 * cbv;
-  const unsigned char* gqv = a.zvq + row0 * qbv;
+  const unsigned char* gck = a.zk + row0 * R.cbk;
+  const unsigned char* gqk = a.zkq + row0 * R.qbk;
+  const unsigned char* gcv = a.zv + row0 * R.cbv;
+  const unsigned char* gqv = a.zvq + row0 * R.qbv;
 
   auto nch = [](int bytes) { return (bytes + 1023) >> 10; };
-  auto tile_chunks = [&](int rows) { return nch(rows * cbk) + nch(rows * qbk) + nch(rows * cbv) + nch(rows * qbv); };
+  auto tile_chunks = [&](int rows) {
+    return nch(rows * R.cbk) + nch(rows * R.qbk) + nch(rows * R.cbv) + nch(rows * R.qbv);
+  };
   auto pcnt = [&](int n) { return n > pw ? (n - pw + kProducers - 1) / kProducers : 0; };
   const int rows_last = ntiles > 0 ? t_end - (t_begin + (ntiles - 1) * kTileTokens) : 0;
   const int cnt_full = pcnt(tile_chunks(kTileTokens));
@@ -339,7 +348,7 @@ __device__ __forceinline__ void producer_i4(const DecodeArgs& a, unsigned char* 
     return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
   };
   auto issue = [&](int t) {
-    unsigned char* st = raw + (t % NR) * rs;
+    unsigned char* st = raw + (t % NR) * R.rs;
     const int t0 = t * kTileTokens;
     const int rows = min(kTileTokens, t_end - t_begin - t0);
     int gc0 = 0;                         // first chunk of the run in the tile's chunk list
@@ -351,46 +360,67 @@ __device__ __forceinline__ void producer_i4(const DecodeArgs& a, unsigned char* 
       }
       gc0 += n;
     };
-    run(gck + (size_t)t0 * cbk, st, rows * cbk);
-    run(gqk + (size_t)t0 * qbk, st + o_qk, rows * qbk);
-    run(gcv + (size_t)t0 * cbv, st + o_cv, rows * cbv);
-    run(gqv + (size_t)t0 * qbv, st + o_qv, rows * qbv);
+    run(gck + (size_t)t0 * R.cbk, st, rows * R.cbk);
+    run(gqk + (size_t)t0 * R.qbk, st + R.o_qk, rows * R.qbk);
+    run(gcv + (size_t)t0 * R.cbv, st + R.o_cv, rows * R.cbv);
+    run(gqv + (size_t)t0 * R.qbv, st + R.o_qv, rows * R.qbv);
   };
 
-  // Dequantisation: one item = half a group (16 codes) of one row; a tile has 16 * (hk + hv)
-  // items, item i = lane + 256 u of the producers. The stage offsets of each lane's items are
-  // the same for every tile, so they are computed once.
-  const int hk = 2 * (cbk >> 4), hv = 2 * (cbv >> 4);              // items per row
-  const int pl = pw * 64 + lane;
+  const int pro = min(NR, ntiles);
+  for (int t = 0; t < pro; ++t) issue(t);
+  wait_vmcnt(count(0, pro - 1));
+  barrier_lds();                                     // raw tile 0 visible to the dequant waves
+  wait_vmcnt(count(1, pro - 1));
+  for (int it = 0; it < ntiles; ++it) {
+    barrier_lds();                                   // raw tile it + 1 visible
+    if (it + NR < ntiles) issue(it + NR);
+    wait_vmcnt(count(it + 2, min(it + NR, ntiles - 1)));
+  }
+}
+
+template <int KS, int RB>
+__device__ __forceinline__ void i4_dequant(const DecodeArgs& a, unsigned char* smem, int t_begin, int t_end,
+                                           int ntiles, int dw) {
+  constexpr int SK = lds_stride_k(KS, 2);
+  constexpr int SV = lds_stride_v(RB, 2);
+  constexpr int ZV = kTileTokens * SK;
+  constexpr int STAGE = lds_stage(KS, RB, 2);
+  const int lane = threadIdx.x & 63;
+  unsigned char* raw = smem + kI4DeqStages * STAGE;
+  const I4Raw R(a);
+  const int NR = a.nr;
+  // Item i (one dword of codes of one row) of a tile, i = lane + 256 u of the dequant waves;
+  // its stage offsets are the same for every tile, so they are computed once.
+  const int dk = R.cbk >> 2, dv = R.cbv >> 2;        // code dwords per row
+  const int pl = dw * 64 + lane;
   int i_src[kI4MaxItems], i_qp[kI4MaxItems], i_dst[kI4MaxItems], i_row[kI4MaxItems];
 #pragma unroll
   for (int u = 0; u < kI4MaxItems; ++u) {
-    const int i = pl + u * kProducers * 64;
+    const int i = pl + u * kI4DequantWaves * 64;
     i_row[u] = kTileTokens;                          // no item
     i_src[u] = i_qp[u] = i_dst[u] = 0;
-    if (i < kTileTokens * (hk + hv)) {
-      const bool isk = i < kTileTokens * hk;
-      const int j = isk ? i : i - kTileTokens * hk;
-      const int h = isk ? hk : hv;
-      const int row = j / h, part = j - row * h;     // part = 2 * group + half
+    if (i < kTileTokens * (dk + dv)) {
+      const bool isk = i < kTileTokens * dk;
+      const int j = isk ? i : i - kTileTokens * dk;
+      const int h = isk ? dk : dv;
+      const int row = j / h, word = j - row * h;    // word = 4 * group + quarter
       i_row[u] = row;
-      i_src[u] = (isk ? row * cbk : o_cv + row * cbv) + part * 8;
-      i_qp[u] = (isk ? o_qk + row * qbk : o_qv + row * qbv) + (part >> 1) * 4;
-      i_dst[u] = (isk ? row * SK : ZV + row * SV) + part * 32;
+      i_src[u] = (isk ? row * R.cbk : R.o_cv + row * R.cbv) + word * 4;
+      i_qp[u] = (isk ? R.o_qk + row * R.qbk : R.o_qv + row * R.qbv) + (word >> 2) * 4;
+      i_dst[u] = (isk ? row * SK : ZV + row * SV) + word * 16;
     }
   }
   unsigned kMask = 0x000F000Fu, kMagic = 0x64006400u;
   asm volatile("" : "+v"(kMask), "+v"(kMagic));
   auto dequant = [&](int t) {
-    const unsigned char* st = raw + (t % NR) * rs;
+    const unsigned char* st = raw + (t % NR) * R.rs;
     unsigned char* dq = smem + (t % kI4DeqStages) * STAGE;
     const int rows = min(kTileTokens, t_end - t_begin - t * kTileTokens);
-    u32x2 w[kI4MaxItems];
-    unsigned qp[kI4MaxItems];
+    unsigned w[kI4MaxItems], qp[kI4MaxItems];
 #pragma unroll
     for (int u = 0; u < kI4MaxItems; ++u) {          // all reads first, one wait
       if (i_row[u] < rows) {
-        w[u] = *(const u32x2*)(st + i_src[u]);
+        w[u] = *(const unsigned*)(st + i_src[u]);
         qp[u] = *(const unsigned*)(st + i_qp[u]);
       }
     }
@@ -399,29 +429,22 @@ __device__ __forceinline__ void producer_i4(const DecodeArgs& a, unsigned char* 
       if (i_row[u] < rows) {
         const f16x2 s2 = __builtin_bit_cast(f16x2, (qp[u] & 0xFFFFu) * 0x10001u);
         const f16x2 z2 = __builtin_bit_cast(f16x2, (qp[u] >> 16) * 0x10001u);
-        *(u32x4*)(dq + i_dst[u]) = dequant8_f16(w[u][0], s2, z2, kMask, kMagic);
-        *(u32x4*)(dq + i_dst[u] + 16) = dequant8_f16(w[u][1], s2, z2, kMask, kMagic);
+        *(u32x4*)(dq + i_dst[u]) = dequant8_f16(w[u], s2, z2, kMask, kMagic);
       }
     }
   };
 
-  const int pro = min(NR, ntiles);
-  for (int t = 0; t < pro; ++t) issue(t);
-  wait_vmcnt(count(0, pro - 1));
-  barrier_lds();                                     // raw tile 0 visible to every producer
+  barrier_lds();                                     // raw tile 0 visible
   if (ntiles > 0) dequant(0);
-  wait_vmcnt(count(1, pro - 1));
   for (int it = 0; it < ntiles; ++it) {
     barrier_lds();                                   // fp16 tile it visible; raw tile it + 1 landed
-    if (it + NR < ntiles) issue(it + NR);
     if (it + 1 < ntiles) dequant(it + 1);
-    wait_vmcnt(count(it + 2, min(it + NR, ntiles - 1)));
   }
 }
 
 template <int KS, int RB, int LT, int G, bool SP>
 __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char* smem, int wg) {
-  constexpr int NTHR = decode_threads(G);
+  constexpr int NTHR = decode_threads(G, LT);
   constexpr bool I4 = LT == LT_I4;
   constexpr int ES = LT == LT_F32 ? 4 : 2;             // bytes per latent element in the LDS tile
   constexpr int SK = lds_stride_k(KS, ES);             // LDS row strides (bytes)
@@ -461,7 +484,9 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   for (int j = 0; j < NVB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (I4 && producer) {
-    producer_i4<KS, RB>(a, smem, b, t_begin, t_end, ntiles, wave - 4 * G);
+    static_assert(kI4DequantWaves == kProducers, "int4 role split");
+    if (wave < 4 * G + kProducers) i4_dma<KS, RB>(a, smem, b, t_begin, t_end, ntiles, wave - 4 * G);
+    else i4_dequant<KS, RB>(a, smem, t_begin, t_end, ntiles, wave - 4 * G - kProducers);
   } else if (producer) {
     // ---------------- producer waves: keep the ring full ----------------
     const int pw = wave - 4 * G;
@@ -765,10 +790,10 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
 }
 
 template <int KS, int RB, int LT, int G, bool SP>
-__global__ __launch_bounds__(decode_threads(G)) void lr_decode(DecodeArgs a) {
+__global__ __launch_bounds__(decode_threads(G, LT)) void lr_decode(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   if ((int)blockIdx.x < a.n_win_blocks) {
-    window_block<LT, decode_threads(G)>(a, smem);
+    window_block<LT, decode_threads(G, LT)>(a, smem);
     return;
   }
   latent_block<KS, RB, LT, G, SP>(a, smem, (int)blockIdx.x - a.n_win_blocks);
@@ -1046,10 +1071,10 @@ static hipError_t launch_decode_kernel(const DecodeArgs& args, int grid, int lds
     attr_set[dev] = true;
   }
   if (ev_begin || ev_end)
-    hipExtLaunchKernelGGL((lr_decode<KS, RB, LT, G, SP>), dim3(grid), dim3(decode_threads(G)), lds, st, ev_begin,
+    hipExtLaunchKernelGGL((lr_decode<KS, RB, LT, G, SP>), dim3(grid), dim3(decode_threads(G, LT)), lds, st, ev_begin,
                           ev_end, 0, args);
   else
-    hipLaunchKernelGGL((lr_decode<KS, RB, LT, G, SP>), dim3(grid), dim3(decode_threads(G)), lds, st, args);
+    hipLaunchKernelGGL((lr_decode<KS, RB, LT, G, SP>), dim3(grid), dim3(decode_threads(G, LT)), lds, st, args);
   return hipGetLastError();
 }
 
