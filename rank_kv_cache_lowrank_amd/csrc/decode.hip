@@ -473,10 +473,30 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   const int niter = (ntiles + TPI - 1) / TPI;
 
   unsigned char* ring = smem;
-  // Zero the ring once: LDS columns past the copied part of a row (K steps and value blocks
-  // beyond the rank, row padding) then read as exact zeros for the whole workgroup.
-  for (int i = tid; i < NST * STAGE / 16; i += NTHR) *(u32x4*)(ring + i * 16) = u32x4{0u, 0u, 0u, 0u};
-  barrier_lds();
+  // Zero, once, the LDS columns of every stage row that no copy (or dequantisation) writes: the
+  // K steps and value blocks past the rank then read as exact zeros for the whole workgroup.
+  // These bytes are disjoint from everything the producers write, so no barrier is needed here:
+  // the first loop barrier orders them before any consumer read.
+  {
+    constexpr int KB = KS * 32 * ES, VB = RB * 32 * ES;        // bytes of a row the operands read
+    const int ck = I4 ? a.nks * 64 : a.copy_k;                  // bytes written per K / V row
+    const int cv = I4 ? ((a.rv + 31) / 32) * 64 : a.copy_v;
+    const int npk = (KB - ck) >> 4, npv = (VB - cv) >> 4;       // 16-byte granules to clear
+    const int per_stage = kTileTokens * (npk + npv);
+    for (int i = tid; i < NST * per_stage; i += NTHR) {
+      const int st = i / per_stage, j = i - st * per_stage;
+      unsigned char* p;
+      if (j < kTileTokens * npk) {
+        const int row = j / npk, gk = j - row * npk;
+        p = ring + st * STAGE + row * SK + ck + gk * 16;
+      } else {
+        const int jj = j - kTileTokens * npk;
+        const int row = jj / npv, gv = jj - row * npv;
+        p = ring + st * STAGE + ZV + row * SV + cv + gv * 16;
+      }
+      *(u32x4*)p = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 acc[NVB];
