@@ -390,21 +390,25 @@ __device__ __forceinline__ void i4_dequant(const DecodeArgs& a, unsigned char* s
   const I4Raw R(a);
   const int NR = a.nr;
   // Item i (one dword of codes of one row) of a tile, i = lane + 256 u of the dequant waves;
-  // its stage offsets are the same for every tile, so they are computed once.
+  // its stage offsets are the same for every tile, so they are computed once. Every item of
+  // the tile's 16 rows is converted, also for a final partial tile (its stale rows are masked
+  // by the consumers), and lanes past the last item write into the never-read 16-byte pad of
+  // row 0, so the loop has no per-lane branch and the items' instruction chains interleave.
   const int dk = R.cbk >> 2, dv = R.cbv >> 2;        // code dwords per row
+  const int nitems = kTileTokens * (dk + dv);
+  const int nu = (nitems + kI4DequantWaves * 64 - 1) / (kI4DequantWaves * 64);   // wave-uniform
   const int pl = dw * 64 + lane;
-  int i_src[kI4MaxItems], i_qp[kI4MaxItems], i_dst[kI4MaxItems], i_row[kI4MaxItems];
+  int i_src[kI4MaxItems], i_qp[kI4MaxItems], i_dst[kI4MaxItems];
 #pragma unroll
   for (int u = 0; u < kI4MaxItems; ++u) {
     const int i = pl + u * kI4DequantWaves * 64;
-    i_row[u] = kTileTokens;                          // no item
-    i_src[u] = i_qp[u] = i_dst[u] = 0;
-    if (i < kTileTokens * (dk + dv)) {
+    i_src[u] = i_qp[u] = 0;
+    i_dst[u] = SK - 16;                              // pad bytes past the K operand's reach
+    if (i < nitems) {
       const bool isk = i < kTileTokens * dk;
       const int j = isk ? i : i - kTileTokens * dk;
       const int h = isk ? dk : dv;
       const int row = j / h, word = j - row * h;    // word = 4 * group + quarter
-      i_row[u] = row;
       i_src[u] = (isk ? row * R.cbk : R.o_cv + row * R.cbv) + word * 4;
       i_qp[u] = (isk ? R.o_qk + row * R.qbk : R.o_qv + row * R.qbv) + (word >> 2) * 4;
       i_dst[u] = (isk ? row * SK : ZV + row * SV) + word * 16;
@@ -415,18 +419,17 @@ __device__ __forceinline__ void i4_dequant(const DecodeArgs& a, unsigned char* s
   auto dequant = [&](int t) {
     const unsigned char* st = raw + (t % NR) * R.rs;
     unsigned char* dq = smem + (t % kI4DeqStages) * STAGE;
-    const int rows = min(kTileTokens, t_end - t_begin - t * kTileTokens);
     unsigned w[kI4MaxItems], qp[kI4MaxItems];
 #pragma unroll
     for (int u = 0; u < kI4MaxItems; ++u) {          // all reads first, one wait
-      if (i_row[u] < rows) {
+      if (u < nu) {
         w[u] = *(const unsigned*)(st + i_src[u]);
         qp[u] = *(const unsigned*)(st + i_qp[u]);
       }
     }
 #pragma unroll
     for (int u = 0; u < kI4MaxItems; ++u) {
-      if (i_row[u] < rows) {
+      if (u < nu) {
         const f16x2 s2 = __builtin_bit_cast(f16x2, (qp[u] & 0xFFFFu) * 0x10001u);
         const f16x2 z2 = __builtin_bit_cast(f16x2, (qp[u] >> 16) * 0x10001u);
         *(u32x4*)(dq + i_dst[u]) = dequant8_f16(w[u], s2, z2, kMask, kMagic);
