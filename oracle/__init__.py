@@ -21,6 +21,7 @@ Modules
 ``attention``  D1 reconstruct-then-attend, D2 latent-domain, D3 pure-Python brute force.
 ``quant``      int4 groups-of-32 min-max quantiser, nibble packing, exact dequantiser.
 ``append``     the append state machine: exact window ring, eviction, projection, storage.
+``rebase``     historical-coordinate sync after a basis update (least-squares coordinates).
 
 Every function works in float64 unless the step it models fixes a narrower
 precision (the quantiser's float32/float16 steps, storage rounding).
