@@ -57,6 +57,12 @@ class HipEvents:
     def destroy(self, e: int) -> None:
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
+    def record(self, e: int, stream: int) -> None:
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
 
 def latent_bytes_per_token(latent: str, rank: int) -> int:
     if latent == "bf16":
@@ -153,6 +159,93 @@ def measured_traffic(workload: str):
     return int(entry["hbm_bytes_per_launch"])
 
 
+def rebase_bench(args):
+    """Historical-coordinate sync of a whole layer cache (every stored K and V row re-expressed
+    in an updated basis), timed per call. One call = one launch of lr_rebase_bf16 over K and V.
+    Algorithmic bytes: each row's old coordinates read once and new coordinates written once."""
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+    import synth
+
+    dev = "cuda"
+    cfg = synth.CONFIGS[args.config]
+    if cfg.n_layers != 1 or cfg.latent != "bf16":
+        raise SystemExit("--op rebase times single-layer bf16 configurations (1 or 2)")
+    K, W = args.steps, args.warmup
+    B, T = cfg.batch, cfg.seq_len
+    rk, rv = synth.layer_ranks(cfg, 0)
+    rk2 = args.rank_new or rk
+    rv2 = args.rank_new or rv
+    log(f"generating inputs for {cfg.name} ...")
+    li = synth.make_layer(cfg, t_cap=T, lat_len=np.full(B, T, np.int32))
+    bk, bv = li.bk.double().numpy(), li.bv.double().numpy()
+    wk = synth.w_storage(synth.sync_projection(bk, synth.gen_basis_update(cfg, "k", 0, bk, rk2)), "bf16").to(dev)
+    wv = synth.w_storage(synth.sync_projection(bv, synth.gen_basis_update(cfg, "v", 0, bv, rv2)), "bf16").to(dev)
+    model = lr.Model(1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, [rk], [rv], cfg.sm_scale, 0, "bf16")
+    lat = torch.full((B,), T, dtype=torch.int32, device=dev)
+    ldk2, ldv2 = synth.latent_ld(rk2), synth.latent_ld(rv2)
+    bytes_call = B * T * 2 * (rk + rk2 + rv + rv2)
+    # src and dst pairs rotated so that the pairs together exceed 2 x the 256 MB Infinity Cache
+    n_pairs = max(1, min(4, -(-(2 * 256 * 2**20) // bytes_call)))
+    pairs = []
+    for _ in range(n_pairs):
+        src = lr.Cache(li.zk.to(dev), li.zv.to(dev), None, None, lat, T, li.ld_k, li.ld_v)
+        dk = torch.empty(B, T, ldk2, dtype=torch.bfloat16, device=dev)
+        dv = torch.empty(B, T, ldv2, dtype=torch.bfloat16, device=dev)
+        pairs.append((src, lr.Cache(dk, dv, None, None, None, T, ldk2, ldv2)))
+    log(f"{n_pairs} src/dst pair(s) of {bytes_call / 1e6:.1f} MB moved per call")
+    ev = HipEvents()
+    evs = [(ev.create(), ev.create()) for _ in range(K)]
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for i in range(W + K):
+        if i == W:
+            torch.cuda.synchronize()
+            start.record()
+        src, dst = pairs[i % n_pairs]
+        if i >= W:
+            ev.record(evs[i - W][0], stream)
+        lr.lowrank_kv_rebase(model, 0, src, dst, T, rk2, rv2, wk, wv, stream=stream)
+        if i >= W:
+            ev.record(evs[i - W][1], stream)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_call = start.elapsed_time(stop) / K
+    kern_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in evs]))
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    assert torch.isfinite(pairs[0][1].zk[:, :, :rk2].float()).all(), "non-finite output"
+    value = bytes_call / (ms_per_call * 1e-3) / 1e9
+    achieved = bytes_call / (kern_ms * 1e-3) / 1e9
+    log(f"ms/call {ms_per_call:.4f}  kernel {kern_ms * 1e3:.2f} us  {value:.1f} GB/s  kernel {achieved:.1f} GB/s")
+    rec = {
+        "metric": "historical-coordinate sync of one layer cache: algorithmic HBM GB/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_call, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"rebase {cfg.name} r{rk}->r{rk2}", "batch": B, "seq_len": T,
+                   "rank_k": rk, "rank_v": rv, "rank_k_new": rk2, "rank_v_new": rv2,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "lr_rebase_bf16", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s",
+                     "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4), "traffic": None,
+                     "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": int(bytes_call),
+                     "mfma_tflops": round(2.0 * B * T * (rk * rk2 + rv * rv2) / (kern_ms * 1e-3) / 1e12, 1)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +258,9 @@ def main():
                     help="cache copies rotated over the steps (0: enough that the copies exceed 2 x 256 MB)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 256 MiB device copy (the counter calibration reference)")
+    ap.add_argument("--op", choices=("decode", "rebase"), default="decode",
+                    help="decode: the decode step (default); rebase: the historical-coordinate sync")
+    ap.add_argument("--rank-new", type=int, default=0, help="--op rebase: new rank (0: unchanged)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -177,6 +273,9 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench needs a GPU"
+    if args.op == "rebase":
+        rebase_bench(args)
+        return
     dev = "cuda"
     cfg = synth.CONFIGS[args.config]
     if cfg.n_layers != 1 or cfg.window:

@@ -191,6 +191,32 @@ int lowrank_kv_store(const lr_model_desc* model, int32_t layer, const lr_layer_c
 int lowrank_kv_dequant(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
                        int32_t batch, int64_t n_rows, float* zk_out, float* zv_out, void* stream);
 
+/*
+ * Historical-coordinate sync after a basis update (iS-KV, English abstract and method summary:
+ * as the low-rank basis evolves, the stored coordinates are synchronised with it, otherwise the
+ * history drifts). Every stored latent row z of rows [0, lat_len[b]) of src becomes its
+ * least-squares coordinates in the new basis B',
+ *     z' = z B pinv(B') = z W^T,
+ * written to the same row of dst in the cache dtype (bf16: round to nearest even).
+ *   wk [rank_k_new][round_up(rank_k, 8)], wv [rank_v_new][round_up(rank_v, 8)]: W = the
+ *     caller's (B pinv(B'))^T in the base dtype (float32 caches: float32, else bfloat16),
+ *     16-byte aligned; pad columns are ignored.
+ *   src: the cache with the current ranks (model->rank_k/rank_v[layer]); only zk, zv, ld_k,
+ *     ld_v, t_cap and lat_len (device, [batch]) are used, with the layout rules of decode.
+ *     dst: latent buffers for the new ranks (ld >= new rank, a multiple of 8, <= 4096;
+ *     t_cap >= max_lat_len); only zk, zv, ld_k, ld_v and t_cap are used. dst may be src itself (same buffers, strides and
+ *     t_cap) when the new coordinates of a row fit one workgroup's W staging (float32 always;
+ *     bf16: LR_EUNSUPPORTED otherwise); partially overlapping buffers are not allowed.
+ *   max_lat_len: host upper bound on lat_len[b] (sizes the grid).
+ * Rows past lat_len[b] and columns past the new rank of dst are not written. Lengths, window
+ * and bases are untouched: the caller switches the model to the new ranks and bases.
+ * int4 caches: LR_EUNSUPPORTED.
+ */
+int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_cache* src,
+                      const lr_layer_cache* dst, int32_t batch, int32_t max_lat_len,
+                      int32_t rank_k_new, int32_t rank_v_new, const void* wk, const void* wv,
+                      void* stream);
+
 /* Message for the last non-OK status returned on this host thread ("" if none). */
 const char* lowrank_last_error(void);
 

@@ -22,7 +22,8 @@ LR_F32, LR_BF16, LR_I4G32 = 0, 1, 2
 DTYPES = {"f32": LR_F32, "bf16": LR_BF16, "i4g32": LR_I4G32}
 
 EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_kv_append",
-           "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_last_error", "lowrank_abi_version")
+           "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_last_error",
+           "lowrank_abi_version")
 
 
 class LowRankError(RuntimeError):
@@ -76,6 +77,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowrank_kv_dequant.restype = c_int32
     lib.lowrank_kv_dequant.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                        c_int64, c_void_p, c_void_p, c_void_p]
+    lib.lowrank_kv_rebase.restype = c_int32
+    lib.lowrank_kv_rebase.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache),
+                                      POINTER(lr_layer_cache), c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                      c_void_p, c_void_p]
     lib.lowrank_last_error.restype = ctypes.c_char_p
     lib.lowrank_last_error.argtypes = []
     lib.lowrank_abi_version.restype = c_int32
@@ -200,6 +205,14 @@ def lowrank_kv_dequant(model: Model, layer: int, cache: Cache, batch: int, n_row
                        zv_out: torch.Tensor, stream=None) -> None:
     _check(load().lowrank_kv_dequant(ctypes.byref(model.desc), layer, ctypes.byref(cache.c), batch, n_rows,
                                      _ptr(zk_out), _ptr(zv_out), _stream(stream)))
+
+
+def lowrank_kv_rebase(model: Model, layer: int, src: Cache, dst: Cache, max_lat_len: int, rank_k_new: int,
+                      rank_v_new: int, wk: torch.Tensor, wv: torch.Tensor, stream=None) -> None:
+    """wk [rank_k_new][round_up(rank_k, 8)], wv likewise: W = (B pinv(B'))^T in the base dtype."""
+    _check(load().lowrank_kv_rebase(ctypes.byref(model.desc), layer, ctypes.byref(src.c), ctypes.byref(dst.c),
+                                    src.zk.shape[0], max_lat_len, rank_k_new, rank_v_new, _ptr(wk), _ptr(wv),
+                                    _stream(stream)))
 
 
 # ---- device memory plumbing ---------------------------------------------------------------------

@@ -334,6 +334,61 @@ int lowrank_kv_dequant(const lr_model_desc* model, int32_t layer, const lr_layer
   LR_GUARD_END
 }
 
+int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_cache* src,
+                      const lr_layer_cache* dst, int32_t batch, int32_t max_lat_len, int32_t rank_k_new,
+                      int32_t rank_v_new, const void* wk, const void* wv, void* stream) {
+  LR_GUARD_BEGIN
+  int rk = 0, rv = 0;
+  const char* msg = "";
+  int st = check_model(model, layer, &rk, &rv, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (model->latent_dtype == LR_I4G32) return fail(LR_EUNSUPPORTED, "rebase supports float32 and bf16 latents");
+  if (batch < 0) return fail(LR_EINVAL, "batch must be >= 0");
+  if (max_lat_len < 0) return fail(LR_EINVAL, "max_lat_len must be >= 0");
+  if (rank_k_new < 1 || rank_k_new > 512 || rank_v_new < 1 || rank_v_new > 512)
+    return fail(LR_EINVAL, "new ranks must be in 1..512");
+  // only the latent rows, their strides, t_cap and (src) lat_len take part
+  if (!src || !dst) return fail(LR_EINVAL, "src/dst is NULL");
+  if (!src->zk || !src->zv || !dst->zk || !dst->zv) return fail(LR_EINVAL, "latent buffers zk/zv must not be NULL");
+  if (!src->lat_len) return fail(LR_EINVAL, "src lat_len must not be NULL");
+  if (src->t_cap < 1 || src->t_cap > (int64_t)1 << 30 || dst->t_cap < 1 || dst->t_cap > (int64_t)1 << 30)
+    return fail(LR_EINVAL, "t_cap must be in 1..2^30");
+  if (!aligned(src->zk, 16) || !aligned(src->zv, 16) || !aligned(dst->zk, 16) || !aligned(dst->zv, 16))
+    return fail(LR_EINVAL, "latent buffers must be 16-byte aligned");
+  if (src->ld_k < rk || src->ld_v < rv) return fail(LR_EINVAL, "src ld must be >= the current rank");
+  if (src->ld_k % 8 != 0 || src->ld_v % 8 != 0 || src->ld_k > 4096 || src->ld_v > 4096)
+    return fail(LR_EINVAL, "src ld must be a multiple of 8, at most 4096");
+  if (dst->ld_k < rank_k_new || dst->ld_v < rank_v_new) return fail(LR_EINVAL, "dst ld must be >= the new rank");
+  if (dst->ld_k % 8 != 0 || dst->ld_v % 8 != 0 || dst->ld_k > 4096 || dst->ld_v > 4096)
+    return fail(LR_EINVAL, "dst ld must be a multiple of 8, at most 4096");
+  if ((int64_t)max_lat_len > src->t_cap || (int64_t)max_lat_len > dst->t_cap)
+    return fail(LR_EINVAL, "max_lat_len must be <= the t_cap of src and dst");
+  if (!wk || !wv) return fail(LR_EINVAL, "wk/wv must not be NULL");
+  if (!aligned(wk, 16) || !aligned(wv, 16)) return fail(LR_EINVAL, "wk/wv must be 16-byte aligned");
+  // in place: same rows and strides, and each row handled by one workgroup (one W chunk)
+  const bool inplace_k = dst->zk == src->zk, inplace_v = dst->zv == src->zv;
+  if ((inplace_k && (dst->ld_k != src->ld_k || dst->t_cap != src->t_cap)) ||
+      (inplace_v && (dst->ld_v != src->ld_v || dst->t_cap != src->t_cap)))
+    return fail(LR_EINVAL, "in-place rebase needs the same row stride and t_cap");
+  if (model->latent_dtype == LR_BF16 &&
+      ((inplace_k && rebase_col_chunk(rk, rank_k_new) < rank_k_new) ||
+       (inplace_v && rebase_col_chunk(rv, rank_v_new) < rank_v_new)))
+    return fail(LR_EUNSUPPORTED, "these ranks need a separate dst (the new coordinates do not fit one LDS chunk)");
+  if (batch == 0 || max_lat_len == 0) return LR_OK;
+  RebasePlan p;
+  p.B = batch;
+  p.rk = rk;
+  p.rv = rv;
+  p.rk_new = rank_k_new;
+  p.rv_new = rank_v_new;
+  p.latent = model->latent_dtype;
+  p.max_len = max_lat_len;
+  hipError_t e = launch_rebase(p, src, dst, wk, wv, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
 const char* lowrank_last_error(void) { return g_last_error.c_str(); }
 
 int lowrank_abi_version(void) { return LOWRANK_ABI_VERSION; }

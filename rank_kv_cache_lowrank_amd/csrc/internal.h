@@ -104,6 +104,14 @@ hipError_t launch_store(const AppendPlan& p, const lr_layer_cache* c, int64_t ro
 hipError_t launch_dequant(const AppendPlan& p, const lr_layer_cache* c, int64_t n_rows, float* zk_out,
                           float* zv_out, hipStream_t st);
 
+struct RebasePlan {
+  int B, rk, rv, rk_new, rv_new, latent, max_len;
+};
+
+hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const lr_layer_cache* dst,
+                         const void* wk, const void* wv, hipStream_t st);
+int rebase_col_chunk(int r_old, int r_new);   // new coordinates per workgroup chunk (bf16)
+
 int device_cu_count();
 
 }  // namespace lr

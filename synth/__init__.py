@@ -30,7 +30,7 @@ import torch
 
 # Stream ids of the seed sequence [cfg_id, stream, layer, b].
 STREAM = dict(q=0, zk=1, zv=2, bk=3, bv=4, lengths=5, ranks=6, k_new=7, v_new=8,
-              window=9, needle=10, perm=11)
+              window=9, needle=10, perm=11, bk_next=12, bv_next=13)
 
 N_Q_HEADS = 28
 N_KV_HEADS = 4
@@ -181,6 +181,34 @@ def gen_new_tokens(cfg: Config, which: str, layer: int, n_new: int) -> np.ndarra
 def down_projection(basis_stored: np.ndarray) -> np.ndarray:
     """P = pinv(B) [D, rank] in float64, computed by the caller from the stored basis."""
     return np.linalg.pinv(np.asarray(basis_stored, dtype=np.float64))
+
+
+def gen_basis_update(cfg: Config, which: str, layer: int, old_basis: np.ndarray, rank_new: int,
+                     eps: float = 0.05, stream: int = 0) -> np.ndarray:
+    """A nearby new basis B' [rank_new, D] float64: the old rows (cut, or extended by fresh
+    orthonormal rows), plus N(0, eps^2 / D) noise, so B' is full rank but not orthonormal."""
+    old = np.asarray(old_basis, np.float64)
+    D = old.shape[1]
+    g = rng(cfg.cfg_id, "bk_next" if which == "k" else "bv_next", layer, stream)
+    rows = old[:rank_new]
+    if rank_new > old.shape[0]:
+        G = g.standard_normal((D, rank_new))
+        Q, R = np.linalg.qr(G)
+        rows = np.concatenate([rows, (Q * np.sign(np.diag(R))[None, :]).T[old.shape[0]:]], axis=0)
+    return rows + g.standard_normal((rank_new, D)) * (eps / np.sqrt(D))
+
+
+def sync_projection(old_basis: np.ndarray, new_basis: np.ndarray) -> np.ndarray:
+    """W = (B pinv(B'))^T [rank_new, rank] in float64, computed by the caller (as P is)."""
+    return (np.asarray(old_basis, np.float64) @ np.linalg.pinv(np.asarray(new_basis, np.float64))).T
+
+
+def w_storage(w: np.ndarray, latent: str, fill: float = 0.0) -> torch.Tensor:
+    """W in the library's layout [rank_new][round_up(rank, 8)] and base dtype; pad = ``fill``."""
+    rn, r = w.shape
+    buf = np.full((rn, round_up(r, 8)), fill, np.float32)
+    buf[:, :r] = w
+    return to_storage(buf, "f32" if latent == "f32" else "bf16")
 
 
 # ----------------------------------------------------------------------------------------------

@@ -160,6 +160,67 @@ def test_append_store_dequant_validation():
                                 None) == L.LR_EINVAL
 
 
+def call_rebase(model, src, dst, **kw):
+    lib = lr.load()
+    a = dict(layer=0, batch=2, max_len=16, rk_new=200, rv_new=200, wk=1 << 29, wv=1 << 30, stream=None)
+    a.update(kw)
+    return lib.lowrank_kv_rebase(ctypes.byref(model.desc), a["layer"],
+                                 ctypes.byref(src) if src is not None else None,
+                                 ctypes.byref(dst) if dst is not None else None, a["batch"], a["max_len"],
+                                 a["rk_new"], a["rv_new"], a["wk"], a["wv"], a["stream"])
+
+
+def fake_dst(**kw):
+    c = L.lr_layer_cache()
+    c.zk, c.zv = 1 << 31, 1 << 32
+    c.ld_k = c.ld_v = 200
+    c.t_cap = 64
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@host_only
+@pytest.mark.parametrize("case,code", [
+    (dict(src=None), L.LR_EINVAL),
+    (dict(dst=None), L.LR_EINVAL),
+    (dict(src_kw=dict(lat_len=None)), L.LR_EINVAL),
+    (dict(src_kw=dict(ld_v=352)), L.LR_EINVAL),               # src ld < current rank
+    (dict(dst_kw=dict(ld_k=192)), L.LR_EINVAL),               # dst ld < new rank
+    (dict(dst_kw=dict(ld_v=204)), L.LR_EINVAL),               # dst ld not a multiple of 8
+    (dict(dst_kw=dict(zv=(1 << 32) + 8)), L.LR_EINVAL),       # misaligned dst
+    (dict(dst_kw=dict(t_cap=10)), L.LR_EINVAL),               # max_lat_len > dst t_cap
+    (dict(max_len=65), L.LR_EINVAL),                          # max_lat_len > src t_cap
+    (dict(rk_new=0), L.LR_EINVAL),
+    (dict(rv_new=513), L.LR_EINVAL),
+    (dict(wk=None), L.LR_EINVAL),
+    (dict(wv=(1 << 30) + 2), L.LR_EINVAL),                    # misaligned W
+    (dict(batch=-1), L.LR_EINVAL),
+    (dict(layer=1), L.LR_EINVAL),
+    (dict(model=dict(latent_dtype="i4g32")), L.LR_EUNSUPPORTED),
+    (dict(inplace=True, dst_kw=dict(ld_k=360, ld_v=360, t_cap=32)), L.LR_EINVAL),   # in place, t_cap differs
+    (dict(inplace=True, rk_new=352, rv_new=352), L.LR_EUNSUPPORTED),  # bf16 in place, two W chunks
+])
+def test_rebase_rejects_invalid_arguments(case, code):
+    model = desc(**case.get("model", {}))
+    src = None if case.get("src", 1) is None else fake_cache(**case.get("src_kw", {}))
+    if case.get("inplace"):
+        dst = fake_cache(**case.get("dst_kw", {}))
+    else:
+        dst = None if case.get("dst", 1) is None else fake_dst(**case.get("dst_kw", {}))
+    kw = {k: v for k, v in case.items() if k not in ("src", "dst", "src_kw", "dst_kw", "model", "inplace")}
+    assert call_rebase(model, src, dst, **kw) == code
+    assert lr.lowrank_last_error() != ""
+
+
+@host_only
+def test_rebase_zero_sizes_are_no_ops():
+    assert call_rebase(desc(), fake_cache(), fake_dst(), batch=0) == L.LR_OK
+    assert call_rebase(desc(), fake_cache(), fake_dst(), max_len=0) == L.LR_OK
+    # in place within one W chunk, nothing to do
+    assert call_rebase(desc(), fake_cache(), fake_cache(), rk_new=192, rv_new=100, batch=0) == L.LR_OK
+
+
 @host_only
 def test_zero_batch_is_a_no_op():
     # valid arguments with batch 0 return OK without launching anything
