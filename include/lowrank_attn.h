@@ -204,10 +204,15 @@ int lowrank_kv_dequant(const lr_model_desc* model, int32_t layer, const lr_layer
  *   src: the cache with the current ranks (model->rank_k/rank_v[layer]); only zk, zv, ld_k,
  *     ld_v, t_cap and lat_len (device, [batch]) are used, with the layout rules of decode.
  *     dst: latent buffers for the new ranks (ld >= new rank, a multiple of 8, <= 4096;
- *     t_cap >= max_lat_len); only zk, zv, ld_k, ld_v and t_cap are used. dst may be src itself (same buffers, strides and
- *     t_cap) when the new coordinates of a row fit one workgroup's W staging (float32 always;
- *     bf16: LR_EUNSUPPORTED otherwise); partially overlapping buffers are not allowed.
- *   max_lat_len: host upper bound on lat_len[b] (sizes the grid).
+ *     t_cap >= max_lat_len); only zk, zv, ld_k, ld_v and t_cap are used.
+ *     dst may be src itself (same buffers, strides and t_cap): always for float32; for bf16
+ *     when one workgroup produces all new coordinates of a row, i.e. new rank <= 512 / 256 /
+ *     192 / 128 for a current rank <= 128 / 256 / 384 / 512 (LR_EUNSUPPORTED otherwise).
+ *     Partially overlapping buffers are not allowed.
+ *   max_lat_len: host upper bound on lat_len[b] (sizes the grid); rows past it are not
+ *     touched even where lat_len[b] is larger.
+ *   stream: hipStream_t (NULL = default stream); the call only enqueues work and returns
+ *     LR_EHIP if a launch fails. All buffers are the caller's and stay so.
  * Rows past lat_len[b] and columns past the new rank of dst are not written. Lengths, window
  * and bases are untouched: the caller switches the model to the new ranks and bases.
  * int4 caches: LR_EUNSUPPORTED.

@@ -370,11 +370,6 @@ int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_
   if ((inplace_k && (dst->ld_k != src->ld_k || dst->t_cap != src->t_cap)) ||
       (inplace_v && (dst->ld_v != src->ld_v || dst->t_cap != src->t_cap)))
     return fail(LR_EINVAL, "in-place rebase needs the same row stride and t_cap");
-  if (model->latent_dtype == LR_BF16 &&
-      ((inplace_k && rebase_col_chunk(rk, rank_k_new) < rank_k_new) ||
-       (inplace_v && rebase_col_chunk(rv, rank_v_new) < rank_v_new)))
-    return fail(LR_EUNSUPPORTED, "these ranks need a separate dst (the new coordinates do not fit one LDS chunk)");
-  if (batch == 0 || max_lat_len == 0) return LR_OK;
   RebasePlan p;
   p.B = batch;
   p.rk = rk;
@@ -383,6 +378,14 @@ int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_
   p.rv_new = rank_v_new;
   p.latent = model->latent_dtype;
   p.max_len = max_lat_len;
+  if (model->latent_dtype == LR_BF16 && (inplace_k || inplace_v)) {
+    RebaseShape sk, sv;
+    rebase_shape(rk, rank_k_new, &sk);
+    rebase_shape(rv, rank_v_new, &sv);
+    if ((inplace_k && sk.nchunk > 1) || (inplace_v && sv.nchunk > 1))
+      return fail(LR_EUNSUPPORTED, "these ranks need a separate dst (the new coordinates of a row span two workgroups)");
+  }
+  if (batch == 0 || max_lat_len == 0) return LR_OK;
   hipError_t e = launch_rebase(p, src, dst, wk, wv, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
   return LR_OK;

@@ -110,7 +110,11 @@ struct RebasePlan {
 
 hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const lr_layer_cache* dst,
                          const void* wk, const void* wv, hipStream_t st);
-int rebase_col_chunk(int r_old, int r_new);   // new coordinates per workgroup chunk (bf16)
+struct RebaseShape {
+  int nks_t, nb, col_chunk, nchunk;
+};
+// bf16 kernel shape of one matrix; it can be rebased in place only when nchunk is 1.
+void rebase_shape(int r_old, int r_new, RebaseShape* s);   // new coordinates per workgroup chunk (bf16)
 
 int device_cu_count();
 

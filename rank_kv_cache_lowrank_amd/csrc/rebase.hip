@@ -7,14 +7,13 @@
 //     z' = z B pinv(B') = z W^T,     W [r_new][r_old] computed by the caller,
 // stored in the cache dtype (bf16: round to nearest even, as the append path stores z).
 //
-// bf16 kernel: W (one chunk of its rows, i.e. of the new coordinates) is staged once per
-// workgroup of 8 waves in LDS with padded rows; each wave then takes 32-row groups of one
-// sequence, holds
-// their two 16-row tiles in registers and runs 16x16x32 bf16 matrix-core products with
-// A = 16 rows of W (new coordinates) and B = the tile's rows transposed (tokens), so a lane's
-// accumulator holds 4 consecutive new coordinates of one token (8-byte stores). Every W read
-// from LDS feeds both tiles. HBM traffic per token: the old row read once per chunk and the new
-// row written once.
+// bf16 kernel (W-stationary): each consumer wave of a workgroup holds a few 16-row blocks of W
+// (new coordinates x all old coordinates) in registers for the whole launch; two producer waves
+// stream 16-row tiles of stored rows through an LDS ring with direct-to-LDS loads, and every
+// tile read from LDS feeds all of a consumer's blocks in 16x16x32 matrix-core products. HBM
+// traffic per row: the old coordinates read once (once per chunk of new coordinates when W
+// does not fit one workgroup's registers; the chunks of a row range run on one XCD and share
+// its L2) and the new coordinates written once.
 #include "device_common.h"
 #include "internal.h"
 
@@ -31,6 +30,9 @@ struct RebaseArgs {
   int ldw[2];
   int B, max_len, groups_per_seq;
   int col_chunk[2];              // bf16: new coordinates per workgroup chunk (multiple of 16)
+  int stages;                    // bf16: LDS ring depth in tiles
+  int kv0;                       // bf16: matrix of blockIdx.y == 0 (0 = K, 1 = V)
+  int sub;                       // bf16: 16-row tiles per ring step
 };
 
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
@@ -44,105 +46,252 @@ __device__ __forceinline__ u32x4 keep_below(int c0, int n) {
   return m;
 }
 
-constexpr int kRebaseRows = 32;      // rows per wave group (two 16-row tiles)
-constexpr int kRebaseWaves = 8;      // waves per workgroup, all sharing the staged W chunk
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {   // round to nearest even
+  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)lo) |
+         ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
+}
 
-__host__ __device__ constexpr int rebase_ws(int nks) { return nks * 64 + 16; }   // W row stride (B)
+constexpr int kRbTile = 16;          // rows per tile (the MFMA's N)
+constexpr int kRbProducers = 2;      // waves 0..1 stream the tiles into LDS
+constexpr int kRbConsumers = 4;      // waves 2..5 multiply: one per SIMD
+constexpr int kRbThreads = (kRbProducers + kRbConsumers) * 64;
+constexpr int kRbMaxStages = 32;
 
-template <int NKS>
-__global__ __launch_bounds__(kRebaseWaves * 64) void lr_rebase_bf16(RebaseArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char wsm[];
-  const int kv = blockIdx.y, chunk = blockIdx.z;
+// 16-byte granule order inside an LDS tile row. A consumer's read of one K step takes granule
+// 4*ks + lg of rows li = 0..15; with G granules per row (G = 4 * K steps) the swizzle makes
+// every 8 consecutive lanes hit 8 different 16-byte bank groups.
+__device__ __forceinline__ int rb_swz(int row, int G) { return (G & 7) ? ((row >> 1) & 3) : (row & 7); }
+
+// New coordinate (relative to a wave's first) of row r of its block nb. Blocks are paired so
+// that the accumulator rows a lane holds (4 from each block of a pair) are 8 consecutive
+// coordinates: one 16-byte store. Block 2p covers 8m + 0..3, block 2p+1 covers 8m + 4..7 of
+// the pair's 32 coordinates (m = r / 4); an unpaired last block covers 16 in order.
+__host__ __device__ constexpr int rb_coord(int nb, int NB, int r) {
+  return nb < (NB & ~1) ? 32 * (nb >> 1) + 8 * (r >> 2) + 4 * (nb & 1) + (r & 3) : 16 * nb + r;
+}
+
+// Walks the steps (16 * sub rows of one sequence) of the linear range [lo, hi) that hold stored
+// rows; every wave of a workgroup walks the same sequence. lat_len is read once per sequence.
+struct RbIter {
+  int idx, hi, sps, b, s, L;   // linear step, end, steps per sequence, sequence, step in it
+  int cb, t0, cL;              // current step: sequence, first row, stored rows of the sequence
+};
+__device__ __forceinline__ void rb_init(RbIter& it, int lo, int hi, int sps) {
+  it.idx = lo;
+  it.hi = hi;
+  it.sps = sps;
+  it.b = lo / sps;
+  it.s = lo - it.b * sps;
+  it.L = -1;
+}
+__device__ __forceinline__ bool rb_next(RbIter& it, const RebaseArgs& a, long long cap, int step_rows) {
+  while (it.idx < it.hi) {
+    if (it.L < 0) {
+      long long Lb = a.lat_len[it.b];
+      Lb = Lb < 0 ? 0 : (Lb > a.max_len ? a.max_len : Lb);
+      it.L = (int)(Lb > cap ? cap : Lb);
+    }
+    const int t0 = it.s * step_rows;
+    if (t0 < it.L) {
+      it.cb = it.b;
+      it.t0 = t0;
+      it.cL = it.L;
+      ++it.idx;
+      if (++it.s == it.sps) {
+        it.s = 0;
+        ++it.b;
+        it.L = -1;
+      }
+      return true;
+    }
+    it.idx += it.sps - it.s;                // rest of this sequence is empty
+    it.s = 0;
+    ++it.b;
+    it.L = -1;
+  }
+  return false;
+}
+
+// bf16 latents. blockIdx.y = K/V, blockIdx.z = chunk of the new coordinates, blockIdx.x = a
+// contiguous range of steps (sub 16-row tiles of one sequence) over (sequence, position). Each
+// consumer wave keeps its NB 16-row blocks of W (new coordinates) x all old coordinates in
+// registers for the whole launch and runs 16x16x32 bf16 products with A = W block, B = tile
+// rows read from LDS, so every LDS read of a tile feeds NB matrix-core products. Waves 0-1
+// stream the steps through an LDS ring with direct-to-LDS loads and exact vmcnt waits (two
+// producers double the loads one wave may keep in flight); one barrier per step.
+template <int NKS, int NB>
+__global__ __launch_bounds__(kRbThreads) void lr_rebase_bf16(RebaseArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
+  const int kv = a.kv0 + blockIdx.y;
   const int r_old = a.r_old[kv], r_new = a.r_new[kv];
-  const int j0 = chunk * a.col_chunk[kv];
-  if (j0 >= r_new) return;                              // workgroup-uniform
-  const int jc = min(a.col_chunk[kv], r_new - j0);
-  const int nblk = (jc + 15) >> 4;                      // 16-coordinate output blocks
-  const int nks = (r_old + 31) >> 5;                    // K steps over the old coordinates
-  const int ws = rebase_ws(nks);                        // +16 B per row spreads rows over banks
-  const int tid = threadIdx.x;
+  const int nks = (r_old + 31) >> 5;                    // K steps, in (NKS - 4, NKS]
+  const int G = nks * 4;                                // granules per tile row
+  const int tile_bytes = kRbTile * G * 16;
+  const int sub = a.sub, step_rows = kRbTile * sub, step_bytes = tile_bytes * sub;
+  const int nst = a.stages;
+  const int sps = a.groups_per_seq;                     // steps per sequence
+  const long long cap = a.src_tcap < a.dst_tcap ? a.src_tcap : a.dst_tcap;
+  const int NT = a.B * sps;
+  const int lo = (int)((long long)NT * blockIdx.x / gridDim.x);
+  const int hi = (int)((long long)NT * (blockIdx.x + 1) / gridDim.x);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sld = a.src_ld[kv];
 
-  // W rows j0 .. j0 + 16*nblk - 1 into LDS; rows past r_new and columns past r_old are zero
+  if (wave < kRbProducers) {
+    // ---- producers: rows -> LDS ring. Instruction k of a 16-row tile (k = wave, wave + 2, ...)
+    // fills LDS slots 64k .. 64k+63 (16 B each) of the tile; slot s holds row s / G, granule
+    // (s % G) ^ swizzle(row). Granules past the rank load granule 0 instead (in bounds, finite;
+    // their W columns are zero). Every tile of a step is loaded (rows past the sequence's end
+    // repeat its last row), so each step costs every producer the same number of loads.
+    constexpr int KP = (NKS + kRbProducers - 1) / kRbProducers;
+    const int my_cnt = (nks - wave + kRbProducers - 1) / kRbProducers;   // loads per tile
+    const __bf16* src = (const __bf16*)a.src[kv];
+    int rowk[KP], colk[KP];
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int k = wave + kRbProducers * u;
+      const int sl = 64 * k + lane;
+      const int row = sl / G, pos = sl - row * G;
+      const int gr = pos ^ rb_swz(row, G);
+      rowk[u] = row;
+      colk[u] = gr * 8 < r_old ? gr * 8 : 0;
+    }
+    auto issue = [&](const RbIter& t, int stage) {
+      const __bf16* base = src + (size_t)t.cb * a.src_tcap * sld;
+      unsigned char* dstl = ring + stage * step_bytes + wave * 1024;
+      for (int q = 0; q < sub; ++q) {
+#pragma unroll
+        for (int u = 0; u < KP; ++u) {
+          if (u < my_cnt) {
+            int row = t.t0 + q * kRbTile + rowk[u];
+            row = row < t.cL ? row : t.cL - 1;
+            dma16(base + (size_t)row * sld + colk[u], dstl + q * tile_bytes + kRbProducers * u * 1024);
+          }
+        }
+      }
+    };
+    RbIter ii, ci;
+    rb_init(ii, lo, hi, sps);
+    rb_init(ci, lo, hi, sps);
+    const int per_step = my_cnt * sub;
+    int issued = 0;
+    for (int s = 0; s < nst - 1; ++s) {
+      if (!rb_next(ii, a, cap, step_rows)) break;
+      issue(ii, issued % nst);
+      ++issued;
+    }
+    for (int c = 0; rb_next(ci, a, cap, step_rows); ++c) {
+      wait_vmcnt((issued - c - 1) * per_step);          // this wave's part of the step landed
+      barrier_lds();                                    // ... for every consumer; stage c-1 is free
+      if (rb_next(ii, a, cap, step_rows)) {
+        issue(ii, issued % nst);
+        ++issued;
+      }
+    }
+    return;
+  }
+
+  // ---- consumers
+  const int cw = wave - kRbProducers, lg = lane >> 4, li = lane & 15;
+  const int jw = blockIdx.z * a.col_chunk[kv] + cw * NB * 16;   // first new coordinate of this wave
+  const int jend = min(r_new, (blockIdx.z + 1) * a.col_chunk[kv]);
+  // W rows -> registers. Every load is issued (rows and columns clamped into the matrix) and
+  // then masked, so the loads overlap: rows past this chunk and columns past r_old are zero.
+  bf16x8 w[NB][NKS];
   {
     const __bf16* wg = (const __bf16*)a.w[kv];
     const int ldw = a.ldw[kv];
-    for (int i = tid; i < nblk * 16 * nks * 4; i += kRebaseWaves * 64) {
-      const int row = i / (nks * 4), g = i - row * (nks * 4);
-      const int j = j0 + row, c = g * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < r_new && c < r_old) v = *(const u32x4*)(wg + (size_t)j * ldw + c) & keep_below(c, r_old);
-      *(u32x4*)(wsm + row * ws + g * 16) = v;
-    }
-  }
-  __syncthreads();
-
-  const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, li = lane & 15;
-  const __bf16* src = (const __bf16*)a.src[kv];
-  __bf16* dst = (__bf16*)a.dst[kv];
-  const int sld = a.src_ld[kv], dld = a.dst_ld[kv];
-  const long long cap = a.src_tcap < a.dst_tcap ? a.src_tcap : a.dst_tcap;
-  const int total = a.B * a.groups_per_seq;
-
-  for (int gi = blockIdx.x * kRebaseWaves + wave; gi < total; gi += gridDim.x * kRebaseWaves) {
-    const int b = gi / a.groups_per_seq;
-    const int t0 = (gi - b * a.groups_per_seq) * kRebaseRows;
-    long long Lb = a.lat_len[b];
-    Lb = Lb < 0 ? 0 : (Lb > a.max_len ? a.max_len : Lb);
-    Lb = Lb > cap ? cap : Lb;
-    const int L = (int)Lb;
-    if (t0 >= L) continue;                              // wave-uniform
-
-    // the group's two 16-row tiles as the B operand: lane (lg, li) holds row li's old
-    // coordinates 32*ks + 8*lg .. +7. Only granules that start below r_old are read (they end
-    // inside the row: the row stride is a multiple of 8 and >= r_old); the last one is masked.
-    bf16x8 zb[2][NKS];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int row = t0 + 16 * tt + li;
-      const bool valid = row < L;
-      const __bf16* zr = src + ((size_t)b * a.src_tcap + (valid ? row : 0)) * sld + lg * 8;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int j = jw + rb_coord(nb, NB, li);
+      const int jc = j < r_new ? j : r_new - 1;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int c = ks * 32 + lg * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (valid && c < r_old) {
-          v = *(const u32x4*)(zr + ks * 32);
-          if (c + 8 > r_old) v &= keep_below(c, r_old);
-        }
-        zb[tt][ks] = __builtin_bit_cast(bf16x8, v);
+        const int cc = c < ldw - 8 ? c : ldw - 8;
+        u32x4 v = *(const u32x4*)(wg + (size_t)jc * ldw + cc);
+        v &= keep_below(c, j < jend ? r_old : 0);
+        w[nb][ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-
-    for (int n = 0; n < nblk; ++n) {
-      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-      const unsigned char* wrow = wsm + (n * 16 + li) * ws + lg * 16;
+  }
+  // z operand: K steps below NKS - 4 always exist. When r_old is not a multiple of 8, the step
+  // holding r_old - 1 keeps only the columns below r_old (its granule carries pad columns, which
+  // may hold anything); steps past nks are zero and skip their products. (Granules wholly past
+  // r_old hold granule 0, finite, against zero W columns.)
+  const u32x4 last_mask = keep_below((nks - 1) * 32 + lg * 8, r_old);
+  const bool fix_tail = (r_old & 7) != 0 || nks < NKS;
+  const int rsw = rb_swz(li, G);
+  __bf16* dst = (__bf16*)a.dst[kv];
+  const int dld = a.dst_ld[kv];
+  constexpr int KF = NKS > 4 ? NKS - 4 : 0;             // K steps that always exist
+  RbIter t;
+  rb_init(t, lo, hi, sps);
+  for (int c = 0; rb_next(t, a, cap, step_rows); ++c) {
+    barrier_lds();
+    const unsigned char* stp = ring + (c % nst) * step_bytes + li * G * 16;
+    for (int q = 0; q < sub; ++q) {
+      const int row = t.t0 + q * kRbTile + li;
+      if (t.t0 + q * kRbTile >= t.cL) break;            // step-uniform
+      const unsigned char* st = stp + q * tile_bytes;
+      u32x4 zv[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        if (ks < nks) {
-          const bf16x8 av = *(const bf16x8*)(wrow + ks * 64);
-          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, zb[0][ks], c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, zb[1][ks], c1, 0, 0, 0);
+        const int kk = (ks < KF || ks < nks) ? ks : nks - 1;
+        zv[ks] = *(const u32x4*)(st + (((4 * kk + lg) ^ rsw) << 4));
+      }
+      if (fix_tail) {
+#pragma unroll
+        for (int ks = KF; ks < NKS; ++ks) {
+          if (ks == nks - 1) zv[ks] &= last_mask;
         }
       }
-      // C[new coordinate n*16 + 4*lg + i][token li]
-      const int jb = j0 + n * 16 + 4 * lg;
+      f32x4 acc[NB];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int row = t0 + 16 * tt + li;
-        if (row >= L) continue;
-        const f32x4 c = tt == 0 ? c0 : c1;
-        __bf16* out = dst + ((size_t)b * a.dst_tcap + row) * dld + jb;
-        if (jb + 4 <= r_new) {
-          u32x2 o;
-          o[0] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)c[0]) |
-                 ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)c[1]) << 16);
-          o[1] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)c[2]) |
-                 ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)c[3]) << 16);
-          *(u32x2*)out = o;
-        } else {
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (jb + i < r_new) out[i] = (__bf16)c[i];
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks < KF || ks < nks) {
+          const bf16x8 zo = __builtin_bit_cast(bf16x8, zv[ks]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[nb][ks], zo, acc[nb], 0, 0, 0);
+        }
+      }
+      // C[block row 4lg + i][token li]: pairs give 8 consecutive coordinates jp + 8lg + 0..7
+      if (row < t.cL) {
+        __bf16* out = dst + ((size_t)t.cb * a.dst_tcap + row) * dld;
+#pragma unroll
+        for (int pb = 0; pb < NB / 2; ++pb) {
+          const int jb = jw + 32 * pb + 8 * lg;
+          const f32x4 v0 = acc[2 * pb], v1 = acc[2 * pb + 1];
+          if (jb + 8 <= jend) {
+            u32x4 o;
+            o[0] = pack_bf16(v0[0], v0[1]);
+            o[1] = pack_bf16(v0[2], v0[3]);
+            o[2] = pack_bf16(v1[0], v1[1]);
+            o[3] = pack_bf16(v1[2], v1[3]);
+            *(u32x4*)(out + jb) = o;
+          } else if (jb < jend) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (jb + i < jend) out[jb + i] = (__bf16)v0[i];
+              if (jb + 4 + i < jend) out[jb + 4 + i] = (__bf16)v1[i];
+            }
+          }
+        }
+        if constexpr ((NB & 1) != 0) {
+          const int jb = jw + 16 * (NB - 1) + 4 * lg;
+          const f32x4 v = acc[NB - 1];
+          if (jb + 4 <= jend) {
+            u32x2 o;
+            o[0] = pack_bf16(v[0], v[1]);
+            o[1] = pack_bf16(v[2], v[3]);
+            *(u32x2*)(out + jb) = o;
+          } else if (jb < jend) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (jb + i < jend) out[jb + i] = (__bf16)v[i];
+          }
         }
       }
     }
@@ -181,13 +330,51 @@ __global__ __launch_bounds__(256) void lr_rebase_f32(RebaseArgs a) {
   }
 }
 
-static int rebase_nks_max(int r_old) { return r_old <= 256 ? 8 : (r_old <= 384 ? 12 : 16); }
+// Launch shape shared by K and V: K-step bound NKS (template), blocks of 16 new coordinates
+// per consumer NB (template; bounded by registers), chunks of new coordinates (each chunk is
+// one workgroup's consumers; every chunk re-reads the rows).
+static int rb_nks_t(int r_old) {
+  const int nks = (r_old + 31) / 32;
+  return nks <= 4 ? 4 : (nks <= 8 ? 8 : (nks <= 12 ? 12 : 16));
+}
+static int rb_nb_max(int nks_t) { return nks_t == 16 ? 2 : (nks_t == 12 ? 3 : (nks_t == 8 ? 4 : 8)); }
 
-int rebase_col_chunk(int r_old, int r_new) {
-  const int ws = rebase_ws((r_old + 31) >> 5);
-  const int rows = ((kLdsBytes - 1024) / ws) & ~15;
-  const int need = (r_new + 15) & ~15;
-  return need < rows ? need : rows;
+void rebase_shape(int r_old, int r_new, RebaseShape* s) {
+  s->nks_t = rb_nks_t(r_old);
+  const int per = kRbConsumers * rb_nb_max(s->nks_t);   // blocks one workgroup holds
+  const int nblk = (r_new + 15) / 16;
+  const int nchunk = (nblk + per - 1) / per;
+  const int blk_chunk = (nblk + nchunk - 1) / nchunk;
+  s->nb = (blk_chunk + kRbConsumers - 1) / kRbConsumers;
+  s->col_chunk = s->nb * kRbConsumers * 16;
+  s->nchunk = (r_new + s->col_chunk - 1) / s->col_chunk;
+}
+
+static hipError_t launch_rebase_bf16(int nks_t, int nb, dim3 grid, size_t lds, hipStream_t st,
+                                     const RebaseArgs& a) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static bool attr[64][24] = {};
+  int vi = 0;
+#define LR_RB_CASES(X) X(4, 1) X(4, 2) X(4, 3) X(4, 4) X(4, 5) X(4, 6) X(4, 7) X(4, 8) \
+                       X(8, 1) X(8, 2) X(8, 3) X(8, 4) X(12, 1) X(12, 2) X(12, 3) X(16, 1) X(16, 2)
+#define LR_RB_LAUNCH(K, N)                                                                      \
+  if (nks_t == K && nb == N) {                                                                  \
+    if (dev >= 0 && dev < 64 && !attr[dev][vi]) {                                               \
+      e = hipFuncSetAttribute((const void*)lr_rebase_bf16<K, N>,                                \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);           \
+      if (e != hipSuccess) return e;                                                            \
+      attr[dev][vi] = true;                                                                     \
+    }                                                                                           \
+    hipLaunchKernelGGL((lr_rebase_bf16<K, N>), grid, dim3(kRbThreads), lds, st, a);             \
+    return hipGetLastError();                                                                   \
+  }                                                                                             \
+  ++vi;
+  LR_RB_CASES(LR_RB_LAUNCH)
+#undef LR_RB_LAUNCH
+#undef LR_RB_CASES
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const lr_layer_cache* dst,
@@ -214,8 +401,11 @@ hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const l
   a.ldw[1] = (p.rv + 7) / 8 * 8;
   a.B = p.B;
   a.max_len = p.max_len;
-  a.groups_per_seq = (p.max_len + kRebaseRows - 1) / kRebaseRows;
+  a.groups_per_seq = 0;
+  a.stages = 0;
   a.col_chunk[0] = a.col_chunk[1] = 0;
+  a.kv0 = 0;
+  a.sub = 1;
   if (p.B == 0 || p.max_len == 0) return hipSuccess;
   if (p.latent == LR_F32) {
     const long long rows = (long long)p.B * p.max_len;
@@ -223,44 +413,43 @@ hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const l
     hipLaunchKernelGGL(lr_rebase_f32, dim3(gx, 2), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  // one launch for K (blockIdx.y = 0) and V (1); blockIdx.z = chunk of the new coordinates
-  const int r_max = p.rk > p.rv ? p.rk : p.rv;
-  const int nmax = rebase_nks_max(r_max);
-  size_t lds = 0;
-  int nchunk = 1;
-  for (int kv = 0; kv < 2; ++kv) {
-    const int r_old = kv == 0 ? p.rk : p.rv, r_new = kv == 0 ? p.rk_new : p.rv_new;
-    const int chunk = rebase_col_chunk(r_old, r_new);
-    const int n = (r_new + chunk - 1) / chunk;
-    const size_t l = (size_t)chunk * rebase_ws((r_old + 31) >> 5);
-    a.col_chunk[kv] = chunk;
-    if (n > nchunk) nchunk = n;
-    if (l > lds) lds = l;
-  }
-  // workgroups per CU allowed by LDS (two at most: 8 waves each, up to ~225 VGPRs per lane)
-  const int per_cu = kLdsBytes / lds >= 2 ? 2 : 1;
-  const long long groups = (long long)p.B * a.groups_per_seq;
-  long long gx = (groups + kRebaseWaves - 1) / kRebaseWaves;
-  long long cap = (long long)device_cu_count() * per_cu / (2 * nchunk);
-  cap = cap < 8 ? 8 : cap & ~7LL;   // a multiple of 8: the workgroups of one row range share an XCD
-  if (gx > cap) gx = cap;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  static bool attr[64][3] = {};
-  const void* fn = nmax == 8 ? (const void*)lr_rebase_bf16<8>
-                 : nmax == 12 ? (const void*)lr_rebase_bf16<12> : (const void*)lr_rebase_bf16<16>;
-  const int vi = nmax == 8 ? 0 : (nmax == 12 ? 1 : 2);
-  if (dev >= 0 && dev < 64 && !attr[dev][vi]) {
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  // K and V share one launch (blockIdx.y = matrix) when their kernel shapes agree
+  RebaseShape sh[2];
+  rebase_shape(p.rk, p.rk_new, &sh[0]);
+  rebase_shape(p.rv, p.rv_new, &sh[1]);
+  a.col_chunk[0] = sh[0].col_chunk;
+  a.col_chunk[1] = sh[1].col_chunk;
+  const bool together = sh[0].nks_t == sh[1].nks_t && sh[0].nb == sh[1].nb;
+  for (int kv0 = 0; kv0 < 2; kv0 += together ? 2 : 1) {
+    const int nmat = together ? 2 : 1;
+    const int kv1 = kv0 + nmat - 1;
+    const int nchunk = sh[kv0].nchunk > sh[kv1].nchunk ? sh[kv0].nchunk : sh[kv1].nchunk;
+    // steps of sub 16-row tiles; ring depth: a producer's outstanding loads ((stages - 1) steps
+    // of its share of the instructions) stay within the 6-bit vmcnt; LDS bounds it too
+    const int r_max = (kv0 == 0 ? p.rk : p.rv) > (kv1 == 0 ? p.rk : p.rv) ? (kv0 == 0 ? p.rk : p.rv)
+                                                                          : (kv1 == 0 ? p.rk : p.rv);
+    const int nks = (r_max + 31) / 32;
+    const int sub = nks <= 8 ? 4 : 2;
+    const int step_bytes = kRbTile * nks * 4 * 16 * sub;
+    const int per_wave = (nks + kRbProducers - 1) / kRbProducers * sub;
+    int stages = 63 / per_wave + 1;
+    if (stages > kRbMaxStages) stages = kRbMaxStages;
+    if (stages * step_bytes > kLdsBytes) stages = kLdsBytes / step_bytes;
+    RebaseArgs ak = a;
+    ak.stages = stages;
+    ak.sub = sub;
+    ak.kv0 = kv0;
+    ak.groups_per_seq = (p.max_len + kRbTile * sub - 1) / (kRbTile * sub);
+    const size_t lds = (size_t)stages * step_bytes;
+    const long long steps = (long long)p.B * ak.groups_per_seq;
+    long long gx = device_cu_count() / (nmat * nchunk);
+    gx = gx < 4 ? 4 : gx & ~3LL;      // 2*gx a multiple of 8: the chunks of one range share an XCD
+    if (gx > steps) gx = steps;
+    hipError_t e = launch_rebase_bf16(sh[kv0].nks_t, sh[kv0].nb, dim3((unsigned)gx, nmat, (unsigned)nchunk),
+                                      lds, st, ak);
     if (e != hipSuccess) return e;
-    attr[dev][vi] = true;
   }
-  const dim3 grid((unsigned)gx, 2, (unsigned)nchunk), block(kRebaseWaves * 64);
-  if (nmax == 8) hipLaunchKernelGGL(lr_rebase_bf16<8>, grid, block, lds, st, a);
-  else if (nmax == 12) hipLaunchKernelGGL(lr_rebase_bf16<12>, grid, block, lds, st, a);
-  else hipLaunchKernelGGL(lr_rebase_bf16<16>, grid, block, lds, st, a);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace lr

@@ -144,7 +144,7 @@ def test_bf16_signed_permutation_is_bit_exact(rk, rk2):
 
 
 @pytest.mark.parametrize("latent,rk,rv,rk2,rv2", [
-    ("bf16", 358, 358, 192, 160), ("bf16", 40, 96, 32, 88), ("bf16", 512, 512, 144, 8),
+    ("bf16", 358, 358, 192, 160), ("bf16", 40, 96, 32, 88), ("bf16", 512, 512, 128, 8),
     ("f32", 128, 128, 128, 128), ("f32", 48, 20, 40, 9)])
 def test_in_place(latent, rk, rv, rk2, rv2):
     lat_len = [33, 0, 200, 17]
