@@ -133,30 +133,45 @@ def cpu_baseline(cfg, li, budget_s: float = 20.0):
                 us_per_layer_step=t_total / done * cfg.batch * 1e6)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the decode kernel's sources: counter figures are valid only for this code."""
+KERNEL_SOURCES = {
+    "lr_decode": ("decode.hip", "device_common.h", "internal.h", "abi.cpp"),
+    "lr_rebase_bf16": ("rebase.hip", "device_common.h"),
+}
+
+
+def kernel_source_hash(kernel: str = "lr_decode") -> str:
+    """sha256 over a kernel's sources: counter figures are valid only for this code."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_kv_cache_lowrank_amd", "csrc")
-    for name in ("decode.hip", "device_common.h", "internal.h", "abi.cpp"):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of lr_decode from the committed counter summary (FETCH_SIZE and
+def measured_traffic(workload: str, kernel: str = "lr_decode"):
+    """HBM bytes per launch of a kernel from its committed counter summary (FETCH_SIZE and
     WRITE_SIZE runs, scaled by a copy kernel of known size), or None when there is none for
     this workload or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "lr_decode_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     entry = rec.get("workloads", {}).get(workload)
-    if entry is None or rec.get("source_sha256") != kernel_source_hash():
+    if entry is None or rec.get("source_sha256") != kernel_source_hash(kernel):
         return None
     return int(entry["hbm_bytes_per_launch"])
+
+
+def copy_probe(torch, dev):
+    """One elementwise kernel that reads 256 MiB and writes 256 MiB (the counter calibration)."""
+    src = torch.zeros(64 * 2**20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
 
 
 def rebase_bench(args):
@@ -218,8 +233,11 @@ def rebase_bench(args):
         ev.destroy(a)
         ev.destroy(b)
     assert torch.isfinite(pairs[0][1].zk[:, :, :rk2].float()).all(), "non-finite output"
+    if args.copy_probe:
+        copy_probe(torch, dev)
     value = bytes_call / (ms_per_call * 1e-3) / 1e9
     achieved = bytes_call / (kern_ms * 1e-3) / 1e9
+    workload = f"rebase {cfg.name} r{rk}->r{rk2}"
     log(f"ms/call {ms_per_call:.4f}  kernel {kern_ms * 1e3:.2f} us  {value:.1f} GB/s  kernel {achieved:.1f} GB/s")
     rec = {
         "metric": "historical-coordinate sync of one layer cache: algorithmic HBM GB/s",
@@ -234,12 +252,13 @@ def rebase_bench(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"rebase {cfg.name} r{rk}->r{rk2}", "batch": B, "seq_len": T,
+        "config": {"workload": workload, "batch": B, "seq_len": T,
                    "rank_k": rk, "rank_v": rv, "rank_k_new": rk2, "rank_v_new": rv2,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "lr_rebase_bf16", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s",
-                     "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4), "traffic": None,
+                     "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4),
+                     "traffic": measured_traffic(workload, "lr_rebase_bf16"),
                      "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": int(bytes_call),
                      "mfma_tflops": round(2.0 * B * T * (rk * rk2 + rv * rv2) / (kern_ms * 1e-3) / 1e12, 1)},
     }
@@ -343,12 +362,7 @@ def main():
     assert torch.isfinite(out).all(), "non-finite output"
 
     if args.copy_probe:
-        # one elementwise kernel that reads 256 MiB and writes 256 MiB (a plain copy of known size)
-        src = torch.zeros(64 * 2**20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log(f"copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
+        copy_probe(torch, dev)
 
     by = [step_bytes(cfg, li.rank_k, li.rank_v, L, np.zeros_like(L), n_new) for L in lens]
     step_total = float(np.mean([x["total"] for x in by]))
