@@ -22,6 +22,8 @@ Modules
 ``quant``      int4 groups-of-32 min-max quantiser, nibble packing, exact dequantiser.
 ``append``     the append state machine: exact window ring, eviction, projection, storage.
 ``rebase``     historical-coordinate sync after a basis update (least-squares coordinates).
+``prefill``    chunked prefill attention: a chunk's queries over the latent history, the exact
+               window and the chunk itself (causal); P1 reconstruct, P2 latent, P3 brute force.
 
 Every function works in float64 unless the step it models fixes a narrower
 precision (the quantiser's float32/float16 steps, storage rounding).
