@@ -152,6 +152,37 @@ int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_laye
                         const lr_decode_opts* opts, void* stream);
 
 /*
+ * Bytes of device workspace lowrank_attn_prefill needs (256-byte aligned base required);
+ * 0 if the arguments are invalid.
+ */
+size_t lowrank_attn_prefill_workspace_size(const lr_model_desc* model, int32_t layer, int32_t batch,
+                                           int32_t n_new, int32_t max_lat_len,
+                                           const lr_decode_opts* opts);
+
+/*
+ * Chunked prefill attention (TraceKV abstract: the latents hold the KV states of large
+ * multimodal contexts; the pages describe decode, and this is the same attention for a chunk of
+ * n_new new tokens per sequence). Query token c of sequence b attends, causally, to the latent
+ * history rows [0, lat_len[b]), the win_len[b] exact window slots (W > 0), and the chunk's own
+ * exact rows 0 .. c:
+ *   q     [B][n_new][Hq][d]: float32 if latent_dtype == LR_F32, else bfloat16.
+ *   k_new, v_new [B][n_new][D] bfloat16: the chunk's dense key and value rows.
+ *   out   [B][n_new][Hq][d]: out_dtype LR_F32 or LR_BF16.
+ *   max_lat_len, workspace, opts: as for decode (workspace from
+ *   lowrank_attn_prefill_workspace_size; opts->nsplit splits each query token's latent range).
+ * 1 <= n_new and batch * n_new <= 65535. The cache is not modified: store the chunk afterwards
+ * with lowrank_kv_append(..., n_new, k_new, v_new, ...), which projects, quantises and evicts
+ * exactly as for decode. Every chunk token reads the whole latent stream (the latent part is
+ * decode's kernel over batch * n_new query sequences that share their stored sequence's rows).
+ * Writes only `out` and `workspace`.
+ */
+int lowrank_attn_prefill(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                         int32_t batch, int32_t n_new, int32_t max_lat_len, const void* q,
+                         const void* k_new, const void* v_new, void* out, int32_t out_dtype,
+                         void* workspace, size_t workspace_bytes, const lr_decode_opts* opts,
+                         void* stream);
+
+/*
  * Append n_new tokens per sequence (iS-KV abstract: keep the recent window exact, fold older
  * tokens into the latent history; TraceKV abstract: latents optionally quantised).
  *   k_new, v_new [B][n_new][D] bfloat16 dense rows, in arrival order.

@@ -21,7 +21,8 @@ LR_OK, LR_EINVAL, LR_EUNSUPPORTED, LR_EWORKSPACE, LR_EHIP = 0, -1, -2, -3, -4
 LR_F32, LR_BF16, LR_I4G32 = 0, 1, 2
 DTYPES = {"f32": LR_F32, "bf16": LR_BF16, "i4g32": LR_I4G32}
 
-EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_kv_append",
+EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_attn_prefill_workspace_size",
+           "lowrank_attn_prefill", "lowrank_kv_append",
            "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_last_error",
            "lowrank_abi_version")
 
@@ -68,6 +69,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowrank_attn_decode.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                         c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                         POINTER(lr_decode_opts), c_void_p]
+    lib.lowrank_attn_prefill_workspace_size.restype = c_size_t
+    lib.lowrank_attn_prefill_workspace_size.argtypes = [POINTER(lr_model_desc), c_int32, c_int32, c_int32,
+                                                        c_int32, POINTER(lr_decode_opts)]
+    lib.lowrank_attn_prefill.restype = c_int32
+    lib.lowrank_attn_prefill.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
+                                         c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                         c_void_p, c_size_t, POINTER(lr_decode_opts), c_void_p]
     lib.lowrank_kv_append.restype = c_int32
     lib.lowrank_kv_append.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                       c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
@@ -187,6 +195,32 @@ def lowrank_attn_decode(model: Model, layer: int, cache: Cache, q: torch.Tensor,
     _check(load().lowrank_attn_decode(ctypes.byref(model.desc), layer, ctypes.byref(cache.c), q.shape[0],
                                       max_lat_len, _ptr(q), _ptr(out), out_dtype, _ptr(workspace), ws_bytes,
                                       _opts(nsplit, events), _stream(stream)))
+
+
+def lowrank_attn_prefill_workspace_size(model: Model, layer: int, batch: int, n_new: int, max_lat_len: int,
+                                        nsplit: int = 0) -> int:
+    return int(load().lowrank_attn_prefill_workspace_size(ctypes.byref(model.desc), layer, batch, n_new,
+                                                          max_lat_len, _opts(nsplit)))
+
+
+def lowrank_attn_prefill(model: Model, layer: int, cache: Cache, q: torch.Tensor, k_new: torch.Tensor,
+                         v_new: torch.Tensor, out: torch.Tensor, max_lat_len: int, workspace: torch.Tensor,
+                         nsplit: int = 0, stream=None, events=None) -> None:
+    """q [B][n_new][Hq][d], k_new/v_new [B][n_new][D], out [B][n_new][Hq][d]."""
+    out_dtype = LR_F32 if out.dtype == torch.float32 else LR_BF16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().lowrank_attn_prefill(ctypes.byref(model.desc), layer, ctypes.byref(cache.c), q.shape[0],
+                                       q.shape[1], max_lat_len, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                       out_dtype, _ptr(workspace), ws_bytes, _opts(nsplit, events),
+                                       _stream(stream)))
+
+
+def prefill_workspace(model: Model, layer: int, batch: int, n_new: int, max_lat_len: int, nsplit: int = 0,
+                      device="cuda") -> torch.Tensor:
+    n = lowrank_attn_prefill_workspace_size(model, layer, batch, n_new, max_lat_len, nsplit)
+    if n == 0:
+        raise LowRankError(LR_EINVAL, "workspace size query rejected the arguments")
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def lowrank_kv_append(model: Model, layer: int, cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor,

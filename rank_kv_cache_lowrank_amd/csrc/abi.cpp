@@ -70,12 +70,12 @@ static void layout_workspace(DecodePlan* p) {
   p->off_acc = off;
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * 4);
   p->off_win = off;
-  if (p->window > 0) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);
+  if (p->exact) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);
   p->ws_bytes = off > 0 ? off : 256;
 }
 
-int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const lr_decode_opts* o,
-                DecodePlan* p, const char** msg) {
+int plan_attention(const lr_model_desc* m, int layer, int batch, int n_q, bool prefill, int max_len,
+                   const lr_decode_opts* o, DecodePlan* p, const char** msg) {
   int rk = 0, rv = 0;
   int st = check_model(m, layer, &rk, &rv, msg);
   if (st != LR_OK) return st;
@@ -87,8 +87,12 @@ int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const
     if (bad) return *msg = "lr_decode_opts reserved fields must be zero", LR_EINVAL;
     if (o->nsplit < 0) return *msg = "nsplit must be >= 0", LR_EINVAL;
   }
+  if (n_q < 1 || n_q > 65536) return *msg = "tokens per sequence must be in 1..65536", LR_EINVAL;
+  if ((int64_t)batch * n_q > 65535) return *msg = "batch x query tokens must be <= 65535", LR_EINVAL;
   memset(p, 0, sizeof(*p));
-  p->B = batch;
+  p->B = batch * n_q;
+  p->qpb = n_q;
+  p->exact = (m->window > 0 || prefill) ? 1 : 0;
   p->Hq = m->n_q_heads;
   p->Hkv = m->n_kv_heads;
   p->d = m->head_dim;
@@ -106,7 +110,8 @@ int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const
 
   // token ranges: about one workgroup per compute unit over the batch unless overridden
   const int max_split = max_len > 0 ? (max_len + kTileTokens - 1) / kTileTokens : 1;
-  int target = (o && o->nsplit > 0) ? o->nsplit : (device_cu_count() + (batch > 0 ? batch : 1) - 1) / (batch > 0 ? batch : 1);
+  const int nb = p->B > 0 ? p->B : 1;
+  int target = (o && o->nsplit > 0) ? o->nsplit : (device_cu_count() + nb - 1) / nb;
   if (target < 1) target = 1;
   if (target > kMaxSplit) target = kMaxSplit;
   if (target > max_split) target = max_split;
@@ -129,7 +134,7 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   const int es = p->latent == LR_F32 ? 4 : 2;
   const int KS = decode_ks(p->nks), RB = decode_rb(p->nrb);
   int window_lds = 0;
-  if (p->window > 0)
+  if (p->exact)
     window_lds = p->Hq * p->d * 4 + 2 * 32 * p->D * 2 + p->Hq * 32 * 4 + p->Hq * 3 * 4;
   if (p->latent == LR_I4G32) {
     const int gk = (p->rk + 31) / 32, gv = (p->rv + 31) / 32;
@@ -254,6 +259,53 @@ int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_laye
   hipError_t e = launch_decode(p, cache, q, out, out_dtype, workspace, (hipStream_t)stream,
                                opts ? (hipEvent_t)opts->event_begin : nullptr,
                                opts ? (hipEvent_t)opts->event_end : nullptr);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+size_t lowrank_attn_prefill_workspace_size(const lr_model_desc* model, int32_t layer, int32_t batch,
+                                           int32_t n_new, int32_t max_lat_len, const lr_decode_opts* opts) {
+  try {
+    DecodePlan p;
+    const char* msg = "";
+    if (plan_attention(model, layer, batch, n_new, true, max_lat_len, opts, &p, &msg) != LR_OK) return 0;
+    return p.ws_bytes;
+  } catch (...) {
+    return 0;
+  }
+}
+
+int lowrank_attn_prefill(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                         int32_t batch, int32_t n_new, int32_t max_lat_len, const void* q,
+                         const void* k_new, const void* v_new, void* out, int32_t out_dtype,
+                         void* workspace, size_t workspace_bytes, const lr_decode_opts* opts, void* stream) {
+  LR_GUARD_BEGIN
+  DecodePlan p;
+  const char* msg = "";
+  int st = plan_attention(model, layer, batch, n_new, true, max_lat_len, opts, &p, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  st = check_cache_common(model, cache, p.rk, p.rv, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if ((int64_t)max_lat_len > cache->t_cap) return fail(LR_EINVAL, "max_lat_len must be <= t_cap");
+  if (!q || !out || !k_new || !v_new) return fail(LR_EINVAL, "q, k_new, v_new and out must not be NULL");
+  if (!cache->bk || !cache->bv) return fail(LR_EINVAL, "bases bk/bv must not be NULL");
+  if (!aligned(cache->bk, 16) || !aligned(cache->bv, 16) || !aligned(q, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16))
+    return fail(LR_EINVAL, "q, k_new, v_new and the bases must be 16-byte aligned");
+  if (out_dtype != LR_F32 && out_dtype != LR_BF16) return fail(LR_EINVAL, "out_dtype must be LR_F32 or LR_BF16");
+  if (p.latent == LR_I4G32 && (!aligned(cache->zk_qp, 16) || !aligned(cache->zv_qp, 16)))
+    return fail(LR_EINVAL, "int4 needs 16-byte aligned scale/zero buffers");
+  st = plan_lds(&p, cache->ld_k, cache->ld_v, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (!workspace) return fail(LR_EINVAL, "workspace must not be NULL");
+  if (!aligned(workspace, 256)) return fail(LR_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.ws_bytes) return fail(LR_EWORKSPACE, "workspace too small");
+  if (batch == 0) return LR_OK;
+  p.t_cap = cache->t_cap;
+  hipError_t e = launch_decode(p, cache, q, out, out_dtype, workspace, (hipStream_t)stream,
+                               opts ? (hipEvent_t)opts->event_begin : nullptr,
+                               opts ? (hipEvent_t)opts->event_end : nullptr, k_new, v_new);
   if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
   return LR_OK;
   LR_GUARD_END

@@ -16,7 +16,7 @@
 //               A += P Zv on the matrix cores. All 28 query heads share the one latent stream,
 //               so every latent byte is read from HBM once. Writes (m, l, A) per range.
 //               Extra workgroups (first in the grid) attend over the exact window, if any.
-//   lr_combine  one workgroup per (sequence, head): merges the ranges and the window partial
+//   lr_combine  one workgroup per (sequence, head): merges the ranges and the exact-keys partial
 //               and up-projects through Bv[:, g(j)].
 // int4 latents (groups of 32 with an fp16 scale and zero): the loads bring the codes and the
 // scale/zero words into a raw LDS ring, the producer waves dequantise each tile into an fp16
@@ -57,6 +57,10 @@ struct DecodeArgs {
   int stage_bytes, zv_off, qpk_off, qpv_off, nst;
   int copy_k, copy_v;       // bytes of each stored row the LDS ring holds
   int nr, raw_stage;        // int4: raw stages in the ring and their size in bytes
+  int qpb;                  // query tokens per stored sequence: 1 (decode) or the chunk (prefill);
+                            // query sequence sq reads the latents of stored sequence sq / qpb
+  const __bf16* kchunk;     // prefill: the chunk's exact rows [B][qpb][D]; NULL for decode
+  const __bf16* vchunk;
 };
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
@@ -165,20 +169,23 @@ __device__ __forceinline__ bf16x4 v_operand_tr(const unsigned char* p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Exact-window workgroup: dense attention of every head over the live window slots of one
-// sequence (iS-KV abstract: the recent window is kept exact). Writes (Aw[d], m, l) per head,
-// in base-2 softmax units like the latent partials.
+// Exact-keys workgroup of query sequence sq: dense attention of every head over the live window
+// slots of its stored sequence (iS-KV abstract: the recent window is kept exact) and, in a
+// prefill, over the chunk's own rows up to and including its token (causal). Writes (Aw[d], m,
+// l) per head, in base-2 softmax units like the latent partials.
 // ---------------------------------------------------------------------------------------------
 template <int LT, int NTHR>
 __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
-  const int b = blockIdx.x;
+  const int sq = blockIdx.x;
+  const int b = sq / a.qpb, ci = sq - b * a.qpb;       // stored sequence, token of the chunk
   const int tid = threadIdx.x;
   const int Hq = a.Hq, d = a.d, D = a.D, W = a.window;
   const int grp = Hq / a.Hkv;
   int L = a.lat_len[b];
   L = L < 0 ? 0 : L;
-  int wl = a.win_len[b];
+  int wl = W > 0 ? a.win_len[b] : 0;
   wl = wl < 0 ? 0 : (wl > W ? W : wl);
+  const int nkeys = wl + (a.kchunk ? ci + 1 : 0);      // window slots, then chunk rows 0 .. ci
 
   float* qs = (float*)smem;                              // [Hq][d]
   __bf16* kc = (__bf16*)(qs + Hq * d);                   // [32][D]
@@ -188,8 +195,8 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
 
   for (int i = tid; i < Hq * d; i += NTHR) {
     float qv;
-    if constexpr (LT == LT_F32) qv = ((const float*)a.q)[(size_t)b * Hq * d + i];
-    else qv = (float)((const __bf16*)a.q)[(size_t)b * Hq * d + i];
+    if constexpr (LT == LT_F32) qv = ((const float*)a.q)[(size_t)sq * Hq * d + i];
+    else qv = (float)((const __bf16*)a.q)[(size_t)sq * Hq * d + i];
     qs[i] = qv * a.wscale;
   }
   for (int j = tid; j < Hq; j += NTHR) { st[j * 3] = -INFINITY; st[j * 3 + 1] = 0.f; }
@@ -200,17 +207,26 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
   for (int u = 0; u < kMaxAcc; ++u) acc[u] = 0.f;
   const int nout = Hq * d;
 
-  for (int c0 = 0; c0 < wl; c0 += 32) {
-    const int n = (wl - c0) < 32 ? (wl - c0) : 32;
+  for (int c0 = 0; c0 < nkeys; c0 += 32) {
+    const int n = (nkeys - c0) < 32 ? (nkeys - c0) : 32;
     __syncthreads();
-    // stage n window rows (16 bytes per thread per step)
+    // stage n exact rows (16 bytes per thread per step)
     const int vec_per_row = D / 8;
     for (int i = tid; i < n * vec_per_row; i += NTHR) {
       const int u = i / vec_per_row, c = i - u * vec_per_row;
-      const int slot = (L + c0 + u) % W;
-      const size_t src = ((size_t)b * W + slot) * D + c * 8;
-      *(u32x4*)(kc + u * D + c * 8) = *(const u32x4*)(a.kwin + src);
-      *(u32x4*)(vc + u * D + c * 8) = *(const u32x4*)(a.vwin + src);
+      const int e = c0 + u;
+      const __bf16 *ks, *vs;
+      if (e < wl) {
+        const size_t src = ((size_t)b * W + (L + e) % W) * D + c * 8;
+        ks = a.kwin + src;
+        vs = a.vwin + src;
+      } else {
+        const size_t src = ((size_t)b * a.qpb + (e - wl)) * D + c * 8;
+        ks = a.kchunk + src;
+        vs = a.vchunk + src;
+      }
+      *(u32x4*)(kc + u * D + c * 8) = *(const u32x4*)ks;
+      *(u32x4*)(vc + u * D + c * 8) = *(const u32x4*)vs;
     }
     __syncthreads();
     for (int i = tid; i < Hq * 32; i += NTHR) {
@@ -257,7 +273,7 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
     }
   }
   __syncthreads();
-  float* wp = a.win_part + (size_t)b * Hq * (d + 2);
+  float* wp = a.win_part + (size_t)sq * Hq * (d + 2);
 #pragma unroll
   for (int u = 0; u < kMaxAcc; ++u) {
     const int o = tid + u * NTHR;
@@ -462,8 +478,9 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   static_assert(I4 || ((kTileTokens * SK + 1023) / 1024 <= kProducers * kMaxChunkPerProducer &&
                        (kTileTokens * SV + 1023) / 1024 <= kProducers * kMaxChunkPerProducer), "DMA chunks");
 
-  const int b = wg / a.nsplit;
-  const int s = wg - b * a.nsplit;
+  const int sq = wg / a.nsplit;                      // query sequence (token of a chunk)
+  const int s = wg - sq * a.nsplit;
+  const int b = sq / a.qpb;                          // stored sequence whose latents it reads
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const bool producer = wave >= 4 * G;
@@ -583,7 +600,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       // The folded query arrives in float32. Its largest magnitude per head is brought into
       // [2^14, 2^15) by a power of two so that the fp16 operand cannot overflow; the scores are
       // multiplied back by that power. The 4 lane groups holding a head share its scale.
-      const float* qrow = (const float*)a.qt + ((size_t)b * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
+      const float* qrow = (const float*)a.qt + ((size_t)sq * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
       float qf[KS][8];
       float mxq = 0.f;
 #pragma unroll
@@ -616,7 +633,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         qop[ks] = __builtin_bit_cast(bf16x8, h);
       }
     } else {
-      const __bf16* qrow = a.qt + ((size_t)b * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
+      const __bf16* qrow = a.qt + ((size_t)sq * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         qop[ks] = (ks < a.nks) ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
@@ -797,7 +814,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
 #pragma unroll
       for (int j = 0; j < NVB; ++j) acc[j] += abuf[(x * NVB + j) * 64 + lane] * wb;
     }
-    const size_t pidx = (size_t)b * a.nsplit + s;
+    const size_t pidx = (size_t)sq * a.nsplit + s;
     const int head = hb * 16 + li;
     if (half == 0 && lg == 0 && head < a.Hq) {
       a.part_ml[(pidx * a.Hq + head) * 2] = ms;
@@ -942,7 +959,8 @@ struct CombineArgs {
   const float* win_part;
   const void* bv;
   void* out;
-  int Hq, Hkv, d, D, rv, rv_pad16, nsplit, window;
+  int Hq, Hkv, d, D, rv, rv_pad16, nsplit;
+  int exact;                // exact-keys partials present (window or prefill chunk)
   int i4_order;             // partials are in the dequantised int4 tiles' block order
 };
 
@@ -984,7 +1002,7 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   for (int s = tid; s < a.nsplit; s += 256) mloc = fmaxf(mloc, a.part_ml[((base + s) * a.Hq + j) * 2]);
   float mw = -INFINITY, lw = 0.f;
   const float* wp = a.win_part + ((size_t)b * a.Hq + j) * (a.d + 2);
-  if (a.window) { mw = wp[a.d]; lw = wp[a.d + 1]; }
+  if (a.exact) { mw = wp[a.d]; lw = wp[a.d + 1]; }
   const float mstar = block_reduce(fmaxf(mloc, mw), red, true);
   const bool live = mstar != -INFINITY;
 
@@ -1121,7 +1139,8 @@ static hipError_t dispatch_decode(const DecodePlan& p, const DecodeArgs& args, i
 }
 
 hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* out,
-                         int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
+                         int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
+                         const void* k_chunk, const void* v_chunk) {
   unsigned char* w = (unsigned char*)ws;
   __bf16* qt = (__bf16*)(w + p.off_qt);
   const float scale = p.sm_scale * kLog2e;
@@ -1144,7 +1163,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
     if (e != hipSuccess) return e;
   }
 
-  // 2. latent decode (+ window workgroups)
+  // 2. latent decode (+ exact-keys workgroups: window, prefill chunk)
   DecodeArgs a;
   a.zk = (const unsigned char*)c->zk;
   a.zv = (const unsigned char*)c->zv;
@@ -1179,7 +1198,10 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.D = p.D;
   a.window = p.window;
   a.wscale = scale;
-  a.n_win_blocks = p.window > 0 ? p.B : 0;
+  a.n_win_blocks = p.exact ? p.B : 0;
+  a.qpb = p.qpb;
+  a.kchunk = (const __bf16*)k_chunk;
+  a.vchunk = (const __bf16*)v_chunk;
   a.stage_bytes = p.stage_bytes;
   a.zv_off = p.zv_off;
   a.qpk_off = p.qpk_off;
@@ -1210,7 +1232,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   ca.rv = p.rv;
   ca.rv_pad16 = p.rv_pad16;
   ca.nsplit = p.nsplit;
-  ca.window = p.window;
+  ca.exact = p.exact;
   ca.i4_order = p.latent == LR_I4G32;
   const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);

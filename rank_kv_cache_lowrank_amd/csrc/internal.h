@@ -63,7 +63,10 @@ constexpr int lds_nst(int KS, int RB, int es) {   // stages in the ring: even, a
 }
 
 struct DecodePlan {
-  int B, Hq, Hkv, d, D;
+  int B;               // query sequences: stored sequences x qpb
+  int qpb;             // query tokens per stored sequence (1 = decode, the chunk = prefill)
+  int exact;           // exact-keys workgroups run (window > 0, or a prefill chunk)
+  int Hq, Hkv, d, D;
   int rk, rv;
   int rk_pad;          // rk rounded up to 32 (matrix-core K steps)
   int rv_pad16;        // rv rounded up to 16 (matrix-core M blocks)
@@ -82,12 +85,18 @@ struct DecodePlan {
   size_t off_qt, off_ml, off_acc, off_win, ws_bytes;
 };
 
-// Fills *p; returns LR_OK or an error code with a message in *msg.
-int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const lr_decode_opts* o,
-                DecodePlan* p, const char** msg);
+// Fills *p; returns LR_OK or an error code with a message in *msg. n_q query tokens per stored
+// sequence; prefill: the queries are a chunk whose own rows are exact keys (causal).
+int plan_attention(const lr_model_desc* m, int layer, int batch, int n_q, bool prefill, int max_len,
+                   const lr_decode_opts* o, DecodePlan* p, const char** msg);
+inline int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len, const lr_decode_opts* o,
+                       DecodePlan* p, const char** msg) {
+  return plan_attention(m, layer, batch, 1, false, max_len, o, p, msg);
+}
 
 hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* out,
-                         int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
+                         int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
+                         const void* k_chunk = nullptr, const void* v_chunk = nullptr);
 
 struct AppendPlan {
   int B, D, rk, rv, latent, window, n_new;

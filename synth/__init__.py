@@ -30,7 +30,7 @@ import torch
 
 # Stream ids of the seed sequence [cfg_id, stream, layer, b].
 STREAM = dict(q=0, zk=1, zv=2, bk=3, bv=4, lengths=5, ranks=6, k_new=7, v_new=8,
-              window=9, needle=10, perm=11, bk_next=12, bv_next=13)
+              window=9, needle=10, perm=11, bk_next=12, bv_next=13, q_chunk=14, kv_chunk=15)
 
 N_Q_HEADS = 28
 N_KV_HEADS = 4
@@ -181,6 +181,24 @@ def gen_new_tokens(cfg: Config, which: str, layer: int, n_new: int) -> np.ndarra
 def down_projection(basis_stored: np.ndarray) -> np.ndarray:
     """P = pinv(B) [D, rank] in float64, computed by the caller from the stored basis."""
     return np.linalg.pinv(np.asarray(basis_stored, dtype=np.float64))
+
+
+def gen_chunk(cfg: Config, layer: int, n_new: int, q_scale: float = 1.0, rank: Optional[int] = None):
+    """A prefill chunk: q [B, n_new, Hq, d] ~ N(0, 1/d) * q_scale, and exact k, v rows
+    [B, n_new, D] ~ N(0, H_r / D) (the variance of a reconstructed history row, as for the
+    window rows), float32."""
+    r = rank if rank is not None else layer_ranks(cfg, layer)[0]
+    h = float(np.sum(1.0 / np.arange(1, r + 1)))
+    q = np.empty((cfg.batch, n_new, cfg.n_q_heads, cfg.head_dim), np.float32)
+    k = np.empty((cfg.batch, n_new, cfg.kv_width), np.float32)
+    v = np.empty_like(k)
+    for b in range(cfg.batch):
+        g = rng(cfg.cfg_id, "q_chunk", layer, b)
+        q[b] = g.standard_normal(q[b].shape, dtype=np.float32) * np.float32(q_scale / np.sqrt(cfg.head_dim))
+        g = rng(cfg.cfg_id, "kv_chunk", layer, b)
+        k[b] = g.standard_normal(k[b].shape, dtype=np.float32) * np.float32(np.sqrt(h / cfg.kv_width))
+        v[b] = g.standard_normal(v[b].shape, dtype=np.float32) * np.float32(np.sqrt(h / cfg.kv_width))
+    return q, k, v
 
 
 def gen_basis_update(cfg: Config, which: str, layer: int, old_basis: np.ndarray, rank_new: int,

@@ -1,0 +1,166 @@
+"""GPU parity of lowrank_attn_prefill (chunked prefill attention) against the oracle (P2, on the
+same stored inputs), at the decode tolerances: 5e-3 (fp32/bf16 latents), 1e-2 (int4)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import rank_kv_cache_lowrank_amd as lr
+from helpers import TOL, device_layer, oracle_latents, rel_err
+from oracle import prefill as OP
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_prefill(model, cache, q, k, v, max_len, nsplit=0, out_dtype=torch.float32):
+    B, C, Hq, d = q.shape
+    n = q.numel()
+    pad = 1024
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=out_dtype, device=DEV)
+    out = buf[pad:pad + n].view(B, C, Hq, d)
+    ws = lr.prefill_workspace(model, 0, B, C, max_len, nsplit)
+    lr.lowrank_attn_prefill(model, 0, cache, q, k, v, out, max_len, ws, nsplit=nsplit)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:pad].float()).all() and torch.isnan(buf[pad + n:].float()).all(), \
+        "prefill wrote outside out"
+    return out.float().cpu().numpy()
+
+
+def chunk_inputs(cfg, C, q_scale=1.0, rank=None):
+    q, k, v = synth.gen_chunk(cfg, 0, C, q_scale, rank)
+    qdt = "f32" if cfg.latent == "f32" else "bf16"
+    return (synth.to_storage(q, qdt).to(DEV), synth.to_storage(k, "bf16").to(DEV),
+            synth.to_storage(v, "bf16").to(DEV))
+
+
+def oracle(li, q, k, v, batches=None):
+    cfg = li.cfg
+    batches = list(range(cfg.batch)) if batches is None else list(batches)
+    zk = oracle_latents(li, "k", batches)
+    zv = oracle_latents(li, "v", batches)
+    idx = {b: i for i, b in enumerate(batches)}
+
+    class ByB:
+        def __init__(self, rows):
+            self.rows = rows
+
+        def __getitem__(self, b):
+            return self.rows[idx[b]]
+
+    kw = li.kwin.float().numpy() if li.kwin is not None else None
+    vw = li.vwin.float().numpy() if li.vwin is not None else None
+    return OP.prefill_latent(q.float().cpu().numpy(), ByB(zk), ByB(zv), li.bk.float().numpy(),
+                             li.bv.float().numpy(), li.lat_len, li.rank_k, li.rank_v, cfg.n_kv_heads,
+                             cfg.sm_scale, k.float().cpu().numpy(), v.float().cpu().numpy(), kwin=kw, vwin=vw,
+                             win_len=li.win_len, window=cfg.window, batches=batches)
+
+
+def small(latent, rank, B=3, L=(0, 37, 300), window=0, wl=None, t_cap=None):
+    cfg = synth.Config(90, f"prefill-{latent}-r{rank}", batch=B, seq_len=max(L), rank_k=rank, rank_v=rank,
+                       latent=latent, window=window)
+    li = synth.make_layer(cfg, lat_len=np.asarray(L, np.int32), t_cap=t_cap,
+                          win_len=None if wl is None else np.asarray(wl, np.int32))
+    return cfg, li
+
+
+@pytest.mark.parametrize("latent,rank,C", [("bf16", 358, 8), ("bf16", 256, 5), ("bf16", 64, 17),
+                                           ("f32", 128, 6), ("i4g32", 358, 4), ("bf16", 512, 3)])
+def test_prefill_matches_oracle(latent, rank, C):
+    cfg, li = small(latent, rank)
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, C, rank=rank)
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
+    ref = oracle(li, q, k, v)
+    assert rel_err(out, ref) < TOL[latent]
+
+
+@pytest.mark.parametrize("q_scale", [32.0, 128.0])
+def test_prefill_sharp_queries(q_scale):
+    cfg, li = small("bf16", 256, L=(200, 64, 1))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 6, q_scale)
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
+def test_prefill_with_exact_window():
+    cfg, li = small("bf16", 358, L=(120, 0, 33), window=16, wl=(16, 5, 0))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 7)
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("nsplit", [1, 3, 16])
+def test_prefill_split_invariance(nsplit):
+    cfg, li = small("bf16", 358, L=(500, 77, 260))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 4)
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()), nsplit=nsplit)
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
+def test_prefill_bf16_output_and_empty_cache():
+    cfg, li = small("bf16", 128, L=(0, 0, 5))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 3)
+    out = run_prefill(model, cache, q, k, v, 5, out_dtype=torch.bfloat16)
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+    # the first token of an empty sequence attends to itself only: its own value rows
+    vv = v.float().cpu().numpy()
+    for j in range(28):
+        g = j // 7
+        np.testing.assert_allclose(out[0, 0, j], vv[0, 0, g * 128:(g + 1) * 128], rtol=1e-2, atol=1e-3)
+
+
+def test_chunk_then_append_then_next_chunk():
+    """Prefill a chunk, store it with lowrank_kv_append (projection + storage), prefill the next
+    chunk: the second chunk sees the first one's stored latents (read back exactly) as history."""
+    C = 8
+    cfg, li = small("bf16", 256, L=(40, 3, 100), t_cap=100 + C)
+    model, cache = device_layer(li, with_proj=True)
+    q1, k1, v1 = chunk_inputs(cfg, C)
+    run_prefill(model, cache, q1, k1, v1, int(li.lat_len.max()))
+    lr.lowrank_kv_append(model, 0, cache, k1, v1)
+    torch.cuda.synchronize()
+    lat2 = cache.lat_len.cpu().numpy()
+    np.testing.assert_array_equal(lat2, li.lat_len + C)
+    T2 = int(lat2.max())
+    ok = torch.empty(cfg.batch, T2, li.rank_k, dtype=torch.float32, device=DEV)
+    ov = torch.empty(cfg.batch, T2, li.rank_v, dtype=torch.float32, device=DEV)
+    lr.lowrank_kv_dequant(model, 0, cache, cfg.batch, T2, ok, ov)
+    q2 = q1.flip(1).contiguous()
+    k2 = (k1 * 0.5).contiguous()
+    v2 = (-v1).contiguous()
+    out = run_prefill(model, cache, q2, k2, v2, T2)
+    zk = ok.cpu().numpy()
+    zv = ov.cpu().numpy()
+    ref = OP.prefill_latent(q2.float().cpu().numpy(), zk, zv, li.bk.float().numpy(), li.bv.float().numpy(), lat2,
+                            li.rank_k, li.rank_v, cfg.n_kv_heads, cfg.sm_scale, k2.float().cpu().numpy(),
+                            v2.float().cpu().numpy())
+    assert rel_err(out, ref) < TOL["bf16"]
+
+
+def test_full_size_sampled():
+    """16 sequences x 4096 latent rows at rank 358 (bf16) and a 32-token chunk, sampled sequences."""
+    cfg = synth.CONFIGS[1]
+    li = synth.make_layer(cfg)
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 32)
+    out = run_prefill(model, cache, q, k, v, cfg.seq_len)
+    batches = [0, 7, 15]
+    ref = oracle(li, q, k, v, batches)
+    assert rel_err(out[batches], ref) < TOL["bf16"]
+
+
+def test_invalid_arguments():
+    cfg, li = small("bf16", 64, L=(4, 4, 4))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 2)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    ws = lr.prefill_workspace(model, 0, 3, 2, 4)
+    with pytest.raises(lr.LowRankError):
+        lr.lowrank_attn_prefill(model, 0, cache, q, k, v, out, 4, ws[:16])
+    assert lr.lowrank_attn_prefill_workspace_size(model, 0, 3, 0, 4) == 0
+    assert lr.lowrank_attn_prefill_workspace_size(model, 0, 65536, 1, 4) == 0
