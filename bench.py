@@ -265,6 +265,83 @@ def rebase_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def prefill_bench(args):
+    """Chunked prefill attention of one layer: every sequence's chunk of --chunk new tokens
+    attends over its latent history and, causally, over itself. One call = fold, the latent
+    kernel (timed with HIP events attached to its dispatch), the exact-keys workgroups and the
+    combine. Algorithmic FLOPs of the latent kernel: 2 * Hq * (rank_k + rank_v) per (query
+    token, latent token)."""
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+    import synth
+    from synth.device import device_layer
+
+    dev = "cuda"
+    cfg = synth.CONFIGS[args.config]
+    if cfg.n_layers != 1:
+        raise SystemExit("--op prefill times single-layer configurations (0-3)")
+    K, W = args.steps, args.warmup
+    B, T, C = cfg.batch, cfg.seq_len, args.chunk
+    log(f"generating inputs for {cfg.name} ...")
+    li = synth.make_layer(cfg, t_cap=T, lat_len=np.full(B, T, np.int32))
+    model, cache = device_layer(li, dev)
+    q, k, v = synth.gen_chunk(cfg, 0, C)
+    qdt = torch.float32 if cfg.latent == "f32" else torch.bfloat16
+    q = torch.from_numpy(q).to(qdt).to(dev)
+    k = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    v = torch.from_numpy(v).to(torch.bfloat16).to(dev)
+    out = torch.empty(B, C, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+    ws = lr.prefill_workspace(model, 0, B, C, T, args.nsplit)
+    ev = HipEvents()
+    evs = [(ev.create(), ev.create()) for _ in range(K)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for i in range(W + K):
+        if i == W:
+            torch.cuda.synchronize()
+            start.record()
+        lr.lowrank_attn_prefill(model, 0, cache, q, k, v, out, T, ws, nsplit=args.nsplit,
+                                events=evs[i - W] if i >= W else None)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_call = start.elapsed_time(stop) / K
+    kern_ms = float(np.mean([ev.elapsed_ms(a, b) for a, b in evs]))
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    assert torch.isfinite(out).all(), "non-finite output"
+    flops = 2.0 * B * C * T * cfg.n_q_heads * (li.rank_k + li.rank_v)
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    value = B * C / (ms_per_call * 1e-3)
+    log(f"ms/call {ms_per_call:.4f}  latent kernel {kern_ms * 1e3:.2f} us  {tflops:.1f} TFLOP/s  "
+        f"{value:.0f} query tokens/s")
+    rec = {
+        "metric": "chunked prefill attention over the latent cache: query tokens per second",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_call, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.latent,
+        "data": "synthetic",
+        "config": {"workload": f"prefill {cfg.name} chunk{C}", "batch": B, "seq_len": T, "chunk": C,
+                   "rank_k": li.rank_k, "rank_v": li.rank_v, "latent": cfg.latent, "q_heads": cfg.n_q_heads,
+                   "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "lr_decode (prefill query sequences)", "achieved": round(tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_us": round(kern_ms * 1e3, 2), "flops_per_launch": flops},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,8 +354,10 @@ def main():
                     help="cache copies rotated over the steps (0: enough that the copies exceed 2 x 256 MB)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 256 MiB device copy (the counter calibration reference)")
-    ap.add_argument("--op", choices=("decode", "rebase"), default="decode",
-                    help="decode: the decode step (default); rebase: the historical-coordinate sync")
+    ap.add_argument("--op", choices=("decode", "rebase", "prefill"), default="decode",
+                    help="decode: the decode step (default); rebase: the historical-coordinate sync; "
+                         "prefill: chunked prefill attention")
+    ap.add_argument("--chunk", type=int, default=32, help="--op prefill: new tokens per sequence")
     ap.add_argument("--rank-new", type=int, default=0, help="--op rebase: new rank (0: unchanged)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -294,6 +373,9 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     if args.op == "rebase":
         rebase_bench(args)
+        return
+    if args.op == "prefill":
+        prefill_bench(args)
         return
     dev = "cuda"
     cfg = synth.CONFIGS[args.config]
