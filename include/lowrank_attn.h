@@ -253,6 +253,27 @@ int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_
                       int32_t rank_k_new, int32_t rank_v_new, const void* wk, const void* wv,
                       void* stream);
 
+/*
+ * Global rank allocation (TraceKV abstract; ai4snews Synopsis and Interpretation: the rank
+ * budget is allocated globally across the KV states). Rule (the pages do not give one): every
+ * matrix m (K or V of a layer) starts at r_min and grows by granules of `granule` up to r_max;
+ * while the budget allows, the granule with the largest energy gain
+ * sum_{k=r}^{r+granule-1} sigma_m[k]^2 is added (float64, index order; equal gains: lower m
+ * first). Equivalently the best min(floor((budget - n_mat*r_min)/granule), all) granules of
+ * the model are taken.
+ *   sigma [n_mat][sigma_ld] float32: each matrix's spectrum (its sensitivity-weighted singular
+ *     values), non-increasing and finite, n_sigma >= r_max entries used. With a spectrum that
+ *     increases somewhere the result is the best-granules rule, not the greedy one.
+ *   ranks [n_mat] int32 (output): r_min + granule * (granules given to m).
+ *   Requires 1 <= r_min <= r_max <= n_sigma, (r_max - r_min) % granule == 0,
+ *   budget >= n_mat * r_min, n_mat * (r_max - r_min) / granule <= 65536.
+ *   workspace: lowrank_rank_allocate_workspace_size() bytes, 256-byte aligned.
+ */
+size_t lowrank_rank_allocate_workspace_size(int32_t n_mat, int32_t r_min, int32_t r_max, int32_t granule);
+int lowrank_rank_allocate(const float* sigma, int32_t n_mat, int32_t n_sigma, int32_t sigma_ld,
+                          int64_t budget, int32_t r_min, int32_t r_max, int32_t granule,
+                          int32_t* ranks, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this host thread ("" if none). */
 const char* lowrank_last_error(void);
 

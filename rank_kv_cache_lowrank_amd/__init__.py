@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     EXPORTS, LR_BF16, LR_EHIP, LR_EINVAL, LR_EUNSUPPORTED, LR_EWORKSPACE, LR_F32, LR_I4G32, LR_OK,
     Cache, LowRankError, Model, latent_storage, load, lowrank_abi_version, lowrank_attn_decode,
     lowrank_attn_decode_workspace_size, lowrank_attn_prefill, lowrank_attn_prefill_workspace_size,
-    lowrank_kv_append, lowrank_kv_dequant, lowrank_kv_rebase,
+    lowrank_kv_append, lowrank_kv_dequant, lowrank_kv_rebase, lowrank_rank_allocate,
+    lowrank_rank_allocate_workspace_size,
     lowrank_kv_store,
     lowrank_last_error, prefill_workspace, workspace)

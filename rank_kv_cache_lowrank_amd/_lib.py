@@ -22,7 +22,8 @@ LR_F32, LR_BF16, LR_I4G32 = 0, 1, 2
 DTYPES = {"f32": LR_F32, "bf16": LR_BF16, "i4g32": LR_I4G32}
 
 EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_attn_prefill_workspace_size",
-           "lowrank_attn_prefill", "lowrank_kv_append",
+           "lowrank_attn_prefill", "lowrank_rank_allocate_workspace_size", "lowrank_rank_allocate",
+           "lowrank_kv_append",
            "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_last_error",
            "lowrank_abi_version")
 
@@ -76,6 +77,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowrank_attn_prefill.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                          c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                          c_void_p, c_size_t, POINTER(lr_decode_opts), c_void_p]
+    lib.lowrank_rank_allocate_workspace_size.restype = c_size_t
+    lib.lowrank_rank_allocate_workspace_size.argtypes = [c_int32, c_int32, c_int32, c_int32]
+    lib.lowrank_rank_allocate.restype = c_int32
+    lib.lowrank_rank_allocate.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int64, c_int32, c_int32, c_int32,
+                                          c_void_p, c_void_p, c_size_t, c_void_p]
     lib.lowrank_kv_append.restype = c_int32
     lib.lowrank_kv_append.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                       c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
@@ -221,6 +227,19 @@ def prefill_workspace(model: Model, layer: int, batch: int, n_new: int, max_lat_
     if n == 0:
         raise LowRankError(LR_EINVAL, "workspace size query rejected the arguments")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lowrank_rank_allocate_workspace_size(n_mat: int, r_min: int, r_max: int, granule: int) -> int:
+    return int(load().lowrank_rank_allocate_workspace_size(n_mat, r_min, r_max, granule))
+
+
+def lowrank_rank_allocate(sigma: torch.Tensor, budget: int, r_min: int, r_max: int, granule: int,
+                          ranks: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """sigma [n_mat][n] float32 (row stride = its row length), ranks [n_mat] int32 output."""
+    n_mat, n = sigma.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().lowrank_rank_allocate(_ptr(sigma), n_mat, n, sigma.stride(0), budget, r_min, r_max, granule,
+                                        _ptr(ranks), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def lowrank_kv_append(model: Model, layer: int, cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor,

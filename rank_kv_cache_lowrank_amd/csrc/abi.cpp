@@ -444,6 +444,48 @@ int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_
   LR_GUARD_END
 }
 
+static int check_rank_args(int32_t n_mat, int32_t n_sigma, int32_t sigma_ld, int32_t r_min, int32_t r_max,
+                           int32_t granule, const char** msg) {
+  if (n_mat < 1) return *msg = "n_mat must be >= 1", LR_EINVAL;
+  if (granule < 1) return *msg = "granule must be >= 1", LR_EINVAL;
+  if (r_min < 1 || r_max < r_min || r_max > n_sigma) return *msg = "need 1 <= r_min <= r_max <= n_sigma", LR_EINVAL;
+  if (sigma_ld < n_sigma) return *msg = "sigma_ld must be >= n_sigma", LR_EINVAL;
+  if ((r_max - r_min) % granule != 0) return *msg = "r_max - r_min must be a multiple of granule", LR_EINVAL;
+  const int64_t N = (int64_t)n_mat * ((r_max - r_min) / granule);
+  if (N > 65536 || n_mat > 65536) return *msg = "at most 65536 granules and 65536 matrices", LR_EINVAL;
+  return LR_OK;
+}
+
+size_t lowrank_rank_allocate_workspace_size(int32_t n_mat, int32_t r_min, int32_t r_max, int32_t granule) {
+  const char* msg = "";
+  if (check_rank_args(n_mat, r_max, r_max, r_min, r_max, granule, &msg) != LR_OK) return 0;
+  const int64_t N = (int64_t)n_mat * ((r_max - r_min) / granule);
+  return align256((size_t)(N > n_mat ? N : n_mat) * 8);
+}
+
+int lowrank_rank_allocate(const float* sigma, int32_t n_mat, int32_t n_sigma, int32_t sigma_ld, int64_t budget,
+                          int32_t r_min, int32_t r_max, int32_t granule, int32_t* ranks, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  LR_GUARD_BEGIN
+  const char* msg = "";
+  int st = check_rank_args(n_mat, n_sigma, sigma_ld, r_min, r_max, granule, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (!sigma || !ranks || !workspace) return fail(LR_EINVAL, "sigma, ranks and workspace must not be NULL");
+  if (!aligned(sigma, 4) || !aligned(ranks, 4) || !aligned(workspace, 256))
+    return fail(LR_EINVAL, "sigma and ranks must be 4-byte aligned, workspace 256-byte aligned");
+  if (budget < (int64_t)n_mat * r_min) return fail(LR_EINVAL, "budget must be >= n_mat * r_min");
+  if (workspace_bytes < lowrank_rank_allocate_workspace_size(n_mat, r_min, r_max, granule))
+    return fail(LR_EWORKSPACE, "workspace too small");
+  const int nb = (r_max - r_min) / granule;
+  int64_t n_take = (budget - (int64_t)n_mat * r_min) / granule;
+  if (n_take > (int64_t)n_mat * nb) n_take = (int64_t)n_mat * nb;
+  hipError_t e = launch_rank_allocate(sigma, n_mat, sigma_ld, (long long)n_take, r_min, granule, nb, ranks,
+                                      workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
 const char* lowrank_last_error(void) { return g_last_error.c_str(); }
 
 int lowrank_abi_version(void) { return LOWRANK_ABI_VERSION; }

@@ -119,6 +119,9 @@ struct RebasePlan {
 
 hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const lr_layer_cache* dst,
                          const void* wk, const void* wv, hipStream_t st);
+hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, long long n_take, int r_min,
+                                int g, int nb, int32_t* ranks, void* ws, hipStream_t st);
+
 struct RebaseShape {
   int nks_t, nb, col_chunk, nchunk;
 };

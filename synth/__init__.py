@@ -30,7 +30,7 @@ import torch
 
 # Stream ids of the seed sequence [cfg_id, stream, layer, b].
 STREAM = dict(q=0, zk=1, zv=2, bk=3, bv=4, lengths=5, ranks=6, k_new=7, v_new=8,
-              window=9, needle=10, perm=11, bk_next=12, bv_next=13, q_chunk=14, kv_chunk=15)
+              window=9, needle=10, perm=11, bk_next=12, bv_next=13, q_chunk=14, kv_chunk=15, spectra=16)
 
 N_Q_HEADS = 28
 N_KV_HEADS = 4
@@ -199,6 +199,16 @@ def gen_chunk(cfg: Config, layer: int, n_new: int, q_scale: float = 1.0, rank: O
         k[b] = g.standard_normal(k[b].shape, dtype=np.float32) * np.float32(np.sqrt(h / cfg.kv_width))
         v[b] = g.standard_normal(v[b].shape, dtype=np.float32) * np.float32(np.sqrt(h / cfg.kv_width))
     return q, k, v
+
+
+def gen_spectra(cfg: Config, n_mat: int, n: int = 512) -> np.ndarray:
+    """Per-matrix singular spectra [n_mat, n] float32, non-increasing: sigma_k = s * k^(-a/2)
+    with a ~ U(0.3, 1.5) (how fast the energy decays) and s ~ U(0.5, 2) per matrix."""
+    g = rng(cfg.cfg_id, "spectra")
+    a = g.uniform(0.3, 1.5, size=n_mat)
+    sc = g.uniform(0.5, 2.0, size=n_mat)
+    k = np.arange(1, n + 1, dtype=np.float64)
+    return (sc[:, None] * k[None, :] ** (-a[:, None] / 2)).astype(np.float32)
 
 
 def gen_basis_update(cfg: Config, which: str, layer: int, old_basis: np.ndarray, rank_new: int,

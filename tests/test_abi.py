@@ -235,3 +235,27 @@ def test_missing_library_fails_loudly(tmp_path):
             L.load(str(tmp_path / "missing.so"))
     finally:
         L._lib = saved
+
+
+@host_only
+@pytest.mark.parametrize("args,code", [
+    ((4, 64, 64, 1000, 8, 64, 8), L.LR_OK),
+    ((4, 64, 64, 10, 8, 64, 8), L.LR_EINVAL),        # budget below n_mat * r_min
+    ((4, 64, 64, 1000, 8, 60, 8), L.LR_EINVAL),      # (r_max - r_min) % granule
+    ((4, 64, 64, 1000, 0, 64, 8), L.LR_EINVAL),      # r_min < 1
+    ((4, 64, 64, 1000, 8, 80, 8), L.LR_EINVAL),      # r_max > n_sigma
+    ((4, 64, 32, 1000, 8, 64, 8), L.LR_EINVAL),      # sigma_ld < n_sigma
+    ((0, 64, 64, 1000, 8, 64, 8), L.LR_EINVAL),      # no matrix
+    ((70000, 64, 64, 10 ** 9, 8, 64, 8), L.LR_EINVAL),  # too many granules
+])
+def test_rank_allocate_validation(args, code):
+    lib = lr.load()
+    n_mat, n_sigma, ld, budget, r_min, r_max, g = args
+    ws = lr.lowrank_rank_allocate_workspace_size(max(n_mat, 1), r_min, max(r_max, r_min), g)
+    if code == L.LR_OK:
+        # valid arguments enqueue work: only check the size query here
+        assert ws >= n_mat * ((r_max - r_min) // g) * 8
+        return
+    assert lib.lowrank_rank_allocate(1 << 20, n_mat, n_sigma, ld, budget, r_min, r_max, g, 1 << 21, 1 << 22,
+                                     1 << 30, None) == code
+    assert lr.lowrank_last_error() != ""
