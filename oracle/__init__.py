@@ -22,6 +22,7 @@ Modules
 ``quant``      int4 groups-of-32 min-max quantiser, nibble packing, exact dequantiser.
 ``append``     the append state machine: exact window ring, eviction, projection, storage.
 ``rebase``     historical-coordinate sync after a basis update (least-squares coordinates).
+``sensvd``     sensitivity-weighted SVD basis construction (top-r right singular vectors).
 ``rankalloc``  global rank allocation: greedy marginal energy gain under a total budget.
 ``prefill``    chunked prefill attention: a chunk's queries over the latent history, the exact
                window and the chunk itself (causal); P1 reconstruct, P2 latent, P3 brute force.
