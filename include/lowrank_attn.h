@@ -254,6 +254,25 @@ int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_
                       void* stream);
 
 /*
+ * Sensitivity-weighted SVD basis construction (TraceKV abstract; ai4snews Synopsis and
+ * Interpretation: KV states are weighted by their sensitivity before the SVD). For samples
+ * x [n_samples][dim] bfloat16 (one KV matrix's rows, e.g. calibration tokens) and sensitivities
+ * w [n_samples] float32 (finite, >= 0), with y_n = bf16(sqrt(w_n) * x_n) (float32 product, one
+ * rounding):
+ *   basis [rank][dim] (basis_dtype LR_F32 or LR_BF16): the top-rank right singular vectors of
+ *     Y as rows, each with its largest-magnitude component positive (ready as bk or bv);
+ *   sigma [dim] float32: all singular values of Y, descending (the spectrum for
+ *     lowrank_rank_allocate).
+ * Method: float32 Gram G = Y^T Y on the matrix cores, then block Jacobi on G (`sweeps` sweeps,
+ * 0 = 10; each sweep is dim/16 - 1 rounds of two launches). dim must be a multiple of 64 in
+ * 64..512. workspace: lowrank_sens_svd_workspace_size() bytes, 256-byte aligned.
+ */
+size_t lowrank_sens_svd_workspace_size(int32_t n_samples, int32_t dim);
+int lowrank_sens_svd(const void* x, const float* w, int32_t n_samples, int32_t dim, int32_t rank,
+                     int32_t sweeps, void* basis, int32_t basis_dtype, float* sigma,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Global rank allocation (TraceKV abstract; ai4snews Synopsis and Interpretation: the rank
  * budget is allocated globally across the KV states). Rule (the pages do not give one): every
  * matrix m (K or V of a layer) starts at r_min and grows by granules of `granule` up to r_max;

@@ -60,7 +60,8 @@ def basis(x, w, r: int):
     D = y.shape[1]
     if y.shape[0] == 0:
         return np.eye(D)[:r], np.zeros(D)
-    _, s, vt = np.linalg.svd(y, full_matrices=True)
+    # the thin factorisation already holds all D right singular vectors when N >= D
+    _, s, vt = np.linalg.svd(y, full_matrices=y.shape[0] < D)
     sig = np.zeros(D)
     sig[:s.shape[0]] = s
     return _fix_signs(vt[:r]), sig

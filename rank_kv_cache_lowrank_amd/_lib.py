@@ -22,7 +22,8 @@ LR_F32, LR_BF16, LR_I4G32 = 0, 1, 2
 DTYPES = {"f32": LR_F32, "bf16": LR_BF16, "i4g32": LR_I4G32}
 
 EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_attn_prefill_workspace_size",
-           "lowrank_attn_prefill", "lowrank_rank_allocate_workspace_size", "lowrank_rank_allocate",
+           "lowrank_attn_prefill", "lowrank_sens_svd_workspace_size", "lowrank_sens_svd",
+           "lowrank_rank_allocate_workspace_size", "lowrank_rank_allocate",
            "lowrank_kv_append",
            "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_last_error",
            "lowrank_abi_version")
@@ -77,6 +78,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowrank_attn_prefill.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                          c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                          c_void_p, c_size_t, POINTER(lr_decode_opts), c_void_p]
+    lib.lowrank_sens_svd_workspace_size.restype = c_size_t
+    lib.lowrank_sens_svd_workspace_size.argtypes = [c_int32, c_int32]
+    lib.lowrank_sens_svd.restype = c_int32
+    lib.lowrank_sens_svd.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                                     c_void_p, c_void_p, c_size_t, c_void_p]
     lib.lowrank_rank_allocate_workspace_size.restype = c_size_t
     lib.lowrank_rank_allocate_workspace_size.argtypes = [c_int32, c_int32, c_int32, c_int32]
     lib.lowrank_rank_allocate.restype = c_int32
@@ -227,6 +233,20 @@ def prefill_workspace(model: Model, layer: int, batch: int, n_new: int, max_lat_
     if n == 0:
         raise LowRankError(LR_EINVAL, "workspace size query rejected the arguments")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lowrank_sens_svd_workspace_size(n_samples: int, dim: int) -> int:
+    return int(load().lowrank_sens_svd_workspace_size(n_samples, dim))
+
+
+def lowrank_sens_svd(x: torch.Tensor, w: torch.Tensor, rank: int, basis: torch.Tensor, sigma: torch.Tensor,
+                     workspace: torch.Tensor, sweeps: int = 0, stream=None) -> None:
+    """x [n][dim] bf16, w [n] f32; basis [rank][dim] f32 or bf16 (output), sigma [dim] f32 (output)."""
+    n, dim = x.shape
+    bdt = LR_F32 if basis.dtype == torch.float32 else LR_BF16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().lowrank_sens_svd(_ptr(x), _ptr(w), n, dim, rank, sweeps, _ptr(basis), bdt, _ptr(sigma),
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def lowrank_rank_allocate_workspace_size(n_mat: int, r_min: int, r_max: int, granule: int) -> int:

@@ -119,6 +119,10 @@ struct RebasePlan {
 
 hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const lr_layer_cache* dst,
                          const void* wk, const void* wv, hipStream_t st);
+size_t svd_workspace_bytes(int n, int D);
+hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank, int sweeps, void* basis,
+                           int basis_f32, float* sigma, void* ws, hipStream_t st);
+
 hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, long long n_take, int r_min,
                                 int g, int nb, int32_t* ranks, void* ws, hipStream_t st);
 

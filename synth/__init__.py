@@ -30,7 +30,7 @@ import torch
 
 # Stream ids of the seed sequence [cfg_id, stream, layer, b].
 STREAM = dict(q=0, zk=1, zv=2, bk=3, bv=4, lengths=5, ranks=6, k_new=7, v_new=8,
-              window=9, needle=10, perm=11, bk_next=12, bv_next=13, q_chunk=14, kv_chunk=15, spectra=16)
+              window=9, needle=10, perm=11, bk_next=12, bv_next=13, q_chunk=14, kv_chunk=15, spectra=16, kv_samples=17)
 
 N_Q_HEADS = 28
 N_KV_HEADS = 4
@@ -199,6 +199,21 @@ def gen_chunk(cfg: Config, layer: int, n_new: int, q_scale: float = 1.0, rank: O
         k[b] = g.standard_normal(k[b].shape, dtype=np.float32) * np.float32(np.sqrt(h / cfg.kv_width))
         v[b] = g.standard_normal(v[b].shape, dtype=np.float32) * np.float32(np.sqrt(h / cfg.kv_width))
     return q, k, v
+
+
+def gen_kv_samples(cfg: Config, n: int, dim: int = 512, decay: float = 1.0, layer: int = 0):
+    """Calibration KV rows for the weighted SVD: x = (g * s) Q^T with g ~ N(0, 1) [n, dim],
+    s_k = k^(-decay/2) and Q a seeded orthogonal matrix, so the rows' spectrum decays like the
+    latent index weights; and sensitivities w: 80% ~ U(0, 0.2) (insensitive states, e.g. visual
+    tokens), 20% ~ U(1, 5) (sensitive ones). Returns float32 x [n, dim] and w [n]."""
+    g = rng(cfg.cfg_id, "kv_samples", layer)
+    q, r = np.linalg.qr(g.standard_normal((dim, dim)))
+    q = q * np.sign(np.diag(r))[None, :]
+    s = np.arange(1, dim + 1, dtype=np.float64) ** (-decay / 2)
+    x = (g.standard_normal((n, dim)) * s[None, :]) @ q.T
+    sens = g.random(n) < 0.2
+    w = np.where(sens, g.uniform(1.0, 5.0, n), g.uniform(0.0, 0.2, n))
+    return x.astype(np.float32), w.astype(np.float32)
 
 
 def gen_spectra(cfg: Config, n_mat: int, n: int = 512) -> np.ndarray:
