@@ -342,6 +342,82 @@ def prefill_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def _timed_calls(fn, K, W):
+    """Mean ms per call of fn over K calls after W warm-up calls (torch events, same stream)."""
+    import torch
+    for _ in range(W):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / K
+
+
+def sensvd_bench(args):
+    """Sensitivity-weighted SVD of one KV matrix's calibration rows (256 samples x 512 tokens =
+    131072 rows of dim 512, rank 358): the weighted Gram on the matrix cores, then block Jacobi.
+    The roofline line is the Gram's algorithmic FLOPs (N * D * (D + 1), the symmetric half plus
+    the diagonal) over the whole call: the Jacobi rounds are launch-latency bound."""
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+    import synth
+
+    dev = "cuda"
+    n, dim, rank = args.samples, 512, 358
+    x, w = synth.gen_kv_samples(synth.CONFIGS[4], n, dim)
+    xd = torch.from_numpy(x).to(torch.bfloat16).to(dev)
+    wd = torch.from_numpy(w).to(dev)
+    basis = torch.empty(rank, dim, dtype=torch.bfloat16, device=dev)
+    sigma = torch.empty(dim, dtype=torch.float32, device=dev)
+    ws = torch.empty(lr.lowrank_sens_svd_workspace_size(n, dim), dtype=torch.uint8, device=dev)
+    ms = _timed_calls(lambda: lr.lowrank_sens_svd(xd, wd, rank, basis, sigma, ws), args.steps, args.warmup)
+    assert torch.isfinite(sigma).all()
+    flops = float(n) * dim * (dim + 1)
+    rec = {"metric": "sensitivity-weighted SVD basis of one KV matrix: ms per call", "value": round(ms, 4),
+           "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"sensvd N{n} D{dim} r{rank}", "samples": n, "dim": dim, "rank": rank,
+                      "sweeps": 10, "parallelism": "single GPU"},
+           "roofline": {"bound": "mfma", "kernel": "lr_svd_gram + block Jacobi (whole call)",
+                        "achieved": round(flops / (ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
+                        "traffic": None, "flops_per_launch": flops}}
+    print(json.dumps(rec), flush=True)
+
+
+def rankalloc_bench(args):
+    """Global rank allocation for the 28-layer model (56 spectra of 512, ranks 128..512 by 8,
+    budget 70% of full rank): a latency-bound pair of launches."""
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+    import synth
+
+    dev = "cuda"
+    s = torch.from_numpy(synth.gen_spectra(synth.CONFIGS[4], 56, 512)).to(dev)
+    ranks = torch.empty(56, dtype=torch.int32, device=dev)
+    ws = torch.empty(lr.lowrank_rank_allocate_workspace_size(56, 128, 512, 8), dtype=torch.uint8, device=dev)
+    budget = int(0.7 * 56 * 512)
+    ms = _timed_calls(lambda: lr.lowrank_rank_allocate(s, budget, 128, 512, 8, ranks, ws), args.steps,
+                      args.warmup)
+    n_gran = 56 * (512 - 128) // 8
+    rec = {"metric": "global rank allocation of a 28-layer model: us per call", "value": round(ms * 1e3, 2),
+           "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f64 gains",
+           "data": "synthetic",
+           "config": {"workload": "rankalloc 56x512 r128..512/8 budget0.7", "matrices": 56, "granules": n_gran,
+                      "parallelism": "single GPU"},
+           "roofline": {"bound": "alu", "kernel": "lr_rank_select", "achieved": round(n_gran ** 2 / (ms * 1e-3) / 1e12, 6),
+                        "peak": 78.6, "unit": "T compares/s", "frac": round(n_gran ** 2 / (ms * 1e-3) / 1e12 / 78.6, 8),
+                        "traffic": None}}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,9 +430,11 @@ def main():
                     help="cache copies rotated over the steps (0: enough that the copies exceed 2 x 256 MB)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 256 MiB device copy (the counter calibration reference)")
-    ap.add_argument("--op", choices=("decode", "rebase", "prefill"), default="decode",
+    ap.add_argument("--op", choices=("decode", "rebase", "prefill", "sensvd", "rankalloc"), default="decode",
                     help="decode: the decode step (default); rebase: the historical-coordinate sync; "
-                         "prefill: chunked prefill attention")
+                         "prefill: chunked prefill attention; sensvd: sensitivity-weighted SVD basis; "
+                         "rankalloc: global rank allocation")
+    ap.add_argument("--samples", type=int, default=131072, help="--op sensvd: calibration rows")
     ap.add_argument("--chunk", type=int, default=32, help="--op prefill: new tokens per sequence")
     ap.add_argument("--rank-new", type=int, default=0, help="--op rebase: new rank (0: unchanged)")
     args = ap.parse_args()
@@ -376,6 +454,12 @@ def main():
         return
     if args.op == "prefill":
         prefill_bench(args)
+        return
+    if args.op == "sensvd":
+        sensvd_bench(args)
+        return
+    if args.op == "rankalloc":
+        rankalloc_bench(args)
         return
     dev = "cuda"
     cfg = synth.CONFIGS[args.config]
