@@ -10,16 +10,21 @@
 //                   32 samples at a time are weighted, rounded and staged in LDS row-major, and
 //                   both 16x16x32 bf16 matrix-core operands (K = samples) come from the gfx950
 //                   transpose read; float32 accumulation.
-//   lr_svd_reduce   G = sum of the partials in range order (deterministic), mirrored; V = I.
-//   lr_jacobi_rows  block Jacobi, one workgroup per pair of 16-index blocks of a round (circle
-//   lr_jacobi_cols  ordering, D/16 - 1 rounds per sweep): the pair's 32x32 block of G is
-//                   diagonalised in LDS by cyclic scalar Jacobi (rotations as in Golub and Van
-//                   Loan's symmetric Schur step), its rotation U [32, 32] then updates the pair's
-//                   rows of G (U^T G), and after the launch boundary its columns of G and V
-//                   (G U, V U). Pairs of a round touch disjoint rows and columns.
-//   lr_svd_finish   eigenvalues from diag(G) sorted descending (bitonic, index breaks ties),
-//                   sigma = sqrt(max(lambda, 0)), basis rows = the matching columns of V,
-//                   normalised, with the largest-magnitude component made positive.
+//   lr_svd_reduce   G = sum of the partials in range order (deterministic), mirrored, and a
+//                   copy G0 of it; V = I.
+//   lr_jacobi_pair  block Jacobi over 16-index blocks, circle ordering (D/16 - 1 rounds per
+//   lr_jacobi_apply sweep): one workgroup per block pair reduces the pair's 32x32 block of G in
+//                   LDS by one cyclic sweep of scalar Jacobi (rotations as in Golub and Van
+//                   Loan's symmetric Schur step), accumulating U [32, 32]; then one launch
+//                   applies all pairs' U: G <- Q^T G Q block by block (U_i^T G_ij U_j) and
+//                   V <- V Q. Pairs of a round touch disjoint rows and columns.
+//   lr_svd_rayleigh eigenvalues as Rayleigh quotients of the columns of V on the unrotated G
+//                   (the sweeps' accumulated rounding in diag(G) stays out of them: the
+//                   quotient's error is second order in the eigenvector's).
+//   lr_svd_sort     eigenvalues sorted descending (bitonic, index breaks ties),
+//                   sigma = sqrt(max(lambda, 0)).
+//   lr_svd_basis    basis rows = the matching columns of V, normalised, with the
+//                   largest-magnitude component made positive.
 #include <math.h>
 
 #include "device_common.h"
@@ -57,8 +62,11 @@ struct SvdArgs {
   const __bf16* x;
   const float* w;
   float* part;       // [nsplit][D][D]
-  float* G;          // [D][D]
+  float* G;          // [D][D], rotated in place by the Jacobi sweeps
+  float* G0;         // [D][D], the Gram as reduced (kept for the Rayleigh quotients)
   float* V;          // [D][D]
+  double* rq;        // [D / 64 + 1][D]: partial quadratic forms of the columns of V, then their norms
+  int* ord;          // [D]: column of V of each basis row
   float* U;          // [npairs][32][32]
   void* basis;       // [rank][D]
   float* sigma;      // [D]
@@ -142,6 +150,7 @@ __global__ __launch_bounds__(256) void lr_svd_reduce(SvdArgs a) {
   float g = 0.f;
   for (int s = 0; s < a.nsplit; ++s) g += a.part[(size_t)s * a.D * a.D + src];
   a.G[idx] = g;
+  a.G0[idx] = g;
   a.V[idx] = (i == j) ? 1.f : 0.f;
 }
 
@@ -159,27 +168,36 @@ __device__ __forceinline__ void circle_pair(int n, int r, int k, int& p, int& q)
 
 constexpr int kJb = 16;                   // Jacobi block size
 constexpr int kJs = 2 * kJb;              // pair subproblem size (32)
-constexpr int kJacobiInner = 3;           // cyclic sweeps over a pair's 32x32 block
+constexpr int kJacobiInner = 1;           // cyclic sweeps over a pair's 32x32 block per round
 
-__device__ __forceinline__ void jacobi_rotation(float app, float aqq, float apq, float& c, float& s) {
-  // Golub and Van Loan, symmetric Schur step: J = [[c, s], [-s, c]] on (p, q) zeroes J^T A J (p, q)
-  if (apq == 0.f || fabsf(apq) <= 1e-30f) {
+// One workgroup per block pair: the pair's 32x32 block S of G is diagonalised in LDS by cyclic
+// scalar Jacobi (circle ordering of the 32 indices: 16 disjoint rotations per step). Thread
+// (a, b) of 16 x 16 owns, in one step, the 2x2 block of S at rows (p_a, q_a) and columns
+// (p_b, q_b) of the step's rotation pairs a and b: S' = J_a^T S J_b there, with both rotations
+// formed by the thread itself from the diagonal of S (every thread forming rotation a reads the
+// same three entries and runs the same instructions, so all get the same one). The same thread
+// rotates U's columns (p_b, q_b) in rows (p_a, q_a): U' = U J. The blocks of a step partition S
+// and U, so each step is one pass from one half of a double buffer into the other. Rotations use
+// the hardware square root and reciprocal: the angles need not be correctly rounded, only
+// orthogonal to float precision (the basis rows are normalised at the end and the eigenvalues
+// are Rayleigh quotients). The accumulated U goes to the workspace.
+// Golub and Van Loan's symmetric Schur step: J = [[c, s], [-s, c]] on (p, q) zeroes (J^T A J)[p][q].
+__device__ __forceinline__ void jacobi_rotation_fast(float app, float aqq, float apq, float& c, float& s) {
+  if (fabsf(apq) <= 1e-30f) {
     c = 1.f;
     s = 0.f;
     return;
   }
-  const float tau = (aqq - app) / (2.f * apq);
-  const float t = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
-  c = 1.f / sqrtf(1.f + t * t);
+  const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+  const float t = (tau >= 0.f ? 1.f : -1.f) * __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.f)));
+  c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
   s = t * c;
 }
 
-__global__ __launch_bounds__(256) void lr_jacobi_rows(SvdArgs a) {
-  extern __shared__ float jsm[];
-  float* S = jsm;                         // [32][33]
-  float* Ul = S + kJs * (kJs + 1);        // [32][33]
-  float* cs = Ul + kJs * (kJs + 1);       // [16][2]
-  float* rows = cs + 2 * kJb;             // [32][D]
+__global__ __launch_bounds__(256) void lr_jacobi_pair(SvdArgs a) {
+  constexpr int LD = kJs + 1;
+  __shared__ float S[2][kJs * LD];
+  __shared__ float Ul[2][kJs * LD];
   const int tid = threadIdx.x;
   const int nb = a.D / kJb;
   int pb, qb;
@@ -187,102 +205,218 @@ __global__ __launch_bounds__(256) void lr_jacobi_rows(SvdArgs a) {
   auto gidx = [&](int l) { return l < kJb ? pb * kJb + l : qb * kJb + (l - kJb); };
   for (int e = tid; e < kJs * kJs; e += 256) {
     const int r = e / kJs, c = e - r * kJs;
-    S[r * (kJs + 1) + c] = a.G[(size_t)gidx(r) * a.D + gidx(c)];
-    Ul[r * (kJs + 1) + c] = (r == c) ? 1.f : 0.f;
+    S[0][r * LD + c] = a.G[(size_t)gidx(r) * a.D + gidx(c)];
+    Ul[0][r * LD + c] = (r == c) ? 1.f : 0.f;
   }
   __syncthreads();
+  const int ta = tid >> 4, tb = tid & 15;
+  int cur = 0;
   for (int sw = 0; sw < kJacobiInner; ++sw) {
     for (int rr = 0; rr < kJs - 1; ++rr) {
-      if (tid < kJb) {
-        int p, q;
-        circle_pair(kJs, rr, tid, p, q);
-        float c, s;
-        jacobi_rotation(S[p * (kJs + 1) + p], S[q * (kJs + 1) + q], S[p * (kJs + 1) + q], c, s);
-        cs[2 * tid] = c;
-        cs[2 * tid + 1] = s;
-      }
+      const float* Sc = S[cur];
+      const float* Uc = Ul[cur];
+      float* Sn = S[cur ^ 1];
+      float* Un = Ul[cur ^ 1];
+      int p0, q0, p1, q1;
+      circle_pair(kJs, rr, ta, p0, q0);
+      circle_pair(kJs, rr, tb, p1, q1);
+      float c0, s0, c1, s1;
+      jacobi_rotation_fast(Sc[p0 * LD + p0], Sc[q0 * LD + q0], Sc[p0 * LD + q0], c0, s0);
+      jacobi_rotation_fast(Sc[p1 * LD + p1], Sc[q1 * LD + q1], Sc[p1 * LD + q1], c1, s1);
+      // J restricted to a pair (p, q): J[p][p] = c, J[p][q] = s, J[q][p] = -s, J[q][q] = c
+      const float xpp = Sc[p0 * LD + p1], xpq = Sc[p0 * LD + q1];
+      const float xqp = Sc[q0 * LD + p1], xqq = Sc[q0 * LD + q1];
+      // T = S_blk J_b
+      const float tpp = xpp * c1 - xpq * s1, tpq = xpp * s1 + xpq * c1;
+      const float tqp = xqp * c1 - xqq * s1, tqq = xqp * s1 + xqq * c1;
+      // S' = J_a^T T
+      Sn[p0 * LD + p1] = c0 * tpp - s0 * tqp;
+      Sn[p0 * LD + q1] = c0 * tpq - s0 * tqq;
+      Sn[q0 * LD + p1] = s0 * tpp + c0 * tqp;
+      Sn[q0 * LD + q1] = s0 * tpq + c0 * tqq;
+      const float upp = Uc[p0 * LD + p1], upq = Uc[p0 * LD + q1];
+      const float uqp = Uc[q0 * LD + p1], uqq = Uc[q0 * LD + q1];
+      Un[p0 * LD + p1] = upp * c1 - upq * s1;
+      Un[p0 * LD + q1] = upp * s1 + upq * c1;
+      Un[q0 * LD + p1] = uqp * c1 - uqq * s1;
+      Un[q0 * LD + q1] = uqp * s1 + uqq * c1;
       __syncthreads();
-      for (int e = tid; e < kJb * kJs; e += 256) {      // rows p, q of S
-        const int k = e / kJs, col = e - k * kJs;
-        int p, q;
-        circle_pair(kJs, rr, k, p, q);
-        const float c = cs[2 * k], s = cs[2 * k + 1];
-        const float rp = S[p * (kJs + 1) + col], rq = S[q * (kJs + 1) + col];
-        S[p * (kJs + 1) + col] = c * rp - s * rq;
-        S[q * (kJs + 1) + col] = s * rp + c * rq;
-      }
-      __syncthreads();
-      for (int e = tid; e < kJb * kJs; e += 256) {      // columns p, q of S and of Ul
-        const int k = e / kJs, row = e - k * kJs;
-        int p, q;
-        circle_pair(kJs, rr, k, p, q);
-        const float c = cs[2 * k], s = cs[2 * k + 1];
-        const float sp = S[row * (kJs + 1) + p], sq = S[row * (kJs + 1) + q];
-        S[row * (kJs + 1) + p] = c * sp - s * sq;
-        S[row * (kJs + 1) + q] = s * sp + c * sq;
-        const float up = Ul[row * (kJs + 1) + p], uq = Ul[row * (kJs + 1) + q];
-        Ul[row * (kJs + 1) + p] = c * up - s * uq;
-        Ul[row * (kJs + 1) + q] = s * up + c * uq;
-      }
-      __syncthreads();
+      cur ^= 1;
     }
   }
   float* Ug = a.U + (size_t)blockIdx.x * kJs * kJs;
-  for (int e = tid; e < kJs * kJs; e += 256) Ug[e] = Ul[(e / kJs) * (kJs + 1) + (e % kJs)];
-  // rows of G: new row a = sum_b U[b][a] * old row b
-  for (int e = tid; e < kJs * a.D; e += 256) {
-    const int r = e / a.D, c = e - r * a.D;
-    rows[e] = a.G[(size_t)gidx(r) * a.D + c];
+  for (int e = tid; e < kJs * kJs; e += 256) Ug[e] = Ul[cur][(e / kJs) * LD + (e % kJs)];
+}
+
+// One round's update G <- Q^T G Q, V <- V Q, with Q the block-diagonal (in permuted order) of the
+// pairs' U. Output block (pair i rows, pair j columns) of G is U_i^T G_ij U_j: it depends on its
+// own input block only, so each workgroup updates its block in place. Workgroups 0 .. np(np+1)/2
+// - 1 take the G blocks with i <= j and write the result and its transpose (G stays exactly
+// symmetric); the rest take 32-row blocks of V times U_j. Thread (r, c4): row r, columns
+// c4 .. c4+3 (inside one 16-index block, so the global accesses are 16-byte vectors).
+__global__ __launch_bounds__(256) void lr_jacobi_apply(SvdArgs a) {
+  constexpr int LD = kJs + 1;
+  __shared__ float B[kJs * LD];
+  __shared__ float Ui[kJs * LD];
+  __shared__ float Uj[kJs * LD];
+  __shared__ float T[kJs * LD];
+  const int tid = threadIdx.x;
+  const int nb = a.D / kJb, np = nb / 2;
+  const int ng = np * (np + 1) / 2;
+  const int r = tid >> 3, c4 = (tid & 7) * 4;
+  int i = 0, j = 0, rb = 0;
+  const bool gblk = (int)blockIdx.x < ng;
+  if (gblk) {
+    int rem = blockIdx.x;
+    while (rem >= np - i) {
+      rem -= np - i;
+      ++i;
+    }
+    j = i + rem;
+  } else {
+    const int v = blockIdx.x - ng;
+    j = v % np;
+    rb = v / np;
+  }
+  int pi, qi, pj, qj;
+  circle_pair(nb, a.round, i, pi, qi);
+  circle_pair(nb, a.round, j, pj, qj);
+  auto gi = [&](int l) { return l < kJb ? pi * kJb + l : qi * kJb + (l - kJb); };
+  auto gj = [&](int l) { return l < kJb ? pj * kJb + l : qj * kJb + (l - kJb); };
+  const f32x4 uj = *(const f32x4*)(a.U + (size_t)j * kJs * kJs + r * kJs + c4);
+  float* src = gblk ? a.G + (size_t)gi(r) * a.D + gj(c4) : a.V + (size_t)(rb * kJs + r) * a.D + gj(c4);
+  const f32x4 bv = *(const f32x4*)src;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    B[r * LD + c4 + k] = bv[k];
+    Uj[r * LD + c4 + k] = uj[k];
+  }
+  if (gblk) {
+    const f32x4 ui = *(const f32x4*)(a.U + (size_t)i * kJs * kJs + r * kJs + c4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Ui[r * LD + c4 + k] = ui[k];
   }
   __syncthreads();
-  for (int e = tid; e < kJs * a.D; e += 256) {
-    const int r = e / a.D, c = e - r * a.D;
-    float v = 0.f;
-    for (int b = 0; b < kJs; ++b) v = fmaf(Ul[b * (kJs + 1) + r], rows[b * a.D + c], v);
-    a.G[(size_t)gidx(r) * a.D + c] = v;
+  float t[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int l = 0; l < kJs; ++l) {
+    const float bl = B[r * LD + l];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = fmaf(bl, Uj[l * LD + c4 + k], t[k]);
+  }
+  if (!gblk) {
+    *(f32x4*)src = f32x4{t[0], t[1], t[2], t[3]};
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) T[r * LD + c4 + k] = t[k];
+  __syncthreads();
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int l = 0; l < kJs; ++l) {
+    const float u = Ui[l * LD + r];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = fmaf(u, T[l * LD + c4 + k], o[k]);
+  }
+  *(f32x4*)src = f32x4{o[0], o[1], o[2], o[3]};
+  if (i == j) return;
+  // the transpose block (pair j rows, pair i columns), staged through LDS
+#pragma unroll
+  for (int k = 0; k < 4; ++k) B[(c4 + k) * LD + r] = o[k];
+  __syncthreads();
+  *(f32x4*)(a.G + (size_t)gj(r) * a.D + gi(c4)) =
+      f32x4{B[r * LD + c4], B[r * LD + c4 + 1], B[r * LD + c4 + 2], B[r * LD + c4 + 3]};
+}
+
+constexpr int kRqCols = 16;   // columns of V per workgroup in lr_svd_rayleigh
+constexpr int kRqRows = 64;   // rows of G0 per workgroup in lr_svd_rayleigh
+
+// lambda_k = v_k^T G0 v_k / v_k^T v_k for the columns v_k of V, as D / 64 partial quadratic
+// forms: workgroup (column group k0 .. k0+15, row range j0 .. j0+63) sums
+// v_k[i] G0[j][i] v_k[j] over all i and its j (G0 is exactly symmetric, so thread t reads row j
+// at columns t and t + 256, coalesced) into rq[j0 / 64][k] (float64); range 0 also writes
+// v_k^T v_k. lr_svd_sort adds the partials in range order.
+__global__ __launch_bounds__(256) void lr_svd_rayleigh(SvdArgs a) {
+  __shared__ __attribute__((aligned(16))) float Vs[512 * kRqCols];
+  __shared__ double red[4][2 * kRqCols];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int k0 = blockIdx.x * kRqCols, j0 = blockIdx.y * kRqRows;
+  for (int e = tid; e < a.D * kRqCols; e += 256) {
+    const int r = e / kRqCols, c = e - r * kRqCols;
+    Vs[e] = a.V[(size_t)r * a.D + k0 + c];
+  }
+  __syncthreads();
+  const int i0 = tid, i1 = tid + 256;
+  const bool h0 = i0 < a.D, h1 = i1 < a.D;
+  float t0[kRqCols], t1[kRqCols];
+#pragma unroll
+  for (int c = 0; c < kRqCols; ++c) t0[c] = t1[c] = 0.f;
+  for (int jj = 0; jj < kRqRows; jj += 8) {
+    float g0[8], g1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      g0[u] = h0 ? a.G0[(size_t)(j0 + jj + u) * a.D + i0] : 0.f;
+      g1[u] = h1 ? a.G0[(size_t)(j0 + jj + u) * a.D + i1] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+      for (int c4 = 0; c4 < kRqCols / 4; ++c4) {
+        const f32x4 v = *(const f32x4*)(Vs + (j0 + jj + u) * kRqCols + 4 * c4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          t0[4 * c4 + q] = fmaf(g0[u], v[q], t0[4 * c4 + q]);
+          t1[4 * c4 + q] = fmaf(g1[u], v[q], t1[4 * c4 + q]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kRqCols; ++c) {
+    const double v0 = h0 ? Vs[i0 * kRqCols + c] : 0.f, v1 = h1 ? Vs[i1 * kRqCols + c] : 0.f;
+    double num = v0 * (double)t0[c] + v1 * (double)t1[c];
+    double den = v0 * v0 + v1 * v1;
+    for (int o = 32; o > 0; o >>= 1) {
+      num += __shfl_down(num, o);
+      den += __shfl_down(den, o);
+    }
+    if (lane == 0) {
+      red[wv][2 * c] = num;
+      red[wv][2 * c + 1] = den;
+    }
+  }
+  __syncthreads();
+  if (tid < kRqCols) {
+    double num = 0.0, den = 0.0;
+    for (int w = 0; w < 4; ++w) {
+      num += red[w][2 * tid];
+      den += red[w][2 * tid + 1];
+    }
+    a.rq[(size_t)blockIdx.y * a.D + k0 + tid] = num;
+    if (blockIdx.y == 0) a.rq[(size_t)(a.D / kRqRows) * a.D + k0 + tid] = den;
   }
 }
 
-__global__ __launch_bounds__(256) void lr_jacobi_cols(SvdArgs a) {
-  extern __shared__ float jsm[];
-  float* Ul = jsm;                        // [32][33]
-  float* cols = Ul + kJs * (kJs + 1);     // [D][33]
-  const int tid = threadIdx.x;
-  const int nb = a.D / kJb;
-  int pb, qb;
-  circle_pair(nb, a.round, blockIdx.x, pb, qb);
-  auto gidx = [&](int l) { return l < kJb ? pb * kJb + l : qb * kJb + (l - kJb); };
-  const float* Ug = a.U + (size_t)blockIdx.x * kJs * kJs;
-  for (int e = tid; e < kJs * kJs; e += 256) Ul[(e / kJs) * (kJs + 1) + (e % kJs)] = Ug[e];
-  for (int m = 0; m < 2; ++m) {
-    float* M = m == 0 ? a.G : a.V;
-    __syncthreads();
-    for (int e = tid; e < a.D * kJs; e += 256) {
-      const int r = e / kJs, l = e - r * kJs;
-      cols[r * (kJs + 1) + l] = M[(size_t)r * a.D + gidx(l)];
-    }
-    __syncthreads();
-    for (int e = tid; e < a.D * kJs; e += 256) {
-      const int r = e / kJs, l = e - r * kJs;
-      float v = 0.f;
-      for (int b = 0; b < kJs; ++b) v = fmaf(cols[r * (kJs + 1) + b], Ul[b * (kJs + 1) + l], v);
-      M[(size_t)r * a.D + gidx(l)] = v;
-    }
-  }
-}
-
-__global__ __launch_bounds__(512) void lr_svd_finish(SvdArgs a) {
+// eigenvalues (the Rayleigh quotients) sorted descending by a bitonic network in LDS, equal
+// values ordered by column index; sigma = sqrt(max(lambda, 0)); the first rank column indices
+// go to ord.
+__global__ __launch_bounds__(512) void lr_svd_sort(SvdArgs a) {
   __shared__ float key[512];
   __shared__ int idx[512];
   const int tid = threadIdx.x;
   int P = 1;
   while (P < a.D) P <<= 1;
+  const int nr = a.D / kRqRows;
   for (int i = tid; i < P; i += 512) {
-    key[i] = i < a.D ? a.G[(size_t)i * a.D + i] : -INFINITY;
+    float k = -INFINITY;
+    if (i < a.D) {
+      double num = 0.0;
+      for (int y = 0; y < nr; ++y) num += a.rq[(size_t)y * a.D + i];
+      const double den = a.rq[(size_t)nr * a.D + i];
+      k = den > 0.0 ? (float)(num / den) : 0.f;
+    }
+    key[i] = k;
     idx[i] = i;
   }
   __syncthreads();
-  // bitonic sort, descending by eigenvalue, ascending index on ties
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < P; i += 512) {
@@ -304,28 +438,62 @@ __global__ __launch_bounds__(512) void lr_svd_finish(SvdArgs a) {
     }
   }
   for (int i = tid; i < a.D; i += 512) a.sigma[i] = sqrtf(fmaxf(key[i], 0.f));
-  for (int k = tid; k < a.rank; k += 512) {
-    const int col = idx[k];
-    int best = 0;
-    float bv = -1.f;
-    double nrm = 0.0;
-    for (int c = 0; c < a.D; ++c) {
-      const float x = a.V[(size_t)c * a.D + col];
-      const float v = fabsf(x);
-      nrm += (double)x * (double)x;
-      if (v > bv) {
-        bv = v;
-        best = c;
-      }
+  for (int k = tid; k < a.rank; k += 512) a.ord[k] = idx[k];
+}
+
+// basis row k (one workgroup each) = column ord[k] of V, normalised (the rotations keep the
+// columns orthogonal to float precision but let their norms drift by a few 1e-4 over the
+// sweeps), its largest-magnitude component (lowest index among equal magnitudes) made positive.
+__global__ __launch_bounds__(256) void lr_svd_basis(SvdArgs a) {
+  __shared__ double rn[4];
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int k = blockIdx.x, col = a.ord[k];
+  const int c0 = tid, c1 = tid + 256;
+  const float x0 = c0 < a.D ? a.V[(size_t)c0 * a.D + col] : 0.f;
+  const float x1 = c1 < a.D ? a.V[(size_t)c1 * a.D + col] : 0.f;
+  double nrm = (double)x0 * x0 + (double)x1 * x1;
+  float bv = fabsf(x0);
+  int bi = c0;
+  if (c1 < a.D && fabsf(x1) > bv) {
+    bv = fabsf(x1);
+    bi = c1;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    nrm += __shfl_down(nrm, o);
+    const float ov = __shfl_down(bv, o);
+    const int oi = __shfl_down(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
     }
-    // the rotations keep the columns orthogonal to float32 precision but let their norms drift
-    // (a few 1e-4 after many sweeps): each basis row is normalised here
-    const float sg = (a.V[(size_t)best * a.D + col] < 0.f ? -1.f : 1.f) / (float)sqrt(nrm > 0.0 ? nrm : 1.0);
-    for (int c = 0; c < a.D; ++c) {
-      const float v = sg * a.V[(size_t)c * a.D + col];
-      if (a.basis_f32) ((float*)a.basis)[(size_t)k * a.D + c] = v;
-      else ((__bf16*)a.basis)[(size_t)k * a.D + c] = (__bf16)v;
+  }
+  if (lane == 0) {
+    rn[wv] = nrm;
+    rv[wv] = bv;
+    ri[wv] = bi;
+  }
+  __syncthreads();
+  double n = 0.0;
+  float v = -1.f;
+  int best = 0;
+  for (int w = 0; w < 4; ++w) {
+    n += rn[w];
+    if (rv[w] > v || (rv[w] == v && ri[w] < best)) {
+      v = rv[w];
+      best = ri[w];
     }
+  }
+  const float sg = (a.V[(size_t)best * a.D + col] < 0.f ? -1.f : 1.f) / (float)sqrt(n > 0.0 ? n : 1.0);
+  if (a.basis_f32) {
+    float* row = (float*)a.basis + (size_t)k * a.D;
+    if (c0 < a.D) row[c0] = sg * x0;
+    if (c1 < a.D) row[c1] = sg * x1;
+  } else {
+    __bf16* row = (__bf16*)a.basis + (size_t)k * a.D;
+    if (c0 < a.D) row[c0] = (__bf16)(sg * x0);
+    if (c1 < a.D) row[c1] = (__bf16)(sg * x1);
   }
 }
 
@@ -336,7 +504,8 @@ int svd_nsplit(int n) {
 
 size_t svd_workspace_bytes(int n, int D) {
   const size_t dd = (size_t)D * D * 4;
-  return (size_t)svd_nsplit(n) * dd + 2 * dd + (size_t)(D / kJs) * kJs * kJs * 4 + 1024;
+  return (size_t)svd_nsplit(n) * dd + 3 * dd + (size_t)(D / kJs) * kJs * kJs * 4 +
+         (size_t)(D / kRqRows + 1) * D * 8 + (size_t)D * 4 + 1024;
 }
 
 hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank, int sweeps, void* basis,
@@ -355,8 +524,11 @@ hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank
   const size_t dd = (size_t)D * D * 4;
   a.part = (float*)p;
   a.G = (float*)(p + (size_t)a.nsplit * dd);
-  a.V = (float*)(p + (size_t)a.nsplit * dd + dd);
-  a.U = (float*)(p + (size_t)a.nsplit * dd + 2 * dd);
+  a.G0 = (float*)(p + (size_t)a.nsplit * dd + dd);
+  a.V = (float*)(p + (size_t)a.nsplit * dd + 2 * dd);
+  a.U = (float*)(p + (size_t)a.nsplit * dd + 3 * dd);
+  a.rq = (double*)(a.U + (size_t)(D / kJs) * kJs * kJs);
+  a.ord = (int*)(a.rq + (size_t)(D / kRqRows + 1) * D);
   a.round = 0;
   const int nbt = D / kSvdTile;
   hipLaunchKernelGGL(lr_svd_gram, dim3(nbt * (nbt + 1) / 2, a.nsplit), dim3(256), 0, st, a);
@@ -366,29 +538,18 @@ hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = D / kJb, npairs = nb / 2;
-  const size_t lds_rows = (size_t)(2 * kJs * (kJs + 1) + 2 * kJb + kJs * D) * 4;
-  const size_t lds_cols = (size_t)(kJs * (kJs + 1) + D * (kJs + 1)) * 4;
-  static bool attr[64] = {};
-  int dev = 0;
-  e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && !attr[dev]) {
-    e = hipFuncSetAttribute((const void*)lr_jacobi_rows, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)lr_jacobi_cols, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr[dev] = true;
-  }
   for (int sw = 0; sw < sweeps; ++sw) {
     for (int r = 0; r < nb - 1; ++r) {
       a.round = r;
-      hipLaunchKernelGGL(lr_jacobi_rows, dim3(npairs), dim3(256), lds_rows, st, a);
-      hipLaunchKernelGGL(lr_jacobi_cols, dim3(npairs), dim3(256), lds_cols, st, a);
+      hipLaunchKernelGGL(lr_jacobi_pair, dim3(npairs), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(lr_jacobi_apply, dim3(npairs * (npairs + 1) / 2 + npairs * (D / kJs)), dim3(256), 0, st, a);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(lr_svd_finish, dim3(1), dim3(512), 0, st, a);
+  hipLaunchKernelGGL(lr_svd_rayleigh, dim3(D / kRqCols, D / kRqRows), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(lr_svd_sort, dim3(1), dim3(512), 0, st, a);
+  if (rank > 0) hipLaunchKernelGGL(lr_svd_basis, dim3(rank), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

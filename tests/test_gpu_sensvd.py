@@ -1,5 +1,5 @@
-"""GPU parity of lowrank_sens_svd (sensitivity-weighted SVD basis) against the oracle: singular
-values within 2e-4 of the largest, basis rows orthonormal to 1e-5, each row an eigenvector of the
+"""GPU parity of lowrank_sens_svd (sensitivity-weighted SVD basis) against the oracle: squared
+singular values within 1e-6 of the largest, basis rows orthonormal to 1e-5, each row an eigenvector of the
 oracle's Gram (residual 1e-4 of the top eigenvalue), and the top-r subspace equal to the oracle's
 where the spectrum has a gap there."""
 import numpy as np
@@ -26,12 +26,16 @@ def run(x, w, rank, basis_dtype=torch.float32, sweeps=0):
     return basis.float().cpu().numpy().astype(np.float64), sigma.cpu().numpy().astype(np.float64)
 
 
-def check(x, w, rank, b, s, gap_at_rank=True, tol_sigma=2e-4):
+def check(x, w, rank, b, s, gap_at_rank=True, tol_sigma=1e-6):
     xb = torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy()   # stored rows
     b_ref, s_ref = SV.basis(xb, w, rank)
     G = SV.gram(xb, w)
     lam_max = max(float(s_ref[0]) ** 2, 1e-30)
-    assert np.max(np.abs(s - s_ref)) <= tol_sigma * max(s_ref[0], 1e-30) + 1e-30
+    # eigenvalues are Rayleigh quotients on the float32 Gram: their error is that of the quadratic
+    # form v^T G v, where the entries' independent roundings largely cancel (measured <= 1e-7
+    # lambda_max up to 131072 samples). Bound: |sigma^2 - sigma_ref^2| <= 1e-6 lambda_max, so
+    # zero singular values read <= 1e-3 sigma_max.
+    assert np.max(np.abs(s * s - s_ref * s_ref)) <= tol_sigma * lam_max + 1e-30
     assert np.all(np.diff(s) <= 0)
     np.testing.assert_allclose(b @ b.T, np.eye(rank), atol=1e-5)
     lam = np.sum((b @ G) * b, axis=1)
