@@ -183,19 +183,21 @@ constexpr int kJacobiInner = 1;           // cyclic sweeps over a pair's 32x32 b
 // are Rayleigh quotients). The accumulated U goes to the workspace.
 // Golub and Van Loan's symmetric Schur step: J = [[c, s], [-s, c]] on (p, q) zeroes (J^T A J)[p][q].
 __device__ __forceinline__ void jacobi_rotation_fast(float app, float aqq, float apq, float& c, float& s) {
-  if (fabsf(apq) <= 1e-30f) {
-    c = 1.f;
-    s = 0.f;
-    return;
-  }
-  const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+  // branch-free: a negligible apq gives the identity by selection (with apq replaced by 1 the
+  // arithmetic stays finite), so the caller's loads need not wait on a branch
+  const bool skip = fabsf(apq) <= 1e-30f;
+  const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * (skip ? 1.f : apq));
   const float t = (tau >= 0.f ? 1.f : -1.f) * __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.f)));
-  c = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
-  s = t * c;
+  const float cc = __builtin_amdgcn_rsqf(fmaf(t, t, 1.f));
+  c = skip ? 1.f : cc;
+  s = skip ? 0.f : t * cc;
 }
 
 __global__ __launch_bounds__(256) void lr_jacobi_pair(SvdArgs a) {
-  constexpr int LD = kJs + 1;
+  // row stride 48: in the circle ordering p + q is the same for every pair of a step, so with a
+  // stride of 33 the pairs' (p, q) entries would all fall in one bank; 48 spreads them and the
+  // two rows of a half-wave's blocks over different banks
+  constexpr int LD = 48;
   __shared__ float S[2][kJs * LD];
   __shared__ float Ul[2][kJs * LD];
   const int tid = threadIdx.x;
@@ -210,6 +212,9 @@ __global__ __launch_bounds__(256) void lr_jacobi_pair(SvdArgs a) {
   }
   __syncthreads();
   const int ta = tid >> 4, tb = tid & 15;
+  int p0, q0, p1, q1;
+  circle_pair(kJs, 0, ta, p0, q0);
+  circle_pair(kJs, 0, tb, p1, q1);
   int cur = 0;
   for (int sw = 0; sw < kJacobiInner; ++sw) {
     for (int rr = 0; rr < kJs - 1; ++rr) {
@@ -217,15 +222,17 @@ __global__ __launch_bounds__(256) void lr_jacobi_pair(SvdArgs a) {
       const float* Uc = Ul[cur];
       float* Sn = S[cur ^ 1];
       float* Un = Ul[cur ^ 1];
-      int p0, q0, p1, q1;
-      circle_pair(kJs, rr, ta, p0, q0);
-      circle_pair(kJs, rr, tb, p1, q1);
-      float c0, s0, c1, s1;
-      jacobi_rotation_fast(Sc[p0 * LD + p0], Sc[q0 * LD + q0], Sc[p0 * LD + q0], c0, s0);
-      jacobi_rotation_fast(Sc[p1 * LD + p1], Sc[q1 * LD + q1], Sc[p1 * LD + q1], c1, s1);
-      // J restricted to a pair (p, q): J[p][p] = c, J[p][q] = s, J[q][p] = -s, J[q][q] = c
+      // all loads of the step first: the two rotations' inputs, the S and U blocks
+      const float a_pp = Sc[p0 * LD + p0], a_qq = Sc[q0 * LD + q0], a_pq = Sc[p0 * LD + q0];
+      const float b_pp = Sc[p1 * LD + p1], b_qq = Sc[q1 * LD + q1], b_pq = Sc[p1 * LD + q1];
       const float xpp = Sc[p0 * LD + p1], xpq = Sc[p0 * LD + q1];
       const float xqp = Sc[q0 * LD + p1], xqq = Sc[q0 * LD + q1];
+      const float upp = Uc[p0 * LD + p1], upq = Uc[p0 * LD + q1];
+      const float uqp = Uc[q0 * LD + p1], uqq = Uc[q0 * LD + q1];
+      float c0, s0, c1, s1;
+      jacobi_rotation_fast(a_pp, a_qq, a_pq, c0, s0);
+      jacobi_rotation_fast(b_pp, b_qq, b_pq, c1, s1);
+      // J restricted to a pair (p, q): J[p][p] = c, J[p][q] = s, J[q][p] = -s, J[q][q] = c
       // T = S_blk J_b
       const float tpp = xpp * c1 - xpq * s1, tpq = xpp * s1 + xpq * c1;
       const float tqp = xqp * c1 - xqq * s1, tqq = xqp * s1 + xqq * c1;
@@ -234,14 +241,17 @@ __global__ __launch_bounds__(256) void lr_jacobi_pair(SvdArgs a) {
       Sn[p0 * LD + q1] = c0 * tpq - s0 * tqq;
       Sn[q0 * LD + p1] = s0 * tpp + c0 * tqp;
       Sn[q0 * LD + q1] = s0 * tpq + c0 * tqq;
-      const float upp = Uc[p0 * LD + p1], upq = Uc[p0 * LD + q1];
-      const float uqp = Uc[q0 * LD + p1], uqq = Uc[q0 * LD + q1];
       Un[p0 * LD + p1] = upp * c1 - upq * s1;
       Un[p0 * LD + q1] = upp * s1 + upq * c1;
       Un[q0 * LD + p1] = uqp * c1 - uqq * s1;
       Un[q0 * LD + q1] = uqp * s1 + uqq * c1;
       __syncthreads();
       cur ^= 1;
+      // next step of the circle ordering: every index except the fixed 31 advances by one mod 31
+      p0 = p0 == kJs - 2 ? 0 : p0 + 1;
+      p1 = p1 == kJs - 2 ? 0 : p1 + 1;
+      q0 = q0 == kJs - 1 ? q0 : (q0 == kJs - 2 ? 0 : q0 + 1);
+      q1 = q1 == kJs - 1 ? q1 : (q1 == kJs - 2 ? 0 : q1 + 1);
     }
   }
   float* Ug = a.U + (size_t)blockIdx.x * kJs * kJs;
