@@ -460,7 +460,7 @@ size_t lowrank_rank_allocate_workspace_size(int32_t n_mat, int32_t r_min, int32_
   const char* msg = "";
   if (check_rank_args(n_mat, r_max, r_max, r_min, r_max, granule, &msg) != LR_OK) return 0;
   const int64_t N = (int64_t)n_mat * ((r_max - r_min) / granule);
-  return align256((size_t)(N > n_mat ? N : n_mat) * 8);
+  return align256((size_t)(N > n_mat ? N : n_mat) * 12);   // keys (8 bytes) and counts (4) per granule
 }
 
 int lowrank_rank_allocate(const float* sigma, int32_t n_mat, int32_t n_sigma, int32_t sigma_ld, int64_t budget,

@@ -11,11 +11,14 @@
 //
 // lr_rank_gains    one thread per granule: its gain in float64 (squares of the float32
 //                  spectrum summed in index order; each square is exact in float64), stored as
-//                  the bits of the double (non-negative doubles order like their bits); one
-//                  thread per matrix also resets its rank to r_min.
-// lr_rank_select   one thread per granule counts the granules ahead of it in that order (all
-//                  N keys streamed through LDS in tiles) and, if fewer than n, adds g to its
-//                  matrix's rank (integer atomics: the sum does not depend on their order).
+//                  the bits of the double (non-negative doubles order like their bits), and its
+//                  count reset; one thread per matrix also resets its rank to r_min.
+// lr_rank_count    grid (granules / 256, key chunks of 256): each thread counts the chunk's
+//                  granules ahead of its own in that order (the chunk is read with wave-uniform
+//                  loads) and adds the count to its granule's (integer atomics: the total does
+//                  not depend on their order).
+// lr_rank_select   one thread per matrix: rank = r_min + g * (its granules with fewer than n
+//                  granules ahead).
 #include "device_common.h"
 #include "internal.h"
 
@@ -24,6 +27,7 @@ namespace lr {
 struct RankArgs {
   const float* sigma;
   unsigned long long* keys;
+  int32_t* ahead;
   int32_t* ranks;
   int n_mat, sigma_ld, r_min, g, nb, N;
   long long n_take;
@@ -40,29 +44,33 @@ __global__ __launch_bounds__(256) void lr_rank_gains(RankArgs a) {
     acc = acc + s * s;
   }
   a.keys[i] = (unsigned long long)__builtin_bit_cast(long long, acc);
+  a.ahead[i] = 0;
   if (j == 0) a.ranks[m] = a.r_min;
 }
 
-constexpr int kRankTile = 256;
+constexpr int kRankChunk = 256;
 
-__global__ __launch_bounds__(256) void lr_rank_select(RankArgs a) {
-  __shared__ unsigned long long tile[kRankTile];
+__global__ __launch_bounds__(256) void lr_rank_count(RankArgs a) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const bool mine = i < a.N;
   const unsigned long long ki = mine ? a.keys[i] : 0ull;
-  long long ahead = 0;
-  for (int t0 = 0; t0 < a.N; t0 += kRankTile) {
-    __syncthreads();
-    const int t = t0 + threadIdx.x;
-    tile[threadIdx.x] = t < a.N ? a.keys[t] : 0ull;
-    __syncthreads();
-    const int n = min(kRankTile, a.N - t0);
-    for (int u = 0; u < n; ++u) {
-      const unsigned long long kj = tile[u];
-      ahead += (kj > ki) || (kj == ki && t0 + u < i);
-    }
+  const int t0 = blockIdx.y * kRankChunk;
+  const int t1 = min(t0 + kRankChunk, a.N);
+  int ahead = 0;
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) {
+    const unsigned long long kj = a.keys[t];   // the same address in every lane
+    ahead += (kj > ki) || (kj == ki && t < i);
   }
-  if (mine && ahead < a.n_take) atomicAdd(&a.ranks[i / a.nb], a.g);
+  if (mine && ahead > 0) atomicAdd(&a.ahead[i], ahead);
+}
+
+__global__ __launch_bounds__(256) void lr_rank_select(RankArgs a) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= a.n_mat) return;
+  int taken = 0;
+  for (int j = 0; j < a.nb; ++j) taken += a.ahead[m * a.nb + j] < a.n_take;
+  a.ranks[m] = a.r_min + a.g * taken;
 }
 
 hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, long long n_take, int r_min,
@@ -77,6 +85,7 @@ hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, lon
   a.g = g;
   a.nb = nb;
   a.N = n_mat * nb;
+  a.ahead = (int32_t*)(a.keys + (a.N > n_mat ? a.N : n_mat));
   a.n_take = n_take;
   if (a.N == 0) {
     // no granule to hand out: every rank is r_min (one thread per matrix)
@@ -87,11 +96,12 @@ hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, lon
     hipLaunchKernelGGL(lr_rank_gains, dim3((n_mat + 255) / 256), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  const dim3 grid((a.N + 255) / 256);
-  hipLaunchKernelGGL(lr_rank_gains, grid, dim3(256), 0, st, a);
+  const unsigned nblk = (unsigned)((a.N + 255) / 256);
+  hipLaunchKernelGGL(lr_rank_gains, dim3(nblk), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lr_rank_select, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(lr_rank_count, dim3(nblk, (unsigned)((a.N + kRankChunk - 1) / kRankChunk)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(lr_rank_select, dim3((n_mat + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
