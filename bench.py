@@ -335,7 +335,7 @@ def prefill_bench(args):
         "config": {"workload": f"prefill {cfg.name} chunk{C}", "batch": B, "seq_len": T, "chunk": C,
                    "rank_k": li.rank_k, "rank_v": li.rank_v, "latent": cfg.latent, "q_heads": cfg.n_q_heads,
                    "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "lr_decode (prefill query sequences)", "achieved": round(tflops, 1),
+        "roofline": {"bound": "mfma", "kernel": "lr_prefill_latent" if cfg.latent == "bf16" else "lr_decode (prefill query sequences)", "achieved": round(tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel_us": round(kern_ms * 1e3, 2), "flops_per_launch": flops},
     }

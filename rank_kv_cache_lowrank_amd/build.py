@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblowrank_attn.so")
-SOURCES = ["abi.cpp", "decode.hip", "append.hip", "rebase.hip", "rankalloc.hip", "sensvd.hip"]
+SOURCES = ["abi.cpp", "decode.hip", "prefill.hip", "append.hip", "rebase.hip", "rankalloc.hip", "sensvd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

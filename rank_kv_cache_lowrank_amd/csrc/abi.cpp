@@ -108,9 +108,14 @@ int plan_attention(const lr_model_desc* m, int layer, int batch, int n_q, bool p
   p->window = m->window;
   p->max_len = max_len;
 
+  // prefill over bf16 latents: the dedicated latent kernel, one workgroup per group of
+  // kPrefillTokensPerWg chunk tokens and token range
+  p->pf = (prefill && p->latent == LR_BF16) ? 1 : 0;
+  p->pf_ntg = p->pf ? (n_q + kPrefillTokensPerWg - 1) / kPrefillTokensPerWg : 0;
+
   // token ranges: about one workgroup per compute unit over the batch unless overridden
   const int max_split = max_len > 0 ? (max_len + kTileTokens - 1) / kTileTokens : 1;
-  const int nb = p->B > 0 ? p->B : 1;
+  const int nb = p->pf ? (batch * p->pf_ntg > 0 ? batch * p->pf_ntg : 1) : (p->B > 0 ? p->B : 1);
   int target = (o && o->nsplit > 0) ? o->nsplit : (device_cu_count() + nb - 1) / nb;
   if (target < 1) target = 1;
   if (target > kMaxSplit) target = kMaxSplit;
@@ -160,6 +165,16 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   // copy the 16-byte granules that hold the rank's elements; the rest of the LDS row is zero
   p->copy_k = (p->rk * es + 15) / 16 * 16;
   p->copy_v = (p->rv * es + 15) / 16 * 16;
+  if (p->pf) {
+    const int nv = prefill_nv(p->nrb);
+    const int pstage = kTileTokens * (lds_stride_k(KS, 2) + lds_stride_v(nv / 2, 2));
+    int nst = (kLdsBytes - kLdsPad) / pstage;
+    nst = nst > 8 ? 8 : nst;
+    if (nv == 0 || nst < 3 || p->copy_k > KS * 64 || p->copy_v > nv * 32)
+      return *msg = "latent rows too wide for the prefill kernel", LR_EUNSUPPORTED;
+    p->pf_nst = nst;
+    p->pf_lds = nst * pstage + kLdsPad;
+  }
   if (p->copy_k > sk - 16 || p->copy_v > sv - 32) return *msg = "rank exceeds the kernel bounds", LR_EINVAL;
   p->stage_bytes = lds_stage(KS, RB, es);
   p->zv_off = kTileTokens * sk;

@@ -1211,11 +1211,19 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.copy_v = p.copy_v;
   a.nr = p.nr;
   a.raw_stage = p.raw_stage;
-  const int grid = a.n_win_blocks + p.B * p.nsplit;
   hipError_t e;
-  if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2, false>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
-  else if (p.latent == LR_I4G32) e = dispatch_decode<LT_I4>(p, a, grid, st, ev_begin, ev_end);
-  else e = dispatch_decode<LT_BF16>(p, a, grid, st, ev_begin, ev_end);
+  if (p.pf) {
+    // prefill over bf16 latents: the decode kernel runs only its exact-keys workgroups (window
+    // slots and the chunk's causal rows); the latent part is the dedicated prefill kernel
+    e = dispatch_decode<LT_BF16>(p, a, a.n_win_blocks, st, nullptr, nullptr);
+    if (e != hipSuccess) return e;
+    e = launch_prefill_latent(p, c, qt, a.part_ml, a.part_acc, st, ev_begin, ev_end);
+  } else {
+    const int grid = a.n_win_blocks + p.B * p.nsplit;
+    if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2, false>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
+    else if (p.latent == LR_I4G32) e = dispatch_decode<LT_I4>(p, a, grid, st, ev_begin, ev_end);
+    else e = dispatch_decode<LT_BF16>(p, a, grid, st, ev_begin, ev_end);
+  }
   if (e != hipSuccess) return e;
 
   // 3. combine + up-projection

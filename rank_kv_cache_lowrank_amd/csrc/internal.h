@@ -52,6 +52,10 @@ constexpr int decode_groups(int latent, int KS, int RB) {
 constexpr int decode_tpi(int latent, int KS, int RB) {
   return decode_groups(latent, KS, RB) * (decode_split(latent, KS, RB) ? 2 : 1);
 }
+// Prefill latent kernel (bf16 latents): bound on the value blocks of 16 one wave accumulates
+// for both of its head blocks (0 = unsupported).
+inline int prefill_nv(int nrb) { return nrb <= 16 ? 16 : (nrb <= 24 ? 24 : (nrb <= 32 ? 32 : 0)); }
+constexpr int kPrefillTokensPerWg = 4;   // chunk tokens per prefill workgroup (one per wave)
 // int4 latents: raw stages (16 rows of codes and scale/zero words, as stored) for the
 // direct-to-LDS loads, dequantised into two fp16 stages of the geometry above.
 constexpr int kI4DeqStages = 2;
@@ -82,6 +86,8 @@ struct DecodePlan {
   int copy_k, copy_v;               // bytes of each stored row the ring holds
   int nr, raw_stage;                // int4: raw (codes + scale/zero) stages and their bytes
   int lds_bytes;                    // dynamic LDS of the decode kernel
+  int pf;                           // prefill with the dedicated latent kernel (bf16 latents)
+  int pf_ntg, pf_nst, pf_lds;       // its token groups per sequence, ring stages, dynamic LDS
   size_t off_qt, off_ml, off_acc, off_win, ws_bytes;
 };
 
@@ -97,6 +103,11 @@ inline int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len
 hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* out,
                          int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
                          const void* k_chunk = nullptr, const void* v_chunk = nullptr);
+
+// The latent part of a prefill (p.pf): partials per (query token, token range) in the decode
+// layout, for the decode combine.
+hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, const __bf16* qt, float* part_ml,
+                                 float* part_acc, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
 
 struct AppendPlan {
   int B, D, rk, rv, latent, window, n_new;

@@ -1,0 +1,428 @@
+// Chunked prefill over a low-rank latent cache: the latent part as one dense product per token
+// group (TraceKV, "TraceKV: Policy-Preserving Low-Rank KV Cache Compression for Reasoning
+// Vision-Language Models", abstract: attention runs on the low-dimensional latents; iS-KV,
+// "iS-KV: Online Low-Rank KV Cache Compression via Block-Incremental SVD", abstract: the recent
+// tokens stay exact).
+//
+// Every token of a prefill chunk attends to the same latent prefix [0, lat_len) of its sequence
+// without a mask (the chunk's own rows and the window are exact keys, handled by the decode
+// kernel's exact-keys workgroups), so the latent part is a plain dense attention of the chunk's
+// C x 32 folded query rows against the latent rows. lr_prefill_latent gives each wave one chunk
+// token (its two 16-row head blocks of the folded query, padded from the query heads to 32)
+// for the whole latent range, so every latent byte brought into LDS feeds all of a workgroup's
+// four tokens, and every 16-byte operand read from LDS feeds two matrix-core products (one per
+// head block):
+//
+//   S^T[16 tokens, 16 heads] = Zk qt^T           16x16x32 bf16, K = rank (A = latent rows)
+//   online softmax in base 2                      (reference max with slack, as in decode)
+//   A^T[16 rv, 16 heads] += Zv^T P^T              16x16x16 bf16, K = the tile's 16 tokens
+//
+// Workgroup = 4 waves, one per SIMD (the accumulators of two head blocks over the full value
+// rank need up to ~430 registers). All four waves load the LDS ring with 16-byte direct-to-LDS
+// loads (nontemporal), each wave waiting for exactly its own loads, one barrier per 16-token
+// tile. The partials (m, l, A) per (query token, token range) have the decode layout, so the
+// decode combine merges them with the exact-keys partials and up-projects.
+#include <hip/hip_ext.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace lr {
+
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 pf_bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short pf_s16x4;
+
+constexpr float kPfMaxLead = 64.f;       // base-2 lead of a score over the reference max that
+                                         // pass 0 tolerates (p <= 2^64: finite in bf16 and f32)
+constexpr int kPfThreads = 256;
+constexpr int kPfWaves = 4;
+constexpr int kPfMaxChunks = 5;          // 1 KB direct-to-LDS chunks per wave per matrix and tile
+
+// Value operand of the 16x16x16 product (A = Zv^T, K = token) through the gfx950 transpose
+// read: in each 16-lane group g, lane j's element e comes from the address of lane 16g + 4e +
+// j/4 at element offset j%4, so lane 16g + 4e + q points at row 4g + e, column 4q of the block.
+__device__ __forceinline__ pf_bf16x4 pf_vread(const unsigned char* p) {
+  return __builtin_bit_cast(pf_bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                           (__attribute__((address_space(3))) pf_s16x4*)(p)));
+}
+
+__device__ __forceinline__ bf16x8 pf_zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
+
+}  // namespace
+
+struct PrefillArgs {
+  const unsigned char* zk;
+  const unsigned char* zv;
+  const __bf16* qt;          // [query sequences][32][rk_pad] folded queries (bf16)
+  const int32_t* lat_len;
+  float* part_ml;            // [query sequence][nsplit][Hq][2]
+  float* part_acc;           // [query sequence][nsplit][Hq][rv_pad16]
+  long long t_cap;
+  int row_bytes_k, row_bytes_v, copy_k, copy_v;
+  int rk, rk_pad, nks, nrb, rv_pad16;
+  int nsplit, split_tokens, max_len;
+  int Hq, C;                 // query heads; query tokens per stored sequence (the chunk)
+  int ntg, nunits, nst;      // token groups per sequence, units (sequence x range), ring stages
+};
+
+// KS: bound on K steps of 32 (nks <= KS); NV: bound on value blocks of 16 (nrb <= NV).
+template <int KS, int NV>
+__global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int SK = lds_stride_k(KS, 2);              // LDS row strides (bytes), as in decode
+  constexpr int SV = lds_stride_v(NV / 2, 2);
+  constexpr int ZV = kTileTokens * SK;
+  constexpr int STAGE = kTileTokens * (SK + SV);
+  static_assert((kTileTokens * SK + 1023) / 1024 <= kPfWaves * kPfMaxChunks &&
+                (kTileTokens * SV + 1023) / 1024 <= kPfWaves * kPfMaxChunks, "DMA chunks");
+  const int NST = a.nst;
+
+  // workgroup -> (unit u = sequence x token range, token group tg). The token groups of a unit
+  // take workgroup indices of one residue mod 8, so they run on one XCD and share its L2.
+  const int wgi = blockIdx.x;
+  const int tg = (wgi >> 3) % a.ntg;
+  const int u = ((wgi >> 3) / a.ntg) * 8 + (wgi & 7);
+  if (u >= a.nunits) return;                           // whole workgroup, before any barrier
+  const int b = u / a.nsplit, s = u - b * a.nsplit;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tok = tg * kPfWaves + wave;                // chunk token of this wave
+  const bool active = tok < a.C;                       // idle waves still load and meet barriers
+  const int sq = b * a.C + tok;
+
+  int L = a.lat_len[b];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  const int t_begin = s * a.split_tokens;
+  const int t_end = min(t_begin + a.split_tokens, L);
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + kTileTokens - 1) / kTileTokens : 0;
+
+  // Zero, once, the LDS columns of every stage row that no load writes (K steps and value
+  // blocks past the rank read as exact zeros). Disjoint from every loaded byte; the first
+  // barrier orders them before any read.
+  {
+    constexpr int KB = KS * 64, VB = NV * 32;
+    const int npk = (KB - a.copy_k) >> 4, npv = (VB - a.copy_v) >> 4;
+    const int per_stage = kTileTokens * (npk + npv);
+    for (int i = tid; i < NST * per_stage; i += kPfThreads) {
+      const int st = i / per_stage, j = i - st * per_stage;
+      unsigned char* p;
+      if (j < kTileTokens * npk) {
+        const int row = j / npk, gk = j - row * npk;
+        p = smem + st * STAGE + row * SK + a.copy_k + gk * 16;
+      } else {
+        const int jj = j - kTileTokens * npk;
+        const int row = jj / npv, gv = jj - row * npv;
+        p = smem + st * STAGE + ZV + row * SV + a.copy_v + gv * 16;
+      }
+      *(u32x4*)p = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- direct-to-LDS loads: chunk c (1 KB of a stage's K or V region) belongs to wave c % 4;
+  // lane l of the chunk lands at c*1024 + 16*l, i.e. at (row, col) of the region's row stride.
+  const unsigned char* gk = a.zk + ((size_t)b * a.t_cap + t_begin) * a.row_bytes_k;
+  const unsigned char* gv = a.zv + ((size_t)b * a.t_cap + t_begin) * a.row_bytes_v;
+  int offk[kPfMaxChunks], offv[kPfMaxChunks];
+#pragma unroll
+  for (int k = 0; k < kPfMaxChunks; ++k) {
+    const int o = (wave + kPfWaves * k) * 1024 + lane * 16;
+    int row = o / SK, col = o - row * SK;
+    offk[k] = (col < a.copy_k) ? row * a.row_bytes_k + col : -1;
+    row = o / SV;
+    col = o - row * SV;
+    offv[k] = (col < a.copy_v) ? row * a.row_bytes_v + col : -1;
+  }
+  // chunks holding at least one loaded byte of a tile with `rows` rows (each such chunk is one
+  // load instruction of its wave: at least one lane is active in it)
+  auto nchunks = [](int rows, int stride, int cp) { return ((rows - 1) * stride + cp + 1023) >> 10; };
+  auto pcnt = [&](int nch) { return nch > wave ? (nch - wave + kPfWaves - 1) / kPfWaves : 0; };
+  auto tile_cnt = [&](int rows) { return pcnt(nchunks(rows, SK, a.copy_k)) + pcnt(nchunks(rows, SV, a.copy_v)); };
+  const int rows_last = ntiles > 0 ? t_end - (t_begin + (ntiles - 1) * kTileTokens) : 0;
+  const int cnt_full = tile_cnt(kTileTokens);
+  const int cnt_last = ntiles > 0 ? tile_cnt(rows_last) : 0;
+  auto count = [&](int lo, int hi) {     // this wave's loads for tiles lo+1 .. hi (hi <= ntiles - 1)
+    if (hi <= lo) return 0;
+    return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
+  };
+  auto issue = [&](int t) {
+    unsigned char* stg = smem + (t % NST) * STAGE;
+    const int t0 = t * kTileTokens;
+    const int rows = min(kTileTokens, t_end - t_begin - t0);
+    if (rows < kTileTokens) {
+      // the stage's value rows past the range end still hold an older tile (possibly NaN
+      // patterns): zero them, so that P = 0 meets 0 there (plain LDS stores, published by the
+      // barrier that precedes the tile's use)
+      const int ng = (kTileTokens - rows) * (NV * 2);          // 16-byte granules (NV*32 bytes a row)
+      for (int g = wave * 64 + lane; g < ng; g += kPfThreads) {
+        const int row = rows + g / (NV * 2), col = (g % (NV * 2)) * 16;
+        *(u32x4*)(stg + ZV + row * SV + col) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    const unsigned char* srck = gk + (size_t)t0 * a.row_bytes_k;
+    const unsigned char* srcv = gv + (size_t)t0 * a.row_bytes_v;
+    const int nck = nchunks(rows, SK, a.copy_k), ncv = nchunks(rows, SV, a.copy_v);
+    const int limk = rows * a.row_bytes_k, limv = rows * a.row_bytes_v;
+#pragma unroll
+    for (int k = 0; k < kPfMaxChunks; ++k) {
+      const int c = wave + kPfWaves * k;
+      if (c < nck && offk[k] >= 0 && offk[k] < limk) dma16(srck + offk[k], stg + c * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < kPfMaxChunks; ++k) {
+      const int c = wave + kPfWaves * k;
+      if (c < ncv && offv[k] >= 0 && offv[k] < limv) dma16(srcv + offv[k], stg + ZV + c * 1024);
+    }
+  };
+
+  // The key granule that holds latent index rk (when rk is not a multiple of 8) also holds
+  // pad columns of the stored row, which may hold anything: the lane that loaded it clears
+  // them in LDS once its load has landed (before the barrier that publishes the tile), so the
+  // score products see exact zeros there.
+  u32x4 gmask;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (a.rk & 7);
+    gmask[i] = (2 * i < e ? 0x0000FFFFu : 0u) | (2 * i + 1 < e ? 0xFFFF0000u : 0u);
+  }
+  const bool ktail = (a.rk & 7) != 0;
+  auto fix_tail = [&](int t) {
+    if (!ktail) return;
+    unsigned char* stg = smem + (t % NST) * STAGE;
+    const int rows = min(kTileTokens, t_end - t_begin - t * kTileTokens);
+    const int nck = nchunks(rows, SK, a.copy_k), limk = rows * a.row_bytes_k;
+#pragma unroll
+    for (int k = 0; k < kPfMaxChunks; ++k) {
+      const int c = wave + kPfWaves * k;
+      const int o = c * 1024 + lane * 16;
+      if (c < nck && offk[k] >= 0 && offk[k] < limk && o % SK == a.copy_k - 16) {
+        u32x4* p = (u32x4*)(stg + o);
+        *p = *p & gmask;
+      }
+    }
+  };
+
+  // ---- this wave's folded query (both head blocks) as B operands: lane (lg, li) holds head
+  // 16*hb + li, latent indices 32*ks + 8*lg .. +7
+  bf16x8 qop[2][KS];
+  {
+    const __bf16* qrow = a.qt + ((size_t)(active ? sq : 0) * kHeadsPad + li) * a.rk_pad + lg * 8;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qop[hb][ks] = (active && ks < a.nks) ? *(const bf16x8*)(qrow + (size_t)hb * 16 * a.rk_pad + ks * 32)
+                                             : pf_zero8();
+  }
+  const int krow_off = li * SK + lg * 16;
+  const int vrow_off = ZV + (4 * lg + (li >> 2)) * SV + (li & 3) * 8;
+
+  // Rescale-free online softmax. The accumulators live in the accumulation registers, which
+  // vector ALU instructions cannot touch, so no pass ever rescales them:
+  //   pass 0: each head's reference max mref is its first tile's max; scores exponentiate
+  //           against it (p <= 2^kPfMaxLead keeps P, l and A finite); a tile whose max leads
+  //           mref by more than kPfMaxLead marks the workgroup;
+  //   pass 1 (marked workgroups only): the exact max of every head over the range (scores only);
+  //   pass 2 (marked only): pass 0 with mref fixed to that max, which no score exceeds.
+  // Each pass is its own loop, so the accumulators' loop-carried values never merge with a
+  // path that skips the products.
+
+  // streams the range's tiles through the ring, calling body(stage, valid rows) per tile
+  auto stream = [&](auto&& body) {
+    const int pro = min(NST - 1, ntiles);
+    for (int t = 0; t < pro; ++t) issue(t);
+    wait_vmcnt(count(0, pro - 1));                     // tile 0 landed (this wave's part)
+    if (ntiles > 0) fix_tail(0);
+    barrier_lds();
+    for (int it = 0; it < ntiles; ++it) {
+      // stage of tile it - 1: every wave finished reading it before the last barrier
+      if (it + NST - 1 < ntiles) issue(it + NST - 1);
+      body(smem + (it % NST) * STAGE, min(kTileTokens, t_end - t_begin - it * kTileTokens));
+      wait_vmcnt(count(it + 1, min(it + NST - 1, ntiles - 1)));   // tile it + 1 landed
+      if (it + 1 < ntiles) fix_tail(it + 1);
+      barrier_lds();
+    }
+  };
+  // scores of both head blocks for one tile: v[hb][i] = S^T[token 4*lg+i][head 16*hb+li] (rows
+  // past the range end -inf, NaN -> +inf so that it survives the max and poisons only its head),
+  // mx[hb] = the tile's max per head (waves without a token compute on a zero query)
+  auto scores = [&](const unsigned char* stg, int nvalid, float (&v)[2][4], float (&mx)[2]) {
+    const unsigned char* krow = stg + krow_off;
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks0 = 0; ks0 < KS; ks0 += 4) {
+      bf16x8 av[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (ks0 + k < KS) av[k] = *(const bf16x8*)(krow + (ks0 + k) * 64);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (ks0 + k < KS) {
+          sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qop[0][ks0 + k], sacc[0], 0, 0, 0);
+          sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qop[1][ks0 + k], sacc[1], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = sacc[hb][i];
+        v[hb][i] = (4 * lg + i < nvalid) ? ((x != x) ? INFINITY : x) : -INFINITY;
+      }
+      mx[hb] = wave_max_lg(fmaxf(fmaxf(v[hb][0], v[hb][1]), fmaxf(v[hb][2], v[hb][3])));
+    }
+  };
+
+  float mref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4 acc[2][NV];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) acc[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+  auto full = [&](const unsigned char* stg, int nvalid) {
+    float v[2][4], mx[2];
+    scores(stg, nvalid, v, mx);
+    // first value operands in flight under the softmax
+    constexpr int VC = 8;
+    const unsigned char* vbase = stg + vrow_off;
+    pf_bf16x4 vop[VC];
+#pragma unroll
+    for (int k = 0; k < VC; ++k) vop[k] = pf_vread(vbase + k * 32);
+    pf_bf16x4 pb[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      // a head without a reference yet takes this tile's max: its A and l are still 0
+      if (mref[hb] == -INFINITY) mref[hb] = mx[hb];
+      bad = bad || (mx[hb] > mref[hb] + kPfMaxLead);
+      const bool live = mref[hb] != -INFINITY;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 pv = (__bf16)(live ? fast_exp2(v[hb][i] - mref[hb]) : 0.f);
+        pb[hb][i] = pv;
+        ps += (float)pv;
+      }
+      lsum[hb] += ps;
+    }
+    // values: A^T[rv][head li] of both head blocks, one operand read per block
+#pragma unroll
+    for (int j0 = 0; j0 < NV; j0 += VC) {
+      if (j0 > 0) {
+#pragma unroll
+        for (int k = 0; k < VC; ++k)
+          if (j0 + k < NV) vop[k] = pf_vread(vbase + (j0 + k) * 32);
+      }
+#pragma unroll
+      for (int k = 0; k < VC; ++k) {
+        if (j0 + k < NV) {
+          acc[0][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[k], pb[0], acc[0][j0 + k], 0, 0, 0);
+          acc[1][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[k], pb[1], acc[1][j0 + k], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  int* flag = (int*)(smem + NST * STAGE + 64);         // in the slack after the ring
+  if (tid == 0) *flag = 0;                             // ordered by the first barrier of the stream
+  stream(full);                                        // pass 0
+  // any wave with a lead beyond kPfMaxLead sends the whole workgroup through passes 1-2
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) *flag = 1;
+  barrier_lds();
+  if (*flag != 0) {
+    float mexact[2] = {-INFINITY, -INFINITY};
+    stream([&](const unsigned char* stg, int nvalid) {   // pass 1
+      float v[2][4], mx[2];
+      scores(stg, nvalid, v, mx);
+      mexact[0] = fmaxf(mexact[0], mx[0]);
+      mexact[1] = fmaxf(mexact[1], mx[1]);
+    });
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      mref[hb] = mexact[hb];
+      lsum[hb] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) acc[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    stream(full);                                      // pass 2
+  }
+
+  if (!active) return;
+  const size_t pidx = (size_t)sq * a.nsplit + s;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const float l = wave_sum_lg(lsum[hb]);
+    const int head = hb * 16 + li;
+    if (head >= a.Hq) continue;
+    if (lg == 0) {
+      a.part_ml[(pidx * a.Hq + head) * 2] = mref[hb];
+      a.part_ml[(pidx * a.Hq + head) * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (j < a.nrb) *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + j * 16 + 4 * lg) = acc[hb][j];
+  }
+}
+
+template <int KS, int NV>
+static hipError_t launch_pf(const PrefillArgs& args, int grid, int lds, hipStream_t st, hipEvent_t ev_begin,
+                            hipEvent_t ev_end) {
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    e = hipFuncSetAttribute((const void*)lr_prefill_latent<KS, NV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  if (ev_begin || ev_end)
+    hipExtLaunchKernelGGL((lr_prefill_latent<KS, NV>), dim3(grid), dim3(kPfThreads), lds, st, ev_begin, ev_end, 0,
+                          args);
+  else
+    hipLaunchKernelGGL((lr_prefill_latent<KS, NV>), dim3(grid), dim3(kPfThreads), lds, st, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, const __bf16* qt, float* part_ml,
+                                 float* part_acc, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  PrefillArgs a;
+  a.zk = (const unsigned char*)c->zk;
+  a.zv = (const unsigned char*)c->zv;
+  a.qt = qt;
+  a.lat_len = c->lat_len;
+  a.part_ml = part_ml;
+  a.part_acc = part_acc;
+  a.t_cap = p.t_cap;
+  a.row_bytes_k = p.row_bytes_k;
+  a.row_bytes_v = p.row_bytes_v;
+  a.copy_k = p.copy_k;
+  a.copy_v = p.copy_v;
+  a.rk = p.rk;
+  a.rk_pad = p.rk_pad;
+  a.nks = p.nks;
+  a.nrb = p.nrb;
+  a.rv_pad16 = p.rv_pad16;
+  a.nsplit = p.nsplit;
+  a.split_tokens = p.split_tokens;
+  a.max_len = p.max_len;
+  a.Hq = p.Hq;
+  a.C = p.qpb;
+  a.ntg = p.pf_ntg;
+  a.nunits = (p.B / p.qpb) * p.nsplit;
+  a.nst = p.pf_nst;
+  const int grid = ((a.nunits + 7) / 8) * 8 * a.ntg;
+  const int ks = decode_ks(p.nks), nv = prefill_nv(p.nrb);
+#define LR_CASE(K, V) \
+  if (ks == K && nv == V) return launch_pf<K, V>(a, grid, p.pf_lds, st, ev_begin, ev_end);
+  LR_CASE(8, 16) LR_CASE(8, 24) LR_CASE(8, 32)
+  LR_CASE(12, 16) LR_CASE(12, 24) LR_CASE(12, 32)
+  LR_CASE(16, 16) LR_CASE(16, 24) LR_CASE(16, 32)
+#undef LR_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lr
