@@ -1213,9 +1213,9 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.raw_stage = p.raw_stage;
   hipError_t e;
   if (p.pf) {
-    // prefill over bf16 latents: the decode kernel runs only its exact-keys workgroups (window
-    // slots and the chunk's causal rows); the latent part is the dedicated prefill kernel
-    e = dispatch_decode<LT_BF16>(p, a, a.n_win_blocks, st, nullptr, nullptr);
+    // prefill over bf16 latents: the dedicated exact-keys kernel (window slots and the chunk's
+    // causal rows) and latent kernel
+    e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
     if (e != hipSuccess) return e;
     e = launch_prefill_latent(p, c, qt, a.part_ml, a.part_acc, st, ev_begin, ev_end);
   } else {

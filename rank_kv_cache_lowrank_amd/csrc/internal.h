@@ -109,6 +109,11 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
 hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, const __bf16* qt, float* part_ml,
                                  float* part_acc, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// The exact keys of a prefill with the dedicated kernels (p.pf): window slots and the chunk's
+// rows, causally; partials in the decode kernel's exact-keys layout.
+hipError_t launch_prefill_exact(const DecodePlan& p, const lr_layer_cache* c, const void* q, const void* k_chunk,
+                                const void* v_chunk, float* win_part, hipStream_t st);
+
 struct AppendPlan {
   int B, D, rk, rv, latent, window, n_new;
   int64_t t_cap;

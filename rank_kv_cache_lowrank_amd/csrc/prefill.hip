@@ -366,6 +366,174 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Exact keys of a prefill chunk (iS-KV abstract: the recent tokens stay exact): the live window
+// slots, then the chunk's own rows, causally. Workgroup = (stored sequence b, KV head g, 64 of
+// the C * grp query rows of that head's group; row = token c * grp + head h), one 16-row block
+// per wave. Keys are staged 32 at a time in LDS (the head's 128-wide slice of K and V) and shared
+// by the workgroup's rows:
+//   S^T[16 keys, 16 rows] = K q^T          16x16x32 bf16 (fp32 sum), times sm_scale * log2 e
+//   online softmax in base 2 (key j is visible to row (c, h) when j < live window + c + 1)
+//   O^T[16 d, 16 rows] += V^T P^T           16x16x16 bf16 through the transpose read
+// The partial (O, m, l) per (query token, head) has the layout of the decode kernel's
+// exact-keys partial, so the combine merges it unchanged.
+// ---------------------------------------------------------------------------------------------
+constexpr int kExD = 128;                 // head dim (the fold requires it too)
+constexpr int kExKeys = 32;               // keys per staged tile
+constexpr int kExSK = kExD * 2 + 16;      // LDS row strides (bytes): key rows for the A operand,
+constexpr int kExSV = kExD * 2 + 32;      // value rows for the transpose read
+
+struct ExactArgs {
+  const __bf16* q;           // [B * C][Hq][d]
+  const __bf16* kwin;        // [B][W][D] ring (slot of window entry e: (lat_len + e) % W)
+  const __bf16* vwin;
+  const __bf16* kchunk;      // [B][C][D]
+  const __bf16* vchunk;
+  const int32_t* lat_len;
+  const int32_t* win_len;
+  float* win_part;           // [B * C][Hq][d + 2]: O (unnormalised), m, l
+  int C, Hq, Hkv, D, W;
+  float wscale;              // sm_scale * log2 e
+  int nrb;                   // 64-row blocks per (b, g)
+};
+
+__global__ __launch_bounds__(256) void lr_prefill_exact(ExactArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kt[kExKeys * kExSK];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[kExKeys * kExSV];
+  const int grp = a.Hq / a.Hkv;
+  const int rb = blockIdx.x % a.nrb;
+  const int g = (blockIdx.x / a.nrb) % a.Hkv;
+  const int b = blockIdx.x / (a.nrb * a.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nrows = a.C * grp;
+  const int row0 = rb * 64 + wave * 16;              // first row of this wave's block
+  const int row = row0 + li;                         // this lane's row (as B-operand column)
+  const bool rvalid = row < nrows;
+  const int c = rvalid ? row / grp : 0, h = rvalid ? row - c * grp : 0;
+  int L = a.lat_len[b];
+  L = L < 0 ? 0 : L;
+  int wl = a.W > 0 ? a.win_len[b] : 0;
+  wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
+  const int nkeys = wl + a.C;
+  // keys this wave's rows can see: up to the last valid row's token
+  const int c_hi = min(row0 + 15, nrows - 1) / grp;
+  const int wave_keys = row0 < nrows ? wl + c_hi + 1 : 0;
+  const int my_keys = rvalid ? wl + c + 1 : 0;
+
+  // q of this lane's row as the B operand: d indices 32 ks + 8 lg .. +7
+  bf16x8 qop[4];
+  {
+    const __bf16* qr = a.q + (((size_t)b * a.C + c) * a.Hq + g * grp + h) * kExD + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qop[ks] = rvalid ? *(const bf16x8*)(qr + ks * 32) : pf_zero8();
+  }
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[kExD / 16];
+#pragma unroll
+  for (int j = 0; j < kExD / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = 0; t0 < nkeys; t0 += kExKeys) {
+    __syncthreads();                                 // the previous tile is no longer read
+    // stage keys t0 .. t0+31 (head g's slice): 16 granules of 16 bytes per row and matrix
+    for (int i = tid; i < kExKeys * 16; i += 256) {
+      const int r = i >> 4, gc = i & 15;
+      const int j = t0 + r;
+      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+      if (j < nkeys) {
+        const __bf16 *ks, *vs;
+        if (j < wl) {
+          const size_t src = ((size_t)b * a.W + (L + j) % a.W) * a.D + g * kExD + gc * 8;
+          ks = a.kwin + src;
+          vs = a.vwin + src;
+        } else {
+          const size_t src = ((size_t)b * a.C + (j - wl)) * a.D + g * kExD + gc * 8;
+          ks = a.kchunk + src;
+          vs = a.vchunk + src;
+        }
+        kv = *(const u32x4*)ks;
+        vv = *(const u32x4*)vs;
+      }
+      *(u32x4*)(kt + r * kExSK + gc * 16) = kv;
+      *(u32x4*)(vt + r * kExSV + gc * 16) = vv;
+    }
+    __syncthreads();
+    if (t0 >= wave_keys) continue;                   // nothing this wave's rows can see
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k0 = t0 + half * 16;
+      if (k0 >= wave_keys) break;
+      // scores S^T[key k0 + 4 lg + i][row li]
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      const unsigned char* krow = kt + (half * 16 + li) * kExSK + lg * 16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(krow + ks * 64), qop[ks], sacc, 0, 0, 0);
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = sacc[i] * a.wscale;
+        v[i] = (k0 + 4 * lg + i < my_keys) ? ((x != x) ? INFINITY : x) : -INFINITY;
+      }
+      const float mx = wave_max_lg(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+      const float mnew = fmaxf(m, mx);
+      if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int j = 0; j < kExD / 16; ++j) acc[j] *= alpha;
+        m = mnew;
+      }
+      const bool live = m != -INFINITY;
+      pf_bf16x4 pb;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 pv = (__bf16)(live ? fast_exp2(v[i] - m) : 0.f);
+        pb[i] = pv;
+        ps += (float)pv;
+      }
+      lsum += ps;
+      const unsigned char* vbase = vt + (half * 16 + 4 * lg + (li >> 2)) * kExSV + (li & 3) * 8;
+#pragma unroll
+      for (int j = 0; j < kExD / 16; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf_vread(vbase + j * 32), pb, acc[j], 0, 0, 0);
+    }
+  }
+  const float l = wave_sum_lg(lsum);
+  if (!rvalid) return;
+  float* wp = a.win_part + (((size_t)b * a.C + c) * a.Hq + g * grp + h) * (kExD + 2);
+#pragma unroll
+  for (int j = 0; j < kExD / 16; ++j) *(f32x4*)(wp + j * 16 + 4 * lg) = acc[j];
+  if (lg == 0) {
+    wp[kExD] = m;
+    wp[kExD + 1] = l;
+  }
+}
+
+hipError_t launch_prefill_exact(const DecodePlan& p, const lr_layer_cache* c, const void* q, const void* k_chunk,
+                                const void* v_chunk, float* win_part, hipStream_t st) {
+  ExactArgs a;
+  a.q = (const __bf16*)q;
+  a.kwin = (const __bf16*)c->kwin;
+  a.vwin = (const __bf16*)c->vwin;
+  a.kchunk = (const __bf16*)k_chunk;
+  a.vchunk = (const __bf16*)v_chunk;
+  a.lat_len = c->lat_len;
+  a.win_len = c->win_len;
+  a.win_part = win_part;
+  a.C = p.qpb;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.D = p.D;
+  a.W = p.window;
+  a.wscale = p.sm_scale * kLog2e;
+  a.nrb = (p.qpb * (p.Hq / p.Hkv) + 63) / 64;
+  const int grid = (p.B / p.qpb) * p.Hkv * a.nrb;
+  hipLaunchKernelGGL(lr_prefill_exact, dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int KS, int NV>
 static hipError_t launch_pf(const PrefillArgs& args, int grid, int lds, hipStream_t st, hipEvent_t ev_begin,
                             hipEvent_t ev_end) {

@@ -142,6 +142,54 @@ def test_chunk_then_append_then_next_chunk():
     assert rel_err(out, ref) < TOL["bf16"]
 
 
+def test_prefill_long_chunk_and_full_window():
+    """Exact keys over several staged tiles (128 window slots + a 40-token chunk) and several
+    64-row blocks per KV head (40 tokens x 7 heads)."""
+    cfg, li = small("bf16", 256, L=(50, 300, 17), window=128, wl=(128, 100, 0))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 40)
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("first_tile_score", [-40.0, -100.0])
+def test_prefill_low_first_tile(first_tile_score):
+    """The first 16 latent rows of sequences 0 and 1 are set to one row z solving q~ . z = target
+    (base-2 score units) for every chunk token and head at once (least norm; 168 equations in 358
+    unknowns). The later tiles then lead the first tile's max by about -target: -40 stays on the
+    single pass (p up to 2^40), -100 sends the workgroups through the exact-max passes. The later
+    scores are unchanged, so the softmax stays as well conditioned as the plain case."""
+    cfg, li = small("bf16", 358, L=(300, 64, 17))
+    C = 6
+    q, k, v = chunk_inputs(cfg, C, rank=358)
+    qn = q.float().cpu().numpy()
+    bk = li.bk.float().numpy().reshape(358, cfg.n_kv_heads, 128)
+    grp = cfg.n_q_heads // cfg.n_kv_heads
+    to_base2 = cfg.sm_scale * 1.4426950408889634
+    for b in (0, 1):
+        qt = np.stack([qn[b, :, h] @ bk[:, h // grp].T for h in range(cfg.n_q_heads)], 1).reshape(-1, 358)
+        z = np.linalg.lstsq(qt, np.full(qt.shape[0], first_tile_score / to_base2), rcond=None)[0]
+        li.zk[b, :16, :358] = torch.from_numpy(np.tile(z, (16, 1))).to(li.zk.dtype)
+    model, cache = device_layer(li)
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
+    assert np.isfinite(out).all()
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("rank", [358, 100])
+def test_prefill_nan_pad_columns(rank):
+    """Stored rows whose pad columns (past the rank, inside the last 16-byte granule) hold NaN:
+    they must not reach the scores."""
+    cfg = synth.Config(91, f"prefill-nanpad-r{rank}", batch=2, seq_len=90, rank_k=rank, rank_v=rank,
+                       latent="bf16")
+    li = synth.make_layer(cfg, lat_len=np.asarray([90, 33], np.int32), pad_fill=float("nan"))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 9, rank=rank)
+    out = run_prefill(model, cache, q, k, v, 90)
+    assert np.isfinite(out).all()
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
 def test_full_size_sampled():
     """16 sequences x 4096 latent rows at rank 358 (bf16) and a 32-token chunk, sampled sequences."""
     cfg = synth.CONFIGS[1]
