@@ -110,7 +110,7 @@ int plan_attention(const lr_model_desc* m, int layer, int batch, int n_q, bool p
 
   // prefill over bf16 latents: the dedicated latent kernel, one workgroup per group of
   // kPrefillTokensPerWg chunk tokens and token range
-  p->pf = (prefill && p->latent == LR_BF16) ? 1 : 0;
+  p->pf = (prefill && p->latent == LR_BF16 && p->Hq / p->Hkv <= 16) ? 1 : 0;
   p->pf_ntg = p->pf ? (n_q + kPrefillTokensPerWg - 1) / kPrefillTokensPerWg : 0;
 
   // token ranges: about one workgroup per compute unit over the batch unless overridden

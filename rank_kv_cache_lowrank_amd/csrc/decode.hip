@@ -898,7 +898,7 @@ __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T*
 
 // ---------------------------------------------------------------------------------------------
 // Fold on the matrix cores for bf16 q and Bk: one wave per (16-column block of latent indices k,
-// KV head g, sequence b). C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d] over d = 128 in four
+// KV head g, nq consecutive query sequences; the Bk operand is loaded once for all of them). C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d] over d = 128 in four
 // 16x16x32 bf16 steps (A = 16 query heads of the group, zero past grp; B = Bk^T; C row
 // h = 4*lg + i, column k = lane % 16), scaled by sm_scale * log2 e.
 // F32OUT (int4 latents): float32 output at the dequantised tiles' block order; the decode
@@ -907,10 +907,10 @@ __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T*
 template <bool F32OUT>
 __global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q, const __bf16* __restrict__ bk,
                                                     void* __restrict__ qt, int Hq, int Hkv, int D, int rk,
-                                                    int rk_pad, float scale) {
+                                                    int rk_pad, float scale, int nseq, int nq) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 4, li = lane & 15;
   const int blk = blockIdx.x * 4 + wave;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y;
   const int grp = Hq / Hkv;
   if (blk >= (rk_pad >> 4)) return;
   const int k = blk * 16 + li;
@@ -921,6 +921,7 @@ __global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q
     for (int ks = 0; ks < 4; ++ks) bop[ks] = k < rk ? *(const bf16x8*)(brow + ks * 32) : zero_bf16x8();
   }
   const int pos = F32OUT ? i4_pos(k) : k;
+  for (int b = blockIdx.z * nq; b < min(nseq, (int)(blockIdx.z + 1) * nq); ++b) {
   for (int h0 = 0; h0 < grp; h0 += 16) {
     const int hl = h0 + li;
     const __bf16* qrow = q + ((size_t)b * Hq + g * grp + hl) * kFoldD + lg * 8;
@@ -946,6 +947,7 @@ __global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q
       if constexpr (F32OUT) ((float*)qt)[o] = 0.f;
       else ((__bf16*)qt)[o] = (__bf16)0.f;
     }
+  }
   }
 }
 
@@ -1151,14 +1153,17 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
     if (p.latent == LR_F32)
       hipLaunchKernelGGL(lr_fold<float>, grid, dim3(256), 0, st, (const float*)q, (const float*)c->bk, qt,
                          p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
-    else if (p.latent == LR_I4G32)
-      hipLaunchKernelGGL(lr_fold_mfma<true>, dim3((p.rk_pad / 16 + 3) / 4, p.Hkv, p.B), dim3(256), 0, st,
-                         (const __bf16*)q, (const __bf16*)c->bk, (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad,
-                         scale);
-    else
-      hipLaunchKernelGGL(lr_fold_mfma<false>, dim3((p.rk_pad / 16 + 3) / 4, p.Hkv, p.B), dim3(256), 0, st,
-                         (const __bf16*)q, (const __bf16*)c->bk, (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad,
-                         scale);
+    else {
+      // query sequences per wave: 1 for a decode batch, up to 16 for a prefill chunk's tokens
+      const int nq = p.B >= 512 ? 16 : (p.B >= 128 ? 4 : 1);
+      const dim3 fgrid((p.rk_pad / 16 + 3) / 4, p.Hkv, (p.B + nq - 1) / nq);
+      if (p.latent == LR_I4G32)
+        hipLaunchKernelGGL(lr_fold_mfma<true>, fgrid, dim3(256), 0, st, (const __bf16*)q, (const __bf16*)c->bk,
+                           (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale, p.B, nq);
+      else
+        hipLaunchKernelGGL(lr_fold_mfma<false>, fgrid, dim3(256), 0, st, (const __bf16*)q, (const __bf16*)c->bk,
+                           (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale, p.B, nq);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1227,6 +1232,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   if (e != hipSuccess) return e;
 
   // 3. combine + up-projection
+  if (p.pf) return launch_prefill_combine(p, c, a.part_ml, a.part_acc, a.win_part, out, out_dtype, st);
   CombineArgs ca;
   ca.part_ml = a.part_ml;
   ca.part_acc = a.part_acc;

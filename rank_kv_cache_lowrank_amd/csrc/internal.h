@@ -114,6 +114,12 @@ hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, c
 hipError_t launch_prefill_exact(const DecodePlan& p, const lr_layer_cache* c, const void* q, const void* k_chunk,
                                 const void* v_chunk, float* win_part, hipStream_t st);
 
+// The combine of a prefill with the dedicated kernels (p.pf): rows of one KV head's group share
+// the up-projection's Bv slice.
+hipError_t launch_prefill_combine(const DecodePlan& p, const lr_layer_cache* c, const float* part_ml,
+                                  const float* part_acc, const float* win_part, void* out, int out_dtype,
+                                  hipStream_t st);
+
 struct AppendPlan {
   int B, D, rk, rv, latent, window, n_new;
   int64_t t_cap;

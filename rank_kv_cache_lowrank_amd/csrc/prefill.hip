@@ -534,6 +534,254 @@ hipError_t launch_prefill_exact(const DecodePlan& p, const lr_layer_cache* c, co
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Combine of a prefill: for each (query token, head) merge the latent partials of the token
+// ranges and the exact-keys partial (m* = max of the m's, weights 2^(m_s - m*), l* = sum w_s l_s,
+// Ahat = sum w_s A_s, in float32) and up-project, out = (Ahat Bv[:, g] + w_x Ax) / l*.
+// Workgroup = (stored sequence b, KV head g, up to 4 chunk tokens): its rows (token, head of the
+// group) share Bv[:, g]. The up-projection runs on the matrix cores: Ahat is split into
+// bf16 hi + lo (hi = bf16(a), lo = bf16(a - hi): a to about 2^-16 relative), Bv is bf16
+// already, so O = hi Bv + lo Bv in two 16x16x32 products with float32 sums; Bv is staged 64
+// rows at a time and read with the transpose read (K = its rows).
+// ---------------------------------------------------------------------------------------------
+constexpr int kCbMaxTokens = 4;                // chunk tokens per workgroup: 4, 2 or 1
+constexpr int kCbChunk = 64;                   // rows of Bv staged at a time
+constexpr int kCbBvStride = 128 * 2 + 32;      // LDS row stride (bytes) of the staged Bv rows
+
+struct PfCombineArgs {
+  const float* part_ml;
+  const float* part_acc;
+  const float* win_part;
+  const __bf16* bv;        // [rv][D]
+  void* out;               // [B * C][Hq][d]
+  int out_f32;
+  int C, Hq, Hkv, D, rv, rv_pad16, nsplit, ntg;
+  int tpw;                 // chunk tokens per workgroup
+  int rows_alloc;          // tpw * (heads per group), rounded up to 16
+  int kp;                  // rv rounded up to 64 (Ahat columns, zero past rv)
+};
+
+// B operand (K = 32 staged Bv rows from row k0, N = 16 columns from c0) by the transpose read:
+// lane (g, j) receives column c0 + j of rows 8g .. 8g + 7 (lane 16g + 4e + q addresses row
+// 8g + e, columns c0 + 4q .. +3; the second read the rows 4 further down).
+__device__ __forceinline__ bf16x8 cb_bv_operand(const unsigned char* tile, int k0, int c0, int lane) {
+  const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+  const unsigned char* p = tile + (k0 + 8 * g + e) * kCbBvStride + (c0 + 4 * q) * 2;
+  const pf_bf16x4 lo = pf_vread(p), hi = pf_vread(p + 4 * kCbBvStride);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = lo[i];
+    r[4 + i] = hi[i];
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(256) void lr_prefill_combine(PfCombineArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char cmem[];
+  const int grp = a.Hq / a.Hkv;
+  const int tg = blockIdx.x % a.ntg;
+  const int g = (blockIdx.x / a.ntg) % a.Hkv;
+  const int b = blockIdx.x / (a.ntg * a.Hkv);
+  const int c0 = tg * a.tpw;
+  const int ntok = min(a.tpw, a.C - c0);
+  const int R = ntok * grp;                      // rows: (token c0 + i / grp, head g*grp + i % grp)
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ahs = a.kp + 4;                      // Ahat row stride (floats): rows spread over banks
+  float* ahat = (float*)cmem;                    // [rows_alloc][ahs]
+  float* rowx = ahat + a.rows_alloc * ahs;       // [rows_alloc][2]: weight of the exact-keys partial, l*
+  float* rowm = rowx + 2 * a.rows_alloc;         // [rows_alloc]: m*
+  unsigned char* bvs = (unsigned char*)(rowm + a.rows_alloc);   // [kCbChunk][kCbBvStride]
+
+  // Bv rows r0 .. r0+63 of head g, four 16-byte granules per thread (zero past rv): loaded into
+  // registers a chunk ahead (the first one before the merge), stored to LDS when it is consumed
+  u32x4 pre[kCbChunk * 16 / 256];
+  auto bv_load = [&](int r0) {
+#pragma unroll
+    for (int k = 0; k < kCbChunk * 16 / 256; ++k) {
+      const int i = tid + 256 * k, r = i >> 4, q = i & 15;
+      pre[k] = (r0 + r < a.rv) ? *(const u32x4*)(a.bv + (size_t)(r0 + r) * a.D + g * 128 + q * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  bv_load(0);
+
+  // ---- per row: m* (over the ranges and the exact-keys partial), its weight, l*
+  if (tid < R) {
+    const int rr = tid;
+    const int sq = b * a.C + c0 + rr / grp, head = g * grp + rr % grp;
+    const float* ml = a.part_ml + ((size_t)sq * a.nsplit * a.Hq + head) * 2;   // range s at + s*Hq*2
+    const float* wp = a.win_part + ((size_t)sq * a.Hq + head) * 130;
+    const float mw = wp[128], lw = wp[129];
+    float mstar = mw;
+    for (int s = 0; s < a.nsplit; ++s) mstar = fmaxf(mstar, ml[(size_t)s * a.Hq * 2]);
+    const bool live = mstar != -INFINITY;
+    float l = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = ml[(size_t)s * a.Hq * 2];
+      const float w = (live && ms != -INFINITY) ? fast_exp2(ms - mstar) : 0.f;
+      if (w != 0.f) l += w * ml[(size_t)s * a.Hq * 2 + 1];
+    }
+    const float ww = (live && mw != -INFINITY) ? fast_exp2(mw - mstar) : 0.f;
+    rowm[rr] = mstar;
+    rowx[rr * 2] = ww;
+    rowx[rr * 2 + 1] = l + ww * lw;
+  }
+  __syncthreads();
+  // ---- Ahat: items (row, 4 consecutive latent indices) over rows_alloc x kp, zero past R and rv;
+  // four independent items per thread at a time so that their loads are in flight together
+  {
+    const int nq4 = a.kp >> 2;
+    const int nitems = a.rows_alloc * nq4;
+    for (int i0 = tid; i0 < nitems; i0 += 4 * 256) {
+      f32x4 acc[4];
+      size_t rowoff[4];
+      float mst[4];
+      bool use[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int idx = min(i0 + 256 * u, nitems - 1);
+        const int rr = idx / nq4, r = 4 * (idx - rr * nq4);
+        use[u] = i0 + 256 * u < nitems && rr < R && r < a.rv;
+        const int rs = rr < R ? rr : 0;
+        const int sq = b * a.C + c0 + rs / grp, head = g * grp + rs % grp;
+        rowoff[u] = (size_t)sq * a.nsplit * a.Hq + head;   // + s * Hq selects range s
+        mst[u] = rowm[rs];
+      }
+      for (int s = 0; s < a.nsplit; ++s) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (use[u]) {
+            const int idx = i0 + 256 * u;
+            const int r4 = idx % nq4;
+            const size_t row = rowoff[u] + (size_t)s * a.Hq;
+            const float ms = a.part_ml[row * 2];
+            const float w = (mst[u] != -INFINITY && ms != -INFINITY) ? fast_exp2(ms - mst[u]) : 0.f;
+            const f32x4 x = *(const f32x4*)(a.part_acc + row * a.rv_pad16 + 4 * r4);
+            if (w != 0.f) acc[u] += w * x;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = i0 + 256 * u;
+        if (idx < nitems) {
+          const int rr = idx / nq4, r = 4 * (idx - rr * nq4);
+          f32x4 v = acc[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (r + e < a.rv) ? v[e] : 0.f;   // pad indices: not merged
+          *(f32x4*)(ahat + rr * ahs + r) = v;
+        }
+      }
+    }
+  }
+
+  // ---- up-project: wave w takes output column blocks 2w, 2w+1 for every 16-row block
+  const int nrbk = a.rows_alloc >> 4;            // <= 4
+  f32x4 oacc[4][2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) oacc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < a.kp; r0 += kCbChunk) {
+    __syncthreads();                             // Ahat complete / previous chunk no longer read
+#pragma unroll
+    for (int k = 0; k < kCbChunk * 16 / 256; ++k) {
+      const int i = tid + 256 * k, r = i >> 4, q = i & 15;
+      *(u32x4*)(bvs + r * kCbBvStride + q * 16) = pre[k];
+    }
+    __syncthreads();
+    if (r0 + kCbChunk < a.kp) bv_load(r0 + kCbChunk);
+#pragma unroll
+    for (int ks = 0; ks < kCbChunk / 32; ++ks) {
+      const bf16x8 b0 = cb_bv_operand(bvs, ks * 32, (2 * wave) * 16, lane);
+      const bf16x8 b1 = cb_bv_operand(bvs, ks * 32, (2 * wave + 1) * 16, lane);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (rb < nrbk) {
+          const float* ar = ahat + (rb * 16 + li) * ahs + r0 + ks * 32 + lg * 8;
+          const f32x4 x0 = *(const f32x4*)ar, x1 = *(const f32x4*)(ar + 4);
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = (__bf16)x0[e];
+            hi[4 + e] = (__bf16)x1[e];
+            lo[e] = (__bf16)(x0[e] - (float)hi[e]);
+            lo[4 + e] = (__bf16)(x1[e] - (float)hi[4 + e]);
+          }
+          oacc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b0, oacc[rb][0], 0, 0, 0);
+          oacc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b0, oacc[rb][0], 0, 0, 0);
+          oacc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b1, oacc[rb][1], 0, 0, 0);
+          oacc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b1, oacc[rb][1], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // ---- out[row 16 rb + 4 lg + i][column 16 cb + li] = (O + w_x Ax) / l*
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    if (rb >= nrbk) break;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = (2 * wave + j) * 16 + li;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = rb * 16 + 4 * lg + i;
+        if (rr >= R) continue;
+        const int sq = b * a.C + c0 + rr / grp, head = g * grp + rr % grp;
+        const float ww = rowx[rr * 2], lstar = rowx[rr * 2 + 1];
+        float v = oacc[rb][j][i];
+        if (ww != 0.f) v += ww * a.win_part[((size_t)sq * a.Hq + head) * 130 + col];
+        v = (lstar == 0.f) ? 0.f : v / lstar;    // 0 only for a row with no keys; NaN stays NaN
+        const size_t o = ((size_t)sq * a.Hq + head) * 128 + col;
+        if (a.out_f32) ((float*)a.out)[o] = v;
+        else ((__bf16*)a.out)[o] = (__bf16)v;
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill_combine(const DecodePlan& p, const lr_layer_cache* c, const float* part_ml,
+                                  const float* part_acc, const float* win_part, void* out, int out_dtype,
+                                  hipStream_t st) {
+  PfCombineArgs a;
+  a.part_ml = part_ml;
+  a.part_acc = part_acc;
+  a.win_part = win_part;
+  a.bv = (const __bf16*)c->bv;
+  a.out = out;
+  a.out_f32 = out_dtype == LR_F32;
+  a.C = p.qpb;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.D = p.D;
+  a.rv = p.rv;
+  a.rv_pad16 = p.rv_pad16;
+  a.nsplit = p.nsplit;
+  // tokens per workgroup: 4 where that still gives >= 512 workgroups, else fewer
+  const int nbg = (p.B / p.qpb) * p.Hkv;
+  a.tpw = kCbMaxTokens;
+  while (a.tpw > 1 && nbg * ((p.qpb + a.tpw - 1) / a.tpw) < 512) a.tpw >>= 1;
+  a.ntg = (p.qpb + a.tpw - 1) / a.tpw;
+  a.rows_alloc = (a.tpw * (p.Hq / p.Hkv) + 15) / 16 * 16;
+  a.kp = (p.rv + 63) / 64 * 64;
+  const int grid = (p.B / p.qpb) * p.Hkv * a.ntg;
+  const size_t lds = (size_t)a.rows_alloc * (a.kp + 4) * 4 + 3 * a.rows_alloc * 4 + kCbChunk * kCbBvStride;
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    e = hipFuncSetAttribute((const void*)lr_prefill_combine, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL(lr_prefill_combine, dim3(grid), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int KS, int NV>
 static hipError_t launch_pf(const PrefillArgs& args, int grid, int lds, hipStream_t st, hipEvent_t ev_begin,
                             hipEvent_t ev_end) {
