@@ -247,9 +247,10 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
   // scores of both head blocks for one tile: v[hb][i] = S^T[token 4*lg+i][head 16*hb+li] (rows
   // past the range end -inf, NaN -> +inf so that it survives the max and poisons only its head),
   // mx[hb] = the tile's max per head (waves without a token compute on a zero query)
-  auto scores = [&](const unsigned char* stg, int nvalid, float (&v)[2][4], float (&mx)[2]) {
+  // raw score products of both head blocks for one tile (sacc[hb][i] = S^T[token 4*lg+i][head li])
+  auto products = [&](const unsigned char* stg, f32x4 (&sacc)[2]) {
     const unsigned char* krow = stg + krow_off;
-    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks0 = 0; ks0 < KS; ks0 += 4) {
       bf16x8 av[4];
@@ -264,6 +265,9 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
         }
       }
     }
+  };
+  // masked base-2 scores and the tile's max per head from the raw products
+  auto masked = [&](const f32x4 (&sacc)[2], int nvalid, float (&v)[2][4], float (&mx)[2]) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
@@ -274,6 +278,11 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
       mx[hb] = wave_max_lg(fmaxf(fmaxf(v[hb][0], v[hb][1]), fmaxf(v[hb][2], v[hb][3])));
     }
   };
+  auto scores = [&](const unsigned char* stg, int nvalid, float (&v)[2][4], float (&mx)[2]) {
+    f32x4 sacc[2];
+    products(stg, sacc);
+    masked(sacc, nvalid, v, mx);
+  };
 
   float mref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
   f32x4 acc[2][NV];
@@ -282,9 +291,9 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) acc[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
-  auto full = [&](const unsigned char* stg, int nvalid) {
+  auto finish = [&](const unsigned char* stg, int nvalid, const f32x4 (&sacc)[2]) {
     float v[2][4], mx[2];
-    scores(stg, nvalid, v, mx);
+    masked(sacc, nvalid, v, mx);
     // first value operands in flight under the softmax
     constexpr int VC = 8;
     const unsigned char* vbase = stg + vrow_off;
@@ -325,9 +334,43 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
     }
   };
 
+  // The full passes, software-pipelined by one tile: iteration it first publishes tile it + 1
+  // (its loads landed, one barrier), refills the stage tile it - 1 left (every wave finished it
+  // before that barrier), then issues tile it + 1's score products before tile it's softmax and
+  // value products, so the matrix cores work on the former while the latter's ALU work runs.
+  // Tiles it - 1, it and it + 1 occupy distinct stages (at least 3).
+  auto stream_full = [&]() {
+    const int pro = min(NST - 1, ntiles);
+    for (int t = 0; t < pro; ++t) issue(t);
+    wait_vmcnt(count(0, pro - 1));                     // tile 0 landed (this wave's part)
+    if (ntiles > 0) fix_tail(0);
+    barrier_lds();
+    f32x4 cur[2];
+    if (ntiles > 0) products(smem, cur);
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + 1 < ntiles) {
+        wait_vmcnt(count(it + 1, min(it + NST - 2, ntiles - 1)));   // tile it + 1 landed
+        fix_tail(it + 1);
+      }
+      barrier_lds();
+      if (it + NST - 1 < ntiles) issue(it + NST - 1);
+      f32x4 nxt[2];
+      products(smem + ((it + 1) % NST) * STAGE, nxt);   // (last iteration: a stale stage, unused)
+      finish(smem + (it % NST) * STAGE, min(kTileTokens, t_end - t_begin - it * kTileTokens), cur);
+      cur[0] = nxt[0];
+      cur[1] = nxt[1];
+      // interleave the next tile's score products with this tile's softmax: one matrix-core
+      // instruction, then three vector ALU instructions, 24 times
+#pragma unroll
+      for (int k = 0; k < 24; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    }
+  };
   int* flag = (int*)(smem + NST * STAGE + 64);         // in the slack after the ring
   if (tid == 0) *flag = 0;                             // ordered by the first barrier of the stream
-  stream(full);                                        // pass 0
+  stream_full();                                       // pass 0
   // any wave with a lead beyond kPfMaxLead sends the whole workgroup through passes 1-2
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) *flag = 1;
   barrier_lds();
@@ -346,7 +389,7 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < NV; ++j) acc[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    stream(full);                                      // pass 2
+    stream_full();                                     // pass 2
   }
 
   if (!active) return;
