@@ -190,6 +190,19 @@ def test_prefill_nan_pad_columns(rank):
     assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 1), (32, 1)])
+def test_prefill_head_layouts(hq, hkv):
+    """Query heads per KV head 4 and 16 (the dedicated bf16 prefill kernels) and 32 (beyond their
+    bound of 16: the decode kernels over the chunk's query tokens), with a window."""
+    cfg = synth.Config(92, f"prefill-h{hq}-{hkv}", batch=2, seq_len=150, rank_k=100, rank_v=100, latent="bf16",
+                       window=8, n_q_heads=hq, n_kv_heads=hkv)
+    li = synth.make_layer(cfg, lat_len=np.asarray([150, 41], np.int32), win_len=np.asarray([8, 3], np.int32))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 9, rank=100)
+    out = run_prefill(model, cache, q, k, v, 150)
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
 def test_full_size_sampled():
     """16 sequences x 4096 latent rows at rank 358 (bf16) and a 32-token chunk, sampled sequences."""
     cfg = synth.CONFIGS[1]
