@@ -228,7 +228,8 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
   // Each pass is its own loop, so the accumulators' loop-carried values never merge with a
   // path that skips the products.
 
-  // streams the range's tiles through the ring, calling body(stage, valid rows) per tile
+  // streams the range's tiles through the ring, calling body(stage, valid rows) per tile (the
+  // exact-max pass; the full passes use the pipelined stream_full below)
   auto stream = [&](auto&& body) {
     const int pro = min(NST - 1, ntiles);
     for (int t = 0; t < pro; ++t) issue(t);
@@ -244,10 +245,8 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
       barrier_lds();
     }
   };
-  // scores of both head blocks for one tile: v[hb][i] = S^T[token 4*lg+i][head 16*hb+li] (rows
-  // past the range end -inf, NaN -> +inf so that it survives the max and poisons only its head),
-  // mx[hb] = the tile's max per head (waves without a token compute on a zero query)
-  // raw score products of both head blocks for one tile (sacc[hb][i] = S^T[token 4*lg+i][head li])
+  // raw score products of both head blocks for one tile: sacc[hb][i] = S^T[token 4*lg+i][head
+  // 16*hb+li] (waves without a token compute on a zero query)
   auto products = [&](const unsigned char* stg, f32x4 (&sacc)[2]) {
     const unsigned char* krow = stg + krow_off;
     sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -266,7 +265,8 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
       }
     }
   };
-  // masked base-2 scores and the tile's max per head from the raw products
+  // masked base-2 scores from the raw products (rows past the range end -inf; NaN -> +inf so
+  // that it survives the max and poisons only its head) and the tile's max per head
   auto masked = [&](const f32x4 (&sacc)[2], int nvalid, float (&v)[2][4], float (&mx)[2]) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
