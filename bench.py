@@ -360,7 +360,8 @@ def _timed_calls(fn, K, W):
 
 def sensvd_bench(args):
     """Sensitivity-weighted SVD of one KV matrix's calibration rows (256 samples x 512 tokens =
-    131072 rows of dim 512, rank 358): the weighted Gram on the matrix cores, then block Jacobi.
+    131072 rows of dim 512, rank 358), or with --matrices M of M matrices in one batched call: the
+    weighted Gram on the matrix cores, then block Jacobi.
     The roofline line is the Gram's algorithmic FLOPs (N * D * (D + 1), the symmetric half plus
     the diagonal) over the whole call: the Jacobi rounds are launch-latency bound."""
     import torch
@@ -368,21 +369,43 @@ def sensvd_bench(args):
     import synth
 
     dev = "cuda"
-    n, dim, rank = args.samples, 512, 358
-    x, w = synth.gen_kv_samples(synth.CONFIGS[4], n, dim)
-    xd = torch.from_numpy(x).to(torch.bfloat16).to(dev)
-    wd = torch.from_numpy(w).to(dev)
-    basis = torch.empty(rank, dim, dtype=torch.bfloat16, device=dev)
-    sigma = torch.empty(dim, dtype=torch.float32, device=dev)
-    ws = torch.empty(lr.lowrank_sens_svd_workspace_size(n, dim), dtype=torch.uint8, device=dev)
-    ms = _timed_calls(lambda: lr.lowrank_sens_svd(xd, wd, rank, basis, sigma, ws), args.steps, args.warmup)
+    M, dim, rank = args.matrices, 512, 358
+    if M == 1:
+        n = args.samples
+        x, w = synth.gen_kv_samples(synth.CONFIGS[4], n, dim)
+        xd = torch.from_numpy(x).to(torch.bfloat16).to(dev)
+        wd = torch.from_numpy(w).to(dev)
+        basis = torch.empty(rank, dim, dtype=torch.bfloat16, device=dev)
+        sigma = torch.empty(dim, dtype=torch.float32, device=dev)
+        ws = torch.empty(lr.lowrank_sens_svd_workspace_size(n, dim), dtype=torch.uint8, device=dev)
+        call = lambda: lr.lowrank_sens_svd(xd, wd, rank, basis, sigma, ws)   # noqa: E731
+        metric = "sensitivity-weighted SVD basis of one KV matrix: ms per call"
+        workload = f"sensvd N{n} D{dim} r{rank}"
+    else:
+        # a model's K and V matrices in one batched call; each matrix its own spectrum decay
+        n = args.samples if args.samples != 131072 else 16384
+        log(f"generating {M} x {n} samples ...")
+        xs = np.empty((M, n, dim), np.float32)
+        wv = np.empty((M, n), np.float32)
+        for m in range(M):
+            xs[m], wv[m] = synth.gen_kv_samples(synth.CONFIGS[4], n, dim, 0.6 + 0.01 * m)
+        xd = torch.from_numpy(xs).to(torch.bfloat16).to(dev)
+        wd = torch.from_numpy(wv).to(dev)
+        del xs
+        basis = torch.empty(M, rank, dim, dtype=torch.bfloat16, device=dev)
+        sigma = torch.empty(M, dim, dtype=torch.float32, device=dev)
+        ws = torch.empty(lr.lowrank_sens_svd_batched_workspace_size(M, n, dim), dtype=torch.uint8, device=dev)
+        call = lambda: lr.lowrank_sens_svd_batched(xd, wd, rank, basis, sigma, ws)   # noqa: E731
+        metric = f"sensitivity-weighted SVD bases of {M} KV matrices in one batched call: ms per call"
+        workload = f"sensvd {M}x N{n} D{dim} r{rank}"
+    ms = _timed_calls(call, args.steps, args.warmup)
     assert torch.isfinite(sigma).all()
-    flops = float(n) * dim * (dim + 1)
-    rec = {"metric": "sensitivity-weighted SVD basis of one KV matrix: ms per call", "value": round(ms, 4),
+    flops = float(M) * n * dim * (dim + 1)
+    rec = {"metric": metric, "value": round(ms, 4),
            "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": f"sensvd N{n} D{dim} r{rank}", "samples": n, "dim": dim, "rank": rank,
+           "config": {"workload": workload, "matrices": M, "samples": n, "dim": dim, "rank": rank,
                       "sweeps": 10, "parallelism": "single GPU"},
            "roofline": {"bound": "mfma", "kernel": "lr_svd_gram + block Jacobi (whole call)",
                         "achieved": round(flops / (ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
@@ -434,7 +457,9 @@ def main():
                     help="decode: the decode step (default); rebase: the historical-coordinate sync; "
                          "prefill: chunked prefill attention; sensvd: sensitivity-weighted SVD basis; "
                          "rankalloc: global rank allocation")
-    ap.add_argument("--samples", type=int, default=131072, help="--op sensvd: calibration rows")
+    ap.add_argument("--samples", type=int, default=131072,
+                    help="--op sensvd: calibration rows per matrix (batched default: 16384)")
+    ap.add_argument("--matrices", type=int, default=1, help="--op sensvd: matrices per (batched) call")
     ap.add_argument("--chunk", type=int, default=32, help="--op prefill: new tokens per sequence")
     ap.add_argument("--rank-new", type=int, default=0, help="--op rebase: new rank (0: unchanged)")
     args = ap.parse_args()

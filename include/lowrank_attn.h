@@ -273,6 +273,20 @@ int lowrank_sens_svd(const void* x, const float* w, int32_t n_samples, int32_t d
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lowrank_sens_svd for n_mat matrices of one shape in one call (e.g. the K and V matrices of
+ * every layer of a model): x [n_mat][n_samples][dim] bfloat16, w [n_mat][n_samples] float32,
+ * basis [n_mat][rank][dim], sigma [n_mat][dim], contiguous; matrix m's results equal those of
+ * lowrank_sens_svd on its slices (the same kernels, with the matrix index as a grid dimension,
+ * so the Jacobi rounds of all matrices run together). 1 <= n_mat <= 65535; the other arguments
+ * and errors as for lowrank_sens_svd. workspace: lowrank_sens_svd_batched_workspace_size()
+ * bytes (n_mat times the single-matrix size), 256-byte aligned.
+ */
+size_t lowrank_sens_svd_batched_workspace_size(int32_t n_mat, int32_t n_samples, int32_t dim);
+int lowrank_sens_svd_batched(const void* x, const float* w, int32_t n_mat, int32_t n_samples, int32_t dim,
+                             int32_t rank, int32_t sweeps, void* basis, int32_t basis_dtype, float* sigma,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Global rank allocation (TraceKV abstract; ai4snews Synopsis and Interpretation: the rank
  * budget is allocated globally across the KV states). Rule (the pages do not give one): every
  * matrix m (K or V of a layer) starts at r_min and grows by granules of `granule` up to r_max;

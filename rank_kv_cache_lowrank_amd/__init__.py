@@ -10,5 +10,6 @@ from ._lib import (  # noqa: F401
     lowrank_attn_decode_workspace_size, lowrank_attn_prefill, lowrank_attn_prefill_workspace_size,
     lowrank_kv_append, lowrank_kv_dequant, lowrank_kv_rebase, lowrank_rank_allocate,
     lowrank_rank_allocate_workspace_size, lowrank_sens_svd, lowrank_sens_svd_workspace_size,
+    lowrank_sens_svd_batched, lowrank_sens_svd_batched_workspace_size,
     lowrank_kv_store,
     lowrank_last_error, prefill_workspace, workspace)

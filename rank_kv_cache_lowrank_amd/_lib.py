@@ -23,6 +23,7 @@ DTYPES = {"f32": LR_F32, "bf16": LR_BF16, "i4g32": LR_I4G32}
 
 EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_attn_prefill_workspace_size",
            "lowrank_attn_prefill", "lowrank_sens_svd_workspace_size", "lowrank_sens_svd",
+           "lowrank_sens_svd_batched_workspace_size", "lowrank_sens_svd_batched",
            "lowrank_rank_allocate_workspace_size", "lowrank_rank_allocate",
            "lowrank_kv_append",
            "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_last_error",
@@ -80,6 +81,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          c_void_p, c_size_t, POINTER(lr_decode_opts), c_void_p]
     lib.lowrank_sens_svd_workspace_size.restype = c_size_t
     lib.lowrank_sens_svd_workspace_size.argtypes = [c_int32, c_int32]
+    lib.lowrank_sens_svd_batched_workspace_size.restype = c_size_t
+    lib.lowrank_sens_svd_batched_workspace_size.argtypes = [c_int32, c_int32, c_int32]
+    lib.lowrank_sens_svd_batched.restype = c_int32
+    lib.lowrank_sens_svd_batched.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                             c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.lowrank_sens_svd.restype = c_int32
     lib.lowrank_sens_svd.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
                                      c_void_p, c_void_p, c_size_t, c_void_p]
@@ -247,6 +253,21 @@ def lowrank_sens_svd(x: torch.Tensor, w: torch.Tensor, rank: int, basis: torch.T
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().lowrank_sens_svd(_ptr(x), _ptr(w), n, dim, rank, sweeps, _ptr(basis), bdt, _ptr(sigma),
                                    _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def lowrank_sens_svd_batched_workspace_size(n_mat: int, n_samples: int, dim: int) -> int:
+    return int(load().lowrank_sens_svd_batched_workspace_size(n_mat, n_samples, dim))
+
+
+def lowrank_sens_svd_batched(x: torch.Tensor, w: torch.Tensor, rank: int, basis: torch.Tensor, sigma: torch.Tensor,
+                             workspace: torch.Tensor, sweeps: int = 0, stream=None) -> None:
+    """x [n_mat][n][dim] bf16, w [n_mat][n] f32; basis [n_mat][rank][dim] f32 or bf16 (output), sigma
+    [n_mat][dim] f32 (output)."""
+    n_mat, n, dim = x.shape
+    bdt = LR_F32 if basis.dtype == torch.float32 else LR_BF16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().lowrank_sens_svd_batched(_ptr(x), _ptr(w), n_mat, n, dim, rank, sweeps, _ptr(basis), bdt,
+                                           _ptr(sigma), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def lowrank_rank_allocate_workspace_size(n_mat: int, r_min: int, r_max: int, granule: int) -> int:

@@ -521,7 +521,35 @@ int lowrank_sens_svd(const void* x, const float* w, int32_t n_samples, int32_t d
     return fail(LR_EINVAL, "x must be 16-byte aligned, workspace 256-byte aligned");
   if (workspace_bytes < lowrank_sens_svd_workspace_size(n_samples, dim))
     return fail(LR_EWORKSPACE, "workspace too small");
-  hipError_t e = launch_sens_svd(x, w, n_samples, dim, rank, sweeps == 0 ? 10 : sweeps, basis,
+  hipError_t e = launch_sens_svd(x, w, 1, n_samples, dim, rank, sweeps == 0 ? 10 : sweeps, basis,
+                                 basis_dtype == LR_F32, sigma, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+size_t lowrank_sens_svd_batched_workspace_size(int32_t n_mat, int32_t n_samples, int32_t dim) {
+  if (n_mat < 1 || n_mat > 65535 || n_samples < 0 || dim < 64 || dim > 512 || dim % 64 != 0) return 0;
+  return (size_t)n_mat * svd_workspace_stride(n_samples, dim);
+}
+
+int lowrank_sens_svd_batched(const void* x, const float* w, int32_t n_mat, int32_t n_samples, int32_t dim,
+                             int32_t rank, int32_t sweeps, void* basis, int32_t basis_dtype, float* sigma,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  LR_GUARD_BEGIN
+  if (n_mat < 1 || n_mat > 65535) return fail(LR_EINVAL, "n_mat must be in 1..65535");
+  if (n_samples < 0) return fail(LR_EINVAL, "n_samples must be >= 0");
+  if (dim < 64 || dim > 512 || dim % 64 != 0) return fail(LR_EUNSUPPORTED, "dim must be a multiple of 64 in 64..512");
+  if (rank < 1 || rank > dim) return fail(LR_EINVAL, "rank must be in 1..dim");
+  if (sweeps < 0 || sweeps > 64) return fail(LR_EINVAL, "sweeps must be in 0..64 (0 = default 10)");
+  if (basis_dtype != LR_F32 && basis_dtype != LR_BF16) return fail(LR_EINVAL, "basis_dtype must be LR_F32 or LR_BF16");
+  if ((n_samples > 0 && (!x || !w)) || !basis || !sigma || !workspace)
+    return fail(LR_EINVAL, "x, w, basis, sigma and workspace must not be NULL");
+  if (!aligned(x, 16) || !aligned(w, 4) || !aligned(basis, 4) || !aligned(sigma, 4) || !aligned(workspace, 256))
+    return fail(LR_EINVAL, "x must be 16-byte aligned, workspace 256-byte aligned");
+  if (workspace_bytes < lowrank_sens_svd_batched_workspace_size(n_mat, n_samples, dim))
+    return fail(LR_EWORKSPACE, "workspace too small");
+  hipError_t e = launch_sens_svd(x, w, n_mat, n_samples, dim, rank, sweeps == 0 ? 10 : sweeps, basis,
                                  basis_dtype == LR_F32, sigma, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
   return LR_OK;

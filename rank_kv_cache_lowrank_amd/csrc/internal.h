@@ -142,7 +142,8 @@ struct RebasePlan {
 hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const lr_layer_cache* dst,
                          const void* wk, const void* wv, hipStream_t st);
 size_t svd_workspace_bytes(int n, int D);
-hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank, int sweeps, void* basis,
+size_t svd_workspace_stride(int n, int D);   // per matrix of a batch (256-byte multiple)
+hipError_t launch_sens_svd(const void* x, const float* w, int n_mat, int n, int D, int rank, int sweeps, void* basis,
                            int basis_f32, float* sigma, void* ws, hipStream_t st);
 
 hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, long long n_take, int r_min,

@@ -1,6 +1,9 @@
 // Sensitivity-weighted SVD basis construction (TraceKV abstract; ai4snews Synopsis and
 // Interpretation: each KV state is weighted by its sensitivity before the SVD).
 //
+// (A batch of matrices of one shape runs as one: every kernel takes the matrix index from a spare
+// grid dimension and its pointers from svd_at.)
+//
 // For KV samples x_n [D] (bf16) and sensitivities w_n >= 0 the basis is the top-r right singular
 // vectors of diag(sqrt(w)) X, and the spectrum its singular values. With y_n = bf16(sqrt(w_n) x_n)
 // (float32 product, one rounding: the matrix-core operand) they are the eigenvectors and the
@@ -10,8 +13,8 @@
 //                   32 samples at a time are weighted, rounded and staged in LDS row-major, and
 //                   both 16x16x32 bf16 matrix-core operands (K = samples) come from the gfx950
 //                   transpose read; float32 accumulation.
-//   lr_svd_reduce   G = sum of the partials in range order (deterministic), mirrored, and a
-//                   copy G0 of it; V = I.
+//   lr_svd_reduce   G = sum of the partials in range order (deterministic), per upper tile,
+//                   mirrored through LDS, and a copy G0 of it; V = I.
 //   lr_jacobi_pair  block Jacobi over 16-index blocks, circle ordering (D/16 - 1 rounds per
 //   lr_jacobi_apply sweep): one workgroup per block pair reduces the pair's 32x32 block of G in
 //                   LDS by one cyclic sweep of scalar Jacobi (rotations as in Golub and Van
@@ -71,9 +74,31 @@ struct SvdArgs {
   void* basis;       // [rank][D]
   float* sigma;      // [D]
   int n, D, nsplit, rank, basis_f32, round;
+  size_t ws_stride;  // workspace bytes per matrix of a batch
 };
 
+// The arguments of matrix m of a batch: inputs [m][n][D] and [m][n], outputs [m][rank][D] and
+// [m][D], and the m-th workspace slice.
+__device__ __forceinline__ SvdArgs svd_at(SvdArgs a, int m) {
+  const size_t nd = (size_t)a.n * a.D;
+  a.x += (size_t)m * nd;
+  a.w += (size_t)m * a.n;
+  const size_t wo = (size_t)m * a.ws_stride;
+  a.part = (float*)((unsigned char*)a.part + wo);
+  a.G = (float*)((unsigned char*)a.G + wo);
+  a.G0 = (float*)((unsigned char*)a.G0 + wo);
+  a.V = (float*)((unsigned char*)a.V + wo);
+  a.U = (float*)((unsigned char*)a.U + wo);
+  a.rq = (double*)((unsigned char*)a.rq + wo);
+  a.ord = (int*)((unsigned char*)a.ord + wo);
+  const size_t bo = (size_t)m * a.rank * a.D * (a.basis_f32 ? 4 : 2);
+  a.basis = (void*)((unsigned char*)a.basis + bo);
+  a.sigma += (size_t)m * a.D;
+  return a;
+}
+
 __global__ __launch_bounds__(256) void lr_svd_gram(SvdArgs a) {
+  a = svd_at(a, blockIdx.z);
   __shared__ __attribute__((aligned(16))) unsigned char tile[kSvdK * kSvdStride];
   // upper-triangle tile index -> (I, J), I <= J
   const int nbt = a.D / kSvdTile;
@@ -141,17 +166,48 @@ __global__ __launch_bounds__(256) void lr_svd_gram(SvdArgs a) {
       }
 }
 
+// One workgroup per 64x64 tile (I, J), I <= J, of the upper triangle (the tiles the partial
+// Grams hold): each entry is the sum of the partials in range order (coalesced rows, eight
+// loads issued ahead of their additions), written to G and G0 at (I, J) and, through LDS, at
+// the mirrored tile (J, I); V = I.
 __global__ __launch_bounds__(256) void lr_svd_reduce(SvdArgs a) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)a.D * a.D) return;
-  const int i = (int)(idx / a.D), j = (int)(idx - (long long)i * a.D);
-  const bool upper = (i / kSvdTile) <= (j / kSvdTile);
-  const size_t src = upper ? (size_t)i * a.D + j : (size_t)j * a.D + i;
-  float g = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) g += a.part[(size_t)s * a.D * a.D + src];
-  a.G[idx] = g;
-  a.G0[idx] = g;
-  a.V[idx] = (i == j) ? 1.f : 0.f;
+  a = svd_at(a, blockIdx.y);
+  __shared__ float T[kSvdTile][kSvdTile + 1];
+  const int nbt = a.D / kSvdTile;
+  int t = blockIdx.x, I = 0;
+  while (t >= nbt - I) {
+    t -= nbt - I;
+    ++I;
+  }
+  const int J = I + t;
+  const size_t dd = (size_t)a.D * a.D;
+  for (int e = threadIdx.x; e < kSvdTile * kSvdTile; e += 256) {
+    const int r = e / kSvdTile, c = e - r * kSvdTile;
+    const size_t src = (size_t)(I * kSvdTile + r) * a.D + J * kSvdTile + c;
+    float g = 0.f;
+    int s = 0;
+    for (; s + 8 <= a.nsplit; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.part[(size_t)(s + u) * dd + src];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) g += v[u];
+    }
+    for (; s < a.nsplit; ++s) g += a.part[(size_t)s * dd + src];
+    a.G[src] = g;
+    a.G0[src] = g;
+    a.V[src] = (I == J && r == c) ? 1.f : 0.f;
+    T[r][c] = g;
+  }
+  if (I == J) return;                            // a diagonal tile holds both triangles
+  __syncthreads();
+  for (int e = threadIdx.x; e < kSvdTile * kSvdTile; e += 256) {
+    const int r = e / kSvdTile, c = e - r * kSvdTile;
+    const size_t dst = (size_t)(J * kSvdTile + r) * a.D + I * kSvdTile + c;
+    a.G[dst] = T[c][r];
+    a.G0[dst] = T[c][r];
+    a.V[dst] = 0.f;
+  }
 }
 
 // circle-method pairing: round r of n (even) players, pair k -> (lo, hi) player indices
@@ -194,6 +250,7 @@ __device__ __forceinline__ void jacobi_rotation_fast(float app, float aqq, float
 }
 
 __global__ __launch_bounds__(256) void lr_jacobi_pair(SvdArgs a) {
+  a = svd_at(a, blockIdx.y);
   // row stride 48: in the circle ordering p + q is the same for every pair of a step, so with a
   // stride of 33 the pairs' (p, q) entries would all fall in one bank; 48 spreads them and the
   // two rows of a half-wave's blocks over different banks
@@ -265,6 +322,7 @@ __global__ __launch_bounds__(256) void lr_jacobi_pair(SvdArgs a) {
 // symmetric); the rest take 32-row blocks of V times U_j. Thread (r, c4): row r, columns
 // c4 .. c4+3 (inside one 16-index block, so the global accesses are 16-byte vectors).
 __global__ __launch_bounds__(256) void lr_jacobi_apply(SvdArgs a) {
+  a = svd_at(a, blockIdx.y);
   constexpr int LD = kJs + 1;
   __shared__ float B[kJs * LD];
   __shared__ float Ui[kJs * LD];
@@ -345,6 +403,7 @@ constexpr int kRqRows = 64;   // rows of G0 per workgroup in lr_svd_rayleigh
 // at columns t and t + 256, coalesced) into rq[j0 / 64][k] (float64); range 0 also writes
 // v_k^T v_k. lr_svd_sort adds the partials in range order.
 __global__ __launch_bounds__(256) void lr_svd_rayleigh(SvdArgs a) {
+  a = svd_at(a, blockIdx.z);
   __shared__ __attribute__((aligned(16))) float Vs[512 * kRqCols];
   __shared__ double red[4][2 * kRqCols];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -409,6 +468,7 @@ __global__ __launch_bounds__(256) void lr_svd_rayleigh(SvdArgs a) {
 // values ordered by column index; sigma = sqrt(max(lambda, 0)); the first rank column indices
 // go to ord.
 __global__ __launch_bounds__(512) void lr_svd_sort(SvdArgs a) {
+  a = svd_at(a, blockIdx.x);
   __shared__ float key[512];
   __shared__ int idx[512];
   const int tid = threadIdx.x;
@@ -455,6 +515,7 @@ __global__ __launch_bounds__(512) void lr_svd_sort(SvdArgs a) {
 // columns orthogonal to float precision but let their norms drift by a few 1e-4 over the
 // sweeps), its largest-magnitude component (lowest index among equal magnitudes) made positive.
 __global__ __launch_bounds__(256) void lr_svd_basis(SvdArgs a) {
+  a = svd_at(a, blockIdx.y);
   __shared__ double rn[4];
   __shared__ float rv[4];
   __shared__ int ri[4];
@@ -518,7 +579,9 @@ size_t svd_workspace_bytes(int n, int D) {
          (size_t)(D / kRqRows + 1) * D * 8 + (size_t)D * 4 + 1024;
 }
 
-hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank, int sweeps, void* basis,
+size_t svd_workspace_stride(int n, int D) { return (svd_workspace_bytes(n, D) + 255) / 256 * 256; }
+
+hipError_t launch_sens_svd(const void* x, const float* w, int n_mat, int n, int D, int rank, int sweeps, void* basis,
                            int basis_f32, float* sigma, void* ws, hipStream_t st) {
   SvdArgs a;
   a.x = (const __bf16*)x;
@@ -530,6 +593,7 @@ hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank
   a.basis = basis;
   a.basis_f32 = basis_f32;
   a.sigma = sigma;
+  a.ws_stride = svd_workspace_stride(n, D);
   unsigned char* p = (unsigned char*)ws;
   const size_t dd = (size_t)D * D * 4;
   a.part = (float*)p;
@@ -541,25 +605,27 @@ hipError_t launch_sens_svd(const void* x, const float* w, int n, int D, int rank
   a.ord = (int*)(a.rq + (size_t)(D / kRqRows + 1) * D);
   a.round = 0;
   const int nbt = D / kSvdTile;
-  hipLaunchKernelGGL(lr_svd_gram, dim3(nbt * (nbt + 1) / 2, a.nsplit), dim3(256), 0, st, a);
+  const unsigned M = (unsigned)n_mat;
+  hipLaunchKernelGGL(lr_svd_gram, dim3(nbt * (nbt + 1) / 2, a.nsplit, M), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lr_svd_reduce, dim3((unsigned)(((long long)D * D + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(lr_svd_reduce, dim3(nbt * (nbt + 1) / 2, M), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = D / kJb, npairs = nb / 2;
   for (int sw = 0; sw < sweeps; ++sw) {
     for (int r = 0; r < nb - 1; ++r) {
       a.round = r;
-      hipLaunchKernelGGL(lr_jacobi_pair, dim3(npairs), dim3(256), 0, st, a);
-      hipLaunchKernelGGL(lr_jacobi_apply, dim3(npairs * (npairs + 1) / 2 + npairs * (D / kJs)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(lr_jacobi_pair, dim3(npairs, M), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(lr_jacobi_apply, dim3(npairs * (npairs + 1) / 2 + npairs * (D / kJs), M), dim3(256), 0, st,
+                         a);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(lr_svd_rayleigh, dim3(D / kRqCols, D / kRqRows), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(lr_svd_sort, dim3(1), dim3(512), 0, st, a);
-  if (rank > 0) hipLaunchKernelGGL(lr_svd_basis, dim3(rank), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(lr_svd_rayleigh, dim3(D / kRqCols, D / kRqRows, M), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(lr_svd_sort, dim3(M), dim3(512), 0, st, a);
+  if (rank > 0) hipLaunchKernelGGL(lr_svd_basis, dim3(rank, M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

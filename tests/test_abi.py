@@ -259,3 +259,43 @@ def test_rank_allocate_validation(args, code):
     assert lib.lowrank_rank_allocate(1 << 20, n_mat, n_sigma, ld, budget, r_min, r_max, g, 1 << 21, 1 << 22,
                                      1 << 30, None) == code
     assert lr.lowrank_last_error() != ""
+
+
+@host_only
+@pytest.mark.parametrize("args,code", [
+    ((3, 1000, 512, 358, 0, L.LR_F32), L.LR_OK),
+    ((0, 1000, 512, 358, 0, L.LR_F32), L.LR_EINVAL),        # no matrix
+    ((3, -1, 512, 358, 0, L.LR_F32), L.LR_EINVAL),          # negative sample count
+    ((3, 1000, 96, 32, 0, L.LR_F32), L.LR_EUNSUPPORTED),    # dim not a multiple of 64
+    ((3, 1000, 576, 32, 0, L.LR_F32), L.LR_EUNSUPPORTED),   # dim above 512
+    ((3, 1000, 512, 513, 0, L.LR_F32), L.LR_EINVAL),        # rank above dim
+    ((3, 1000, 512, 0, 0, L.LR_F32), L.LR_EINVAL),          # rank below 1
+    ((3, 1000, 512, 358, 65, L.LR_F32), L.LR_EINVAL),       # too many sweeps
+    ((3, 1000, 512, 358, 0, L.LR_I4G32), L.LR_EINVAL),      # basis dtype
+])
+def test_sens_svd_batched_validation(args, code):
+    """Argument checks of the batched and single-matrix weighted SVD (no work is enqueued)."""
+    lib = lr.load()
+    n_mat, n, dim, rank, sweeps, bdt = args
+    ws = lr.lowrank_sens_svd_batched_workspace_size(n_mat, n, dim)
+    if code == L.LR_OK:
+        one = lr.lowrank_sens_svd_workspace_size(n, dim)
+        assert one > 0 and ws == n_mat * one
+        return
+    assert lib.lowrank_sens_svd_batched(1 << 20, 1 << 21, n_mat, n, dim, rank, sweeps, 1 << 22, bdt, 1 << 23,
+                                        1 << 24, 1 << 40, None) == code
+    assert lr.lowrank_last_error() != ""
+    if n_mat == 1 or n_mat == 3:
+        assert lib.lowrank_sens_svd(1 << 20, 1 << 21, n, dim, rank, sweeps, 1 << 22, bdt, 1 << 23, 1 << 24,
+                                    1 << 40, None) == code
+
+
+@host_only
+def test_sens_svd_batched_workspace_checks():
+    lib = lr.load()
+    ws = lr.lowrank_sens_svd_batched_workspace_size(4, 2048, 256)
+    assert lib.lowrank_sens_svd_batched(1 << 20, 1 << 21, 4, 2048, 256, 64, 0, 1 << 22, L.LR_F32, 1 << 23, 1 << 24,
+                                        ws - 1, None) == L.LR_EWORKSPACE
+    assert lib.lowrank_sens_svd_batched(1 << 20, 1 << 21, 4, 2048, 256, 64, 0, 1 << 22, L.LR_F32, 1 << 23,
+                                        (1 << 24) + 16, ws, None) == L.LR_EINVAL   # workspace alignment
+    assert lr.lowrank_sens_svd_batched_workspace_size(70000, 2048, 256) == 0

@@ -107,6 +107,29 @@ def test_full_calibration_shape():
     check(x, w, 358, b, s)
 
 
+@pytest.mark.parametrize("n_mat,n,dim,rank", [(3, 1000, 256, 64), (4, 4096, 512, 358)])
+def test_batched_equals_single_calls(n_mat, n, dim, rank):
+    """lowrank_sens_svd_batched: matrix m's basis and spectrum are bit-identical to a single call on
+    its slices (the same kernels), and match the oracle."""
+    xs, ws_ = [], []
+    for m in range(n_mat):
+        x, w = synth.gen_kv_samples(synth.CONFIGS[4], n, dim, 0.6 + 0.2 * m)
+        xs.append(x)
+        ws_.append(w)
+    xd = torch.from_numpy(np.stack(xs).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    wd = torch.from_numpy(np.stack(ws_).astype(np.float32)).to(DEV)
+    basis = torch.full((n_mat, rank, dim), float("nan"), dtype=torch.float32, device=DEV)
+    sigma = torch.empty(n_mat, dim, dtype=torch.float32, device=DEV)
+    ws = torch.empty(lr.lowrank_sens_svd_batched_workspace_size(n_mat, n, dim), dtype=torch.uint8, device=DEV)
+    lr.lowrank_sens_svd_batched(xd, wd, rank, basis, sigma, ws)
+    torch.cuda.synchronize()
+    for m in range(n_mat):
+        b1, s1 = run(xs[m], ws_[m], rank)
+        np.testing.assert_array_equal(basis[m].cpu().numpy().astype(np.float64), b1)
+        np.testing.assert_array_equal(sigma[m].cpu().numpy().astype(np.float64), s1)
+        check(xs[m], ws_[m], rank, b1, s1, gap_at_rank=rank < dim)
+
+
 def test_invalid_arguments():
     x = torch.zeros(16, 96, dtype=torch.bfloat16, device=DEV)
     w = torch.ones(16, device=DEV)
