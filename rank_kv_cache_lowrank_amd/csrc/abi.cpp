@@ -145,15 +145,15 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
     const int gk = (p->rk + 31) / 32, gv = (p->rv + 31) / 32;
     p->qp_bytes_k = gk * 4;
     p->qp_bytes_v = gv * 4;
-    p->stage_bytes = lds_stage(KS, RB, 2);
-    p->zv_off = kTileTokens * lds_stride_k(KS, 2);
-    p->nst = kI4DeqStages;
+    p->stage_bytes = i4_vstage(RB);
+    p->zv_off = 0;
+    p->nst = kI4VStages;
     p->raw_stage = i4_raw_stage(gk, gv);
-    int nr = (kLdsBytes - kLdsPad - kI4DeqStages * p->stage_bytes) / p->raw_stage;
+    int nr = (kLdsBytes - kLdsPad - kI4VStages * p->stage_bytes) / p->raw_stage;
     if (nr > kI4MaxRawStages) nr = kI4MaxRawStages;
-    if (nr < 3) return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
+    if (nr < kI4MinRawStages) return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
     p->nr = nr;
-    int lds = kI4DeqStages * p->stage_bytes + nr * p->raw_stage + kLdsPad;
+    int lds = kI4VStages * p->stage_bytes + nr * p->raw_stage + kLdsPad;
     if (window_lds > lds) lds = window_lds;
     if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;
     p->lds_bytes = lds;

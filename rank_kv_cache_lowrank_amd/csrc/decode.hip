@@ -139,19 +139,25 @@ __device__ __forceinline__ f32x4 mfma_v(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 
 // Eight int4 codes (w: index i in bits 4i..4i+3) -> eight fp16 values zhat = fma(code, scale,
-// zero), one rounding. Output dword i holds indices i and i + 4 (block order 0,4,1,5,2,6,3,7):
-// (w >> 4i) & 0x000F000F places those two codes in the two halves, and or-ing in 0x6400 makes
-// each half the fp16 number 1024 + code exactly, so one packed subtraction recovers the code.
-// kMask / kMagic arrive in registers (0x000F000F, 0x64006400) so that the and-or is one
-// three-operand instruction.
-__device__ __forceinline__ u32x4 dequant8_f16(unsigned w, f16x2 s2, f16x2 z2, unsigned kMask, unsigned kMagic) {
+// zero), one rounding. Output dword i holds indices i and i + 4 (block order 0,4,1,5,2,6,3,7).
+// A code lands in the mantissa of an fp16 number whose value is then exactly magic + code: from
+// bits 0-3 of a half word under the exponent of 1024 (mantissa unit 1), from bits 4-7 under
+// that of 64 (mantissa unit 1/16). So w and w >> 8, each masked twice (one three-operand
+// and-or apiece), place all eight codes, and one packed subtraction of the magic recovers them.
+// The masks and exponents arrive in registers (0x000F000F, 0x00F000F0, 0x64006400, 0x54005400).
+__device__ __forceinline__ u32x4 dequant8_f16(unsigned w, f16x2 s2, f16x2 z2, unsigned m0, unsigned m1,
+                                              unsigned e0, unsigned e1) {
+  const unsigned w8 = w >> 8;
+  const f16x2 k0 = {(_Float16)1024.f, (_Float16)1024.f}, k1 = {(_Float16)64.f, (_Float16)64.f};
+  const f16x2 c0 = __builtin_bit_cast(f16x2, (w & m0) | e0) - k0;    // indices 0, 4
+  const f16x2 c1 = __builtin_bit_cast(f16x2, (w & m1) | e1) - k1;    // 1, 5
+  const f16x2 c2 = __builtin_bit_cast(f16x2, (w8 & m0) | e0) - k0;   // 2, 6
+  const f16x2 c3 = __builtin_bit_cast(f16x2, (w8 & m1) | e1) - k1;   // 3, 7
   u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const unsigned m = ((w >> (4 * i)) & kMask) | kMagic;
-    const f16x2 c = __builtin_bit_cast(f16x2, m) - (f16x2){(_Float16)1024.f, (_Float16)1024.f};
-    o[i] = __builtin_bit_cast(unsigned, __builtin_elementwise_fma(c, s2, z2));
-  }
+  o[0] = __builtin_bit_cast(unsigned, __builtin_elementwise_fma(c0, s2, z2));
+  o[1] = __builtin_bit_cast(unsigned, __builtin_elementwise_fma(c1, s2, z2));
+  o[2] = __builtin_bit_cast(unsigned, __builtin_elementwise_fma(c2, s2, z2));
+  o[3] = __builtin_bit_cast(unsigned, __builtin_elementwise_fma(c3, s2, z2));
   return o;
 }
 
@@ -310,25 +316,24 @@ constexpr int kProducers = 4;           // waves that only move data (direct-to-
 constexpr int kMaxChunkPerProducer = 5; // 1 KB DMA chunks per producer per matrix and tile
 constexpr float kRescaleSlack = 8.f;    // base-2 headroom before the running reference max moves
 
-// Threads of the decode workgroup for G consumer groups (int4: plus its dequantisation waves).
-constexpr int decode_threads(int G, int LT) { return 64 * (4 * G + kProducers + (LT == LT_I4 ? 4 : 0)); }
+// Threads of the decode workgroup for G consumer groups.
+constexpr int decode_threads(int G, int LT) { return 64 * (4 * G + kProducers); }
 
 // ---------------------------------------------------------------------------------------------
-// int4 latents: three roles of 4 waves each, one workgroup barrier per 16-token tile.
-//   DMA waves      copy a tile's stored bytes (16 rows of codes and of scale/zero words, for Zk
-//                  then Zv: four contiguous runs in HBM) by 1 KB direct-to-LDS chunks into raw
-//                  stage t % nr; per iteration they issue tile it + nr (its stage held tile it,
-//                  dequantised before this barrier) and wait for tile it + 2.
-//   dequant waves  turn raw tile it + 1 (landed before this barrier) into fp16 stage
-//                  (it + 1) % 2 with the bf16 tile geometry (consumers finished tile it - 1
-//                  there before this barrier). One item = one dword of codes (8 latent
-//                  indices) -> 16 bytes of fp16, so consecutive lanes write consecutive bytes.
-//   consumers      as for bf16, on fp16 stage it % 2.
+// int4 latents: 4 consumer waves and 4 loader waves, one workgroup barrier per pair of tiles.
+//   loaders    copy a tile's stored bytes (16 rows of codes and of scale/zero words, for Zk then
+//              Zv: four contiguous runs in HBM) by 1 KB direct-to-LDS chunks into raw stage
+//              t % nr, and turn the value rows of the next iteration's two tiles into fp16
+//              stages (t % 4) with the bf16 value-row geometry. In iteration it the raw stages
+//              of tiles below 2 it are free (their keys were read in iteration it - 1), so tiles
+//              2 it - 2 + nr and 2 it - 1 + nr are issued; tiles 2 it + 2 and 2 it + 3 (landed
+//              before the barrier) are dequantised; then the wave waits for tiles up to 2 it + 5.
+//   consumers  wave (slot, hb) takes tile 2 it + slot for head block hb: it dequantises the
+//              tile's key rows from the raw stage straight into matrix-core operands, and reads
+//              the value rows from the fp16 stage through the transpose read.
+// Each stored byte thus crosses LDS once as raw bytes; the key codes are read once per head
+// block and only the value rows are written back, as fp16.
 // ---------------------------------------------------------------------------------------------
-constexpr int kI4DequantWaves = 4;
-// dequantisation items (8 codes each) per dequant lane and tile at rank 512
-constexpr int kI4MaxItems = (kTileTokens * 2 * 64 + kI4DequantWaves * 64 - 1) / (kI4DequantWaves * 64);
-
 struct I4Raw {      // byte offsets of the four runs inside a raw stage, and the stage size
   int cbk, qbk, cbv, qbv, o_qk, o_cv, o_qv, rs;
   __device__ I4Raw(const DecodeArgs& a)
@@ -337,127 +342,161 @@ struct I4Raw {      // byte offsets of the four runs inside a raw stage, and the
         o_qv(o_cv + kTileTokens * a.row_bytes_v), rs(a.raw_stage) {}
 };
 
-template <int KS, int RB>
-__device__ __forceinline__ void i4_dma(const DecodeArgs& a, unsigned char* smem, int b, int t_begin, int t_end,
-                                       int ntiles, int pw) {
-  constexpr int STAGE = lds_stage(KS, RB, 2);
+// fp16 pairs (x, x) of the low and of the high half of a scale/zero word
+__device__ __forceinline__ f16x2 bcast_lo16(unsigned w) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(w, w, 0x01000100u));
+}
+__device__ __forceinline__ f16x2 bcast_hi16(unsigned w) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(w, w, 0x03020302u));
+}
+
+// 1 KB chunks a loader wave copies per tile: a full tile's four runs hold at most 10 chunks
+// (rank 512: 4 + 1 + 4 + 1), numbered across the runs and dealt round-robin to the 4 waves.
+constexpr int kI4ChunksPerWave = 3;
+
+template <int RB>
+__device__ __forceinline__ void i4_loader(const DecodeArgs& a, unsigned char* smem, int b, int t_begin, int t_end,
+                                          int ntiles, int pw) {
+  constexpr int SV = lds_stride_v(RB, 2);
+  constexpr int VSTAGE = i4_vstage(RB);
+  constexpr int NI = RB / 4;          // value dwords (8 codes each) per loader lane and tile
   const int lane = threadIdx.x & 63;
-  unsigned char* raw = smem + kI4DeqStages * STAGE;
+  unsigned char* raw = smem + kI4VStages * VSTAGE;
   const I4Raw R(a);
   const int NR = a.nr;
   const size_t row0 = (size_t)b * a.t_cap + t_begin;
-  const unsigned char* gck = a.zk + row0 * R.cbk;
-  const unsigned char* gqk = a.zkq + row0 * R.qbk;
-  const unsigned char* gcv = a.zv + row0 * R.cbv;
-  const unsigned char* gqv = a.zvq + row0 * R.qbv;
 
-  auto nch = [](int bytes) { return (bytes + 1023) >> 10; };
-  auto tile_chunks = [&](int rows) {
-    return nch(rows * R.cbk) + nch(rows * R.qbk) + nch(rows * R.cbv) + nch(rows * R.qbv);
+  // This wave's chunks of a tile (the numbering of a full tile; a final partial tile copies the
+  // chunks that start inside its shorter runs): run, start byte inside the run, LDS offset.
+  const unsigned char* c_src[kI4ChunksPerWave];
+  int c_rb[kI4ChunksPerWave], c_start[kI4ChunksPerWave], c_dst[kI4ChunksPerWave];
+  int nchw = 0;
+  {
+    const unsigned char* rsrc[4] = {a.zk + row0 * R.cbk, a.zkq + row0 * R.qbk, a.zv + row0 * R.cbv,
+                                    a.zvq + row0 * R.qbv};
+    const int rrb[4] = {R.cbk, R.qbk, R.cbv, R.qbv};
+    const int rdst[4] = {0, R.o_qk, R.o_cv, R.o_qv};
+    int gc = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = (kTileTokens * rrb[r] + 1023) >> 10;
+      for (int c = 0; c < n; ++c, ++gc) {
+        if ((gc & 3) == pw && nchw < kI4ChunksPerWave) {
+          c_src[nchw] = rsrc[r];
+          c_rb[nchw] = rrb[r];
+          c_start[nchw] = c * 1024;
+          c_dst[nchw] = rdst[r] + c * 1024;
+          ++nchw;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kI4ChunksPerWave; ++u)
+      if (u >= nchw) { c_src[u] = rsrc[0]; c_rb[u] = 0; c_start[u] = 0; c_dst[u] = 0; }
+  }
+  auto tile_loads = [&](int rows) {                  // chunks this wave copies for a tile
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < kI4ChunksPerWave; ++u) n += (u < nchw && c_start[u] < rows * c_rb[u]) ? 1 : 0;
+    return n;
   };
-  auto pcnt = [&](int n) { return n > pw ? (n - pw + kProducers - 1) / kProducers : 0; };
   const int rows_last = ntiles > 0 ? t_end - (t_begin + (ntiles - 1) * kTileTokens) : 0;
-  const int cnt_full = pcnt(tile_chunks(kTileTokens));
-  const int cnt_last = ntiles > 0 ? pcnt(tile_chunks(rows_last)) : 0;
+  const int cnt_full = tile_loads(kTileTokens);
+  const int cnt_last = ntiles > 0 ? tile_loads(rows_last) : 0;
   auto count = [&](int lo, int hi) {     // this wave's loads for tiles (lo, hi]
     if (hi <= lo) return 0;
     return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
   };
+  int issue_stage = 0;                   // raw stage of the next tile issued (tiles go in order)
   auto issue = [&](int t) {
-    unsigned char* st = raw + (t % NR) * R.rs;
+    unsigned char* st = raw + issue_stage * R.rs;
+    issue_stage = issue_stage + 1 == NR ? 0 : issue_stage + 1;
     const int t0 = t * kTileTokens;
     const int rows = min(kTileTokens, t_end - t_begin - t0);
-    int gc0 = 0;                         // first chunk of the run in the tile's chunk list
-    auto run = [&](const unsigned char* src, unsigned char* dst, int bytes) {
-      const int n = nch(bytes);
-      for (int c = ((pw - gc0) % kProducers + kProducers) % kProducers; c < n; c += kProducers) {
-        const int off = c * 1024 + lane * 16;
-        if (off < bytes) dma16(src + off, dst + c * 1024);
+#pragma unroll
+    for (int u = 0; u < kI4ChunksPerWave; ++u) {
+      const int lim = rows * c_rb[u];
+      if (u < nchw && c_start[u] < lim) {
+        const int off = c_start[u] + lane * 16;
+        if (off < lim) dma16(c_src[u] + (size_t)t0 * c_rb[u] + off, st + c_dst[u]);
       }
-      gc0 += n;
-    };
-    run(gck + (size_t)t0 * R.cbk, st, rows * R.cbk);
-    run(gqk + (size_t)t0 * R.qbk, st + R.o_qk, rows * R.qbk);
-    run(gcv + (size_t)t0 * R.cbv, st + R.o_cv, rows * R.cbv);
-    run(gqv + (size_t)t0 * R.qbv, st + R.o_qv, rows * R.qbv);
+    }
+  };
+
+  // Value item i (one dword of codes of one row) of a tile, i = lane + 256 u over the loader
+  // waves; its offsets are the same for every tile, so they are computed once. Every item of
+  // the tile's 16 rows is converted, also for a final partial tile (its stale rows are masked
+  // by the consumers); items past the row's groups read row 0 and write into the never-read
+  // 32-byte pad of row 0. So the conversion has no branch, and two tiles' reads are all issued
+  // before the first conversion.
+  const int dv = R.cbv >> 2;                         // code dwords per value row
+  const int nitems = kTileTokens * dv;
+  int i_src[NI], i_qp[NI], i_dst[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int i = pw * 64 + lane + u * kProducers * 64;
+    i_src[u] = R.o_cv;
+    i_qp[u] = R.o_qv;
+    i_dst[u] = SV - 16;
+    if (i < nitems) {
+      const int row = i / dv, word = i - row * dv;  // word = 4 * group + quarter
+      i_src[u] = R.o_cv + row * R.cbv + word * 4;
+      i_qp[u] = R.o_qv + row * R.qbv + (word >> 2) * 4;
+      i_dst[u] = row * SV + word * 16;
+    }
+  }
+  unsigned kM0 = 0x000F000Fu, kM1 = 0x00F000F0u, kE0 = 0x64006400u, kE1 = 0x54005400u;
+  asm volatile("" : "+v"(kM0), "+v"(kM1), "+v"(kE0), "+v"(kE1));
+  // Dequantise tiles t and t + 1 (raw stages rs0, rs1) into fp16 value stages t % 4, (t+1) % 4;
+  // tile t + 1 only if two (wave-uniform).
+  auto dequant2 = [&](int t, int rs0, int rs1, bool two) {
+    const unsigned char* s0 = raw + rs0 * R.rs;
+    const unsigned char* s1 = raw + rs1 * R.rs;
+    unsigned w0[NI], q0[NI], w1[NI], q1[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      w0[u] = *(const unsigned*)(s0 + i_src[u]);
+      q0[u] = *(const unsigned*)(s0 + i_qp[u]);
+    }
+    if (two) {
+#pragma unroll
+      for (int u = 0; u < NI; ++u) {
+        w1[u] = *(const unsigned*)(s1 + i_src[u]);
+        q1[u] = *(const unsigned*)(s1 + i_qp[u]);
+      }
+    }
+    unsigned char* d0 = smem + (t & 3) * VSTAGE;
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      *(u32x4*)(d0 + i_dst[u]) = dequant8_f16(w0[u], bcast_lo16(q0[u]), bcast_hi16(q0[u]), kM0, kM1, kE0, kE1);
+    if (two) {
+      unsigned char* d1 = smem + ((t + 1) & 3) * VSTAGE;
+#pragma unroll
+      for (int u = 0; u < NI; ++u)
+        *(u32x4*)(d1 + i_dst[u]) = dequant8_f16(w1[u], bcast_lo16(q1[u]), bcast_hi16(q1[u]), kM0, kM1, kE0, kE1);
+    }
   };
 
   const int pro = min(NR, ntiles);
   for (int t = 0; t < pro; ++t) issue(t);
-  wait_vmcnt(count(0, pro - 1));
-  barrier_lds();                                     // raw tile 0 visible to the dequant waves
-  wait_vmcnt(count(1, pro - 1));
-  for (int it = 0; it < ntiles; ++it) {
-    barrier_lds();                                   // raw tile it + 1 visible
-    if (it + NR < ntiles) issue(it + NR);
-    wait_vmcnt(count(it + 2, min(it + NR, ntiles - 1)));
-  }
-}
-
-template <int KS, int RB>
-__device__ __forceinline__ void i4_dequant(const DecodeArgs& a, unsigned char* smem, int t_begin, int t_end,
-                                           int ntiles, int dw) {
-  constexpr int SK = lds_stride_k(KS, 2);
-  constexpr int SV = lds_stride_v(RB, 2);
-  constexpr int ZV = kTileTokens * SK;
-  constexpr int STAGE = lds_stage(KS, RB, 2);
-  const int lane = threadIdx.x & 63;
-  unsigned char* raw = smem + kI4DeqStages * STAGE;
-  const I4Raw R(a);
-  const int NR = a.nr;
-  // Item i (one dword of codes of one row) of a tile, i = lane + 256 u of the dequant waves;
-  // its stage offsets are the same for every tile, so they are computed once. Every item of
-  // the tile's 16 rows is converted, also for a final partial tile (its stale rows are masked
-  // by the consumers), and lanes past the last item write into the never-read 16-byte pad of
-  // row 0, so the loop has no per-lane branch and the items' instruction chains interleave.
-  const int dk = R.cbk >> 2, dv = R.cbv >> 2;        // code dwords per row
-  const int nitems = kTileTokens * (dk + dv);
-  const int nu = (nitems + kI4DequantWaves * 64 - 1) / (kI4DequantWaves * 64);   // wave-uniform
-  const int pl = dw * 64 + lane;
-  int i_src[kI4MaxItems], i_qp[kI4MaxItems], i_dst[kI4MaxItems];
-#pragma unroll
-  for (int u = 0; u < kI4MaxItems; ++u) {
-    const int i = pl + u * kI4DequantWaves * 64;
-    i_src[u] = i_qp[u] = 0;
-    i_dst[u] = SK - 16;                              // pad bytes past the K operand's reach
-    if (i < nitems) {
-      const bool isk = i < kTileTokens * dk;
-      const int j = isk ? i : i - kTileTokens * dk;
-      const int h = isk ? dk : dv;
-      const int row = j / h, word = j - row * h;    // word = 4 * group + quarter
-      i_src[u] = (isk ? row * R.cbk : R.o_cv + row * R.cbv) + word * 4;
-      i_qp[u] = (isk ? R.o_qk + row * R.qbk : R.o_qv + row * R.qbv) + (word >> 2) * 4;
-      i_dst[u] = (isk ? row * SK : ZV + row * SV) + word * 16;
+  wait_vmcnt(count(1, pro - 1));                     // tiles 0 and 1 landed
+  barrier_lds();                                     // ... and visible to every loader
+  if (ntiles > 0) dequant2(0, 0, 1 % NR, ntiles > 1);
+  wait_vmcnt(count(3, pro - 1));                     // tiles 2 and 3 landed
+  const int niter = (ntiles + 1) / 2;
+  int dq_stage = 2 % NR;                             // raw stage of tile 2 it + 2
+  for (int it = 0; it < niter; ++it) {
+    barrier_lds();                                   // fp16 values of 2it, 2it+1 visible
+    // the copies first, as early as their stages are free (measured: converting first and
+    // copying after it is slower)
+    if (it > 0) {
+      if (2 * it - 2 + NR < ntiles) issue(2 * it - 2 + NR);
+      if (2 * it - 1 + NR < ntiles) issue(2 * it - 1 + NR);
     }
-  }
-  unsigned kMask = 0x000F000Fu, kMagic = 0x64006400u;
-  asm volatile("" : "+v"(kMask), "+v"(kMagic));
-  auto dequant = [&](int t) {
-    const unsigned char* st = raw + (t % NR) * R.rs;
-    unsigned char* dq = smem + (t % kI4DeqStages) * STAGE;
-    unsigned w[kI4MaxItems], qp[kI4MaxItems];
-#pragma unroll
-    for (int u = 0; u < kI4MaxItems; ++u) {          // all reads first, one wait
-      if (u < nu) {
-        w[u] = *(const unsigned*)(st + i_src[u]);
-        qp[u] = *(const unsigned*)(st + i_qp[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kI4MaxItems; ++u) {
-      if (u < nu) {
-        const f16x2 s2 = __builtin_bit_cast(f16x2, (qp[u] & 0xFFFFu) * 0x10001u);
-        const f16x2 z2 = __builtin_bit_cast(f16x2, (qp[u] >> 16) * 0x10001u);
-        *(u32x4*)(dq + i_dst[u]) = dequant8_f16(w[u], s2, z2, kMask, kMagic);
-      }
-    }
-  };
-
-  barrier_lds();                                     // raw tile 0 visible
-  if (ntiles > 0) dequant(0);
-  for (int it = 0; it < ntiles; ++it) {
-    barrier_lds();                                   // fp16 tile it visible; raw tile it + 1 landed
-    if (it + 1 < ntiles) dequant(it + 1);
+    const int dq1 = dq_stage + 1 == NR ? 0 : dq_stage + 1;
+    if (2 * it + 2 < ntiles) dequant2(2 * it + 2, dq_stage, dq1, 2 * it + 3 < ntiles);
+    dq_stage = dq1 + 1 == NR ? 0 : dq1 + 1;
+    wait_vmcnt(count(2 * it + 5, min(2 * it - 1 + NR, ntiles - 1)));
   }
 }
 
@@ -468,13 +507,15 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   constexpr int ES = LT == LT_F32 ? 4 : 2;             // bytes per latent element in the LDS tile
   constexpr int SK = lds_stride_k(KS, ES);             // LDS row strides (bytes)
   constexpr int SV = lds_stride_v(RB, ES);
-  constexpr int ZV = kTileTokens * SK;                 // value rows' offset inside a stage
-  constexpr int STAGE = lds_stage(KS, RB, ES);
-  constexpr int NST = I4 ? kI4DeqStages : lds_nst(KS, RB, ES);
+  // value rows' offset inside a stage, stage bytes, stages (int4: the fp16 value stages; the
+  // raw ring follows them)
+  constexpr int ZV = I4 ? 0 : kTileTokens * SK;
+  constexpr int STAGE = I4 ? i4_vstage(RB) : lds_stage(KS, RB, ES);
+  constexpr int NST = I4 ? kI4VStages : lds_nst(KS, RB, ES);
   constexpr int TPI = SP ? 2 * G : G;                  // tiles per iteration
   constexpr int NVB = SP ? 2 * RB : RB;                // value blocks per consumer wave
   static_assert(NST % TPI == 0 && NST / TPI >= 2, "LDS ring must hold two iterations of tiles");
-  static_assert(!I4 || (G == 1 && !SP), "int4 tiles are consumed by one group of halves");
+  static_assert(!I4 || (G == 1 && SP && KS % 4 == 0), "int4: one split group, key groups in fours");
   static_assert(I4 || ((kTileTokens * SK + 1023) / 1024 <= kProducers * kMaxChunkPerProducer &&
                        (kTileTokens * SV + 1023) / 1024 <= kProducers * kMaxChunkPerProducer), "DMA chunks");
 
@@ -501,13 +542,13 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
     constexpr int KB = KS * 32 * ES, VB = RB * 32 * ES;        // bytes of a row the operands read
     const int ck = I4 ? a.nks * 64 : a.copy_k;                  // bytes written per K / V row
     const int cv = I4 ? ((a.rv + 31) / 32) * 64 : a.copy_v;
-    const int npk = (KB - ck) >> 4, npv = (VB - cv) >> 4;       // 16-byte granules to clear
+    const int npk = I4 ? 0 : (KB - ck) >> 4, npv = (VB - cv) >> 4;   // 16-byte granules to clear
     const int per_stage = kTileTokens * (npk + npv);
     for (int i = tid; i < NST * per_stage; i += NTHR) {
       const int st = i / per_stage, j = i - st * per_stage;
       unsigned char* p;
       if (j < kTileTokens * npk) {
-        const int row = j / npk, gk = j - row * npk;
+        const int row = j / (npk > 0 ? npk : 1), gk = j - row * npk;
         p = ring + st * STAGE + row * SK + ck + gk * 16;
       } else {
         const int jj = j - kTileTokens * npk;
@@ -524,9 +565,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   for (int j = 0; j < NVB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (I4 && producer) {
-    static_assert(kI4DequantWaves == kProducers, "int4 role split");
-    if (wave < 4 * G + kProducers) i4_dma<KS, RB>(a, smem, b, t_begin, t_end, ntiles, wave - 4 * G);
-    else i4_dequant<KS, RB>(a, smem, t_begin, t_end, ntiles, wave - 4 * G - kProducers);
+    i4_loader<RB>(a, smem, b, t_begin, t_end, ntiles, wave - 4 * G);
   } else if (producer) {
     // ---------------- producer waves: keep the ring full ----------------
     const int pw = wave - 4 * G;
@@ -600,14 +639,17 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       // The folded query arrives in float32. Its largest magnitude per head is brought into
       // [2^14, 2^15) by a power of two so that the fp16 operand cannot overflow; the scores are
       // multiplied back by that power. The 4 lane groups holding a head share its scale.
-      const float* qrow = (const float*)a.qt + ((size_t)sq * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
+      // K step 4*kq + j of lane group lg holds quarter j (8 indices) of key group 4*kq + lg,
+      // the order in which the key operands are dequantised below; groups past the rank are 0.
+      const float* qrow = (const float*)a.qt + ((size_t)sq * kHeadsPad + hb * 16 + li) * a.rk_pad;
       float qf[KS][8];
       float mxq = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks < a.nks) {
-          const f32x4 x0 = *(const f32x4*)(qrow + ks * 32);
-          const f32x4 x1 = *(const f32x4*)(qrow + ks * 32 + 4);
+        const int g = 4 * (ks >> 2) + lg;
+        if (g < a.nks) {
+          const f32x4 x0 = *(const f32x4*)(qrow + g * 32 + (ks & 3) * 8);
+          const f32x4 x1 = *(const f32x4*)(qrow + g * 32 + (ks & 3) * 8 + 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) { qf[ks][e] = x0[e]; qf[ks][4 + e] = x1[e]; }
         } else {
@@ -639,27 +681,70 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         qop[ks] = (ks < a.nks) ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
     }
     LR_WAIT_VM(0);
-    if constexpr (I4) barrier_lds();                 // pairs with the producers' first barrier
+    if constexpr (I4) barrier_lds();                 // pairs with the loaders' first barrier
+    unsigned kM0 = 0x000F000Fu, kM1 = 0x00F000F0u, kE0 = 0x64006400u, kE1 = 0x54005400u;
+    if constexpr (I4) asm volatile("" : "+v"(kM0), "+v"(kM1), "+v"(kE0), "+v"(kE1));
     // AND-mask for the last K step: latent indices >= rk read as 0 (the copied granule may
-    // hold pad columns, and they may hold anything, including NaN patterns; a dequantised int4
-    // tile holds zero + 0 * scale there, which is infinite for an infinite zero).
+    // hold pad columns, and they may hold anything, including NaN patterns). int4 keys need
+    // none: a pad index of a stored group dequantises, like the group's own indices, to
+    // code * scale + zero with a 4-bit code, and its query entry is 0.
     u32x4 tailmask;
     {
       const int k0 = (a.nks - 1) * 32 + lg * 8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (I4)   // dword i holds indices i and i + 4 of the 8-block
-          tailmask[i] = (k0 + i < a.rk ? 0x0000FFFFu : 0u) | (k0 + i + 4 < a.rk ? 0xFFFF0000u : 0u);
-        else
-          tailmask[i] = (k0 + 2 * i < a.rk ? 0x0000FFFFu : 0u) | (k0 + 2 * i + 1 < a.rk ? 0xFFFF0000u : 0u);
-      }
+      for (int i = 0; i < 4; ++i)
+        tailmask[i] = (k0 + 2 * i < a.rk ? 0x0000FFFFu : 0u) | (k0 + 2 * i + 1 < a.rk ? 0xFFFF0000u : 0u);
     }
-    const bool ktail = I4 ? (a.rk & 31) != 0 : (a.rk & 7) != 0;
+    const bool ktail = !I4 && (a.rk & 7) != 0;
     // value block j of this wave covers latent indices 16*rb .. 16*rb+15 with rb = j (split) or
     // half + 2j (blocks past the rank read the zero-filled tail of the rows, never stored)
     const int krow_off = li * SK + lg * 8 * ES;
     const int vrow_off = (LT == LT_F32) ? ZV + 4 * lg * SV + li * ES + half * 16 * ES
                                         : ZV + (4 * lg + (li >> 2)) * SV + (li & 3) * 8 + half * 32;
+
+    // int4 keys straight from the raw stage: lane (li, lg) reads the 16 code bytes of group
+    // 4*kq + lg of token li and that group's scale/zero word, and dequantises the four 8-index
+    // quarters into the operands of K steps 4*kq .. 4*kq+3. Groups past the rank read as zero
+    // codes with a zero scale/zero word (their query entries are 0 as well).
+    const I4Raw R(a);
+    auto i4_scores = [&](int rstage) -> f32x4 {
+      const unsigned char* rst = smem + NST * STAGE + rstage * R.rs;
+      u32x4 cw[KS / 4];
+      unsigned qw[KS / 4];
+#pragma unroll
+      for (int kq = 0; kq < KS / 4; ++kq) {
+        const int g = 4 * kq + lg;
+        const int ge = g < a.nks ? g : 0;
+        cw[kq] = *(const u32x4*)(rst + li * R.cbk + ge * 16);
+        qw[kq] = *(const unsigned*)(rst + R.o_qk + li * R.qbk + ge * 4);
+        if (g >= a.nks) {
+          cw[kq] = u32x4{0u, 0u, 0u, 0u};
+          qw[kq] = 0u;
+        }
+      }
+      f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kq = 0; kq < KS / 4; ++kq) {
+        if (4 * kq < a.nks) {                          // wave-uniform
+          const f16x2 s2 = bcast_lo16(qw[kq]), z2 = bcast_hi16(qw[kq]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x4 op = dequant8_f16(cw[kq][j], s2, z2, kM0, kM1, kE0, kE1);
+            c2[j & 1] = mfma_k<LT>(__builtin_bit_cast(bf16x8, op), qop[4 * kq + j], c2[j & 1]);
+          }
+        }
+      }
+      return c2[0] + c2[1];
+    };
+    // int4: scores of the wave's tile of the next iteration (its raw tile landed before this
+    // iteration's barrier), and the raw stage that tile sits in
+    f32x4 s_cur = {0.f, 0.f, 0.f, 0.f};
+    int rs_next = 0;
+    if constexpr (I4) {
+      rs_next = slot % a.nr;
+      if (slot < ntiles) s_cur = i4_scores(rs_next);
+      rs_next = (rs_next + TPI) % a.nr;
+    }
 
     for (int it = 0; it < niter; ++it) {
       barrier_lds();
@@ -674,6 +759,9 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         // (one chain where the registers of two consumer groups with wide value blocks are tight)
         constexpr int NCH = (G == 2 && NVB > 8) ? 1 : 2;
         f32x4 sacc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if constexpr (I4) {
+          sacc2[0] = s_cur;                            // computed one iteration ahead
+        } else {
 #pragma unroll
         for (int ks0 = 0; ks0 < KS; ks0 += 4) {      // 4 K steps of reads in flight, then 4 products
           bf16x8 av[4];
@@ -690,6 +778,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
           for (int u = 0; u < 4; ++u)
             if (ks0 + u < KS) sacc2[u % NCH] = mfma_k<LT>(av[u], qop[ks0 + u], sacc2[u % NCH]);
         }
+        }
         const f32x4 sacc = NCH == 2 ? sacc2[0] + sacc2[1] : sacc2[0];
 
         // ---- value operands: read in chunks of VC blocks; the first chunk's reads are issued
@@ -703,6 +792,12 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         bf16x4 vop[VC];
 #pragma unroll
         for (int u = 0; u < VC; ++u) vop[u] = vread(u);
+        if constexpr (I4) {
+          // the next tile's scores interleave with this tile's softmax and values (a stage
+          // past the last tile holds stale bytes: its scores are never used)
+          s_cur = i4_scores(rs_next);
+          rs_next = rs_next + TPI >= a.nr ? rs_next + TPI - a.nr : rs_next + TPI;
+        }
 
         // ---- online softmax over the tile's 16 tokens (4 per lane, 4 lane groups)
         float v[4];

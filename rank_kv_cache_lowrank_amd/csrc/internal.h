@@ -40,8 +40,10 @@ constexpr int lds_stage(int KS, int RB, int es) {
 //   half:  the two waves of a head block share each tile and split the value blocks.
 // (split needs up to 256 registers per consumer wave: one group; the narrowest rows keep two
 // groups of halves instead, which fit three waves per SIMD.)
+//   int4 latents always split (their workgroup has 8 waves, so 256 registers per wave).
 constexpr bool decode_split(int latent, int KS, int RB) {
-  return latent == LR_BF16 && !(KS <= 8 && RB <= 8) && ((KS <= 12 && RB <= 12) || (KS == 16 && RB == 8));
+  return latent == LR_I4G32 ||
+         (latent == LR_BF16 && !(KS <= 8 && RB <= 8) && ((KS <= 12 && RB <= 12) || (KS == 16 && RB == 8)));
 }
 constexpr int decode_groups(int latent, int KS, int RB) {
   return latent == LR_I4G32 ? 1
@@ -57,9 +59,12 @@ constexpr int decode_tpi(int latent, int KS, int RB) {
 inline int prefill_nv(int nrb) { return nrb <= 16 ? 16 : (nrb <= 24 ? 24 : (nrb <= 32 ? 32 : 0)); }
 constexpr int kPrefillTokensPerWg = 4;   // chunk tokens per prefill workgroup (one per wave)
 // int4 latents: raw stages (16 rows of codes and scale/zero words, as stored) for the
-// direct-to-LDS loads, dequantised into two fp16 stages of the geometry above.
-constexpr int kI4DeqStages = 2;
+// direct-to-LDS loads; the value rows are dequantised into four fp16 stages of 16 value rows
+// (two iterations of two tiles), the key rows are read raw by the consumers.
+constexpr int kI4VStages = 4;
 constexpr int kI4MaxRawStages = 16;
+constexpr int kI4MinRawStages = 6;   // tiles of iterations it (keys) and it + 1 (values) + 2 in flight
+constexpr int i4_vstage(int RB) { return kTileTokens * lds_stride_v(RB, 2); }
 constexpr int i4_raw_stage(int gk, int gv) { return kTileTokens * 20 * (gk + gv); }
 constexpr int lds_nst(int KS, int RB, int es) {   // stages in the ring: even, at most 8
   return ((kLdsBytes - kLdsPad) / lds_stage(KS, RB, es) > 8 ? 8
