@@ -149,11 +149,11 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
     p->zv_off = 0;
     p->nst = kI4VStages;
     p->raw_stage = i4_raw_stage(gk, gv);
-    int nr = (kLdsBytes - kLdsPad - kI4VStages * p->stage_bytes) / p->raw_stage;
+    int nr = (kLdsBytes - kLdsPad - kI4VStages * p->stage_bytes - kI4XchBytes) / p->raw_stage;
     if (nr > kI4MaxRawStages) nr = kI4MaxRawStages;
     if (nr < kI4MinRawStages) return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
     p->nr = nr;
-    int lds = kI4VStages * p->stage_bytes + nr * p->raw_stage + kLdsPad;
+    int lds = kI4VStages * p->stage_bytes + nr * p->raw_stage + kI4XchBytes + kLdsPad;
     if (window_lds > lds) lds = window_lds;
     if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;
     p->lds_bytes = lds;

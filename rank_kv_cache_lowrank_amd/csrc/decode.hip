@@ -352,6 +352,8 @@ __device__ __forceinline__ f16x2 bcast_hi16(unsigned w) {
 
 // 1 KB chunks a loader wave copies per tile: a full tile's four runs hold at most 10 chunks
 // (rank 512: 4 + 1 + 4 + 1), numbered across the runs and dealt round-robin to the 4 waves.
+// (All four waves copy: measured, one wave copying for all is slower, since a wave's copies
+// stall in issue once the memory pipeline holds enough of them.)
 constexpr int kI4ChunksPerWave = 3;
 
 template <int RB>
@@ -477,11 +479,15 @@ __device__ __forceinline__ void i4_loader(const DecodeArgs& a, unsigned char* sm
     }
   };
 
-  const int pro = min(NR, ntiles);
-  for (int t = 0; t < pro; ++t) issue(t);
-  wait_vmcnt(count(1, pro - 1));                     // tiles 0 and 1 landed
+  // The consumers' query loads go first (the copies would queue ahead of them in the memory
+  // pipeline); then tiles 0-3 are copied, 0 and 1 converted, and the rest of the ring filled.
+  barrier_lds();                                     // the consumers' query loads are issued
+  const int pro = min(NR, ntiles), pro0 = min(4, pro);
+  for (int t = 0; t < pro0; ++t) issue(t);
+  wait_vmcnt(count(1, pro0 - 1));                    // tiles 0 and 1 landed
   barrier_lds();                                     // ... and visible to every loader
   if (ntiles > 0) dequant2(0, 0, 1 % NR, ntiles > 1);
+  for (int t = pro0; t < pro; ++t) issue(t);
   wait_vmcnt(count(3, pro - 1));                     // tiles 2 and 3 landed
   const int niter = (ntiles + 1) / 2;
   int dq_stage = 2 % NR;                             // raw stage of tile 2 it + 2
@@ -633,46 +639,67 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
     const int slot = SP ? (wave >> 1) : (wave >> 2);   // tile of the iteration this wave takes
     const int hb = wave & 1;
     const int half = SP ? 0 : (wave >> 1) & 1;
+    // int4: the two waves of a tile split the keys' K steps, each computing partial scores of
+    // both head blocks; qop[h2 * KS/2 + 2*kq + jj] is head block h2's operand of K step
+    // (kq, 2*hb + jj).
+    constexpr int KH = KS / 2;
     bf16x8 qop[KS];
-    float qx = 1.f;          // int4: the power of two the fp16 folded query was divided by
+    float qxh[2] = {1.f, 1.f};  // int4: per head block, the power of two its fp16 operands were divided by
     if constexpr (I4) {
-      // The folded query arrives in float32. Its largest magnitude per head is brought into
-      // [2^14, 2^15) by a power of two so that the fp16 operand cannot overflow; the scores are
-      // multiplied back by that power. The 4 lane groups holding a head share its scale.
-      // K step 4*kq + j of lane group lg holds quarter j (8 indices) of key group 4*kq + lg,
-      // the order in which the key operands are dequantised below; groups past the rank are 0.
-      const float* qrow = (const float*)a.qt + ((size_t)sq * kHeadsPad + hb * 16 + li) * a.rk_pad;
-      float qf[KS][8];
-      float mxq = 0.f;
+      // The folded query arrives in float32. For each head block, the largest magnitude of the
+      // wave's half of a head's row is brought into [2^14, 2^15) by a power of two so that the
+      // fp16 operands cannot overflow; the partial scores are multiplied back by that power
+      // before the two waves add them. The 4 lane groups holding a head share its scale.
+      // K step (kq, j) of lane group lg holds quarter j (8 indices) of key group 4*kq + lg, the
+      // order in which the key operands are dequantised; groups past the rank are 0.
+      const float* qb = (const float*)a.qt + (size_t)sq * kHeadsPad * a.rk_pad;
+      float qf[2][KH][8];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int g = 4 * (ks >> 2) + lg;
-        if (g < a.nks) {
-          const f32x4 x0 = *(const f32x4*)(qrow + g * 32 + (ks & 3) * 8);
-          const f32x4 x1 = *(const f32x4*)(qrow + g * 32 + (ks & 3) * 8 + 4);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float* qrow = qb + (size_t)(h2 * 16 + li) * a.rk_pad;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { qf[ks][e] = x0[e]; qf[ks][4 + e] = x1[e]; }
-        } else {
+        for (int kq = 0; kq < KS / 4; ++kq) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[ks][e] = 0.f;
+          for (int jj = 0; jj < 2; ++jj) {
+            const int g = 4 * kq + lg;
+            if (g < a.nks) {
+              const float* p = qrow + g * 32 + (2 * hb + jj) * 8;
+              const f32x4 x0 = *(const f32x4*)p;
+              const f32x4 x1 = *(const f32x4*)(p + 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) { qf[h2][2 * kq + jj][e] = x0[e]; qf[h2][2 * kq + jj][4 + e] = x1[e]; }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) qf[h2][2 * kq + jj][e] = 0.f;
+            }
+          }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mxq = fmaxf(mxq, fabsf(qf[ks][e]));
       }
-      mxq = wave_max_lg(mxq);
-      int ex = 0;
-      if (mxq > 0.f && mxq <= 3.4e38f) {
-        ex = ilogbf(mxq) - 14;
-        ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
-      }
-      const float fac = ldexpf(1.f, -ex);
-      qx = ldexpf(1.f, ex);
+      // the loaders start their copies after this barrier: the query loads, issued above, are
+      // ahead of them in the memory pipeline
+      barrier_lds();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        f16x8 h;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float mxq = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (_Float16)(qf[ks][e] * fac);
-        qop[ks] = __builtin_bit_cast(bf16x8, h);
+        for (int k = 0; k < KH; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mxq = fmaxf(mxq, fabsf(qf[h2][k][e]));
+        mxq = wave_max_lg(mxq);
+        int ex = 0;
+        if (mxq > 0.f && mxq <= 3.4e38f) {
+          ex = ilogbf(mxq) - 14;
+          ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+        }
+        const float fac = ldexpf(1.f, -ex);
+        qxh[h2] = ldexpf(1.f, ex);
+#pragma unroll
+        for (int k = 0; k < KH; ++k) {
+          f16x8 h;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = (_Float16)(qf[h2][k][e] * fac);
+          qop[h2 * KH + k] = __builtin_bit_cast(bf16x8, h);
+        }
       }
     } else {
       const __bf16* qrow = a.qt + ((size_t)sq * kHeadsPad + hb * 16 + li) * a.rk_pad + lg * 8;
@@ -681,7 +708,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         qop[ks] = (ks < a.nks) ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
     }
     LR_WAIT_VM(0);
-    if constexpr (I4) barrier_lds();                 // pairs with the loaders' first barrier
+    if constexpr (I4) barrier_lds();                 // pairs with the loaders' second barrier
     unsigned kM0 = 0x000F000Fu, kM1 = 0x00F000F0u, kE0 = 0x64006400u, kE1 = 0x54005400u;
     if constexpr (I4) asm volatile("" : "+v"(kM0), "+v"(kM1), "+v"(kE0), "+v"(kE1));
     // AND-mask for the last K step: latent indices >= rk read as 0 (the copied granule may
@@ -702,48 +729,62 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
     const int vrow_off = (LT == LT_F32) ? ZV + 4 * lg * SV + li * ES + half * 16 * ES
                                         : ZV + (4 * lg + (li >> 2)) * SV + (li & 3) * 8 + half * 32;
 
-    // int4 keys straight from the raw stage: lane (li, lg) reads the 16 code bytes of group
-    // 4*kq + lg of token li and that group's scale/zero word, and dequantises the four 8-index
-    // quarters into the operands of K steps 4*kq .. 4*kq+3. Groups past the rank read as zero
-    // codes with a zero scale/zero word (their query entries are 0 as well).
+    // int4 keys straight from the raw stage: lane (li, lg) reads quarters 2*hb and 2*hb + 1 of
+    // key group 4*kq + lg of token li (8 code bytes) and the group's scale/zero word, and
+    // dequantises them into the operands of K steps (kq, 2*hb) and (kq, 2*hb + 1), each shared
+    // by the products of both head blocks. Groups past the rank read as zero codes with a zero
+    // scale/zero word (their query entries are 0 as well).
     const I4Raw R(a);
-    auto i4_scores = [&](int rstage) -> f32x4 {
+    auto i4_scores = [&](int rstage, f32x4& c0, f32x4& c1) {
       const unsigned char* rst = smem + NST * STAGE + rstage * R.rs;
-      u32x4 cw[KS / 4];
+      u32x2 cw[KS / 4];
       unsigned qw[KS / 4];
 #pragma unroll
       for (int kq = 0; kq < KS / 4; ++kq) {
         const int g = 4 * kq + lg;
         const int ge = g < a.nks ? g : 0;
-        cw[kq] = *(const u32x4*)(rst + li * R.cbk + ge * 16);
+        cw[kq] = *(const u32x2*)(rst + li * R.cbk + ge * 16 + hb * 8);
         qw[kq] = *(const unsigned*)(rst + R.o_qk + li * R.qbk + ge * 4);
         if (g >= a.nks) {
-          cw[kq] = u32x4{0u, 0u, 0u, 0u};
+          cw[kq] = u32x2{0u, 0u};
           qw[kq] = 0u;
         }
       }
-      f32x4 c2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      c0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      c1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kq = 0; kq < KS / 4; ++kq) {
         if (4 * kq < a.nks) {                          // wave-uniform
           const f16x2 s2 = bcast_lo16(qw[kq]), z2 = bcast_hi16(qw[kq]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4 op = dequant8_f16(cw[kq][j], s2, z2, kM0, kM1, kE0, kE1);
-            c2[j & 1] = mfma_k<LT>(__builtin_bit_cast(bf16x8, op), qop[4 * kq + j], c2[j & 1]);
+          for (int jj = 0; jj < 2; ++jj) {
+            const bf16x8 op = __builtin_bit_cast(bf16x8, dequant8_f16(cw[kq][jj], s2, z2, kM0, kM1, kE0, kE1));
+            c0 = mfma_k<LT>(op, qop[2 * kq + jj], c0);
+            c1 = mfma_k<LT>(op, qop[KH + 2 * kq + jj], c1);
           }
         }
       }
-      return c2[0] + c2[1];
+      c0 *= qxh[0];
+      c1 *= qxh[1];
     };
-    // int4: scores of the wave's tile of the next iteration (its raw tile landed before this
-    // iteration's barrier), and the raw stage that tile sits in
-    f32x4 s_cur = {0.f, 0.f, 0.f, 0.f};
+    // int4: this wave's partial scores of its tile of the next iteration (its raw tile landed
+    // before this iteration's barrier) go through LDS to the partner wave: the half for the
+    // partner's head block is written to xch[parity][slot][other hb], and after the next barrier
+    // each wave adds the partner's half to its own. Parity = the iteration that wrote it.
+    f32x4 s_own = {0.f, 0.f, 0.f, 0.f};
     int rs_next = 0;
+    f32x4* xch = (f32x4*)(smem + NST * STAGE + a.nr * R.rs);
+    auto xslot = [&](int par, int h) { return xch + ((par * 2 + slot) * 2 + h) * 64 + lane; };
+    auto next_scores = [&](int par) {
+      f32x4 c0, c1;
+      i4_scores(rs_next, c0, c1);
+      s_own = hb ? c1 : c0;
+      *xslot(par, 1 - hb) = hb ? c0 : c1;
+      rs_next = rs_next + TPI >= a.nr ? rs_next + TPI - a.nr : rs_next + TPI;
+    };
     if constexpr (I4) {
       rs_next = slot % a.nr;
-      if (slot < ntiles) s_cur = i4_scores(rs_next);
-      rs_next = (rs_next + TPI) % a.nr;
+      if (slot < ntiles) next_scores(1);
     }
 
     for (int it = 0; it < niter; ++it) {
@@ -760,7 +801,7 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         constexpr int NCH = (G == 2 && NVB > 8) ? 1 : 2;
         f32x4 sacc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if constexpr (I4) {
-          sacc2[0] = s_cur;                            // computed one iteration ahead
+          sacc2[0] = s_own + *xslot((it + 1) & 1, hb);  // computed one iteration ahead
         } else {
 #pragma unroll
         for (int ks0 = 0; ks0 < KS; ks0 += 4) {      // 4 K steps of reads in flight, then 4 products
@@ -792,18 +833,15 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
         bf16x4 vop[VC];
 #pragma unroll
         for (int u = 0; u < VC; ++u) vop[u] = vread(u);
-        if constexpr (I4) {
-          // the next tile's scores interleave with this tile's softmax and values (a stage
-          // past the last tile holds stale bytes: its scores are never used)
-          s_cur = i4_scores(rs_next);
-          rs_next = rs_next + TPI >= a.nr ? rs_next + TPI - a.nr : rs_next + TPI;
-        }
+        // the next tile's scores interleave with this tile's softmax and values (a stage past
+        // the last tile holds stale bytes: its scores are never used)
+        if constexpr (I4) next_scores(it & 1);
 
         // ---- online softmax over the tile's 16 tokens (4 per lane, 4 lane groups)
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[i] = I4 ? sacc[i] * qx : sacc[i];
+          v[i] = sacc[i];
           v[i] = (v[i] != v[i]) ? INFINITY : v[i];   // NaN survives the max, poisons only this head
         }
         // rows past the range's end: score -inf, value operand 0 (the stage may hold stale rows)

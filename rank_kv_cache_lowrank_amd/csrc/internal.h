@@ -65,6 +65,8 @@ constexpr int kI4VStages = 4;
 constexpr int kI4MaxRawStages = 16;
 constexpr int kI4MinRawStages = 6;   // tiles of iterations it (keys) and it + 1 (values) + 2 in flight
 constexpr int i4_vstage(int RB) { return kTileTokens * lds_stride_v(RB, 2); }
+// int4: the consumers' partial-score exchange (2 iterations x 2 tiles x 2 head blocks x 1 KB)
+constexpr int kI4XchBytes = 8 * 1024;
 constexpr int i4_raw_stage(int gk, int gv) { return kTileTokens * 20 * (gk + gv); }
 constexpr int lds_nst(int KS, int RB, int es) {   // stages in the ring: even, at most 8
   return ((kLdsBytes - kLdsPad) / lds_stage(KS, RB, es) > 8 ? 8
