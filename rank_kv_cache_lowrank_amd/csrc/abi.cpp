@@ -132,6 +132,15 @@ int plan_attention(const lr_model_desc* m, int layer, int batch, int n_q, bool p
   return LR_OK;
 }
 
+// End-of-range merge of the consumer waves' partials: (m, l, value blocks) per extra wave.
+static int merge_lds(int latent, int KS, int RB) {
+  const int G = decode_groups(latent, KS, RB);
+  const bool split = decode_split(latent, KS, RB);
+  const int extra = split ? 4 * G - 2 : 4 * (G - 1);
+  const int nvb = split ? 2 * RB : RB;
+  return extra * (512 + nvb * 1024);
+}
+
 // LDS ring for the cache's row strides (the geometry itself is fixed by the kernel's bounds).
 static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   p->row_bytes_k = row_bytes(p->latent, p->rk, ld_k);
@@ -154,6 +163,8 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
     if (nr < kI4MinRawStages) return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
     p->nr = nr;
     int lds = kI4VStages * p->stage_bytes + nr * p->raw_stage + kI4XchBytes + kLdsPad;
+    const int merge = merge_lds(p->latent, KS, RB);
+    if (merge > lds) lds = merge;
     if (window_lds > lds) lds = window_lds;
     if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;
     p->lds_bytes = lds;
@@ -179,16 +190,11 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   p->stage_bytes = lds_stage(KS, RB, es);
   p->zv_off = kTileTokens * sk;
   p->nst = lds_nst(KS, RB, es);
-  const int G = decode_groups(p->latent, KS, RB);
   const int tpi = decode_tpi(p->latent, KS, RB);
-  const bool split = decode_split(p->latent, KS, RB);
   if (p->nst < 2 * tpi || p->nst % tpi != 0)
     return *msg = "latent rows too wide for the LDS ring", LR_EUNSUPPORTED;
   int lds = p->nst * p->stage_bytes + kLdsPad;
-  // end-of-range merge of the consumer waves' partials: (m, l, value blocks) per extra wave
-  const int extra = split ? 4 * G - 2 : 4 * (G - 1);
-  const int nvb = split ? 2 * RB : RB;
-  const int merge = extra * (512 + nvb * 1024);
+  const int merge = merge_lds(p->latent, KS, RB);
   if (merge > lds) lds = merge;
   if (window_lds > lds) lds = window_lds;
   if (lds > kLdsBytes) return *msg = "decode staging exceeds LDS", LR_EUNSUPPORTED;
