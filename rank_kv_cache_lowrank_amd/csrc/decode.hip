@@ -308,11 +308,12 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
 //   S^T[16 tokens, 16 heads] = Zk qt^T            (16x16x32, K = rank)
 //   online softmax of its 4 scores per lane       (base 2; only cross-lane max)
 //   A^T[16 rv, 16 heads] += Zv^T P^T               (16x16x16, K = the 16 tokens)
-// so no data crosses waves inside a tile. At the end the waves holding the same role's partial
+// so no data crosses waves inside a tile (int4 latents excepted: there the two waves of a tile
+// exchange partial scores, see below). At the end the waves holding the same role's partial
 // (m, l, A) for different tiles are merged through LDS and written once.
 // KS: compile-time bound on K steps of 32; RB: bound on value blocks of a half.
 // ---------------------------------------------------------------------------------------------
-constexpr int kProducers = 4;           // waves that only move data (direct-to-LDS loads)
+constexpr int kProducers = 4;           // waves that move data (direct-to-LDS loads; int4: and convert)
 constexpr int kMaxChunkPerProducer = 5; // 1 KB DMA chunks per producer per matrix and tile
 constexpr float kRescaleSlack = 8.f;    // base-2 headroom before the running reference max moves
 
@@ -328,11 +329,14 @@ constexpr int decode_threads(int G, int LT) { return 64 * (4 * G + kProducers); 
 //              of tiles below 2 it are free (their keys were read in iteration it - 1), so tiles
 //              2 it - 2 + nr and 2 it - 1 + nr are issued; tiles 2 it + 2 and 2 it + 3 (landed
 //              before the barrier) are dequantised; then the wave waits for tiles up to 2 it + 5.
-//   consumers  wave (slot, hb) takes tile 2 it + slot for head block hb: it dequantises the
-//              tile's key rows from the raw stage straight into matrix-core operands, and reads
-//              the value rows from the fp16 stage through the transpose read.
-// Each stored byte thus crosses LDS once as raw bytes; the key codes are read once per head
-// block and only the value rows are written back, as fp16.
+//   consumers  wave (slot, hb) takes tile 2 it + slot for head block hb. The tile's two waves
+//              split its key side: each dequantises half of every key group's codes from the
+//              raw stage straight into matrix-core operands, computes the partial scores of
+//              both head blocks (one tile ahead), and passes the other head block's half to its
+//              partner through LDS. Values come from the fp16 stage through the transpose read.
+// Each stored byte thus crosses LDS once as raw bytes, each key code is read and dequantised
+// once, and only the value rows are written back, as fp16. Before any copy the consumers issue
+// their query loads (a barrier orders the two), so that those do not queue behind the copies.
 // ---------------------------------------------------------------------------------------------
 struct I4Raw {      // byte offsets of the four runs inside a raw stage, and the stage size
   int cbk, qbk, cbv, qbv, o_qk, o_cv, o_qv, rs;
