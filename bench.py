@@ -118,17 +118,25 @@ def cpu_baseline(cfg, li, budget_s: float = 20.0):
             def __getitem__(self, i):
                 return self.rows
 
+        win = {}
+        if cfg.window:
+            win = dict(kwin=li.kwin.float().numpy(), vwin=li.vwin.float().numpy(), win_len=li.win_len,
+                       window=cfg.window)
         t0 = time.perf_counter()
         OA.decode_latent(q, One(zk), One(zv), bk, bv, li.lat_len, li.rank_k, li.rank_v, cfg.n_kv_heads,
-                         cfg.sm_scale, batches=[b])
+                         cfg.sm_scale, batches=[b], **win)
         t_total += time.perf_counter() - t0
         done += 1
         nbytes += int(li.lat_len[b]) * (latent_bytes_per_token(cfg.latent, li.rank_k)
                                         + latent_bytes_per_token(cfg.latent, li.rank_v))
+        if cfg.window:
+            nbytes += int(li.win_len[b]) * 2 * cfg.kv_width * 2
         if t_total >= budget_s:
             break
+    lens = "x".join(str(int(x)) for x in li.lat_len[:done]) if cfg.len_range else str(int(li.lat_len[0]))
     return dict(value=nbytes / t_total / 1e12, unit="TB/s", cores=int(threads), kind="oracle",
-                sample=f"{done} of {cfg.batch} sequences x {int(li.lat_len[0])} tokens, fp64 latent-domain "
+                sample=f"{done} of {cfg.batch} sequences x {lens} tokens"
+                       f"{' (+ window)' if cfg.window else ''} of layer {li.layer}, fp64 latent-domain "
                        f"oracle, {t_total:.2f} s; latent bytes per second in the benchmark's units",
                 us_per_layer_step=t_total / done * cfg.batch * 1e6)
 
@@ -172,6 +180,134 @@ def copy_probe(torch, dev):
     torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     log(f"copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
+
+
+def decode28_bench(args):
+    """The full 28-layer decode step of the global-rank-allocation workload: batch 16, total
+    lengths per sequence drawn from U{2048..8192} with the last 128 tokens kept exact in the
+    window ring, per-layer ranks rK, rV drawn independently from {128, 136, ..., 512}, bf16
+    latents. A step = for each of the 28 layers, lowrank_kv_append (one new token per sequence:
+    it enters the window and the oldest window token is projected and stored as a latent row)
+    then lowrank_attn_decode. The lengths start W+K tokens short, so the last timed step attends
+    over exactly the drawn lengths. The caches of all layers (~5 GB) far exceed the 256 MB
+    Infinity Cache, so every step streams from HBM."""
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+    import synth
+    from synth.device import device_layer
+
+    dev = "cuda"
+    cfg = synth.CONFIGS[4]
+    K, W = args.steps, args.warmup
+    NL = cfg.n_layers
+    n_new = 1
+    ranks = [synth.layer_ranks(cfg, l) for l in range(NL)]
+    model = lr.Model(NL, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, [r[0] for r in ranks],
+                     [r[1] for r in ranks], cfg.sm_scale, cfg.window, cfg.latent)
+    ll, wl = synth.split_lengths(cfg)
+    start_len = (ll - (W + K) * n_new).astype(np.int32)
+    assert np.all(start_len >= 0)
+    max_len = int(ll.max())
+    caches, qs, li0 = [], [], None
+    t0 = time.time()
+    for l in range(NL):
+        li = synth.make_layer(cfg, l, t_cap=max_len)
+        _, cache = device_layer(li, dev, with_proj=True)
+        cache.tensors["lat_len"].copy_(torch.from_numpy(start_len).to(dev))
+        caches.append(cache)
+        qs.append(li.q.to(dev))
+        if l == 0:
+            li0 = li
+        log(f"layer {l}: ranks {li.rank_k}/{li.rank_v} staged ({time.time() - t0:.1f} s)")
+    gen = np.random.default_rng(12345)
+    k_new = torch.from_numpy(gen.standard_normal((cfg.batch, n_new, cfg.kv_width), dtype=np.float32)).to(
+        torch.bfloat16).to(dev)
+    v_new = torch.from_numpy(gen.standard_normal((cfg.batch, n_new, cfg.kv_width), dtype=np.float32)).to(
+        torch.bfloat16).to(dev)
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
+    ws_bytes = max(lr.lowrank_attn_decode_workspace_size(model, l, cfg.batch, max_len, args.nsplit)
+                   for l in range(NL))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ev = HipEvents()
+    evs = [[(ev.create(), ev.create()) for _ in range(NL)] for _ in range(K)]
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for i in range(W + K):
+        if i == W:
+            torch.cuda.synchronize()
+            start.record()
+        timed = i >= W
+        for l in range(NL):
+            lr.lowrank_kv_append(model, l, caches[l], k_new, v_new)
+            lr.lowrank_attn_decode(model, l, caches[l], qs[l], out, max_len, ws, nsplit=args.nsplit,
+                                   events=evs[i - W][l] if timed else None)
+        if i % 5 == 0:
+            log(f"step {i} enqueued")
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / K
+    kern_ms = np.array([[ev.elapsed_ms(a, b) for a, b in row] for row in evs])   # [K, NL]
+    for row in evs:
+        for a, b in row:
+            ev.destroy(a)
+            ev.destroy(b)
+    assert torch.isfinite(out).all(), "non-finite output"
+    for l in range(NL):
+        got = caches[l].tensors["lat_len"].cpu().numpy()
+        assert np.array_equal(got, ll), "lengths did not advance to the drawn lengths"
+
+    # bytes of each timed step: lat_len after that step's append = start + (i + 1)
+    step_tot, kern_bytes = [], np.zeros((K, NL))
+    for k in range(K):
+        L = start_len + (W + k + 1) * n_new
+        tot = 0
+        for l in range(NL):
+            by = step_bytes(cfg, ranks[l][0], ranks[l][1], L, wl, n_new)
+            tot += by["total"]
+            kern_bytes[k, l] = by["latents"]        # the window slots are the exact-keys kernel's
+        step_tot.append(tot)
+    step_total = float(np.mean(step_tot))
+    value = step_total / (ms_per_step * 1e-3) / 1e12
+    kern_avg_ms = float(kern_ms.mean())
+    bytes_per_launch = float(kern_bytes.mean())
+    achieved = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
+    per_layer_us = (kern_ms.mean(axis=0) * 1e3).round(2).tolist()
+    log(f"ms/step {ms_per_step:.4f} ({NL} layers)  decode kernel avg {kern_avg_ms * 1e3:.2f} us  "
+        f"step {value:.3f} TB/s  kernel {achieved / 1e3:.3f} TB/s")
+
+    rec = {
+        "metric": "µs per layer decode step & achieved HBM TB/s (B=16, T=4K–32K)",
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_layer_step": round(ms_per_step * 1e3 / NL, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.latent,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "layers": NL,
+                   "total_len_range": list(cfg.len_range), "window": cfg.window,
+                   "rank_range": [int(min(cfg.rank_choices)), int(max(cfg.rank_choices))],
+                   "latent": cfg.latent, "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "new_tokens_per_step": n_new, "parallelism": "single GPU"},
+        "step_bytes": int(step_total),
+        "decode_kernel_us_per_layer": per_layer_us,
+        "roofline": {"bound": "hbm", "kernel": "lr_decode", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s",
+                     "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4), "traffic": None,
+                     "kernel_us": round(kern_avg_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch)},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        li0.lat_len = ll
+        rec["cpu_baseline"] = cpu_baseline(cfg, li0)
+    print(json.dumps(rec), flush=True)
 
 
 def rebase_bench(args):
@@ -488,8 +624,11 @@ def main():
         return
     dev = "cuda"
     cfg = synth.CONFIGS[args.config]
+    if cfg.n_layers == 28 and cfg.window:
+        decode28_bench(args)
+        return
     if cfg.n_layers != 1 or cfg.window:
-        raise SystemExit("bench.py times single-layer configurations without a window (0-3)")
+        raise SystemExit("bench.py times the single-layer configurations 0-3 and the 28-layer step (4)")
     K, W = args.steps, args.warmup
     T = cfg.seq_len
     n_new = 1

@@ -1340,7 +1340,11 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.D = p.D;
   a.window = p.window;
   a.wscale = scale;
-  a.n_win_blocks = p.exact ? p.B : 0;
+  // Exact keys (window slots; in a prefill also the chunk's own rows): for bf16 queries the
+  // matrix-core exact-keys kernel runs first; for float32 queries B extra workgroups of the
+  // decode kernel (window_block) take them.
+  const bool exact_mfma = p.exact && p.latent != LR_F32;
+  a.n_win_blocks = (p.exact && !exact_mfma) ? p.B : 0;
   a.qpb = p.qpb;
   a.kchunk = (const __bf16*)k_chunk;
   a.vchunk = (const __bf16*)v_chunk;
@@ -1361,6 +1365,10 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
     if (e != hipSuccess) return e;
     e = launch_prefill_latent(p, c, qt, a.part_ml, a.part_acc, st, ev_begin, ev_end);
   } else {
+    if (exact_mfma) {
+      e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
+      if (e != hipSuccess) return e;
+    }
     const int grid = a.n_win_blocks + p.B * p.nsplit;
     if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2, false>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
     else if (p.latent == LR_I4G32) e = dispatch_decode<LT_I4>(p, a, grid, st, ev_begin, ev_end);

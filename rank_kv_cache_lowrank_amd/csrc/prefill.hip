@@ -430,7 +430,7 @@ struct ExactArgs {
   const __bf16* q;           // [B * C][Hq][d]
   const __bf16* kwin;        // [B][W][D] ring (slot of window entry e: (lat_len + e) % W)
   const __bf16* vwin;
-  const __bf16* kchunk;      // [B][C][D]
+  const __bf16* kchunk;      // [B][C][D], or NULL: no chunk rows among the keys (decode)
   const __bf16* vchunk;
   const int32_t* lat_len;
   const int32_t* win_len;
@@ -458,11 +458,14 @@ __global__ __launch_bounds__(256) void lr_prefill_exact(ExactArgs a) {
   L = L < 0 ? 0 : L;
   int wl = a.W > 0 ? a.win_len[b] : 0;
   wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
-  const int nkeys = wl + a.C;
+  // chunk rows as keys (causal): the prefill's own rows; none for a decode step, whose new token
+  // is already a window slot
+  const bool chunk_keys = a.kchunk != nullptr;
+  const int nkeys = wl + (chunk_keys ? a.C : 0);
   // keys this wave's rows can see: up to the last valid row's token
   const int c_hi = min(row0 + 15, nrows - 1) / grp;
-  const int wave_keys = row0 < nrows ? wl + c_hi + 1 : 0;
-  const int my_keys = rvalid ? wl + c + 1 : 0;
+  const int wave_keys = row0 < nrows ? wl + (chunk_keys ? c_hi + 1 : 0) : 0;
+  const int my_keys = rvalid ? wl + (chunk_keys ? c + 1 : 0) : 0;
 
   // q of this lane's row as the B operand: d indices 32 ks + 8 lg .. +7
   bf16x8 qop[4];
