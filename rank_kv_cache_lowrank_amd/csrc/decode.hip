@@ -1366,7 +1366,8 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
     e = launch_prefill_latent(p, c, qt, a.part_ml, a.part_acc, st, ev_begin, ev_end);
   } else {
     if (exact_mfma) {
-      e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
+      if (p.qpb == 1 && p.Hq / p.Hkv <= 16) e = launch_exact_decode(p, c, q, a.win_part, st);
+      else e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
       if (e != hipSuccess) return e;
     }
     const int grid = a.n_win_blocks + p.B * p.nsplit;

@@ -118,6 +118,9 @@ hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, c
 
 // The exact keys of a prefill with the dedicated kernels (p.pf): window slots and the chunk's
 // rows, causally; partials in the decode kernel's exact-keys layout.
+// Exact keys of a decode step (one query per sequence, grp <= 16 heads per KV head, no chunk rows).
+hipError_t launch_exact_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, float* win_part,
+                               hipStream_t st);
 hipError_t launch_prefill_exact(const DecodePlan& p, const lr_layer_cache* c, const void* q, const void* k_chunk,
                                 const void* v_chunk, float* win_part, hipStream_t st);
 
