@@ -594,22 +594,34 @@ __global__ __launch_bounds__(256) void lr_exact_decode(ExactArgs a) {
   for (int j = 0; j < kExD / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   unsigned char* kw = kt[wave];
   unsigned char* vw = vt[wave];
-  for (int k0 = wave * kExdKeys; k0 < wl; k0 += 4 * kExdKeys) {
-    // slots k0 .. k0+15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V
+  // slots k0 .. k0+15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V; the next
+  // tile's loads are issued before this tile is processed
+  u32x4 kn[4], vn[4];
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = lane + 64 * u;
       const int r = i >> 4, gc = i & 15;
       const int j = k0 + r;
-      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+      kn[u] = u32x4{0u, 0u, 0u, 0u};
+      vn[u] = u32x4{0u, 0u, 0u, 0u};
       if (j < wl) {
         const size_t src = ((size_t)b * a.W + (L + j) % a.W) * a.D + g * kExD + gc * 8;
-        kv = *(const u32x4*)(a.kwin + src);
-        vv = *(const u32x4*)(a.vwin + src);
+        kn[u] = *(const u32x4*)(a.kwin + src);
+        vn[u] = *(const u32x4*)(a.vwin + src);
       }
-      *(u32x4*)(kw + r * kExSK + gc * 16) = kv;
-      *(u32x4*)(vw + r * kExSV + gc * 16) = vv;
     }
+  };
+  if (wave * kExdKeys < wl) load_tile(wave * kExdKeys);
+  for (int k0 = wave * kExdKeys; k0 < wl; k0 += 4 * kExdKeys) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      const int r = i >> 4, gc = i & 15;
+      *(u32x4*)(kw + r * kExSK + gc * 16) = kn[u];
+      *(u32x4*)(vw + r * kExSV + gc * 16) = vn[u];
+    }
+    if (k0 + 4 * kExdKeys < wl) load_tile(k0 + 4 * kExdKeys);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS before it is read
     // scores S^T[slot k0 + 4 lg + i][head li]
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
