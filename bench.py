@@ -7,7 +7,8 @@ decode, combine + up-projection). Inputs are seeded synthetic data already resid
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 Default workload: batch 16, 32768 cached tokens per sequence, rank 256 for K and V, bf16 latents
-(the long-context point of the TraceKV latency setting: batch 16, 4K-32K context).
+(the long-context point of the TraceKV latency setting: batch 16, 4K-32K context). --config 4
+times the whole 28-layer step instead (per-layer ranks, ragged lengths, exact recent window).
 """
 from __future__ import annotations
 
