@@ -149,7 +149,7 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
   const int KS = decode_ks(p->nks), RB = decode_rb(p->nrb);
   int window_lds = 0;
   if (p->exact)
-    window_lds = p->Hq * p->d * 4 + 2 * 32 * p->D * 2 + p->Hq * 32 * 4 + p->Hq * 3 * 4;
+    window_lds = p->Hq * p->d * 4 + 2 * 32 * p->D * 2 + 32 * 16 + p->Hq * 32 * 4 + p->Hq * 3 * 4;
   if (p->latent == LR_I4G32) {
     const int gk = (p->rk + 31) / 32, gv = (p->rv + 31) / 32;
     p->qp_bytes_k = gk * 4;

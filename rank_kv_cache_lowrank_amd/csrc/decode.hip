@@ -193,9 +193,12 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
   wl = wl < 0 ? 0 : (wl > W ? W : wl);
   const int nkeys = wl + (a.kchunk ? ci + 1 : 0);      // window slots, then chunk rows 0 .. ci
 
+  // key rows padded by 16 bytes: the score loop reads 32 rows at once, which would otherwise
+  // share one LDS bank (rows 1 KB apart)
+  const int KD = D + 8;
   float* qs = (float*)smem;                              // [Hq][d]
-  __bf16* kc = (__bf16*)(qs + Hq * d);                   // [32][D]
-  __bf16* vc = kc + 32 * D;                              // [32][D]
+  __bf16* kc = (__bf16*)(qs + Hq * d);                   // [32][KD]
+  __bf16* vc = kc + 32 * KD;                             // [32][D]
   float* sc = (float*)(vc + 32 * D);                     // [Hq][32]
   float* st = sc + Hq * 32;                              // [Hq][3]: m, l, alpha
 
@@ -231,7 +234,7 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
         ks = a.kchunk + src;
         vs = a.vchunk + src;
       }
-      *(u32x4*)(kc + u * D + c * 8) = *(const u32x4*)ks;
+      *(u32x4*)(kc + u * KD + c * 8) = *(const u32x4*)ks;
       *(u32x4*)(vc + u * D + c * 8) = *(const u32x4*)vs;
     }
     __syncthreads();
@@ -241,7 +244,7 @@ __device__ void window_block(const DecodeArgs& a, unsigned char* smem) {
       if (u < n) {
         const int g = j / grp;
         const float* qj = qs + j * d;
-        const __bf16* kr = kc + u * D + g * d;
+        const __bf16* kr = kc + u * KD + g * d;
         s = 0.f;
         for (int c = 0; c < d; ++c) s += qj[c] * (float)kr[c];
         s = (s != s) ? INFINITY : s;   // NaN propagates to this head only (see latent_block)

@@ -84,12 +84,15 @@ def test_prefill_sharp_queries(q_scale):
     assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
 
 
-def test_prefill_with_exact_window():
-    cfg, li = small("bf16", 358, L=(120, 0, 33), window=16, wl=(16, 5, 0))
+@pytest.mark.parametrize("latent,rank", [("bf16", 358), ("f32", 128), ("i4g32", 200)])
+def test_prefill_with_exact_window(latent, rank):
+    """Window slots and the chunk's own rows as exact keys: the dedicated bf16 kernels, the
+    matrix-core exact-keys kernel beside the decode kernels (int4), the VALU workgroups (fp32)."""
+    cfg, li = small(latent, rank, L=(120, 0, 33), window=16, wl=(16, 5, 0))
     model, cache = device_layer(li)
     q, k, v = chunk_inputs(cfg, 7)
     out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
-    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+    assert rel_err(out, oracle(li, q, k, v)) < TOL[latent]
 
 
 @pytest.mark.parametrize("nsplit", [1, 3, 16])

@@ -51,6 +51,20 @@ def test_all_28_layers_through_one_rank_table():
         check(li, model=model, layer=layer)
 
 
+@pytest.mark.parametrize("latent,rk,rv", [("f32", 128, 96), ("i4g32", 200, 72)])
+def test_window_with_other_latent_types(latent, rk, rv):
+    """fp32 latents (fp32 queries: the window on the VALU workgroups of the decode kernel) and int4
+    latents (the matrix-core exact-keys kernel), with partial and wrapped windows."""
+    cfg = CFG4.replace(batch=4, latent=latent, rank_choices=None, rank_k=rk, rank_v=rv)
+    li = synth.make_layer(cfg, 2, q_scale=16.0, lat_len=np.array([700, 130, 0, 1], np.int32),
+                          win_len=np.array([128, 77, 9, 128], np.int32))
+    m1, cache = device_layer(li)
+    out = run_decode(m1, cache, li.q.cuda(), int(li.lat_len.max()))
+    err = rel_err(out.numpy(), oracle_decode(li, list(range(4))))
+    print(f"{latent} r=({rk},{rv}) err={err:.3e}", flush=True)
+    assert err <= TOL[latent], err
+
+
 def test_window_only_sequences():
     cfg = CFG4.replace(batch=5)
     li = synth.make_layer(cfg, 3, q_scale=16.0, lat_len=np.zeros(5, np.int32),
