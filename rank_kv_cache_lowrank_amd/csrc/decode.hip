@@ -1044,13 +1044,25 @@ __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T*
 // F32OUT (int4 latents): float32 output at the dequantised tiles' block order; the decode
 // kernel picks each head's power-of-two scale and rounds to fp16. Else bf16 output.
 // ---------------------------------------------------------------------------------------------
+struct FoldArgs {
+  const __bf16* q;
+  const __bf16* bk;
+  void* qt;
+  int Hq, Hkv, D, rk, rk_pad;
+  float scale;
+  int nseq, nq;
+};
+
 template <bool F32OUT>
-__global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q, const __bf16* __restrict__ bk,
-                                                    void* __restrict__ qt, int Hq, int Hkv, int D, int rk,
-                                                    int rk_pad, float scale, int nseq, int nq) {
+__device__ __forceinline__ void fold_body(const FoldArgs& f, int bx, int by, int bz) {
+  const __bf16* __restrict__ q = f.q;
+  const __bf16* __restrict__ bk = f.bk;
+  void* __restrict__ qt = f.qt;
+  const int Hq = f.Hq, Hkv = f.Hkv, D = f.D, rk = f.rk, rk_pad = f.rk_pad, nseq = f.nseq, nq = f.nq;
+  const float scale = f.scale;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 4, li = lane & 15;
-  const int blk = blockIdx.x * 4 + wave;
-  const int g = blockIdx.y;
+  const int blk = bx * 4 + wave;
+  const int g = by;
   const int grp = Hq / Hkv;
   if (blk >= (rk_pad >> 4)) return;
   const int k = blk * 16 + li;
@@ -1061,7 +1073,7 @@ __global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q
     for (int ks = 0; ks < 4; ++ks) bop[ks] = k < rk ? *(const bf16x8*)(brow + ks * 32) : zero_bf16x8();
   }
   const int pos = F32OUT ? i4_pos(k) : k;
-  for (int b = blockIdx.z * nq; b < min(nseq, (int)(blockIdx.z + 1) * nq); ++b) {
+  for (int b = bz * nq; b < min(nseq, (bz + 1) * nq); ++b) {
   for (int h0 = 0; h0 < grp; h0 += 16) {
     const int hl = h0 + li;
     const __bf16* qrow = q + ((size_t)b * Hq + g * grp + hl) * kFoldD + lg * 8;
@@ -1089,6 +1101,161 @@ __global__ __launch_bounds__(256) void lr_fold_mfma(const __bf16* __restrict__ q
     }
   }
   }
+}
+
+
+template <bool F32OUT>
+__global__ __launch_bounds__(256) void lr_fold_mfma(FoldArgs f) {
+  fold_body<F32OUT>(f, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Exact keys of a decode step: one query token per sequence and no chunk rows (the new token is
+// already a window slot). One workgroup per (sequence, KV head) for its grp <= 16 heads. Wave w
+// takes the 16-key tiles w, w + 4, ... of the live window slots and stages each one itself (a
+// wave's LDS writes and reads stay in order), and the four waves' (O, m, l) are merged through
+// LDS. (The prefill's exact-keys kernel would give every key to the one wave that holds a decode
+// step's rows.)
+// ---------------------------------------------------------------------------------------------
+constexpr int kExdKeys = 16;
+__device__ __forceinline__ void exact_decode_body(const ExactArgs& a, int blk) {
+  __shared__ __attribute__((aligned(16))) unsigned char kt[4][kExdKeys * kExSK];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[4][kExdKeys * kExSV];
+  __shared__ float mrg_ml[4][2][16];
+  __shared__ f32x4 mrg_o[3][kExD / 16][64];
+  const int grp = a.Hq / a.Hkv;
+  const int g = blk % a.Hkv;
+  const int b = blk / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool rvalid = li < grp;
+  int L = a.lat_len[b];
+  L = L < 0 ? 0 : L;
+  int wl = a.W > 0 ? a.win_len[b] : 0;
+  wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
+
+  // q of this lane's head as the B operand: d indices 32 ks + 8 lg .. +7
+  bf16x8 qop[4];
+  {
+    const __bf16* qr = a.q + ((size_t)b * a.Hq + g * grp + (rvalid ? li : 0)) * kExD + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qop[ks] = rvalid ? *(const bf16x8*)(qr + ks * 32) : zero_bf16x8();
+  }
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[kExD / 16];
+#pragma unroll
+  for (int j = 0; j < kExD / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned char* kw = kt[wave];
+  unsigned char* vw = vt[wave];
+  // slots k0 .. k0+15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V; the next
+  // tile's loads are issued before this tile is processed
+  u32x4 kn[4], vn[4];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      const int r = i >> 4, gc = i & 15;
+      const int j = k0 + r;
+      kn[u] = u32x4{0u, 0u, 0u, 0u};
+      vn[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j < wl) {
+        const size_t src = ((size_t)b * a.W + (L + j) % a.W) * a.D + g * kExD + gc * 8;
+        kn[u] = *(const u32x4*)(a.kwin + src);
+        vn[u] = *(const u32x4*)(a.vwin + src);
+      }
+    }
+  };
+  if (wave * kExdKeys < wl) load_tile(wave * kExdKeys);
+  for (int k0 = wave * kExdKeys; k0 < wl; k0 += 4 * kExdKeys) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      const int r = i >> 4, gc = i & 15;
+      *(u32x4*)(kw + r * kExSK + gc * 16) = kn[u];
+      *(u32x4*)(vw + r * kExSV + gc * 16) = vn[u];
+    }
+    if (k0 + 4 * kExdKeys < wl) load_tile(k0 + 4 * kExdKeys);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS before it is read
+    // scores S^T[slot k0 + 4 lg + i][head li]
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    const unsigned char* krow = kw + li * kExSK + lg * 16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(krow + ks * 64), qop[ks], sacc, 0, 0, 0);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = sacc[i] * a.wscale;
+      v[i] = (k0 + 4 * lg + i < wl) ? ((x != x) ? INFINITY : x) : -INFINITY;
+    }
+    const float mx = wave_max_lg(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    const float mnew = fmaxf(m, mx);
+    if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int j = 0; j < kExD / 16; ++j) acc[j] *= alpha;
+      m = mnew;
+    }
+    const bool live = m != -INFINITY;
+    bf16x4 pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 pv = (__bf16)(live ? fast_exp2(v[i] - m) : 0.f);
+      pb[i] = pv;
+      ps += (float)pv;
+    }
+    lsum += ps;
+    const unsigned char* vbase = vw + (4 * lg + (li >> 2)) * kExSV + (li & 3) * 8;
+#pragma unroll
+    for (int j = 0; j < kExD / 16; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr(vbase + j * 32), pb, acc[j], 0, 0, 0);
+  }
+  const float l = wave_sum_lg(lsum);
+  // merge the four waves' partials into wave 0
+  if (lg == 0) {
+    mrg_ml[wave][0][li] = m;
+    mrg_ml[wave][1][li] = l;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < kExD / 16; ++j) mrg_o[wave - 1][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wave != 0 || !rvalid) return;
+  float ms = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) ms = fmaxf(ms, mrg_ml[w][0][li]);
+  float wb[4], lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = mrg_ml[w][0][li];
+    wb[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - ms);
+    lt += mrg_ml[w][1][li] * wb[w];
+  }
+  float* wp = a.win_part + ((size_t)b * a.Hq + g * grp + li) * (kExD + 2);
+#pragma unroll
+  for (int j = 0; j < kExD / 16; ++j) {
+    f32x4 o = acc[j] * wb[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) o += mrg_o[w - 1][j][lane] * wb[w];
+    *(f32x4*)(wp + j * 16 + 4 * lg) = o;
+  }
+  if (lg == 0) {
+    wp[kExD] = ms;
+    wp[kExD + 1] = lt;
+  }
+}
+
+// The fold and a decode step's exact keys in one launch (both read only the query, the bases and
+// the window, and write disjoint workspace): workgroups [0, nfold) fold, the rest take one
+// (sequence, KV head) of exact keys each.
+template <bool F32OUT>
+__global__ __launch_bounds__(256) void lr_fold_exact(FoldArgs f, ExactArgs e, int nfx, int nfy, int nfold) {
+  const int x = blockIdx.x;
+  if (x < nfold) fold_body<F32OUT>(f, x % nfx, (x / nfx) % nfy, x / (nfx * nfy));
+  else exact_decode_body(e, x - nfold);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1119,6 +1286,7 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
   return r;
 }
+
 
 template <typename T>
 __device__ __forceinline__ void load8f(const T* p, float* out) { load8<T>(p, out); }
@@ -1287,7 +1455,14 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   __bf16* qt = (__bf16*)(w + p.off_qt);
   const float scale = p.sm_scale * kLog2e;
 
-  // 1. fold
+  // Exact keys (window slots; in a prefill also the chunk's own rows): for bf16 queries the
+  // matrix-core exact-keys code runs before the latent kernel (a decode step's in the same launch
+  // as the fold); for float32 queries B extra workgroups of the decode kernel (window_block).
+  const bool exact_mfma = p.exact && p.latent != LR_F32;
+  const bool fused_exact = exact_mfma && p.qpb == 1 && p.Hq / p.Hkv <= 16;
+  float* win_part = (float*)(w + p.off_win);
+
+  // 1. fold (+ a decode step's exact keys)
   {
     dim3 grid((p.rk_pad + 63) / 64, p.Hkv, p.B);
     if (p.latent == LR_F32)
@@ -1297,12 +1472,47 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
       // query sequences per wave: 1 for a decode batch, up to 16 for a prefill chunk's tokens
       const int nq = p.B >= 512 ? 16 : (p.B >= 128 ? 4 : 1);
       const dim3 fgrid((p.rk_pad / 16 + 3) / 4, p.Hkv, (p.B + nq - 1) / nq);
-      if (p.latent == LR_I4G32)
-        hipLaunchKernelGGL(lr_fold_mfma<true>, fgrid, dim3(256), 0, st, (const __bf16*)q, (const __bf16*)c->bk,
-                           (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale, p.B, nq);
-      else
-        hipLaunchKernelGGL(lr_fold_mfma<false>, fgrid, dim3(256), 0, st, (const __bf16*)q, (const __bf16*)c->bk,
-                           (void*)qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale, p.B, nq);
+      FoldArgs f;
+      f.q = (const __bf16*)q;
+      f.bk = (const __bf16*)c->bk;
+      f.qt = (void*)qt;
+      f.Hq = p.Hq;
+      f.Hkv = p.Hkv;
+      f.D = p.D;
+      f.rk = p.rk;
+      f.rk_pad = p.rk_pad;
+      f.scale = scale;
+      f.nseq = p.B;
+      f.nq = nq;
+      const bool i4 = p.latent == LR_I4G32;
+      if (fused_exact) {
+        ExactArgs e;
+        e.q = (const __bf16*)q;
+        e.kwin = (const __bf16*)c->kwin;
+        e.vwin = (const __bf16*)c->vwin;
+        e.kchunk = nullptr;
+        e.vchunk = nullptr;
+        e.lat_len = c->lat_len;
+        e.win_len = c->win_len;
+        e.win_part = win_part;
+        e.C = 1;
+        e.Hq = p.Hq;
+        e.Hkv = p.Hkv;
+        e.D = p.D;
+        e.W = p.window;
+        e.wscale = scale;
+        e.nrb = 1;
+        const int nfold = (int)(fgrid.x * fgrid.y * fgrid.z);
+        const dim3 g2(nfold + p.B * p.Hkv);
+        if (i4)
+          hipLaunchKernelGGL(lr_fold_exact<true>, g2, dim3(256), 0, st, f, e, (int)fgrid.x, (int)fgrid.y, nfold);
+        else
+          hipLaunchKernelGGL(lr_fold_exact<false>, g2, dim3(256), 0, st, f, e, (int)fgrid.x, (int)fgrid.y, nfold);
+      } else if (i4) {
+        hipLaunchKernelGGL(lr_fold_mfma<true>, fgrid, dim3(256), 0, st, f);
+      } else {
+        hipLaunchKernelGGL(lr_fold_mfma<false>, fgrid, dim3(256), 0, st, f);
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1343,10 +1553,6 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.D = p.D;
   a.window = p.window;
   a.wscale = scale;
-  // Exact keys (window slots; in a prefill also the chunk's own rows): for bf16 queries the
-  // matrix-core exact-keys kernel runs first; for float32 queries B extra workgroups of the
-  // decode kernel (window_block) take them.
-  const bool exact_mfma = p.exact && p.latent != LR_F32;
   a.n_win_blocks = (p.exact && !exact_mfma) ? p.B : 0;
   a.qpb = p.qpb;
   a.kchunk = (const __bf16*)k_chunk;
@@ -1368,9 +1574,8 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
     if (e != hipSuccess) return e;
     e = launch_prefill_latent(p, c, qt, a.part_ml, a.part_acc, st, ev_begin, ev_end);
   } else {
-    if (exact_mfma) {
-      if (p.qpb == 1 && p.Hq / p.Hkv <= 16) e = launch_exact_decode(p, c, q, a.win_part, st);
-      else e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
+    if (exact_mfma && !fused_exact) {
+      e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
       if (e != hipSuccess) return e;
     }
     const int grid = a.n_win_blocks + p.B * p.nsplit;

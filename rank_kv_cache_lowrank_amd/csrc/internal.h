@@ -73,6 +73,26 @@ constexpr int lds_nst(int KS, int RB, int es) {   // stages in the ring: even, a
                                                              : (kLdsBytes - kLdsPad) / lds_stage(KS, RB, es)) & ~1;
 }
 
+// Exact keys (window slots and, in a prefill, the chunk's own rows): dense attention of each head
+// on the matrix cores, written as an (O, m, l) partial the combine merges.
+constexpr int kExD = 128;                 // head dim (the fold requires it too)
+constexpr int kExSK = kExD * 2 + 16;      // LDS row strides (bytes): key rows for the A operand,
+constexpr int kExSV = kExD * 2 + 32;      // value rows for the transpose read
+
+struct ExactArgs {
+  const __bf16* q;           // [B * C][Hq][d]
+  const __bf16* kwin;        // [B][W][D] ring (slot of window entry e: (lat_len + e) % W)
+  const __bf16* vwin;
+  const __bf16* kchunk;      // [B][C][D], or NULL: no chunk rows among the keys (decode)
+  const __bf16* vchunk;
+  const int32_t* lat_len;
+  const int32_t* win_len;
+  float* win_part;           // [B * C][Hq][d + 2]: O (unnormalised), m, l
+  int C, Hq, Hkv, D, W;
+  float wscale;              // sm_scale * log2 e
+  int nrb;                   // 64-row blocks per (b, g)
+};
+
 struct DecodePlan {
   int B;               // query sequences: stored sequences x qpb
   int qpb;             // query tokens per stored sequence (1 = decode, the chunk = prefill)
@@ -118,9 +138,6 @@ hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, c
 
 // The exact keys of a prefill with the dedicated kernels (p.pf): window slots and the chunk's
 // rows, causally; partials in the decode kernel's exact-keys layout.
-// Exact keys of a decode step (one query per sequence, grp <= 16 heads per KV head, no chunk rows).
-hipError_t launch_exact_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, float* win_part,
-                               hipStream_t st);
 hipError_t launch_prefill_exact(const DecodePlan& p, const lr_layer_cache* c, const void* q, const void* k_chunk,
                                 const void* v_chunk, float* win_part, hipStream_t st);
 

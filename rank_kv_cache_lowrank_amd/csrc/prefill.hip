@@ -421,24 +421,7 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
 // The partial (O, m, l) per (query token, head) has the layout of the decode kernel's
 // exact-keys partial, so the combine merges it unchanged.
 // ---------------------------------------------------------------------------------------------
-constexpr int kExD = 128;                 // head dim (the fold requires it too)
 constexpr int kExKeys = 32;               // keys per staged tile
-constexpr int kExSK = kExD * 2 + 16;      // LDS row strides (bytes): key rows for the A operand,
-constexpr int kExSV = kExD * 2 + 32;      // value rows for the transpose read
-
-struct ExactArgs {
-  const __bf16* q;           // [B * C][Hq][d]
-  const __bf16* kwin;        // [B][W][D] ring (slot of window entry e: (lat_len + e) % W)
-  const __bf16* vwin;
-  const __bf16* kchunk;      // [B][C][D], or NULL: no chunk rows among the keys (decode)
-  const __bf16* vchunk;
-  const int32_t* lat_len;
-  const int32_t* win_len;
-  float* win_part;           // [B * C][Hq][d + 2]: O (unnormalised), m, l
-  int C, Hq, Hkv, D, W;
-  float wscale;              // sm_scale * log2 e
-  int nrb;                   // 64-row blocks per (b, g)
-};
 
 __global__ __launch_bounds__(256) void lr_prefill_exact(ExactArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char kt[kExKeys * kExSK];
@@ -555,166 +538,6 @@ __global__ __launch_bounds__(256) void lr_prefill_exact(ExactArgs a) {
     wp[kExD] = m;
     wp[kExD + 1] = l;
   }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Exact keys of a decode step: one query token per sequence and no chunk rows (the new token is
-// already a window slot). One workgroup per (sequence, KV head) for its grp <= 16 heads. Wave w
-// takes the 16-key tiles w, w + 4, ... of the live window slots and stages each one itself (a
-// wave's LDS writes and reads stay in order), and the four waves' (O, m, l) are merged through
-// LDS. (The kernel above gives every key to the one wave that holds a decode step's rows.)
-// ---------------------------------------------------------------------------------------------
-constexpr int kExdKeys = 16;
-__global__ __launch_bounds__(256) void lr_exact_decode(ExactArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char kt[4][kExdKeys * kExSK];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[4][kExdKeys * kExSV];
-  __shared__ float mrg_ml[4][2][16];
-  __shared__ f32x4 mrg_o[3][kExD / 16][64];
-  const int grp = a.Hq / a.Hkv;
-  const int g = blockIdx.x % a.Hkv;
-  const int b = blockIdx.x / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool rvalid = li < grp;
-  int L = a.lat_len[b];
-  L = L < 0 ? 0 : L;
-  int wl = a.W > 0 ? a.win_len[b] : 0;
-  wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
-
-  // q of this lane's head as the B operand: d indices 32 ks + 8 lg .. +7
-  bf16x8 qop[4];
-  {
-    const __bf16* qr = a.q + ((size_t)b * a.Hq + g * grp + (rvalid ? li : 0)) * kExD + lg * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qop[ks] = rvalid ? *(const bf16x8*)(qr + ks * 32) : pf_zero8();
-  }
-  float m = -INFINITY, lsum = 0.f;
-  f32x4 acc[kExD / 16];
-#pragma unroll
-  for (int j = 0; j < kExD / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  unsigned char* kw = kt[wave];
-  unsigned char* vw = vt[wave];
-  // slots k0 .. k0+15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V; the next
-  // tile's loads are issued before this tile is processed
-  u32x4 kn[4], vn[4];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      const int r = i >> 4, gc = i & 15;
-      const int j = k0 + r;
-      kn[u] = u32x4{0u, 0u, 0u, 0u};
-      vn[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < wl) {
-        const size_t src = ((size_t)b * a.W + (L + j) % a.W) * a.D + g * kExD + gc * 8;
-        kn[u] = *(const u32x4*)(a.kwin + src);
-        vn[u] = *(const u32x4*)(a.vwin + src);
-      }
-    }
-  };
-  if (wave * kExdKeys < wl) load_tile(wave * kExdKeys);
-  for (int k0 = wave * kExdKeys; k0 < wl; k0 += 4 * kExdKeys) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      const int r = i >> 4, gc = i & 15;
-      *(u32x4*)(kw + r * kExSK + gc * 16) = kn[u];
-      *(u32x4*)(vw + r * kExSV + gc * 16) = vn[u];
-    }
-    if (k0 + 4 * kExdKeys < wl) load_tile(k0 + 4 * kExdKeys);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS before it is read
-    // scores S^T[slot k0 + 4 lg + i][head li]
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* krow = kw + li * kExSK + lg * 16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(krow + ks * 64), qop[ks], sacc, 0, 0, 0);
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = sacc[i] * a.wscale;
-      v[i] = (k0 + 4 * lg + i < wl) ? ((x != x) ? INFINITY : x) : -INFINITY;
-    }
-    const float mx = wave_max_lg(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-    const float mnew = fmaxf(m, mx);
-    if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int j = 0; j < kExD / 16; ++j) acc[j] *= alpha;
-      m = mnew;
-    }
-    const bool live = m != -INFINITY;
-    pf_bf16x4 pb;
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 pv = (__bf16)(live ? fast_exp2(v[i] - m) : 0.f);
-      pb[i] = pv;
-      ps += (float)pv;
-    }
-    lsum += ps;
-    const unsigned char* vbase = vw + (4 * lg + (li >> 2)) * kExSV + (li & 3) * 8;
-#pragma unroll
-    for (int j = 0; j < kExD / 16; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pf_vread(vbase + j * 32), pb, acc[j], 0, 0, 0);
-  }
-  const float l = wave_sum_lg(lsum);
-  // merge the four waves' partials into wave 0
-  if (lg == 0) {
-    mrg_ml[wave][0][li] = m;
-    mrg_ml[wave][1][li] = l;
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int j = 0; j < kExD / 16; ++j) mrg_o[wave - 1][j][lane] = acc[j];
-  }
-  __syncthreads();
-  if (wave != 0 || !rvalid) return;
-  float ms = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) ms = fmaxf(ms, mrg_ml[w][0][li]);
-  float wb[4], lt = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = mrg_ml[w][0][li];
-    wb[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - ms);
-    lt += mrg_ml[w][1][li] * wb[w];
-  }
-  float* wp = a.win_part + ((size_t)b * a.Hq + g * grp + li) * (kExD + 2);
-#pragma unroll
-  for (int j = 0; j < kExD / 16; ++j) {
-    f32x4 o = acc[j] * wb[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) o += mrg_o[w - 1][j][lane] * wb[w];
-    *(f32x4*)(wp + j * 16 + 4 * lg) = o;
-  }
-  if (lg == 0) {
-    wp[kExD] = ms;
-    wp[kExD + 1] = lt;
-  }
-}
-
-hipError_t launch_exact_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, float* win_part,
-                               hipStream_t st) {
-  ExactArgs a;
-  a.q = (const __bf16*)q;
-  a.kwin = (const __bf16*)c->kwin;
-  a.vwin = (const __bf16*)c->vwin;
-  a.kchunk = nullptr;
-  a.vchunk = nullptr;
-  a.lat_len = c->lat_len;
-  a.win_len = c->win_len;
-  a.win_part = win_part;
-  a.C = 1;
-  a.Hq = p.Hq;
-  a.Hkv = p.Hkv;
-  a.D = p.D;
-  a.W = p.window;
-  a.wscale = p.sm_scale * kLog2e;
-  a.nrb = 1;
-  hipLaunchKernelGGL(lr_exact_decode, dim3(p.B * p.Hkv), dim3(256), 0, st, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_prefill_exact(const DecodePlan& p, const lr_layer_cache* c, const void* q, const void* k_chunk,
