@@ -500,14 +500,15 @@ __device__ __forceinline__ void i4_loader(const DecodeArgs& a, unsigned char* sm
   int dq_stage = 2 % NR;                             // raw stage of tile 2 it + 2
   for (int it = 0; it < niter; ++it) {
     barrier_lds();                                   // fp16 values of 2it, 2it+1 visible
-    // the copies first, as early as their stages are free (measured: converting first and
-    // copying after it is slower)
-    if (it > 0) {
-      if (2 * it - 2 + NR < ntiles) issue(2 * it - 2 + NR);
-      if (2 * it - 1 + NR < ntiles) issue(2 * it - 1 + NR);
-    }
+    // copies as early as their stages are free (measured: converting both tiles first and
+    // copying after is slower)
+    // one tile's copies, one tile's conversion, then the other's: spread out, the copies stall
+    // less on the memory pipeline's backlog (measured: 53.1 against 54.1 us at T = 16K)
     const int dq1 = dq_stage + 1 == NR ? 0 : dq_stage + 1;
-    if (2 * it + 2 < ntiles) dequant2(2 * it + 2, dq_stage, dq1, 2 * it + 3 < ntiles);
+    if (it > 0 && 2 * it - 2 + NR < ntiles) issue(2 * it - 2 + NR);
+    if (2 * it + 2 < ntiles) dequant2(2 * it + 2, dq_stage, dq1, false);
+    if (it > 0 && 2 * it - 1 + NR < ntiles) issue(2 * it - 1 + NR);
+    if (2 * it + 3 < ntiles) dequant2(2 * it + 3, dq1, dq1, false);
     dq_stage = dq1 + 1 == NR ? 0 : dq1 + 1;
     wait_vmcnt(count(2 * it + 5, min(2 * it - 1 + NR, ntiles - 1)));
   }
