@@ -65,6 +65,21 @@ def test_window_with_other_latent_types(latent, rk, rv):
     assert err <= TOL[latent], err
 
 
+@pytest.mark.parametrize("hq,hkv,latent", [(32, 8, "bf16"), (16, 1, "bf16"), (32, 1, "bf16"), (16, 1, "i4g32")])
+def test_window_head_layouts(hq, hkv, latent):
+    """Query heads per KV head 4 and 16 (the fold and the exact keys in one launch) and 32 (beyond
+    that launch's bound of 16: the general exact-keys kernel, with no chunk rows)."""
+    cfg = synth.Config(93, f"window-h{hq}-{hkv}", batch=3, seq_len=300, rank_k=120, rank_v=88, latent=latent,
+                       window=32, n_q_heads=hq, n_kv_heads=hkv)
+    li = synth.make_layer(cfg, q_scale=8.0, lat_len=np.array([300, 0, 45], np.int32),
+                          win_len=np.array([32, 19, 1], np.int32))
+    m1, cache = device_layer(li)
+    out = run_decode(m1, cache, li.q.cuda(), int(li.lat_len.max()))
+    err = rel_err(out.numpy(), oracle_decode(li, list(range(3))))
+    print(f"Hq={hq} Hkv={hkv} {latent} err={err:.3e}", flush=True)
+    assert err <= TOL[latent], err
+
+
 def test_window_only_sequences():
     cfg = CFG4.replace(batch=5)
     li = synth.make_layer(cfg, 3, q_scale=16.0, lat_len=np.zeros(5, np.int32),
