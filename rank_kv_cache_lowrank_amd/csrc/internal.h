@@ -38,17 +38,18 @@ constexpr int lds_stage(int KS, int RB, int es) {
 //   split: each consumer wave owns one 16-head block for every other tile of its group and
 //          accumulates all value blocks (bf16 latents, value rank <= 384);
 //   half:  the two waves of a head block share each tile and split the value blocks.
-// (split needs up to 256 registers per consumer wave: one group; the narrowest rows keep two
-// groups of halves instead, which fit three waves per SIMD.)
-//   int4 latents always split (their workgroup has 8 waves, so 256 registers per wave).
+// (split needs up to 256 registers per consumer wave, so one group: 8 waves. Measured at rank
+// 256, T = 32K: split is ~5% faster than two groups of halves, 12 waves. fp32 latents keep the
+// two groups of halves.)
+//   int4 latents always split.
 constexpr bool decode_split(int latent, int KS, int RB) {
   return latent == LR_I4G32 ||
-         (latent == LR_BF16 && !(KS <= 8 && RB <= 8) && ((KS <= 12 && RB <= 12) || (KS == 16 && RB == 8)));
+         (latent == LR_BF16 && ((KS <= 12 && RB <= 12) || (KS == 16 && RB == 8)));
 }
 constexpr int decode_groups(int latent, int KS, int RB) {
   return latent == LR_I4G32 ? 1
        : latent == LR_F32   ? 2
-       : (KS <= 8 && RB <= 8) ? 2 : 1;
+       : 1;
 }
 // Tiles each iteration of the decode loop consumes (one workgroup barrier per iteration).
 constexpr int decode_tpi(int latent, int KS, int RB) {
