@@ -1039,9 +1039,10 @@ __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T*
 
 // ---------------------------------------------------------------------------------------------
 // Fold on the matrix cores for bf16 q and Bk: one wave per (16-column block of latent indices k,
-// KV head g, nq consecutive query sequences; the Bk operand is loaded once for all of them). C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d] over d = 128 in four
-// 16x16x32 bf16 steps (A = 16 query heads of the group, zero past grp; B = Bk^T; C row
-// h = 4*lg + i, column k = lane % 16), scaled by sm_scale * log2 e.
+// KV head g, nq consecutive query sequences; the Bk operand is loaded once for all of them).
+// C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d] over d = 128 in four 16x16x32 bf16 steps
+// (A = 16 query heads of the group, zero past grp; B = Bk^T; C row h = 4*lg + i, column
+// k = lane % 16), scaled by sm_scale * log2 e.
 // F32OUT (int4 latents): float32 output at the dequantised tiles' block order; the decode
 // kernel picks each head's power-of-two scale and rounds to fp16. Else bf16 output.
 // ---------------------------------------------------------------------------------------------
