@@ -1461,7 +1461,8 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   // matrix-core exact-keys code runs before the latent kernel (a decode step's in the same launch
   // as the fold); for float32 queries B extra workgroups of the decode kernel (window_block).
   const bool exact_mfma = p.exact && p.latent != LR_F32;
-  const bool fused_exact = exact_mfma && p.qpb == 1 && p.Hq / p.Hkv <= 16;
+  // (a decode step only: a prefill chunk's own rows are keys too, even for a one-token chunk)
+  const bool fused_exact = exact_mfma && k_chunk == nullptr && p.qpb == 1 && p.Hq / p.Hkv <= 16;
   float* win_part = (float*)(w + p.off_win);
 
   // 1. fold (+ a decode step's exact keys)

@@ -75,6 +75,17 @@ def test_prefill_matches_oracle(latent, rank, C):
     assert rel_err(out, ref) < TOL[latent]
 
 
+@pytest.mark.parametrize("latent,rank", [("bf16", 358), ("i4g32", 200), ("f32", 128)])
+def test_prefill_one_token_chunk(latent, rank):
+    """A chunk of one token per sequence, with a window: the token's own row is among its keys
+    (unlike a decode step, where the new token is already stored)."""
+    cfg, li = small(latent, rank, L=(120, 0, 33), window=16, wl=(16, 5, 0))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 1)
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
+    assert rel_err(out, oracle(li, q, k, v)) < TOL[latent]
+
+
 @pytest.mark.parametrize("q_scale", [32.0, 128.0])
 def test_prefill_sharp_queries(q_scale):
     cfg, li = small("bf16", 256, L=(200, 64, 1))
