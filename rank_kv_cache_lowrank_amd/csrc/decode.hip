@@ -1371,24 +1371,24 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
-    int r = rg;
-    for (; r + 48 < a.rv; r += 64) {
-      float v[4][8];
+    // 8 rows per round, every load issued: rows past rv read row rv - 1 (finite) against a zero
+    // weight, so the rows still add in ascending order and a rank that is not a multiple of
+    // 128 costs no extra one-load rounds
+    constexpr int U = 8;
+    for (int r = rg; r < a.rv; r += 16 * U) {
+      float v[U][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load8f<BT>(bv + (size_t)(r + 16 * u) * a.D, v[u]);
+      for (int u = 0; u < U; ++u) {
+        const int row = r + 16 * u;
+        load8f<BT>(bv + (size_t)(row < a.rv ? row : a.rv - 1) * a.D, v[u]);
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float h = ahat[r + 16 * u];
+      for (int u = 0; u < U; ++u) {
+        const int row = r + 16 * u;
+        const float h = row < a.rv ? ahat[row] : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] += h * v[u][e];
       }
-    }
-    for (; r < a.rv; r += 16) {
-      float v[8];
-      load8f<BT>(bv + (size_t)r * a.D, v);
-      const float h = ahat[r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] += h * v[e];
     }
     float* ored = part;     // [16][128]
 #pragma unroll
