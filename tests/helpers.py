@@ -60,18 +60,54 @@ def oracle_decode(li: synth.LayerInputs, batches=None, fn=OA.decode_latent) -> n
               win_len=li.win_len, window=cfg.window, batches=batches)
 
 
+def bits(t: torch.Tensor) -> torch.Tensor:
+    """Integer view of a tensor's storage (NaN patterns compare equal bit for bit)."""
+    view = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[t.element_size()]
+    return t.view(view)
+
+
+def cache_snapshot(cache) -> dict:
+    """Bit copies of every buffer of a cache (latents, scale/zero words, rings, lengths)."""
+    return {k: bits(t).clone() for k, t in cache.tensors.items() if t is not None}
+
+
+def assert_cache_unchanged(cache, snap: dict, what: str) -> None:
+    for k, t in snap.items():
+        assert torch.equal(bits(cache.tensors[k]), t), f"{what} modified the cache buffer {k}"
+
+
+WS_CANARY = 0xA5
+WS_GUARD = 4096
+
+
+def guarded_workspace(n: int, device) -> tuple:
+    """A workspace of n bytes followed by a canary band; returns (workspace view, full buffer)."""
+    buf = torch.full((n + WS_GUARD,), WS_CANARY, dtype=torch.uint8, device=device)
+    return buf[:n], buf
+
+
+def assert_canary(buf: torch.Tensor, n: int, what: str) -> None:
+    assert bool((buf[n:] == WS_CANARY).all()), f"{what} wrote past the end of its workspace"
+
+
 def run_decode(model, cache, q, max_lat_len, nsplit=0, out_dtype=torch.float32, guard=True, layer=0):
-    """Runs lowrank_attn_decode; checks guard bands around the output; returns out (CPU)."""
+    """Runs lowrank_attn_decode; checks guard bands around the output and past the workspace, and
+    that the cache is untouched; returns out (CPU)."""
     B, Hq, d = q.shape
     n = B * Hq * d
     pad = 1024
     buf = torch.full((n + 2 * pad,), float("nan"), dtype=out_dtype, device=q.device)
     out = buf[pad:pad + n].view(B, Hq, d)
-    ws = lr.workspace(model, layer, B, max_lat_len, nsplit)
+    ws_n = lr.lowrank_attn_decode_workspace_size(model, layer, B, max_lat_len, nsplit)
+    assert ws_n > 0
+    ws, ws_buf = guarded_workspace(ws_n, q.device)
+    snap = cache_snapshot(cache) if guard else None
     lr.lowrank_attn_decode(model, layer, cache, q, out, max_lat_len, ws, nsplit=nsplit)
     torch.cuda.synchronize()
     if guard:
         head = buf[:pad].float()
         tail = buf[pad + n:].float()
         assert torch.isnan(head).all() and torch.isnan(tail).all(), "decode wrote outside out"
+        assert_canary(ws_buf, ws_n, "decode")
+        assert_cache_unchanged(cache, snap, "decode")
     return out.float().cpu()

@@ -17,10 +17,46 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def make_cache(latent, B, t_cap, rk, rv, window=0, pk=None, pv=None, D=512, lat0=0, win0=0):
+GUARD_ROWS = 3
+
+
+def sentinel_storage(latent, B, t_cap, rank, ld):
+    """Latent storage whose every byte starts as 0xFF (NaN for float rows and for the float16
+    scale/zero words), laid out as [B][t_cap] rows followed by GUARD_ROWS spare rows; returns the
+    [B, t_cap, ...] views and the flat buffers (views share their memory)."""
+    if latent in ("f32", "bf16"):
+        dt = torch.float32 if latent == "f32" else torch.bfloat16
+        full = torch.empty(B * t_cap + GUARD_ROWS, ld, dtype=dt, device=DEV)
+        full.view(torch.uint8).fill_(0xFF)
+        return full[:B * t_cap].view(B, t_cap, ld), None, (full, None)
+    g = (rank + 31) // 32
+    codes = torch.full((B * t_cap + GUARD_ROWS, g * 16), 0xFF, dtype=torch.uint8, device=DEV)
+    qp = torch.full((B * t_cap + GUARD_ROWS, g), -1, dtype=torch.int32, device=DEV)
+    return codes[:B * t_cap].view(B, t_cap, g * 16), qp[:B * t_cap].view(B, t_cap, g), (codes, qp)
+
+
+def assert_rows_untouched(full, B, t_cap, written):
+    """Every row of a sentinel buffer outside `written` ({(b, row)}) still holds 0xFF bytes."""
+    if full is None:
+        return
+    rows = full.view(torch.uint8).view(full.shape[0], -1)
+    keep = torch.ones(rows.shape[0], dtype=torch.bool)
+    for b, t in written:
+        keep[b * t_cap + t] = False
+    idx = torch.nonzero(keep).flatten().to(rows.device)
+    assert bool((rows[idx] == 0xFF).all()), "append wrote a latent row it does not own (or past t_cap)"
+
+
+def make_cache(latent, B, t_cap, rk, rv, window=0, pk=None, pv=None, D=512, lat0=0, win0=0,
+               sentinel=False):
     ld_k, ld_v = synth.latent_ld(rk), synth.latent_ld(rv)
-    zk, zkq = lr.latent_storage(latent, B, t_cap, rk, ld_k, DEV)
-    zv, zvq = lr.latent_storage(latent, B, t_cap, rv, ld_v, DEV)
+    if sentinel:
+        zk, zkq, fk = sentinel_storage(latent, B, t_cap, rk, ld_k)
+        zv, zvq, fv = sentinel_storage(latent, B, t_cap, rv, ld_v)
+    else:
+        zk, zkq = lr.latent_storage(latent, B, t_cap, rk, ld_k, DEV)
+        zv, zvq = lr.latent_storage(latent, B, t_cap, rv, ld_v, DEV)
+        fk = fv = (None, None)
     dt = torch.float32 if latent == "f32" else torch.bfloat16
     bk = torch.zeros(rk, D, dtype=dt, device=DEV)
     bv = torch.zeros(rv, D, dtype=dt, device=DEV)
@@ -30,6 +66,7 @@ def make_cache(latent, B, t_cap, rk, rv, window=0, pk=None, pv=None, D=512, lat0
     vw = torch.zeros(B, window, D, dtype=torch.bfloat16, device=DEV) if window else None
     cache = lr.Cache(zk, zv, bk, bv, lat, t_cap, ld_k, ld_v, zk_qp=zkq, zv_qp=zvq, pk=pk, pv=pv,
                      kwin=kw, vwin=vw, win_len=win)
+    cache.sentinel_buffers = [fk[0], fk[1], fv[0], fv[1]]
     model = lr.Model(1, 28, 4, 128, [rk], [rv], 128 ** -0.5, window, latent)
     return model, cache
 
@@ -212,3 +249,112 @@ def test_append_clamps_at_capacity():
     x = np.ones((B, 3, D), np.float32)
     model, cache, _ = _run_append("bf16", D, D, eye, eye, x, x, lat0=7, t_cap=8, with_debug=False)
     assert torch.all(cache.lat_len == 8)
+
+
+def _pinv_bf16(cfg, which, r):
+    """The caller's down-projection of a stored bf16 basis: P = pinv(B) rounded to bf16, as float64."""
+    b = synth.to_storage(synth.gen_basis(cfg, which, 0, r), "bf16").double().numpy()
+    return torch.from_numpy(synth.down_projection(b)).to(torch.bfloat16).double().numpy()
+
+
+def _z_bound(x, P):
+    """float32-accumulation bound of z = x P over D terms: D * 2^-24 * sum |x| |P| (+ underflow slack)."""
+    return x.shape[-1] * 2.0 ** -24 * (np.abs(np.asarray(x, np.float64)) @ np.abs(P)) + 1e-30
+
+
+def test_append_bf16_general_projection():
+    """bf16 cache, W = 0, three new tokens per sequence through a general pseudo-inverse P: z_debug
+    lies within the float32 accumulation bound of the exact x P, and every stored row is the
+    round-to-nearest-even bf16 of that same float32 z, bit for bit; no other row changes."""
+    cfg = synth.CONFIGS[1]
+    r, B, n_new, lat0, t_cap = cfg.rank_k, 4, 3, 5, 12
+    Pk, Pv = _pinv_bf16(cfg, "k", r), _pinv_bf16(cfg, "v", r)
+    big = cfg.replace(batch=B)
+    xk = synth.to_storage(synth.gen_new_tokens(big, "k", 0, n_new), "bf16").float().numpy()
+    xv = synth.to_storage(synth.gen_new_tokens(big, "v", 0, n_new), "bf16").float().numpy()
+    dt = torch.bfloat16
+    pk = torch.from_numpy(Pk.astype(np.float32)).to(dt).to(DEV).contiguous()
+    pv = torch.from_numpy(Pv.astype(np.float32)).to(dt).to(DEV).contiguous()
+    model, cache = make_cache("bf16", B, t_cap, r, r, 0, pk, pv, lat0=lat0, sentinel=True)
+    zdbg = torch.full((B, n_new, 2 * r), float("nan"), device=DEV)
+    lr.lowrank_kv_append(model, 0, cache, torch.from_numpy(xk).to(dt).to(DEV),
+                         torch.from_numpy(xv).to(dt).to(DEV), zdbg)
+    torch.cuda.synchronize()
+    zdbg = zdbg.cpu().numpy()
+    assert torch.all(cache.lat_len == lat0 + n_new)
+    for which, x, P, zg in (("k", xk, Pk, zdbg[:, :, :r]), ("v", xv, Pv, zdbg[:, :, r:])):
+        z64 = x.astype(np.float64) @ P
+        assert np.all(np.abs(zg.astype(np.float64) - z64) <= _z_bound(x, P))
+        got = stored_rows(cache, "bf16", which, r, lat0 + n_new)[:, lat0:]
+        assert np.array_equal(got.view(np.uint32), OAP.bf16_rne(zg).view(np.uint32))
+    written = {(b, lat0 + i) for b in range(B) for i in range(n_new)}
+    for full in cache.sentinel_buffers:
+        assert_rows_untouched(full, B, t_cap, written)
+
+
+@pytest.mark.parametrize("latent", ["bf16", "i4g32"])
+def test_window_eviction_general_projection(latent):
+    """An exact window W = 8 fed an 11-token stream in calls of 1-3 tokens, with a general
+    pseudo-inverse P: window slots and lengths equal the oracle's token-list model; each evicted
+    token's z (z_debug of the call that evicted it) lies within the float32 accumulation bound of
+    the oracle's x_old P; the stored row is that z's storage form (bf16 rounding, or the int4
+    codes / scale / zero), bit for bit; no other latent row and nothing past t_cap changes."""
+    cfg = synth.CONFIGS[1]
+    B, D, W, r, t_cap = 3, 512, 8, 200, 8
+    calls = (1, 3, 2, 1, 3, 1)
+    Pk, Pv = _pinv_bf16(cfg, "k", r), _pinv_bf16(cfg, "v", r)
+    dt = torch.bfloat16
+    pk = torch.from_numpy(Pk.astype(np.float32)).to(dt).to(DEV).contiguous()
+    pv = torch.from_numpy(Pv.astype(np.float32)).to(dt).to(DEV).contiguous()
+    model, cache = make_cache(latent, B, t_cap, r, r, W, pk, pv, sentinel=True)
+    rng = np.random.default_rng(11)
+    stream_k = torch.from_numpy(rng.standard_normal((B, sum(calls), D)).astype(np.float32)).to(dt)
+    stream_v = torch.from_numpy(rng.standard_normal((B, sum(calls), D)).astype(np.float32)).to(dt)
+    states = [OAP.SeqState(window=W, D=D) for _ in range(B)]
+    z_gpu = [[] for _ in range(B)]            # (z_k, z_v) float32 of each evicted row, in order
+    pos = 0
+    for n in calls:
+        xk, xv = stream_k[:, pos:pos + n].contiguous(), stream_v[:, pos:pos + n].contiguous()
+        before = [st.lat_len for st in states]
+        zdbg = torch.full((B, n, 2 * r), float("nan"), device=DEV)
+        lr.lowrank_kv_append(model, 0, cache, xk.to(DEV), xv.to(DEV), zdbg)
+        torch.cuda.synchronize()
+        zdbg = zdbg.cpu().numpy()
+        for b in range(B):
+            for i in range(n):
+                OAP.append_token(states[b], xk[b, i].double().numpy(), xv[b, i].double().numpy(), Pk, Pv)
+            n_ev = states[b].lat_len - before[b]
+            for i in range(n_ev):
+                z_gpu[b].append((zdbg[b, i, :r], zdbg[b, i, r:]))
+            assert np.all(np.isnan(zdbg[b, n_ev:]))      # no z for rows the call did not write
+        pos += n
+    lat = cache.lat_len.cpu().numpy()
+    win = cache.win_len.cpu().numpy()
+    kw = cache.kwin.float().cpu().numpy()
+    vw = cache.vwin.float().cpu().numpy()
+    written = set()
+    for b in range(B):
+        st = states[b]
+        assert st.lat_len == 3 and st.win_len == W          # 11 tokens: 3 evicted, 8 in the window
+        assert lat[b] == st.lat_len and win[b] == st.win_len
+        for i in range(st.win_len):
+            slot = (st.lat_len + i) % W
+            assert np.array_equal(kw[b, slot], st.ring_k[slot])
+            assert np.array_equal(vw[b, slot], st.ring_v[slot])
+        for t in range(st.lat_len):                        # evicted = the oldest tokens, in order
+            written.add((b, t))
+            xs = (stream_k[b, t].double().numpy(), stream_v[b, t].double().numpy())
+            for which, x, P, zg, z64 in (("k", xs[0], Pk, z_gpu[b][t][0], st.lat_z_k[t]),
+                                         ("v", xs[1], Pv, z_gpu[b][t][1], st.lat_z_v[t])):
+                assert np.all(np.abs(zg.astype(np.float64) - z64) <= _z_bound(x[None], P)[0])
+                if latent == "bf16":
+                    got = stored_rows(cache, "bf16", which, r, t + 1)[b, t]
+                    assert np.array_equal(got.view(np.uint32), OAP.bf16_rne(zg).view(np.uint32))
+                else:
+                    codes, s16, z16 = OQ.quantize_rows(zg[None])
+                    gc, gs, gz = stored_rows(cache, "i4g32", which, r, t + 1)
+                    assert np.array_equal(gc[b, t], codes[0])
+                    assert np.array_equal(gs[b, t].view(np.uint16), s16[0].view(np.uint16))
+                    assert np.array_equal(gz[b, t].view(np.uint16), z16[0].view(np.uint16))
+    for full in cache.sentinel_buffers:
+        assert_rows_untouched(full, B, t_cap, written)

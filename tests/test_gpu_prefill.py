@@ -6,7 +6,8 @@ import torch
 
 import synth
 import rank_kv_cache_lowrank_amd as lr
-from helpers import TOL, device_layer, oracle_latents, rel_err
+from helpers import (TOL, assert_cache_unchanged, assert_canary, cache_snapshot, device_layer, guarded_workspace,
+                     oracle_latents, rel_err)
 from oracle import prefill as OP
 
 pytestmark = pytest.mark.gpu
@@ -19,11 +20,16 @@ def run_prefill(model, cache, q, k, v, max_len, nsplit=0, out_dtype=torch.float3
     pad = 1024
     buf = torch.full((n + 2 * pad,), float("nan"), dtype=out_dtype, device=DEV)
     out = buf[pad:pad + n].view(B, C, Hq, d)
-    ws = lr.prefill_workspace(model, 0, B, C, max_len, nsplit)
+    ws_n = lr.lowrank_attn_prefill_workspace_size(model, 0, B, C, max_len, nsplit)
+    assert ws_n > 0
+    ws, ws_buf = guarded_workspace(ws_n, DEV)
+    snap = cache_snapshot(cache)
     lr.lowrank_attn_prefill(model, 0, cache, q, k, v, out, max_len, ws, nsplit=nsplit)
     torch.cuda.synchronize()
     assert torch.isnan(buf[:pad].float()).all() and torch.isnan(buf[pad + n:].float()).all(), \
         "prefill wrote outside out"
+    assert_canary(ws_buf, ws_n, "prefill")
+    assert_cache_unchanged(cache, snap, "prefill")
     return out.float().cpu().numpy()
 
 
