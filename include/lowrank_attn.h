@@ -20,7 +20,8 @@
  *
  * Conventions (all entry points)
  *   - Every pointer not marked "host" is HIP device memory owned by the caller. The library
- *     allocates nothing, keeps no pointer after a call returns and holds no state.
+ *     allocates nothing, keeps no pointer after a call returns and holds no state (apart from
+ *     the per-GPU device scratch array behind lowrank_attn_decode_noalloc).
  *   - All device work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     nothing synchronises with the host. Buffers must stay alive until the stream reaches
  *     the work.
@@ -150,6 +151,21 @@ int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_laye
                         int32_t batch, int32_t max_lat_len, const void* q, void* out,
                         int32_t out_dtype, void* workspace, size_t workspace_bytes,
                         const lr_decode_opts* opts, void* stream);
+
+/*
+ * lowrank_attn_decode without a caller workspace, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid hipMalloc). The workspace
+ * is a device array inside the library, LOWRANK_NOALLOC_SCRATCH_BYTES long, one per GPU, held from
+ * the first call on that GPU until the process ends; the call allocates nothing. Arguments,
+ * results and errors are those of lowrank_attn_decode (same kernels, same output bit for bit), and
+ * a call whose lowrank_attn_decode_workspace_size(...) exceeds the array returns LR_EWORKSPACE
+ * before any launch. All calls on one GPU share the array: calls that overlap in time on one GPU
+ * (different streams, or host threads) race and must be serialised by the caller.
+ */
+#define LOWRANK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int lowrank_attn_decode_noalloc(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                                int32_t batch, int32_t max_lat_len, const void* q, void* out,
+                                int32_t out_dtype, const lr_decode_opts* opts, void* stream);
 
 /*
  * Bytes of device workspace lowrank_attn_prefill needs (256-byte aligned base required);

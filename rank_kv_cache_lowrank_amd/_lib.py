@@ -21,7 +21,8 @@ LR_OK, LR_EINVAL, LR_EUNSUPPORTED, LR_EWORKSPACE, LR_EHIP = 0, -1, -2, -3, -4
 LR_F32, LR_BF16, LR_I4G32 = 0, 1, 2
 DTYPES = {"f32": LR_F32, "bf16": LR_BF16, "i4g32": LR_I4G32}
 
-EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_attn_prefill_workspace_size",
+EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank_attn_decode_noalloc",
+           "lowrank_attn_prefill_workspace_size",
            "lowrank_attn_prefill", "lowrank_sens_svd_workspace_size", "lowrank_sens_svd",
            "lowrank_sens_svd_batched_workspace_size", "lowrank_sens_svd_batched",
            "lowrank_rank_allocate_workspace_size", "lowrank_rank_allocate",
@@ -72,6 +73,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowrank_attn_decode.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                         c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                         POINTER(lr_decode_opts), c_void_p]
+    lib.lowrank_attn_decode_noalloc.restype = c_int32
+    lib.lowrank_attn_decode_noalloc.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
+                                                c_int32, c_void_p, c_void_p, c_int32, POINTER(lr_decode_opts),
+                                                c_void_p]
     lib.lowrank_attn_prefill_workspace_size.restype = c_size_t
     lib.lowrank_attn_prefill_workspace_size.argtypes = [POINTER(lr_model_desc), c_int32, c_int32, c_int32,
                                                         c_int32, POINTER(lr_decode_opts)]
@@ -213,6 +218,18 @@ def lowrank_attn_decode(model: Model, layer: int, cache: Cache, q: torch.Tensor,
     _check(load().lowrank_attn_decode(ctypes.byref(model.desc), layer, ctypes.byref(cache.c), q.shape[0],
                                       max_lat_len, _ptr(q), _ptr(out), out_dtype, _ptr(workspace), ws_bytes,
                                       _opts(nsplit, events), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # LOWRANK_NOALLOC_SCRATCH_BYTES
+
+
+def lowrank_attn_decode_noalloc(model: Model, layer: int, cache: Cache, q: torch.Tensor, out: torch.Tensor,
+                                max_lat_len: int, nsplit: int = 0, stream=None, events=None) -> None:
+    """lowrank_attn_decode through the library's own device scratch (no workspace argument)."""
+    out_dtype = LR_F32 if out.dtype == torch.float32 else LR_BF16
+    _check(load().lowrank_attn_decode_noalloc(ctypes.byref(model.desc), layer, ctypes.byref(cache.c), q.shape[0],
+                                              max_lat_len, _ptr(q), _ptr(out), out_dtype, _opts(nsplit, events),
+                                              _stream(stream)))
 
 
 def lowrank_attn_prefill_workspace_size(model: Model, layer: int, batch: int, n_new: int, max_lat_len: int,

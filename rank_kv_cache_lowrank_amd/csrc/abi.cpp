@@ -285,6 +285,41 @@ int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_laye
   LR_GUARD_END
 }
 
+int lowrank_attn_decode_noalloc(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                                int32_t batch, int32_t max_lat_len, const void* q, void* out, int32_t out_dtype,
+                                const lr_decode_opts* opts, void* stream) {
+  LR_GUARD_BEGIN
+  DecodePlan p;
+  const char* msg = "";
+  int st = plan_decode(model, layer, batch, max_lat_len, opts, &p, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  st = check_cache_common(model, cache, p.rk, p.rv, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if ((int64_t)max_lat_len > cache->t_cap) return fail(LR_EINVAL, "max_lat_len must be <= t_cap");
+  if (!q || !out) return fail(LR_EINVAL, "q and out must not be NULL");
+  if (!cache->bk || !cache->bv) return fail(LR_EINVAL, "bases bk/bv must not be NULL");
+  if (!aligned(cache->bk, 16) || !aligned(cache->bv, 16) || !aligned(q, 16))
+    return fail(LR_EINVAL, "q and the bases must be 16-byte aligned");
+  if (out_dtype != LR_F32 && out_dtype != LR_BF16) return fail(LR_EINVAL, "out_dtype must be LR_F32 or LR_BF16");
+  if (p.latent == LR_I4G32 && (!aligned(cache->zk_qp, 16) || !aligned(cache->zv_qp, 16)))
+    return fail(LR_EINVAL, "int4 decode needs 16-byte aligned scale/zero buffers");
+  st = plan_lds(&p, cache->ld_k, cache->ld_v, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (p.ws_bytes > kNoAllocScratchBytes)
+    return fail(LR_EWORKSPACE, "this decode needs more workspace than the library's scratch array holds "
+                               "(LOWRANK_NOALLOC_SCRATCH_BYTES); use lowrank_attn_decode with a caller workspace");
+  if (batch == 0) return LR_OK;
+  void* ws = nullptr;
+  hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  p.t_cap = cache->t_cap;
+  e = launch_decode(p, cache, q, out, out_dtype, ws, (hipStream_t)stream,
+                    opts ? (hipEvent_t)opts->event_begin : nullptr, opts ? (hipEvent_t)opts->event_end : nullptr);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
 size_t lowrank_attn_prefill_workspace_size(const lr_model_desc* model, int32_t layer, int32_t batch,
                                            int32_t n_new, int32_t max_lat_len, const lr_decode_opts* opts) {
   try {

@@ -185,4 +185,9 @@ void rebase_shape(int r_old, int r_new, RebaseShape* s);   // new coordinates pe
 
 int device_cu_count();
 
+// Allocation-free decode: the workspace is a device array of the library (noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace lr
