@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define LOWRANK_ABI_VERSION 1
+#define LOWRANK_ABI_VERSION 2
 
 typedef enum {
   LR_OK = 0,
@@ -94,8 +94,10 @@ typedef struct {
  *   min/max run over its real elements): zero = f16(min), scale = f16(f32(max-min)/15),
  *   code = clamp(rint((z - zero)/scale), 0, 15) in float32, all codes 0 if scale == 0.
  * Bases (row-major): bk [rank_k][D], bv [rank_v][D]; float32 if latent_dtype == LR_F32, else
- *   bfloat16. Down-projections pk [D][rank_k], pv [D][rank_v] (the caller's pseudo-inverse of
- *   the bases, same dtype as the bases): used by append only, may be NULL for decode.
+ *   bfloat16. Down-projections pk [rank_k][D], pv [rank_v][D], rank-major: row i holds the
+ *   weights that give latent coordinate i of a dense row x, z_i = x . pk[i] (the caller's
+ *   pseudo-inverse P = pinv(B) [D][rank], stored transposed; for orthonormal bases pk = bk). Same
+ *   dtype as the bases, 16-byte aligned; used by append only, may be NULL for decode.
  * Exact window (window W > 0): kwin, vwin [B][W][D] bfloat16 rings; the token at absolute
  *   position p sits in slot p mod W. Sequence b holds win_len[b] window tokens at positions
  *   lat_len[b] .. lat_len[b]+win_len[b]-1. NULL when W == 0.
@@ -117,7 +119,7 @@ typedef struct {
   int32_t* win_len;
   int32_t ld_k;            /* latent row stride in elements (F32/BF16): >= rank_k, multiple of 8 */
   int32_t ld_v;            /* >= rank_v, multiple of 8 */
-  int64_t t_cap;           /* latent rows allocated per sequence, >= 1 */
+  int64_t t_cap;           /* latent rows allocated per sequence, 1 .. 2^24 - 1 */
 } lr_layer_cache;
 
 /* Optional decode tuning and timing hooks. */
@@ -210,6 +212,10 @@ int lowrank_attn_prefill(const lr_model_desc* model, int32_t layer, const lr_lay
  *   lat_len[b] grows by one. Requires n_new <= W.
  * Requires lat_len[b] + (number of new latent rows) <= t_cap (clamped otherwise: rows past
  * t_cap are dropped and lengths stop at t_cap).
+ * One launch: while it runs, bits 24..30 of each lat_len word count the workgroups that have read
+ * that sequence's inputs (the length itself stays in bits 0..23); the last one writes the final
+ * lengths, so after the call the words hold plain lengths again. Nothing may read or write the
+ * lengths on another stream during the call.
  * z_debug: NULL, or [B][n_new][rank_k + rank_v] float32 receiving, for each latent row this
  *   call writes (the i-th such row of sequence b at index i), its z before storage rounding.
  * Writes latent rows, window slots and the two length arrays, nothing else.
@@ -322,6 +328,38 @@ size_t lowrank_rank_allocate_workspace_size(int32_t n_mat, int32_t r_min, int32_
 int lowrank_rank_allocate(const float* sigma, int32_t n_mat, int32_t n_sigma, int32_t sigma_ld,
                           int64_t budget, int32_t r_min, int32_t r_max, int32_t granule,
                           int32_t* ranks, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-incremental basis update of one KV matrix (iS-KV, "iS-KV: Online Low-Rank KV Cache
+ * Compression via Block-Incremental SVD", English abstract and method summary: the low-rank basis
+ * evolves incrementally while older states are folded, block by block, into the bounded-rank
+ * history, and the historical coordinates are synchronised with the updated basis; the pages name
+ * block-incremental SVD without its equations, read here as the textbook incremental SVD).
+ * The history is held as U diag(sigma) B; folding the block of dense rows Y gives the new basis
+ * and spectrum as the top rank_new right singular vectors and values of M = [diag(sigma) B ; Y].
+ *   basis   [rank][dim] (basis_dtype LR_F32 or LR_BF16): the current basis, orthonormal rows
+ *   sigma   [rank] float32 >= 0: its singular values (e.g. from lowrank_sens_svd or an earlier
+ *           update)
+ *   rows    [n_rows][dim] bfloat16: the block of dense K (or V) rows being folded in, e.g. the
+ *           tokens leaving the exact window (may be NULL when n_rows == 0)
+ *   basis_new [rank_new][dim] (basis_dtype, output): the new basis, each row with its
+ *           largest-magnitude component positive
+ *   sigma_new [rank_new] float32 (output): the new singular values, descending
+ *   w       [rank_new][round_up(rank, 8)] (basis_dtype, output; pad columns 0): W = B' B^T, the
+ *           sync weights lowrank_kv_rebase takes (z' = z W^T; B' has orthonormal rows, so this is
+ *           z B pinv(B'))
+ * Computed on the rows [bf16(sigma_i * B_i) (float32 product, one rounding) ; Y] with the weighted
+ * SVD of lowrank_sens_svd (unit weights; `sweeps` Jacobi sweeps, 0 = 10): the exact SVD of those
+ * rows to the Jacobi's float32 accuracy. Requires dim a multiple of 64 in 64..512,
+ * 1 <= rank <= dim, 0 <= n_rows <= 65536, 1 <= rank_new <= min(dim, rank + n_rows). workspace:
+ * lowrank_basis_update_workspace_size() bytes, 256-byte aligned. The inputs are only read; the
+ * outputs must not overlap them.
+ */
+size_t lowrank_basis_update_workspace_size(int32_t rank, int32_t n_rows, int32_t dim);
+int lowrank_basis_update(const void* basis, int32_t basis_dtype, const float* sigma, int32_t rank,
+                         const void* rows, int32_t n_rows, int32_t dim, int32_t rank_new, int32_t sweeps,
+                         void* basis_new, float* sigma_new, void* w, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this host thread ("" if none). */
 const char* lowrank_last_error(void);

@@ -27,7 +27,8 @@ EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank
            "lowrank_sens_svd_batched_workspace_size", "lowrank_sens_svd_batched",
            "lowrank_rank_allocate_workspace_size", "lowrank_rank_allocate",
            "lowrank_kv_append",
-           "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_last_error",
+           "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_basis_update_workspace_size",
+           "lowrank_basis_update", "lowrank_last_error",
            "lowrank_abi_version")
 
 
@@ -112,6 +113,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowrank_kv_rebase.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache),
                                       POINTER(lr_layer_cache), c_int32, c_int32, c_int32, c_int32, c_void_p,
                                       c_void_p, c_void_p]
+    lib.lowrank_basis_update_workspace_size.restype = c_size_t
+    lib.lowrank_basis_update_workspace_size.argtypes = [c_int32, c_int32, c_int32]
+    lib.lowrank_basis_update.restype = c_int32
+    lib.lowrank_basis_update.argtypes = [c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
+                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.lowrank_last_error.restype = ctypes.c_char_p
     lib.lowrank_last_error.argtypes = []
     lib.lowrank_abi_version.restype = c_int32
@@ -324,6 +330,24 @@ def lowrank_kv_rebase(model: Model, layer: int, src: Cache, dst: Cache, max_lat_
     _check(load().lowrank_kv_rebase(ctypes.byref(model.desc), layer, ctypes.byref(src.c), ctypes.byref(dst.c),
                                     src.zk.shape[0], max_lat_len, rank_k_new, rank_v_new, _ptr(wk), _ptr(wv),
                                     _stream(stream)))
+
+
+def lowrank_basis_update_workspace_size(rank: int, n_rows: int, dim: int) -> int:
+    return int(load().lowrank_basis_update_workspace_size(rank, n_rows, dim))
+
+
+def lowrank_basis_update(basis: torch.Tensor, sigma: torch.Tensor, rows: Optional[torch.Tensor], rank_new: int,
+                         basis_new: torch.Tensor, sigma_new: torch.Tensor, w: torch.Tensor, workspace: torch.Tensor,
+                         sweeps: int = 0, stream=None) -> None:
+    """basis [rank][dim] f32 or bf16, sigma [rank] f32, rows [n][dim] bf16 (or None); outputs basis_new
+    [rank_new][dim] (basis dtype), sigma_new [rank_new] f32, w [rank_new][round_up(rank, 8)] (basis dtype)."""
+    rank, dim = basis.shape
+    n = 0 if rows is None else rows.shape[0]
+    bdt = LR_F32 if basis.dtype == torch.float32 else LR_BF16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().lowrank_basis_update(_ptr(basis), bdt, _ptr(sigma), rank, _ptr(rows), n, dim, rank_new, sweeps,
+                                       _ptr(basis_new), _ptr(sigma_new), _ptr(w), _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
 
 
 # ---- device memory plumbing ---------------------------------------------------------------------

@@ -207,7 +207,7 @@ static int check_cache_common(const lr_model_desc* m, const lr_layer_cache* c, i
   if (!c) return *msg = "cache is NULL", LR_EINVAL;
   if (!c->zk || !c->zv) return *msg = "latent buffers zk/zv must not be NULL", LR_EINVAL;
   if (!c->lat_len) return *msg = "lat_len must not be NULL", LR_EINVAL;
-  if (c->t_cap < 1 || c->t_cap > (int64_t)1 << 30) return *msg = "t_cap must be in 1..2^30", LR_EINVAL;
+  if (c->t_cap < 1 || c->t_cap > kMaxTCap) return *msg = "t_cap must be in 1..2^24-1", LR_EINVAL;
   if (!aligned(c->zk, 16) || !aligned(c->zv, 16)) return *msg = "latent buffers must be 16-byte aligned", LR_EINVAL;
   if (m->latent_dtype == LR_I4G32) {
     if (!c->zk_qp || !c->zv_qp) return *msg = "int4 caches need zk_qp/zv_qp", LR_EINVAL;
@@ -399,6 +399,7 @@ int lowrank_kv_append(const lr_model_desc* model, int32_t layer, const lr_layer_
   if (model->window > 0 && n_new > model->window) return fail(LR_EINVAL, "n_new must be <= window");
   if (n_new > 0 && (!k_new || !v_new)) return fail(LR_EINVAL, "k_new/v_new must not be NULL");
   if (!cache->pk || !cache->pv) return fail(LR_EINVAL, "append needs the down-projections pk/pv");
+  if (!aligned(cache->pk, 16) || !aligned(cache->pv, 16)) return fail(LR_EINVAL, "pk/pv must be 16-byte aligned");
   if ((k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)))
     return fail(LR_EINVAL, "k_new/v_new must be 16-byte aligned");
   if (batch == 0 || n_new == 0) return LR_OK;
@@ -459,8 +460,8 @@ int lowrank_kv_rebase(const lr_model_desc* model, int32_t layer, const lr_layer_
   if (!src || !dst) return fail(LR_EINVAL, "src/dst is NULL");
   if (!src->zk || !src->zv || !dst->zk || !dst->zv) return fail(LR_EINVAL, "latent buffers zk/zv must not be NULL");
   if (!src->lat_len) return fail(LR_EINVAL, "src lat_len must not be NULL");
-  if (src->t_cap < 1 || src->t_cap > (int64_t)1 << 30 || dst->t_cap < 1 || dst->t_cap > (int64_t)1 << 30)
-    return fail(LR_EINVAL, "t_cap must be in 1..2^30");
+  if (src->t_cap < 1 || src->t_cap > kMaxTCap || dst->t_cap < 1 || dst->t_cap > kMaxTCap)
+    return fail(LR_EINVAL, "t_cap must be in 1..2^24-1");
   if (!aligned(src->zk, 16) || !aligned(src->zv, 16) || !aligned(dst->zk, 16) || !aligned(dst->zv, 16))
     return fail(LR_EINVAL, "latent buffers must be 16-byte aligned");
   if (src->ld_k < rk || src->ld_v < rv) return fail(LR_EINVAL, "src ld must be >= the current rank");
@@ -592,6 +593,45 @@ int lowrank_sens_svd_batched(const void* x, const float* w, int32_t n_mat, int32
     return fail(LR_EWORKSPACE, "workspace too small");
   hipError_t e = launch_sens_svd(x, w, n_mat, n_samples, dim, rank, sweeps == 0 ? 10 : sweeps, basis,
                                  basis_dtype == LR_F32, sigma, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+static int check_basis_update_args(int32_t rank, int32_t n_rows, int32_t dim, int32_t rank_new, const char** msg) {
+  if (dim < 64 || dim > 512 || dim % 64 != 0) return *msg = "dim must be a multiple of 64 in 64..512", LR_EUNSUPPORTED;
+  if (rank < 1 || rank > dim) return *msg = "rank must be in 1..dim", LR_EINVAL;
+  if (n_rows < 0 || n_rows > 65536) return *msg = "n_rows must be in 0..65536", LR_EINVAL;
+  const int cap = rank + n_rows < dim ? rank + n_rows : dim;
+  if (rank_new < 1 || rank_new > cap) return *msg = "rank_new must be in 1..min(dim, rank + n_rows)", LR_EINVAL;
+  return LR_OK;
+}
+
+size_t lowrank_basis_update_workspace_size(int32_t rank, int32_t n_rows, int32_t dim) {
+  const char* msg = "";
+  if (check_basis_update_args(rank, n_rows, dim, 1, &msg) != LR_OK) return 0;
+  return align256(basis_update_workspace_bytes(rank, n_rows, dim));
+}
+
+int lowrank_basis_update(const void* basis, int32_t basis_dtype, const float* sigma, int32_t rank, const void* rows,
+                         int32_t n_rows, int32_t dim, int32_t rank_new, int32_t sweeps, void* basis_new,
+                         float* sigma_new, void* w, void* workspace, size_t workspace_bytes, void* stream) {
+  LR_GUARD_BEGIN
+  const char* msg = "";
+  int st = check_basis_update_args(rank, n_rows, dim, rank_new, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (basis_dtype != LR_F32 && basis_dtype != LR_BF16) return fail(LR_EINVAL, "basis_dtype must be LR_F32 or LR_BF16");
+  if (sweeps < 0 || sweeps > 64) return fail(LR_EINVAL, "sweeps must be in 0..64 (0 = default 10)");
+  if (!basis || !sigma || (n_rows > 0 && !rows) || !basis_new || !sigma_new || !w || !workspace)
+    return fail(LR_EINVAL, "basis, sigma, rows, basis_new, sigma_new, w and workspace must not be NULL");
+  if (!aligned(basis, 4) || !aligned(sigma, 4) || (rows && !aligned(rows, 2)) || !aligned(basis_new, 4) ||
+      !aligned(sigma_new, 4) || !aligned(w, 4) || !aligned(workspace, 256))
+    return fail(LR_EINVAL, "buffers must be 4-byte aligned (rows 2-byte), workspace 256-byte aligned");
+  if (workspace_bytes < lowrank_basis_update_workspace_size(rank, n_rows, dim))
+    return fail(LR_EWORKSPACE, "workspace too small");
+  hipError_t e = launch_basis_update(basis, basis_dtype == LR_F32, sigma, rank, rows, n_rows, dim, rank_new,
+                                     sweeps == 0 ? 10 : sweeps, basis_new, sigma_new, w, workspace,
+                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
   return LR_OK;
   LR_GUARD_END

@@ -91,34 +91,48 @@ struct AppendArgs {
   int D, rk, rv, ld_k, ld_v, latent, window, n_new, B;
 };
 
-// Projection + storage of every latent row this call creates.
-// grid (column chunks of 64 over max(rk, rv), 2 = {K, V}, B); 512 threads = 8 waves.
-// For each row: wave w accumulates z over input dims [w*D/8, (w+1)*D/8) for the chunk's 64
-// columns (lane = column; the loads of P are independent and coalesced, 32 in flight per
-// lane), the 8 partial sums are added in a fixed order through LDS and wave 0 stores the row.
-constexpr int kAppendWaves = 8;
+// One launch does the whole append: projection, storage, window ring and lengths.
+//
+// grid (nck + ncv, ceil(B / 16)): workgroup (x, y) owns latent columns 64c .. 64c + 63 of K (x < nck,
+// c = x) or of V (c = x - nck) for the 16 sequences 16y .. 16y + 15, and every row this call stores
+// for them. Per row index e (0 .. n_new - 1): the 16 sequences' source rows (the new token, or the
+// window token being evicted) are staged in LDS as the bf16 A operand, z [16 seq, 64 col] = X P on
+// the matrix cores (bf16 bases: 16x16x32 with float32 accumulation, wave w owning columns
+// 16w .. 16w + 15; float32 bases: the VALU, float32 throughout), and wave w stores the rows of
+// sequences 4w .. 4w + 3 (store_chunk: bf16 rounding, or int4 quantisation of the 2 groups).
+//
+// The window ring and the lengths may change only after every workgroup of a sequence has read
+// them (and the evicted ring slots). Each workgroup, once its reads of a sequence are done, adds
+// 1 << 24 to lat_len[b]: the word carries the arrival count in bits 24..30 while L stays in bits
+// 0..23 (t_cap < 2^24, so every reader masks it off). The workgroup that sees the count reach
+// gx - 1 is the last one: it writes the new tokens into the ring and the final lengths, which
+// also clears the count. So a call leaves the lengths clean, and no buffer needs clearing first.
+constexpr int kAppendSeqs = 16;       // sequences per workgroup (the matrix-core M)
+constexpr int kAppendCols = 64;       // latent columns per workgroup (4 waves x 16; 2 int4 groups)
+constexpr int kAppendK = 512;         // source-row chunk along D staged at a time
+constexpr int kAppendLdsX = kAppendK * 2 + 16;   // LDS row stride of a staged source chunk (bytes)
+constexpr unsigned kLenMask = 0x00FFFFFFu;
+constexpr unsigned kArrival = 1u << 24;
 
-template <typename PT>
-__global__ __launch_bounds__(kAppendWaves * 64) void lr_append_project(AppendArgs a) {
-  extern __shared__ float xs[];    // [D] source row as float, then [8][64] partial sums
-  const int kv = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ int clamp_len(int32_t raw, long long cap) {
+  const unsigned v = (unsigned)raw & kLenMask;
+  return (int)((long long)v > cap ? cap : (long long)v);
+}
+
+template <bool F32P>
+__global__ __launch_bounds__(256) void lr_append(AppendArgs a, int nck, int ncv) {
+  __shared__ __attribute__((aligned(16))) unsigned char xs[kAppendSeqs * kAppendLdsX];   // staged rows
+  __shared__ float zt[kAppendSeqs][kAppendCols];                                         // z tile
+  __shared__ int s_len[kAppendSeqs], s_win[kAppendSeqs], s_rows[kAppendSeqs], s_last[kAppendSeqs];
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gx = nck + ncv;
+  const int kv = (int)blockIdx.x < nck ? 0 : 1;
+  const int col0 = ((int)blockIdx.x - (kv ? nck : 0)) * kAppendCols;
   const int r = kv == 0 ? a.rk : a.rv;
-  const int col0 = blockIdx.x * 64;
-  if (col0 >= r) return;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  int L = a.lat_len[b];
-  L = L < 0 ? 0 : (L > a.t_cap ? (int)a.t_cap : L);
-  int wl = 0, n_rows;
-  if (a.window > 0) {
-    wl = a.win_len[b];
-    wl = wl < 0 ? 0 : (wl > a.window ? a.window : wl);
-    n_rows = wl + a.n_new - a.window;
-    n_rows = n_rows < 0 ? 0 : n_rows;
-  } else {
-    n_rows = a.n_new;
-  }
-  const PT* P = (const PT*)(kv == 0 ? a.pk : a.pv);
+  const int b0 = blockIdx.y * kAppendSeqs;
+  const int nseq = min(kAppendSeqs, a.B - b0);
+  const int D = a.D, W = a.window;
   const __bf16* xnew = kv == 0 ? a.k_new : a.v_new;
   const __bf16* win = kv == 0 ? a.kwin : a.vwin;
   unsigned char* zbase = kv == 0 ? a.zk : a.zv;
@@ -126,74 +140,204 @@ __global__ __launch_bounds__(kAppendWaves * 64) void lr_append_project(AppendArg
   const int ld = kv == 0 ? a.ld_k : a.ld_v;
   const int rb = row_bytes_of(a.latent, r, ld);
   const int G = (r + kGroup - 1) / kGroup;
-  const int col = col0 + lane;
-  const int dq = a.D / kAppendWaves;
-  float* x = xs;
-  float* zpart = xs + a.D;
+  const bool one_chunk = D <= kAppendK;
 
-  for (int e = 0; e < n_rows; ++e) {
-    const __bf16* src = (a.window > 0) ? win + ((size_t)b * a.window + (L + e) % a.window) * a.D
-                                       : xnew + ((size_t)b * a.n_new + e) * a.D;
-    __syncthreads();
-    for (int c = tid; c < a.D; c += kAppendWaves * 64) x[c] = (float)src[c];
-    __syncthreads();
-    float z = 0.f;
-    if (col < r) {
-      const PT* pc = P + (size_t)(wave * dq) * r + col;
-      const float* xw = x + wave * dq;
-      int c = 0;
-      for (; c + 32 <= dq; c += 32) {
-        float pv[32];
+  // ---- every load that does not depend on the lengths goes out first, with the lengths' own
+  // loads, so that the workgroup waits for one memory round trip instead of several in a row.
+  int32_t raw_len = 0, raw_win = 0;
+  if (tid < nseq) {
+    raw_len = a.lat_len[b0 + tid];
+    if (W > 0) raw_win = a.win_len[b0 + tid];
+  }
+  // P operand of this wave's 16 columns for one K chunk of up to 512 (bf16 bases). The projection
+  // is stored rank-major, pt[i][k] = P[k][i], so lane (li, lg) loads its 8 values
+  // pt[col0 + 16 wave + li][kc + 32 ks + 8 lg .. +7] as one 16-byte load (columns past the rank
+  // read as 0). With one chunk (D <= 512) it is loaded once for all row indices.
+  const int pcol = col0 + 16 * wave + li;
+  bf16x8 pop[F32P ? 1 : kAppendK / 32];
+  auto load_pop = [&](int kc, int nks) {
+    if constexpr (!F32P) {
+      const __bf16* pt = (const __bf16*)(kv == 0 ? a.pk : a.pv) + (size_t)(pcol < r ? pcol : r - 1) * D + kc + 8 * lg;
 #pragma unroll
-        for (int u = 0; u < 32; ++u) pv[u] = to_f32(pc[(size_t)(c + u) * r]);
-#pragma unroll
-        for (int u = 0; u < 32; ++u) z += xw[c + u] * pv[u];
+      for (int ks = 0; ks < kAppendK / 32; ++ks) {
+        pop[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        if (ks < nks && pcol < r) pop[ks] = *(const bf16x8*)(pt + 32 * ks);
       }
-      for (; c < dq; ++c) z += xw[c] * to_f32(pc[(size_t)c * r]);
     }
-    zpart[wave * 64 + lane] = z;
-    __syncthreads();
-    if (wave == 0) {
-      z = 0.f;
+  };
+  if (one_chunk) load_pop(0, D / 32);
+  // Source rows of one row index e and K chunk: item i = tid + 256 u is granule c of sequence sq
+  // (zeros for sequences without a row e). The new token's row (W == 0) does not depend on the
+  // lengths, the evicted window slot does.
+  constexpr int XV = kAppendSeqs * (kAppendK / 8) / 256;
+  u32x4 xv[XV];
+  auto load_x = [&](int e, int kc, int kw, bool from_new) {
 #pragma unroll
-      for (int w = 0; w < kAppendWaves; ++w) z += zpart[w * 64 + lane];
-      const long long row = (long long)L + e;
-      if (a.z_debug && col < r)
-        a.z_debug[((size_t)b * a.n_new + e) * (a.rk + a.rv) + (kv == 0 ? 0 : a.rk) + col] = z;
-      if (row < a.t_cap)
-        store_chunk(a.latent, z, lane, col0, r, zbase + ((size_t)b * a.t_cap + row) * rb,
-                    qbase ? qbase + ((size_t)b * a.t_cap + row) * G : nullptr);
+    for (int u = 0; u < XV; ++u) {
+      const int i = tid + 256 * u;
+      const int sq = i / (kw / 8), c = i - sq * (kw / 8);
+      xv[u] = u32x4{0u, 0u, 0u, 0u};
+      if (sq < nseq) {
+        const int b = b0 + sq;
+        if (from_new) {
+          if (e < a.n_new) xv[u] = *(const u32x4*)(xnew + ((size_t)b * a.n_new + e) * D + kc + c * 8);
+        } else if (e < s_rows[sq]) {
+          xv[u] = *(const u32x4*)(win + ((size_t)b * W + (s_len[sq] + e) % W) * D + kc + c * 8);
+        }
+      }
+    }
+  };
+  const bool pre_x = W == 0 && one_chunk;
+  if (pre_x) load_x(0, 0, D, true);
+  // A decode step (W > 0, one new token): the new rows the last workgroup of a sequence writes into
+  // the ring are loaded now too.
+  const bool pre_new = W > 0 && a.n_new == 1 && one_chunk;
+  u32x4 kn[XV], vn[XV];
+  if (pre_new) {
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+      const int i = tid + 256 * u;
+      const int sq = i / (D / 8), c = i - sq * (D / 8);
+      if (sq < nseq) {
+        kn[u] = *(const u32x4*)(a.k_new + (size_t)(b0 + sq) * D + c * 8);
+        vn[u] = *(const u32x4*)(a.v_new + (size_t)(b0 + sq) * D + c * 8);
+      }
     }
   }
-}
 
-// Window ring write and length update; runs after the projection kernel on the same stream.
-__global__ __launch_bounds__(256) void lr_append_finish(AppendArgs a) {
-  const int b = blockIdx.x;
-  int L = a.lat_len[b];
-  L = L < 0 ? 0 : (L > a.t_cap ? (int)a.t_cap : L);
-  if (a.window > 0) {
-    int wl = a.win_len[b];
-    wl = wl < 0 ? 0 : (wl > a.window ? a.window : wl);
-    const int vec = a.D / 8;
-    for (int i = threadIdx.x; i < a.n_new * vec; i += blockDim.x) {
-      const int t = i / vec, c = i - t * vec;
-      const int slot = (L + wl + t) % a.window;
-      const size_t dst = ((size_t)b * a.window + slot) * a.D + c * 8;
-      const size_t src = ((size_t)b * a.n_new + t) * a.D + c * 8;
-      *(u32x4*)(a.kwin + dst) = *(const u32x4*)(a.k_new + src);
-      *(u32x4*)(a.vwin + dst) = *(const u32x4*)(a.v_new + src);
+  if (tid < kAppendSeqs) {
+    int L = 0, wl = 0, rows = 0;
+    if (tid < nseq) {
+      L = clamp_len(raw_len, a.t_cap);
+      if (W > 0) {
+        wl = raw_win < 0 ? 0 : (raw_win > W ? W : raw_win);
+        rows = wl + a.n_new - W;
+        rows = rows < 0 ? 0 : rows;
+      } else {
+        rows = a.n_new;
+      }
     }
-    if (threadIdx.x == 0) {
-      int n_ev = wl + a.n_new - a.window;
-      n_ev = n_ev < 0 ? 0 : n_ev;
-      long long nl = (long long)L + n_ev;
+    s_len[tid] = L;
+    s_win[tid] = wl;
+    s_rows[tid] = rows;
+    s_last[tid] = 0;
+  }
+  __syncthreads();
+  int emax = 0;
+#pragma unroll
+  for (int sq = 0; sq < kAppendSeqs; ++sq) emax = max(emax, s_rows[sq]);
+
+  for (int e = 0; e < emax; ++e) {
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < D; kc += kAppendK) {
+      const int kw = min(kAppendK, D - kc);                    // a multiple of 128
+      if (!(pre_x && e == 0)) load_x(e, kc, kw, W == 0);
+#pragma unroll
+      for (int u = 0; u < XV; ++u) {
+        const int i = tid + 256 * u;
+        const int sq = i / (kw / 8), c = i - sq * (kw / 8);
+        if (sq < kAppendSeqs) *(u32x4*)(xs + sq * kAppendLdsX + c * 16) = xv[u];
+      }
+      if (!one_chunk) load_pop(kc, kw / 32);
+      __syncthreads();
+      if constexpr (!F32P) {
+        // C[seq 4 lg + i][col li] of this wave's 16 columns (two accumulation chains)
+        const unsigned char* xr = xs + li * kAppendLdsX + lg * 16;
+#pragma unroll
+        for (int ks = 0; ks < kAppendK / 32; ks += 2) {
+          if (ks < kw / 32) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xr + ks * 64), pop[ks], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xr + ks * 64 + 64), pop[ks + 1], c1, 0,
+                                                         0, 0);
+          }
+        }
+      } else {
+        // float32 bases: thread (column lane, sequences 4 wave .. 4 wave + 3), float32 throughout
+        const int col = col0 + lane;
+        const float* pt = (const float*)(kv == 0 ? a.pk : a.pv) + (size_t)(col < r ? col : r - 1) * D + kc;
+        for (int k = 0; k < kw; ++k) {
+          const float pv = pt[k];
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            acc[s4] += (float)*(const __bf16*)(xs + (4 * wave + s4) * kAppendLdsX + k * 2) * pv;
+        }
+      }
+      __syncthreads();                                         // xs is restaged
+    }
+    if constexpr (!F32P) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zt[4 * lg + i][16 * wave + li] = c0[i] + c1[i];
+    } else {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) zt[4 * wave + s4][lane] = col0 + lane < r ? acc[s4] : 0.f;
+    }
+    __syncthreads();
+    // store: wave w writes the rows of sequences 4w .. 4w + 3 (lane = column)
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int sq = 4 * wave + s4;
+      if (sq < nseq && e < s_rows[sq]) {                       // wave-uniform
+        const int b = b0 + sq;
+        const float z = zt[sq][lane];
+        const long long row = (long long)s_len[sq] + e;
+        if (a.z_debug && col0 + lane < r)
+          a.z_debug[((size_t)b * a.n_new + e) * (a.rk + a.rv) + (kv == 0 ? 0 : a.rk) + col0 + lane] = z;
+        if (row < a.t_cap)
+          store_chunk(a.latent, z, lane, col0, r, zbase + ((size_t)b * a.t_cap + row) * rb,
+                      qbase ? qbase + ((size_t)b * a.t_cap + row) * G : nullptr);
+      }
+    }
+    __syncthreads();                                           // zt is reused
+  }
+
+  // arrivals: this workgroup's reads of its sequences are done (the barrier above)
+  if (tid < nseq) {
+    const unsigned old = atomicAdd((unsigned*)&a.lat_len[b0 + tid], kArrival);
+    s_last[tid] = ((old >> 24) & 0x7Fu) == (unsigned)(gx - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  // the last workgroup of a sequence: new tokens into the ring, then the final lengths
+  if (W > 0) {
+    if (pre_new) {
+#pragma unroll
+      for (int u = 0; u < XV; ++u) {
+        const int i = tid + 256 * u;
+        const int sq = i / (D / 8), c = i - sq * (D / 8);
+        if (sq < nseq && s_last[sq]) {
+          const size_t dst = ((size_t)(b0 + sq) * W + (s_len[sq] + s_win[sq]) % W) * D + c * 8;
+          *(u32x4*)(a.kwin + dst) = kn[u];
+          *(u32x4*)(a.vwin + dst) = vn[u];
+        }
+      }
+    } else {
+      const int vec = D / 8;
+      for (int i = tid; i < kAppendSeqs * a.n_new * vec; i += 256) {
+        const int sq = i / (a.n_new * vec);
+        const int rest = i - sq * a.n_new * vec;
+        const int t = rest / vec, c = rest - t * vec;
+        if (sq < nseq && s_last[sq]) {
+          const int b = b0 + sq;
+          const int slot = (s_len[sq] + s_win[sq] + t) % W;
+          const size_t dst = ((size_t)b * W + slot) * D + c * 8;
+          const size_t src = ((size_t)b * a.n_new + t) * D + c * 8;
+          *(u32x4*)(a.kwin + dst) = *(const u32x4*)(a.k_new + src);
+          *(u32x4*)(a.vwin + dst) = *(const u32x4*)(a.v_new + src);
+        }
+      }
+    }
+  }
+  if (tid < nseq && s_last[tid]) {
+    const int b = b0 + tid;
+    const long long L = s_len[tid];
+    if (W > 0) {
+      const long long nl = L + s_rows[tid];
+      a.win_len[b] = s_win[tid] + a.n_new > W ? W : s_win[tid] + a.n_new;
       a.lat_len[b] = (int)(nl > a.t_cap ? a.t_cap : nl);
-      a.win_len[b] = wl + a.n_new > a.window ? a.window : wl + a.n_new;
+    } else {
+      const long long nl = L + a.n_new;
+      a.lat_len[b] = (int)(nl > a.t_cap ? a.t_cap : nl);
     }
-  } else if (threadIdx.x == 0) {
-    long long nl = (long long)L + a.n_new;
-    a.lat_len[b] = (int)(nl > a.t_cap ? a.t_cap : nl);
   }
 }
 
@@ -302,14 +446,10 @@ hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const voi
   a.window = p.window;
   a.n_new = p.n_new;
   a.B = p.B;
-  const int rmax = p.rk > p.rv ? p.rk : p.rv;
-  dim3 grid((rmax + 63) / 64, 2, p.B);
-  const size_t lds = (size_t)(p.D + kAppendWaves * 64) * sizeof(float);
-  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append_project<float>, grid, dim3(kAppendWaves * 64), lds, st, a);
-  else hipLaunchKernelGGL(lr_append_project<__bf16>, grid, dim3(kAppendWaves * 64), lds, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lr_append_finish, dim3(p.B), dim3(256), 0, st, a);
+  const int nck = (p.rk + kAppendCols - 1) / kAppendCols, ncv = (p.rv + kAppendCols - 1) / kAppendCols;
+  const dim3 grid(nck + ncv, (p.B + kAppendSeqs - 1) / kAppendSeqs);
+  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append<true>, grid, dim3(256), 0, st, a, nck, ncv);
+  else hipLaunchKernelGGL(lr_append<false>, grid, dim3(256), 0, st, a, nck, ncv);
   return hipGetLastError();
 }
 

@@ -14,6 +14,9 @@ constexpr int kHeadsPad = 32;       // query heads padded for the 16x16 matrix-c
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kLdsPad = 128;        // slack after the ring for operand over-reads
 constexpr int kMaxSplit = 4096;     // token ranges per sequence (bounds the combine's LDS)
+// Latent rows per sequence: lengths stay below 2^24, so append can carry an arrival count in the
+// high bits of the length words while it runs.
+constexpr int64_t kMaxTCap = ((int64_t)1 << 24) - 1;
 
 // Compile-time bounds the decode kernel is instantiated for: KS K steps of 32 latent indices
 // for the keys, RB value blocks of 16 per wave (two waves share the value blocks, so
@@ -173,6 +176,11 @@ size_t svd_workspace_bytes(int n, int D);
 size_t svd_workspace_stride(int n, int D);   // per matrix of a batch (256-byte multiple)
 hipError_t launch_sens_svd(const void* x, const float* w, int n_mat, int n, int D, int rank, int sweeps, void* basis,
                            int basis_f32, float* sigma, void* ws, hipStream_t st);
+
+size_t basis_update_workspace_bytes(int r, int n, int D);
+hipError_t launch_basis_update(const void* basis, int f32, const float* sigma, int r, const void* rows, int n, int D,
+                               int r_new, int sweeps, void* basis_new, float* sigma_new, void* w, void* ws,
+                               hipStream_t st);
 
 hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, long long n_take, int r_min,
                                 int g, int nb, int32_t* ranks, void* ws, hipStream_t st);

@@ -183,6 +183,12 @@ def down_projection(basis_stored: np.ndarray) -> np.ndarray:
     return np.linalg.pinv(np.asarray(basis_stored, dtype=np.float64))
 
 
+def projection_storage(p: np.ndarray, dtype) -> torch.Tensor:
+    """The library's layout of a down-projection P [D, rank]: rank-major [rank][D] (row i = P[:, i]),
+    rounded once to ``dtype`` (a torch dtype)."""
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(p, np.float64).T, dtype=np.float32)).to(dtype).contiguous()
+
+
 def gen_chunk(cfg: Config, layer: int, n_new: int, q_scale: float = 1.0, rank: Optional[int] = None):
     """A prefill chunk: q [B, n_new, Hq, d] ~ N(0, 1/d) * q_scale, and exact k, v rows
     [B, n_new, D] ~ N(0, H_r / D) (the variance of a reconstructed history row, as for the

@@ -11,7 +11,7 @@ import torch
 
 import rank_kv_cache_lowrank_amd as lr
 
-from . import LayerInputs, down_projection
+from . import LayerInputs, down_projection, projection_storage
 
 
 def device_layer(li: LayerInputs, device="cuda", with_proj: bool = False):
@@ -27,8 +27,8 @@ def device_layer(li: LayerInputs, device="cuda", with_proj: bool = False):
     pk = pv = None
     if with_proj:
         dt = torch.float32 if cfg.latent == "f32" else torch.bfloat16
-        pk = torch.from_numpy(down_projection(li.bk.double().numpy())).to(dt).to(device).contiguous()
-        pv = torch.from_numpy(down_projection(li.bv.double().numpy())).to(dt).to(device).contiguous()
+        pk = projection_storage(down_projection(li.bk.double().numpy()), dt).to(device)
+        pv = projection_storage(down_projection(li.bv.double().numpy()), dt).to(device)
     if cfg.latent in ("f32", "bf16"):
         cache = lr.Cache(li.zk.to(device), li.zv.to(device), li.bk.to(device), li.bv.to(device), lat_len,
                          li.t_cap, li.ld_k, li.ld_v, pk=pk, pv=pv, kwin=kw, vwin=vw, win_len=win_len)

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert lr.lowrank_abi_version() == 1
+    assert lr.lowrank_abi_version() == 2
 
 
 # The validation tests hand the library addresses that map nothing; every case is rejected before
@@ -299,3 +299,33 @@ def test_sens_svd_batched_workspace_checks():
     assert lib.lowrank_sens_svd_batched(1 << 20, 1 << 21, 4, 2048, 256, 64, 0, 1 << 22, L.LR_F32, 1 << 23,
                                         (1 << 24) + 16, ws, None) == L.LR_EINVAL   # workspace alignment
     assert lr.lowrank_sens_svd_batched_workspace_size(70000, 2048, 256) == 0
+
+
+def test_basis_update_workspace_size_and_rejections():
+    assert lr.lowrank_basis_update_workspace_size(256, 128, 512) > 0
+    assert lr.lowrank_basis_update_workspace_size(256, 128, 500) == 0       # dim not a multiple of 64
+    assert lr.lowrank_basis_update_workspace_size(0, 128, 512) == 0
+    assert lr.lowrank_basis_update_workspace_size(600, 0, 512) == 0         # rank > dim
+    assert lr.lowrank_basis_update_workspace_size(8, -1, 512) == 0
+
+
+@host_only
+@pytest.mark.parametrize("kw,code", [
+    (dict(dim=500), L.LR_EUNSUPPORTED),
+    (dict(rank_new=0), L.LR_EINVAL),
+    (dict(rank_new=385), L.LR_EINVAL),                    # > rank + n_rows
+    (dict(basis_dtype=2), L.LR_EINVAL),
+    (dict(basis=None), L.LR_EINVAL),
+    (dict(ws_bytes=1024), L.LR_EWORKSPACE),
+    (dict(sweeps=65), L.LR_EINVAL),
+])
+def test_basis_update_rejects_invalid_arguments(kw, code):
+    lib = lr.load()
+    a = dict(basis=1 << 20, basis_dtype=L.LR_BF16, sigma=1 << 21, rank=256, rows=1 << 22, n_rows=128, dim=512,
+             rank_new=256, sweeps=0, basis_new=1 << 23, sigma_new=1 << 24, w=1 << 25, ws=1 << 26, ws_bytes=1 << 40)
+    a.update(kw)
+    rc = lib.lowrank_basis_update(a["basis"], a["basis_dtype"], a["sigma"], a["rank"], a["rows"], a["n_rows"],
+                                  a["dim"], a["rank_new"], a["sweeps"], a["basis_new"], a["sigma_new"], a["w"],
+                                  a["ws"], a["ws_bytes"], None)
+    assert rc == code
+    assert lr.lowrank_last_error() != ""

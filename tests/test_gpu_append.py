@@ -122,8 +122,8 @@ def test_store_then_dequant_is_bit_exact(latent, rank):
 def _run_append(latent, rk, rv, P_k, P_v, xk, xv, window=0, lat0=0, win0=0, t_cap=64, with_debug=True):
     B, n_new, D = xk.shape
     dt = torch.float32 if latent == "f32" else torch.bfloat16
-    pk = torch.from_numpy(P_k.astype(np.float32)).to(dt).to(DEV).contiguous()
-    pv = torch.from_numpy(P_v.astype(np.float32)).to(dt).to(DEV).contiguous()
+    pk = synth.projection_storage(P_k, dt).to(DEV)
+    pv = synth.projection_storage(P_v, dt).to(DEV)
     model, cache = make_cache(latent, B, t_cap, rk, rv, window, pk, pv, D, lat0, win0)
     zdbg = torch.full((B, n_new, rk + rv), float("nan"), device=DEV) if with_debug else None
     lr.lowrank_kv_append(model, 0, cache, torch.from_numpy(xk).to(torch.bfloat16).to(DEV),
@@ -273,8 +273,8 @@ def test_append_bf16_general_projection():
     xk = synth.to_storage(synth.gen_new_tokens(big, "k", 0, n_new), "bf16").float().numpy()
     xv = synth.to_storage(synth.gen_new_tokens(big, "v", 0, n_new), "bf16").float().numpy()
     dt = torch.bfloat16
-    pk = torch.from_numpy(Pk.astype(np.float32)).to(dt).to(DEV).contiguous()
-    pv = torch.from_numpy(Pv.astype(np.float32)).to(dt).to(DEV).contiguous()
+    pk = synth.projection_storage(Pk, dt).to(DEV)
+    pv = synth.projection_storage(Pv, dt).to(DEV)
     model, cache = make_cache("bf16", B, t_cap, r, r, 0, pk, pv, lat0=lat0, sentinel=True)
     zdbg = torch.full((B, n_new, 2 * r), float("nan"), device=DEV)
     lr.lowrank_kv_append(model, 0, cache, torch.from_numpy(xk).to(dt).to(DEV),
@@ -304,8 +304,8 @@ def test_window_eviction_general_projection(latent):
     calls = (1, 3, 2, 1, 3, 1)
     Pk, Pv = _pinv_bf16(cfg, "k", r), _pinv_bf16(cfg, "v", r)
     dt = torch.bfloat16
-    pk = torch.from_numpy(Pk.astype(np.float32)).to(dt).to(DEV).contiguous()
-    pv = torch.from_numpy(Pv.astype(np.float32)).to(dt).to(DEV).contiguous()
+    pk = synth.projection_storage(Pk, dt).to(DEV)
+    pv = synth.projection_storage(Pv, dt).to(DEV)
     model, cache = make_cache(latent, B, t_cap, r, r, W, pk, pv, sentinel=True)
     rng = np.random.default_rng(11)
     stream_k = torch.from_numpy(rng.standard_normal((B, sum(calls), D)).astype(np.float32)).to(dt)
