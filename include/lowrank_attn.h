@@ -225,6 +225,19 @@ int lowrank_kv_append(const lr_model_desc* model, int32_t layer, const lr_layer_
                       float* z_debug, void* stream);
 
 /*
+ * One decode step of one layer: lowrank_kv_append of one new token per sequence (k_new, v_new
+ * [B][1][D] bfloat16, no z_debug) followed by lowrank_attn_decode for the query q, with the same
+ * results as those two calls in that order. max_lat_len bounds lat_len[b] after the append;
+ * workspace as for lowrank_attn_decode. Fewer launches: for bf16 queries the append and the query
+ * fold share one launch (the fold needs only q and the key basis), then the latent kernel, then
+ * the combine. Errors: those of both calls, checked before any launch.
+ */
+int lowrank_decode_step(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
+                        int32_t batch, const void* k_new, const void* v_new, const void* q, void* out,
+                        int32_t out_dtype, int32_t max_lat_len, void* workspace, size_t workspace_bytes,
+                        const lr_decode_opts* opts, void* stream);
+
+/*
  * Bulk store of given latent rows (e.g. a prompt compressed elsewhere): rows
  * [row0, row0 + n_rows) of every sequence receive zk_rows [B][n_rows][rank_k] and zv_rows
  * [B][n_rows][rank_v] (float32), converted to the cache dtype exactly as append stores z.

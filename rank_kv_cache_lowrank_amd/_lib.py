@@ -26,7 +26,7 @@ EXPORTS = ("lowrank_attn_decode_workspace_size", "lowrank_attn_decode", "lowrank
            "lowrank_attn_prefill", "lowrank_sens_svd_workspace_size", "lowrank_sens_svd",
            "lowrank_sens_svd_batched_workspace_size", "lowrank_sens_svd_batched",
            "lowrank_rank_allocate_workspace_size", "lowrank_rank_allocate",
-           "lowrank_kv_append",
+           "lowrank_kv_append", "lowrank_decode_step",
            "lowrank_kv_store", "lowrank_kv_dequant", "lowrank_kv_rebase", "lowrank_basis_update_workspace_size",
            "lowrank_basis_update", "lowrank_last_error",
            "lowrank_abi_version")
@@ -103,6 +103,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lowrank_kv_append.restype = c_int32
     lib.lowrank_kv_append.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                       c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.lowrank_decode_step.restype = c_int32
+    lib.lowrank_decode_step.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
+                                        POINTER(lr_decode_opts), c_void_p]
     lib.lowrank_kv_store.restype = c_int32
     lib.lowrank_kv_store.argtypes = [POINTER(lr_model_desc), c_int32, POINTER(lr_layer_cache), c_int32,
                                      c_int64, c_int64, c_void_p, c_void_p, c_void_p]
@@ -310,6 +314,17 @@ def lowrank_kv_append(model: Model, layer: int, cache: Cache, k_new: torch.Tenso
                       z_debug: Optional[torch.Tensor] = None, stream=None) -> None:
     _check(load().lowrank_kv_append(ctypes.byref(model.desc), layer, ctypes.byref(cache.c), k_new.shape[0],
                                     k_new.shape[1], _ptr(k_new), _ptr(v_new), _ptr(z_debug), _stream(stream)))
+
+
+def lowrank_decode_step(model: Model, layer: int, cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor,
+                        q: torch.Tensor, out: torch.Tensor, max_lat_len: int, workspace: torch.Tensor,
+                        nsplit: int = 0, stream=None, events=None) -> None:
+    """lowrank_kv_append of one token per sequence (k_new, v_new [B][1][D]) then lowrank_attn_decode."""
+    out_dtype = LR_F32 if out.dtype == torch.float32 else LR_BF16
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().lowrank_decode_step(ctypes.byref(model.desc), layer, ctypes.byref(cache.c), q.shape[0],
+                                      _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), out_dtype, max_lat_len,
+                                      _ptr(workspace), ws_bytes, _opts(nsplit, events), _stream(stream)))
 
 
 def lowrank_kv_store(model: Model, layer: int, cache: Cache, row0: int, zk_rows: torch.Tensor,

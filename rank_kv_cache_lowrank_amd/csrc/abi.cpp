@@ -252,31 +252,41 @@ size_t lowrank_attn_decode_workspace_size(const lr_model_desc* model, int32_t la
   }
 }
 
+// Everything lowrank_attn_decode checks before its workspace: the plan, the cache, the query and
+// output buffers, the LDS layout.
+static int plan_decode_call(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache, int32_t batch,
+                            int32_t max_lat_len, const void* q, const void* out, int32_t out_dtype,
+                            const lr_decode_opts* opts, DecodePlan* p, const char** msg) {
+  int st = plan_decode(model, layer, batch, max_lat_len, opts, p, msg);
+  if (st != LR_OK) return st;
+  st = check_cache_common(model, cache, p->rk, p->rv, msg);
+  if (st != LR_OK) return st;
+  if ((int64_t)max_lat_len > cache->t_cap) return *msg = "max_lat_len must be <= t_cap", LR_EINVAL;
+  if (!q || !out) return *msg = "q and out must not be NULL", LR_EINVAL;
+  if (!cache->bk || !cache->bv) return *msg = "bases bk/bv must not be NULL", LR_EINVAL;
+  if (!aligned(cache->bk, 16) || !aligned(cache->bv, 16) || !aligned(q, 16))
+    return *msg = "q and the bases must be 16-byte aligned", LR_EINVAL;
+  if (out_dtype != LR_F32 && out_dtype != LR_BF16) return *msg = "out_dtype must be LR_F32 or LR_BF16", LR_EINVAL;
+  if (p->latent == LR_I4G32 && (!aligned(cache->zk_qp, 16) || !aligned(cache->zv_qp, 16)))
+    return *msg = "int4 decode needs 16-byte aligned scale/zero buffers", LR_EINVAL;
+  st = plan_lds(p, cache->ld_k, cache->ld_v, msg);
+  if (st != LR_OK) return st;
+  p->t_cap = cache->t_cap;
+  return LR_OK;
+}
+
 int lowrank_attn_decode(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
                         int32_t batch, int32_t max_lat_len, const void* q, void* out, int32_t out_dtype,
                         void* workspace, size_t workspace_bytes, const lr_decode_opts* opts, void* stream) {
   LR_GUARD_BEGIN
   DecodePlan p;
   const char* msg = "";
-  int st = plan_decode(model, layer, batch, max_lat_len, opts, &p, &msg);
-  if (st != LR_OK) return fail(st, msg);
-  st = check_cache_common(model, cache, p.rk, p.rv, &msg);
-  if (st != LR_OK) return fail(st, msg);
-  if ((int64_t)max_lat_len > cache->t_cap) return fail(LR_EINVAL, "max_lat_len must be <= t_cap");
-  if (!q || !out) return fail(LR_EINVAL, "q and out must not be NULL");
-  if (!cache->bk || !cache->bv) return fail(LR_EINVAL, "bases bk/bv must not be NULL");
-  if (!aligned(cache->bk, 16) || !aligned(cache->bv, 16) || !aligned(q, 16))
-    return fail(LR_EINVAL, "q and the bases must be 16-byte aligned");
-  if (out_dtype != LR_F32 && out_dtype != LR_BF16) return fail(LR_EINVAL, "out_dtype must be LR_F32 or LR_BF16");
-  if (p.latent == LR_I4G32 && (!aligned(cache->zk_qp, 16) || !aligned(cache->zv_qp, 16)))
-    return fail(LR_EINVAL, "int4 decode needs 16-byte aligned scale/zero buffers");
-  st = plan_lds(&p, cache->ld_k, cache->ld_v, &msg);
+  int st = plan_decode_call(model, layer, cache, batch, max_lat_len, q, out, out_dtype, opts, &p, &msg);
   if (st != LR_OK) return fail(st, msg);
   if (!workspace) return fail(LR_EINVAL, "workspace must not be NULL");
   if (!aligned(workspace, 256)) return fail(LR_EINVAL, "workspace must be 256-byte aligned");
   if (workspace_bytes < p.ws_bytes) return fail(LR_EWORKSPACE, "workspace too small");
   if (batch == 0) return LR_OK;
-  p.t_cap = cache->t_cap;
   hipError_t e = launch_decode(p, cache, q, out, out_dtype, workspace, (hipStream_t)stream,
                                opts ? (hipEvent_t)opts->event_begin : nullptr,
                                opts ? (hipEvent_t)opts->event_end : nullptr);
@@ -291,19 +301,7 @@ int lowrank_attn_decode_noalloc(const lr_model_desc* model, int32_t layer, const
   LR_GUARD_BEGIN
   DecodePlan p;
   const char* msg = "";
-  int st = plan_decode(model, layer, batch, max_lat_len, opts, &p, &msg);
-  if (st != LR_OK) return fail(st, msg);
-  st = check_cache_common(model, cache, p.rk, p.rv, &msg);
-  if (st != LR_OK) return fail(st, msg);
-  if ((int64_t)max_lat_len > cache->t_cap) return fail(LR_EINVAL, "max_lat_len must be <= t_cap");
-  if (!q || !out) return fail(LR_EINVAL, "q and out must not be NULL");
-  if (!cache->bk || !cache->bv) return fail(LR_EINVAL, "bases bk/bv must not be NULL");
-  if (!aligned(cache->bk, 16) || !aligned(cache->bv, 16) || !aligned(q, 16))
-    return fail(LR_EINVAL, "q and the bases must be 16-byte aligned");
-  if (out_dtype != LR_F32 && out_dtype != LR_BF16) return fail(LR_EINVAL, "out_dtype must be LR_F32 or LR_BF16");
-  if (p.latent == LR_I4G32 && (!aligned(cache->zk_qp, 16) || !aligned(cache->zv_qp, 16)))
-    return fail(LR_EINVAL, "int4 decode needs 16-byte aligned scale/zero buffers");
-  st = plan_lds(&p, cache->ld_k, cache->ld_v, &msg);
+  int st = plan_decode_call(model, layer, cache, batch, max_lat_len, q, out, out_dtype, opts, &p, &msg);
   if (st != LR_OK) return fail(st, msg);
   if (p.ws_bytes > kNoAllocScratchBytes)
     return fail(LR_EWORKSPACE, "this decode needs more workspace than the library's scratch array holds "
@@ -312,7 +310,6 @@ int lowrank_attn_decode_noalloc(const lr_model_desc* model, int32_t layer, const
   void* ws = nullptr;
   hipError_t e = noalloc_scratch(&ws);
   if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
-  p.t_cap = cache->t_cap;
   e = launch_decode(p, cache, q, out, out_dtype, ws, (hipStream_t)stream,
                     opts ? (hipEvent_t)opts->event_begin : nullptr, opts ? (hipEvent_t)opts->event_end : nullptr);
   if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
@@ -405,6 +402,35 @@ int lowrank_kv_append(const lr_model_desc* model, int32_t layer, const lr_layer_
   if (batch == 0 || n_new == 0) return LR_OK;
   p.n_new = n_new;
   hipError_t e = launch_append(p, cache, k_new, v_new, z_debug, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
+  return LR_OK;
+  LR_GUARD_END
+}
+
+int lowrank_decode_step(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache, int32_t batch,
+                        const void* k_new, const void* v_new, const void* q, void* out, int32_t out_dtype,
+                        int32_t max_lat_len, void* workspace, size_t workspace_bytes, const lr_decode_opts* opts,
+                        void* stream) {
+  LR_GUARD_BEGIN
+  DecodePlan p;
+  const char* msg = "";
+  int st = plan_decode_call(model, layer, cache, batch, max_lat_len, q, out, out_dtype, opts, &p, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  AppendPlan ap;
+  st = plan_append(model, layer, cache, batch, &ap, &msg);
+  if (st != LR_OK) return fail(st, msg);
+  if (!k_new || !v_new) return fail(LR_EINVAL, "k_new/v_new must not be NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(LR_EINVAL, "k_new/v_new must be 16-byte aligned");
+  if (!cache->pk || !cache->pv) return fail(LR_EINVAL, "append needs the down-projections pk/pv");
+  if (!aligned(cache->pk, 16) || !aligned(cache->pv, 16)) return fail(LR_EINVAL, "pk/pv must be 16-byte aligned");
+  if (!workspace) return fail(LR_EINVAL, "workspace must not be NULL");
+  if (!aligned(workspace, 256)) return fail(LR_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < p.ws_bytes) return fail(LR_EWORKSPACE, "workspace too small");
+  if (batch == 0) return LR_OK;
+  ap.n_new = 1;
+  hipError_t e = launch_decode_step(ap, p, cache, k_new, v_new, q, out, out_dtype, workspace, (hipStream_t)stream,
+                                    opts ? (hipEvent_t)opts->event_begin : nullptr,
+                                    opts ? (hipEvent_t)opts->event_end : nullptr);
   if (e != hipSuccess) return fail(LR_EHIP, hipGetErrorString(e));
   return LR_OK;
   LR_GUARD_END

@@ -12,6 +12,7 @@
 //   zero16 = f16(min), scale16 = f16(f32(max - min) / 15), code = clamp(rint((z - zero)/scale))
 // every step one IEEE float32/float16 operation, so results are reproducible bit for bit.
 #include "device_common.h"
+#include "fold.h"
 #include "internal.h"
 
 #include <math.h>
@@ -120,17 +121,17 @@ __device__ __forceinline__ int clamp_len(int32_t raw, long long cap) {
 }
 
 template <bool F32P>
-__global__ __launch_bounds__(256) void lr_append(AppendArgs a, int nck, int ncv) {
+__device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int ncv, int bx, int by) {
   __shared__ __attribute__((aligned(16))) unsigned char xs[kAppendSeqs * kAppendLdsX];   // staged rows
   __shared__ float zt[kAppendSeqs][kAppendCols];                                         // z tile
   __shared__ int s_len[kAppendSeqs], s_win[kAppendSeqs], s_rows[kAppendSeqs], s_last[kAppendSeqs];
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gx = nck + ncv;
-  const int kv = (int)blockIdx.x < nck ? 0 : 1;
-  const int col0 = ((int)blockIdx.x - (kv ? nck : 0)) * kAppendCols;
+  const int kv = bx < nck ? 0 : 1;
+  const int col0 = (bx - (kv ? nck : 0)) * kAppendCols;
   const int r = kv == 0 ? a.rk : a.rv;
-  const int b0 = blockIdx.y * kAppendSeqs;
+  const int b0 = by * kAppendSeqs;
   const int nseq = min(kAppendSeqs, a.B - b0);
   const int D = a.D, W = a.window;
   const __bf16* xnew = kv == 0 ? a.k_new : a.v_new;
@@ -341,6 +342,26 @@ __global__ __launch_bounds__(256) void lr_append(AppendArgs a, int nck, int ncv)
   }
 }
 
+template <bool F32P>
+__global__ __launch_bounds__(256) void lr_append(AppendArgs a, int nck, int ncv) {
+  append_body<F32P>(a, nck, ncv, blockIdx.x, blockIdx.y);
+}
+
+// A decode step's first launch: the append's workgroups [0, nck + ncv) x ceil(B / 16) (as lr_append,
+// flattened) and the fold's workgroups after them. The fold reads only the query and the key basis,
+// so it does not depend on the append (the decode step's window is attended in the combine).
+template <bool F32OUT>
+__global__ __launch_bounds__(256) void lr_step_front(AppendArgs a, int nck, int ncv, int n_append, FoldArgs f,
+                                                     int nfx, int nfy) {
+  const int x = blockIdx.x;
+  if (x < n_append) {
+    append_body<false>(a, nck, ncv, x % (nck + ncv), x / (nck + ncv));
+  } else {
+    const int y = x - n_append;
+    fold_body<F32OUT>(f, y % nfx, (y / nfx) % nfy, y / (nfx * nfy));
+  }
+}
+
 // Bulk store: rows [row0, row0 + n_rows) from float32 z.
 // grid (ceil(n_rows / 4), 2, B); wave w handles one row, looping over 64-column chunks.
 struct StoreArgs {
@@ -420,9 +441,8 @@ __global__ __launch_bounds__(256) void lr_dequant(DequantArgs a) {
   }
 }
 
-hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const void* k_new,
-                         const void* v_new, float* z_debug, hipStream_t st) {
-  AppendArgs a;
+static void append_args(const AppendPlan& p, const lr_layer_cache* c, const void* k_new, const void* v_new,
+                        float* z_debug, AppendArgs& a) {
   a.k_new = (const __bf16*)k_new;
   a.v_new = (const __bf16*)v_new;
   a.pk = c->pk;
@@ -446,10 +466,28 @@ hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const voi
   a.window = p.window;
   a.n_new = p.n_new;
   a.B = p.B;
+}
+
+hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const void* k_new,
+                         const void* v_new, float* z_debug, hipStream_t st) {
+  AppendArgs a;
+  append_args(p, c, k_new, v_new, z_debug, a);
   const int nck = (p.rk + kAppendCols - 1) / kAppendCols, ncv = (p.rv + kAppendCols - 1) / kAppendCols;
   const dim3 grid(nck + ncv, (p.B + kAppendSeqs - 1) / kAppendSeqs);
   if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append<true>, grid, dim3(256), 0, st, a, nck, ncv);
   else hipLaunchKernelGGL(lr_append<false>, grid, dim3(256), 0, st, a, nck, ncv);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_front(const AppendPlan& p, const lr_layer_cache* c, const void* k_new, const void* v_new,
+                             const FoldArgs& f, int nfx, int nfy, int nfold, bool i4, hipStream_t st) {
+  AppendArgs a;
+  append_args(p, c, k_new, v_new, nullptr, a);
+  const int nck = (p.rk + kAppendCols - 1) / kAppendCols, ncv = (p.rv + kAppendCols - 1) / kAppendCols;
+  const int n_append = (nck + ncv) * ((p.B + kAppendSeqs - 1) / kAppendSeqs);
+  const dim3 grid(n_append + nfold);
+  if (i4) hipLaunchKernelGGL(lr_step_front<true>, grid, dim3(256), 0, st, a, nck, ncv, n_append, f, nfx, nfy);
+  else hipLaunchKernelGGL(lr_step_front<false>, grid, dim3(256), 0, st, a, nck, ncv, n_append, f, nfx, nfy);
   return hipGetLastError();
 }
 

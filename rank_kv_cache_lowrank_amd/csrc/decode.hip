@@ -25,6 +25,7 @@
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
+#include "fold.h"
 #include "internal.h"
 
 #include <math.h>
@@ -63,9 +64,6 @@ struct DecodeArgs {
   const __bf16* vchunk;
 };
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-}
 
 // ---------------------------------------------------------------------------------------------
 // Matrix-core operands from the LDS tile.
@@ -161,8 +159,6 @@ __device__ __forceinline__ u32x4 dequant8_f16(unsigned w, f16x2 s2, f16x2 z2, un
   return o;
 }
 
-// Position of latent index k inside a dequantised row (the 8-block order above).
-__device__ __forceinline__ int i4_pos(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
 // Value operand through the gfx950 transpose read: within each 16-lane group g, lane j's element
 // e comes from the address given by lane 16g + 4e + j/4, at element offset j%4. Lane
@@ -1001,7 +997,6 @@ __device__ __forceinline__ void load8<float>(const float* p, float* out) {
   for (int e = 0; e < 4; ++e) { out[e] = v0[e]; out[4 + e] = v1[e]; }
 }
 
-constexpr int kFoldD = 128;     // head_dim handled by the fold (validated on the host)
 
 template <typename T>
 __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T* __restrict__ bk,
@@ -1037,227 +1032,9 @@ __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T*
     for (int j = Hq + hs; j < kHeadsPad; j += 4) out[(size_t)j * rk_pad] = (__bf16)0.f;
 }
 
-// ---------------------------------------------------------------------------------------------
-// Fold on the matrix cores for bf16 q and Bk: one wave per (16-column block of latent indices k,
-// KV head g, nq consecutive query sequences; the Bk operand is loaded once for all of them).
-// C[h, k] = q[b, g*grp + h, :] . Bk[k, g*d : g*d+d] over d = 128 in four 16x16x32 bf16 steps
-// (A = 16 query heads of the group, zero past grp; B = Bk^T; C row h = 4*lg + i, column
-// k = lane % 16), scaled by sm_scale * log2 e.
-// F32OUT (int4 latents): float32 output at the dequantised tiles' block order; the decode
-// kernel picks each head's power-of-two scale and rounds to fp16. Else bf16 output.
-// ---------------------------------------------------------------------------------------------
-struct FoldArgs {
-  const __bf16* q;
-  const __bf16* bk;
-  void* qt;
-  int Hq, Hkv, D, rk, rk_pad;
-  float scale;
-  int nseq, nq;
-};
-
-template <bool F32OUT>
-__device__ __forceinline__ void fold_body(const FoldArgs& f, int bx, int by, int bz) {
-  const __bf16* __restrict__ q = f.q;
-  const __bf16* __restrict__ bk = f.bk;
-  void* __restrict__ qt = f.qt;
-  const int Hq = f.Hq, Hkv = f.Hkv, D = f.D, rk = f.rk, rk_pad = f.rk_pad, nseq = f.nseq, nq = f.nq;
-  const float scale = f.scale;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 4, li = lane & 15;
-  const int blk = bx * 4 + wave;
-  const int g = by;
-  const int grp = Hq / Hkv;
-  if (blk >= (rk_pad >> 4)) return;
-  const int k = blk * 16 + li;
-  bf16x8 bop[4];
-  {
-    const __bf16* brow = bk + (size_t)k * D + g * kFoldD + lg * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) bop[ks] = k < rk ? *(const bf16x8*)(brow + ks * 32) : zero_bf16x8();
-  }
-  const int pos = F32OUT ? i4_pos(k) : k;
-  for (int b = bz * nq; b < min(nseq, (bz + 1) * nq); ++b) {
-  for (int h0 = 0; h0 < grp; h0 += 16) {
-    const int hl = h0 + li;
-    const __bf16* qrow = q + ((size_t)b * Hq + g * grp + hl) * kFoldD + lg * 8;
-    bf16x8 aop[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) aop[ks] = hl < grp ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ks], bop[ks], c, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = h0 + 4 * lg + i;
-      if (h < grp) {
-        const size_t o = ((size_t)b * kHeadsPad + g * grp + h) * rk_pad + pos;
-        if constexpr (F32OUT) ((float*)qt)[o] = c[i] * scale;
-        else ((__bf16*)qt)[o] = (__bf16)(c[i] * scale);
-      }
-    }
-  }
-  if (g == 0) {   // query heads past Hq: zero rows
-    for (int h = Hq + lg; h < kHeadsPad; h += 4) {
-      const size_t o = ((size_t)b * kHeadsPad + h) * rk_pad + k;
-      if constexpr (F32OUT) ((float*)qt)[o] = 0.f;
-      else ((__bf16*)qt)[o] = (__bf16)0.f;
-    }
-  }
-  }
-}
-
-
 template <bool F32OUT>
 __global__ __launch_bounds__(256) void lr_fold_mfma(FoldArgs f) {
   fold_body<F32OUT>(f, blockIdx.x, blockIdx.y, blockIdx.z);
-}
-
-// ---------------------------------------------------------------------------------------------
-// Exact keys of a decode step: one query token per sequence and no chunk rows (the new token is
-// already a window slot). One workgroup per (sequence, KV head) for its grp <= 16 heads. Wave w
-// takes the 16-key tiles w, w + 4, ... of the live window slots and stages each one itself (a
-// wave's LDS writes and reads stay in order), and the four waves' (O, m, l) are merged through
-// LDS. (The prefill's exact-keys kernel would give every key to the one wave that holds a decode
-// step's rows.)
-// ---------------------------------------------------------------------------------------------
-constexpr int kExdKeys = 16;
-__device__ __forceinline__ void exact_decode_body(const ExactArgs& a, int blk) {
-  __shared__ __attribute__((aligned(16))) unsigned char kt[4][kExdKeys * kExSK];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[4][kExdKeys * kExSV];
-  __shared__ float mrg_ml[4][2][16];
-  __shared__ f32x4 mrg_o[3][kExD / 16][64];
-  const int grp = a.Hq / a.Hkv;
-  const int g = blk % a.Hkv;
-  const int b = blk / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool rvalid = li < grp;
-  int L = a.lat_len[b];
-  L = L < 0 ? 0 : L;
-  int wl = a.W > 0 ? a.win_len[b] : 0;
-  wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
-
-  // q of this lane's head as the B operand: d indices 32 ks + 8 lg .. +7
-  bf16x8 qop[4];
-  {
-    const __bf16* qr = a.q + ((size_t)b * a.Hq + g * grp + (rvalid ? li : 0)) * kExD + lg * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qop[ks] = rvalid ? *(const bf16x8*)(qr + ks * 32) : zero_bf16x8();
-  }
-  float m = -INFINITY, lsum = 0.f;
-  f32x4 acc[kExD / 16];
-#pragma unroll
-  for (int j = 0; j < kExD / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  unsigned char* kw = kt[wave];
-  unsigned char* vw = vt[wave];
-  // slots k0 .. k0+15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V; the next
-  // tile's loads are issued before this tile is processed
-  u32x4 kn[4], vn[4];
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      const int r = i >> 4, gc = i & 15;
-      const int j = k0 + r;
-      kn[u] = u32x4{0u, 0u, 0u, 0u};
-      vn[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < wl) {
-        const size_t src = ((size_t)b * a.W + (L + j) % a.W) * a.D + g * kExD + gc * 8;
-        kn[u] = *(const u32x4*)(a.kwin + src);
-        vn[u] = *(const u32x4*)(a.vwin + src);
-      }
-    }
-  };
-  if (wave * kExdKeys < wl) load_tile(wave * kExdKeys);
-  for (int k0 = wave * kExdKeys; k0 < wl; k0 += 4 * kExdKeys) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      const int r = i >> 4, gc = i & 15;
-      *(u32x4*)(kw + r * kExSK + gc * 16) = kn[u];
-      *(u32x4*)(vw + r * kExSV + gc * 16) = vn[u];
-    }
-    if (k0 + 4 * kExdKeys < wl) load_tile(k0 + 4 * kExdKeys);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS before it is read
-    // scores S^T[slot k0 + 4 lg + i][head li]
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* krow = kw + li * kExSK + lg * 16;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(krow + ks * 64), qop[ks], sacc, 0, 0, 0);
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = sacc[i] * a.wscale;
-      v[i] = (k0 + 4 * lg + i < wl) ? ((x != x) ? INFINITY : x) : -INFINITY;
-    }
-    const float mx = wave_max_lg(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-    const float mnew = fmaxf(m, mx);
-    if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int j = 0; j < kExD / 16; ++j) acc[j] *= alpha;
-      m = mnew;
-    }
-    const bool live = m != -INFINITY;
-    bf16x4 pb;
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 pv = (__bf16)(live ? fast_exp2(v[i] - m) : 0.f);
-      pb[i] = pv;
-      ps += (float)pv;
-    }
-    lsum += ps;
-    const unsigned char* vbase = vw + (4 * lg + (li >> 2)) * kExSV + (li & 3) * 8;
-#pragma unroll
-    for (int j = 0; j < kExD / 16; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr(vbase + j * 32), pb, acc[j], 0, 0, 0);
-  }
-  const float l = wave_sum_lg(lsum);
-  // merge the four waves' partials into wave 0
-  if (lg == 0) {
-    mrg_ml[wave][0][li] = m;
-    mrg_ml[wave][1][li] = l;
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int j = 0; j < kExD / 16; ++j) mrg_o[wave - 1][j][lane] = acc[j];
-  }
-  __syncthreads();
-  if (wave != 0 || !rvalid) return;
-  float ms = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) ms = fmaxf(ms, mrg_ml[w][0][li]);
-  float wb[4], lt = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = mrg_ml[w][0][li];
-    wb[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - ms);
-    lt += mrg_ml[w][1][li] * wb[w];
-  }
-  float* wp = a.win_part + ((size_t)b * a.Hq + g * grp + li) * (kExD + 2);
-#pragma unroll
-  for (int j = 0; j < kExD / 16; ++j) {
-    f32x4 o = acc[j] * wb[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) o += mrg_o[w - 1][j][lane] * wb[w];
-    *(f32x4*)(wp + j * 16 + 4 * lg) = o;
-  }
-  if (lg == 0) {
-    wp[kExD] = ms;
-    wp[kExD + 1] = lt;
-  }
-}
-
-// The fold and a decode step's exact keys in one launch (both read only the query, the bases and
-// the window, and write disjoint workspace): workgroups [0, nfold) fold, the rest take one
-// (sequence, KV head) of exact keys each.
-template <bool F32OUT>
-__global__ __launch_bounds__(256) void lr_fold_exact(FoldArgs f, ExactArgs e, int nfx, int nfy, int nfold) {
-  const int x = blockIdx.x;
-  if (x < nfold) fold_body<F32OUT>(f, x % nfx, (x / nfx) % nfy, x / (nfx * nfy));
-  else exact_decode_body(e, x - nfold);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1271,9 +1048,108 @@ struct CombineArgs {
   const void* bv;
   void* out;
   int Hq, Hkv, d, D, rv, rv_pad16, nsplit;
-  int exact;                // exact-keys partials present (window or prefill chunk)
+  int exact;                // exact-keys partials present in win_part (a prefill chunk)
   int i4_order;             // partials are in the dequantised int4 tiles' block order
+  // a decode step's exact window, attended inside the combine (window > 0):
+  const void* q;            // [B][Hq][d], the base dtype (float32 or bf16)
+  const __bf16* kwin;       // [B][W][D] rings
+  const __bf16* vwin;
+  const int32_t* lat_len;
+  const int32_t* win_len;
+  int window;               // W (0: no window)
+  long long t_cap;
+  float wscale;             // sm_scale * log2 e
 };
+
+// A decode step's exact window inside the combine workgroup (b, j): head j attends over the live
+// slots of its KV head g (ring positions L .. L + wl - 1, slot = position mod W) in float32 on the
+// VALU, in the latent partials' base-2 units. 128 slots per round: thread (u = tid / 2, h = tid % 2)
+// forms half of slot u's score (64 dims, 16-byte loads); thread (c8 = tid % 16, sg = tid / 16)
+// accumulates columns 8 c8 .. 8 c8 + 7 over slots 8 sg .. 8 sg + 7 with a running max (the value
+// rows are loaded before the scores are known). Leaves m_w, l_w in the returned pair and the
+// unnormalised output in ow[0 .. 127]. NaN scores become +inf (as in the latent kernel).
+template <typename QT>
+__device__ void combine_window(const CombineArgs& a, int b, int j, float* qs, float* sc, float* owp, float* red,
+                               float& m_w, float& l_w) {
+  const int tid = threadIdx.x;
+  const int g = j / (a.Hq / a.Hkv);
+  const int W = a.window;
+  long long Ll = (unsigned)a.lat_len[b] & 0x00FFFFFFu;
+  Ll = Ll > a.t_cap ? a.t_cap : Ll;
+  const int L = (int)Ll;
+  int wl = a.win_len[b];
+  wl = wl < 0 ? 0 : (wl > W ? W : wl);
+  if (tid < kFoldD) qs[tid] = to_f32(((const QT*)a.q)[((size_t)b * a.Hq + j) * kFoldD + tid]) * a.wscale;
+  const int u = tid >> 1, h = tid & 1;
+  const int c8 = tid & 15, sg = tid >> 4;
+  float m = -INFINITY, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int c0 = 0; c0 < wl; c0 += 128) {
+    // value rows of this thread's 8 slots, issued before the scores are formed
+    u32x4 vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = c0 + 8 * sg + i;
+      vr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t < wl) vr[i] = *(const u32x4*)(a.vwin + ((size_t)b * W + (L + t) % W) * a.D + g * kFoldD + 8 * c8);
+    }
+    u32x4 kr[8];
+    const bool kval = c0 + u < wl;
+    const size_t krow = ((size_t)b * W + (L + c0 + u) % W) * a.D + g * kFoldD + 64 * h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kr[i] = kval ? *(const u32x4*)(a.kwin + krow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();                                       // qs visible; sc of the last round read
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8 kv8 = __builtin_bit_cast(bf16x8, kr[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += qs[64 * h + 8 * i + e] * (float)kv8[e];
+    }
+    const float s = part + __shfl_xor(part, 1);
+    if (h == 0) sc[u] = kval ? ((s != s) ? INFINITY : s) : -INFINITY;
+    __syncthreads();
+    float mx = -INFINITY;
+    for (int t = 0; t < 128; t += 4) {
+      const f32x4 v4 = *(const f32x4*)(sc + t);
+      mx = fmaxf(fmaxf(mx, fmaxf(v4[0], v4[1])), fmaxf(v4[2], v4[3]));
+    }
+    const float mnew = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = mnew == -INFINITY ? 0.f : fast_exp2(sc[8 * sg + i] - mnew);
+      ps += p;
+      const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += p * (float)v8[e];
+    }
+    if (c8 == 0) red[sg] = ps;
+    __syncthreads();
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lsum += red[i];
+    l = l * alpha + lsum;
+    m = mnew;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) owp[sg * kFoldD + 8 * c8 + e] = acc[e];
+  __syncthreads();
+  if (tid < kFoldD) {
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o += owp[i * kFoldD + tid];
+    owp[16 * kFoldD + tid] = o;                            // ow
+  }
+  __syncthreads();
+  m_w = m;
+  l_w = l;
+}
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
   const int tid = threadIdx.x;
@@ -1307,14 +1183,21 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   float* part = cs;                       // [4][pw] merge partials, reused as [16][128]
   float* ahat = part + 4 * pw;            // [rv_pad16]
   float* ws = ahat + a.rv_pad16;          // [nsplit]
-  float* red = ws + a.nsplit;             // [8]
+  float* red = ws + a.nsplit;             // [16]
+  float* wsc = red + 16;                  // window: q [128], scores [128], partial outputs [17][128]
   const size_t base = (size_t)b * a.nsplit;
 
-  float mloc = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += 256) mloc = fmaxf(mloc, a.part_ml[((base + s) * a.Hq + j) * 2]);
   float mw = -INFINITY, lw = 0.f;
   const float* wp = a.win_part + ((size_t)b * a.Hq + j) * (a.d + 2);
-  if (a.exact) { mw = wp[a.d]; lw = wp[a.d + 1]; }
+  if (a.window > 0) {
+    combine_window<BT>(a, b, j, wsc, wsc + kFoldD, wsc + 2 * kFoldD, red, mw, lw);
+    wp = wsc + 2 * kFoldD + 16 * kFoldD;  // ow
+  } else if (a.exact) {
+    mw = wp[a.d];
+    lw = wp[a.d + 1];
+  }
+  float mloc = -INFINITY;
+  for (int s = tid; s < a.nsplit; s += 256) mloc = fmaxf(mloc, a.part_ml[((base + s) * a.Hq + j) * 2]);
   const float mstar = block_reduce(fmaxf(mloc, mw), red, true);
   const bool live = mstar != -INFINITY;
 
@@ -1450,72 +1333,70 @@ static hipError_t dispatch_decode(const DecodePlan& p, const DecodeArgs& args, i
   return hipErrorInvalidValue;
 }
 
+// Arguments of the matrix-core fold (bf16 queries) for plan p; *nfold = its workgroups.
+static void fold_args(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* qt, float scale, FoldArgs* f,
+                      int* nfold) {
+  // query sequences per wave: 1 for a decode batch, up to 16 for a prefill chunk's tokens
+  const int nq = p.B >= 512 ? 16 : (p.B >= 128 ? 4 : 1);
+  f->q = (const __bf16*)q;
+  f->bk = (const __bf16*)c->bk;
+  f->qt = qt;
+  f->Hq = p.Hq;
+  f->Hkv = p.Hkv;
+  f->D = p.D;
+  f->rk = p.rk;
+  f->rk_pad = p.rk_pad;
+  f->scale = scale;
+  f->nseq = p.B;
+  f->nq = nq;
+  *nfold = ((p.rk_pad / 16 + 3) / 4) * p.Hkv * ((p.B + nq - 1) / nq);
+}
+
+hipError_t launch_decode_step(const AppendPlan& ap, const DecodePlan& p, const lr_layer_cache* c, const void* k_new,
+                              const void* v_new, const void* q, void* out, int out_dtype, void* ws, hipStream_t st,
+                              hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (p.latent == LR_F32) {
+    const hipError_t e = launch_append(ap, c, k_new, v_new, nullptr, st);
+    if (e != hipSuccess) return e;
+    return launch_decode(p, c, q, out, out_dtype, ws, st, ev_begin, ev_end);
+  }
+  FoldArgs f;
+  int nfold = 0;
+  fold_args(p, c, q, (unsigned char*)ws + p.off_qt, p.sm_scale * kLog2e, &f, &nfold);
+  const int nfx = (p.rk_pad / 16 + 3) / 4, nfy = p.Hkv;
+  const hipError_t e = launch_step_front(ap, c, k_new, v_new, f, nfx, nfy, nfold, p.latent == LR_I4G32, st);
+  if (e != hipSuccess) return e;
+  return launch_decode(p, c, q, out, out_dtype, ws, st, ev_begin, ev_end, nullptr, nullptr, true);
+}
+
 hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* out,
                          int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
-                         const void* k_chunk, const void* v_chunk) {
+                         const void* k_chunk, const void* v_chunk, bool fold_done) {
   unsigned char* w = (unsigned char*)ws;
   __bf16* qt = (__bf16*)(w + p.off_qt);
   const float scale = p.sm_scale * kLog2e;
 
-  // Exact keys (window slots; in a prefill also the chunk's own rows): for bf16 queries the
-  // matrix-core exact-keys code runs before the latent kernel (a decode step's in the same launch
-  // as the fold); for float32 queries B extra workgroups of the decode kernel (window_block).
-  const bool exact_mfma = p.exact && p.latent != LR_F32;
-  // (a decode step only: a prefill chunk's own rows are keys too, even for a one-token chunk)
-  const bool fused_exact = exact_mfma && k_chunk == nullptr && p.qpb == 1 && p.Hq / p.Hkv <= 16;
+  // Exact keys. A decode step (no chunk rows): the window is attended inside the combine, per head.
+  // A prefill chunk (the window and the chunk's own rows, causally): for bf16 queries the
+  // matrix-core exact-keys kernel runs before the latent kernel, for float32 queries B extra
+  // workgroups of the decode kernel (window_block); both leave a partial the combine merges.
+  const bool decode_step = k_chunk == nullptr;
+  const bool exact_mfma = !decode_step && p.exact && p.latent != LR_F32;
   float* win_part = (float*)(w + p.off_win);
 
-  // 1. fold (+ a decode step's exact keys)
-  {
+  // 1. fold
+  if (!fold_done) {
     dim3 grid((p.rk_pad + 63) / 64, p.Hkv, p.B);
     if (p.latent == LR_F32)
       hipLaunchKernelGGL(lr_fold<float>, grid, dim3(256), 0, st, (const float*)q, (const float*)c->bk, qt,
                          p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
     else {
-      // query sequences per wave: 1 for a decode batch, up to 16 for a prefill chunk's tokens
-      const int nq = p.B >= 512 ? 16 : (p.B >= 128 ? 4 : 1);
-      const dim3 fgrid((p.rk_pad / 16 + 3) / 4, p.Hkv, (p.B + nq - 1) / nq);
       FoldArgs f;
-      f.q = (const __bf16*)q;
-      f.bk = (const __bf16*)c->bk;
-      f.qt = (void*)qt;
-      f.Hq = p.Hq;
-      f.Hkv = p.Hkv;
-      f.D = p.D;
-      f.rk = p.rk;
-      f.rk_pad = p.rk_pad;
-      f.scale = scale;
-      f.nseq = p.B;
-      f.nq = nq;
-      const bool i4 = p.latent == LR_I4G32;
-      if (fused_exact) {
-        ExactArgs e;
-        e.q = (const __bf16*)q;
-        e.kwin = (const __bf16*)c->kwin;
-        e.vwin = (const __bf16*)c->vwin;
-        e.kchunk = nullptr;
-        e.vchunk = nullptr;
-        e.lat_len = c->lat_len;
-        e.win_len = c->win_len;
-        e.win_part = win_part;
-        e.C = 1;
-        e.Hq = p.Hq;
-        e.Hkv = p.Hkv;
-        e.D = p.D;
-        e.W = p.window;
-        e.wscale = scale;
-        e.nrb = 1;
-        const int nfold = (int)(fgrid.x * fgrid.y * fgrid.z);
-        const dim3 g2(nfold + p.B * p.Hkv);
-        if (i4)
-          hipLaunchKernelGGL(lr_fold_exact<true>, g2, dim3(256), 0, st, f, e, (int)fgrid.x, (int)fgrid.y, nfold);
-        else
-          hipLaunchKernelGGL(lr_fold_exact<false>, g2, dim3(256), 0, st, f, e, (int)fgrid.x, (int)fgrid.y, nfold);
-      } else if (i4) {
-        hipLaunchKernelGGL(lr_fold_mfma<true>, fgrid, dim3(256), 0, st, f);
-      } else {
-        hipLaunchKernelGGL(lr_fold_mfma<false>, fgrid, dim3(256), 0, st, f);
-      }
+      int nfold = 0;
+      fold_args(p, c, q, qt, scale, &f, &nfold);
+      const dim3 fgrid((p.rk_pad / 16 + 3) / 4, p.Hkv, (p.B + f.nq - 1) / f.nq);
+      if (p.latent == LR_I4G32) hipLaunchKernelGGL(lr_fold_mfma<true>, fgrid, dim3(256), 0, st, f);
+      else hipLaunchKernelGGL(lr_fold_mfma<false>, fgrid, dim3(256), 0, st, f);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1556,7 +1437,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.D = p.D;
   a.window = p.window;
   a.wscale = scale;
-  a.n_win_blocks = (p.exact && !exact_mfma) ? p.B : 0;
+  a.n_win_blocks = (!decode_step && p.exact && !exact_mfma) ? p.B : 0;
   a.qpb = p.qpb;
   a.kchunk = (const __bf16*)k_chunk;
   a.vchunk = (const __bf16*)v_chunk;
@@ -1577,7 +1458,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
     if (e != hipSuccess) return e;
     e = launch_prefill_latent(p, c, qt, a.part_ml, a.part_acc, st, ev_begin, ev_end);
   } else {
-    if (exact_mfma && !fused_exact) {
+    if (exact_mfma) {
       e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
       if (e != hipSuccess) return e;
     }
@@ -1603,9 +1484,18 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   ca.rv = p.rv;
   ca.rv_pad16 = p.rv_pad16;
   ca.nsplit = p.nsplit;
-  ca.exact = p.exact;
+  ca.exact = decode_step ? 0 : p.exact;
   ca.i4_order = p.latent == LR_I4G32;
-  const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
+  ca.q = q;
+  ca.kwin = (const __bf16*)c->kwin;
+  ca.vwin = (const __bf16*)c->vwin;
+  ca.lat_len = c->lat_len;
+  ca.win_len = c->win_len;
+  ca.window = decode_step ? p.window : 0;
+  ca.t_cap = p.t_cap;
+  ca.wscale = scale;
+  const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 16 +
+                              (ca.window > 0 ? 19 * kFoldD : 0)) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);
   const bool f32b = p.latent == LR_F32;
   const bool f32o = out_dtype == LR_F32;

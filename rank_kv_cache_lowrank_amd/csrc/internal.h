@@ -133,7 +133,7 @@ inline int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len
 
 hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* out,
                          int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
-                         const void* k_chunk = nullptr, const void* v_chunk = nullptr);
+                         const void* k_chunk = nullptr, const void* v_chunk = nullptr, bool fold_done = false);
 
 // The latent part of a prefill (p.pf): partials per (query token, token range) in the decode
 // layout, for the decode combine.
@@ -156,6 +156,13 @@ struct AppendPlan {
   int64_t t_cap;
   int ld_k, ld_v;
 };
+
+// One decode step: the append of one new token per sequence, then decode (fold, latent kernel,
+// combine); for bf16 queries the append and the fold share the first launch.
+struct DecodePlan;
+hipError_t launch_decode_step(const AppendPlan& ap, const DecodePlan& p, const lr_layer_cache* c, const void* k_new,
+                              const void* v_new, const void* q, void* out, int out_dtype, void* ws, hipStream_t st,
+                              hipEvent_t ev_begin, hipEvent_t ev_end);
 
 hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const void* k_new,
                          const void* v_new, float* z_debug, hipStream_t st);
