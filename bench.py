@@ -1,9 +1,10 @@
 """Benchmark: one layer decode step of low-rank KV-cache attention on one MI355X.
 
 A step is one pass of the whole hot path for one layer and one new token per sequence:
-lowrank_kv_append (project the new K/V rows with the caller's pseudo-inverse, store them in
-the cache format, advance the lengths) followed by lowrank_attn_decode (fold, split-token latent
-decode, combine + up-projection). Inputs are seeded synthetic data already resident in HBM.
+lowrank_decode_step, i.e. the append (project the new K/V rows with the caller's pseudo-inverse,
+store them in the cache format, advance the lengths) and the decode (fold, split-token latent
+decode, combine + up-projection, the exact window if any), in three launches: append + fold, the
+latent kernel, the combine. Inputs are seeded synthetic data already resident in HBM.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 Default workload: batch 16, 32768 cached tokens per sequence, rank 256 for K and V, bf16 latents
@@ -88,9 +89,11 @@ def step_bytes(cfg, rk, rv, lat_len, win_len, n_new):
                 total=lat + win + bases + q_out + append)
 
 
-def cpu_baseline(cfg, li, budget_s: float = 20.0):
-    """Times the fp64 oracle (latent-domain path) on the host cores over whole sequences of the
-    same workload, as many as fit the time budget (at least one)."""
+def cpu_baseline(cfg, li, budget_s: float = 6.0, reps: int = 3):
+    """Times the fp64 oracle on the host cores, in the same run as the GPU measurement:
+    D2 (latent domain, the algorithmic counterpart of the kernels) over whole sequences of the same
+    workload, as many as fit `budget_s` (at least one), `reps` times (median); and D1 (reconstruct
+    K = Zk Bk, V = Zv Bv, then plain attention) over one whole sequence, `reps` times (median)."""
     from threadpoolctl import threadpool_info
     from oracle import attention as OA
     from oracle import quant as OQ
@@ -103,47 +106,82 @@ def cpu_baseline(cfg, li, budget_s: float = 20.0):
             rows = OQ.dequant_rows(*OQ.quantize_rows(rows), r)
         return rows.astype(np.float64)
 
+    class One:
+        def __init__(self, rows):
+            self.rows = rows
+
+        def __getitem__(self, i):
+            return self.rows
+
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     q = li.q.float().numpy()
     bk = li.bk.float().numpy()
     bv = li.bv.float().numpy()
-    done, t_total, nbytes = 0, 0.0, 0
-    for b in range(cfg.batch):
-        zk = oracle_latents("k", b)
-        zv = oracle_latents("v", b)
+    win = {}
+    if cfg.window:
+        win = dict(kwin=li.kwin.float().numpy(), vwin=li.vwin.float().numpy(), win_len=li.win_len,
+                   window=cfg.window)
 
-        class One:
-            def __init__(self, rows):
-                self.rows = rows
+    def seq_bytes(b):
+        n = int(li.lat_len[b]) * (latent_bytes_per_token(cfg.latent, li.rank_k)
+                                  + latent_bytes_per_token(cfg.latent, li.rank_v))
+        return n + (int(li.win_len[b]) * 2 * cfg.kv_width * 2 if cfg.window else 0)
 
-            def __getitem__(self, i):
-                return self.rows
+    lat = {b: (oracle_latents("k", b), oracle_latents("v", b)) for b in range(min(cfg.batch, 4))}
 
-        win = {}
-        if cfg.window:
-            win = dict(kwin=li.kwin.float().numpy(), vwin=li.vwin.float().numpy(), win_len=li.win_len,
-                       window=cfg.window)
+    def run(fn, b):
+        zk, zv = lat[b] if b in lat else (oracle_latents("k", b), oracle_latents("v", b))
         t0 = time.perf_counter()
-        OA.decode_latent(q, One(zk), One(zv), bk, bv, li.lat_len, li.rank_k, li.rank_v, cfg.n_kv_heads,
-                         cfg.sm_scale, batches=[b], **win)
-        t_total += time.perf_counter() - t0
+        fn(q, One(zk), One(zv), bk, bv, li.lat_len, li.rank_k, li.rank_v, cfg.n_kv_heads, cfg.sm_scale,
+           batches=[b], **win)
+        return time.perf_counter() - t0
+
+    # D2: as many whole sequences as fit the budget, then the same sample `reps` times
+    done, t_first = 0, 0.0
+    while done < cfg.batch and (done == 0 or t_first < budget_s / reps):
+        t_first += run(OA.decode_latent, done)
         done += 1
-        nbytes += int(li.lat_len[b]) * (latent_bytes_per_token(cfg.latent, li.rank_k)
-                                        + latent_bytes_per_token(cfg.latent, li.rank_v))
-        if cfg.window:
-            nbytes += int(li.win_len[b]) * 2 * cfg.kv_width * 2
-        if t_total >= budget_s:
-            break
+    times = [t_first] + [sum(run(OA.decode_latent, b) for b in range(done)) for _ in range(reps - 1)]
+    t2 = float(np.median(times))
+    nbytes = sum(seq_bytes(b) for b in range(done))
+    d1 = [run(OA.decode_reconstruct, 0) for _ in range(reps)]
+    t1 = float(np.median(d1))
     lens = "x".join(str(int(x)) for x in li.lat_len[:done]) if cfg.len_range else str(int(li.lat_len[0]))
-    return dict(value=nbytes / t_total / 1e12, unit="TB/s", cores=int(threads), kind="oracle",
-                sample=f"{done} of {cfg.batch} sequences x {lens} tokens"
-                       f"{' (+ window)' if cfg.window else ''} of layer {li.layer}, fp64 latent-domain "
-                       f"oracle, {t_total:.2f} s; latent bytes per second in the benchmark's units",
-                us_per_layer_step=t_total / done * cfg.batch * 1e6)
+    return dict(value=nbytes / t2 / 1e12, unit="TB/s", cores=int(threads), kind="oracle",
+                sample=f"D2 (latent-domain fp64 oracle): {done} of {cfg.batch} sequences x {lens} tokens"
+                       f"{' (+ window)' if cfg.window else ''} of layer {li.layer}, median of {reps} runs "
+                       f"{t2:.2f} s; latent bytes per second in the benchmark's units",
+                us_per_layer_step=t2 / done * cfg.batch * 1e6,
+                d1={"value": seq_bytes(0) / t1 / 1e12, "unit": "TB/s", "sample": f"D1 (reconstruct K, V then "
+                    f"attend, fp64): sequence 0 ({int(li.lat_len[0])} tokens), median of {reps} runs {t1:.2f} s",
+                    "us_per_layer_step": t1 * cfg.batch * 1e6})
+
+
+def copy_ceiling(torch, dev, nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device copy of `nbytes` (read once, written once), timed with events in the same run:
+    the practical ceiling of a 1:1 read/write stream on this GPU (median of `reps`)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    del src, dst
+    return {"GB/s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1), "bytes_moved": 2 * nbytes,
+            "kind": "device-to-device copy (read + write), median of %d" % reps}
 
 
 KERNEL_SOURCES = {
-    "lr_decode": ("decode.hip", "device_common.h", "internal.h", "abi.cpp"),
+    "lr_decode": ("decode.hip", "fold.h", "device_common.h", "internal.h", "abi.cpp"),
     "lr_rebase_bf16": ("rebase.hip", "device_common.h"),
 }
 
@@ -206,7 +244,8 @@ def decode28_bench(args):
     model = lr.Model(NL, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, [r[0] for r in ranks],
                      [r[1] for r in ranks], cfg.sm_scale, cfg.window, cfg.latent)
     ll, wl = synth.split_lengths(cfg)
-    start_len = (ll - (W + K) * n_new).astype(np.int32)
+    total = W + 2 * K
+    start_len = (ll - total * n_new).astype(np.int32)
     assert np.all(start_len >= 0)
     max_len = int(ll.max())
     caches, qs, li0 = [], [], None
@@ -230,53 +269,68 @@ def decode28_bench(args):
                    for l in range(NL))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ev = HipEvents()
-    evs = [[(ev.create(), ev.create()) for _ in range(NL)] for _ in range(K)]
-    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
 
+    def full_step(events=None):
+        for l in range(NL):
+            lr.lowrank_decode_step(model, l, caches[l], k_new, v_new, qs[l], out, max_len, ws, nsplit=args.nsplit,
+                                   events=events[l] if events is not None else None)
+
+    # W warm-up steps, pass A (timed, no per-dispatch events), pass B (events on every layer's latent
+    # kernel dispatch and around every step); one step = the 28 layers' lowrank_decode_step calls
+    for i in range(W):
+        full_step()
+        if i % 5 == 0:
+            log(f"warm-up step {i} enqueued")
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    for i in range(W + K):
-        if i == W:
-            torch.cuda.synchronize()
-            start.record()
-        timed = i >= W
-        for l in range(NL):
-            lr.lowrank_kv_append(model, l, caches[l], k_new, v_new)
-            lr.lowrank_attn_decode(model, l, caches[l], qs[l], out, max_len, ws, nsplit=args.nsplit,
-                                   events=evs[i - W][l] if timed else None)
-        if i % 5 == 0:
-            log(f"step {i} enqueued")
+    start.record()
+    for i in range(K):
+        full_step()
     stop.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / K
+    evs = [[(ev.create(), ev.create()) for _ in range(NL)] for _ in range(K)]
+    sev = [(ev.create(), ev.create()) for _ in range(K)]
+    for k in range(K):
+        ev.record(sev[k][0], stream)
+        full_step(evs[k])
+        ev.record(sev[k][1], stream)
+    torch.cuda.synchronize()
     kern_ms = np.array([[ev.elapsed_ms(a, b) for a, b in row] for row in evs])   # [K, NL]
+    span_ms = [ev.elapsed_ms(a, b) for a, b in sev]
     for row in evs:
         for a, b in row:
             ev.destroy(a)
             ev.destroy(b)
+    for a, b in sev:
+        ev.destroy(a)
+        ev.destroy(b)
     assert torch.isfinite(out).all(), "non-finite output"
     for l in range(NL):
         got = caches[l].tensors["lat_len"].cpu().numpy()
         assert np.array_equal(got, ll), "lengths did not advance to the drawn lengths"
 
-    # bytes of each timed step: lat_len after that step's append = start + (i + 1)
-    step_tot, kern_bytes = [], np.zeros((K, NL))
+    ceiling = copy_ceiling(torch, dev)
+    # bytes of each step: lat_len after that step's append = start + (i + 1)
+    def step_total_at(i):
+        L = start_len + (i + 1) * n_new
+        return sum(step_bytes(cfg, ranks[l][0], ranks[l][1], L, wl, n_new)["total"] for l in range(NL))
+
+    step_total = float(np.mean([step_total_at(W + k) for k in range(K)]))
+    kern_bytes = np.zeros((K, NL))
     for k in range(K):
-        L = start_len + (W + k + 1) * n_new
-        tot = 0
+        L = start_len + (W + K + k + 1) * n_new
         for l in range(NL):
-            by = step_bytes(cfg, ranks[l][0], ranks[l][1], L, wl, n_new)
-            tot += by["total"]
-            kern_bytes[k, l] = by["latents"]        # the window slots are the exact-keys kernel's
-        step_tot.append(tot)
-    step_total = float(np.mean(step_tot))
+            kern_bytes[k, l] = step_bytes(cfg, ranks[l][0], ranks[l][1], L, wl, n_new)["latents"]
     value = step_total / (ms_per_step * 1e-3) / 1e12
     kern_avg_ms = float(kern_ms.mean())
     bytes_per_launch = float(kern_bytes.mean())
     achieved = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     per_layer_us = (kern_ms.mean(axis=0) * 1e3).round(2).tolist()
     log(f"ms/step {ms_per_step:.4f} ({NL} layers)  decode kernel avg {kern_avg_ms * 1e3:.2f} us  "
-        f"step {value:.3f} TB/s  kernel {achieved / 1e3:.3f} TB/s")
+        f"step span (events) {np.median(span_ms):.4f} ms  step {value:.3f} TB/s  kernel {achieved / 1e3:.3f} TB/s")
 
     rec = {
         "metric": "µs per layer decode step & achieved HBM TB/s (B=16, T=4K–32K)",
@@ -296,13 +350,17 @@ def decode28_bench(args):
                    "total_len_range": list(cfg.len_range), "window": cfg.window,
                    "rank_range": [int(min(cfg.rank_choices)), int(max(cfg.rank_choices))],
                    "latent": cfg.latent, "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
-                   "head_dim": cfg.head_dim, "new_tokens_per_step": n_new, "parallelism": "single GPU"},
+                   "head_dim": cfg.head_dim, "new_tokens_per_step": n_new,
+                   "step": "28 x lowrank_decode_step (append + fold, latent kernel, combine with the window)",
+                   "parallelism": "single GPU"},
         "step_bytes": int(step_total),
+        "step_span_ms_events": round(float(np.median(span_ms)), 5),
         "decode_kernel_us_per_layer": per_layer_us,
         "roofline": {"bound": "hbm", "kernel": "lr_decode", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s",
                      "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4), "traffic": None,
                      "kernel_us": round(kern_avg_ms * 1e3, 2), "bytes_per_launch": int(bytes_per_launch)},
+        "copy_ceiling": ceiling,
     }
     if not args.no_cpu:
         log("timing the CPU oracle ...")
@@ -633,8 +691,6 @@ def main():
     K, W = args.steps, args.warmup
     T = cfg.seq_len
     n_new = 1
-    # Lengths start W+K short of T so that the last timed step attends over exactly T tokens.
-    start_len = np.full(cfg.batch, T - (W + K) * n_new, np.int32)
     log(f"generating inputs for {cfg.name} ...")
     t0 = time.time()
     li = synth.make_layer(cfg, t_cap=T, lat_len=np.full(cfg.batch, T, np.int32))
@@ -647,7 +703,6 @@ def main():
     caches = []
     for _ in range(n_copies):
         model, cache = device_layer(li, dev, with_proj=True)
-        cache.tensors["lat_len"].copy_(torch.from_numpy(start_len).to(dev))
         caches.append(cache)
     log(f"{n_copies} cache cop{'y' if n_copies == 1 else 'ies'} of {lat_bytes / 1e6:.1f} MB")
     q = li.q.to(dev)
@@ -659,49 +714,69 @@ def main():
     out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=dev)
     ws = lr.workspace(model, 0, cfg.batch, T, args.nsplit)
     ev = HipEvents()
-    evs = [(ev.create(), ev.create()) for _ in range(K)]
-    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
 
-    # every copy takes the same number of appends: lengths advance once per pass over the copies
-    steps_per_copy = -(-(W + K) // n_copies)
+    # Two passes of K steps after W warm-up steps: pass A is the timed region (no per-dispatch
+    # events: they lengthen the gaps around the dispatch they are attached to); pass B repeats the
+    # steps with HIP events attached to the latent kernel's dispatch (its duration) and recorded
+    # around each step call (the step's span). Every copy takes the same number of steps; the
+    # lengths start short so that the last step of pass B attends over exactly T tokens.
+    total = W + 2 * K
+    steps_per_copy = -(-total // n_copies)
+    L0 = T - steps_per_copy * n_new
     for cache in caches:
-        cache.tensors["lat_len"].copy_(torch.from_numpy(np.full(cfg.batch, T - steps_per_copy * n_new,
-                                                                 np.int32)).to(dev))
-    lens = []
+        cache.tensors["lat_len"].copy_(torch.from_numpy(np.full(cfg.batch, L0, np.int32)).to(dev))
+
+    def step(i, events=None):
+        cache = caches[i % n_copies]
+        lr.lowrank_decode_step(model, 0, cache, k_new, v_new, q, out, T, ws, nsplit=args.nsplit, events=events)
+        return np.full(cfg.batch, L0 + (i // n_copies + 1) * n_new, np.int32)   # lengths the step attends
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    for i in range(W + K):
-        if i == W:
-            torch.cuda.synchronize()
-            start.record()
-        cache = caches[i % n_copies]
-        lr.lowrank_kv_append(model, 0, cache, k_new, v_new)
-        timed = i >= W
-        lr.lowrank_attn_decode(model, 0, cache, q, out, T, ws, nsplit=args.nsplit,
-                               events=evs[i - W] if timed else None)
-        if timed:
-            lens.append(np.full(cfg.batch, T - steps_per_copy * n_new + (i // n_copies + 1) * n_new, np.int32))
+    lens_a = []
+    start.record()
+    for i in range(W, W + K):
+        lens_a.append(step(i))
     stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / K
-    kern_ms = [ev.elapsed_ms(a, b) for a, b in evs]
-    kern_avg_ms = float(np.mean(kern_ms))
-    for a, b in evs:
+    ms_per_step = start.elapsed_time(stop) / K
+    # pass B
+    kev = [(ev.create(), ev.create()) for _ in range(K)]
+    sev = [(ev.create(), ev.create()) for _ in range(K)]
+    lens_b = []
+    for k in range(K):
+        i = W + K + k
+        ev.record(sev[k][0], stream)
+        lens_b.append(step(i, events=kev[k]))
+        ev.record(sev[k][1], stream)
+    torch.cuda.synchronize()
+    kern_ms = [ev.elapsed_ms(a, b) for a, b in kev]
+    span_ms = [ev.elapsed_ms(a, b) for a, b in sev]
+    for a, b in kev + sev:
         ev.destroy(a)
         ev.destroy(b)
     assert torch.isfinite(out).all(), "non-finite output"
+    got = caches[(W + 2 * K - 1) % n_copies].tensors["lat_len"].cpu().numpy()
+    assert np.all(got <= T), "lengths past the cache capacity"
 
+    ceiling = copy_ceiling(torch, dev)
     if args.copy_probe:
         copy_probe(torch, dev)
 
-    by = [step_bytes(cfg, li.rank_k, li.rank_v, L, np.zeros_like(L), n_new) for L in lens]
+    by = [step_bytes(cfg, li.rank_k, li.rank_v, L, np.zeros_like(L), n_new) for L in lens_a]
     step_total = float(np.mean([x["total"] for x in by]))
-    lat_avg = float(np.mean([x["latents"] + x["window"] for x in by]))
+    by_b = [step_bytes(cfg, li.rank_k, li.rank_v, L, np.zeros_like(L), n_new) for L in lens_b]
+    lat_avg = float(np.mean([x["latents"] + x["window"] for x in by_b]))
+    kern_avg_ms = float(np.mean(kern_ms))
     value = step_total / (ms_per_step * 1e-3) / 1e12
     achieved = lat_avg / (kern_avg_ms * 1e-3) / 1e9
-    log(f"ms/step {ms_per_step:.4f}  decode kernel {kern_avg_ms * 1e3:.2f} us  step {value:.3f} TB/s  "
-        f"kernel {achieved / 1e3:.3f} TB/s")
+    log(f"ms/step {ms_per_step:.4f}  decode kernel {kern_avg_ms * 1e3:.2f} us  step span (events) "
+        f"{np.median(span_ms) * 1e3:.2f} us  step {value:.3f} TB/s  kernel {achieved / 1e3:.3f} TB/s  "
+        f"copy ceiling {ceiling['GB/s'] / 1e3:.2f} TB/s")
 
     rec = {
         "metric": "µs per layer decode step & achieved HBM TB/s (B=16, T=4K–32K)",
@@ -720,13 +795,16 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": T, "rank_k": li.rank_k,
                    "rank_v": li.rank_v, "latent": cfg.latent, "q_heads": cfg.n_q_heads,
                    "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "new_tokens_per_step": n_new,
+                   "step": "lowrank_decode_step (append + fold, latent kernel, combine)",
                    "parallelism": "single GPU"},
         "step_bytes": int(step_total),
+        "step_span_us_events": round(float(np.median(span_ms)) * 1e3, 2),
         "roofline": {"bound": "hbm", "kernel": "lr_decode", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_TBS * 1000, "unit": "GB/s",
                      "frac": round(achieved / (PEAK_HBM_TBS * 1000), 4),
                      "traffic": measured_traffic(cfg.name),
                      "kernel_us": round(kern_avg_ms * 1e3, 2), "bytes_per_launch": int(lat_avg)},
+        "copy_ceiling": ceiling,
         "cache_copies": n_copies,
     }
     if not args.no_cpu:

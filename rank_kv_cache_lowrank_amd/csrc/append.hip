@@ -16,6 +16,7 @@
 #include "internal.h"
 
 #include <math.h>
+#include <string.h>
 
 namespace lr {
 
@@ -120,14 +121,21 @@ __device__ __forceinline__ int clamp_len(int32_t raw, long long cap) {
   return (int)((long long)v > cap ? cap : (long long)v);
 }
 
+// readers: workgroups that read each sequence's lengths and ring (nck + ncv, plus a decode step's
+// window workgroups, which read the ring in the same launch).
+constexpr int kAppendLds = kAppendSeqs * kAppendLdsX + kAppendSeqs * kAppendCols * 4 + 4 * kAppendSeqs * 4;
+
 template <bool F32P>
-__device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int ncv, int bx, int by) {
-  __shared__ __attribute__((aligned(16))) unsigned char xs[kAppendSeqs * kAppendLdsX];   // staged rows
-  __shared__ float zt[kAppendSeqs][kAppendCols];                                         // z tile
-  __shared__ int s_len[kAppendSeqs], s_win[kAppendSeqs], s_rows[kAppendSeqs], s_last[kAppendSeqs];
+__device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int ncv, int bx, int by, int readers,
+                                            unsigned char* smem) {
+  unsigned char* xs = smem;                                                   // [16][kAppendLdsX] staged rows
+  float (*zt)[kAppendCols] = (float (*)[kAppendCols])(smem + kAppendSeqs * kAppendLdsX);   // [16][64] z tile
+  int* s_len = (int*)(smem + kAppendSeqs * kAppendLdsX + kAppendSeqs * kAppendCols * 4);
+  int* s_win = s_len + kAppendSeqs;
+  int* s_rows = s_win + kAppendSeqs;
+  int* s_last = s_rows + kAppendSeqs;
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gx = nck + ncv;
   const int kv = bx < nck ? 0 : 1;
   const int col0 = (bx - (kv ? nck : 0)) * kAppendCols;
   const int r = kv == 0 ? a.rk : a.rv;
@@ -295,7 +303,7 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int nc
   // arrivals: this workgroup's reads of its sequences are done (the barrier above)
   if (tid < nseq) {
     const unsigned old = atomicAdd((unsigned*)&a.lat_len[b0 + tid], kArrival);
-    s_last[tid] = ((old >> 24) & 0x7Fu) == (unsigned)(gx - 1) ? 1 : 0;
+    s_last[tid] = ((old >> 24) & 0x7Fu) == (unsigned)(readers - 1) ? 1 : 0;
   }
   __syncthreads();
   // the last workgroup of a sequence: new tokens into the ring, then the final lengths
@@ -344,21 +352,361 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int nc
 
 template <bool F32P>
 __global__ __launch_bounds__(256) void lr_append(AppendArgs a, int nck, int ncv) {
-  append_body<F32P>(a, nck, ncv, blockIdx.x, blockIdx.y);
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  append_body<F32P>(a, nck, ncv, blockIdx.x, blockIdx.y, nck + ncv, smem);
 }
 
-// A decode step's first launch: the append's workgroups [0, nck + ncv) x ceil(B / 16) (as lr_append,
-// flattened) and the fold's workgroups after them. The fold reads only the query and the key basis,
-// so it does not depend on the append (the decode step's window is attended in the combine).
-template <bool F32OUT>
-__global__ __launch_bounds__(256) void lr_step_front(AppendArgs a, int nck, int ncv, int n_append, FoldArgs f,
-                                                     int nfx, int nfy) {
+// ---------------------------------------------------------------------------------------------
+// Exact window of a decode step (iS-KV abstract: the most recent tokens stay exact), one workgroup
+// per (sequence b, KV head g), float32 on the VALU: every head j of the group attends over the live
+// window slots with base-2 scores (sm_scale * log2 e folded into the query), and the workgroup
+// writes (O unnormalised, m, l) per head for the combine.
+// In lowrank_decode_step the window is the one after this step's append, read in the same launch
+// as the append: positions L' .. L' + wl' - 1 with L' = L + evicted, wl' = min(wl + 1, W), the
+// last being the new token, taken from k_new / v_new; the others are ring slots the append does
+// not write. Such a workgroup is one of the sequence's readers in the append's arrival count, and
+// if it arrives last it writes the new token into the ring and the final lengths.
+// Heads in batches of 8; slots in rounds of 128: thread (u = tid / 2, h = tid % 2) forms half of
+// slot u's score (64 dims) for each head, thread (c8 = tid % 16, sg = tid / 16) accumulates
+// columns 8 c8 .. +7 over slots 8 sg .. +7 (the value rows are loaded with the key rows, before the
+// scores are known); one running max per head.
+// ---------------------------------------------------------------------------------------------
+struct WinArgs {
+  const void* q;            // [B][Hq][d], float32 or bf16
+  float* win_part;          // [B][Hq][d + 2]
+  int Hq, Hkv;
+  float wscale;
+  int step;                 // the window after this launch's append (lowrank_decode_step)
+  int readers;              // arrival count of a sequence in that case
+};
+
+constexpr int kWinHeads = 8;
+
+constexpr int kWinValuLds = (kWinHeads * kFoldD + kWinHeads * 128 + 4 * kWinHeads + 4 * kWinHeads * kFoldD +
+                             4 * kWinHeads) * 4 + 16;
+
+// The last reader of a sequence in a decode step's first launch: the new token into its ring slot
+// (L + wl) mod W and the lengths after the step (workgroup-wide).
+__device__ __forceinline__ void window_step_finish(const AppendArgs& a, int b, int L, int wl, int n_ev) {
+  const int D = a.D, W = a.window;
+  const int slot = (L + wl) % W;
+  for (int i = threadIdx.x; i < 2 * (D / 8); i += 256) {
+    const int kvs = i / (D / 8), c = i % (D / 8);
+    const __bf16* src = (kvs == 0 ? a.k_new : a.v_new) + (size_t)b * D + c * 8;
+    __bf16* dst = (kvs == 0 ? a.kwin : a.vwin) + ((size_t)b * W + slot) * D + c * 8;
+    *(u32x4*)dst = *(const u32x4*)src;
+  }
+  if (threadIdx.x == 0) {
+    const long long nl = (long long)L + n_ev;
+    a.win_len[b] = wl + 1 > W ? W : wl + 1;
+    a.lat_len[b] = (int)(nl > a.t_cap ? a.t_cap : nl);
+  }
+}
+
+template <typename QT>
+__device__ void window_body(const WinArgs& w, const AppendArgs& a, int blk, unsigned char* smem) {
+  float (*wq)[kFoldD] = (float (*)[kFoldD])smem;                                 // [8][128]
+  float (*wsc)[128] = (float (*)[128])(smem + kWinHeads * kFoldD * 4);          // [8][128]
+  float (*wmx)[kWinHeads] = (float (*)[kWinHeads])((unsigned char*)wsc + kWinHeads * 128 * 4);   // [4][8]
+  float (*wred)[kWinHeads][kFoldD] = (float (*)[kWinHeads][kFoldD])((unsigned char*)wmx + 4 * kWinHeads * 4);
+  float (*wl4)[kWinHeads] = (float (*)[kWinHeads])((unsigned char*)wred + 4 * kWinHeads * kFoldD * 4);
+  int& w_last = *(int*)((unsigned char*)wl4 + 4 * kWinHeads * 4);
+  const int grp = w.Hq / w.Hkv, D = a.D, W = a.window;
+  const int g = blk % w.Hkv, b = blk / w.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int u = tid >> 1, h2 = tid & 1, c8 = tid & 15, sg = tid >> 4;
+  const int L = clamp_len(a.lat_len[b], a.t_cap);
+  int wl = a.win_len[b];
+  wl = wl < 0 ? 0 : (wl > W ? W : wl);
+  int Lw = L, wlw = wl, n_ev = 0;
+  if (w.step) {
+    n_ev = wl + 1 > W ? wl + 1 - W : 0;
+    Lw = L + n_ev;
+    wlw = wl + 1 > W ? W : wl + 1;
+  }
+  // source of window position index t (0 .. wlw - 1) of head g: a ring slot, or the new token
+  auto row = [&](const __bf16* ring, const __bf16* xnew, int t) -> const __bf16* {
+    if (w.step && t == wlw - 1) return xnew + (size_t)b * D + g * kFoldD;
+    return ring + ((size_t)b * W + (Lw + t) % W) * D + g * kFoldD;
+  };
+  for (int h0 = 0; h0 < grp; h0 += kWinHeads) {
+    const int nh = min(kWinHeads, grp - h0);
+    __syncthreads();                                  // wq / wred of the previous batch consumed
+    for (int i = tid; i < nh * kFoldD; i += 256)
+      wq[i / kFoldD][i % kFoldD] =
+          to_f32(((const QT*)w.q)[((size_t)b * w.Hq + g * grp + h0) * kFoldD + i]) * w.wscale;
+    float m[kWinHeads], lt[kWinHeads], acc[kWinHeads][8];
+#pragma unroll
+    for (int hh = 0; hh < kWinHeads; ++hh) {
+      m[hh] = -INFINITY;
+      lt[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    }
+    for (int c0 = 0; c0 < wlw; c0 += 128) {
+      u32x4 kr[8], vr[8];
+      const bool kval = c0 + u < wlw;
+      const __bf16* kp = row(a.kwin, a.k_new, kval ? c0 + u : 0) + 64 * h2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = kval ? *(const u32x4*)(kp + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = c0 + 8 * sg + i;
+        vr[i] = t < wlw ? *(const u32x4*)(row(a.vwin, a.v_new, t) + 8 * c8) : u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();                                // wq visible; the previous round's wsc read
+      float sv[kWinHeads];
+#pragma unroll
+      for (int hh = 0; hh < kWinHeads; ++hh) {
+        float part = 0.f;
+        if (hh < nh) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const bf16x8 k8 = __builtin_bit_cast(bf16x8, kr[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += wq[hh][64 * h2 + 8 * i + e] * (float)k8[e];
+          }
+        }
+        const float sc = part + __shfl_xor(part, 1);
+        sv[hh] = kval ? ((sc != sc) ? INFINITY : sc) : -INFINITY;   // NaN: this head only
+        if (h2 == 0) wsc[hh][u] = sv[hh];
+        float mx = sv[hh];
+        for (int o = 2; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if (lane == 0) wmx[wave][hh] = mx;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int hh = 0; hh < kWinHeads; ++hh) {
+        const float mx = fmaxf(fmaxf(wmx[0][hh], wmx[1][hh]), fmaxf(wmx[2][hh], wmx[3][hh]));
+        const float mnew = fmaxf(m[hh], mx);
+        const float alpha = (m[hh] == -INFINITY) ? 0.f : fast_exp2(m[hh] - mnew);
+        const bool live = mnew != -INFINITY;
+        // running l over this thread's slot (score threads), running O over its 8 slots
+        lt[hh] = lt[hh] * alpha + ((h2 == 0 && live) ? fast_exp2(sv[hh] - mnew) : 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = live ? fast_exp2(wsc[hh][8 * sg + i] - mnew) : 0.f;
+          const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr[i]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[hh][e] += p * (float)v8[e];
+        }
+        m[hh] = mnew;
+      }
+    }
+    // reduce: O over the 16 slot groups (4 per wave by shuffles, then the 4 waves through LDS),
+    // l over the score threads
+#pragma unroll
+    for (int hh = 0; hh < kWinHeads; ++hh) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[hh][e];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (lane < 16) wred[wave][hh][8 * c8 + e] = v;
+      }
+      float lv = lt[hh];
+      for (int o = 1; o < 64; o <<= 1) lv += __shfl_xor(lv, o);
+      if (lane == 0) wl4[wave][hh] = lv;
+    }
+    __syncthreads();
+    for (int i = tid; i < nh * kFoldD; i += 256) {
+      const int hh = i / kFoldD, c = i % kFoldD;
+      float* wp = w.win_part + ((size_t)b * w.Hq + g * grp + h0 + hh) * (kFoldD + 2);
+      wp[c] = ((wred[0][hh][c] + wred[1][hh][c]) + wred[2][hh][c]) + wred[3][hh][c];
+      if (c == 0) {
+        wp[kFoldD] = m[hh];
+        wp[kFoldD + 1] = ((wl4[0][hh] + wl4[1][hh]) + wl4[2][hh]) + wl4[3][hh];
+      }
+    }
+  }
+  if (!w.step) return;
+  // this workgroup's reads of the sequence are done: count it among the readers
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = atomicAdd((unsigned*)&a.lat_len[b], kArrival);
+    w_last = ((old >> 24) & 0x7Fu) == (unsigned)(w.readers - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (w_last) window_step_finish(a, b, L, wl, n_ev);
+}
+
+// The same on the matrix cores, for bf16 queries and at most 16 heads per KV head: the grp heads
+// are the 16 rows of the products (zero past grp). Wave v takes the 16-slot tiles v, v + 4, ... of
+// the window and stages each in its own part of LDS (a wave's LDS writes and reads stay in order;
+// the next tile's loads are issued before the current one is processed): scores from the 16x16x32
+// bf16 product (16 slots x 16 heads), a base-2 online softmax, values from the 16x16x16 product
+// through the transpose read; the four waves' (O, m, l) are merged through LDS.
+constexpr int kWinSlots = 16;
+constexpr int kWinMfmaLds = 4 * kWinSlots * kExSK + 4 * kWinSlots * kExSV + 4 * 2 * 16 * 4 + 3 * (kExD / 16) * 64 * 16 + 16;
+
+__device__ void window_mfma_body(const WinArgs& w, const AppendArgs& a, int blk, unsigned char* smem) {
+  unsigned char* ktb = smem;                                          // [4][16 * kExSK]
+  unsigned char* vtb = ktb + 4 * kWinSlots * kExSK;                   // [4][16 * kExSV]
+  float* mrg_ml = (float*)(vtb + 4 * kWinSlots * kExSV);              // [4][2][16]
+  f32x4* mrg_o = (f32x4*)(mrg_ml + 4 * 2 * 16);                       // [3][8][64]
+  int& w_last = *(int*)(mrg_o + 3 * (kExD / 16) * 64);
+  const int grp = w.Hq / w.Hkv, D = a.D, W = a.window;
+  const int g = blk % w.Hkv, b = blk / w.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool rvalid = li < grp;
+  const int L = clamp_len(a.lat_len[b], a.t_cap);
+  int wl = a.win_len[b];
+  wl = wl < 0 ? 0 : (wl > W ? W : wl);
+  int Lw = L, wlw = wl, n_ev = 0;
+  if (w.step) {
+    n_ev = wl + 1 > W ? wl + 1 - W : 0;
+    Lw = L + n_ev;
+    wlw = wl + 1 > W ? W : wl + 1;
+  }
+  auto row = [&](const __bf16* ring, const __bf16* xnew, int t) -> const __bf16* {
+    if (w.step && t == wlw - 1) return xnew + (size_t)b * D + g * kExD;
+    return ring + ((size_t)b * W + (Lw + t) % W) * D + g * kExD;
+  };
+  // q of this lane's head as the B operand: d indices 32 ks + 8 lg .. +7
+  bf16x8 qop[4];
+  {
+    const __bf16* qr = (const __bf16*)w.q + ((size_t)b * w.Hq + g * grp + (rvalid ? li : 0)) * kExD + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qop[ks] = rvalid ? *(const bf16x8*)(qr + ks * 32) : zero_bf16x8();
+  }
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[kExD / 16];
+#pragma unroll
+  for (int j = 0; j < kExD / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned char* kw = ktb + wave * kWinSlots * kExSK;
+  unsigned char* vw = vtb + wave * kWinSlots * kExSV;
+  // slots k0 .. k0+15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V
+  u32x4 kn[4], vn[4];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      const int r = i >> 4, gc = i & 15;
+      const int j = k0 + r;
+      kn[u] = u32x4{0u, 0u, 0u, 0u};
+      vn[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j < wlw) {
+        kn[u] = *(const u32x4*)(row(a.kwin, a.k_new, j) + gc * 8);
+        vn[u] = *(const u32x4*)(row(a.vwin, a.v_new, j) + gc * 8);
+      }
+    }
+  };
+  if (wave * kWinSlots < wlw) load_tile(wave * kWinSlots);
+  for (int k0 = wave * kWinSlots; k0 < wlw; k0 += 4 * kWinSlots) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      const int r = i >> 4, gc = i & 15;
+      *(u32x4*)(kw + r * kExSK + gc * 16) = kn[u];
+      *(u32x4*)(vw + r * kExSV + gc * 16) = vn[u];
+    }
+    if (k0 + 4 * kWinSlots < wlw) load_tile(k0 + 4 * kWinSlots);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS before it is read
+    // scores S^T[slot k0 + 4 lg + i][head li]
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    const unsigned char* krow = kw + li * kExSK + lg * 16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(krow + ks * 64), qop[ks], sacc, 0, 0, 0);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = sacc[i] * w.wscale;
+      v[i] = (k0 + 4 * lg + i < wlw) ? ((x != x) ? INFINITY : x) : -INFINITY;
+    }
+    const float mx = wave_max_lg(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    const float mnew = fmaxf(m, mx);
+    if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int j = 0; j < kExD / 16; ++j) acc[j] *= alpha;
+      m = mnew;
+    }
+    const bool live = m != -INFINITY;
+    bf16x4 pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 pv = (__bf16)(live ? fast_exp2(v[i] - m) : 0.f);
+      pb[i] = pv;
+      ps += (float)pv;
+    }
+    lsum += ps;
+    const unsigned char* vbase = vw + (4 * lg + (li >> 2)) * kExSV + (li & 3) * 8;
+#pragma unroll
+    for (int j = 0; j < kExD / 16; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr(vbase + j * 32), pb, acc[j], 0, 0, 0);
+  }
+  const float l = wave_sum_lg(lsum);
+  // merge the four waves' partials into wave 0
+  if (lg == 0) {
+    mrg_ml[(wave * 2) * 16 + li] = m;
+    mrg_ml[(wave * 2 + 1) * 16 + li] = l;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < kExD / 16; ++j) mrg_o[((wave - 1) * (kExD / 16) + j) * 64 + lane] = acc[j];
+  }
+  __syncthreads();
+  if (wave == 0 && rvalid) {
+    float ms = -INFINITY;
+#pragma unroll
+    for (int v2 = 0; v2 < 4; ++v2) ms = fmaxf(ms, mrg_ml[(v2 * 2) * 16 + li]);
+    float wb[4], lt = 0.f;
+#pragma unroll
+    for (int v2 = 0; v2 < 4; ++v2) {
+      const float mw = mrg_ml[(v2 * 2) * 16 + li];
+      wb[v2] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - ms);
+      lt += mrg_ml[(v2 * 2 + 1) * 16 + li] * wb[v2];
+    }
+    float* wp = w.win_part + ((size_t)b * w.Hq + g * grp + li) * (kExD + 2);
+#pragma unroll
+    for (int j = 0; j < kExD / 16; ++j) {
+      f32x4 o = acc[j] * wb[0];
+#pragma unroll
+      for (int v2 = 1; v2 < 4; ++v2) o += mrg_o[((v2 - 1) * (kExD / 16) + j) * 64 + lane] * wb[v2];
+      *(f32x4*)(wp + j * 16 + 4 * lg) = o;
+    }
+    if (lg == 0) {
+      wp[kExD] = ms;
+      wp[kExD + 1] = lt;
+    }
+  }
+  if (!w.step) return;
+  // this workgroup's reads of the sequence are done (the barrier above): count it among the readers
+  if (tid == 0) {
+    const unsigned old = atomicAdd((unsigned*)&a.lat_len[b], kArrival);
+    w_last = ((old >> 24) & 0x7Fu) == (unsigned)(w.readers - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (w_last) window_step_finish(a, b, L, wl, n_ev);
+}
+
+constexpr int kFrontLds = kWinMfmaLds > kAppendLds ? (kWinMfmaLds > kWinValuLds ? kWinMfmaLds : kWinValuLds)
+                                                   : (kAppendLds > kWinValuLds ? kAppendLds : kWinValuLds);
+static_assert(kFrontLds >= kHeadsPad * kFoldD * 4, "the float32 fold's query tile fits");
+
+// The first launch of a decode call: [append (a decode step only)] [fold] [window, W > 0].
+template <int LAT>
+__global__ __launch_bounds__(256) void lr_front(AppendArgs a, int nck, int ncv, int n_append, FoldArgs f, int nfx,
+                                                int nfy, int n_fold, WinArgs w) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int x = blockIdx.x;
   if (x < n_append) {
-    append_body<false>(a, nck, ncv, x % (nck + ncv), x / (nck + ncv));
-  } else {
+    append_body<LAT == LR_F32>(a, nck, ncv, x % (nck + ncv), x / (nck + ncv), w.readers > 0 ? w.readers : nck + ncv,
+                               smem);
+  } else if (x < n_append + n_fold) {
     const int y = x - n_append;
-    fold_body<F32OUT>(f, y % nfx, (y / nfx) % nfy, y / (nfx * nfy));
+    if constexpr (LAT == LR_F32) fold_f32_body(f, y % nfx, (y / nfx) % nfy, y / (nfx * nfy), (float*)smem);
+    else fold_body<LAT == LR_I4G32>(f, y % nfx, (y / nfx) % nfy, y / (nfx * nfy));
+  } else {
+    if constexpr (LAT == LR_F32) window_body<float>(w, a, x - n_append - n_fold, smem);
+    else if (w.Hq / w.Hkv <= 16) window_mfma_body(w, a, x - n_append - n_fold, smem);
+    else window_body<__bf16>(w, a, x - n_append - n_fold, smem);
   }
 }
 
@@ -474,20 +822,45 @@ hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const voi
   append_args(p, c, k_new, v_new, z_debug, a);
   const int nck = (p.rk + kAppendCols - 1) / kAppendCols, ncv = (p.rv + kAppendCols - 1) / kAppendCols;
   const dim3 grid(nck + ncv, (p.B + kAppendSeqs - 1) / kAppendSeqs);
-  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append<true>, grid, dim3(256), 0, st, a, nck, ncv);
-  else hipLaunchKernelGGL(lr_append<false>, grid, dim3(256), 0, st, a, nck, ncv);
+  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append<true>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
+  else hipLaunchKernelGGL(lr_append<false>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
   return hipGetLastError();
 }
 
-hipError_t launch_step_front(const AppendPlan& p, const lr_layer_cache* c, const void* k_new, const void* v_new,
-                             const FoldArgs& f, int nfx, int nfy, int nfold, bool i4, hipStream_t st) {
+hipError_t launch_front(const FrontPlan& fp, const AppendPlan* ap, const lr_layer_cache* c, const void* k_new,
+                        const void* v_new, const FoldArgs& f, float* win_part, float wscale, hipStream_t st) {
   AppendArgs a;
-  append_args(p, c, k_new, v_new, nullptr, a);
-  const int nck = (p.rk + kAppendCols - 1) / kAppendCols, ncv = (p.rv + kAppendCols - 1) / kAppendCols;
-  const int n_append = (nck + ncv) * ((p.B + kAppendSeqs - 1) / kAppendSeqs);
-  const dim3 grid(n_append + nfold);
-  if (i4) hipLaunchKernelGGL(lr_step_front<true>, grid, dim3(256), 0, st, a, nck, ncv, n_append, f, nfx, nfy);
-  else hipLaunchKernelGGL(lr_step_front<false>, grid, dim3(256), 0, st, a, nck, ncv, n_append, f, nfx, nfy);
+  if (ap) {
+    append_args(*ap, c, k_new, v_new, nullptr, a);
+  } else {      // no append: the window workgroups read only the ring and the lengths
+    memset(&a, 0, sizeof(a));
+    a.kwin = (__bf16*)c->kwin;
+    a.vwin = (__bf16*)c->vwin;
+    a.lat_len = c->lat_len;
+    a.win_len = c->win_len;
+    a.D = f.D;
+    a.window = fp.window;
+    a.t_cap = fp.t_cap;
+  }
+  WinArgs w;
+  w.q = f.q;
+  w.win_part = win_part;
+  w.Hq = f.Hq;
+  w.Hkv = f.Hkv;
+  w.wscale = wscale;
+  w.step = ap != nullptr && fp.n_win > 0;
+  w.readers = w.step ? fp.nck + fp.ncv + f.Hkv : 0;
+  const dim3 grid(fp.n_append + fp.n_fold + fp.n_win);
+  if (grid.x == 0) return hipSuccess;
+  if (fp.latent == LR_F32)
+    hipLaunchKernelGGL(lr_front<LR_F32>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx, fp.nfy,
+                       fp.n_fold, w);
+  else if (fp.latent == LR_I4G32)
+    hipLaunchKernelGGL(lr_front<LR_I4G32>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx,
+                       fp.nfy, fp.n_fold, w);
+  else
+    hipLaunchKernelGGL(lr_front<LR_BF16>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx,
+                       fp.nfy, fp.n_fold, w);
   return hipGetLastError();
 }
 

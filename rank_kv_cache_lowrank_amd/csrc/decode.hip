@@ -90,7 +90,6 @@ __device__ __forceinline__ bf16x8 k_operand(const unsigned char* row, int k0) {
   }
 }
 
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 // Value operand of the 16x16x16 bf16 product: lane (lg, li) holds latent index rv of tokens
 // 4*lg .. 4*lg+3 (K index = token), the rows the score tile's C layout gives this lane.
@@ -160,15 +159,6 @@ __device__ __forceinline__ u32x4 dequant8_f16(unsigned w, f16x2 s2, f16x2 z2, un
 }
 
 
-// Value operand through the gfx950 transpose read: within each 16-lane group g, lane j's element
-// e comes from the address given by lane 16g + 4e + j/4, at element offset j%4. Lane
-// 16g + 4e + q therefore points at row 4g+e, column 4q of the 16-column block, and every lane j
-// receives column j of rows 4g .. 4g+3: the A operand of the 16x16x16 product with K = token.
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-__device__ __forceinline__ bf16x4 v_operand_tr(const unsigned char* p) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                        (__attribute__((address_space(3))) s16x4*)(p)));
-}
 
 // ---------------------------------------------------------------------------------------------
 // Exact-keys workgroup of query sequence sq: dense attention of every head over the live window
@@ -976,60 +966,22 @@ __global__ __launch_bounds__(decode_threads(G, LT)) void lr_decode(DecodeArgs a)
   latent_block<KS, RB, LT, G, SP>(a, smem, (int)blockIdx.x - a.n_win_blocks);
 }
 
-// ---------------------------------------------------------------------------------------------
-// Fold: qt[b][j][k] = scale * sum_c q[b][j][c] * Bk[k][g(j)*d + c], bf16, zero-padded.
-// grid (rk_pad/64, Hkv, B), 256 threads: thread (hs, k) computes heads hs, hs+4, ... of KV head
-// g for latent index k; its 256-byte slice of Bk row k is loaded with independent 16-byte loads.
-// ---------------------------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float* out);
-template <>
-__device__ __forceinline__ void load8<__bf16>(const __bf16* p, float* out) {
-  const bf16x8 v = *(const bf16x8*)p;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* out) {
-  const f32x4 v0 = *(const f32x4*)p;
-  const f32x4 v1 = *(const f32x4*)(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { out[e] = v0[e]; out[4 + e] = v1[e]; }
-}
-
-
 template <typename T>
 __global__ __launch_bounds__(256) void lr_fold(const T* __restrict__ q, const T* __restrict__ bk,
                                                __bf16* __restrict__ qt, int Hq, int Hkv, int D,
                                                int rk, int rk_pad, float scale) {
+  FoldArgs f;
+  f.q = (const __bf16*)q;
+  f.bk = (const __bf16*)bk;
+  f.qt = qt;
+  f.Hq = Hq;
+  f.Hkv = Hkv;
+  f.D = D;
+  f.rk = rk;
+  f.rk_pad = rk_pad;
+  f.scale = scale;
   __shared__ float qs[kHeadsPad * kFoldD];
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int grp = Hq / Hkv;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < grp * kFoldD; i += 256)
-    qs[i] = to_f32(q[((size_t)b * Hq + g * grp) * kFoldD + i]) * scale;
-  __syncthreads();
-  const int k = blockIdx.x * 64 + (tid & 63);
-  const int hs = tid >> 6;
-  if (k >= rk_pad) return;
-  __bf16* out = qt + (size_t)b * kHeadsPad * rk_pad + k;
-  float bvals[kFoldD];
-  if (k < rk) {
-    const T* brow = bk + (size_t)k * D + g * kFoldD;
-#pragma unroll
-    for (int c = 0; c < kFoldD; c += 8) load8<T>(brow + c, bvals + c);
-  }
-  for (int h = hs; h < grp; h += 4) {
-    float acc = 0.f;
-    if (k < rk) {
-      const float* qh = qs + h * kFoldD;
-#pragma unroll
-      for (int c = 0; c < kFoldD; ++c) acc += qh[c] * bvals[c];
-    }
-    out[(size_t)(g * grp + h) * rk_pad] = (__bf16)acc;
-  }
-  if (g == 0)
-    for (int j = Hq + hs; j < kHeadsPad; j += 4) out[(size_t)j * rk_pad] = (__bf16)0.f;
+  fold_f32_body(f, blockIdx.x, blockIdx.y, blockIdx.z, qs);
 }
 
 template <bool F32OUT>
@@ -1048,108 +1000,9 @@ struct CombineArgs {
   const void* bv;
   void* out;
   int Hq, Hkv, d, D, rv, rv_pad16, nsplit;
-  int exact;                // exact-keys partials present in win_part (a prefill chunk)
+  int exact;                // exact-keys partials present in win_part (window, prefill chunk)
   int i4_order;             // partials are in the dequantised int4 tiles' block order
-  // a decode step's exact window, attended inside the combine (window > 0):
-  const void* q;            // [B][Hq][d], the base dtype (float32 or bf16)
-  const __bf16* kwin;       // [B][W][D] rings
-  const __bf16* vwin;
-  const int32_t* lat_len;
-  const int32_t* win_len;
-  int window;               // W (0: no window)
-  long long t_cap;
-  float wscale;             // sm_scale * log2 e
 };
-
-// A decode step's exact window inside the combine workgroup (b, j): head j attends over the live
-// slots of its KV head g (ring positions L .. L + wl - 1, slot = position mod W) in float32 on the
-// VALU, in the latent partials' base-2 units. 128 slots per round: thread (u = tid / 2, h = tid % 2)
-// forms half of slot u's score (64 dims, 16-byte loads); thread (c8 = tid % 16, sg = tid / 16)
-// accumulates columns 8 c8 .. 8 c8 + 7 over slots 8 sg .. 8 sg + 7 with a running max (the value
-// rows are loaded before the scores are known). Leaves m_w, l_w in the returned pair and the
-// unnormalised output in ow[0 .. 127]. NaN scores become +inf (as in the latent kernel).
-template <typename QT>
-__device__ void combine_window(const CombineArgs& a, int b, int j, float* qs, float* sc, float* owp, float* red,
-                               float& m_w, float& l_w) {
-  const int tid = threadIdx.x;
-  const int g = j / (a.Hq / a.Hkv);
-  const int W = a.window;
-  long long Ll = (unsigned)a.lat_len[b] & 0x00FFFFFFu;
-  Ll = Ll > a.t_cap ? a.t_cap : Ll;
-  const int L = (int)Ll;
-  int wl = a.win_len[b];
-  wl = wl < 0 ? 0 : (wl > W ? W : wl);
-  if (tid < kFoldD) qs[tid] = to_f32(((const QT*)a.q)[((size_t)b * a.Hq + j) * kFoldD + tid]) * a.wscale;
-  const int u = tid >> 1, h = tid & 1;
-  const int c8 = tid & 15, sg = tid >> 4;
-  float m = -INFINITY, l = 0.f;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int c0 = 0; c0 < wl; c0 += 128) {
-    // value rows of this thread's 8 slots, issued before the scores are formed
-    u32x4 vr[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = c0 + 8 * sg + i;
-      vr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (t < wl) vr[i] = *(const u32x4*)(a.vwin + ((size_t)b * W + (L + t) % W) * a.D + g * kFoldD + 8 * c8);
-    }
-    u32x4 kr[8];
-    const bool kval = c0 + u < wl;
-    const size_t krow = ((size_t)b * W + (L + c0 + u) % W) * a.D + g * kFoldD + 64 * h;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kr[i] = kval ? *(const u32x4*)(a.kwin + krow + 8 * i) : u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();                                       // qs visible; sc of the last round read
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x8 kv8 = __builtin_bit_cast(bf16x8, kr[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += qs[64 * h + 8 * i + e] * (float)kv8[e];
-    }
-    const float s = part + __shfl_xor(part, 1);
-    if (h == 0) sc[u] = kval ? ((s != s) ? INFINITY : s) : -INFINITY;
-    __syncthreads();
-    float mx = -INFINITY;
-    for (int t = 0; t < 128; t += 4) {
-      const f32x4 v4 = *(const f32x4*)(sc + t);
-      mx = fmaxf(fmaxf(mx, fmaxf(v4[0], v4[1])), fmaxf(v4[2], v4[3]));
-    }
-    const float mnew = fmaxf(m, mx);
-    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = mnew == -INFINITY ? 0.f : fast_exp2(sc[8 * sg + i] - mnew);
-      ps += p;
-      const bf16x8 v8 = __builtin_bit_cast(bf16x8, vr[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += p * (float)v8[e];
-    }
-    if (c8 == 0) red[sg] = ps;
-    __syncthreads();
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lsum += red[i];
-    l = l * alpha + lsum;
-    m = mnew;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) owp[sg * kFoldD + 8 * c8 + e] = acc[e];
-  __syncthreads();
-  if (tid < kFoldD) {
-    float o = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o += owp[i * kFoldD + tid];
-    owp[16 * kFoldD + tid] = o;                            // ow
-  }
-  __syncthreads();
-  m_w = m;
-  l_w = l;
-}
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
   const int tid = threadIdx.x;
@@ -1183,16 +1036,12 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   float* part = cs;                       // [4][pw] merge partials, reused as [16][128]
   float* ahat = part + 4 * pw;            // [rv_pad16]
   float* ws = ahat + a.rv_pad16;          // [nsplit]
-  float* red = ws + a.nsplit;             // [16]
-  float* wsc = red + 16;                  // window: q [128], scores [128], partial outputs [17][128]
+  float* red = ws + a.nsplit;             // [8]
   const size_t base = (size_t)b * a.nsplit;
 
   float mw = -INFINITY, lw = 0.f;
   const float* wp = a.win_part + ((size_t)b * a.Hq + j) * (a.d + 2);
-  if (a.window > 0) {
-    combine_window<BT>(a, b, j, wsc, wsc + kFoldD, wsc + 2 * kFoldD, red, mw, lw);
-    wp = wsc + 2 * kFoldD + 16 * kFoldD;  // ow
-  } else if (a.exact) {
+  if (a.exact) {
     mw = wp[a.d];
     lw = wp[a.d + 1];
   }
@@ -1352,19 +1201,39 @@ static void fold_args(const DecodePlan& p, const lr_layer_cache* c, const void* 
   *nfold = ((p.rk_pad / 16 + 3) / 4) * p.Hkv * ((p.B + nq - 1) / nq);
 }
 
+// The first launch of a decode call: the fold, the exact window (W > 0) and, for a decode step,
+// the append of the step's token.
+static hipError_t decode_front(const DecodePlan& p, const AppendPlan* ap, const lr_layer_cache* c, const void* q,
+                               const void* k_new, const void* v_new, void* ws, hipStream_t st) {
+  unsigned char* w = (unsigned char*)ws;
+  const float scale = p.sm_scale * kLog2e;
+  FoldArgs f;
+  int nfold = 0;
+  fold_args(p, c, q, w + p.off_qt, scale, &f, &nfold);
+  FrontPlan fp;
+  fp.latent = p.latent;
+  fp.nck = ap ? (ap->rk + 63) / 64 : 0;
+  fp.ncv = ap ? (ap->rv + 63) / 64 : 0;
+  fp.n_append = ap ? (fp.nck + fp.ncv) * ((ap->B + 15) / 16) : 0;
+  if (p.latent == LR_F32) {
+    fp.nfx = (p.rk_pad + 63) / 64;
+    fp.nfy = p.Hkv;
+    fp.n_fold = fp.nfx * fp.nfy * p.B;
+  } else {
+    fp.nfx = (p.rk_pad / 16 + 3) / 4;
+    fp.nfy = p.Hkv;
+    fp.n_fold = nfold;
+  }
+  fp.n_win = p.window > 0 ? p.B * p.Hkv : 0;
+  fp.window = p.window;
+  fp.t_cap = p.t_cap;
+  return launch_front(fp, ap, c, k_new, v_new, f, (float*)(w + p.off_win), scale, st);
+}
+
 hipError_t launch_decode_step(const AppendPlan& ap, const DecodePlan& p, const lr_layer_cache* c, const void* k_new,
                               const void* v_new, const void* q, void* out, int out_dtype, void* ws, hipStream_t st,
                               hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (p.latent == LR_F32) {
-    const hipError_t e = launch_append(ap, c, k_new, v_new, nullptr, st);
-    if (e != hipSuccess) return e;
-    return launch_decode(p, c, q, out, out_dtype, ws, st, ev_begin, ev_end);
-  }
-  FoldArgs f;
-  int nfold = 0;
-  fold_args(p, c, q, (unsigned char*)ws + p.off_qt, p.sm_scale * kLog2e, &f, &nfold);
-  const int nfx = (p.rk_pad / 16 + 3) / 4, nfy = p.Hkv;
-  const hipError_t e = launch_step_front(ap, c, k_new, v_new, f, nfx, nfy, nfold, p.latent == LR_I4G32, st);
+  const hipError_t e = decode_front(p, &ap, c, q, k_new, v_new, ws, st);
   if (e != hipSuccess) return e;
   return launch_decode(p, c, q, out, out_dtype, ws, st, ev_begin, ev_end, nullptr, nullptr, true);
 }
@@ -1376,29 +1245,31 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   __bf16* qt = (__bf16*)(w + p.off_qt);
   const float scale = p.sm_scale * kLog2e;
 
-  // Exact keys. A decode step (no chunk rows): the window is attended inside the combine, per head.
-  // A prefill chunk (the window and the chunk's own rows, causally): for bf16 queries the
-  // matrix-core exact-keys kernel runs before the latent kernel, for float32 queries B extra
-  // workgroups of the decode kernel (window_block); both leave a partial the combine merges.
+  // Exact keys. A decode step (no chunk rows): the window workgroups of the first launch. A prefill
+  // chunk (the window and the chunk's own rows, causally): for bf16 queries the matrix-core
+  // exact-keys kernel runs before the latent kernel, for float32 queries B extra workgroups of the
+  // decode kernel (window_block); each leaves a partial the combine merges.
   const bool decode_step = k_chunk == nullptr;
   const bool exact_mfma = !decode_step && p.exact && p.latent != LR_F32;
-  float* win_part = (float*)(w + p.off_win);
 
-  // 1. fold
+  // 1. fold (+ the window of a decode step), unless a decode step's first launch already ran it
   if (!fold_done) {
-    dim3 grid((p.rk_pad + 63) / 64, p.Hkv, p.B);
-    if (p.latent == LR_F32)
-      hipLaunchKernelGGL(lr_fold<float>, grid, dim3(256), 0, st, (const float*)q, (const float*)c->bk, qt,
-                         p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
-    else {
+    hipError_t e;
+    if (decode_step) {
+      e = decode_front(p, nullptr, c, q, nullptr, nullptr, ws, st);
+    } else if (p.latent == LR_F32) {
+      hipLaunchKernelGGL(lr_fold<float>, dim3((p.rk_pad + 63) / 64, p.Hkv, p.B), dim3(256), 0, st, (const float*)q,
+                         (const float*)c->bk, qt, p.Hq, p.Hkv, p.D, p.rk, p.rk_pad, scale);
+      e = hipGetLastError();
+    } else {
       FoldArgs f;
       int nfold = 0;
       fold_args(p, c, q, qt, scale, &f, &nfold);
       const dim3 fgrid((p.rk_pad / 16 + 3) / 4, p.Hkv, (p.B + f.nq - 1) / f.nq);
       if (p.latent == LR_I4G32) hipLaunchKernelGGL(lr_fold_mfma<true>, fgrid, dim3(256), 0, st, f);
       else hipLaunchKernelGGL(lr_fold_mfma<false>, fgrid, dim3(256), 0, st, f);
+      e = hipGetLastError();
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
 
@@ -1484,18 +1355,9 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   ca.rv = p.rv;
   ca.rv_pad16 = p.rv_pad16;
   ca.nsplit = p.nsplit;
-  ca.exact = decode_step ? 0 : p.exact;
+  ca.exact = p.exact;
   ca.i4_order = p.latent == LR_I4G32;
-  ca.q = q;
-  ca.kwin = (const __bf16*)c->kwin;
-  ca.vwin = (const __bf16*)c->vwin;
-  ca.lat_len = c->lat_len;
-  ca.win_len = c->win_len;
-  ca.window = decode_step ? p.window : 0;
-  ca.t_cap = p.t_cap;
-  ca.wscale = scale;
-  const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 16 +
-                              (ca.window > 0 ? 19 * kFoldD : 0)) * sizeof(float);
+  const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);
   const bool f32b = p.latent == LR_F32;
   const bool f32o = out_dtype == LR_F32;

@@ -10,6 +10,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kGroup = 32;        // int4 quantisation group along the rank
@@ -49,6 +51,15 @@ __device__ __forceinline__ void barrier_lds() {
 constexpr int kCachePolicyNT = 2;
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, LR_LDS(lds_wave_base), 16, 0, kCachePolicyNT);
+}
+
+// Value operand through the gfx950 transpose read: within each 16-lane group g, lane j's element
+// e comes from the address given by lane 16g + 4e + j/4, at element offset j%4. Lane
+// 16g + 4e + q therefore points at row 4g+e, column 4q of the 16-column block, and every lane j
+// receives column j of rows 4g .. 4g+3: the A operand of the 16x16x16 product with K = token.
+__device__ __forceinline__ bf16x4 v_operand_tr(const unsigned char* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                        (__attribute__((address_space(3))) s16x4*)(p)));
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

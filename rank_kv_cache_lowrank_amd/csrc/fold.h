@@ -27,7 +27,7 @@ constexpr int kFoldD = 128;     // head_dim handled by the fold (validated on th
 // kernel picks each head's power-of-two scale and rounds to fp16. Else bf16 output.
 // ---------------------------------------------------------------------------------------------
 struct FoldArgs {
-  const __bf16* q;
+  const __bf16* q;          // (float32 for the VALU fold)
   const __bf16* bk;
   void* qt;
   int Hq, Hkv, D, rk, rk_pad;
@@ -86,8 +86,72 @@ __device__ __forceinline__ void fold_body(const FoldArgs& f, int bx, int by, int
 }
 
 
-// A decode step's first launch (append.hip): the append's workgroups and the fold's in one grid.
-hipError_t launch_step_front(const AppendPlan& p, const lr_layer_cache* c, const void* k_new, const void* v_new,
-                             const FoldArgs& f, int nfx, int nfy, int nfold, bool i4, hipStream_t st);
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* out);
+template <>
+__device__ __forceinline__ void load8<__bf16>(const __bf16* p, float* out) {
+  const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* out) {
+  const f32x4 v0 = *(const f32x4*)p;
+  const f32x4 v1 = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { out[e] = v0[e]; out[4 + e] = v1[e]; }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fold with float32 queries and bases (float32 latents), on the VALU:
+// qt[b][j][k] = scale * sum_c q[b][j][c] * Bk[k][g(j)*d + c], bf16, zero-padded.
+// Workgroup (bx, by = g, bz = b) of rk_pad/64 x Hkv x B, 256 threads: thread (hs, k) computes heads
+// hs, hs+4, ... of KV head g for latent index k; its 512-byte slice of Bk row k is loaded with
+// independent 16-byte loads.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void fold_f32_body(const FoldArgs& f, int bx, int g, int b, float* qs /* [32 x 128] LDS */) {
+  const float* __restrict__ q = (const float*)f.q;
+  const float* __restrict__ bk = (const float*)f.bk;
+  __bf16* __restrict__ qt = (__bf16*)f.qt;
+  const int Hq = f.Hq, grp = f.Hq / f.Hkv, D = f.D, rk = f.rk, rk_pad = f.rk_pad;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < grp * kFoldD; i += 256) qs[i] = q[((size_t)b * Hq + g * grp) * kFoldD + i] * f.scale;
+  __syncthreads();
+  const int k = bx * 64 + (tid & 63);
+  const int hs = tid >> 6;
+  if (k >= rk_pad) return;
+  __bf16* out = qt + (size_t)b * kHeadsPad * rk_pad + k;
+  float bvals[kFoldD];
+  if (k < rk) {
+    const float* brow = bk + (size_t)k * D + g * kFoldD;
+#pragma unroll
+    for (int c = 0; c < kFoldD; c += 8) load8<float>(brow + c, bvals + c);
+  }
+  for (int h = hs; h < grp; h += 4) {
+    float acc = 0.f;
+    if (k < rk) {
+      const float* qh = qs + h * kFoldD;
+#pragma unroll
+      for (int c = 0; c < kFoldD; ++c) acc += qh[c] * bvals[c];
+    }
+    out[(size_t)(g * grp + h) * rk_pad] = (__bf16)acc;
+  }
+  if (g == 0)
+    for (int j = Hq + hs; j < kHeadsPad; j += 4) out[(size_t)j * rk_pad] = (__bf16)0.f;
+}
+
+// The first launch of a decode call (append.hip): workgroups [0, n_append) append the step's
+// token (lowrank_decode_step only), [n_append, n_append + n_fold) fold the query, and the rest
+// (W > 0) attend over the exact window, one per (sequence, KV head).
+struct FrontPlan {
+  int latent;               // lr_dtype of the latents (selects the fold and the append's bases)
+  int n_append, nck, ncv;   // append workgroups and their column chunks (0 when no append)
+  int n_fold, nfx, nfy;     // fold workgroups and the fold's grid extents (x, y; z follows)
+  int n_win;                // window workgroups (B x Hkv, or 0)
+  int window;               // W
+  long long t_cap;
+};
+hipError_t launch_front(const FrontPlan& fp, const AppendPlan* ap, const lr_layer_cache* c, const void* k_new,
+                        const void* v_new, const FoldArgs& f, float* win_part, float wscale, hipStream_t st);
 
 }  // namespace lr
