@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblowrank_attn.so")
+# LOWRANK_ATTN_LIB selects another build of the library (e.g. a host-only sanitizer build for tests)
+LIB_PATH = os.environ.get("LOWRANK_ATTN_LIB") or os.path.join(HERE, "liblowrank_attn.so")
 
 LR_OK, LR_EINVAL, LR_EUNSUPPORTED, LR_EWORKSPACE, LR_EHIP = 0, -1, -2, -3, -4
 LR_F32, LR_BF16, LR_I4G32 = 0, 1, 2

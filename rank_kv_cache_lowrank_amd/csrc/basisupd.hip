@@ -95,13 +95,6 @@ __global__ __launch_bounds__(256) void lr_bu_finish(BuArgs a) {
 
 static inline size_t bu_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace: staged rows, unit weights, the SVD's own workspace, B' (float32), the spectrum.
-size_t basis_update_workspace_bytes(int r, int n, int D) {
-  const int m = r + n;
-  return bu_align((size_t)m * D * 2) + bu_align((size_t)m * 4) + bu_align(svd_workspace_bytes(m, D)) +
-         bu_align((size_t)D * D * 4) + bu_align((size_t)D * 4);
-}
-
 hipError_t launch_basis_update(const void* basis, int f32, const float* sigma, int r, const void* rows, int n, int D,
                                int r_new, int sweeps, void* basis_new, float* sigma_new, void* w, void* ws,
                                hipStream_t st) {

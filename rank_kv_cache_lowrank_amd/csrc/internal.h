@@ -192,6 +192,13 @@ hipError_t launch_basis_update(const void* basis, int f32, const float* sigma, i
 hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, long long n_take, int r_min,
                                 int g, int nb, int32_t* ranks, void* ws, hipStream_t st);
 
+// Host plans of the rebase and weighted-SVD kernels (plans.cpp), shared with their launchers.
+constexpr int kRbConsumers = 4;     // rebase: waves that hold W blocks and multiply (one per SIMD)
+constexpr int kJb = 16;             // weighted SVD: Jacobi block size
+constexpr int kJs = 2 * kJb;        // its pair subproblem size (32)
+constexpr int kRqRows = 64;         // rows of G0 per workgroup of the Rayleigh quotients
+int svd_nsplit(int n);              // sample ranges of the Gram
+
 struct RebaseShape {
   int nks_t, nb, col_chunk, nchunk;
 };

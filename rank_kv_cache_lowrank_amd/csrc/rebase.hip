@@ -53,7 +53,6 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {   // round t
 
 constexpr int kRbTile = 16;          // rows per tile (the MFMA's N)
 constexpr int kRbProducers = 2;      // waves 0..1 stream the tiles into LDS
-constexpr int kRbConsumers = 4;      // waves 2..5 multiply: one per SIMD
 constexpr int kRbThreads = (kRbProducers + kRbConsumers) * 64;
 constexpr int kRbMaxStages = 32;
 
@@ -333,23 +332,6 @@ __global__ __launch_bounds__(256) void lr_rebase_f32(RebaseArgs a) {
 // Launch shape shared by K and V: K-step bound NKS (template), blocks of 16 new coordinates
 // per consumer NB (template; bounded by registers), chunks of new coordinates (each chunk is
 // one workgroup's consumers; every chunk re-reads the rows).
-static int rb_nks_t(int r_old) {
-  const int nks = (r_old + 31) / 32;
-  return nks <= 4 ? 4 : (nks <= 8 ? 8 : (nks <= 12 ? 12 : 16));
-}
-static int rb_nb_max(int nks_t) { return nks_t == 16 ? 2 : (nks_t == 12 ? 3 : (nks_t == 8 ? 4 : 8)); }
-
-void rebase_shape(int r_old, int r_new, RebaseShape* s) {
-  s->nks_t = rb_nks_t(r_old);
-  const int per = kRbConsumers * rb_nb_max(s->nks_t);   // blocks one workgroup holds
-  const int nblk = (r_new + 15) / 16;
-  const int nchunk = (nblk + per - 1) / per;
-  const int blk_chunk = (nblk + nchunk - 1) / nchunk;
-  s->nb = (blk_chunk + kRbConsumers - 1) / kRbConsumers;
-  s->col_chunk = s->nb * kRbConsumers * 16;
-  s->nchunk = (r_new + s->col_chunk - 1) / s->col_chunk;
-}
-
 static hipError_t launch_rebase_bf16(int nks_t, int nb, dim3 grid, size_t lds, hipStream_t st,
                                      const RebaseArgs& a) {
   int dev = 0;

@@ -222,8 +222,6 @@ __device__ __forceinline__ void circle_pair(int n, int r, int k, int& p, int& q)
   }
 }
 
-constexpr int kJb = 16;                   // Jacobi block size
-constexpr int kJs = 2 * kJb;              // pair subproblem size (32)
 constexpr int kJacobiInner = 1;           // cyclic sweeps over a pair's 32x32 block per round
 
 // One workgroup per block pair: the pair's 32x32 block S of G is diagonalised in LDS by cyclic
@@ -395,7 +393,6 @@ __global__ __launch_bounds__(256) void lr_jacobi_apply(SvdArgs a) {
 }
 
 constexpr int kRqCols = 16;   // columns of V per workgroup in lr_svd_rayleigh
-constexpr int kRqRows = 64;   // rows of G0 per workgroup in lr_svd_rayleigh
 
 // lambda_k = v_k^T G0 v_k / v_k^T v_k for the columns v_k of V, as D / 64 partial quadratic
 // forms: workgroup (column group k0 .. k0+15, row range j0 .. j0+63) sums
@@ -567,19 +564,6 @@ __global__ __launch_bounds__(256) void lr_svd_basis(SvdArgs a) {
     if (c1 < a.D) row[c1] = (__bf16)(sg * x1);
   }
 }
-
-int svd_nsplit(int n) {
-  int s = (n + 255) / 256;
-  return s < 1 ? 1 : (s > 64 ? 64 : s);
-}
-
-size_t svd_workspace_bytes(int n, int D) {
-  const size_t dd = (size_t)D * D * 4;
-  return (size_t)svd_nsplit(n) * dd + 3 * dd + (size_t)(D / kJs) * kJs * kJs * 4 +
-         (size_t)(D / kRqRows + 1) * D * 8 + (size_t)D * 4 + 1024;
-}
-
-size_t svd_workspace_stride(int n, int D) { return (svd_workspace_bytes(n, D) + 255) / 256 * 256; }
 
 hipError_t launch_sens_svd(const void* x, const float* w, int n_mat, int n, int D, int rank, int sweeps, void* basis,
                            int basis_f32, float* sigma, void* ws, hipStream_t st) {
