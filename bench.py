@@ -89,11 +89,13 @@ def step_bytes(cfg, rk, rv, lat_len, win_len, n_new):
                 total=lat + win + bases + q_out + append)
 
 
-def cpu_baseline(cfg, li, budget_s: float = 6.0, reps: int = 3):
+def cpu_baseline(cfg, li, budget_s: float = 8.0, reps: int = 3, d1_budget_s: float = 4.0):
     """Times the fp64 oracle on the host cores, in the same run as the GPU measurement:
     D2 (latent domain, the algorithmic counterpart of the kernels) over whole sequences of the same
-    workload, as many as fit `budget_s` (at least one), `reps` times (median); and D1 (reconstruct
-    K = Zk Bk, V = Zv Bv, then plain attention) over one whole sequence, `reps` times (median)."""
+    workload, as many as fit a third of `budget_s` (at least one), then that sample repeated until
+    `budget_s` of CPU time is spent (at least `reps` runs; median); and D1 (reconstruct K = Zk Bk,
+    V = Zv Bv, then plain attention) over one whole sequence, repeated the same way within
+    `d1_budget_s`. About 10-15 s of host work in all."""
     from threadpoolctl import threadpool_info
     from oracle import attention as OA
     from oracle import quant as OQ
@@ -136,24 +138,28 @@ def cpu_baseline(cfg, li, budget_s: float = 6.0, reps: int = 3):
            batches=[b], **win)
         return time.perf_counter() - t0
 
-    # D2: as many whole sequences as fit the budget, then the same sample `reps` times
+    def repeated(once, first, budget):
+        times = [first]
+        while len(times) < reps or (sum(times) < budget and len(times) < 100):
+            times.append(once())
+        return float(np.median(times)), len(times)
+
+    # D2: as many whole sequences as fit a third of the budget, then that sample repeated
     done, t_first = 0, 0.0
     while done < cfg.batch and (done == 0 or t_first < budget_s / reps):
         t_first += run(OA.decode_latent, done)
         done += 1
-    times = [t_first] + [sum(run(OA.decode_latent, b) for b in range(done)) for _ in range(reps - 1)]
-    t2 = float(np.median(times))
+    t2, n2 = repeated(lambda: sum(run(OA.decode_latent, b) for b in range(done)), t_first, budget_s)
     nbytes = sum(seq_bytes(b) for b in range(done))
-    d1 = [run(OA.decode_reconstruct, 0) for _ in range(reps)]
-    t1 = float(np.median(d1))
+    t1, n1 = repeated(lambda: run(OA.decode_reconstruct, 0), run(OA.decode_reconstruct, 0), d1_budget_s)
     lens = "x".join(str(int(x)) for x in li.lat_len[:done]) if cfg.len_range else str(int(li.lat_len[0]))
     return dict(value=nbytes / t2 / 1e12, unit="TB/s", cores=int(threads), kind="oracle",
                 sample=f"D2 (latent-domain fp64 oracle): {done} of {cfg.batch} sequences x {lens} tokens"
-                       f"{' (+ window)' if cfg.window else ''} of layer {li.layer}, median of {reps} runs "
-                       f"{t2:.2f} s; latent bytes per second in the benchmark's units",
+                       f"{' (+ window)' if cfg.window else ''} of layer {li.layer}, median of {n2} runs "
+                       f"{t2:.3f} s; latent bytes per second in the benchmark's units",
                 us_per_layer_step=t2 / done * cfg.batch * 1e6,
                 d1={"value": seq_bytes(0) / t1 / 1e12, "unit": "TB/s", "sample": f"D1 (reconstruct K, V then "
-                    f"attend, fp64): sequence 0 ({int(li.lat_len[0])} tokens), median of {reps} runs {t1:.2f} s",
+                    f"attend, fp64): sequence 0 ({int(li.lat_len[0])} tokens), median of {n1} runs {t1:.3f} s",
                     "us_per_layer_step": t1 * cfg.batch * 1e6})
 
 
@@ -221,14 +227,24 @@ def copy_probe(torch, dev):
     log(f"copy probe: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
 
 
+def capture_graph(torch, fn):
+    """One HIP graph holding the launches fn makes on the current stream (captured on a side
+    stream: nothing runs during capture; every replay runs all of them again)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
 def decode28_bench(args):
     """The full 28-layer decode step of the global-rank-allocation workload: batch 16, total
     lengths per sequence drawn from U{2048..8192} with the last 128 tokens kept exact in the
     window ring, per-layer ranks rK, rV drawn independently from {128, 136, ..., 512}, bf16
-    latents. A step = for each of the 28 layers, lowrank_kv_append (one new token per sequence:
-    it enters the window and the oldest window token is projected and stored as a latent row)
-    then lowrank_attn_decode. The lengths start W+K tokens short, so the last timed step attends
-    over exactly the drawn lengths. The caches of all layers (~5 GB) far exceed the 256 MB
+    latents. A step = for each of the 28 layers, lowrank_decode_step (one new token per sequence
+    enters the window, the oldest window token is projected and stored as a latent row, and the
+    layer's attention runs). The lengths start W + 2K tokens short, so the last step of the
+    event pass attends over exactly the drawn lengths. With --graph the timed pass replays one
+    HIP graph of the 28 layers' launches. The caches of all layers (~5 GB) far exceed the 256 MB
     Infinity Cache, so every step streams from HBM."""
     import torch
     import rank_kv_cache_lowrank_amd as lr
@@ -283,11 +299,15 @@ def decode28_bench(args):
         if i % 5 == 0:
             log(f"warm-up step {i} enqueued")
     torch.cuda.synchronize()
+    graph = capture_graph(torch, full_step) if args.graph else None
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(K):
-        full_step()
+        if graph is not None:
+            graph.replay()
+        else:
+            full_step()
     stop.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / K
@@ -351,7 +371,8 @@ def decode28_bench(args):
                    "rank_range": [int(min(cfg.rank_choices)), int(max(cfg.rank_choices))],
                    "latent": cfg.latent, "q_heads": cfg.n_q_heads, "kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "new_tokens_per_step": n_new,
-                   "step": "28 x lowrank_decode_step (append + fold, latent kernel, combine with the window)",
+                   "step": "28 x lowrank_decode_step (append + fold + window, latent kernel, combine)"
+                           + ("; timed pass replayed from one HIP graph" if args.graph else ""),
                    "parallelism": "single GPU"},
         "step_bytes": int(step_total),
         "step_span_ms_events": round(float(np.median(span_ms)), 5),
@@ -609,6 +630,44 @@ def sensvd_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def basisupd_bench(args):
+    """Block-incremental basis update of one KV matrix: a rank-256 history (D = 512) takes the 128
+    tokens of one window's worth of evictions and keeps rank 256 (bf16 basis): staging, the Gram of
+    the 384 stacked rows on the matrix cores, block Jacobi, and the sync weights W = B' B^T. Once
+    per block of evictions, not per token; the Jacobi rounds are launch-latency bound."""
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+
+    dev = "cuda"
+    r, n, dim = 256, 128, 512
+    rng = np.random.default_rng(21)
+    q, rr = np.linalg.qr(rng.standard_normal((dim, r)))
+    B = (q * np.sign(np.diag(rr))[None, :]).T
+    sigma = np.sqrt(4096.0 / np.arange(1, r + 1))
+    Y = rng.standard_normal((n, dim)) / np.sqrt(dim) * sigma[0]
+    bd = torch.from_numpy(B.astype(np.float32)).to(torch.bfloat16).to(dev)
+    sd = torch.from_numpy(sigma.astype(np.float32)).to(dev)
+    yd = torch.from_numpy(Y.astype(np.float32)).to(torch.bfloat16).to(dev)
+    bn = torch.empty(r, dim, dtype=torch.bfloat16, device=dev)
+    sn = torch.empty(r, dtype=torch.float32, device=dev)
+    w = torch.empty(r, (r + 7) // 8 * 8, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lr.lowrank_basis_update_workspace_size(r, n, dim), dtype=torch.uint8, device=dev)
+    ms = _timed_calls(lambda: lr.lowrank_basis_update(bd, sd, yd, r, bn, sn, w, ws), args.steps, args.warmup)
+    assert torch.isfinite(sn).all()
+    flops = float(r + n) * dim * (dim + 1)
+    rec = {"metric": "block-incremental basis update of one KV matrix: ms per call", "value": round(ms, 4),
+           "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"basis update r{r} + {n} rows D{dim} -> r{r}", "rank": r, "rows": n,
+                      "dim": dim, "rank_new": r, "sweeps": 10, "parallelism": "single GPU"},
+           "roofline": {"bound": "latency", "kernel": "whole call (stage, Gram, block Jacobi, finish)",
+                        "achieved": round(flops / (ms * 1e-3) / 1e12, 4), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 7),
+                        "traffic": None, "flops_per_launch": flops}}
+    print(json.dumps(rec), flush=True)
+
+
 def rankalloc_bench(args):
     """Global rank allocation for the 28-layer model (56 spectra of 512, ranks 128..512 by 8,
     budget 70% of full rank): three short launches (gains, split ordered counts, selection)."""
@@ -646,12 +705,15 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated over the steps (0: enough that the copies exceed 2 x 256 MB)")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: time the steps as replays of HIP graphs captured from them")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 256 MiB device copy (the counter calibration reference)")
-    ap.add_argument("--op", choices=("decode", "rebase", "prefill", "sensvd", "rankalloc"), default="decode",
+    ap.add_argument("--op", choices=("decode", "rebase", "prefill", "sensvd", "rankalloc", "basisupdate"),
+                    default="decode",
                     help="decode: the decode step (default); rebase: the historical-coordinate sync; "
                          "prefill: chunked prefill attention; sensvd: sensitivity-weighted SVD basis; "
-                         "rankalloc: global rank allocation")
+                         "rankalloc: global rank allocation; basisupdate: block-incremental basis update")
     ap.add_argument("--samples", type=int, default=131072,
                     help="--op sensvd: calibration rows per matrix (batched default: 16384)")
     ap.add_argument("--matrices", type=int, default=1, help="--op sensvd: matrices per (batched) call")
@@ -680,6 +742,9 @@ def main():
         return
     if args.op == "rankalloc":
         rankalloc_bench(args)
+        return
+    if args.op == "basisupdate":
+        basisupd_bench(args)
         return
     dev = "cuda"
     cfg = synth.CONFIGS[args.config]
@@ -727,20 +792,27 @@ def main():
     for cache in caches:
         cache.tensors["lat_len"].copy_(torch.from_numpy(np.full(cfg.batch, L0, np.int32)).to(dev))
 
+    def launch(c, events=None):
+        lr.lowrank_decode_step(model, 0, caches[c], k_new, v_new, q, out, T, ws, nsplit=args.nsplit, events=events)
+
     def step(i, events=None):
-        cache = caches[i % n_copies]
-        lr.lowrank_decode_step(model, 0, cache, k_new, v_new, q, out, T, ws, nsplit=args.nsplit, events=events)
+        launch(i % n_copies, events)
         return np.full(cfg.batch, L0 + (i // n_copies + 1) * n_new, np.int32)   # lengths the step attends
 
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+    graphs = [capture_graph(torch, lambda c=c: launch(c)) for c in range(n_copies)] if args.graph else None
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     lens_a = []
     start.record()
     for i in range(W, W + K):
-        lens_a.append(step(i))
+        if graphs is not None:
+            graphs[i % n_copies].replay()
+            lens_a.append(np.full(cfg.batch, L0 + (i // n_copies + 1) * n_new, np.int32))
+        else:
+            lens_a.append(step(i))
     stop.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / K
@@ -795,7 +867,8 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": T, "rank_k": li.rank_k,
                    "rank_v": li.rank_v, "latent": cfg.latent, "q_heads": cfg.n_q_heads,
                    "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "new_tokens_per_step": n_new,
-                   "step": "lowrank_decode_step (append + fold, latent kernel, combine)",
+                   "step": "lowrank_decode_step (append + fold, latent kernel, combine)"
+                           + ("; timed pass replayed from HIP graphs" if args.graph else ""),
                    "parallelism": "single GPU"},
         "step_bytes": int(step_total),
         "step_span_us_events": round(float(np.median(span_ms)) * 1e3, 2),
