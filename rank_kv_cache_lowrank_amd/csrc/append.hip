@@ -95,13 +95,15 @@ struct AppendArgs {
 
 // One launch does the whole append: projection, storage, window ring and lengths.
 //
-// grid (nck + ncv, ceil(B / 16)): workgroup (x, y) owns latent columns 64c .. 64c + 63 of K (x < nck,
-// c = x) or of V (c = x - nck) for the 16 sequences 16y .. 16y + 15, and every row this call stores
-// for them. Per row index e (0 .. n_new - 1): the 16 sequences' source rows (the new token, or the
-// window token being evicted) are staged in LDS as the bf16 A operand, z [16 seq, 64 col] = X P on
-// the matrix cores (bf16 bases: 16x16x32 with float32 accumulation, wave w owning columns
-// 16w .. 16w + 15; float32 bases: the VALU, float32 throughout), and wave w stores the rows of
-// sequences 4w .. 4w + 3 (store_chunk: bf16 rounding, or int4 quantisation of the 2 groups).
+// grid (nck + ncv, ceil(B / 16)): workgroup (x, y) owns latent columns 32c .. 32c + 31 of K
+// (x < nck, c = x) or of V (c = x - nck) for sequences 16y .. 16y + 15, and is the only writer
+// of them. Per row index e (0 .. n_new - 1): the 16 sequences' source rows (the new token, or
+// the window token being evicted) are staged in LDS as the bf16 A operand, and z [16 seq, 32 col]
+// = X P runs on the matrix cores (bf16 bases: 16x16x32 with float32 accumulation; wave w owns
+// columns 16 (w & 1) .. +15 over half (w >> 1) of each chunk of D, and the two halves' partial
+// sums are added in LDS; float32 bases: the VALU, float32 throughout). Each wave then stores the
+// rows of sequences 4w .. 4w + 3, two at a time (lanes 0-31 and 32-63; store_chunk: bf16
+// rounding, or int4 quantisation of the one group).
 //
 // The window ring and the lengths may change only after every workgroup of a sequence has read
 // them (and the evicted ring slots). Each workgroup, once its reads of a sequence are done, adds
@@ -109,33 +111,34 @@ struct AppendArgs {
 // 0..23 (t_cap < 2^24, so every reader masks it off). The workgroup that sees the count reach
 // gx - 1 is the last one: it writes the new tokens into the ring and the final lengths, which
 // also clears the count. So a call leaves the lengths clean, and no buffer needs clearing first.
+//
+// Latency: the lengths go out first, each thread loading those of the sequences it stages, then
+// the projection columns, then the source rows (an evicted slot's address needs its lengths; the
+// projection's loads stay in flight meanwhile), so the workgroup waits for about one round trip.
 constexpr int kAppendSeqs = 16;       // sequences per workgroup (the matrix-core M)
-constexpr int kAppendCols = 64;       // latent columns per workgroup (4 waves x 16; 2 int4 groups)
 constexpr int kAppendK = 512;         // source-row chunk along D staged at a time
 constexpr int kAppendLdsX = kAppendK * 2 + 16;   // LDS row stride of a staged source chunk (bytes)
-constexpr unsigned kLenMask = 0x00FFFFFFu;
 constexpr unsigned kArrival = 1u << 24;
+static_assert(kAppendCols == 32, "one int4 group per workgroup and row");
 
-__device__ __forceinline__ int clamp_len(int32_t raw, long long cap) {
-  const unsigned v = (unsigned)raw & kLenMask;
-  return (int)((long long)v > cap ? cap : (long long)v);
-}
-
-// readers: workgroups that read each sequence's lengths and ring (nck + ncv, plus a decode step's
-// window workgroups, which read the ring in the same launch).
-constexpr int kAppendLds = kAppendSeqs * kAppendLdsX + kAppendSeqs * kAppendCols * 4 + 4 * kAppendSeqs * 4;
+// readers: the workgroups that read each sequence's lengths and ring (nck + ncv), or 0 inside a
+// decode step's front launch, where the lengths and the ring are left as they were and the step's
+// last launch finishes them (step_finish).
+constexpr int kAppendLds = kAppendSeqs * kAppendLdsX + 2 * kAppendSeqs * kAppendCols * 4 + 4 * kAppendSeqs * 4;
 
 template <bool F32P>
 __device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int ncv, int bx, int by, int readers,
                                             unsigned char* smem) {
   unsigned char* xs = smem;                                                   // [16][kAppendLdsX] staged rows
-  float (*zt)[kAppendCols] = (float (*)[kAppendCols])(smem + kAppendSeqs * kAppendLdsX);   // [16][64] z tile
-  int* s_len = (int*)(smem + kAppendSeqs * kAppendLdsX + kAppendSeqs * kAppendCols * 4);
+  float (*zt)[kAppendSeqs][kAppendCols] =                                     // [2 halves][16][32] z partials
+      (float (*)[kAppendSeqs][kAppendCols])(smem + kAppendSeqs * kAppendLdsX);
+  int* s_len = (int*)(smem + kAppendSeqs * kAppendLdsX + 2 * kAppendSeqs * kAppendCols * 4);
   int* s_win = s_len + kAppendSeqs;
   int* s_rows = s_win + kAppendSeqs;
   int* s_last = s_rows + kAppendSeqs;
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cb = wave & 1, kh = wave >> 1;                    // column block, half of the K chunk
   const int kv = bx < nck ? 0 : 1;
   const int col0 = (bx - (kv ? nck : 0)) * kAppendCols;
   const int r = kv == 0 ? a.rk : a.rv;
@@ -150,37 +153,49 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int nc
   const int rb = row_bytes_of(a.latent, r, ld);
   const int G = (r + kGroup - 1) / kGroup;
   const bool one_chunk = D <= kAppendK;
+  constexpr int XV = kAppendSeqs * (kAppendK / 8) / 256;     // staged 16-byte granules per thread
+  // with one chunk, staged item i = tid + 256 u is granule c of sequence sq (D / 8 granules a row)
+  auto item_seq = [&](int u, int kw) { return (tid + 256 * u) / (kw / 8); };
 
-  // ---- every load that does not depend on the lengths goes out first, with the lengths' own
-  // loads, so that the workgroup waits for one memory round trip instead of several in a row.
+  // ---- 1. lengths: for the LDS copy, and (W > 0, one chunk) per thread for its staged rows
   int32_t raw_len = 0, raw_win = 0;
   if (tid < nseq) {
     raw_len = a.lat_len[b0 + tid];
     if (W > 0) raw_win = a.win_len[b0 + tid];
   }
-  // P operand of this wave's 16 columns for one K chunk of up to 512 (bf16 bases). The projection
-  // is stored rank-major, pt[i][k] = P[k][i], so lane (li, lg) loads its 8 values
-  // pt[col0 + 16 wave + li][kc + 32 ks + 8 lg .. +7] as one 16-byte load (columns past the rank
-  // read as 0). With one chunk (D <= 512) it is loaded once for all row indices.
-  const int pcol = col0 + 16 * wave + li;
-  bf16x8 pop[F32P ? 1 : kAppendK / 32];
-  auto load_pop = [&](int kc, int nks) {
-    if constexpr (!F32P) {
-      const __bf16* pt = (const __bf16*)(kv == 0 ? a.pk : a.pv) + (size_t)(pcol < r ? pcol : r - 1) * D + kc + 8 * lg;
+  const bool pre_ev = W > 0 && one_chunk;
+  int32_t xlen[XV], xwin[XV];
+  if (pre_ev) {
 #pragma unroll
-      for (int ks = 0; ks < kAppendK / 32; ++ks) {
+    for (int u = 0; u < XV; ++u) {
+      const int sq = item_seq(u, D);
+      xlen[u] = sq < nseq ? a.lat_len[b0 + sq] : 0;
+      xwin[u] = sq < nseq ? a.win_len[b0 + sq] : 0;
+    }
+  }
+  // ---- 2. P operand of this wave's 16 columns over its half of one K chunk (bf16 bases). The
+  // projection is stored rank-major, pt[i][k] = P[k][i], so lane (li, lg) loads its 8 values
+  // pt[col0 + 16 cb + li][k0 + 32 ks + 8 lg .. +7] as one 16-byte load (columns past the rank
+  // read as 0). With one chunk (D <= 512) it is loaded once for all row indices.
+  const int pcol = col0 + 16 * cb + li;
+  bf16x8 pop[F32P ? 1 : kAppendK / 64];
+  auto load_pop = [&](int kc, int kw) {
+    if constexpr (!F32P) {
+      const int nks = kw / 64, k0 = kc + kh * (kw / 2);
+      const __bf16* pt = (const __bf16*)(kv == 0 ? a.pk : a.pv) + (size_t)(pcol < r ? pcol : r - 1) * D + k0 + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < kAppendK / 64; ++ks) {
         pop[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
         if (ks < nks && pcol < r) pop[ks] = *(const bf16x8*)(pt + 32 * ks);
       }
     }
   };
-  if (one_chunk) load_pop(0, D / 32);
-  // Source rows of one row index e and K chunk: item i = tid + 256 u is granule c of sequence sq
-  // (zeros for sequences without a row e). The new token's row (W == 0) does not depend on the
-  // lengths, the evicted window slot does.
-  constexpr int XV = kAppendSeqs * (kAppendK / 8) / 256;
+  if (one_chunk) load_pop(0, D);
+  // ---- 3. source rows of row index e and K chunk kc (zeros for sequences without a row e): the
+  // new token's row (W == 0), or the evicted window slot (W > 0), whose slot comes from the
+  // lengths (per thread for the first row of one chunk, else from LDS)
   u32x4 xv[XV];
-  auto load_x = [&](int e, int kc, int kw, bool from_new) {
+  auto load_x = [&](int e, int kc, int kw, bool per_thread) {
 #pragma unroll
     for (int u = 0; u < XV; ++u) {
       const int i = tid + 256 * u;
@@ -188,19 +203,28 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int nc
       xv[u] = u32x4{0u, 0u, 0u, 0u};
       if (sq < nseq) {
         const int b = b0 + sq;
-        if (from_new) {
+        if (W == 0) {
           if (e < a.n_new) xv[u] = *(const u32x4*)(xnew + ((size_t)b * a.n_new + e) * D + kc + c * 8);
-        } else if (e < s_rows[sq]) {
-          xv[u] = *(const u32x4*)(win + ((size_t)b * W + (s_len[sq] + e) % W) * D + kc + c * 8);
+        } else {
+          int L, rows;
+          if (per_thread) {
+            L = clamp_len(xlen[u], a.t_cap);
+            const int wl = xwin[u] < 0 ? 0 : (xwin[u] > W ? W : xwin[u]);
+            rows = wl + a.n_new - W;
+          } else {
+            L = s_len[sq];
+            rows = s_rows[sq];
+          }
+          if (e < rows) xv[u] = *(const u32x4*)(win + ((size_t)b * W + (L + e) % W) * D + kc + c * 8);
         }
       }
     }
   };
-  const bool pre_x = W == 0 && one_chunk;
+  const bool pre_x = one_chunk;
   if (pre_x) load_x(0, 0, D, true);
-  // A decode step (W > 0, one new token): the new rows the last workgroup of a sequence writes into
-  // the ring are loaded now too.
-  const bool pre_new = W > 0 && a.n_new == 1 && one_chunk;
+  // the new rows the last workgroup of a sequence writes into the ring (a standalone one-token
+  // append with a window)
+  const bool pre_new = W > 0 && a.n_new == 1 && one_chunk && readers > 0;
   u32x4 kn[XV], vn[XV];
   if (pre_new) {
 #pragma unroll
@@ -238,68 +262,77 @@ __device__ __forceinline__ void append_body(const AppendArgs& a, int nck, int nc
 
   for (int e = 0; e < emax; ++e) {
     f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[2] = {0.f, 0.f};
     for (int kc = 0; kc < D; kc += kAppendK) {
       const int kw = min(kAppendK, D - kc);                    // a multiple of 128
-      if (!(pre_x && e == 0)) load_x(e, kc, kw, W == 0);
+      if (!(pre_x && e == 0)) load_x(e, kc, kw, false);
 #pragma unroll
       for (int u = 0; u < XV; ++u) {
         const int i = tid + 256 * u;
         const int sq = i / (kw / 8), c = i - sq * (kw / 8);
         if (sq < kAppendSeqs) *(u32x4*)(xs + sq * kAppendLdsX + c * 16) = xv[u];
       }
-      if (!one_chunk) load_pop(kc, kw / 32);
+      if (!one_chunk) load_pop(kc, kw);
       __syncthreads();
       if constexpr (!F32P) {
-        // C[seq 4 lg + i][col li] of this wave's 16 columns (two accumulation chains)
-        const unsigned char* xr = xs + li * kAppendLdsX + lg * 16;
+        // C[seq 4 lg + i][col li] of this wave's 16 columns over its K half (two chains)
+        const unsigned char* xr = xs + li * kAppendLdsX + kh * kw + lg * 16;
 #pragma unroll
-        for (int ks = 0; ks < kAppendK / 32; ks += 2) {
-          if (ks < kw / 32) {
+        for (int ks = 0; ks < kAppendK / 64; ks += 2) {
+          if (ks < kw / 64) {
             c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xr + ks * 64), pop[ks], c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xr + ks * 64 + 64), pop[ks + 1], c1, 0,
-                                                         0, 0);
+            if (ks + 1 < kw / 64)
+              c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xr + ks * 64 + 64), pop[ks + 1], c1, 0,
+                                                           0, 0);
           }
         }
       } else {
-        // float32 bases: thread (column lane, sequences 4 wave .. 4 wave + 3), float32 throughout
-        const int col = col0 + lane;
+        // float32 bases: thread (column lane & 31, sequences 2 (tid >> 5), +1), float32 throughout
+        const int cl = tid & 31, s2 = 2 * (tid >> 5);
+        const int col = col0 + cl;
         const float* pt = (const float*)(kv == 0 ? a.pk : a.pv) + (size_t)(col < r ? col : r - 1) * D + kc;
         for (int k = 0; k < kw; ++k) {
           const float pv = pt[k];
 #pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4)
-            acc[s4] += (float)*(const __bf16*)(xs + (4 * wave + s4) * kAppendLdsX + k * 2) * pv;
+          for (int s1 = 0; s1 < 2; ++s1)
+            acc[s1] += (float)*(const __bf16*)(xs + (s2 + s1) * kAppendLdsX + k * 2) * pv;
         }
       }
       __syncthreads();                                         // xs is restaged
     }
     if constexpr (!F32P) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) zt[4 * lg + i][16 * wave + li] = c0[i] + c1[i];
+      for (int i = 0; i < 4; ++i) zt[kh][4 * lg + i][16 * cb + li] = c0[i] + c1[i];
     } else {
+      const int cl = tid & 31, s2 = 2 * (tid >> 5);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) zt[4 * wave + s4][lane] = col0 + lane < r ? acc[s4] : 0.f;
+      for (int s1 = 0; s1 < 2; ++s1) {
+        zt[0][s2 + s1][cl] = col0 + cl < r ? acc[s1] : 0.f;
+        zt[1][s2 + s1][cl] = 0.f;
+      }
     }
     __syncthreads();
-    // store: wave w writes the rows of sequences 4w .. 4w + 3 (lane = column)
+    // store: wave w writes the rows of sequences 4w .. 4w + 3, two per pass (lane = column + 32 x
+    // which of the two)
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int sq = 4 * wave + s4;
-      if (sq < nseq && e < s_rows[sq]) {                       // wave-uniform
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const int sq = 4 * wave + 2 * p2 + (lane >> 5);
+      const int cl = lane & 31;
+      if (sq < nseq && e < s_rows[sq]) {                       // uniform over each 32-lane half
         const int b = b0 + sq;
-        const float z = zt[sq][lane];
+        const float z = zt[0][sq][cl] + zt[1][sq][cl];
         const long long row = (long long)s_len[sq] + e;
-        if (a.z_debug && col0 + lane < r)
-          a.z_debug[((size_t)b * a.n_new + e) * (a.rk + a.rv) + (kv == 0 ? 0 : a.rk) + col0 + lane] = z;
+        if (a.z_debug && col0 + cl < r)
+          a.z_debug[((size_t)b * a.n_new + e) * (a.rk + a.rv) + (kv == 0 ? 0 : a.rk) + col0 + cl] = z;
         if (row < a.t_cap)
-          store_chunk(a.latent, z, lane, col0, r, zbase + ((size_t)b * a.t_cap + row) * rb,
+          store_chunk(a.latent, z, cl, col0, r, zbase + ((size_t)b * a.t_cap + row) * rb,
                       qbase ? qbase + ((size_t)b * a.t_cap + row) * G : nullptr);
       }
     }
     __syncthreads();                                           // zt is reused
   }
 
+  if (readers == 0) return;
   // arrivals: this workgroup's reads of its sequences are done (the barrier above)
   if (tid < nseq) {
     const unsigned old = atomicAdd((unsigned*)&a.lat_len[b0 + tid], kArrival);
@@ -376,32 +409,14 @@ struct WinArgs {
   float* win_part;          // [B][Hq][d + 2]
   int Hq, Hkv;
   float wscale;
-  int step;                 // the window after this launch's append (lowrank_decode_step)
-  int readers;              // arrival count of a sequence in that case
+  int step;                 // the window after the step's append (lowrank_decode_step): the ring
+                            // as it was, without the evicted slot, plus the new token
 };
 
 constexpr int kWinHeads = 8;
 
 constexpr int kWinValuLds = (kWinHeads * kFoldD + kWinHeads * 128 + 4 * kWinHeads + 4 * kWinHeads * kFoldD +
                              4 * kWinHeads) * 4 + 16;
-
-// The last reader of a sequence in a decode step's first launch: the new token into its ring slot
-// (L + wl) mod W and the lengths after the step (workgroup-wide).
-__device__ __forceinline__ void window_step_finish(const AppendArgs& a, int b, int L, int wl, int n_ev) {
-  const int D = a.D, W = a.window;
-  const int slot = (L + wl) % W;
-  for (int i = threadIdx.x; i < 2 * (D / 8); i += 256) {
-    const int kvs = i / (D / 8), c = i % (D / 8);
-    const __bf16* src = (kvs == 0 ? a.k_new : a.v_new) + (size_t)b * D + c * 8;
-    __bf16* dst = (kvs == 0 ? a.kwin : a.vwin) + ((size_t)b * W + slot) * D + c * 8;
-    *(u32x4*)dst = *(const u32x4*)src;
-  }
-  if (threadIdx.x == 0) {
-    const long long nl = (long long)L + n_ev;
-    a.win_len[b] = wl + 1 > W ? W : wl + 1;
-    a.lat_len[b] = (int)(nl > a.t_cap ? a.t_cap : nl);
-  }
-}
 
 template <typename QT>
 __device__ void window_body(const WinArgs& w, const AppendArgs& a, int blk, unsigned char* smem) {
@@ -410,7 +425,6 @@ __device__ void window_body(const WinArgs& w, const AppendArgs& a, int blk, unsi
   float (*wmx)[kWinHeads] = (float (*)[kWinHeads])((unsigned char*)wsc + kWinHeads * 128 * 4);   // [4][8]
   float (*wred)[kWinHeads][kFoldD] = (float (*)[kWinHeads][kFoldD])((unsigned char*)wmx + 4 * kWinHeads * 4);
   float (*wl4)[kWinHeads] = (float (*)[kWinHeads])((unsigned char*)wred + 4 * kWinHeads * kFoldD * 4);
-  int& w_last = *(int*)((unsigned char*)wl4 + 4 * kWinHeads * 4);
   const int grp = w.Hq / w.Hkv, D = a.D, W = a.window;
   const int g = blk % w.Hkv, b = blk / w.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -521,23 +535,20 @@ __device__ void window_body(const WinArgs& w, const AppendArgs& a, int blk, unsi
       }
     }
   }
-  if (!w.step) return;
-  // this workgroup's reads of the sequence are done: count it among the readers
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = atomicAdd((unsigned*)&a.lat_len[b], kArrival);
-    w_last = ((old >> 24) & 0x7Fu) == (unsigned)(w.readers - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (w_last) window_step_finish(a, b, L, wl, n_ev);
 }
 
 // The same on the matrix cores, for bf16 queries and at most 16 heads per KV head: the grp heads
-// are the 16 rows of the products (zero past grp). Wave v takes the 16-slot tiles v, v + 4, ... of
-// the window and stages each in its own part of LDS (a wave's LDS writes and reads stay in order;
-// the next tile's loads are issued before the current one is processed): scores from the 16x16x32
-// bf16 product (16 slots x 16 heads), a base-2 online softmax, values from the 16x16x16 product
-// through the transpose read; the four waves' (O, m, l) are merged through LDS.
+// are the 16 rows of the products (zero past grp). The ring is walked in physical slot order:
+// 16-slot tiles of slots 16 t .. 16 t + 15, wave v taking the tiles t = v mod 4 that hold live
+// slots, each staged in the wave's own part of LDS: scores from the 16x16x32 bf16 product (16
+// slots x 16 heads), a base-2 online softmax, values from the 16x16x16 product through the
+// transpose read; the four waves' (O, m, l) are merged through LDS. Slot s holds window position
+// (s - Lw) mod W, live when that is below wlw. The order depends only on the window after the
+// step, so a decode step (which reads the ring as it was, with the new token in the slot it is
+// about to take) and a decode after the append add the same terms in the same order.
+// A window of at most 128 slots has at most two tiles per wave: their loads go out with the
+// lengths' (every slot of the ring is in bounds), and dead slots are zeroed when staged, so the
+// workgroup waits for one round trip. Larger windows load each live tile when it is reached.
 constexpr int kWinSlots = 16;
 constexpr int kWinMfmaLds = 4 * kWinSlots * kExSK + 4 * kWinSlots * kExSV + 4 * 2 * 16 * 4 + 3 * (kExD / 16) * 64 * 16 + 16;
 
@@ -546,25 +557,43 @@ __device__ void window_mfma_body(const WinArgs& w, const AppendArgs& a, int blk,
   unsigned char* vtb = ktb + 4 * kWinSlots * kExSK;                   // [4][16 * kExSV]
   float* mrg_ml = (float*)(vtb + 4 * kWinSlots * kExSV);              // [4][2][16]
   f32x4* mrg_o = (f32x4*)(mrg_ml + 4 * 2 * 16);                       // [3][8][64]
-  int& w_last = *(int*)(mrg_o + 3 * (kExD / 16) * 64);
   const int grp = w.Hq / w.Hkv, D = a.D, W = a.window;
   const int g = blk % w.Hkv, b = blk / w.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool rvalid = li < grp;
-  const int L = clamp_len(a.lat_len[b], a.t_cap);
-  int wl = a.win_len[b];
-  wl = wl < 0 ? 0 : (wl > W ? W : wl);
-  int Lw = L, wlw = wl, n_ev = 0;
-  if (w.step) {
-    n_ev = wl + 1 > W ? wl + 1 - W : 0;
-    Lw = L + n_ev;
-    wlw = wl + 1 > W ? W : wl + 1;
-  }
-  auto row = [&](const __bf16* ring, const __bf16* xnew, int t) -> const __bf16* {
-    if (w.step && t == wlw - 1) return xnew + (size_t)b * D + g * kExD;
-    return ring + ((size_t)b * W + (Lw + t) % W) * D + g * kExD;
+  const int ntiles = (W + kWinSlots - 1) / kWinSlots;
+  const bool spec = W <= 8 * kWinSlots;                               // at most two tiles per wave
+  const int32_t raw_len = a.lat_len[b];
+  const int32_t raw_win = a.win_len[b];
+  const __bf16* kring = a.kwin + (size_t)b * W * D + g * kExD;
+  const __bf16* vring = a.vwin + (size_t)b * W * D + g * kExD;
+  // slots 16 t .. 16 t + 15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V (item
+  // i = lane + 64 u is row i >> 4, granule i & 15; slots past W read as 0)
+  auto load_tile = [&](int t, u32x4 (&kn)[4], u32x4 (&vn)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      const int s = t * kWinSlots + (i >> 4), gc = i & 15;
+      kn[u] = u32x4{0u, 0u, 0u, 0u};
+      vn[u] = u32x4{0u, 0u, 0u, 0u};
+      if (s < W) {
+        kn[u] = *(const u32x4*)(kring + (size_t)s * D + gc * 8);
+        vn[u] = *(const u32x4*)(vring + (size_t)s * D + gc * 8);
+      }
+    }
   };
+  u32x4 kA[4], vA[4], kB[4], vB[4];
+  if (spec) {
+    load_tile(wave, kA, vA);
+    load_tile(wave + 4, kB, vB);
+  }
+  // the step's token, granule lane & 15 of head g's slice (every row item of a lane has that granule)
+  u32x4 knew = u32x4{0u, 0u, 0u, 0u}, vnew = u32x4{0u, 0u, 0u, 0u};
+  if (w.step) {
+    knew = *(const u32x4*)(a.k_new + (size_t)b * D + g * kExD + (lane & 15) * 8);
+    vnew = *(const u32x4*)(a.v_new + (size_t)b * D + g * kExD + (lane & 15) * 8);
+  }
   // q of this lane's head as the B operand: d indices 32 ks + 8 lg .. +7
   bf16x8 qop[4];
   {
@@ -572,38 +601,61 @@ __device__ void window_mfma_body(const WinArgs& w, const AppendArgs& a, int blk,
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qop[ks] = rvalid ? *(const bf16x8*)(qr + ks * 32) : zero_bf16x8();
   }
+  // the window after the step: positions 0 .. wlw - 1 in slots (Lw + t) mod W
+  const int L = clamp_len(raw_len, a.t_cap);
+  const int wl = raw_win < 0 ? 0 : (raw_win > W ? W : raw_win);
+  int Lw = L, wlw = wl;
+  if (w.step) {
+    Lw = L + (wl + 1 > W ? wl + 1 - W : 0);
+    wlw = wl + 1 > W ? W : wl + 1;
+  }
+  const int s0 = Lw % W;                                              // slot of position 0
+  const int new_slot = w.step ? (Lw + wlw - 1) % W : -1;
+  auto live_slot = [&](int s) {
+    int t = s - s0;
+    if (t < 0) t += W;
+    return s < W && t < wlw;
+  };
+  // live tiles: [ta0, tb0] and [ta1, tb1] (empty when a > b), in physical order
+  int ta0 = 0, tb0 = -1, ta1 = 0, tb1 = -1;
+  if (wlw > 0) {
+    const int e = s0 + wlw - 1;                                       // last live slot, unwrapped
+    if (e < W) {
+      ta0 = s0 / kWinSlots;
+      tb0 = e / kWinSlots;
+    } else {
+      ta0 = 0;
+      tb0 = (e - W) / kWinSlots;
+      ta1 = s0 / kWinSlots;
+      tb1 = ntiles - 1;
+      if (ta1 <= tb0 + 1) {                                           // the two runs touch: one
+        tb0 = tb1;
+        ta1 = 0;
+        tb1 = -1;
+      }
+    }
+  }
+  auto tile_live = [&](int t) { return (t >= ta0 && t <= tb0) || (t >= ta1 && t <= tb1); };
+
   float m = -INFINITY, lsum = 0.f;
   f32x4 acc[kExD / 16];
 #pragma unroll
   for (int j = 0; j < kExD / 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   unsigned char* kw = ktb + wave * kWinSlots * kExSK;
   unsigned char* vw = vtb + wave * kWinSlots * kExSV;
-  // slots k0 .. k0+15 of head g's slice: 16 rows x 16 granules of 16 bytes, K and V
-  u32x4 kn[4], vn[4];
-  auto load_tile = [&](int k0) {
+  auto process = [&](int t, const u32x4 (&kn)[4], const u32x4 (&vn)[4]) {
+    const int k0 = t * kWinSlots;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = lane + 64 * u;
       const int r = i >> 4, gc = i & 15;
-      const int j = k0 + r;
-      kn[u] = u32x4{0u, 0u, 0u, 0u};
-      vn[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < wlw) {
-        kn[u] = *(const u32x4*)(row(a.kwin, a.k_new, j) + gc * 8);
-        vn[u] = *(const u32x4*)(row(a.vwin, a.v_new, j) + gc * 8);
-      }
+      const int s = k0 + r;
+      const bool lv = live_slot(s);
+      const u32x4 kx = s == new_slot ? knew : kn[u];
+      const u32x4 vx = s == new_slot ? vnew : vn[u];
+      *(u32x4*)(kw + r * kExSK + gc * 16) = lv ? kx : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(vw + r * kExSV + gc * 16) = lv ? vx : u32x4{0u, 0u, 0u, 0u};
     }
-  };
-  if (wave * kWinSlots < wlw) load_tile(wave * kWinSlots);
-  for (int k0 = wave * kWinSlots; k0 < wlw; k0 += 4 * kWinSlots) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      const int r = i >> 4, gc = i & 15;
-      *(u32x4*)(kw + r * kExSK + gc * 16) = kn[u];
-      *(u32x4*)(vw + r * kExSV + gc * 16) = vn[u];
-    }
-    if (k0 + 4 * kWinSlots < wlw) load_tile(k0 + 4 * kWinSlots);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the tile is in LDS before it is read
     // scores S^T[slot k0 + 4 lg + i][head li]
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -615,7 +667,7 @@ __device__ void window_mfma_body(const WinArgs& w, const AppendArgs& a, int blk,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x = sacc[i] * w.wscale;
-      v[i] = (k0 + 4 * lg + i < wlw) ? ((x != x) ? INFINITY : x) : -INFINITY;
+      v[i] = live_slot(k0 + 4 * lg + i) ? ((x != x) ? INFINITY : x) : -INFINITY;
     }
     const float mx = wave_max_lg(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
     const float mnew = fmaxf(m, mx);
@@ -640,6 +692,18 @@ __device__ void window_mfma_body(const WinArgs& w, const AppendArgs& a, int blk,
 #pragma unroll
     for (int j = 0; j < kExD / 16; ++j)
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr(vbase + j * 32), pb, acc[j], 0, 0, 0);
+  };
+  if (spec) {
+    if (tile_live(wave)) process(wave, kA, vA);
+    if (tile_live(wave + 4)) process(wave + 4, kB, vB);
+  } else {
+    for (int run = 0; run < 2; ++run) {
+      const int ta = run == 0 ? ta0 : ta1, tb = run == 0 ? tb0 : tb1;
+      for (int t = ta + ((wave - ta) % 4 + 4) % 4; t <= tb; t += 4) {
+        load_tile(t, kA, vA);
+        process(t, kA, vA);
+      }
+    }
   }
   const float l = wave_sum_lg(lsum);
   // merge the four waves' partials into wave 0
@@ -676,37 +740,33 @@ __device__ void window_mfma_body(const WinArgs& w, const AppendArgs& a, int blk,
       wp[kExD + 1] = lt;
     }
   }
-  if (!w.step) return;
-  // this workgroup's reads of the sequence are done (the barrier above): count it among the readers
-  if (tid == 0) {
-    const unsigned old = atomicAdd((unsigned*)&a.lat_len[b], kArrival);
-    w_last = ((old >> 24) & 0x7Fu) == (unsigned)(w.readers - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (w_last) window_step_finish(a, b, L, wl, n_ev);
 }
 
 constexpr int kFrontLds = kWinMfmaLds > kAppendLds ? (kWinMfmaLds > kWinValuLds ? kWinMfmaLds : kWinValuLds)
                                                    : (kAppendLds > kWinValuLds ? kAppendLds : kWinValuLds);
 static_assert(kFrontLds >= kHeadsPad * kFoldD * 4, "the float32 fold's query tile fits");
 
-// The first launch of a decode call: [append (a decode step only)] [fold] [window, W > 0].
+// The first launch of a decode call: [window, W > 0] [append (a decode step only)] [fold], the
+// longest roles first so that they are dispatched first. Within a decode step none of them writes
+// what another reads: the append stores the new latent row at index L (which no role of this
+// launch reads), the window reads the ring as it was, and the lengths are left for the step's
+// last launch.
 template <int LAT>
 __global__ __launch_bounds__(256) void lr_front(AppendArgs a, int nck, int ncv, int n_append, FoldArgs f, int nfx,
-                                                int nfy, int n_fold, WinArgs w) {
+                                                int nfy, int n_win, WinArgs w) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int x = blockIdx.x;
-  if (x < n_append) {
-    append_body<LAT == LR_F32>(a, nck, ncv, x % (nck + ncv), x / (nck + ncv), w.readers > 0 ? w.readers : nck + ncv,
-                               smem);
-  } else if (x < n_append + n_fold) {
-    const int y = x - n_append;
+  if (x < n_win) {
+    if constexpr (LAT == LR_F32) window_body<float>(w, a, x, smem);
+    else if (w.Hq / w.Hkv <= 16) window_mfma_body(w, a, x, smem);
+    else window_body<__bf16>(w, a, x, smem);
+  } else if (x < n_win + n_append) {
+    const int y = x - n_win;
+    append_body<LAT == LR_F32>(a, nck, ncv, y % (nck + ncv), y / (nck + ncv), 0, smem);
+  } else {
+    const int y = x - n_win - n_append;
     if constexpr (LAT == LR_F32) fold_f32_body(f, y % nfx, (y / nfx) % nfy, y / (nfx * nfy), (float*)smem);
     else fold_body<LAT == LR_I4G32>(f, y % nfx, (y / nfx) % nfy, y / (nfx * nfy));
-  } else {
-    if constexpr (LAT == LR_F32) window_body<float>(w, a, x - n_append - n_fold, smem);
-    else if (w.Hq / w.Hkv <= 16) window_mfma_body(w, a, x - n_append - n_fold, smem);
-    else window_body<__bf16>(w, a, x - n_append - n_fold, smem);
   }
 }
 
@@ -849,18 +909,17 @@ hipError_t launch_front(const FrontPlan& fp, const AppendPlan* ap, const lr_laye
   w.Hkv = f.Hkv;
   w.wscale = wscale;
   w.step = ap != nullptr && fp.n_win > 0;
-  w.readers = w.step ? fp.nck + fp.ncv + f.Hkv : 0;
   const dim3 grid(fp.n_append + fp.n_fold + fp.n_win);
   if (grid.x == 0) return hipSuccess;
   if (fp.latent == LR_F32)
     hipLaunchKernelGGL(lr_front<LR_F32>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx, fp.nfy,
-                       fp.n_fold, w);
+                       fp.n_win, w);
   else if (fp.latent == LR_I4G32)
     hipLaunchKernelGGL(lr_front<LR_I4G32>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx,
-                       fp.nfy, fp.n_fold, w);
+                       fp.nfy, fp.n_win, w);
   else
     hipLaunchKernelGGL(lr_front<LR_BF16>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx,
-                       fp.nfy, fp.n_fold, w);
+                       fp.nfy, fp.n_win, w);
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@
 #include "internal.h"
 
 #include <math.h>
+#include <string.h>
 
 namespace lr {
 
@@ -62,6 +63,8 @@ struct DecodeArgs {
                             // query sequence sq reads the latents of stored sequence sq / qpb
   const __bf16* kchunk;     // prefill: the chunk's exact rows [B][qpb][D]; NULL for decode
   const __bf16* vchunk;
+  int step;                 // a decode step: lat_len / win_len still hold the lengths before the
+                            // step's token, and the latent rows attended are step_lens().L_new
 };
 
 
@@ -526,7 +529,8 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const bool producer = wave >= 4 * G;
 
-  int L = a.lat_len[b];
+  int L = a.step ? step_lens(a.lat_len[b], a.window > 0 ? a.win_len[b] : 0, a.window, a.t_cap).L_new
+                 : a.lat_len[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int t_begin = s * a.split_tokens;
   const int t_end = min(t_begin + a.split_tokens, L);
@@ -1002,6 +1006,8 @@ struct CombineArgs {
   int Hq, Hkv, d, D, rv, rv_pad16, nsplit;
   int exact;                // exact-keys partials present in win_part (window, prefill chunk)
   int i4_order;             // partials are in the dequantised int4 tiles' block order
+  StepFinish fin;           // a decode step (fin.lat_len != NULL): workgroup (b, head 0) also
+                            // writes sequence b's new token into the ring and its new lengths
 };
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
@@ -1038,6 +1044,8 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   float* ws = ahat + a.rv_pad16;          // [nsplit]
   float* red = ws + a.nsplit;             // [8]
   const size_t base = (size_t)b * a.nsplit;
+  // no reader of the ring or the lengths is left in the step (this launch reads neither)
+  if (a.fin.lat_len != nullptr && j == 0) step_finish(a.fin, b);
 
   float mw = -INFINITY, lw = 0.f;
   const float* wp = a.win_part + ((size_t)b * a.Hq + j) * (a.d + 2);
@@ -1137,6 +1145,7 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   }
 }
 
+
 // ---------------------------------------------------------------------------------------------
 // Host launch
 // ---------------------------------------------------------------------------------------------
@@ -1185,8 +1194,9 @@ static hipError_t dispatch_decode(const DecodePlan& p, const DecodeArgs& args, i
 // Arguments of the matrix-core fold (bf16 queries) for plan p; *nfold = its workgroups.
 static void fold_args(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* qt, float scale, FoldArgs* f,
                       int* nfold) {
-  // query sequences per wave: 1 for a decode batch, up to 16 for a prefill chunk's tokens
-  const int nq = p.B >= 512 ? 16 : (p.B >= 128 ? 4 : 1);
+  // query sequences per wave: 4 (the loads of kFoldQB sequences go out together, and a decode
+  // batch of 16 takes a quarter of the workgroups), 16 for the many tokens of a prefill chunk
+  const int nq = p.B >= 512 ? 16 : (p.B >= 4 ? 4 : 1);
   f->q = (const __bf16*)q;
   f->bk = (const __bf16*)c->bk;
   f->qt = qt;
@@ -1212,8 +1222,8 @@ static hipError_t decode_front(const DecodePlan& p, const AppendPlan* ap, const 
   fold_args(p, c, q, w + p.off_qt, scale, &f, &nfold);
   FrontPlan fp;
   fp.latent = p.latent;
-  fp.nck = ap ? (ap->rk + 63) / 64 : 0;
-  fp.ncv = ap ? (ap->rv + 63) / 64 : 0;
+  fp.nck = ap ? (ap->rk + kAppendCols - 1) / kAppendCols : 0;
+  fp.ncv = ap ? (ap->rv + kAppendCols - 1) / kAppendCols : 0;
   fp.n_append = ap ? (fp.nck + fp.ncv) * ((ap->B + 15) / 16) : 0;
   if (p.latent == LR_F32) {
     fp.nfx = (p.rk_pad + 63) / 64;
@@ -1235,12 +1245,13 @@ hipError_t launch_decode_step(const AppendPlan& ap, const DecodePlan& p, const l
                               hipEvent_t ev_begin, hipEvent_t ev_end) {
   const hipError_t e = decode_front(p, &ap, c, q, k_new, v_new, ws, st);
   if (e != hipSuccess) return e;
-  return launch_decode(p, c, q, out, out_dtype, ws, st, ev_begin, ev_end, nullptr, nullptr, true);
+  return launch_decode(p, c, q, out, out_dtype, ws, st, ev_begin, ev_end, nullptr, nullptr, k_new, v_new);
 }
 
 hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* out,
                          int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
-                         const void* k_chunk, const void* v_chunk, bool fold_done) {
+                         const void* k_chunk, const void* v_chunk, const void* step_k_new,
+                         const void* step_v_new) {
   unsigned char* w = (unsigned char*)ws;
   __bf16* qt = (__bf16*)(w + p.off_qt);
   const float scale = p.sm_scale * kLog2e;
@@ -1251,9 +1262,10 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   // decode kernel (window_block); each leaves a partial the combine merges.
   const bool decode_step = k_chunk == nullptr;
   const bool exact_mfma = !decode_step && p.exact && p.latent != LR_F32;
+  const bool step = step_k_new != nullptr;            // lowrank_decode_step: the front already ran
 
   // 1. fold (+ the window of a decode step), unless a decode step's first launch already ran it
-  if (!fold_done) {
+  if (!step) {
     hipError_t e;
     if (decode_step) {
       e = decode_front(p, nullptr, c, q, nullptr, nullptr, ws, st);
@@ -1321,6 +1333,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.copy_v = p.copy_v;
   a.nr = p.nr;
   a.raw_stage = p.raw_stage;
+  a.step = step;
   hipError_t e;
   if (p.pf) {
     // prefill over bf16 latents: the dedicated exact-keys kernel (window slots and the chunk's
@@ -1357,6 +1370,18 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   ca.nsplit = p.nsplit;
   ca.exact = p.exact;
   ca.i4_order = p.latent == LR_I4G32;
+  memset(&ca.fin, 0, sizeof(ca.fin));
+  if (step) {
+    ca.fin.k_new = (const __bf16*)step_k_new;
+    ca.fin.v_new = (const __bf16*)step_v_new;
+    ca.fin.kwin = (__bf16*)c->kwin;
+    ca.fin.vwin = (__bf16*)c->vwin;
+    ca.fin.lat_len = c->lat_len;
+    ca.fin.win_len = c->win_len;
+    ca.fin.t_cap = p.t_cap;
+    ca.fin.D = p.D;
+    ca.fin.window = p.window;
+  }
   const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);
   const bool f32b = p.latent == LR_F32;

@@ -16,6 +16,71 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 __device__ __forceinline__ int i4_pos(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 
 constexpr int kFoldD = 128;     // head_dim handled by the fold (validated on the host)
+constexpr int kFoldQB = 4;      // query sequences of a fold wave whose loads are in flight together
+constexpr int kAppendCols = 32; // latent columns of one append workgroup (one int4 group)
+
+// ---------------------------------------------------------------------------------------------
+// Lengths. A standalone append (lowrank_kv_append) counts its workgroups' arrivals in bits 24..30
+// of the length word while it runs, so readers mask the length to bits 0..23 (t_cap < 2^24).
+// A decode step (lowrank_decode_step) keeps the words as they were before the step until its last
+// launch: the front's append and window workgroups and the latent kernel read the old words and
+// derive the lengths after the step (step_lens); one combine workgroup per sequence then writes
+// the new token into the ring and the new lengths (step_finish), after every reader is done.
+// ---------------------------------------------------------------------------------------------
+constexpr unsigned kLenMask = 0x00FFFFFFu;
+
+__device__ __forceinline__ int clamp_len(int32_t raw, long long cap) {
+  const unsigned v = (unsigned)raw & kLenMask;
+  return (int)((long long)v > cap ? cap : (long long)v);
+}
+
+// One new token per sequence: L, wl the lengths before the step (latent rows, window slots);
+// rows the latent rows it adds (the evicted window token, or with no window the token itself);
+// L_new, wl_new the lengths after it. The same rules as a one-token lowrank_kv_append.
+struct StepLens {
+  int L, wl, rows, L_new, wl_new;
+};
+
+__device__ __forceinline__ StepLens step_lens(int32_t raw_len, int32_t raw_win, int W, long long t_cap) {
+  StepLens s;
+  s.L = clamp_len(raw_len, t_cap);
+  s.wl = W > 0 ? (raw_win < 0 ? 0 : (raw_win > W ? W : raw_win)) : 0;
+  s.rows = W > 0 ? (s.wl + 1 > W ? s.wl + 1 - W : 0) : 1;
+  const long long nl = (long long)s.L + s.rows;
+  s.L_new = (int)(nl > t_cap ? t_cap : nl);
+  s.wl_new = W > 0 ? (s.wl + 1 > W ? W : s.wl + 1) : 0;
+  return s;
+}
+
+struct StepFinish {
+  const __bf16* k_new;      // [B][D] the step's token
+  const __bf16* v_new;
+  __bf16* kwin;             // [B][W][D] rings (W > 0)
+  __bf16* vwin;
+  int32_t* lat_len;         // NULL: not a decode step
+  int32_t* win_len;
+  long long t_cap;
+  int D, window;
+};
+
+// Sequence b, by one whole workgroup: the token into ring slot (L + wl) mod W, then the lengths.
+__device__ __forceinline__ void step_finish(const StepFinish& f, int b) {
+  const StepLens s = step_lens(f.lat_len[b], f.window > 0 ? f.win_len[b] : 0, f.window, f.t_cap);
+  if (f.window > 0) {
+    const int slot = (s.L + s.wl) % f.window;
+    for (int i = threadIdx.x; i < 2 * (f.D / 8); i += blockDim.x) {
+      const int kv = i / (f.D / 8), c = i - kv * (f.D / 8);
+      const __bf16* src = (kv == 0 ? f.k_new : f.v_new) + (size_t)b * f.D + c * 8;
+      __bf16* dst = (kv == 0 ? f.kwin : f.vwin) + ((size_t)b * f.window + slot) * f.D + c * 8;
+      *(u32x4*)dst = *(const u32x4*)src;
+    }
+  }
+  __syncthreads();                                   // every thread has read the old lengths
+  if (threadIdx.x == 0) {
+    if (f.window > 0) f.win_len[b] = s.wl_new;
+    f.lat_len[b] = s.L_new;
+  }
+}
 
 // ---------------------------------------------------------------------------------------------
 // Fold on the matrix cores for bf16 q and Bk: one wave per (16-column block of latent indices k,
@@ -55,33 +120,45 @@ __device__ __forceinline__ void fold_body(const FoldArgs& f, int bx, int by, int
     for (int ks = 0; ks < 4; ++ks) bop[ks] = k < rk ? *(const bf16x8*)(brow + ks * 32) : zero_bf16x8();
   }
   const int pos = F32OUT ? i4_pos(k) : k;
-  for (int b = bz * nq; b < min(nseq, (bz + 1) * nq); ++b) {
-  for (int h0 = 0; h0 < grp; h0 += 16) {
-    const int hl = h0 + li;
-    const __bf16* qrow = q + ((size_t)b * Hq + g * grp + hl) * kFoldD + lg * 8;
-    bf16x8 aop[4];
+  // kFoldQB query sequences at a time: their query loads are all issued before the first product
+  const int bend = min(nseq, (bz + 1) * nq);
+  for (int b0 = bz * nq; b0 < bend; b0 += kFoldQB) {
+    for (int h0 = 0; h0 < grp; h0 += 16) {
+      const int hl = h0 + li;
+      bf16x8 aop[kFoldQB][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) aop[ks] = hl < grp ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < kFoldQB; ++u) {
+        const bool ok = hl < grp && b0 + u < bend;
+        const __bf16* qrow = q + ((size_t)(ok ? b0 + u : 0) * Hq + g * grp + (ok ? hl : 0)) * kFoldD + lg * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[ks], bop[ks], c, 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks) aop[u][ks] = ok ? *(const bf16x8*)(qrow + ks * 32) : zero_bf16x8();
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = h0 + 4 * lg + i;
-      if (h < grp) {
-        const size_t o = ((size_t)b * kHeadsPad + g * grp + h) * rk_pad + pos;
-        if constexpr (F32OUT) ((float*)qt)[o] = c[i] * scale;
-        else ((__bf16*)qt)[o] = (__bf16)(c[i] * scale);
+      for (int u = 0; u < kFoldQB; ++u) {
+        const int b = b0 + u;
+        if (b >= bend) break;
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[u][ks], bop[ks], c, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = h0 + 4 * lg + i;
+          if (h < grp) {
+            const size_t o = ((size_t)b * kHeadsPad + g * grp + h) * rk_pad + pos;
+            if constexpr (F32OUT) ((float*)qt)[o] = c[i] * scale;
+            else ((__bf16*)qt)[o] = (__bf16)(c[i] * scale);
+          }
+        }
       }
     }
-  }
-  if (g == 0) {   // query heads past Hq: zero rows
-    for (int h = Hq + lg; h < kHeadsPad; h += 4) {
-      const size_t o = ((size_t)b * kHeadsPad + h) * rk_pad + k;
-      if constexpr (F32OUT) ((float*)qt)[o] = 0.f;
-      else ((__bf16*)qt)[o] = (__bf16)0.f;
+    if (g == 0) {   // query heads past Hq: zero rows
+      for (int b = b0; b < min(bend, b0 + kFoldQB); ++b)
+        for (int h = Hq + lg; h < kHeadsPad; h += 4) {
+          const size_t o = ((size_t)b * kHeadsPad + h) * rk_pad + k;
+          if constexpr (F32OUT) ((float*)qt)[o] = 0.f;
+          else ((__bf16*)qt)[o] = (__bf16)0.f;
+        }
     }
-  }
   }
 }
 
@@ -140,9 +217,9 @@ __device__ __forceinline__ void fold_f32_body(const FoldArgs& f, int bx, int g, 
     for (int j = Hq + hs; j < kHeadsPad; j += 4) out[(size_t)j * rk_pad] = (__bf16)0.f;
 }
 
-// The first launch of a decode call (append.hip): workgroups [0, n_append) append the step's
-// token (lowrank_decode_step only), [n_append, n_append + n_fold) fold the query, and the rest
-// (W > 0) attend over the exact window, one per (sequence, KV head).
+// The first launch of a decode call (append.hip): workgroups [0, n_win) attend over the exact
+// window (W > 0), one per (sequence, KV head); [n_win, n_win + n_append) append the step's token
+// (lowrank_decode_step only); the rest fold the query. The longest roles are dispatched first.
 struct FrontPlan {
   int latent;               // lr_dtype of the latents (selects the fold and the append's bases)
   int n_append, nck, ncv;   // append workgroups and their column chunks (0 when no append)

@@ -133,7 +133,8 @@ inline int plan_decode(const lr_model_desc* m, int layer, int batch, int max_len
 
 hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const void* q, void* out,
                          int out_dtype, void* ws, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end,
-                         const void* k_chunk = nullptr, const void* v_chunk = nullptr, bool fold_done = false);
+                         const void* k_chunk = nullptr, const void* v_chunk = nullptr,
+                         const void* step_k_new = nullptr, const void* step_v_new = nullptr);
 
 // The latent part of a prefill (p.pf): partials per (query token, token range) in the decode
 // layout, for the decode combine.
@@ -157,8 +158,10 @@ struct AppendPlan {
   int ld_k, ld_v;
 };
 
-// One decode step: the append of one new token per sequence, then decode (fold, latent kernel,
-// combine); for bf16 queries the append and the fold share the first launch.
+// One decode step: the append of one new token per sequence, then decode, in three launches: the
+// append, the fold and the window in the first; the latent kernel; the combine, which also writes
+// the new token into the ring and the lengths after the step (step_k_new / step_v_new non-NULL in
+// launch_decode: the first launch already ran, and the lengths are still those before the step).
 struct DecodePlan;
 hipError_t launch_decode_step(const AppendPlan& ap, const DecodePlan& p, const lr_layer_cache* c, const void* k_new,
                               const void* v_new, const void* q, void* out, int out_dtype, void* ws, hipStream_t st,

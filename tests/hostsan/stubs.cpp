@@ -18,7 +18,7 @@ const char* hipGetErrorString(hipError_t) { return "stub"; }
 
 namespace lr {
 hipError_t launch_decode(const DecodePlan&, const lr_layer_cache*, const void*, void*, int, void*, hipStream_t,
-                         hipEvent_t, hipEvent_t, const void*, const void*, bool) {
+                         hipEvent_t, hipEvent_t, const void*, const void*, const void*, const void*) {
   return hipSuccess;
 }
 hipError_t launch_decode_step(const AppendPlan&, const DecodePlan&, const lr_layer_cache*, const void*, const void*,

@@ -12,7 +12,8 @@ from helpers import TOL, bits, device_layer, oracle_decode, rel_err
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("latent,window", [("bf16", 0), ("bf16", 128), ("i4g32", 0), ("i4g32", 32), ("f32", 16)])
+@pytest.mark.parametrize("latent,window", [("bf16", 0), ("bf16", 128), ("bf16", 200), ("i4g32", 0), ("i4g32", 32),
+                                           ("f32", 16)])
 def test_step_equals_append_then_decode(latent, window):
     base = synth.CONFIGS[4] if window else synth.CONFIGS[1]
     kw = dict(batch=5, latent=latent)

@@ -104,6 +104,28 @@ def test_sharp_scores_mixed_window_and_history():
     check(li)
 
 
+@pytest.mark.parametrize("W", [48, 128, 200, 256])
+def test_window_dead_slots_hold_nan(W):
+    """Ring slots outside the live window hold NaN: the window's walk over physical slots must keep
+    them out of both the scores and the values. Full windows whose live slots wrap (two runs of
+    tiles that merge), partial windows inside one run or wrapping, a single slot, and W > 128 (the
+    tiles are loaded when reached)."""
+    import dataclasses
+    cfg = CFG4.replace(batch=6, window=W, rank_choices=None, rank_k=136, rank_v=200)
+    lat = np.array([3 * W + 5, 7, 0, W - 3, 1000, 2 * W - 10], np.int32)
+    wl = np.array([W, W // 2, 1, W - 1, 17, 30], np.int32)
+    li = synth.make_layer(cfg, 3, q_scale=16.0, lat_len=lat, win_len=wl)
+    kw, vw = li.kwin.clone(), li.vwin.clone()
+    for b in range(cfg.batch):
+        live = {(int(lat[b]) + i) % W for i in range(int(wl[b]))}
+        dead = [s for s in range(W) if s not in live]
+        kw[b, dead] = float("nan")
+        vw[b, dead] = float("nan")
+    li = dataclasses.replace(li, kwin=kw, vwin=vw)
+    out = check(li)
+    assert torch.isfinite(out).all()
+
+
 @pytest.mark.parametrize("nsplit", [1, 5, 32])
 def test_window_with_split_counts(nsplit):
     cfg = CFG4.replace(batch=2)
