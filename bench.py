@@ -668,6 +668,57 @@ def basisupd_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def append_bench(args):
+    """Storing a chunk of new tokens per sequence (lowrank_kv_append with n_new = --chunk), as after
+    a prefill chunk: the projection and storage of every new (or evicted) row, the window ring
+    and the lengths. --config 1 (B=16, r=358 bf16, no window, 2000 stored rows) or 4 (the
+    28-layer workload's layer 0 shape with W = 128, full windows: every new token evicts one).
+    Algorithmic bytes per call: the new dense rows read (2 D bf16 each) and the latent rows
+    written."""
+    import torch
+    import rank_kv_cache_lowrank_amd as lr
+    import synth
+    from synth.device import device_layer
+
+    dev = "cuda"
+    C = args.chunk
+    K, W = args.steps, args.warmup
+    cfg = synth.CONFIGS[args.config]
+    calls = K + W
+    if cfg.window:
+        cfg = cfg.replace(rank_choices=None, rank_k=358, rank_v=358)
+        lat = np.full(cfg.batch, 3000, np.int32)
+        li = synth.make_layer(cfg, 0, lat_len=lat, win_len=np.full(cfg.batch, cfg.window, np.int32),
+                              t_cap=3000 + C * calls)
+    elif cfg.n_layers == 1:
+        li = synth.make_layer(cfg, t_cap=2000 + C * calls, lat_len=np.full(cfg.batch, 2000, np.int32))
+    else:
+        raise SystemExit("--op append takes --config 1 or 4")
+    model, cache = device_layer(li, dev, with_proj=True)
+    B, D = cfg.batch, cfg.kv_width
+    gen = np.random.default_rng(5)
+    k = torch.from_numpy(gen.standard_normal((B, C, D), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    v = torch.from_numpy(gen.standard_normal((B, C, D), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    ms = _timed_calls(lambda: lr.lowrank_kv_append(model, 0, cache, k, v), K, W)
+    got = cache.tensors["lat_len"].cpu().numpy()
+    assert np.all(got == li.lat_len + C * calls), "lengths did not advance by the chunk"
+    row_bytes = latent_bytes_per_token(cfg.latent, li.rank_k) + latent_bytes_per_token(cfg.latent, li.rank_v)
+    nbytes = B * C * (2 * D * 2 + row_bytes)
+    rec = {"metric": "storing a chunk of new tokens per sequence: us per call", "value": round(ms * 1e3, 2),
+           "unit": "us", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 5),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": cfg.latent,
+           "data": "synthetic",
+           "config": {"workload": f"{cfg.name} append chunk {C}", "batch": B, "new_tokens_per_sequence": C,
+                      "rank_k": li.rank_k, "rank_v": li.rank_v, "window": cfg.window,
+                      "parallelism": "single GPU"},
+           "tokens_per_s": round(B * C / (ms * 1e-3), 1),
+           "roofline": {"bound": "latency", "kernel": "lr_append_rows + lr_append_finish (n_new > 1), lr_append (1)",
+                        "achieved": round(nbytes / (ms * 1e-3) / 1e9, 2), "peak": PEAK_HBM_TBS * 1000,
+                        "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / (PEAK_HBM_TBS * 1000), 5),
+                        "traffic": None, "bytes_per_launch": nbytes}}
+    print(json.dumps(rec), flush=True)
+
+
 def rankalloc_bench(args):
     """Global rank allocation for the 28-layer model (56 spectra of 512, ranks 128..512 by 8,
     budget 70% of full rank): three short launches (gains, split ordered counts, selection)."""
@@ -709,15 +760,16 @@ def main():
                     help="decode: time the steps as replays of HIP graphs captured from them")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 256 MiB device copy (the counter calibration reference)")
-    ap.add_argument("--op", choices=("decode", "rebase", "prefill", "sensvd", "rankalloc", "basisupdate"),
+    ap.add_argument("--op", choices=("decode", "rebase", "prefill", "sensvd", "rankalloc", "basisupdate", "append"),
                     default="decode",
                     help="decode: the decode step (default); rebase: the historical-coordinate sync; "
                          "prefill: chunked prefill attention; sensvd: sensitivity-weighted SVD basis; "
-                         "rankalloc: global rank allocation; basisupdate: block-incremental basis update")
+                         "rankalloc: global rank allocation; basisupdate: block-incremental basis update; "
+                         "append: storing a chunk of new tokens")
     ap.add_argument("--samples", type=int, default=131072,
                     help="--op sensvd: calibration rows per matrix (batched default: 16384)")
     ap.add_argument("--matrices", type=int, default=1, help="--op sensvd: matrices per (batched) call")
-    ap.add_argument("--chunk", type=int, default=32, help="--op prefill: new tokens per sequence")
+    ap.add_argument("--chunk", type=int, default=32, help="--op prefill / append: new tokens per sequence")
     ap.add_argument("--rank-new", type=int, default=0, help="--op rebase: new rank (0: unchanged)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -745,6 +797,9 @@ def main():
         return
     if args.op == "basisupdate":
         basisupd_bench(args)
+        return
+    if args.op == "append":
+        append_bench(args)
         return
     dev = "cuda"
     cfg = synth.CONFIGS[args.config]

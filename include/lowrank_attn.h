@@ -212,10 +212,12 @@ int lowrank_attn_prefill(const lr_model_desc* model, int32_t layer, const lr_lay
  *   lat_len[b] grows by one. Requires n_new <= W.
  * Requires lat_len[b] + (number of new latent rows) <= t_cap (clamped otherwise: rows past
  * t_cap are dropped and lengths stop at t_cap).
- * One launch: while it runs, bits 24..30 of each lat_len word count the workgroups that have read
- * that sequence's inputs (the length itself stays in bits 0..23); the last one writes the final
- * lengths, so after the call the words hold plain lengths again. Nothing may read or write the
- * lengths on another stream during the call.
+ * n_new == 1 is one launch: while it runs, bits 24..30 of each lat_len word count the workgroups
+ * that have read that sequence's inputs (the length itself stays in bits 0..23); the last one
+ * writes the final lengths, so after the call the words hold plain lengths again. n_new > 1 is
+ * two launches: one matrix-core product over all B * n_new rows, then one that writes the ring
+ * and the lengths. Either way nothing may read or write the lengths on another stream during
+ * the call.
  * z_debug: NULL, or [B][n_new][rank_k + rank_v] float32 receiving, for each latent row this
  *   call writes (the i-th such row of sequence b at index i), its z before storage rounding.
  * Writes latent rows, window slots and the two length arrays, nothing else.
@@ -228,9 +230,11 @@ int lowrank_kv_append(const lr_model_desc* model, int32_t layer, const lr_layer_
  * One decode step of one layer: lowrank_kv_append of one new token per sequence (k_new, v_new
  * [B][1][D] bfloat16, no z_debug) followed by lowrank_attn_decode for the query q, with the same
  * results as those two calls in that order. max_lat_len bounds lat_len[b] after the append;
- * workspace as for lowrank_attn_decode. Fewer launches: for bf16 queries the append and the query
- * fold share one launch (the fold needs only q and the key basis), then the latent kernel, then
- * the combine. Errors: those of both calls, checked before any launch.
+ * workspace as for lowrank_attn_decode. Three launches: the append, the query fold and the
+ * exact window in the first (the window is read as it was, with the new token in the slot it
+ * takes), the latent kernel, then the combine, which also writes the new token into the ring
+ * and the new lengths; until then lat_len and win_len hold their values from before the call.
+ * Errors: those of both calls, checked before any launch.
  */
 int lowrank_decode_step(const lr_model_desc* model, int32_t layer, const lr_layer_cache* cache,
                         int32_t batch, const void* k_new, const void* v_new, const void* q, void* out,

@@ -93,7 +93,9 @@ struct AppendArgs {
   int D, rk, rv, ld_k, ld_v, latent, window, n_new, B;
 };
 
-// One launch does the whole append: projection, storage, window ring and lengths.
+// One launch does the whole append of one token per sequence (a decode step's; more tokens per
+// call go through lr_append_rows below): projection, storage, window ring and lengths. The row
+// loop below handles any n_new, but the launcher sends only n_new == 1 here.
 //
 // grid (nck + ncv, ceil(B / 16)): workgroup (x, y) owns latent columns 32c .. 32c + 31 of K
 // (x < nck, c = x) or of V (c = x - nck) for sequences 16y .. 16y + 15, and is the only writer
@@ -387,6 +389,186 @@ template <bool F32P>
 __global__ __launch_bounds__(256) void lr_append(AppendArgs a, int nck, int ncv) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   append_body<F32P>(a, nck, ncv, blockIdx.x, blockIdx.y, nck + ncv, smem);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Bulk append (n_new > 1, e.g. storing a prefill chunk), two launches:
+//   lr_append_rows    one matrix-core product over the flattened rows f = b * n_new + e of the
+//                     call: workgroup (x, y) owns latent columns 32c .. 32c + 31 of K or V (as
+//                     above) for rows 16y .. 16y + 15, whatever sequences they belong to. Row
+//                     (b, e) is the new token e (W == 0) or the evicted window slot (L + e) mod W
+//                     (W > 0, e < rows_b); it is stored as latent row L + e. The lengths and the
+//                     ring are only read.
+//   lr_append_finish  one workgroup per sequence, after every read: the new tokens into the ring
+//                     (slots (L + wl + t) mod W) and the lengths after the call.
+// The same arithmetic per row as the one-launch path (the same K halves, chains and rounding), so
+// the stored rows do not depend on which path stored them.
+// ---------------------------------------------------------------------------------------------
+template <bool F32P>
+__global__ __launch_bounds__(256) void lr_append_rows(AppendArgs a, int nck, int ncv) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* xs = smem;                                                   // [16][kAppendLdsX] staged rows
+  float (*zt)[kAppendSeqs][kAppendCols] =                                     // [2 halves][16][32] z partials
+      (float (*)[kAppendSeqs][kAppendCols])(smem + kAppendSeqs * kAppendLdsX);
+  const int bx = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cb = wave & 1, kh = wave >> 1;
+  const int kv = bx < nck ? 0 : 1;
+  const int col0 = (bx - (kv ? nck : 0)) * kAppendCols;
+  const int r = kv == 0 ? a.rk : a.rv;
+  const int D = a.D, W = a.window, n_new = a.n_new;
+  const long long nrows = (long long)a.B * n_new;
+  const long long f0 = (long long)blockIdx.y * kAppendSeqs;
+  const __bf16* xnew = kv == 0 ? a.k_new : a.v_new;
+  const __bf16* win = kv == 0 ? a.kwin : a.vwin;
+  unsigned char* zbase = kv == 0 ? a.zk : a.zv;
+  uint32_t* qbase = kv == 0 ? a.zkq : a.zvq;
+  const int ld = kv == 0 ? a.ld_k : a.ld_v;
+  const int rb = row_bytes_of(a.latent, r, ld);
+  const int G = (r + kGroup - 1) / kGroup;
+  // (L, rows) of flattened row f's sequence, and whether the row exists (e < rows)
+  auto row_info = [&](long long f, int& b, int& e, int& L, bool& live) {
+    live = false;
+    b = 0;
+    e = 0;
+    L = 0;
+    if (f >= nrows) return;
+    b = (int)(f / n_new);
+    e = (int)(f - (long long)b * n_new);
+    L = clamp_len(a.lat_len[b], a.t_cap);
+    int rows = n_new;
+    if (W > 0) {
+      const int raw = a.win_len[b];
+      const int wl = raw < 0 ? 0 : (raw > W ? W : raw);
+      rows = wl + n_new - W;
+    }
+    live = e < rows;
+  };
+  const int pcol = col0 + 16 * cb + li;
+  bf16x8 pop[F32P ? 1 : kAppendK / 64];
+  u32x4 xv[4];
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+  float acc[2] = {0.f, 0.f};
+  for (int kc = 0; kc < D; kc += kAppendK) {
+    const int kw = min(kAppendK, D - kc);                      // a multiple of 128
+    // lengths of the rows this thread stages first, then P (its loads stay in flight while the
+    // lengths give the evicted slots' addresses), then the source rows
+    int xb[4], xe[4], xL[4];
+    bool xlive[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sq = (tid + 256 * u) / (kw / 8);
+      row_info(sq < kAppendSeqs ? f0 + sq : nrows, xb[u], xe[u], xL[u], xlive[u]);
+    }
+    if constexpr (!F32P) {
+      const int nks = kw / 64, k0 = kc + kh * (kw / 2);
+      const __bf16* pt = (const __bf16*)(kv == 0 ? a.pk : a.pv) + (size_t)(pcol < r ? pcol : r - 1) * D + k0 + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < kAppendK / 64; ++ks) {
+        pop[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        if (ks < nks && pcol < r) pop[ks] = *(const bf16x8*)(pt + 32 * ks);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int c = i - (i / (kw / 8)) * (kw / 8);
+      xv[u] = u32x4{0u, 0u, 0u, 0u};
+      if (xlive[u]) {
+        const __bf16* src = W == 0 ? xnew + ((size_t)xb[u] * n_new + xe[u]) * D
+                                   : win + ((size_t)xb[u] * W + (xL[u] + xe[u]) % W) * D;
+        xv[u] = *(const u32x4*)(src + kc + c * 8);
+      }
+    }
+    if (kc > 0) __syncthreads();                               // xs of the previous chunk consumed
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int sq = i / (kw / 8), c = i - sq * (kw / 8);
+      if (sq < kAppendSeqs) *(u32x4*)(xs + sq * kAppendLdsX + c * 16) = xv[u];
+    }
+    __syncthreads();
+    if constexpr (!F32P) {
+      const unsigned char* xr = xs + li * kAppendLdsX + kh * kw + lg * 16;
+#pragma unroll
+      for (int ks = 0; ks < kAppendK / 64; ks += 2) {
+        if (ks < kw / 64) {
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xr + ks * 64), pop[ks], c0, 0, 0, 0);
+          if (ks + 1 < kw / 64)
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(xr + ks * 64 + 64), pop[ks + 1], c1, 0, 0, 0);
+        }
+      }
+    } else {
+      const int cl = tid & 31, s2 = 2 * (tid >> 5);
+      const int col = col0 + cl;
+      const float* pt = (const float*)(kv == 0 ? a.pk : a.pv) + (size_t)(col < r ? col : r - 1) * D + kc;
+      for (int k = 0; k < kw; ++k) {
+        const float pv = pt[k];
+#pragma unroll
+        for (int s1 = 0; s1 < 2; ++s1) acc[s1] += (float)*(const __bf16*)(xs + (s2 + s1) * kAppendLdsX + k * 2) * pv;
+      }
+    }
+  }
+  if constexpr (!F32P) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zt[kh][4 * lg + i][16 * cb + li] = c0[i] + c1[i];
+  } else {
+    const int cl = tid & 31, s2 = 2 * (tid >> 5);
+#pragma unroll
+    for (int s1 = 0; s1 < 2; ++s1) {
+      zt[0][s2 + s1][cl] = col0 + cl < r ? acc[s1] : 0.f;
+      zt[1][s2 + s1][cl] = 0.f;
+    }
+  }
+  __syncthreads();
+  // store: wave w writes rows 4w .. 4w + 3, two per pass (lane = column + 32 x which of the two)
+#pragma unroll
+  for (int p2 = 0; p2 < 2; ++p2) {
+    const int sq = 4 * wave + 2 * p2 + (lane >> 5);
+    const int cl = lane & 31;
+    int b, e, L;
+    bool live;
+    row_info(f0 + sq, b, e, L, live);
+    if (live) {                                                // uniform over each 32-lane half
+      const float z = zt[0][sq][cl] + zt[1][sq][cl];
+      const long long row = (long long)L + e;
+      if (a.z_debug && col0 + cl < r)
+        a.z_debug[((size_t)b * n_new + e) * (a.rk + a.rv) + (kv == 0 ? 0 : a.rk) + col0 + cl] = z;
+      if (row < a.t_cap)
+        store_chunk(a.latent, z, cl, col0, r, zbase + ((size_t)b * a.t_cap + row) * rb,
+                    qbase ? qbase + ((size_t)b * a.t_cap + row) * G : nullptr);
+    }
+  }
+}
+
+// grid (B): the new tokens of sequence b into the ring, then its lengths (every reader of them,
+// the rows launch, has finished).
+__global__ __launch_bounds__(256) void lr_append_finish(AppendArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int W = a.window, D = a.D, n_new = a.n_new;
+  const int L = clamp_len(a.lat_len[b], a.t_cap);
+  int wl = 0, rows = n_new;
+  if (W > 0) {
+    const int raw = a.win_len[b];
+    wl = raw < 0 ? 0 : (raw > W ? W : raw);
+    rows = wl + n_new - W;
+    rows = rows < 0 ? 0 : rows;
+    const int vec = D / 8;
+    for (int i = tid; i < n_new * vec; i += 256) {
+      const int t = i / vec, c = i - t * vec;
+      const size_t dst = ((size_t)b * W + (L + wl + t) % W) * D + c * 8;
+      const size_t src = ((size_t)b * n_new + t) * D + c * 8;
+      *(u32x4*)(a.kwin + dst) = *(const u32x4*)(a.k_new + src);
+      *(u32x4*)(a.vwin + dst) = *(const u32x4*)(a.v_new + src);
+    }
+  }
+  __syncthreads();                                             // every thread has read the lengths
+  if (tid == 0) {
+    const long long nl = (long long)L + rows;
+    if (W > 0) a.win_len[b] = wl + n_new > W ? W : wl + n_new;
+    a.lat_len[b] = (int)(nl > a.t_cap ? a.t_cap : nl);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -881,9 +1063,19 @@ hipError_t launch_append(const AppendPlan& p, const lr_layer_cache* c, const voi
   AppendArgs a;
   append_args(p, c, k_new, v_new, z_debug, a);
   const int nck = (p.rk + kAppendCols - 1) / kAppendCols, ncv = (p.rv + kAppendCols - 1) / kAppendCols;
-  const dim3 grid(nck + ncv, (p.B + kAppendSeqs - 1) / kAppendSeqs);
-  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append<true>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
-  else hipLaunchKernelGGL(lr_append<false>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
+  if (p.n_new == 1) {
+    const dim3 grid(nck + ncv, (p.B + kAppendSeqs - 1) / kAppendSeqs);
+    if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append<true>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
+    else hipLaunchKernelGGL(lr_append<false>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
+    return hipGetLastError();
+  }
+  const long long nrows = (long long)p.B * p.n_new;
+  const dim3 grid(nck + ncv, (unsigned)((nrows + kAppendSeqs - 1) / kAppendSeqs));
+  if (p.latent == LR_F32) hipLaunchKernelGGL(lr_append_rows<true>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
+  else hipLaunchKernelGGL(lr_append_rows<false>, grid, dim3(256), kAppendLds, st, a, nck, ncv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lr_append_finish, dim3(p.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
