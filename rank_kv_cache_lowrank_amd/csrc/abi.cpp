@@ -71,6 +71,8 @@ static void layout_workspace(DecodePlan* p) {
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * 4);
   p->off_win = off;
   if (p->exact) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);
+  p->off_rng = off;   // range table: [nwg] int4 (sequence, slot, first token, end token), [B] int
+  if (p->bal) off = align256(off + (size_t)p->nwg * 16 + (size_t)p->B * 4);
   p->ws_bytes = off > 0 ? off : 256;
 }
 
@@ -126,6 +128,18 @@ int plan_attention(const lr_model_desc* m, int layer, int batch, int n_q, bool p
   } else {
     p->split_tokens = round_up((max_len + target - 1) / target, kTileTokens);
     p->nsplit = (max_len + p->split_tokens - 1) / p->split_tokens;
+  }
+  p->nwg = p->B * p->nsplit;
+  // ragged lengths: the same grid, ranges balanced over the sequences on the device (the front
+  // launch writes the range table), up to twice the slots per sequence
+  if (!prefill && n_q == 1 && !(o && o->nsplit > 0) && p->B >= 2 && p->B <= kBalMaxSeqs && max_len > 0) {
+    int slots = 2 * p->nsplit;
+    if (slots > max_split) slots = max_split;
+    if (slots > kMaxSplit) slots = kMaxSplit;
+    if (slots > p->nsplit) {
+      p->bal = 1;
+      p->nsplit = slots;
+    }
   }
 
   layout_workspace(p);

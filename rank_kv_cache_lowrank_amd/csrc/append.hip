@@ -928,17 +928,98 @@ constexpr int kFrontLds = kWinMfmaLds > kAppendLds ? (kWinMfmaLds > kWinValuLds 
                                                    : (kAppendLds > kWinValuLds ? kAppendLds : kWinValuLds);
 static_assert(kFrontLds >= kHeadsPad * kFoldD * 4, "the float32 fold's query tile fits");
 
-// The first launch of a decode call: [window, W > 0] [append (a decode step only)] [fold], the
-// longest roles first so that they are dispatched first. Within a decode step none of them writes
+// ---------------------------------------------------------------------------------------------
+// Range planning of a decode call (one wave of the first launch; RangeArgs in fold.h). Integer
+// arithmetic only, the same on every run, and no workgroup barrier: lane l holds sequences l,
+// l + 64, ...; for each candidate Q the wave sums ceil(tiles_b / Q) with one DPP reduction; a
+// binary search finds the smallest Q whose total fits the grid. Prefixes and the sequence of
+// each workgroup come from broadcast LDS reads (no chain of dependent cross-lane steps).
+// ---------------------------------------------------------------------------------------------
+constexpr int kPlanLds = 3 * kBalMaxSeqs * 4;
+static_assert(kFrontLds >= kPlanLds, "the range plan's tables fit");
+
+__device__ void range_plan_body(const RangeArgs& r, unsigned char* smem) {
+  if (threadIdx.x >= 64) return;
+  int* tl = (int*)smem;                  // [B] tiles of each sequence
+  int* pre = tl + kBalMaxSeqs;           // [B] first latent workgroup of each sequence
+  int* lens = pre + kBalMaxSeqs;         // [B] tokens attended
+  const int lane = threadIdx.x, B = r.B;
+  auto attended = [&](int b) {           // tokens the latent kernel attends for sequence b
+    int L = r.step ? step_lens(r.lat_len[b], r.window > 0 ? r.win_len[b] : 0, r.window, r.t_cap).L_new
+                   : r.lat_len[b];
+    return L < 0 ? 0 : (L > r.max_len ? r.max_len : L);
+  };
+  // sequence `lane` stays in registers (the common case B <= 64); the rest go through LDS
+  const int L0 = lane < B ? attended(lane) : 0;
+  const int t0 = (L0 + kTileTokens - 1) / kTileTokens;
+  int tmax = t0, tsum = t0;
+  tl[lane] = t0;
+  lens[lane] = L0;
+  for (int b = lane + 64; b < B; b += 64) {
+    const int L = attended(b);
+    const int t = (L + kTileTokens - 1) / kTileTokens;
+    lens[b] = L;
+    tl[b] = t;
+    tmax = max(tmax, t);
+    tsum += t;
+  }
+  tmax = __ockl_wfred_max_i32(tmax);
+  tsum = __ockl_wfred_add_i32(tsum);
+  // the smallest Q in [lo, hi] with sum_b ceil(tiles_b / Q) <= nwg; at Q = tmax the sum is the
+  // number of non-empty sequences, at most B <= nwg
+  int lo = max(1, max((tmax + r.nslot - 1) / r.nslot, (tsum + r.nwg - 1) / r.nwg));
+  int hi = max(1, tmax);
+  if (lo > hi) lo = hi;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    int c = (t0 + mid - 1) / mid;
+    for (int b = lane + 64; b < B; b += 64) c += (tl[b] + mid - 1) / mid;
+    c = __ockl_wfred_add_i32(c);
+    if (c <= r.nwg) hi = mid;
+    else lo = mid + 1;
+  }
+  const int Q = lo;
+  // ranges per sequence into LDS (tl now holds them), then each lane's exclusive prefix from
+  // broadcast reads of all the sequences before it
+  tl[lane] = lane < B ? (t0 + Q - 1) / Q : 0;
+  for (int b = lane + 64; b < B; b += 64) tl[b] = (tl[b] + Q - 1) / Q;
+  for (int b = lane; b < B; b += 64) {
+    int p = 0;
+    for (int k = 0; k < b; ++k) p += tl[k];
+    pre[b] = p;
+    r.nrng[b] = tl[b];
+  }
+  int total = 0;
+  for (int k = 0; k < B; ++k) total += tl[k];
+  const int qt = Q * kTileTokens;
+  for (int w = lane; w < r.nwg; w += 64) {
+    int e0 = -1, e1 = 0, e2 = 0, e3 = 0;
+    if (w < total) {
+      int b = 0;                         // the last sequence whose first workgroup is <= w
+      for (int k = 1; k < B; ++k) b = pre[k] <= w ? k : b;
+      const int s = w - pre[b];
+      e0 = b;
+      e1 = s;
+      e2 = s * qt;
+      e3 = min(e2 + qt, lens[b]);
+    }
+    *(int4*)(r.table + 4 * w) = make_int4(e0, e1, e2, e3);
+  }
+}
+
+// The first launch of a decode call: [range plan] [window, W > 0] [append (a decode step only)]
+// [fold], the longest roles first so that they are dispatched first. Within a decode step none of them writes
 // what another reads: the append stores the new latent row at index L (which no role of this
 // launch reads), the window reads the ring as it was, and the lengths are left for the step's
 // last launch.
 template <int LAT>
 __global__ __launch_bounds__(256) void lr_front(AppendArgs a, int nck, int ncv, int n_append, FoldArgs f, int nfx,
-                                                int nfy, int n_win, WinArgs w) {
+                                                int nfy, int n_win, WinArgs w, int n_plan, RangeArgs rg) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int x = blockIdx.x;
-  if (x < n_win) {
+  const int x = blockIdx.x - n_plan;
+  if (x < 0) {
+    range_plan_body(rg, smem);
+  } else if (x < n_win) {
     if constexpr (LAT == LR_F32) window_body<float>(w, a, x, smem);
     else if (w.Hq / w.Hkv <= 16) window_mfma_body(w, a, x, smem);
     else window_body<__bf16>(w, a, x, smem);
@@ -1101,17 +1182,17 @@ hipError_t launch_front(const FrontPlan& fp, const AppendPlan* ap, const lr_laye
   w.Hkv = f.Hkv;
   w.wscale = wscale;
   w.step = ap != nullptr && fp.n_win > 0;
-  const dim3 grid(fp.n_append + fp.n_fold + fp.n_win);
+  const dim3 grid(fp.n_plan + fp.n_append + fp.n_fold + fp.n_win);
   if (grid.x == 0) return hipSuccess;
   if (fp.latent == LR_F32)
     hipLaunchKernelGGL(lr_front<LR_F32>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx, fp.nfy,
-                       fp.n_win, w);
+                       fp.n_win, w, fp.n_plan, fp.rng);
   else if (fp.latent == LR_I4G32)
     hipLaunchKernelGGL(lr_front<LR_I4G32>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx,
-                       fp.nfy, fp.n_win, w);
+                       fp.nfy, fp.n_win, w, fp.n_plan, fp.rng);
   else
     hipLaunchKernelGGL(lr_front<LR_BF16>, grid, dim3(256), kFrontLds, st, a, fp.nck, fp.ncv, fp.n_append, f, fp.nfx,
-                       fp.nfy, fp.n_win, w);
+                       fp.nfy, fp.n_win, w, fp.n_plan, fp.rng);
   return hipGetLastError();
 }
 

@@ -65,6 +65,7 @@ struct DecodeArgs {
   const __bf16* vchunk;
   int step;                 // a decode step: lat_len / win_len still hold the lengths before the
                             // step's token, and the latent rows attended are step_lens().L_new
+  const int* rng;           // balanced ranges (RangeArgs table, written by the first launch) or NULL
 };
 
 
@@ -522,18 +523,32 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
   static_assert(I4 || ((kTileTokens * SK + 1023) / 1024 <= kProducers * kMaxChunkPerProducer &&
                        (kTileTokens * SV + 1023) / 1024 <= kProducers * kMaxChunkPerProducer), "DMA chunks");
 
-  const int sq = wg / a.nsplit;                      // query sequence (token of a chunk)
-  const int s = wg - sq * a.nsplit;
-  const int b = sq / a.qpb;                          // stored sequence whose latents it reads
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const bool producer = wave >= 4 * G;
-
-  int L = a.step ? step_lens(a.lat_len[b], a.window > 0 ? a.win_len[b] : 0, a.window, a.t_cap).L_new
-                 : a.lat_len[b];
-  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
-  const int t_begin = s * a.split_tokens;
-  const int t_end = min(t_begin + a.split_tokens, L);
+  int sq, s, t_begin, t_end;
+  if (a.rng) {                                       // balanced: this workgroup's table entry
+    const int* e = a.rng + 4 * wg;
+    sq = e[0];
+    s = e[1];
+    t_begin = e[2];
+    t_end = e[3];
+    if (sq < 0) {                                    // no range: an empty pass, nothing written
+      sq = 0;
+      s = -1;
+      t_begin = t_end = 0;
+    }
+  } else {
+    sq = wg / a.nsplit;                              // query sequence (token of a chunk)
+    s = wg - sq * a.nsplit;
+    const int b0 = sq / a.qpb;
+    int L = a.step ? step_lens(a.lat_len[b0], a.window > 0 ? a.win_len[b0] : 0, a.window, a.t_cap).L_new
+                   : a.lat_len[b0];
+    L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+    t_begin = s * a.split_tokens;
+    t_end = min(t_begin + a.split_tokens, L);
+  }
+  const int b = sq / a.qpb;                          // stored sequence whose latents it reads
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTileTokens - 1) / kTileTokens : 0;
   const int niter = (ntiles + TPI - 1) / TPI;
 
@@ -945,8 +960,8 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
 #pragma unroll
       for (int j = 0; j < NVB; ++j) acc[j] += abuf[(x * NVB + j) * 64 + lane] * wb;
     }
-    const size_t pidx = (size_t)sq * a.nsplit + s;
-    const int head = hb * 16 + li;
+    const size_t pidx = (size_t)sq * a.nsplit + (s < 0 ? 0 : s);
+    const int head = s < 0 ? a.Hq : hb * 16 + li;    // a workgroup without a range writes nothing
     if (half == 0 && lg == 0 && head < a.Hq) {
       a.part_ml[(pidx * a.Hq + head) * 2] = ms;
       a.part_ml[(pidx * a.Hq + head) * 2 + 1] = lt;
@@ -1008,6 +1023,7 @@ struct CombineArgs {
   int i4_order;             // partials are in the dequantised int4 tiles' block order
   StepFinish fin;           // a decode step (fin.lat_len != NULL): workgroup (b, head 0) also
                             // writes sequence b's new token into the ring and its new lengths
+  const int* nrng;          // balanced ranges: ranges (partial slots in use) per sequence, or NULL
 };
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
@@ -1044,6 +1060,7 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   float* ws = ahat + a.rv_pad16;          // [nsplit]
   float* red = ws + a.nsplit;             // [8]
   const size_t base = (size_t)b * a.nsplit;
+  const int ns = a.nrng ? a.nrng[b] : a.nsplit;  // slots of this sequence in use
   // no reader of the ring or the lengths is left in the step (this launch reads neither)
   if (a.fin.lat_len != nullptr && j == 0) step_finish(a.fin, b);
 
@@ -1054,12 +1071,16 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
     lw = wp[a.d + 1];
   }
   float mloc = -INFINITY;
-  for (int s = tid; s < a.nsplit; s += 256) mloc = fmaxf(mloc, a.part_ml[((base + s) * a.Hq + j) * 2]);
+  // the slot loads do not wait for ns: slots past it are loaded and then ignored
+  for (int s = tid; s < a.nsplit; s += 256) {
+    const float mv = a.part_ml[((base + s) * a.Hq + j) * 2];
+    if (s < ns) mloc = fmaxf(mloc, mv);
+  }
   const float mstar = block_reduce(fmaxf(mloc, mw), red, true);
   const bool live = mstar != -INFINITY;
 
   float lloc = 0.f;
-  for (int s = tid; s < a.nsplit; s += 256) {
+  for (int s = tid; s < ns; s += 256) {
     const float ms = a.part_ml[((base + s) * a.Hq + j) * 2];
     const float w = (live && ms != -INFINITY) ? fast_exp2(ms - mstar) : 0.f;
     ws[s] = w;
@@ -1069,29 +1090,30 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   const float lstar = block_reduce(lloc, red, false) + ww * lw;
   __syncthreads();
 
-  // merge the ranges: Ahat[r] = sum_s w_s A_s[r]
+  // merge the ranges: Ahat[r] = sum_s w_s A_s[r], thread (sg, r4) over slots s = sg, sg + 4, ...
+  // in ascending order; the loads of up to 8 slots go out together (slot indices clamped to the
+  // last one in use, with weight 0 past it), so a sequence with more ranges costs no extra round
+  // trip until it has more than 32
   {
+    constexpr int U = 8;
     const int sg = tid >> 6, r4 = (tid & 63) * 4;
     for (int r0 = 0; r0 < a.rv_pad16; r0 += 256) {
       const int r = r0 + r4;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (r < a.rv_pad16) {
-        int s = sg;
-        for (; s + 12 < a.nsplit; s += 16) {
-          f32x4 v[4];
-          float w[4];
+        for (int s0 = sg; s0 < ns; s0 += 4 * U) {
+          f32x4 v[U];
+          float w[U];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            w[u] = ws[s + 4 * u];
-            v[u] = *(const f32x4*)(a.part_acc + ((base + s + 4 * u) * a.Hq + j) * a.rv_pad16 + r);
+          for (int u = 0; u < U; ++u) {
+            const int s = s0 + 4 * u;
+            const int sc = s < ns ? s : ns - 1;
+            w[u] = s < ns ? ws[sc] : 0.f;
+            v[u] = *(const f32x4*)(a.part_acc + ((base + sc) * a.Hq + j) * a.rv_pad16 + r);
           }
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < U; ++u)
             if (w[u] != 0.f) acc += w[u] * v[u];
-        }
-        for (; s < a.nsplit; s += 4) {
-          const float w = ws[s];
-          if (w != 0.f) acc += w * *(const f32x4*)(a.part_acc + ((base + s) * a.Hq + j) * a.rv_pad16 + r);
         }
         *(f32x4*)(part + sg * pw + r) = acc;
       }
@@ -1237,6 +1259,21 @@ static hipError_t decode_front(const DecodePlan& p, const AppendPlan* ap, const 
   fp.n_win = p.window > 0 ? p.B * p.Hkv : 0;
   fp.window = p.window;
   fp.t_cap = p.t_cap;
+  memset(&fp.rng, 0, sizeof(fp.rng));
+  fp.n_plan = p.bal ? 1 : 0;
+  if (p.bal) {
+    fp.rng.lat_len = c->lat_len;
+    fp.rng.win_len = c->win_len;
+    fp.rng.table = (int*)(w + p.off_rng);
+    fp.rng.nrng = (int*)(w + p.off_rng) + 4 * p.nwg;
+    fp.rng.t_cap = p.t_cap;
+    fp.rng.B = p.B;
+    fp.rng.nwg = p.nwg;
+    fp.rng.nslot = p.nsplit;
+    fp.rng.max_len = p.max_len;
+    fp.rng.window = p.window;
+    fp.rng.step = ap != nullptr;
+  }
   return launch_front(fp, ap, c, k_new, v_new, f, (float*)(w + p.off_win), scale, st);
 }
 
@@ -1334,6 +1371,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   a.nr = p.nr;
   a.raw_stage = p.raw_stage;
   a.step = step;
+  a.rng = p.bal ? (const int*)(w + p.off_rng) : nullptr;
   hipError_t e;
   if (p.pf) {
     // prefill over bf16 latents: the dedicated exact-keys kernel (window slots and the chunk's
@@ -1346,7 +1384,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
       e = launch_prefill_exact(p, c, q, k_chunk, v_chunk, a.win_part, st);
       if (e != hipSuccess) return e;
     }
-    const int grid = a.n_win_blocks + p.B * p.nsplit;
+    const int grid = a.n_win_blocks + p.nwg;
     if (p.latent == LR_F32) e = launch_decode_kernel<8, 8, LT_F32, 2, false>(a, grid, p.lds_bytes, st, ev_begin, ev_end);
     else if (p.latent == LR_I4G32) e = dispatch_decode<LT_I4>(p, a, grid, st, ev_begin, ev_end);
     else e = dispatch_decode<LT_BF16>(p, a, grid, st, ev_begin, ev_end);
@@ -1370,6 +1408,7 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   ca.nsplit = p.nsplit;
   ca.exact = p.exact;
   ca.i4_order = p.latent == LR_I4G32;
+  ca.nrng = p.bal ? (const int*)(w + p.off_rng) + 4 * p.nwg : nullptr;
   memset(&ca.fin, 0, sizeof(ca.fin));
   if (step) {
     ca.fin.k_new = (const __bf16*)step_k_new;

@@ -217,9 +217,26 @@ __device__ __forceinline__ void fold_f32_body(const FoldArgs& f, int bx, int g, 
     for (int j = Hq + hs; j < kHeadsPad; j += 4) out[(size_t)j * rk_pad] = (__bf16)0.f;
 }
 
-// The first launch of a decode call (append.hip): workgroups [0, n_win) attend over the exact
-// window (W > 0), one per (sequence, KV head); [n_win, n_win + n_append) append the step's token
-// (lowrank_decode_step only); the rest fold the query. The longest roles are dispatched first.
+// Balanced token ranges of a decode call, planned on the device by one workgroup of the first
+// launch (the lengths live on the device): every sequence is cut into ranges of the same Q
+// tiles, Q the smallest that gives at most nwg ranges in all and at most nslot per sequence;
+// sequence b takes n_b = ceil(tiles_b / Q) of them, placed in sequence order. table[4 w ..]:
+// (b, slot, first token, end token) of latent workgroup w, b = -1 for a workgroup without a
+// range; nrng[b] = n_b. The lengths are those the latent kernel attends (after the step's
+// append in a decode step, clamped to max_len).
+struct RangeArgs {
+  const int32_t* lat_len;
+  const int32_t* win_len;
+  int* table;               // [nwg][4]
+  int* nrng;                // [B]
+  long long t_cap;
+  int B, nwg, nslot, max_len, window, step;
+};
+
+// The first launch of a decode call (append.hip): workgroup 0 plans the balanced ranges (when
+// they are on); then [n_win] workgroups attend over the exact window (W > 0), one per (sequence,
+// KV head); [n_append] append the step's token (lowrank_decode_step only); the rest fold the
+// query. The longest roles are dispatched first.
 struct FrontPlan {
   int latent;               // lr_dtype of the latents (selects the fold and the append's bases)
   int n_append, nck, ncv;   // append workgroups and their column chunks (0 when no append)
@@ -227,6 +244,8 @@ struct FrontPlan {
   int n_win;                // window workgroups (B x Hkv, or 0)
   int window;               // W
   long long t_cap;
+  int n_plan;               // 1: the range-planning workgroup runs (rng is filled in)
+  RangeArgs rng;
 };
 hipError_t launch_front(const FrontPlan& fp, const AppendPlan* ap, const lr_layer_cache* c, const void* k_new,
                         const void* v_new, const FoldArgs& f, float* win_part, float wscale, hipStream_t st);

@@ -109,7 +109,9 @@ struct DecodePlan {
   int latent;          // lr_dtype
   float sm_scale;
   int window;
-  int max_len, nsplit, split_tokens;
+  int max_len, nsplit, split_tokens;  // nsplit: partial slots per sequence
+  int bal;             // decode with ranges balanced over the sequences' lengths (range table)
+  int nwg;             // latent workgroups of the grid (B x nsplit when not balanced)
   int64_t t_cap;
   int row_bytes_k, row_bytes_v;     // bytes of one stored latent row (codes for int4)
   int qp_bytes_k, qp_bytes_v;       // int4: bytes of one row's scale/zero words, else 0
@@ -119,8 +121,13 @@ struct DecodePlan {
   int lds_bytes;                    // dynamic LDS of the decode kernel
   int pf;                           // prefill with the dedicated latent kernel (bf16 latents)
   int pf_ntg, pf_nst, pf_lds;       // its token groups per sequence, ring stages, dynamic LDS
-  size_t off_qt, off_ml, off_acc, off_win, ws_bytes;
+  size_t off_qt, off_ml, off_acc, off_win, off_rng, ws_bytes;
 };
+
+// Balanced token ranges (decode, automatic split, 2 <= B <= kBalMaxSeqs): the grid keeps about
+// one latent workgroup per compute unit, and each sequence gets up to twice as many partial
+// slots, so that longer sequences can take more ranges.
+constexpr int kBalMaxSeqs = 256;
 
 // Fills *p; returns LR_OK or an error code with a message in *msg. n_q query tokens per stored
 // sequence; prefill: the queries are a chunk whose own rows are exact keys (causal).
