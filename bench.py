@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import gc
 import json
 import os
 import sys
@@ -302,6 +303,8 @@ def decode28_bench(args):
     graph = capture_graph(torch, full_step) if args.graph else None
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()                 # no collector pause while the host enqueues the timed steps
     start.record()
     for i in range(K):
         if graph is not None:
@@ -310,6 +313,7 @@ def decode28_bench(args):
             full_step()
     stop.record()
     torch.cuda.synchronize()
+    gc.enable()
     ms_per_step = start.elapsed_time(stop) / K
     evs = [[(ev.create(), ev.create()) for _ in range(NL)] for _ in range(K)]
     sev = [(ev.create(), ev.create()) for _ in range(K)]
@@ -861,6 +865,8 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     lens_a = []
+    gc.collect()
+    gc.disable()                 # no collector pause while the host enqueues the timed steps
     start.record()
     for i in range(W, W + K):
         if graphs is not None:
@@ -870,6 +876,7 @@ def main():
             lens_a.append(step(i))
     stop.record()
     torch.cuda.synchronize()
+    gc.enable()
     ms_per_step = start.elapsed_time(stop) / K
     # pass B
     kev = [(ev.create(), ev.create()) for _ in range(K)]

@@ -69,6 +69,21 @@ def test_split_invariance(nsplit):
     assert rel_err(out.numpy(), ref_out.numpy()) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("latent", ["bf16", "i4g32"])
+def test_balanced_ranges_extreme_raggedness(latent):
+    """Ragged lengths take balanced ranges (planned on the device from the lengths): one long
+    sequence gets up to twice the uniform count of ranges, tiny and empty ones none or one. Every
+    sequence against the oracle, an explicit split count (uniform ranges) as a second reference,
+    and a max_lat_len above every length."""
+    cfg = synth.CONFIGS[1].replace(batch=12, seq_len=4100, latent=latent)
+    lens = np.array([4100, 1, 0, 16, 17, 3000, 5, 2500, 0, 33, 4095, 64], np.int32)
+    li = synth.make_layer(cfg, q_scale=16.0, lat_len=lens, t_cap=4100)
+    out, _ = check(li, max_lat_len=4100)
+    assert torch.all(out[2] == 0) and torch.all(out[8] == 0)
+    uni, _ = check(li, nsplit=7, max_lat_len=4100)
+    assert rel_err(out.numpy(), uni.numpy()) <= TOL[latent]
+
+
 def test_ragged_lengths_and_empty_sequences():
     cfg = synth.CONFIGS[1].replace(batch=8, seq_len=300)
     lens = np.array([0, 1, 31, 32, 33, 200, 299, 300], np.int32)
