@@ -643,14 +643,31 @@ __global__ __launch_bounds__(256) void lr_prefill_combine(PfCombineArgs a) {
     const float* ml = a.part_ml + ((size_t)sq * a.nsplit * a.Hq + head) * 2;   // range s at + s*Hq*2
     const float* wp = a.win_part + ((size_t)sq * a.Hq + head) * 130;
     const float mw = wp[128], lw = wp[129];
+    // ranges 8 at a time: their loads go out together (indices clamped, extra ones ignored)
     float mstar = mw;
-    for (int s = 0; s < a.nsplit; ++s) mstar = fmaxf(mstar, ml[(size_t)s * a.Hq * 2]);
+    for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
+      float mv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mv[k] = ml[(size_t)min(s0 + k, a.nsplit - 1) * a.Hq * 2];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < a.nsplit) mstar = fmaxf(mstar, mv[k]);
+    }
     const bool live = mstar != -INFINITY;
     float l = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = ml[(size_t)s * a.Hq * 2];
-      const float w = (live && ms != -INFINITY) ? fast_exp2(ms - mstar) : 0.f;
-      if (w != 0.f) l += w * ml[(size_t)s * a.Hq * 2 + 1];
+    for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
+      float mv[8], lv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const size_t o = (size_t)min(s0 + k, a.nsplit - 1) * a.Hq * 2;
+        mv[k] = ml[o];
+        lv[k] = ml[o + 1];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = (s0 + k < a.nsplit && live && mv[k] != -INFINITY) ? fast_exp2(mv[k] - mstar) : 0.f;
+        if (w != 0.f) l += w * lv[k];
+      }
     }
     const float ww = (live && mw != -INFINITY) ? fast_exp2(mw - mstar) : 0.f;
     rowm[rr] = mstar;
@@ -679,17 +696,31 @@ __global__ __launch_bounds__(256) void lr_prefill_combine(PfCombineArgs a) {
         rowoff[u] = (size_t)sq * a.nsplit * a.Hq + head;   // + s * Hq selects range s
         mst[u] = rowm[rs];
       }
-      for (int s = 0; s < a.nsplit; ++s) {
+      // 4 ranges x 4 items of loads in flight together (range indices clamped; the ranges are
+      // still added in ascending order)
+      int r4s[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r4s[u] = min(i0 + 256 * u, nitems - 1) % nq4;
+      for (int s0 = 0; s0 < a.nsplit; s0 += 4) {
+        float msv[4][4];
+        f32x4 xv[4][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          if (use[u]) {
-            const int idx = i0 + 256 * u;
-            const int r4 = idx % nq4;
-            const size_t row = rowoff[u] + (size_t)s * a.Hq;
-            const float ms = a.part_ml[row * 2];
-            const float w = (mst[u] != -INFINITY && ms != -INFINITY) ? fast_exp2(ms - mst[u]) : 0.f;
-            const f32x4 x = *(const f32x4*)(a.part_acc + row * a.rv_pad16 + 4 * r4);
-            if (w != 0.f) acc[u] += w * x;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const size_t row = rowoff[u] + (size_t)min(s0 + k, a.nsplit - 1) * a.Hq;
+            msv[u][k] = a.part_ml[row * 2];
+            xv[u][k] = *(const f32x4*)(a.part_acc + row * a.rv_pad16 + 4 * r4s[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float ms = msv[u][k];
+            const float w = (use[u] && s0 + k < a.nsplit && mst[u] != -INFINITY && ms != -INFINITY)
+                                ? fast_exp2(ms - mst[u]) : 0.f;
+            if (w != 0.f) acc[u] += w * xv[u][k];
           }
         }
       }
