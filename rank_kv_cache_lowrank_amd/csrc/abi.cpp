@@ -68,7 +68,10 @@ static void layout_workspace(DecodePlan* p) {
   p->off_ml = off;
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * 2 * 4);
   p->off_acc = off;
-  off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * 4);
+  // value partials: bf16 from the decode kernel (bf16 / int4 latents), float32 for float32
+  // latents and for the dedicated bf16 prefill kernel
+  const int acc_bytes = (p->latent == LR_F32 || p->pf) ? 4 : 2;
+  off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * acc_bytes);
   p->off_win = off;
   if (p->exact) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);
   p->off_rng = off;   // range table: [nwg] int4 (sequence, slot, first token, end token), [B] int

@@ -966,11 +966,23 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       a.part_ml[(pidx * a.Hq + head) * 2] = ms;
       a.part_ml[(pidx * a.Hq + head) * 2 + 1] = lt;
     }
+    // the range's value partial: float32 for float32 latents, else bf16 (one rounding of the
+    // fp32 sum, the precision of the bf16 P it was accumulated from), half the bytes to write
+    // and for the combine to read
 #pragma unroll
     for (int j = 0; j < NVB; ++j) {
       const int rb = SP ? j : half + 2 * j;
-      if (rb < a.nrb && head < a.Hq)
-        *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + rb * 16 + 4 * lg) = acc[j];
+      const size_t o = (pidx * a.Hq + head) * a.rv_pad16 + rb * 16 + 4 * lg;
+      if (rb < a.nrb && head < a.Hq) {
+        if constexpr (LT == LT_F32) {
+          *(f32x4*)(a.part_acc + o) = acc[j];
+        } else {
+          bf16x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (__bf16)acc[j][e];
+          *(bf16x4*)((__bf16*)a.part_acc + o) = h;
+        }
+      }
     }
   }
 }
@@ -1014,7 +1026,7 @@ __global__ __launch_bounds__(256) void lr_fold_mfma(FoldArgs f) {
 // ---------------------------------------------------------------------------------------------
 struct CombineArgs {
   const float* part_ml;
-  const float* part_acc;
+  const float* part_acc;    // [B][nsplit][Hq][rv_pad16]: float32 (f32 latents) or bf16 values
   const float* win_part;
   const void* bv;
   void* out;
@@ -1109,7 +1121,13 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
             const int s = s0 + 4 * u;
             const int sc = s < ns ? s : ns - 1;
             w[u] = s < ns ? ws[sc] : 0.f;
-            v[u] = *(const f32x4*)(a.part_acc + ((base + sc) * a.Hq + j) * a.rv_pad16 + r);
+            const size_t o = ((base + sc) * a.Hq + j) * a.rv_pad16 + r;
+            if constexpr (sizeof(BT) == 2) {      // bf16 partials (bf16 / int4 latents)
+              const bf16x4 h = *(const bf16x4*)((const __bf16*)a.part_acc + o);
+              v[u] = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+            } else {
+              v[u] = *(const f32x4*)(a.part_acc + o);
+            }
           }
 #pragma unroll
           for (int u = 0; u < U; ++u)
