@@ -966,15 +966,16 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       a.part_ml[(pidx * a.Hq + head) * 2] = ms;
       a.part_ml[(pidx * a.Hq + head) * 2 + 1] = lt;
     }
-    // the range's value partial: float32 for float32 latents, else bf16 (one rounding of the
-    // fp32 sum, the precision of the bf16 P it was accumulated from), half the bytes to write
-    // and for the combine to read
+    // the range's value partial: bf16 for int4 latents (one rounding of the fp32 sum: half the
+    // bytes to write and for the combine to read, at most 2^-9 of each output element, a fifth of
+    // the int4 error budget), float32 for float32 and bf16 latents, whose tighter budget the
+    // bf16 query fold and bf16 P already use most of
 #pragma unroll
     for (int j = 0; j < NVB; ++j) {
       const int rb = SP ? j : half + 2 * j;
       const size_t o = (pidx * a.Hq + head) * a.rv_pad16 + rb * 16 + 4 * lg;
       if (rb < a.nrb && head < a.Hq) {
-        if constexpr (LT == LT_F32) {
+        if constexpr (LT != LT_I4) {
           *(f32x4*)(a.part_acc + o) = acc[j];
         } else {
           bf16x4 h;
@@ -1026,7 +1027,7 @@ __global__ __launch_bounds__(256) void lr_fold_mfma(FoldArgs f) {
 // ---------------------------------------------------------------------------------------------
 struct CombineArgs {
   const float* part_ml;
-  const float* part_acc;    // [B][nsplit][Hq][rv_pad16]: float32 (f32 latents) or bf16 values
+  const float* part_acc;    // [B][nsplit][Hq][rv_pad16]: float32, or bf16 values for int4 latents
   const float* win_part;
   const void* bv;
   void* out;
@@ -1060,7 +1061,7 @@ __device__ __forceinline__ void load8f(const T* p, float* out) { load8<T>(p, out
 // s = sg, sg+4, ... over 4 consecutive latent indices with 16-byte loads. Phase 3 (up-project):
 // thread (rg, cg) accumulates 8 output columns over latent rows rg, rg+16, ... with 16-byte
 // loads of Bv; the 16 row groups are reduced through LDS.
-template <typename BT, typename OT>
+template <typename BT, typename OT, bool PB>
 __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
   extern __shared__ float cs[];
   const int tid = threadIdx.x;
@@ -1122,7 +1123,7 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
             const int sc = s < ns ? s : ns - 1;
             w[u] = s < ns ? ws[sc] : 0.f;
             const size_t o = ((base + sc) * a.Hq + j) * a.rv_pad16 + r;
-            if constexpr (sizeof(BT) == 2) {      // bf16 partials (bf16 / int4 latents)
+            if constexpr (PB) {                   // bf16 partials (int4 latents)
               const bf16x4 h = *(const bf16x4*)((const __bf16*)a.part_acc + o);
               v[u] = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
             } else {
@@ -1442,11 +1443,14 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);
   const bool f32b = p.latent == LR_F32;
+  const bool i4 = p.latent == LR_I4G32;
   const bool f32o = out_dtype == LR_F32;
-  if (f32b && f32o) hipLaunchKernelGGL((lr_combine<float, float>), cgrid, dim3(256), lds, st, ca);
-  else if (f32b) hipLaunchKernelGGL((lr_combine<float, __bf16>), cgrid, dim3(256), lds, st, ca);
-  else if (f32o) hipLaunchKernelGGL((lr_combine<__bf16, float>), cgrid, dim3(256), lds, st, ca);
-  else hipLaunchKernelGGL((lr_combine<__bf16, __bf16>), cgrid, dim3(256), lds, st, ca);
+  if (f32b && f32o) hipLaunchKernelGGL((lr_combine<float, float, false>), cgrid, dim3(256), lds, st, ca);
+  else if (f32b) hipLaunchKernelGGL((lr_combine<float, __bf16, false>), cgrid, dim3(256), lds, st, ca);
+  else if (i4 && f32o) hipLaunchKernelGGL((lr_combine<__bf16, float, true>), cgrid, dim3(256), lds, st, ca);
+  else if (i4) hipLaunchKernelGGL((lr_combine<__bf16, __bf16, true>), cgrid, dim3(256), lds, st, ca);
+  else if (f32o) hipLaunchKernelGGL((lr_combine<__bf16, float, false>), cgrid, dim3(256), lds, st, ca);
+  else hipLaunchKernelGGL((lr_combine<__bf16, __bf16, false>), cgrid, dim3(256), lds, st, ca);
   return hipGetLastError();
 }
 
