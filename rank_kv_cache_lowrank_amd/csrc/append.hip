@@ -929,82 +929,112 @@ constexpr int kFrontLds = kWinMfmaLds > kAppendLds ? (kWinMfmaLds > kWinValuLds 
 static_assert(kFrontLds >= kHeadsPad * kFoldD * 4, "the float32 fold's query tile fits");
 
 // ---------------------------------------------------------------------------------------------
-// Range planning of a decode call (one wave of the first launch; RangeArgs in fold.h). Integer
-// arithmetic only, the same on every run, and no workgroup barrier: lane l holds sequences l,
-// l + 64, ...; for each candidate Q the wave sums ceil(tiles_b / Q) with one DPP reduction; a
-// binary search finds the smallest Q whose total fits the grid. Prefixes and the sequence of
-// each workgroup come from broadcast LDS reads (no chain of dependent cross-lane steps).
+// Range planning of a decode call (one wave of the first launch; RangeArgs in fold.h). Exact
+// integer results, the same on every run, and no workgroup barrier: lane l loads sequences l,
+// l + 64, ... into LDS; the search for the smallest Q whose ranges fit the grid gives every lane
+// its own candidate per round (64 candidates spread over the interval, a ballot picks the first
+// that fits, so the interval shrinks 64-fold per round and no cross-lane reduction is chained).
+// Totals and prefixes come from broadcast LDS reads, 16 in flight at a time, and each lane
+// writes the table entries of its own sequences' ranges.
 // ---------------------------------------------------------------------------------------------
-constexpr int kPlanLds = 3 * kBalMaxSeqs * 4;
+constexpr int kPlanLds = 2 * kBalMaxSeqs * 4;
 static_assert(kFrontLds >= kPlanLds, "the range plan's tables fit");
+
+// ceil(t / q) for 0 <= t < 2^21, 1 <= q < 2^21: a float quotient (within one of the answer) and
+// one exact integer correction each way
+__device__ __forceinline__ int plan_cdiv(int t, int q, float rq) {
+  const int n = t + q - 1;
+  int k = (int)((float)n * rq);
+  k -= (k * q > n) ? 1 : 0;
+  k += ((k + 1) * q <= n) ? 1 : 0;
+  return k;
+}
+
+// f(k, tl[k]) for k < B in ascending order, every lane the same: 16-byte broadcast reads, 16 in
+// flight per round trip (tl is padded with zeros to a multiple of 64 entries)
+template <typename F>
+__device__ __forceinline__ void plan_scan(const int* tl, int B, F&& f) {
+  for (int k0 = 0; k0 < B; k0 += 64) {
+    int4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = *(const int4*)(tl + k0 + 4 * i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = k0 + 4 * i;
+      if (k < B) {
+        f(k, v[i].x);
+        f(k + 1, v[i].y);
+        f(k + 2, v[i].z);
+        f(k + 3, v[i].w);
+      }
+    }
+  }
+}
 
 __device__ void range_plan_body(const RangeArgs& r, unsigned char* smem) {
   if (threadIdx.x >= 64) return;
-  int* tl = (int*)smem;                  // [B] tiles of each sequence
-  int* pre = tl + kBalMaxSeqs;           // [B] first latent workgroup of each sequence
-  int* lens = pre + kBalMaxSeqs;         // [B] tokens attended
+  int* tl = (int*)smem;                  // [B padded to 64] tiles, then ranges, of each sequence
+  int* lens = tl + kBalMaxSeqs;          // [B] tokens attended
   const int lane = threadIdx.x, B = r.B;
+  const int Bp = (B + 63) & ~63;
   auto attended = [&](int b) {           // tokens the latent kernel attends for sequence b
     int L = r.step ? step_lens(r.lat_len[b], r.window > 0 ? r.win_len[b] : 0, r.window, r.t_cap).L_new
                    : r.lat_len[b];
     return L < 0 ? 0 : (L > r.max_len ? r.max_len : L);
   };
-  // sequence `lane` stays in registers (the common case B <= 64); the rest go through LDS
-  const int L0 = lane < B ? attended(lane) : 0;
-  const int t0 = (L0 + kTileTokens - 1) / kTileTokens;
-  int tmax = t0, tsum = t0;
-  tl[lane] = t0;
-  lens[lane] = L0;
-  for (int b = lane + 64; b < B; b += 64) {
-    const int L = attended(b);
-    const int t = (L + kTileTokens - 1) / kTileTokens;
+  // the loads of all of a lane's sequences go out together; tiles and tokens into LDS, zeros
+  // past B (a sequence with no tiles has no ranges)
+  for (int b = lane; b < Bp; b += 64) {
+    const int L = b < B ? attended(b) : 0;
     lens[b] = L;
-    tl[b] = t;
+    tl[b] = (L + kTileTokens - 1) / kTileTokens;
+  }
+  int tmax = 0, tsum = 0;
+  plan_scan(tl, B, [&](int, int t) {
     tmax = max(tmax, t);
     tsum += t;
-  }
-  tmax = __ockl_wfred_max_i32(tmax);
-  tsum = __ockl_wfred_add_i32(tsum);
+  });
   // the smallest Q in [lo, hi] with sum_b ceil(tiles_b / Q) <= nwg; at Q = tmax the sum is the
-  // number of non-empty sequences, at most B <= nwg
+  // number of non-empty sequences, at most B <= nwg, so the last lane's candidate always fits
+  // and the sum never increases with Q (tiles < 2^20: t_cap < 2^24)
   int lo = max(1, max((tmax + r.nslot - 1) / r.nslot, (tsum + r.nwg - 1) / r.nwg));
   int hi = max(1, tmax);
   if (lo > hi) lo = hi;
   while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    int c = (t0 + mid - 1) / mid;
-    for (int b = lane + 64; b < B; b += 64) c += (tl[b] + mid - 1) / mid;
-    c = __ockl_wfred_add_i32(c);
-    if (c <= r.nwg) hi = mid;
-    else lo = mid + 1;
+    const int step = (hi - lo + 64) / 64;
+    const int qc = min(lo + (lane + 1) * step - 1, hi);   // lane k covers [lo + k step, qc]
+    const float rq = __builtin_amdgcn_rcpf((float)qc);
+    int c = 0;
+    plan_scan(tl, B, [&](int, int t) { c += plan_cdiv(t, qc, rq); });
+    const unsigned long long fits = __ballot(c <= r.nwg);
+    const int k = __builtin_ctzll(fits);
+    hi = min(lo + (k + 1) * step - 1, hi);
+    lo = lo + k * step;
   }
   const int Q = lo;
-  // ranges per sequence into LDS (tl now holds them), then each lane's exclusive prefix from
-  // broadcast reads of all the sequences before it
-  tl[lane] = lane < B ? (t0 + Q - 1) / Q : 0;
-  for (int b = lane + 64; b < B; b += 64) tl[b] = (tl[b] + Q - 1) / Q;
-  for (int b = lane; b < B; b += 64) {
-    int p = 0;
-    for (int k = 0; k < b; ++k) p += tl[k];
-    pre[b] = p;
-    r.nrng[b] = tl[b];
-  }
-  int total = 0;
-  for (int k = 0; k < B; ++k) total += tl[k];
   const int qt = Q * kTileTokens;
-  for (int w = lane; w < r.nwg; w += 64) {
-    int e0 = -1, e1 = 0, e2 = 0, e3 = 0;
-    if (w < total) {
-      int b = 0;                         // the last sequence whose first workgroup is <= w
-      for (int k = 1; k < B; ++k) b = pre[k] <= w ? k : b;
-      const int s = w - pre[b];
-      e0 = b;
-      e1 = s;
-      e2 = s * qt;
-      e3 = min(e2 + qt, lens[b]);
+  // ranges per sequence (tl now holds them); each lane's sequences b = lane + 64 i take the
+  // workgroups from the exclusive prefix of the ranges before them
+  for (int b = lane; b < Bp; b += 64) tl[b] = (tl[b] + Q - 1) / Q;
+  int pre[kBalMaxSeqs / 64] = {0}, total = 0;
+  plan_scan(tl, B, [&](int k, int t) {
+#pragma unroll
+    for (int i = 0; i < kBalMaxSeqs / 64; ++i) pre[i] += k < lane + 64 * i ? t : 0;
+    total += t;
+  });
+#pragma unroll
+  for (int i = 0; i < kBalMaxSeqs / 64; ++i) {
+    const int b = lane + 64 * i;
+    if (b < B) {
+      const int n = tl[b], L = lens[b];
+      r.nrng[b] = n;
+      for (int s = 0; s < n; ++s) {
+        const int t0 = s * qt;
+        *(int4*)(r.table + 4 * (pre[i] + s)) = make_int4(b, s, t0, min(t0 + qt, L));
+      }
     }
-    *(int4*)(r.table + 4 * w) = make_int4(e0, e1, e2, e3);
   }
+  for (int w = total + lane; w < r.nwg; w += 64) *(int4*)(r.table + 4 * w) = make_int4(-1, 0, 0, 0);
 }
 
 // The first launch of a decode call: [range plan] [window, W > 0] [append (a decode step only)]
