@@ -61,7 +61,7 @@ constexpr int decode_tpi(int latent, int KS, int RB) {
 // Prefill latent kernel (bf16 latents): bound on the value blocks of 16 one wave accumulates
 // for both of its head blocks (0 = unsupported).
 inline int prefill_nv(int nrb) { return nrb <= 16 ? 16 : (nrb <= 24 ? 24 : (nrb <= 32 ? 32 : 0)); }
-constexpr int kPrefillTokensPerWg = 4;   // chunk tokens per prefill workgroup (one per wave)
+constexpr int kPrefillTokensPerWg = 4;   // chunk tokens per prefill workgroup
 // int4 latents: raw stages (16 rows of codes and scale/zero words, as stored) for the
 // direct-to-LDS loads; the value rows are dequantised into four fp16 stages of 16 value rows
 // (two iterations of two tiles), the key rows are read raw by the consumers.

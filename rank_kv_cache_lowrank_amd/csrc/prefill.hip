@@ -8,20 +8,22 @@
 // without a mask (the chunk's own rows and the window are exact keys, handled by the decode
 // kernel's exact-keys workgroups), so the latent part is a plain dense attention of the chunk's
 // C x 32 folded query rows against the latent rows. lr_prefill_latent gives each wave one chunk
-// token (its two 16-row head blocks of the folded query, padded from the query heads to 32)
-// for the whole latent range, so every latent byte brought into LDS feeds all of a workgroup's
-// four tokens, and every 16-byte operand read from LDS feeds two matrix-core products (one per
-// head block):
+// token's 16-row head blocks (one or both) of the folded query (heads padded from the query heads
+// to 32) for the whole latent range, so every latent byte brought into LDS feeds all of a
+// workgroup's four tokens and both head blocks:
 //
 //   S^T[16 tokens, 16 heads] = Zk qt^T           16x16x32 bf16, K = rank (A = latent rows)
 //   online softmax in base 2                      (reference max with slack, as in decode)
 //   A^T[16 rv, 16 heads] += Zv^T P^T              16x16x16 bf16, K = the tile's 16 tokens
 //
-// Workgroup = 4 waves, one per SIMD (the accumulators of two head blocks over the full value
-// rank need up to ~430 registers). All four waves load the LDS ring with 16-byte direct-to-LDS
-// loads (nontemporal), each wave waiting for exactly its own loads, one barrier per 16-token
-// tile. The partials (m, l, A) per (query token, token range) have the decode layout, so the
-// decode combine merges them with the exact-keys partials and up-projects.
+// Workgroup = 4 chunk tokens, as 8 waves of one (token, head block) each (two waves per SIMD: the
+// accumulators of one head block over the full value rank fit half the register file) or 4 waves
+// of one token with both head blocks (one wave per SIMD; ~430 registers), chosen by the length of
+// the token range (launch_prefill_latent). All waves load the LDS ring with 16-byte
+// direct-to-LDS loads, cached (the token groups of a range share its rows through L2), each wave
+// waiting for exactly its own loads, one barrier per 16-token tile. The partials (m, l, A) per
+// (query token, token range) have the decode layout, so the decode combine merges them with the
+// exact-keys partials and up-projects.
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
@@ -36,9 +38,18 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short pf_s16x4;
 
 constexpr float kPfMaxLead = 64.f;       // base-2 lead of a score over the reference max that
                                          // pass 0 tolerates (p <= 2^64: finite in bf16 and f32)
-constexpr int kPfThreads = 256;
-constexpr int kPfWaves = 4;
-constexpr int kPfMaxChunks = 5;          // 1 KB direct-to-LDS chunks per wave per matrix and tile
+constexpr int kPfTokens = 4;             // chunk tokens per workgroup
+// NHB = head blocks per wave: 2 (4 waves, one chunk token each) or 1 (8 waves, one (token, head
+// block) each); waves, threads and 1 KB direct-to-LDS chunks per wave per matrix and tile
+constexpr int pf_waves(int nhb) { return nhb == 2 ? 4 : 8; }
+constexpr int pf_threads(int nhb) { return 64 * pf_waves(nhb); }
+constexpr int pf_max_chunks(int nhb) { return nhb == 2 ? 5 : 3; }
+
+// 16 bytes per lane straight into LDS, cached: the token groups of a range read the same rows
+// through their XCD's L2
+__device__ __forceinline__ void pf_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, LR_LDS(lds_wave_base), 16, 0, 0);
+}
 
 // Value operand of the 16x16x16 product (A = Zv^T, K = token) through the gfx950 transpose
 // read: in each 16-lane group g, lane j's element e comes from the address of lane 16g + 4e +
@@ -67,9 +78,11 @@ struct PrefillArgs {
   int ntg, nunits, nst;      // token groups per sequence, units (sequence x range), ring stages
 };
 
-// KS: bound on K steps of 32 (nks <= KS); NV: bound on value blocks of 16 (nrb <= NV).
-template <int KS, int NV>
-__global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
+// KS: bound on K steps of 32 (nks <= KS); NV: bound on value blocks of 16 (nrb <= NV); NHB: head
+// blocks per wave.
+template <int KS, int NV, int NHB>
+__global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs a) {
+  constexpr int kPfWaves = pf_waves(NHB), kPfThreads = pf_threads(NHB), kPfMaxChunks = pf_max_chunks(NHB);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int SK = lds_stride_k(KS, 2);              // LDS row strides (bytes), as in decode
   constexpr int SV = lds_stride_v(NV / 2, 2);
@@ -88,7 +101,8 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
   const int b = u / a.nsplit, s = u - b * a.nsplit;
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 4, li = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tok = tg * kPfWaves + wave;                // chunk token of this wave
+  const int tok = tg * kPfTokens + (NHB == 2 ? wave : wave >> 1);   // chunk token of this wave
+  const int hb0 = NHB == 2 ? 0 : wave & 1;             // its first head block (heads 16 hb0 ..)
   const bool active = tok < a.C;                       // idle waves still load and meet barriers
   const int sq = b * a.C + tok;
 
@@ -167,12 +181,12 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
 #pragma unroll
     for (int k = 0; k < kPfMaxChunks; ++k) {
       const int c = wave + kPfWaves * k;
-      if (c < nck && offk[k] >= 0 && offk[k] < limk) dma16(srck + offk[k], stg + c * 1024);
+      if (c < nck && offk[k] >= 0 && offk[k] < limk) pf_dma16(srck + offk[k], stg + c * 1024);
     }
 #pragma unroll
     for (int k = 0; k < kPfMaxChunks; ++k) {
       const int c = wave + kPfWaves * k;
-      if (c < ncv && offv[k] >= 0 && offv[k] < limv) dma16(srcv + offv[k], stg + ZV + c * 1024);
+      if (c < ncv && offv[k] >= 0 && offv[k] < limv) pf_dma16(srcv + offv[k], stg + ZV + c * 1024);
     }
   };
 
@@ -203,17 +217,17 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
     }
   };
 
-  // ---- this wave's folded query (both head blocks) as B operands: lane (lg, li) holds head
-  // 16*hb + li, latent indices 32*ks + 8*lg .. +7
-  bf16x8 qop[2][KS];
+  // ---- this wave's folded query (its head blocks) as B operands: lane (lg, li) holds head
+  // 16*(hb0+h) + li, latent indices 32*ks + 8*lg .. +7
+  bf16x8 qop[NHB][KS];
   {
-    const __bf16* qrow = a.qt + ((size_t)(active ? sq : 0) * kHeadsPad + li) * a.rk_pad + lg * 8;
+    const __bf16* qrow = a.qt + ((size_t)(active ? sq : 0) * kHeadsPad + hb0 * 16 + li) * a.rk_pad + lg * 8;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int h = 0; h < NHB; ++h)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qop[hb][ks] = (active && ks < a.nks) ? *(const bf16x8*)(qrow + (size_t)hb * 16 * a.rk_pad + ks * 32)
-                                             : pf_zero8();
+        qop[h][ks] = (active && ks < a.nks) ? *(const bf16x8*)(qrow + (size_t)h * 16 * a.rk_pad + ks * 32)
+                                            : pf_zero8();
   }
   const int krow_off = li * SK + lg * 16;
   const int vrow_off = ZV + (4 * lg + (li >> 2)) * SV + (li & 3) * 8;
@@ -245,11 +259,12 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
       barrier_lds();
     }
   };
-  // raw score products of both head blocks for one tile: sacc[hb][i] = S^T[token 4*lg+i][head
-  // 16*hb+li] (waves without a token compute on a zero query)
-  auto products = [&](const unsigned char* stg, f32x4 (&sacc)[2]) {
+  // raw score products of this wave's head blocks for one tile: sacc[h][i] = S^T[token 4*lg+i]
+  // [head 16*(hb0+h)+li] (waves without a token compute on a zero query); with one head block,
+  // two accumulation chains (even and odd K steps)
+  auto products = [&](const unsigned char* stg, f32x4 (&sacc)[NHB]) {
     const unsigned char* krow = stg + krow_off;
-    sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 s2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks0 = 0; ks0 < KS; ks0 += 4) {
       bf16x8 av[4];
@@ -259,40 +274,53 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         if (ks0 + k < KS) {
-          sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qop[0][ks0 + k], sacc[0], 0, 0, 0);
-          sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qop[1][ks0 + k], sacc[1], 0, 0, 0);
+          if constexpr (NHB == 2) {
+            s2[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qop[0][ks0 + k], s2[0], 0, 0, 0);
+            s2[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qop[1][ks0 + k], s2[1], 0, 0, 0);
+          } else {
+            s2[k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qop[0][ks0 + k], s2[k & 1], 0, 0, 0);
+          }
         }
       }
+    }
+    if constexpr (NHB == 2) {
+      sacc[0] = s2[0];
+      sacc[1] = s2[1];
+    } else {
+      sacc[0] = s2[0] + s2[1];
     }
   };
   // masked base-2 scores from the raw products (rows past the range end -inf; NaN -> +inf so
   // that it survives the max and poisons only its head) and the tile's max per head
-  auto masked = [&](const f32x4 (&sacc)[2], int nvalid, float (&v)[2][4], float (&mx)[2]) {
+  auto masked = [&](const f32x4 (&sacc)[NHB], int nvalid, float (&v)[NHB][4], float (&mx)[NHB]) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int h = 0; h < NHB; ++h) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = sacc[hb][i];
-        v[hb][i] = (4 * lg + i < nvalid) ? ((x != x) ? INFINITY : x) : -INFINITY;
+        const float x = sacc[h][i];
+        v[h][i] = (4 * lg + i < nvalid) ? ((x != x) ? INFINITY : x) : -INFINITY;
       }
-      mx[hb] = wave_max_lg(fmaxf(fmaxf(v[hb][0], v[hb][1]), fmaxf(v[hb][2], v[hb][3])));
+      mx[h] = wave_max_lg(fmaxf(fmaxf(v[h][0], v[h][1]), fmaxf(v[h][2], v[h][3])));
     }
   };
-  auto scores = [&](const unsigned char* stg, int nvalid, float (&v)[2][4], float (&mx)[2]) {
-    f32x4 sacc[2];
+  auto scores = [&](const unsigned char* stg, int nvalid, float (&v)[NHB][4], float (&mx)[NHB]) {
+    f32x4 sacc[NHB];
     products(stg, sacc);
     masked(sacc, nvalid, v, mx);
   };
 
-  float mref[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  f32x4 acc[2][NV];
+  float mref[NHB], lsum[NHB];
+  f32x4 acc[NHB][NV];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
+  for (int h = 0; h < NHB; ++h) {
+    mref[h] = -INFINITY;
+    lsum[h] = 0.f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) acc[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NV; ++j) acc[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   bool bad = false;
-  auto finish = [&](const unsigned char* stg, int nvalid, const f32x4 (&sacc)[2]) {
-    float v[2][4], mx[2];
+  auto finish = [&](const unsigned char* stg, int nvalid, const f32x4 (&sacc)[NHB]) {
+    float v[NHB][4], mx[NHB];
     masked(sacc, nvalid, v, mx);
     // first value operands in flight under the softmax
     constexpr int VC = 8;
@@ -300,23 +328,23 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
     pf_bf16x4 vop[VC];
 #pragma unroll
     for (int k = 0; k < VC; ++k) vop[k] = pf_vread(vbase + k * 32);
-    pf_bf16x4 pb[2];
+    pf_bf16x4 pb[NHB];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int h = 0; h < NHB; ++h) {
       // a head without a reference yet takes this tile's max: its A and l are still 0
-      if (mref[hb] == -INFINITY) mref[hb] = mx[hb];
-      bad = bad || (mx[hb] > mref[hb] + kPfMaxLead);
-      const bool live = mref[hb] != -INFINITY;
+      if (mref[h] == -INFINITY) mref[h] = mx[h];
+      bad = bad || (mx[h] > mref[h] + kPfMaxLead);
+      const bool live = mref[h] != -INFINITY;
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __bf16 pv = (__bf16)(live ? fast_exp2(v[hb][i] - mref[hb]) : 0.f);
-        pb[hb][i] = pv;
+        const __bf16 pv = (__bf16)(live ? fast_exp2(v[h][i] - mref[h]) : 0.f);
+        pb[h][i] = pv;
         ps += (float)pv;
       }
-      lsum[hb] += ps;
+      lsum[h] += ps;
     }
-    // values: A^T[rv][head li] of both head blocks, one operand read per block
+    // values: A^T[rv][head li] of the wave's head blocks, one operand read per block
 #pragma unroll
     for (int j0 = 0; j0 < NV; j0 += VC) {
       if (j0 > 0) {
@@ -325,12 +353,11 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
           if (j0 + k < NV) vop[k] = pf_vread(vbase + (j0 + k) * 32);
       }
 #pragma unroll
-      for (int k = 0; k < VC; ++k) {
-        if (j0 + k < NV) {
-          acc[0][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[k], pb[0], acc[0][j0 + k], 0, 0, 0);
-          acc[1][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[k], pb[1], acc[1][j0 + k], 0, 0, 0);
-        }
-      }
+      for (int k = 0; k < VC; ++k)
+        if (j0 + k < NV)
+#pragma unroll
+          for (int h = 0; h < NHB; ++h)
+            acc[h][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[k], pb[h], acc[h][j0 + k], 0, 0, 0);
     }
   };
 
@@ -345,7 +372,7 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
     wait_vmcnt(count(0, pro - 1));                     // tile 0 landed (this wave's part)
     if (ntiles > 0) fix_tail(0);
     barrier_lds();
-    f32x4 cur[2];
+    f32x4 cur[NHB];
     if (ntiles > 0) products(smem, cur);
     for (int it = 0; it < ntiles; ++it) {
       if (it + 1 < ntiles) {
@@ -354,15 +381,15 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
       }
       barrier_lds();
       if (it + NST - 1 < ntiles) issue(it + NST - 1);
-      f32x4 nxt[2];
+      f32x4 nxt[NHB];
       products(smem + ((it + 1) % NST) * STAGE, nxt);   // (last iteration: a stale stage, unused)
       finish(smem + (it % NST) * STAGE, min(kTileTokens, t_end - t_begin - it * kTileTokens), cur);
-      cur[0] = nxt[0];
-      cur[1] = nxt[1];
-      // interleave the next tile's score products with this tile's softmax: one matrix-core
-      // instruction, then three vector ALU instructions, 24 times
 #pragma unroll
-      for (int k = 0; k < 24; ++k) {
+      for (int h = 0; h < NHB; ++h) cur[h] = nxt[h];
+      // interleave the next tile's score products with this tile's softmax: one matrix-core
+      // instruction, then three vector ALU instructions, once per score product
+#pragma unroll
+      for (int k = 0; k < NHB * KS; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
@@ -375,19 +402,21 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) *flag = 1;
   barrier_lds();
   if (*flag != 0) {
-    float mexact[2] = {-INFINITY, -INFINITY};
+    float mexact[NHB];
+#pragma unroll
+    for (int h = 0; h < NHB; ++h) mexact[h] = -INFINITY;
     stream([&](const unsigned char* stg, int nvalid) {   // pass 1
-      float v[2][4], mx[2];
+      float v[NHB][4], mx[NHB];
       scores(stg, nvalid, v, mx);
-      mexact[0] = fmaxf(mexact[0], mx[0]);
-      mexact[1] = fmaxf(mexact[1], mx[1]);
+#pragma unroll
+      for (int h = 0; h < NHB; ++h) mexact[h] = fmaxf(mexact[h], mx[h]);
     });
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      mref[hb] = mexact[hb];
-      lsum[hb] = 0.f;
+    for (int h = 0; h < NHB; ++h) {
+      mref[h] = mexact[h];
+      lsum[h] = 0.f;
 #pragma unroll
-      for (int j = 0; j < NV; ++j) acc[hb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NV; ++j) acc[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     stream_full();                                     // pass 2
   }
@@ -395,17 +424,17 @@ __global__ __launch_bounds__(kPfThreads) void lr_prefill_latent(PrefillArgs a) {
   if (!active) return;
   const size_t pidx = (size_t)sq * a.nsplit + s;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const float l = wave_sum_lg(lsum[hb]);
-    const int head = hb * 16 + li;
+  for (int h = 0; h < NHB; ++h) {
+    const float l = wave_sum_lg(lsum[h]);
+    const int head = (hb0 + h) * 16 + li;
     if (head >= a.Hq) continue;
     if (lg == 0) {
-      a.part_ml[(pidx * a.Hq + head) * 2] = mref[hb];
+      a.part_ml[(pidx * a.Hq + head) * 2] = mref[h];
       a.part_ml[(pidx * a.Hq + head) * 2 + 1] = l;
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-      if (j < a.nrb) *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + j * 16 + 4 * lg) = acc[hb][j];
+      if (j < a.nrb) *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + j * 16 + 4 * lg) = acc[h][j];
   }
 }
 
@@ -842,7 +871,7 @@ hipError_t launch_prefill_combine(const DecodePlan& p, const lr_layer_cache* c, 
   return hipGetLastError();
 }
 
-template <int KS, int NV>
+template <int KS, int NV, int NHB>
 static hipError_t launch_pf(const PrefillArgs& args, int grid, int lds, hipStream_t st, hipEvent_t ev_begin,
                             hipEvent_t ev_end) {
   static bool attr_set[64] = {false};
@@ -850,18 +879,25 @@ static hipError_t launch_pf(const PrefillArgs& args, int grid, int lds, hipStrea
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    e = hipFuncSetAttribute((const void*)lr_prefill_latent<KS, NV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void*)lr_prefill_latent<KS, NV, NHB>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
   if (ev_begin || ev_end)
-    hipExtLaunchKernelGGL((lr_prefill_latent<KS, NV>), dim3(grid), dim3(kPfThreads), lds, st, ev_begin, ev_end, 0,
-                          args);
+    hipExtLaunchKernelGGL((lr_prefill_latent<KS, NV, NHB>), dim3(grid), dim3(pf_threads(NHB)), lds, st, ev_begin,
+                          ev_end, 0, args);
   else
-    hipLaunchKernelGGL((lr_prefill_latent<KS, NV>), dim3(grid), dim3(kPfThreads), lds, st, args);
+    hipLaunchKernelGGL((lr_prefill_latent<KS, NV, NHB>), dim3(grid), dim3(pf_threads(NHB)), lds, st, args);
   return hipGetLastError();
 }
+
+// Head blocks per wave of the latent kernel. Measured over whole prefill calls at B = 16: token
+// ranges of up to 4096 tokens run faster with one head block per wave (eight waves; T = 4K: 302
+// against 334 us at rank 358 and C = 32, 227 against 252 us at rank 256), longer ranges with two
+// (four waves; T = 32K, rank 256, C = 16: 790 against 841 us; T = 16K, rank 512, C = 32: 1086
+// against 1251 us).
+static int pf_heads_per_wave(const DecodePlan& p) { return p.split_tokens <= 4096 ? 1 : 2; }
 
 hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, const __bf16* qt, float* part_ml,
                                  float* part_acc, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
@@ -892,8 +928,11 @@ hipError_t launch_prefill_latent(const DecodePlan& p, const lr_layer_cache* c, c
   a.nst = p.pf_nst;
   const int grid = ((a.nunits + 7) / 8) * 8 * a.ntg;
   const int ks = decode_ks(p.nks), nv = prefill_nv(p.nrb);
-#define LR_CASE(K, V) \
-  if (ks == K && nv == V) return launch_pf<K, V>(a, grid, p.pf_lds, st, ev_begin, ev_end);
+  const int nhb = pf_heads_per_wave(p);
+#define LR_CASE(K, V)                                                                          \
+  if (ks == K && nv == V)                                                                      \
+    return nhb == 2 ? launch_pf<K, V, 2>(a, grid, p.pf_lds, st, ev_begin, ev_end)              \
+                    : launch_pf<K, V, 1>(a, grid, p.pf_lds, st, ev_begin, ev_end);
   LR_CASE(8, 16) LR_CASE(8, 24) LR_CASE(8, 32)
   LR_CASE(12, 16) LR_CASE(12, 24) LR_CASE(12, 32)
   LR_CASE(16, 16) LR_CASE(16, 24) LR_CASE(16, 32)
