@@ -209,7 +209,9 @@ int lowrank_attn_prefill(const lr_model_desc* model, int32_t layer, const lr_lay
  *   as described above).
  * W > 0: tokens enter the window ring; whenever the window is full the oldest window token
  *   (absolute position lat_len[b]) is projected and stored as latent row lat_len[b], and
- *   lat_len[b] grows by one. Requires n_new <= W.
+ *   lat_len[b] grows by one. The result is that of appending the tokens one at a time, for any
+ *   n_new: a call of more than W tokens leaves only its last W in the window, and the ones
+ *   before them go to the latent rows after the window tokens they push out.
  * Requires lat_len[b] + (number of new latent rows) <= t_cap (clamped otherwise: rows past
  * t_cap are dropped and lengths stop at t_cap).
  * n_new == 1 is one launch: while it runs, bits 24..30 of each lat_len word count the workgroups

@@ -410,7 +410,6 @@ int lowrank_kv_append(const lr_model_desc* model, int32_t layer, const lr_layer_
   int st = plan_append(model, layer, cache, batch, &p, &msg);
   if (st != LR_OK) return fail(st, msg);
   if (n_new < 0) return fail(LR_EINVAL, "n_new must be >= 0");
-  if (model->window > 0 && n_new > model->window) return fail(LR_EINVAL, "n_new must be <= window");
   if (n_new > 0 && (!k_new || !v_new)) return fail(LR_EINVAL, "k_new/v_new must not be NULL");
   if (!cache->pk || !cache->pv) return fail(LR_EINVAL, "append needs the down-projections pk/pv");
   if (!aligned(cache->pk, 16) || !aligned(cache->pv, 16)) return fail(LR_EINVAL, "pk/pv must be 16-byte aligned");

@@ -396,11 +396,14 @@ __global__ __launch_bounds__(256) void lr_append(AppendArgs a, int nck, int ncv)
 //   lr_append_rows    one matrix-core product over the flattened rows f = b * n_new + e of the
 //                     call: workgroup (x, y) owns latent columns 32c .. 32c + 31 of K or V (as
 //                     above) for rows 16y .. 16y + 15, whatever sequences they belong to. Row
-//                     (b, e) is the new token e (W == 0) or the evicted window slot (L + e) mod W
-//                     (W > 0, e < rows_b); it is stored as latent row L + e. The lengths and the
-//                     ring are only read.
-//   lr_append_finish  one workgroup per sequence, after every read: the new tokens into the ring
-//                     (slots (L + wl + t) mod W) and the lengths after the call.
+//                     (b, e) is the e-th token of the stream to leave for the latents: the new
+//                     token e (W == 0); with a window, the window token in slot (L + e) mod W
+//                     while e < wl, after them (a call of more than W tokens) new token e - wl,
+//                     for e < rows_b = wl + n_new - W. It is stored as latent row L + e. The
+//                     lengths and the ring are only read.
+//   lr_append_finish  one workgroup per sequence, after every read: the last min(n_new, W) new
+//                     tokens into the ring (token t in slot (L + wl + t) mod W) and the lengths
+//                     after the call.
 // The same arithmetic per row as the one-launch path (the same K halves, chains and rounding), so
 // the stored rows do not depend on which path stored them.
 // ---------------------------------------------------------------------------------------------
@@ -427,12 +430,13 @@ __global__ __launch_bounds__(256) void lr_append_rows(AppendArgs a, int nck, int
   const int ld = kv == 0 ? a.ld_k : a.ld_v;
   const int rb = row_bytes_of(a.latent, r, ld);
   const int G = (r + kGroup - 1) / kGroup;
-  // (L, rows) of flattened row f's sequence, and whether the row exists (e < rows)
-  auto row_info = [&](long long f, int& b, int& e, int& L, bool& live) {
+  // (L, wl, rows) of flattened row f's sequence, and whether the row exists (e < rows)
+  auto row_info = [&](long long f, int& b, int& e, int& L, int& wl, bool& live) {
     live = false;
     b = 0;
     e = 0;
     L = 0;
+    wl = 0;
     if (f >= nrows) return;
     b = (int)(f / n_new);
     e = (int)(f - (long long)b * n_new);
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(256) void lr_append_rows(AppendArgs a, int nck, int
     int rows = n_new;
     if (W > 0) {
       const int raw = a.win_len[b];
-      const int wl = raw < 0 ? 0 : (raw > W ? W : raw);
+      wl = raw < 0 ? 0 : (raw > W ? W : raw);
       rows = wl + n_new - W;
     }
     live = e < rows;
@@ -454,12 +458,12 @@ __global__ __launch_bounds__(256) void lr_append_rows(AppendArgs a, int nck, int
     const int kw = min(kAppendK, D - kc);                      // a multiple of 128
     // lengths of the rows this thread stages first, then P (its loads stay in flight while the
     // lengths give the evicted slots' addresses), then the source rows
-    int xb[4], xe[4], xL[4];
+    int xb[4], xe[4], xL[4], xw[4];
     bool xlive[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int sq = (tid + 256 * u) / (kw / 8);
-      row_info(sq < kAppendSeqs ? f0 + sq : nrows, xb[u], xe[u], xL[u], xlive[u]);
+      row_info(sq < kAppendSeqs ? f0 + sq : nrows, xb[u], xe[u], xL[u], xw[u], xlive[u]);
     }
     if constexpr (!F32P) {
       const int nks = kw / 64, k0 = kc + kh * (kw / 2);
@@ -476,8 +480,9 @@ __global__ __launch_bounds__(256) void lr_append_rows(AppendArgs a, int nck, int
       const int c = i - (i / (kw / 8)) * (kw / 8);
       xv[u] = u32x4{0u, 0u, 0u, 0u};
       if (xlive[u]) {
-        const __bf16* src = W == 0 ? xnew + ((size_t)xb[u] * n_new + xe[u]) * D
-                                   : win + ((size_t)xb[u] * W + (xL[u] + xe[u]) % W) * D;
+        const bool from_ring = W > 0 && xe[u] < xw[u];
+        const __bf16* src = from_ring ? win + ((size_t)xb[u] * W + (xL[u] + xe[u]) % W) * D
+                                      : xnew + ((size_t)xb[u] * n_new + (xe[u] - xw[u])) * D;
         xv[u] = *(const u32x4*)(src + kc + c * 8);
       }
     }
@@ -527,9 +532,9 @@ __global__ __launch_bounds__(256) void lr_append_rows(AppendArgs a, int nck, int
   for (int p2 = 0; p2 < 2; ++p2) {
     const int sq = 4 * wave + 2 * p2 + (lane >> 5);
     const int cl = lane & 31;
-    int b, e, L;
+    int b, e, L, wl;
     bool live;
-    row_info(f0 + sq, b, e, L, live);
+    row_info(f0 + sq, b, e, L, wl, live);
     if (live) {                                                // uniform over each 32-lane half
       const float z = zt[0][sq][cl] + zt[1][sq][cl];
       const long long row = (long long)L + e;
@@ -554,9 +559,11 @@ __global__ __launch_bounds__(256) void lr_append_finish(AppendArgs a) {
     wl = raw < 0 ? 0 : (raw > W ? W : raw);
     rows = wl + n_new - W;
     rows = rows < 0 ? 0 : rows;
+    // only the last W tokens stay exact (each slot is written once: no two threads race on it)
+    const int t0 = n_new > W ? n_new - W : 0;
     const int vec = D / 8;
-    for (int i = tid; i < n_new * vec; i += 256) {
-      const int t = i / vec, c = i - t * vec;
+    for (int i = tid; i < (n_new - t0) * vec; i += 256) {
+      const int t = t0 + i / vec, c = i - (i / vec) * vec;
       const size_t dst = ((size_t)b * W + (L + wl + t) % W) * D + c * 8;
       const size_t src = ((size_t)b * n_new + t) * D + c * 8;
       *(u32x4*)(a.kwin + dst) = *(const u32x4*)(a.k_new + src);

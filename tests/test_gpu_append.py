@@ -206,10 +206,12 @@ def test_append_pseudo_inverse_projection_config3_shape():
         assert np.all(np.abs(ref.astype(np.float64) - z64) <= OQ.error_bound(s16, z16, r) + bound)
 
 
-@pytest.mark.parametrize("n_calls", [[1] * 11, [3, 3, 2, 5], [8, 8, 1]])
+@pytest.mark.parametrize("n_calls", [[1] * 11, [3, 3, 2, 5], [8, 8, 1], [11], [3, 20, 2], [2, 9, 30, 1]])
 def test_window_ring_matches_token_stream(n_calls):
     """Appends through an exact window W=8 from an empty sequence: window slots, lengths and the
-    evicted latent rows (P = I, bf16 storage: exact) equal the oracle's token-list model."""
+    evicted latent rows (P = I, bf16 storage: exact) equal the oracle's token-list model, also
+    for calls of more than W tokens (the call's early tokens go to the latents after the window
+    tokens they push out)."""
     B, D, W = 2, 512, 8
     rng = np.random.default_rng(sum(n_calls))
     eye = np.eye(D)
@@ -292,16 +294,18 @@ def test_append_bf16_general_projection():
         assert_rows_untouched(full, B, t_cap, written)
 
 
+@pytest.mark.parametrize("calls", [(1, 3, 2, 1, 3, 1), (2, 13, 4)])
 @pytest.mark.parametrize("latent", ["bf16", "i4g32"])
-def test_window_eviction_general_projection(latent):
-    """An exact window W = 8 fed an 11-token stream in calls of 1-3 tokens, with a general
-    pseudo-inverse P: window slots and lengths equal the oracle's token-list model; each evicted
-    token's z (z_debug of the call that evicted it) lies within the float32 accumulation bound of
-    the oracle's x_old P; the stored row is that z's storage form (bf16 rounding, or the int4
-    codes / scale / zero), bit for bit; no other latent row and nothing past t_cap changes."""
+def test_window_eviction_general_projection(latent, calls):
+    """An exact window W = 8 fed a token stream in calls of 1-3 tokens, or with one call longer
+    than the window, with a general pseudo-inverse P: window slots and lengths equal the oracle's
+    token-list model; each evicted token's z (z_debug of the call that evicted it) lies within the
+    float32 accumulation bound of the oracle's x_old P; the stored row is that z's storage form
+    (bf16 rounding, or the int4 codes / scale / zero), bit for bit; no other latent row and
+    nothing past t_cap changes."""
     cfg = synth.CONFIGS[1]
-    B, D, W, r, t_cap = 3, 512, 8, 200, 8
-    calls = (1, 3, 2, 1, 3, 1)
+    B, D, W, r = 3, 512, 8, 200
+    t_cap = max(8, sum(calls) - W)
     Pk, Pv = _pinv_bf16(cfg, "k", r), _pinv_bf16(cfg, "v", r)
     dt = torch.bfloat16
     pk = synth.projection_storage(Pk, dt).to(DEV)
@@ -335,7 +339,7 @@ def test_window_eviction_general_projection(latent):
     written = set()
     for b in range(B):
         st = states[b]
-        assert st.lat_len == 3 and st.win_len == W          # 11 tokens: 3 evicted, 8 in the window
+        assert st.lat_len == sum(calls) - W and st.win_len == W   # the oldest evicted, W in the window
         assert lat[b] == st.lat_len and win[b] == st.win_len
         for i in range(st.win_len):
             slot = (st.lat_len + i) % W
