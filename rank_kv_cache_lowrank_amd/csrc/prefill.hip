@@ -160,11 +160,34 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
     if (hi <= lo) return 0;
     return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
   };
-  auto issue = [&](int t) {
-    unsigned char* stg = smem + (t % NST) * STAGE;
+  // whether this lane loads 16 bytes of chunk k of a full tile (16 rows), and whether they are the
+  // key granule holding latent index rk: fixed for the whole range, so a full tile's loads test
+  // one precomputed lane flag each (the partial last tile takes the general conditions)
+  const int nck16 = nchunks(kTileTokens, SK, a.copy_k), ncv16 = nchunks(kTileTokens, SV, a.copy_v);
+  bool fk[kPfMaxChunks], fv[kPfMaxChunks], ft[kPfMaxChunks];
+#pragma unroll
+  for (int k = 0; k < kPfMaxChunks; ++k) {
+    const int c = wave + kPfWaves * k;
+    fk[k] = c < nck16 && offk[k] >= 0 && offk[k] < kTileTokens * a.row_bytes_k;
+    fv[k] = c < ncv16 && offv[k] >= 0 && offv[k] < kTileTokens * a.row_bytes_v;
+    ft[k] = fk[k] && (c * 1024 + lane * 16) % SK == a.copy_k - 16;
+  }
+  // tile t into stage stg (the callers track stages incrementally)
+  auto issue = [&](int t, unsigned char* stg) {
     const int t0 = t * kTileTokens;
     const int rows = min(kTileTokens, t_end - t_begin - t0);
-    if (rows < kTileTokens) {
+    const unsigned char* srck = gk + (size_t)t0 * a.row_bytes_k;
+    const unsigned char* srcv = gv + (size_t)t0 * a.row_bytes_v;
+    if (rows == kTileTokens) {
+#pragma unroll
+      for (int k = 0; k < kPfMaxChunks; ++k)
+        if (fk[k]) pf_dma16(srck + offk[k], stg + (wave + kPfWaves * k) * 1024);
+#pragma unroll
+      for (int k = 0; k < kPfMaxChunks; ++k)
+        if (fv[k]) pf_dma16(srcv + offv[k], stg + ZV + (wave + kPfWaves * k) * 1024);
+      return;
+    }
+    {
       // the stage's value rows past the range end still hold an older tile (possibly NaN
       // patterns): zero them, so that P = 0 meets 0 there (plain LDS stores, published by the
       // barrier that precedes the tile's use)
@@ -174,8 +197,6 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
         *(u32x4*)(stg + ZV + row * SV + col) = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    const unsigned char* srck = gk + (size_t)t0 * a.row_bytes_k;
-    const unsigned char* srcv = gv + (size_t)t0 * a.row_bytes_v;
     const int nck = nchunks(rows, SK, a.copy_k), ncv = nchunks(rows, SV, a.copy_v);
     const int limk = rows * a.row_bytes_k, limv = rows * a.row_bytes_v;
 #pragma unroll
@@ -201,10 +222,19 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
     gmask[i] = (2 * i < e ? 0x0000FFFFu : 0u) | (2 * i + 1 < e ? 0xFFFF0000u : 0u);
   }
   const bool ktail = (a.rk & 7) != 0;
-  auto fix_tail = [&](int t) {
+  auto fix_tail = [&](int t, unsigned char* stg) {
     if (!ktail) return;
-    unsigned char* stg = smem + (t % NST) * STAGE;
     const int rows = min(kTileTokens, t_end - t_begin - t * kTileTokens);
+    if (rows == kTileTokens) {
+#pragma unroll
+      for (int k = 0; k < kPfMaxChunks; ++k) {
+        if (ft[k]) {
+          u32x4* p = (u32x4*)(stg + (wave + kPfWaves * k) * 1024 + lane * 16);
+          *p = *p & gmask;
+        }
+      }
+      return;
+    }
     const int nck = nchunks(rows, SK, a.copy_k), limk = rows * a.row_bytes_k;
 #pragma unroll
     for (int k = 0; k < kPfMaxChunks; ++k) {
@@ -244,18 +274,24 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
 
   // streams the range's tiles through the ring, calling body(stage, valid rows) per tile (the
   // exact-max pass; the full passes use the pipelined stream_full below)
+  // stage of the tile after the one in stage p
+  auto next_stage = [&](unsigned char* p) { return p + STAGE == smem + NST * STAGE ? smem : p + STAGE; };
   auto stream = [&](auto&& body) {
     const int pro = min(NST - 1, ntiles);
-    for (int t = 0; t < pro; ++t) issue(t);
+    for (int t = 0; t < pro; ++t) issue(t, smem + t * STAGE);
     wait_vmcnt(count(0, pro - 1));                     // tile 0 landed (this wave's part)
-    if (ntiles > 0) fix_tail(0);
+    if (ntiles > 0) fix_tail(0, smem);
     barrier_lds();
+    unsigned char* s_cur = smem;                       // stage of tile it
+    unsigned char* s_iss = smem + (NST - 1) * STAGE;   // stage of tile it + NST - 1
     for (int it = 0; it < ntiles; ++it) {
       // stage of tile it - 1: every wave finished reading it before the last barrier
-      if (it + NST - 1 < ntiles) issue(it + NST - 1);
-      body(smem + (it % NST) * STAGE, min(kTileTokens, t_end - t_begin - it * kTileTokens));
+      if (it + NST - 1 < ntiles) issue(it + NST - 1, s_iss);
+      body(s_cur, min(kTileTokens, t_end - t_begin - it * kTileTokens));
       wait_vmcnt(count(it + 1, min(it + NST - 1, ntiles - 1)));   // tile it + 1 landed
-      if (it + 1 < ntiles) fix_tail(it + 1);
+      s_cur = next_stage(s_cur);
+      s_iss = next_stage(s_iss);
+      if (it + 1 < ntiles) fix_tail(it + 1, s_cur);
       barrier_lds();
     }
   };
@@ -368,22 +404,28 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
   // Tiles it - 1, it and it + 1 occupy distinct stages (at least 3).
   auto stream_full = [&]() {
     const int pro = min(NST - 1, ntiles);
-    for (int t = 0; t < pro; ++t) issue(t);
+    for (int t = 0; t < pro; ++t) issue(t, smem + t * STAGE);
     wait_vmcnt(count(0, pro - 1));                     // tile 0 landed (this wave's part)
-    if (ntiles > 0) fix_tail(0);
+    if (ntiles > 0) fix_tail(0, smem);
     barrier_lds();
+    unsigned char* s_cur = smem;                       // stage of tile it
+    unsigned char* s_nxt = next_stage(smem);           // stage of tile it + 1
+    unsigned char* s_iss = smem + (NST - 1) * STAGE;   // stage of tile it + NST - 1
     f32x4 cur[NHB];
     if (ntiles > 0) products(smem, cur);
     for (int it = 0; it < ntiles; ++it) {
       if (it + 1 < ntiles) {
         wait_vmcnt(count(it + 1, min(it + NST - 2, ntiles - 1)));   // tile it + 1 landed
-        fix_tail(it + 1);
+        fix_tail(it + 1, s_nxt);
       }
       barrier_lds();
-      if (it + NST - 1 < ntiles) issue(it + NST - 1);
+      if (it + NST - 1 < ntiles) issue(it + NST - 1, s_iss);
       f32x4 nxt[NHB];
-      products(smem + ((it + 1) % NST) * STAGE, nxt);   // (last iteration: a stale stage, unused)
-      finish(smem + (it % NST) * STAGE, min(kTileTokens, t_end - t_begin - it * kTileTokens), cur);
+      products(s_nxt, nxt);                            // (last iteration: a stale stage, unused)
+      finish(s_cur, min(kTileTokens, t_end - t_begin - it * kTileTokens), cur);
+      s_cur = s_nxt;
+      s_nxt = next_stage(s_nxt);
+      s_iss = next_stage(s_iss);
 #pragma unroll
       for (int h = 0; h < NHB; ++h) cur[h] = nxt[h];
       // interleave the next tile's score products with this tile's softmax: one matrix-core
