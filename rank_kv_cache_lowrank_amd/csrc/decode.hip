@@ -406,12 +406,22 @@ __device__ __forceinline__ void i4_loader(const DecodeArgs& a, unsigned char* sm
     if (hi <= lo) return 0;
     return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
   };
+  // whether this lane copies 16 bytes of copy u of a full tile (16 rows), computed once
+  bool fu[kI4ChunksPerWave];
+#pragma unroll
+  for (int u = 0; u < kI4ChunksPerWave; ++u) fu[u] = u < nchw && c_start[u] + lane * 16 < kTileTokens * c_rb[u];
   int issue_stage = 0;                   // raw stage of the next tile issued (tiles go in order)
   auto issue = [&](int t) {
     unsigned char* st = raw + issue_stage * R.rs;
     issue_stage = issue_stage + 1 == NR ? 0 : issue_stage + 1;
     const int t0 = t * kTileTokens;
     const int rows = min(kTileTokens, t_end - t_begin - t0);
+    if (rows == kTileTokens) {
+#pragma unroll
+      for (int u = 0; u < kI4ChunksPerWave; ++u)
+        if (fu[u]) dma16(c_src[u] + (size_t)t0 * c_rb[u] + c_start[u] + lane * 16, st + c_dst[u]);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kI4ChunksPerWave; ++u) {
       const int lim = rows * c_rb[u];
@@ -616,12 +626,32 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
       if (hi <= lo) return 0;
       return (hi - lo) * cnt_full + (hi == ntiles - 1 ? cnt_last - cnt_full : 0);
     };
+    // whether this lane copies 16 bytes of chunk u of a full tile (16 rows): fixed for the range,
+    // so a full tile's loads test one precomputed lane flag each (the general per-lane
+    // conditions cost a compare chain and an exec-mask round trip per load)
+    const int nck16 = nchunks(kTileTokens, SK, a.copy_k), ncv16 = nchunks(kTileTokens, SV, a.copy_v);
+    bool fk[kMaxChunkPerProducer], fv[kMaxChunkPerProducer];
+#pragma unroll
+    for (int u = 0; u < kMaxChunkPerProducer; ++u) {
+      const int c = pw + kProducers * u;
+      fk[u] = c < nck16 && offk[u] >= 0 && offk[u] < kTileTokens * a.row_bytes_k;
+      fv[u] = c < ncv16 && offv[u] >= 0 && offv[u] < kTileTokens * a.row_bytes_v;
+    }
     auto issue = [&](int t) {
       unsigned char* stg = ring + (t % NST) * STAGE;
       const int t0 = t * kTileTokens;
       const int rows = min(kTileTokens, t_end - t_begin - t0);
       const unsigned char* srck = gk + (size_t)t0 * a.row_bytes_k;
       const unsigned char* srcv = gv + (size_t)t0 * a.row_bytes_v;
+      if (rows == kTileTokens) {
+#pragma unroll
+        for (int u = 0; u < kMaxChunkPerProducer; ++u)
+          if (fk[u]) dma16(srck + offk[u], stg + (pw + kProducers * u) * 1024);
+#pragma unroll
+        for (int u = 0; u < kMaxChunkPerProducer; ++u)
+          if (fv[u]) dma16(srcv + offv[u], stg + ZV + (pw + kProducers * u) * 1024);
+        return;
+      }
       const int nck = nchunks(rows, SK, a.copy_k);
       const int ncv = nchunks(rows, SV, a.copy_v);
       const int limk = rows * a.row_bytes_k, limv = rows * a.row_bytes_v;
