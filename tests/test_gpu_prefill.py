@@ -173,13 +173,16 @@ def test_prefill_long_chunk_and_full_window():
 
 
 @pytest.mark.parametrize("first_tile_score", [-40.0, -100.0])
-def test_prefill_low_first_tile(first_tile_score):
+@pytest.mark.parametrize("long_ranges", [False, True])
+def test_prefill_low_first_tile(first_tile_score, long_ranges):
     """The first 16 latent rows of sequences 0 and 1 are set to one row z solving q~ . z = target
     (base-2 score units) for every chunk token and head at once (least norm; 168 equations in 358
     unknowns). The later tiles then lead the first tile's max by about -target: -40 stays on the
     single pass (p up to 2^40), -100 sends the workgroups through the exact-max passes. The later
-    scores are unchanged, so the softmax stays as well conditioned as the plain case."""
-    cfg, li = small("bf16", 358, L=(300, 64, 17))
+    scores are unchanged, so the softmax stays as well conditioned as the plain case. With
+    long_ranges, one range per sequence of more than 4096 tokens: the layout with both head blocks
+    in one wave."""
+    cfg, li = small("bf16", 358, L=(4500, 4200, 17) if long_ranges else (300, 64, 17))
     C = 6
     q, k, v = chunk_inputs(cfg, C, rank=358)
     qn = q.float().cpu().numpy()
@@ -191,9 +194,23 @@ def test_prefill_low_first_tile(first_tile_score):
         z = np.linalg.lstsq(qt, np.full(qt.shape[0], first_tile_score / to_base2), rcond=None)[0]
         li.zk[b, :16, :358] = torch.from_numpy(np.tile(z, (16, 1))).to(li.zk.dtype)
     model, cache = device_layer(li)
-    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()))
+    out = run_prefill(model, cache, q, k, v, int(li.lat_len.max()), nsplit=1 if long_ranges else 0)
     assert np.isfinite(out).all()
     assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("rank,C", [(358, 5), (256, 9), (512, 2)])
+def test_prefill_long_ranges(rank, C):
+    """Token ranges of more than 4096 tokens (one per sequence) take the latent kernel's layout
+    with both head blocks in one wave, short ranges the one with a head block per wave: both
+    against the oracle."""
+    cfg, li = small("bf16", rank, B=2, L=(5000, 4200))
+    q, k, v = chunk_inputs(cfg, C, rank=rank)
+    model, cache = device_layer(li)
+    ref = oracle(li, q, k, v)
+    for nsplit in (1, 8):                   # 5000-token ranges, then 625-token ranges
+        out = run_prefill(model, cache, q, k, v, 5000, nsplit=nsplit)
+        assert rel_err(out, ref) < TOL["bf16"], nsplit
 
 
 @pytest.mark.parametrize("rank", [358, 100])
