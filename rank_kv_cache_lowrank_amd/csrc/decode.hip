@@ -867,7 +867,10 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
 
         // ---- value operands: read in chunks of VC blocks; the first chunk's reads are issued
         // before the softmax so that its LDS latency hides under it
-        constexpr int VC = NVB < 8 ? NVB : 8;
+        // (6 for more than 16 blocks: with 8, the rank-358 bf16 wave needed 256 registers and
+        // spilled q operands; their reloads from scratch queue behind the producers' loads in the
+        // compute unit's memory pipeline)
+        constexpr int VC = NVB < 8 ? NVB : (NVB > 16 ? 6 : 8);
         const unsigned char* vbase = stg + vrow_off;
         auto vread = [&](int j) -> bf16x4 {
           if constexpr (LT == LT_F32) return v_operand4<LT, SV>(vbase, j * (SP ? 16 : 32) * ES);
@@ -992,29 +995,59 @@ __device__ __forceinline__ void latent_block(const DecodeArgs& a, unsigned char*
     }
     const size_t pidx = (size_t)sq * a.nsplit + (s < 0 ? 0 : s);
     const int head = s < 0 ? a.Hq : hb * 16 + li;    // a workgroup without a range writes nothing
+    // The range's value partial. float32 latents: float32. bf16 and int4 latents: fp16 with a
+    // power of two per (range, head) folded into (m, l): the head's largest |A| is brought into
+    // [2^14, 2^15) by A' = A 2^-e, and (m', l') = (m + e, l 2^-e), so 2^(m' - m*) A' = 2^(m - m*) A
+    // for any reference m* of the combine. One rounding to 11 significant bits: at most 2^-12 of
+    // the head's largest value per element, under a tenth of the bf16 latents' 5e-3 budget,
+    // while the bytes written here and read by the combine halve. (bf16 partials, at 2^-9, took
+    // the rank-1 bf16 case to 96% of that budget.)
+    float psc = 1.f;
+    if constexpr (LT != LT_F32) {
+      float mxa = 0.f;
+#pragma unroll
+      for (int j = 0; j < NVB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mxa = fmaxf(mxa, fabsf(acc[j][e]));
+      mxa = wave_max_lg(mxa);                        // the head's 4 lane groups
+      if constexpr (!SP) {                           // halves: the head's other half (role ^ 2)
+        float* xm = (float*)(smem + 512 * (NX > 0 ? NX : 1) + NX * NVB * 1024);   // past the merge buffers
+        xm[role * 64 + lane] = mxa;
+        barrier_lds();                               // every other wave: the barrier below
+        mxa = fmaxf(mxa, xm[(role ^ 2) * 64 + lane]);
+      }
+      int ex = 0;
+      if (mxa > 0.f && mxa <= 3.4e38f) {             // 0, inf and NaN keep e = 0
+        ex = ilogbf(mxa) - 14;
+        ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+      }
+      psc = ldexpf(1.f, -ex);
+      if (ms != -INFINITY) ms += (float)ex;
+      lt *= psc;
+    } else if constexpr (!SP) {
+      barrier_lds();                                 // pairs with the exchange barrier above
+    }
     if (half == 0 && lg == 0 && head < a.Hq) {
       a.part_ml[(pidx * a.Hq + head) * 2] = ms;
       a.part_ml[(pidx * a.Hq + head) * 2 + 1] = lt;
     }
-    // the range's value partial: bf16 for int4 latents (one rounding of the fp32 sum: half the
-    // bytes to write and for the combine to read, at most 2^-9 of each output element, a fifth of
-    // the int4 error budget), float32 for float32 and bf16 latents, whose tighter budget the
-    // bf16 query fold and bf16 P already use most of
 #pragma unroll
     for (int j = 0; j < NVB; ++j) {
       const int rb = SP ? j : half + 2 * j;
       const size_t o = (pidx * a.Hq + head) * a.rv_pad16 + rb * 16 + 4 * lg;
       if (rb < a.nrb && head < a.Hq) {
-        if constexpr (LT != LT_I4) {
+        if constexpr (LT == LT_F32) {
           *(f32x4*)(a.part_acc + o) = acc[j];
         } else {
-          bf16x4 h;
+          f16x4 h;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = (__bf16)acc[j][e];
-          *(bf16x4*)((__bf16*)a.part_acc + o) = h;
+          for (int e = 0; e < 4; ++e) h[e] = (_Float16)(acc[j][e] * psc);
+          *(f16x4*)((_Float16*)a.part_acc + o) = h;
         }
       }
     }
+  } else if constexpr (!SP) {
+    barrier_lds();                                   // pairs with the main waves' exchange barrier
   }
 }
 
@@ -1057,7 +1090,8 @@ __global__ __launch_bounds__(256) void lr_fold_mfma(FoldArgs f) {
 // ---------------------------------------------------------------------------------------------
 struct CombineArgs {
   const float* part_ml;
-  const float* part_acc;    // [B][nsplit][Hq][rv_pad16]: float32, or bf16 values for int4 latents
+  const float* part_acc;    // [B][nsplit][Hq][rv_pad16]: float32 (float32 latents), else fp16
+                            // values scaled by 2^-e, e folded into part_ml
   const float* win_part;
   const void* bv;
   void* out;
@@ -1153,8 +1187,8 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
             const int sc = s < ns ? s : ns - 1;
             w[u] = s < ns ? ws[sc] : 0.f;
             const size_t o = ((base + sc) * a.Hq + j) * a.rv_pad16 + r;
-            if constexpr (PB) {                   // bf16 partials (int4 latents)
-              const bf16x4 h = *(const bf16x4*)((const __bf16*)a.part_acc + o);
+            if constexpr (PB) {                   // fp16 partials (bf16 and int4 latents)
+              const f16x4 h = *(const f16x4*)((const _Float16*)a.part_acc + o);
               v[u] = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
             } else {
               v[u] = *(const f32x4*)(a.part_acc + o);
@@ -1473,14 +1507,11 @@ hipError_t launch_decode(const DecodePlan& p, const lr_layer_cache* c, const voi
   const size_t lds = (size_t)(p.nsplit + p.rv_pad16 + 4 * (p.rv_pad16 > 512 ? p.rv_pad16 : 512) + 8) * sizeof(float);
   const dim3 cgrid(p.B * p.Hq);
   const bool f32b = p.latent == LR_F32;
-  const bool i4 = p.latent == LR_I4G32;
   const bool f32o = out_dtype == LR_F32;
   if (f32b && f32o) hipLaunchKernelGGL((lr_combine<float, float, false>), cgrid, dim3(256), lds, st, ca);
   else if (f32b) hipLaunchKernelGGL((lr_combine<float, __bf16, false>), cgrid, dim3(256), lds, st, ca);
-  else if (i4 && f32o) hipLaunchKernelGGL((lr_combine<__bf16, float, true>), cgrid, dim3(256), lds, st, ca);
-  else if (i4) hipLaunchKernelGGL((lr_combine<__bf16, __bf16, true>), cgrid, dim3(256), lds, st, ca);
-  else if (f32o) hipLaunchKernelGGL((lr_combine<__bf16, float, false>), cgrid, dim3(256), lds, st, ca);
-  else hipLaunchKernelGGL((lr_combine<__bf16, __bf16, false>), cgrid, dim3(256), lds, st, ca);
+  else if (f32o) hipLaunchKernelGGL((lr_combine<__bf16, float, true>), cgrid, dim3(256), lds, st, ca);
+  else hipLaunchKernelGGL((lr_combine<__bf16, __bf16, true>), cgrid, dim3(256), lds, st, ca);
   return hipGetLastError();
 }
 

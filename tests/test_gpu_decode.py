@@ -1,5 +1,6 @@
 """GPU parity of lowrank_attn_decode against the fp64 oracle (max|gpu-ref|/max|ref| gates:
 5e-3 for fp32/bf16 latents, 1e-2 for int4)."""
+import dataclasses
 import math
 
 import numpy as np
@@ -267,3 +268,19 @@ def test_resume_from_saved_cache_is_bitwise_identical(latent):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     for k in names:
         assert torch.equal(cache.tensors[k].view(torch.uint8), cache2.tensors[k].view(torch.uint8)), k
+
+
+@pytest.mark.parametrize("latent,rank", [("bf16", 358), ("bf16", 512), ("i4g32", 358)])
+@pytest.mark.parametrize("vscale", [1e4, 1e-6])
+@pytest.mark.parametrize("nsplit", [0, 7])
+def test_value_partials_far_from_unit_scale(latent, rank, vscale, nsplit):
+    """The token ranges' value partials of bf16 and int4 latents are stored as fp16 with a power
+    of two per (range, head) folded into the range's (m, l). Value latents scaled by 1e4 make the
+    unscaled partials overflow fp16 (a range sums up to 2^8 times its tokens' values, since the
+    reference max moves lazily), and by 1e-6 push them into fp16's subnormals; both must still
+    meet the oracle gate. Rank 512 takes the layout in which two waves hold each head's value
+    blocks (they agree on one power of two through LDS); automatic (balanced) and explicit splits."""
+    cfg = synth.CONFIGS[1].replace(batch=3, seq_len=3000, latent=latent, rank_k=rank, rank_v=rank)
+    li = synth.make_layer(cfg, q_scale=8.0)
+    li = dataclasses.replace(li, zv=(li.zv.float() * vscale).to(li.zv.dtype))
+    check(li, nsplit=nsplit)
