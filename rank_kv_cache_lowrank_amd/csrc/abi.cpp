@@ -198,7 +198,7 @@ static int plan_lds(DecodePlan* p, int ld_k, int ld_v, const char** msg) {
     const int pstage = kTileTokens * (lds_stride_k(KS, 2) + lds_stride_v(nv / 2, 2));
     int nst = (kLdsBytes - kLdsPad) / pstage;
     nst = nst > 8 ? 8 : nst;
-    if (nv == 0 || nst < 3 || p->copy_k > KS * 64 || p->copy_v > nv * 32)
+    if (nv == 0 || nst < 4 || p->copy_k > KS * 64 || p->copy_v > nv * 32)
       return *msg = "latent rows too wide for the prefill kernel", LR_EUNSUPPORTED;
     p->pf_nst = nst;
     p->pf_lds = nst * pstage + kLdsPad;

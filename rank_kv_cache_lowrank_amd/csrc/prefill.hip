@@ -26,6 +26,8 @@
 // exact-keys partials and up-projects.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -355,15 +357,33 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
     for (int j = 0; j < NV; ++j) acc[h][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   bool bad = false;
-  auto finish = [&](const unsigned char* stg, int nvalid, const f32x4 (&sacc)[NHB]) {
+  // Softmax of one tile, then its value products. The 16x16x16 products take as long per
+  // instruction as the 16x16x32 ones (measured on gfx950: 1.2 against 2.3 PFLOP/s), so tiles go
+  // in pairs: mode 0 keeps the first tile's P in registers (pdef) and does no products; mode 1
+  // contracts both tiles at once, K = 32 tokens: slots 0-3 of lane group lg hold tokens 4 lg ..
+  // 4 lg + 3 of the first tile and slots 4-7 the same tokens of the second, which is how the two
+  // score tiles and the two transpose reads land (no shuffle); mode 2 is a lone last tile, K = 16.
+  // No pass rescales, so a deferred P stays valid.
+  pf_bf16x4 pdef[NHB];
+  auto finish = [&](auto mode_c, const unsigned char* stg, const unsigned char* sprev, int nvalid,
+                    const f32x4 (&sacc)[NHB]) {
+    constexpr int MODE = decltype(mode_c)::value;
     float v[NHB][4], mx[NHB];
     masked(sacc, nvalid, v, mx);
-    // first value operands in flight under the softmax
-    constexpr int VC = 8;
+    // first value operands in flight under the softmax (a pair reads two per block: 4 blocks in
+    // flight past 24 blocks, where 8 would spill)
+    constexpr int VC = (MODE == 1 && NV > 24) ? 4 : 8;
     const unsigned char* vbase = stg + vrow_off;
-    pf_bf16x4 vop[VC];
+    const unsigned char* pbase = sprev + vrow_off;
+    pf_bf16x4 vop[VC], vpr[VC];
+    if constexpr (MODE != 0) {
 #pragma unroll
-    for (int k = 0; k < VC; ++k) vop[k] = pf_vread(vbase + k * 32);
+      for (int k = 0; k < VC; ++k) vop[k] = pf_vread(vbase + k * 32);
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int k = 0; k < VC; ++k) vpr[k] = pf_vread(pbase + k * 32);
+    }
     pf_bf16x4 pb[NHB];
 #pragma unroll
     for (int h = 0; h < NHB; ++h) {
@@ -380,49 +400,71 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
       }
       lsum[h] += ps;
     }
-    // values: A^T[rv][head li] of the wave's head blocks, one operand read per block
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int h = 0; h < NHB; ++h) pdef[h] = pb[h];
+      return;
+    }
+    bf16x8 pb8[NHB];
+#pragma unroll
+    for (int h = 0; h < NHB; ++h) pb8[h] = __builtin_shufflevector(pdef[h], pb[h], 0, 1, 2, 3, 4, 5, 6, 7);
+    // values: A^T[rv][head li] of the wave's head blocks, one operand read per block and tile
 #pragma unroll
     for (int j0 = 0; j0 < NV; j0 += VC) {
       if (j0 > 0) {
 #pragma unroll
-        for (int k = 0; k < VC; ++k)
-          if (j0 + k < NV) vop[k] = pf_vread(vbase + (j0 + k) * 32);
+        for (int k = 0; k < VC; ++k) {
+          if (j0 + k < NV) {
+            vop[k] = pf_vread(vbase + (j0 + k) * 32);
+            if constexpr (MODE == 1) vpr[k] = pf_vread(pbase + (j0 + k) * 32);
+          }
+        }
       }
 #pragma unroll
       for (int k = 0; k < VC; ++k)
         if (j0 + k < NV)
 #pragma unroll
-          for (int h = 0; h < NHB; ++h)
-            acc[h][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[k], pb[h], acc[h][j0 + k], 0, 0, 0);
+          for (int h = 0; h < NHB; ++h) {
+            if constexpr (MODE == 1)
+              acc[h][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_shufflevector(vpr[k], vop[k], 0, 1, 2, 3, 4, 5, 6, 7), pb8[h], acc[h][j0 + k], 0, 0, 0);
+            else
+              acc[h][j0 + k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop[k], pb[h], acc[h][j0 + k], 0, 0, 0);
+          }
     }
   };
 
-  // The full passes, software-pipelined by one tile: iteration it first publishes tile it + 1
-  // (its loads landed, one barrier), refills the stage tile it - 1 left (every wave finished it
-  // before that barrier), then issues tile it + 1's score products before tile it's softmax and
-  // value products, so the matrix cores work on the former while the latter's ALU work runs.
-  // Tiles it - 1, it and it + 1 occupy distinct stages (at least 3).
+  // The full passes, software-pipelined by one tile: step it first publishes tile it + 1 (its
+  // loads landed, one barrier), refills the stage tile it - 2 left (every wave finished it before
+  // that barrier: a pair's value products run in the step of its second tile), then issues tile
+  // it + 1's score products before tile it's softmax and value products, so the matrix cores work
+  // on the former while the latter's ALU work runs. Tiles it - 1 (the first of a pair, read again
+  // by the pair's products), it, it + 1 and the refilled one occupy distinct stages (at least 4).
+  // Each loop iteration takes one pair of tiles in two straight-line steps, so the accumulators'
+  // loop-carried values never merge with a path that skips the products.
   auto stream_full = [&]() {
-    const int pro = min(NST - 1, ntiles);
+    const int pro = min(NST - 2, ntiles);
     for (int t = 0; t < pro; ++t) issue(t, smem + t * STAGE);
     wait_vmcnt(count(0, pro - 1));                     // tile 0 landed (this wave's part)
     if (ntiles > 0) fix_tail(0, smem);
     barrier_lds();
+    unsigned char* s_prv = smem;                       // stage of tile it - 1
     unsigned char* s_cur = smem;                       // stage of tile it
     unsigned char* s_nxt = next_stage(smem);           // stage of tile it + 1
-    unsigned char* s_iss = smem + (NST - 1) * STAGE;   // stage of tile it + NST - 1
+    unsigned char* s_iss = smem + (NST - 2) * STAGE;   // stage of tile it + NST - 2 (= it - 2)
     f32x4 cur[NHB];
     if (ntiles > 0) products(smem, cur);
-    for (int it = 0; it < ntiles; ++it) {
+    auto step = [&](int it, auto mode_c) {
       if (it + 1 < ntiles) {
-        wait_vmcnt(count(it + 1, min(it + NST - 2, ntiles - 1)));   // tile it + 1 landed
+        wait_vmcnt(count(it + 1, min(it + NST - 3, ntiles - 1)));   // tile it + 1 landed
         fix_tail(it + 1, s_nxt);
       }
       barrier_lds();
-      if (it + NST - 1 < ntiles) issue(it + NST - 1, s_iss);
+      if (it + NST - 2 < ntiles) issue(it + NST - 2, s_iss);
       f32x4 nxt[NHB];
-      products(s_nxt, nxt);                            // (last iteration: a stale stage, unused)
-      finish(s_cur, min(kTileTokens, t_end - t_begin - it * kTileTokens), cur);
+      products(s_nxt, nxt);                            // (last step: a stale stage, unused)
+      finish(mode_c, s_cur, s_prv, min(kTileTokens, t_end - t_begin - it * kTileTokens), cur);
+      s_prv = s_cur;
       s_cur = s_nxt;
       s_nxt = next_stage(s_nxt);
       s_iss = next_stage(s_iss);
@@ -435,7 +477,12 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
+    };
+    for (int it = 0; it + 1 < ntiles; it += 2) {
+      step(it, std::integral_constant<int, 0>{});
+      step(it + 1, std::integral_constant<int, 1>{});
     }
+    if (ntiles & 1) step(ntiles - 1, std::integral_constant<int, 2>{});
   };
   int* flag = (int*)(smem + NST * STAGE + 64);         // in the slack after the ring
   if (tid == 0) *flag = 0;                             // ordered by the first barrier of the stream

@@ -214,6 +214,20 @@ def test_prefill_long_ranges(rank, C):
 
 
 @pytest.mark.parametrize("rank", [358, 100])
+def test_prefill_tile_pairs(rank):
+    """Latent lengths of 1 to 5 tiles of 16 rows, full and ragged, one range per sequence: the
+    latent kernel runs the value products of two tiles at once (K = 32 tokens) and a lone last
+    tile on its own when the count is odd."""
+    cfg, li = small("bf16", rank, B=8, L=(1, 16, 17, 32, 33, 48, 64, 79))
+    q, k, v = chunk_inputs(cfg, 5, rank=rank)
+    model, cache = device_layer(li)
+    ref = oracle(li, q, k, v)
+    for nsplit in (1, 3):
+        out = run_prefill(model, cache, q, k, v, 79, nsplit=nsplit)
+        assert rel_err(out, ref) < TOL["bf16"], nsplit
+
+
+@pytest.mark.parametrize("rank", [358, 100])
 def test_prefill_nan_pad_columns(rank):
     """Stored rows whose pad columns (past the rank, inside the last 16-byte granule) hold NaN:
     they must not reach the scores."""
