@@ -68,9 +68,9 @@ static void layout_workspace(DecodePlan* p) {
   p->off_ml = off;
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * 2 * 4);
   p->off_acc = off;
-  // value partials: fp16 from the decode kernel for bf16 and int4 latents, float32 otherwise
-  // (float32 latents, the dedicated prefill kernel)
-  const int acc_bytes = (p->latent != LR_F32 && !p->pf) ? 2 : 4;
+  // value partials: fp16 for bf16 and int4 latents (the decode and the prefill latent kernels),
+  // float32 for float32 latents
+  const int acc_bytes = p->latent != LR_F32 ? 2 : 4;
   off = align256(off + (size_t)p->B * p->nsplit * p->Hq * p->rv_pad16 * acc_bytes);
   p->off_win = off;
   if (p->exact) off = align256(off + (size_t)p->B * p->Hq * (p->d + 2) * 4);

@@ -22,8 +22,8 @@
 // the token range (launch_prefill_latent). All waves load the LDS ring with 16-byte
 // direct-to-LDS loads, cached (the token groups of a range share its rows through L2), each wave
 // waiting for exactly its own loads, one barrier per 16-token tile. The partials (m, l, A) per
-// (query token, token range) have the decode layout, so the decode combine merges them with the
-// exact-keys partials and up-projects.
+// (query token, token range), A in fp16, have the decode layout; lr_prefill_combine merges them
+// with the exact-keys partials and up-projects.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -37,6 +37,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 pf_bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short pf_s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 pf_f16x4;
 
 constexpr float kPfMaxLead = 64.f;       // base-2 lead of a score over the reference max that
                                          // pass 0 tolerates (p <= 2^64: finite in bf16 and f32)
@@ -71,7 +72,7 @@ struct PrefillArgs {
   const __bf16* qt;          // [query sequences][32][rk_pad] folded queries (bf16)
   const int32_t* lat_len;
   float* part_ml;            // [query sequence][nsplit][Hq][2]
-  float* part_acc;           // [query sequence][nsplit][Hq][rv_pad16]
+  float* part_acc;           // [query sequence][nsplit][Hq][rv_pad16] as fp16
   long long t_cap;
   int row_bytes_k, row_bytes_v, copy_k, copy_v;
   int rk, rk_pad, nks, nrb, rv_pad16;
@@ -511,19 +512,45 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
   }
 
   if (!active) return;
+  // The partial (m, l, A) of each (chunk token, range, head), A in fp16 with a power of two per
+  // row folded into (m, l): the head's largest |A| is brought into [2^14, 2^15) by A' = A 2^-e,
+  // and (m', l') = (m + e, l 2^-e), so 2^(m' - m*) A' = 2^(m - m*) A for any reference m* of the
+  // combine. One rounding to 11 significant bits (at most 2^-12 of the row's largest value per
+  // element), and half the bytes written here and read by the combine.
   const size_t pidx = (size_t)sq * a.nsplit + s;
 #pragma unroll
   for (int h = 0; h < NHB; ++h) {
-    const float l = wave_sum_lg(lsum[h]);
+    float l = wave_sum_lg(lsum[h]);
+    float mxa = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mxa = fmaxf(mxa, fabsf(acc[h][j][e]));
+    mxa = wave_max_lg(mxa);                          // the head's 4 lane groups
+    int ex = 0;
+    if (mxa > 0.f && mxa <= 3.4e38f) {               // 0, inf and NaN keep e = 0
+      ex = ilogbf(mxa) - 14;
+      ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+    }
+    const float psc = ldexpf(1.f, -ex);
+    const float mw = mref[h] == -INFINITY ? mref[h] : mref[h] + (float)ex;
+    l *= psc;
     const int head = (hb0 + h) * 16 + li;
     if (head >= a.Hq) continue;
     if (lg == 0) {
-      a.part_ml[(pidx * a.Hq + head) * 2] = mref[h];
+      a.part_ml[(pidx * a.Hq + head) * 2] = mw;
       a.part_ml[(pidx * a.Hq + head) * 2 + 1] = l;
     }
+    _Float16* pa = (_Float16*)a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + 4 * lg;
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if (j < a.nrb) *(f32x4*)(a.part_acc + (pidx * a.Hq + head) * a.rv_pad16 + j * 16 + 4 * lg) = acc[h][j];
+    for (int j = 0; j < NV; ++j) {
+      if (j < a.nrb) {
+        pf_f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc[h][j][e] * psc);
+        *(pf_f16x4*)(pa + j * 16) = v;
+      }
+    }
   }
 }
 
@@ -696,8 +723,8 @@ constexpr int kCbChunk = 64;                   // rows of Bv staged at a time
 constexpr int kCbBvStride = 128 * 2 + 32;      // LDS row stride (bytes) of the staged Bv rows
 
 struct PfCombineArgs {
-  const float* part_ml;
-  const float* part_acc;
+  const float* part_ml;     // [query sequence][nsplit][Hq][2]: (m, l), the row's 2^e folded in
+  const float* part_acc;    // [query sequence][nsplit][Hq][rv_pad16] fp16 values scaled by 2^-e
   const float* win_part;
   const __bf16* bv;        // [rv][D]
   void* out;               // [B * C][Hq][d]
@@ -828,7 +855,8 @@ __global__ __launch_bounds__(256) void lr_prefill_combine(PfCombineArgs a) {
           for (int k = 0; k < 4; ++k) {
             const size_t row = rowoff[u] + (size_t)min(s0 + k, a.nsplit - 1) * a.Hq;
             msv[u][k] = a.part_ml[row * 2];
-            xv[u][k] = *(const f32x4*)(a.part_acc + row * a.rv_pad16 + 4 * r4s[u]);
+            const pf_f16x4 h = *(const pf_f16x4*)((const _Float16*)a.part_acc + row * a.rv_pad16 + 4 * r4s[u]);
+            xv[u][k] = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
           }
         }
 #pragma unroll

@@ -227,6 +227,23 @@ def test_prefill_tile_pairs(rank):
         assert rel_err(out, ref) < TOL["bf16"], nsplit
 
 
+@pytest.mark.parametrize("rank", [358, 512])
+@pytest.mark.parametrize("vscale", [1e4, 1e-6])
+@pytest.mark.parametrize("nsplit", [0, 1])
+def test_prefill_value_partials_far_from_unit_scale(rank, vscale, nsplit):
+    """The latent kernel stores each (chunk token, range, head) value partial as fp16 with a power
+    of two folded into its (m, l). Value latents scaled by 1e4 would overflow unscaled fp16
+    partials and by 1e-6 push them into the subnormals; both must meet the oracle gate, with
+    several ranges per sequence and with one range of more than 4096 tokens (the layout with
+    both head blocks in one wave)."""
+    cfg, li = small("bf16", rank, B=2, L=(4500, 1300))
+    li.zv.mul_(vscale)
+    q, k, v = chunk_inputs(cfg, 6, rank=rank)
+    model, cache = device_layer(li)
+    out = run_prefill(model, cache, q, k, v, 4500, nsplit=nsplit)
+    assert rel_err(out, oracle(li, q, k, v)) < TOL["bf16"]
+
+
 @pytest.mark.parametrize("rank", [358, 100])
 def test_prefill_nan_pad_columns(rank):
     """Stored rows whose pad columns (past the rank, inside the last 16-byte granule) hold NaN:
