@@ -435,16 +435,22 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
     }
   };
 
-  // The full passes, software-pipelined by one tile: step it first publishes tile it + 1 (its
-  // loads landed, one barrier), refills the stage tile it - 2 left (every wave finished it before
-  // that barrier: a pair's value products run in the step of its second tile), then issues tile
-  // it + 1's score products before tile it's softmax and value products, so the matrix cores work
-  // on the former while the latter's ALU work runs. Tiles it - 1 (the first of a pair, read again
-  // by the pair's products), it, it + 1 and the refilled one occupy distinct stages (at least 4).
-  // Each loop iteration takes one pair of tiles in two straight-line steps, so the accumulators'
-  // loop-carried values never merge with a path that skips the products.
+  // The full passes, software-pipelined by one tile: step it issues tile it + 1's score products
+  // before tile it's softmax and value products, so the matrix cores work on the former while the
+  // latter's ALU work runs. A pair's value products run in the step of its second tile, so tile
+  // it - 1 is still read in step it. Each loop iteration takes one pair of tiles in two
+  // straight-line steps, so the accumulators' loop-carried values never merge with a path that
+  // skips the products.
+  // Publication: with at least 5 stages, only the first step of a pair meets the workgroup
+  // barrier: it publishes tiles it + 1 and it + 2 (the next step's score products need the
+  // latter) and refills the stages of tiles it - 2 and it - 1 (the pair before, finished before
+  // that barrier) with tiles it + NST - 2 and it + NST - 1. With 4 stages every step meets the
+  // barrier, publishes tile it + 1 and refills the stage of tile it - 2 with tile it + NST - 2.
+  // Either way tile t lives in stage t mod NST, and before step it tiles up to it + NST - 3 are
+  // issued.
   auto stream_full = [&]() {
-    const int pro = min(NST - 2, ntiles);
+    const bool pairb = NST >= 5;
+    const int pro = min(NST - 2, ntiles);                // tiles 0 .. NST - 3
     for (int t = 0; t < pro; ++t) issue(t, smem + t * STAGE);
     wait_vmcnt(count(0, pro - 1));                     // tile 0 landed (this wave's part)
     if (ntiles > 0) fix_tail(0, smem);
@@ -456,12 +462,18 @@ __global__ __launch_bounds__(pf_threads(NHB)) void lr_prefill_latent(PrefillArgs
     f32x4 cur[NHB];
     if (ntiles > 0) products(smem, cur);
     auto step = [&](int it, auto mode_c) {
-      if (it + 1 < ntiles) {
-        wait_vmcnt(count(it + 1, min(it + NST - 3, ntiles - 1)));   // tile it + 1 landed
-        fix_tail(it + 1, s_nxt);
+      constexpr int MODE = decltype(mode_c)::value;
+      if (!pairb || MODE != 1) {
+        const int last = min(it + (pairb ? 2 : 1), ntiles - 1);   // last tile this step publishes
+        if (it + 1 < ntiles) {
+          wait_vmcnt(count(last, min(it + NST - 3, ntiles - 1)));
+          fix_tail(it + 1, s_nxt);
+          if (last > it + 1) fix_tail(last, next_stage(s_nxt));
+        }
+        barrier_lds();
+        if (it + NST - 2 < ntiles) issue(it + NST - 2, s_iss);
+        if (pairb && it + NST - 1 < ntiles) issue(it + NST - 1, next_stage(s_iss));
       }
-      barrier_lds();
-      if (it + NST - 2 < ntiles) issue(it + NST - 2, s_iss);
       f32x4 nxt[NHB];
       products(s_nxt, nxt);                            // (last step: a stale stage, unused)
       finish(mode_c, s_cur, s_prv, min(kTileTokens, t_end - t_begin - it * kTileTokens), cur);
