@@ -227,6 +227,22 @@ def test_prefill_tile_pairs(rank):
         assert rel_err(out, ref) < TOL["bf16"], nsplit
 
 
+@pytest.mark.parametrize("rank_k,rank_v", [(358, 400), (400, 358), (450, 512)])
+def test_prefill_unequal_ranks_ring_depths(rank_k, rank_v):
+    """Unequal key and value ranks give the latent kernel 5-stage rings (one barrier per pair of
+    tiles with the shallowest lookahead that allows) and 4-stage rings (one barrier per tile);
+    long single ranges of odd and even tile counts and ragged ends, against the oracle."""
+    cfg = synth.Config(93, f"prefill-r{rank_k}-{rank_v}", batch=3, seq_len=500, rank_k=rank_k, rank_v=rank_v,
+                       latent="bf16")
+    li = synth.make_layer(cfg, lat_len=np.asarray([500, 77, 264], np.int32))
+    model, cache = device_layer(li)
+    q, k, v = chunk_inputs(cfg, 5)
+    ref = oracle(li, q, k, v)
+    for nsplit in (1, 2):
+        out = run_prefill(model, cache, q, k, v, 500, nsplit=nsplit)
+        assert rel_err(out, ref) < TOL["bf16"], nsplit
+
+
 @pytest.mark.parametrize("rank", [358, 512])
 @pytest.mark.parametrize("vscale", [1e4, 1e-6])
 @pytest.mark.parametrize("nsplit", [0, 1])
