@@ -164,6 +164,22 @@ def cpu_baseline(cfg, li, budget_s: float = 8.0, reps: int = 3, d1_budget_s: flo
                     "us_per_layer_step": t1 * cfg.batch * 1e6})
 
 
+def oracle_time(fn, budget_s: float = 4.0, reps: int = 3):
+    """Median wall time (s) of fn() on the host over at least `reps` runs, repeated until `budget_s`
+    is spent (at most 50 runs), and the number of runs: the oracle beside an operation's GPU line."""
+    times = []
+    while len(times) < reps or (sum(times) < budget_s and len(times) < 50):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times)
+
+
+def host_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+
+
 def copy_ceiling(torch, dev, nbytes: int = 1 << 30, reps: int = 5):
     """A plain device copy of `nbytes` (read once, written once), timed with events in the same run:
     the practical ceiling of a 1:1 read/write stream on this GPU (median of `reps`)."""
@@ -414,8 +430,10 @@ def rebase_bench(args):
     log(f"generating inputs for {cfg.name} ...")
     li = synth.make_layer(cfg, t_cap=T, lat_len=np.full(B, T, np.int32))
     bk, bv = li.bk.double().numpy(), li.bv.double().numpy()
-    wk = synth.w_storage(synth.sync_projection(bk, synth.gen_basis_update(cfg, "k", 0, bk, rk2)), "bf16").to(dev)
-    wv = synth.w_storage(synth.sync_projection(bv, synth.gen_basis_update(cfg, "v", 0, bv, rv2)), "bf16").to(dev)
+    wk64 = synth.sync_projection(bk, synth.gen_basis_update(cfg, "k", 0, bk, rk2))
+    wv64 = synth.sync_projection(bv, synth.gen_basis_update(cfg, "v", 0, bv, rv2))
+    wk = synth.w_storage(wk64, "bf16").to(dev)
+    wv = synth.w_storage(wv64, "bf16").to(dev)
     model = lr.Model(1, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, [rk], [rv], cfg.sm_scale, 0, "bf16")
     lat = torch.full((B,), T, dtype=torch.int32, device=dev)
     ldk2, ldv2 = synth.latent_ld(rk2), synth.latent_ld(rv2)
@@ -482,6 +500,20 @@ def rebase_bench(args):
                      "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": int(bytes_call),
                      "mfma_tflops": round(2.0 * B * T * (rk * rk2 + rv * rv2) / (kern_ms * 1e-3) / 1e12, 1)},
     }
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        from oracle import rebase as ORB
+        zk0 = li.zk[0, :T, :rk].float().numpy()
+        zv0 = li.zv[0, :T, :rv].float().numpy()
+        w_k = synth.w_storage(wk64, "bf16")[:, :rk].float().numpy()
+        w_v = synth.w_storage(wv64, "bf16")[:, :rv].float().numpy()
+        t, n = oracle_time(lambda: (ORB.store(ORB.rebase_rows(zk0, w_k), "bf16"),
+                                    ORB.store(ORB.rebase_rows(zv0, w_v), "bf16")))
+        sample_bytes = T * 2 * (rk + rk2 + rv + rv2)
+        rec["cpu_baseline"] = {
+            "value": round(sample_bytes / t / 1e9, 3), "unit": "GB/s", "cores": host_threads(), "kind": "oracle",
+            "sample": f"rebase_rows + store (fp64 oracle) of sequence 0's K and V rows ({T} each), "
+                      f"median of {n} runs {t:.4f} s; algorithmic bytes per second as the GPU line"}
     print(json.dumps(rec), flush=True)
 
 
@@ -559,6 +591,31 @@ def prefill_bench(args):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel_us": round(kern_ms * 1e3, 2), "flops_per_launch": flops},
     }
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        from oracle import prefill as OP
+        from oracle import quant as OQ
+
+        def rows(z, r):
+            x = z[0, :T, :r].float().numpy()
+            return OQ.dequant_rows(*OQ.quantize_rows(x), r) if cfg.latent == "i4g32" else x.astype(np.float64)
+
+        class One:
+            def __init__(self, x):
+                self.x = x
+
+            def __getitem__(self, b):
+                return self.x
+
+        zk0, zv0 = One(rows(li.zk, li.rank_k)), One(rows(li.zv, li.rank_v))
+        qn, kn, vn = q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy()
+        bkn, bvn = li.bk.float().numpy(), li.bv.float().numpy()
+        t, n = oracle_time(lambda: OP.prefill_latent(qn, zk0, zv0, bkn, bvn, li.lat_len, li.rank_k, li.rank_v,
+                                                     cfg.n_kv_heads, cfg.sm_scale, kn, vn, batches=[0]))
+        rec["cpu_baseline"] = {
+            "value": round(C / t, 1), "unit": "tokens/s", "cores": host_threads(), "kind": "oracle",
+            "sample": f"prefill_latent (P2, fp64 oracle): sequence 0, {C} query tokens over {T} latent rows, "
+                      f"median of {n} runs {t:.3f} s"}
     print(json.dumps(rec), flush=True)
 
 
@@ -599,6 +656,7 @@ def sensvd_bench(args):
         sigma = torch.empty(dim, dtype=torch.float32, device=dev)
         ws = torch.empty(lr.lowrank_sens_svd_workspace_size(n, dim), dtype=torch.uint8, device=dev)
         call = lambda: lr.lowrank_sens_svd(xd, wd, rank, basis, sigma, ws)   # noqa: E731
+        n_rows = n
         metric = "sensitivity-weighted SVD basis of one KV matrix: ms per call"
         workload = f"sensvd N{n} D{dim} r{rank}"
     else:
@@ -611,6 +669,7 @@ def sensvd_bench(args):
             xs[m], wv[m] = synth.gen_kv_samples(synth.CONFIGS[4], n, dim, 0.6 + 0.01 * m)
         xd = torch.from_numpy(xs).to(torch.bfloat16).to(dev)
         wd = torch.from_numpy(wv).to(dev)
+        xs0, ws0, n_rows = xs[0].copy(), wv[0].copy(), n
         del xs
         basis = torch.empty(M, rank, dim, dtype=torch.bfloat16, device=dev)
         sigma = torch.empty(M, dim, dtype=torch.float32, device=dev)
@@ -631,6 +690,17 @@ def sensvd_bench(args):
                         "achieved": round(flops / (ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5),
                         "traffic": None, "flops_per_launch": flops}}
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        from oracle import sensvd as OS
+        xs, wsm = (x, w) if M == 1 else (xs0, ws0)
+        ns = min(xs.shape[0], 16384)
+        t, n = oracle_time(lambda: OS.basis(xs[:ns], wsm[:ns], rank))
+        n_all = M * n_rows
+        rec["cpu_baseline"] = {
+            "value": round(t * 1e3 * n_all / ns, 1), "unit": "ms", "cores": host_threads(), "kind": "oracle",
+            "sample": f"basis (fp64 oracle: weighted rows, thin SVD) of the first {ns} rows of matrix 0, median "
+                      f"of {n} runs {t:.3f} s, scaled by rows to the call's {n_all} rows"}
     print(json.dumps(rec), flush=True)
 
 
@@ -669,6 +739,21 @@ def basisupd_bench(args):
                         "achieved": round(flops / (ms * 1e-3) / 1e12, 4), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 7),
                         "traffic": None, "flops_per_launch": flops}}
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        from oracle import basis_update as OB
+        b64 = bd.float().cpu().numpy().astype(np.float64)
+        s64 = sd.cpu().numpy().astype(np.float64)
+        y64 = yd.float().cpu().numpy().astype(np.float64)
+
+        def upd():
+            b2, _ = OB.incremental_update(s64, b64, y64, r)
+            return OB.sync_weights(b64, b2)
+
+        t, n = oracle_time(upd)
+        rec["cpu_baseline"] = {
+            "value": round(t * 1e3, 3), "unit": "ms", "cores": host_threads(), "kind": "oracle",
+            "sample": f"incremental_update + sync_weights (fp64 oracle), the whole call, median of {n} runs"}
     print(json.dumps(rec), flush=True)
 
 
@@ -720,6 +805,29 @@ def append_bench(args):
                         "achieved": round(nbytes / (ms * 1e-3) / 1e9, 2), "peak": PEAK_HBM_TBS * 1000,
                         "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / (PEAK_HBM_TBS * 1000), 5),
                         "traffic": None, "bytes_per_launch": nbytes}}
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        from oracle import append as OA
+        # the stored down-projections are rank-major [r][D]; the oracle takes P [D, r]
+        pk = cache.tensors["pk"].float().cpu().numpy().astype(np.float64).T
+        pv = cache.tensors["pv"].float().cpu().numpy().astype(np.float64).T
+        kn, vn = k[0].float().cpu().numpy(), v[0].float().cpu().numpy()
+
+        def one_seq():
+            st = OA.SeqState(cfg.window, D)
+            if cfg.window:
+                st.win_len = cfg.window
+            for c in range(C):
+                OA.append_token(st, kn[c], vn[c], pk, pv, pos_base=int(li.lat_len[0]))
+            if st.lat_len:
+                OA.store_rows(np.asarray(st.lat_z_k), cfg.latent)
+                OA.store_rows(np.asarray(st.lat_z_v), cfg.latent)
+
+        t, n = oracle_time(one_seq, budget_s=2.0)
+        rec["cpu_baseline"] = {
+            "value": round(t * B * 1e6, 2), "unit": "us", "cores": host_threads(), "kind": "oracle",
+            "sample": f"append_token x {C} + store_rows (fp64 oracle) for sequence 0, median of {n} runs "
+                      f"{t * 1e6:.1f} us, times the {B} sequences of the call"}
     print(json.dumps(rec), flush=True)
 
 
@@ -747,6 +855,14 @@ def rankalloc_bench(args):
            "roofline": {"bound": "alu", "kernel": "whole call (lr_rank_gains, lr_rank_count, lr_rank_select)", "achieved": round(n_gran ** 2 / (ms * 1e-3) / 1e12, 6),
                         "peak": 78.6, "unit": "T compares/s", "frac": round(n_gran ** 2 / (ms * 1e-3) / 1e12 / 78.6, 8),
                         "traffic": None}}
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        from oracle import rankalloc as ORA
+        sn = s.cpu().numpy()
+        t, n = oracle_time(lambda: ORA.allocate(sn, budget, 128, 512, 8), budget_s=2.0, reps=1)
+        rec["cpu_baseline"] = {
+            "value": round(t * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+            "sample": f"allocate (the literal greedy oracle, pure Python), the whole call, median of {n} runs"}
     print(json.dumps(rec), flush=True)
 
 
