@@ -14,14 +14,16 @@
 //
 //   S^T[16 tokens, 16 heads] = Zk qt^T           16x16x32 bf16, K = rank (A = latent rows)
 //   online softmax in base 2                      (reference max with slack, as in decode)
-//   A^T[16 rv, 16 heads] += Zv^T P^T              16x16x16 bf16, K = the tile's 16 tokens
+//   A^T[16 rv, 16 heads] += Zv^T P^T              16x16x32 bf16, K = a pair of tiles' 32 tokens
 //
 // Workgroup = 4 chunk tokens, as 8 waves of one (token, head block) each (two waves per SIMD: the
 // accumulators of one head block over the full value rank fit half the register file) or 4 waves
 // of one token with both head blocks (one wave per SIMD; ~430 registers), chosen by the length of
 // the token range (launch_prefill_latent). All waves load the LDS ring with 16-byte
 // direct-to-LDS loads, cached (the token groups of a range share its rows through L2), each wave
-// waiting for exactly its own loads, one barrier per 16-token tile. The partials (m, l, A) per
+// waiting for exactly its own loads, one barrier per pair of 16-token tiles (per tile when the
+// ring holds only 4 stages); the value products contract a pair of tiles at once (K = 32
+// tokens). The partials (m, l, A) per
 // (query token, token range), A in fp16, have the decode layout; lr_prefill_combine merges them
 // with the exact-keys partials and up-projects.
 #include <hip/hip_ext.h>
