@@ -204,6 +204,7 @@ hipError_t launch_rank_allocate(const float* sigma, int n_mat, int sigma_ld, lon
 
 // Host plans of the rebase and weighted-SVD kernels (plans.cpp), shared with their launchers.
 constexpr int kRbConsumers = 4;     // rebase: waves that hold W blocks and multiply (one per SIMD)
+constexpr int kRbAllWaves = 8;      // rebase, all-waves form: every wave loads and multiplies
 constexpr int kJb = 16;             // weighted SVD: Jacobi block size
 constexpr int kJs = 2 * kJb;        // its pair subproblem size (32)
 constexpr int kRqRows = 64;         // rows of G0 per workgroup of the Rayleigh quotients
@@ -211,6 +212,7 @@ int svd_nsplit(int n);              // sample ranges of the Gram
 
 struct RebaseShape {
   int nks_t, nb, col_chunk, nchunk;
+  int all;             // the all-waves form (kRbAllWaves waves of nb blocks each)
 };
 // bf16 kernel shape of one matrix; it can be rebased in place only when nchunk is 1.
 void rebase_shape(int r_old, int r_new, RebaseShape* s);   // new coordinates per workgroup chunk (bf16)

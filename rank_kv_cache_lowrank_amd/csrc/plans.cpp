@@ -23,6 +23,16 @@ void rebase_shape(int r_old, int r_new, RebaseShape* s) {
   s->nb = (blk_chunk + kRbConsumers - 1) / kRbConsumers;
   s->col_chunk = s->nb * kRbConsumers * 16;
   s->nchunk = (r_new + s->col_chunk - 1) / s->col_chunk;
+  s->all = 0;
+  // 12 K steps leave room for 3 W blocks per wave: where 4 waves would need two chunks (each
+  // re-reading the rows), 8 waves that also load the ring make all new coordinates in one
+  const int all_cols = kRbAllWaves * 3 * 16;
+  if (s->nks_t == 12 && s->nchunk > 1 && r_new <= all_cols) {
+    s->all = 1;
+    s->nb = 3;
+    s->col_chunk = all_cols;
+    s->nchunk = 1;
+  }
 }
 
 int svd_nsplit(int n) {

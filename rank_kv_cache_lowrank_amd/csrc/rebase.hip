@@ -54,6 +54,7 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {   // round t
 constexpr int kRbTile = 16;          // rows per tile (the MFMA's N)
 constexpr int kRbProducers = 2;      // waves 0..1 stream the tiles into LDS
 constexpr int kRbThreads = (kRbProducers + kRbConsumers) * 64;
+constexpr int rb_threads(bool all) { return all ? kRbAllWaves * 64 : kRbThreads; }
 constexpr int kRbMaxStages = 32;
 
 // 16-byte granule order inside an LDS tile row. A consumer's read of one K step takes granule
@@ -118,8 +119,12 @@ __device__ __forceinline__ bool rb_next(RbIter& it, const RebaseArgs& a, long lo
 // rows read from LDS, so every LDS read of a tile feeds NB matrix-core products. Waves 0-1
 // stream the steps through an LDS ring with direct-to-LDS loads and exact vmcnt waits (two
 // producers double the loads one wave may keep in flight); one barrier per step.
-template <int NKS, int NB>
-__global__ __launch_bounds__(kRbThreads) void lr_rebase_bf16(RebaseArgs a) {
+// ALL: 8 waves that each hold NB blocks of W (twice the new coordinates of one workgroup, for
+// ranks whose W blocks leave room for only 3 per wave) and each load their share of every
+// step: a wave waits for its own loads of step c, the barrier publishes the step and frees the
+// stage of step c - 1, and the wave then issues step c + stages - 1 into it.
+template <int NKS, int NB, bool ALL>
+__global__ __launch_bounds__(rb_threads(ALL)) void lr_rebase_bf16(RebaseArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   const int kv = a.kv0 + blockIdx.y;
   const int r_old = a.r_old[kv], r_new = a.r_new[kv];
@@ -136,43 +141,47 @@ __global__ __launch_bounds__(kRbThreads) void lr_rebase_bf16(RebaseArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sld = a.src_ld[kv];
 
-  if (wave < kRbProducers) {
-    // ---- producers: rows -> LDS ring. Instruction k of a 16-row tile (k = wave, wave + 2, ...)
-    // fills LDS slots 64k .. 64k+63 (16 B each) of the tile; slot s holds row s / G, granule
-    // (s % G) ^ swizzle(row). Granules past the rank load granule 0 instead (in bounds, finite;
-    // their W columns are zero). Every tile of a step is loaded (rows past the sequence's end
-    // repeat its last row), so each step costs every producer the same number of loads.
-    constexpr int KP = (NKS + kRbProducers - 1) / kRbProducers;
-    const int my_cnt = (nks - wave + kRbProducers - 1) / kRbProducers;   // loads per tile
-    const __bf16* src = (const __bf16*)a.src[kv];
-    int rowk[KP], colk[KP];
+  // ---- loads: rows -> LDS ring, by the NL loading waves (the producers, or with ALL every
+  // wave). Instruction k of a 16-row tile (k = lw, lw + NL, ...) fills LDS slots 64k .. 64k+63
+  // (16 B each) of the tile; slot s holds row s / G, granule (s % G) ^ swizzle(row). Granules past
+  // the rank load granule 0 instead (in bounds, finite; their W columns are zero). Every tile of a
+  // step is loaded (rows past the sequence's end repeat its last row), so each step costs every
+  // loading wave the same number of loads.
+  constexpr int NL = ALL ? kRbAllWaves : kRbProducers;
+  constexpr int KP = (NKS + NL - 1) / NL;
+  const int lw = wave < NL ? wave : 0;                  // this wave's loader index
+  const int my_cnt = (nks - lw + NL - 1) / NL;          // loads per tile
+  const __bf16* src = (const __bf16*)a.src[kv];
+  int rowk[KP], colk[KP];
 #pragma unroll
-    for (int u = 0; u < KP; ++u) {
-      const int k = wave + kRbProducers * u;
-      const int sl = 64 * k + lane;
-      const int row = sl / G, pos = sl - row * G;
-      const int gr = pos ^ rb_swz(row, G);
-      rowk[u] = row;
-      colk[u] = gr * 8 < r_old ? gr * 8 : 0;
-    }
-    auto issue = [&](const RbIter& t, int stage) {
-      const __bf16* base = src + (size_t)t.cb * a.src_tcap * sld;
-      unsigned char* dstl = ring + stage * step_bytes + wave * 1024;
-      for (int q = 0; q < sub; ++q) {
+  for (int u = 0; u < KP; ++u) {
+    const int k = lw + NL * u;
+    const int sl = 64 * k + lane;
+    const int row = sl / G, pos = sl - row * G;
+    const int gr = pos ^ rb_swz(row, G);
+    rowk[u] = row;
+    colk[u] = gr * 8 < r_old ? gr * 8 : 0;
+  }
+  auto issue = [&](const RbIter& t, int stage) {
+    const __bf16* base = src + (size_t)t.cb * a.src_tcap * sld;
+    unsigned char* dstl = ring + stage * step_bytes + lw * 1024;
+    for (int q = 0; q < sub; ++q) {
 #pragma unroll
-        for (int u = 0; u < KP; ++u) {
-          if (u < my_cnt) {
-            int row = t.t0 + q * kRbTile + rowk[u];
-            row = row < t.cL ? row : t.cL - 1;
-            dma16(base + (size_t)row * sld + colk[u], dstl + q * tile_bytes + kRbProducers * u * 1024);
-          }
+      for (int u = 0; u < KP; ++u) {
+        if (u < my_cnt) {
+          int row = t.t0 + q * kRbTile + rowk[u];
+          row = row < t.cL ? row : t.cL - 1;
+          dma16(base + (size_t)row * sld + colk[u], dstl + q * tile_bytes + NL * u * 1024);
         }
       }
-    };
+    }
+  };
+  const int per_step = my_cnt * sub;
+
+  if (!ALL && wave < kRbProducers) {
     RbIter ii, ci;
     rb_init(ii, lo, hi, sps);
     rb_init(ci, lo, hi, sps);
-    const int per_step = my_cnt * sub;
     int issued = 0;
     for (int s = 0; s < nst - 1; ++s) {
       if (!rb_next(ii, a, cap, step_rows)) break;
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(kRbThreads) void lr_rebase_bf16(RebaseArgs a) {
   }
 
   // ---- consumers
-  const int cw = wave - kRbProducers, lg = lane >> 4, li = lane & 15;
+  const int cw = ALL ? wave : wave - kRbProducers, lg = lane >> 4, li = lane & 15;
   const int jw = blockIdx.z * a.col_chunk[kv] + cw * NB * 16;   // first new coordinate of this wave
   const int jend = min(r_new, (blockIdx.z + 1) * a.col_chunk[kv]);
   // W rows -> registers. Every load is issued (rows and columns clamped into the matrix) and
@@ -226,34 +235,66 @@ __global__ __launch_bounds__(kRbThreads) void lr_rebase_bf16(RebaseArgs a) {
   constexpr int KF = NKS > 4 ? NKS - 4 : 0;             // K steps that always exist
   RbIter t;
   rb_init(t, lo, hi, sps);
+  RbIter ii;                                            // ALL: the next step to load
+  int issued = 0;
+  if constexpr (ALL) {
+    // W is in registers before any ring load goes out, so no wait inside the loop is ever for it
+    LR_WAIT_VM(0);
+    rb_init(ii, lo, hi, sps);
+    for (int s2 = 0; s2 < nst - 1; ++s2) {
+      if (!rb_next(ii, a, cap, step_rows)) break;
+      issue(ii, issued % nst);
+      ++issued;
+    }
+  }
   for (int c = 0; rb_next(t, a, cap, step_rows); ++c) {
+    if constexpr (ALL) {
+      // this wave's loads of step c landed (a conservative count: this wave's result stores are
+      // counted too, and they only make it wait longer)
+      wait_vmcnt((issued - c - 1) * per_step);
+    }
     barrier_lds();
+    if constexpr (ALL) {
+      if (rb_next(ii, a, cap, step_rows)) {               // into the stage step c - 1 left
+        issue(ii, issued % nst);
+        ++issued;
+      }
+    }
     const unsigned char* stp = ring + (c % nst) * step_bytes + li * G * 16;
     for (int q = 0; q < sub; ++q) {
       const int row = t.t0 + q * kRbTile + li;
       if (t.t0 + q * kRbTile >= t.cL) break;            // step-uniform
       const unsigned char* st = stp + q * tile_bytes;
-      u32x4 zv[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int kk = (ks < KF || ks < nks) ? ks : nks - 1;
-        zv[ks] = *(const u32x4*)(st + (((4 * kk + lg) ^ rsw) << 4));
-      }
-      if (fix_tail) {
-#pragma unroll
-        for (int ks = KF; ks < NKS; ++ks) {
-          if (ks == nks - 1) zv[ks] &= last_mask;
-        }
-      }
       f32x4 acc[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // the tile's z operands, all K steps at once (ALL: in halves, for the registers the loads
+      // of the ring take); the products add the K steps in order either way
+      constexpr int ZC = ALL ? (NKS + 1) / 2 : NKS;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (ks < KF || ks < nks) {
-          const bf16x8 zo = __builtin_bit_cast(bf16x8, zv[ks]);
+      for (int ks0 = 0; ks0 < NKS; ks0 += ZC) {
+        u32x4 zv[ZC];
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[nb][ks], zo, acc[nb], 0, 0, 0);
+        for (int u = 0; u < ZC; ++u) {
+          const int ks = ks0 + u;
+          const int kk = (ks < KF || ks < nks) ? ks : nks - 1;
+          if (ks < NKS) zv[u] = *(const u32x4*)(st + (((4 * kk + lg) ^ rsw) << 4));
+        }
+        if (fix_tail) {
+#pragma unroll
+          for (int u = 0; u < ZC; ++u) {
+            const int ks = ks0 + u;
+            if (ks >= KF && ks < NKS && ks == nks - 1) zv[u] &= last_mask;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < ZC; ++u) {
+          const int ks = ks0 + u;
+          if (ks < NKS && (ks < KF || ks < nks)) {
+            const bf16x8 zo = __builtin_bit_cast(bf16x8, zv[u]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[nb][ks], zo, acc[nb], 0, 0, 0);
+          }
         }
       }
       // C[block row 4lg + i][token li]: pairs give 8 consecutive coordinates jp + 8lg + 0..7
@@ -332,7 +373,7 @@ __global__ __launch_bounds__(256) void lr_rebase_f32(RebaseArgs a) {
 // Launch shape shared by K and V: K-step bound NKS (template), blocks of 16 new coordinates
 // per consumer NB (template; bounded by registers), chunks of new coordinates (each chunk is
 // one workgroup's consumers; every chunk re-reads the rows).
-static hipError_t launch_rebase_bf16(int nks_t, int nb, dim3 grid, size_t lds, hipStream_t st,
+static hipError_t launch_rebase_bf16(int nks_t, int nb, bool all, dim3 grid, size_t lds, hipStream_t st,
                                      const RebaseArgs& a) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -342,20 +383,31 @@ static hipError_t launch_rebase_bf16(int nks_t, int nb, dim3 grid, size_t lds, h
 #define LR_RB_CASES(X) X(4, 1) X(4, 2) X(4, 3) X(4, 4) X(4, 5) X(4, 6) X(4, 7) X(4, 8) \
                        X(8, 1) X(8, 2) X(8, 3) X(8, 4) X(12, 1) X(12, 2) X(12, 3) X(16, 1) X(16, 2)
 #define LR_RB_LAUNCH(K, N)                                                                      \
-  if (nks_t == K && nb == N) {                                                                  \
+  if (nks_t == K && nb == N && !all) {                                                          \
     if (dev >= 0 && dev < 64 && !attr[dev][vi]) {                                               \
-      e = hipFuncSetAttribute((const void*)lr_rebase_bf16<K, N>,                                \
+      e = hipFuncSetAttribute((const void*)lr_rebase_bf16<K, N, false>,                         \
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);           \
       if (e != hipSuccess) return e;                                                            \
       attr[dev][vi] = true;                                                                     \
     }                                                                                           \
-    hipLaunchKernelGGL((lr_rebase_bf16<K, N>), grid, dim3(kRbThreads), lds, st, a);             \
+    hipLaunchKernelGGL((lr_rebase_bf16<K, N, false>), grid, dim3(rb_threads(false)), lds, st, a); \
     return hipGetLastError();                                                                   \
   }                                                                                             \
   ++vi;
   LR_RB_CASES(LR_RB_LAUNCH)
 #undef LR_RB_LAUNCH
 #undef LR_RB_CASES
+  // the all-waves form: ranks of 12 K steps with 3 blocks per wave (8 waves, 384 coordinates)
+  if (nks_t == 12 && nb == 3 && all) {
+    if (dev >= 0 && dev < 64 && !attr[dev][23]) {
+      e = hipFuncSetAttribute((const void*)lr_rebase_bf16<12, 3, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kLdsBytes);
+      if (e != hipSuccess) return e;
+      attr[dev][23] = true;
+    }
+    hipLaunchKernelGGL((lr_rebase_bf16<12, 3, true>), grid, dim3(rb_threads(true)), lds, st, a);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 
@@ -401,7 +453,7 @@ hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const l
   rebase_shape(p.rv, p.rv_new, &sh[1]);
   a.col_chunk[0] = sh[0].col_chunk;
   a.col_chunk[1] = sh[1].col_chunk;
-  const bool together = sh[0].nks_t == sh[1].nks_t && sh[0].nb == sh[1].nb;
+  const bool together = sh[0].nks_t == sh[1].nks_t && sh[0].nb == sh[1].nb && sh[0].all == sh[1].all;
   for (int kv0 = 0; kv0 < 2; kv0 += together ? 2 : 1) {
     const int nmat = together ? 2 : 1;
     const int kv1 = kv0 + nmat - 1;
@@ -413,7 +465,8 @@ hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const l
     const int nks = (r_max + 31) / 32;
     const int sub = nks <= 8 ? 4 : 2;
     const int step_bytes = kRbTile * nks * 4 * 16 * sub;
-    const int per_wave = (nks + kRbProducers - 1) / kRbProducers * sub;
+    const int nl = sh[kv0].all ? kRbAllWaves : kRbProducers;   // waves that load the ring
+    const int per_wave = (nks + nl - 1) / nl * sub;
     int stages = 63 / per_wave + 1;
     if (stages > kRbMaxStages) stages = kRbMaxStages;
     if (stages * step_bytes > kLdsBytes) stages = kLdsBytes / step_bytes;
@@ -427,8 +480,8 @@ hipError_t launch_rebase(const RebasePlan& p, const lr_layer_cache* src, const l
     long long gx = device_cu_count() / (nmat * nchunk);
     gx = gx < 4 ? 4 : gx & ~3LL;      // 2*gx a multiple of 8: the chunks of one range share an XCD
     if (gx > steps) gx = steps;
-    hipError_t e = launch_rebase_bf16(sh[kv0].nks_t, sh[kv0].nb, dim3((unsigned)gx, nmat, (unsigned)nchunk),
-                                      lds, st, ak);
+    hipError_t e = launch_rebase_bf16(sh[kv0].nks_t, sh[kv0].nb, sh[kv0].all != 0,
+                                      dim3((unsigned)gx, nmat, (unsigned)nchunk), lds, st, ak);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

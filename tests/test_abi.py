@@ -199,7 +199,8 @@ def fake_dst(**kw):
     (dict(layer=1), L.LR_EINVAL),
     (dict(model=dict(latent_dtype="i4g32")), L.LR_EUNSUPPORTED),
     (dict(inplace=True, dst_kw=dict(ld_k=360, ld_v=360, t_cap=32)), L.LR_EINVAL),   # in place, t_cap differs
-    (dict(inplace=True, rk_new=352, rv_new=352), L.LR_EUNSUPPORTED),  # bf16 in place, two W chunks
+    (dict(inplace=True, model=dict(rank_k=[512], rank_v=[512]), src_kw=dict(ld_k=512, ld_v=512),
+          dst_kw=dict(ld_k=512, ld_v=512), rk_new=352, rv_new=352), L.LR_EUNSUPPORTED),  # bf16 in place, 3 W chunks
 ])
 def test_rebase_rejects_invalid_arguments(case, code):
     model = desc(**case.get("model", {}))
@@ -219,6 +220,8 @@ def test_rebase_zero_sizes_are_no_ops():
     assert call_rebase(desc(), fake_cache(), fake_dst(), max_len=0) == L.LR_OK
     # in place within one W chunk, nothing to do
     assert call_rebase(desc(), fake_cache(), fake_cache(), rk_new=192, rv_new=100, batch=0) == L.LR_OK
+    # rank 358 -> 352 in place: one chunk of the all-waves form
+    assert call_rebase(desc(), fake_cache(), fake_cache(), rk_new=352, rv_new=352, batch=0) == L.LR_OK
 
 
 @host_only
