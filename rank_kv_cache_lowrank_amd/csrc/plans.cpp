@@ -24,14 +24,19 @@ void rebase_shape(int r_old, int r_new, RebaseShape* s) {
   s->col_chunk = s->nb * kRbConsumers * 16;
   s->nchunk = (r_new + s->col_chunk - 1) / s->col_chunk;
   s->all = 0;
-  // 12 K steps leave room for 3 W blocks per wave: where 4 waves would need two chunks (each
-  // re-reading the rows), 8 waves that also load the ring make all new coordinates in one
-  const int all_cols = kRbAllWaves * 3 * 16;
-  if (s->nks_t == 12 && s->nchunk > 1 && r_new <= all_cols) {
-    s->all = 1;
-    s->nb = 3;
-    s->col_chunk = all_cols;
-    s->nchunk = 1;
+  // Where 4 consumer waves need several chunks (each re-reading the rows), 8 waves that also
+  // load the ring, each with as many W blocks as its registers hold, need half as many (one
+  // for ranks up to 384 at 12 K steps and up to 512 at 8).
+  if (s->nchunk > 1 && s->nks_t >= 8) {
+    const int nb = rb_nb_max(s->nks_t);
+    const int cols = kRbAllWaves * nb * 16;
+    const int nch = (r_new + cols - 1) / cols;
+    if (nch < s->nchunk) {
+      s->all = 1;
+      s->nb = nb;
+      s->col_chunk = cols;
+      s->nchunk = nch;
+    }
   }
 }
 

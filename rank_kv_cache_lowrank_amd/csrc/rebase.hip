@@ -397,17 +397,20 @@ static hipError_t launch_rebase_bf16(int nks_t, int nb, bool all, dim3 grid, siz
   LR_RB_CASES(LR_RB_LAUNCH)
 #undef LR_RB_LAUNCH
 #undef LR_RB_CASES
-  // the all-waves form: ranks of 12 K steps with 3 blocks per wave (8 waves, 384 coordinates)
-  if (nks_t == 12 && nb == 3 && all) {
-    if (dev >= 0 && dev < 64 && !attr[dev][23]) {
-      e = hipFuncSetAttribute((const void*)lr_rebase_bf16<12, 3, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              kLdsBytes);
-      if (e != hipSuccess) return e;
-      attr[dev][23] = true;
-    }
-    hipLaunchKernelGGL((lr_rebase_bf16<12, 3, true>), grid, dim3(rb_threads(true)), lds, st, a);
-    return hipGetLastError();
+  // the all-waves form: 8 waves of the most W blocks their registers hold
+#define LR_RB_ALL(K, N, I)                                                                        \
+  if (nks_t == K && nb == N && all) {                                                             \
+    if (dev >= 0 && dev < 64 && !attr[dev][I]) {                                                  \
+      e = hipFuncSetAttribute((const void*)lr_rebase_bf16<K, N, true>,                            \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);             \
+      if (e != hipSuccess) return e;                                                              \
+      attr[dev][I] = true;                                                                        \
+    }                                                                                             \
+    hipLaunchKernelGGL((lr_rebase_bf16<K, N, true>), grid, dim3(rb_threads(true)), lds, st, a);   \
+    return hipGetLastError();                                                                     \
   }
+  LR_RB_ALL(8, 4, 21) LR_RB_ALL(12, 3, 22) LR_RB_ALL(16, 2, 23)
+#undef LR_RB_ALL
   return hipErrorInvalidValue;
 }
 

@@ -107,7 +107,7 @@ def check_all(latent, src_host, dst_t, lat_len, r_old, r_new, w_host, exact_bits
 
 @pytest.mark.parametrize("rk,rv,rk2,rv2", [
     (358, 358, 358, 358), (256, 256, 256, 256), (512, 512, 512, 512), (1, 33, 33, 1),
-    (100, 64, 512, 80), (512, 130, 7, 200), (32, 48, 40, 16), (200, 300, 144, 460)])
+    (100, 64, 512, 80), (512, 130, 7, 200), (32, 48, 40, 16), (200, 300, 144, 460), (256, 250, 512, 400)])
 def test_bf16_general_update(rk, rv, rk2, rv2):
     lat_len = [0, 1, 31, 32, 33, 95, 300, 517]
     B, t_cap = len(lat_len), 520
