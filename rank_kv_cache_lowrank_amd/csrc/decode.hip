@@ -119,6 +119,7 @@ __device__ __forceinline__ bf16x4 v_operand4(const unsigned char* base, int col_
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
 // Matrix-core products on 16-bit operands held as raw bits: bf16 for float32/bf16 latents,
 // fp16 for the dequantised int4 tiles.
@@ -1148,20 +1149,36 @@ __global__ __launch_bounds__(256) void lr_combine(CombineArgs a) {
     lw = wp[a.d + 1];
   }
   float mloc = -INFINITY;
-  // the slot loads do not wait for ns: slots past it are loaded and then ignored
-  for (int s = tid; s < a.nsplit; s += 256) {
-    const float mv = a.part_ml[((base + s) * a.Hq + j) * 2];
-    if (s < ns) mloc = fmaxf(mloc, mv);
+  // the slot loads do not wait for ns: slots past it are loaded and then ignored. Up to 256 slots
+  // (one per thread) the slot's (m, l) come in one load and stay in registers for the weights.
+  const bool one = a.nsplit <= 256;
+  f32x2 ml_own = {-INFINITY, 0.f};
+  if (one) {
+    if (tid < a.nsplit) ml_own = *(const f32x2*)(a.part_ml + ((base + tid) * a.Hq + j) * 2);
+    if (tid < ns) mloc = ml_own[0];
+  } else {
+    for (int s = tid; s < a.nsplit; s += 256) {
+      const float mv = a.part_ml[((base + s) * a.Hq + j) * 2];
+      if (s < ns) mloc = fmaxf(mloc, mv);
+    }
   }
   const float mstar = block_reduce(fmaxf(mloc, mw), red, true);
   const bool live = mstar != -INFINITY;
 
   float lloc = 0.f;
-  for (int s = tid; s < ns; s += 256) {
-    const float ms = a.part_ml[((base + s) * a.Hq + j) * 2];
-    const float w = (live && ms != -INFINITY) ? fast_exp2(ms - mstar) : 0.f;
-    ws[s] = w;
-    if (w != 0.f) lloc += w * a.part_ml[((base + s) * a.Hq + j) * 2 + 1];
+  if (one) {
+    if (tid < ns) {
+      const float w = (live && ml_own[0] != -INFINITY) ? fast_exp2(ml_own[0] - mstar) : 0.f;
+      ws[tid] = w;
+      if (w != 0.f) lloc += w * ml_own[1];
+    }
+  } else {
+    for (int s = tid; s < ns; s += 256) {
+      const float ms = a.part_ml[((base + s) * a.Hq + j) * 2];
+      const float w = (live && ms != -INFINITY) ? fast_exp2(ms - mstar) : 0.f;
+      ws[s] = w;
+      if (w != 0.f) lloc += w * a.part_ml[((base + s) * a.Hq + j) * 2 + 1];
+    }
   }
   const float ww = (live && mw != -INFINITY) ? fast_exp2(mw - mstar) : 0.f;
   const float lstar = block_reduce(lloc, red, false) + ww * lw;
