@@ -487,6 +487,22 @@ __device__ __forceinline__ void i4_loader(const DecodeArgs& a, unsigned char* sm
     }
   };
 
+  // the two halves of dequant2 for one tile: its raw words into registers, then its fp16 stage
+  auto raw_read = [&](int rs, unsigned (&w)[NI], unsigned (&q)[NI]) {
+    const unsigned char* s0 = raw + rs * R.rs;
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      w[u] = *(const unsigned*)(s0 + i_src[u]);
+      q[u] = *(const unsigned*)(s0 + i_qp[u]);
+    }
+  };
+  auto stage_write = [&](int t, const unsigned (&w)[NI], const unsigned (&q)[NI]) {
+    unsigned char* d0 = smem + (t & 3) * VSTAGE;
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+      *(u32x4*)(d0 + i_dst[u]) = dequant8_f16(w[u], bcast_lo16(q[u]), bcast_hi16(q[u]), kM0, kM1, kE0, kE1);
+  };
+
   // The consumers' query loads go first (the copies would queue ahead of them in the memory
   // pipeline); then tiles 0-3 are copied, 0 and 1 converted, and the rest of the ring filled.
   barrier_lds();                                     // the consumers' query loads are issued
@@ -505,11 +521,18 @@ __device__ __forceinline__ void i4_loader(const DecodeArgs& a, unsigned char* sm
     // copying after is slower)
     // one tile's copies, one tile's conversion, then the other's: spread out, the copies stall
     // less on the memory pipeline's backlog (measured: 53.1 against 54.1 us at T = 16K)
+    // Both tiles' raw words are read first (their stages landed before the barrier; the copies
+    // issued below go to stages of tiles 2it - 2 and 2it - 1, as the ring holds at least 6), so
+    // the second tile's LDS round trip overlaps the first one's conversion.
     const int dq1 = dq_stage + 1 == NR ? 0 : dq_stage + 1;
+    const bool ha = 2 * it + 2 < ntiles, hb = 2 * it + 3 < ntiles;   // wave-uniform
+    unsigned wa[NI], qa[NI], wb[NI], qb[NI];
+    if (ha) raw_read(dq_stage, wa, qa);
+    if (hb) raw_read(dq1, wb, qb);
     if (it > 0 && 2 * it - 2 + NR < ntiles) issue(2 * it - 2 + NR);
-    if (2 * it + 2 < ntiles) dequant2(2 * it + 2, dq_stage, dq1, false);
+    if (ha) stage_write(2 * it + 2, wa, qa);
     if (it > 0 && 2 * it - 1 + NR < ntiles) issue(2 * it - 1 + NR);
-    if (2 * it + 3 < ntiles) dequant2(2 * it + 3, dq1, dq1, false);
+    if (hb) stage_write(2 * it + 3, wb, qb);
     dq_stage = dq1 + 1 == NR ? 0 : dq1 + 1;
     wait_vmcnt(count(2 * it + 5, min(2 * it - 1 + NR, ntiles - 1)));
   }
